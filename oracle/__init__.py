@@ -1,0 +1,26 @@
+"""fp64 CPU oracle for block-sparse attention -- TEST INFRASTRUCTURE ONLY.
+
+This package is the slow, obviously correct statement of what the HIP path
+computes.  It is test infrastructure: only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or call it.  The
+product path (``block_sparse_transformer_amd``) never imports it and has no
+CPU fallback; the oracle shares no code, table or constant generator with the
+HIP sources.
+
+Modules
+-------
+``layout``    the block layout rule (sliding window + global + hash-random
+              blocks) written out with plain Python lists, expanded to a
+              0/1 token mask.
+``attention`` dense masked softmax attention in fp64 from that mask.
+``router``    the routed-query selection: exact fp64 score q.w and top-k.
+
+Parity pins (see ``tests/test_oracle_*.py``): every function is checked
+against something other than itself -- published splitmix64 outputs, closed
+form layout counts, library routines (``scaled_dot_product_attention`` in
+fp64), brute-force loops, exact rational arithmetic and closed forms of the
+softmax.  Parity unpinned: the concrete choice of random blocks beyond the
+hash stream itself (the composition of the per-row seed and the shuffle are
+this library's own specification; any uniform draw satisfies the pages).
+"""
+from . import layout, attention, router  # noqa: F401

@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs for block-sparse attention.
+
+This module only *draws* inputs.  It holds none of the method's arithmetic
+(no layout rule, no attention, no routing): both the HIP path and the fp64
+oracle consume the tensors it returns, and neither imports the other.
+
+The five named workloads mirror the shapes the pages talk about:
+
+* BERT-base heads (12 heads of width 64) at 512 and 2048 tokens -- the
+  primer page's 512-token example and the 2048-token figures quoted by the
+  Adaptive-Sparse-Transformer and SQA pages;
+* 8192 tokens, the sequence length of the BigBird page's performance table
+  (section 性能分析);
+* long padded documents (16384 tokens, head width 128) for the key-padding
+  mask of the primer page's code sample;
+* the SQA page's LLaMA-7B head shape (32 heads of width 128) with k=64 routed
+  queries and a +-32 token local window (sections 2.1 and 4).
+
+None of the pages' datasets (GLUE, IMDb, WikiText-103, PubMed, WMT14,
+genomes) is available; kernel time does not depend on token content, so
+Gaussian Q/K/V of the right shape stand in for them.
+
+Draw order per workload, from one ``torch.Generator`` seeded with
+``data_seed``: Q, K, V (fp32 ``randn * sigma``, then cast to bf16 with
+round-to-nearest-even for bf16 workloads), then the router weight ``w``
+(fp32, routed workloads), then ``valid_len`` (padded workloads,
+``randint(L//2, L+1)`` -- uniform on the inclusive range [L/2, L]).
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    heads: int
+    seq_len: int
+    head_dim: int
+    dtype: str                      # "f32" or "bf16": the input/output element type
+    data_seed: int
+    block: int = 64
+    window_blocks: int = 0          # odd; self +- (window_blocks-1)/2 blocks, clipped
+    global_blocks: Tuple[int, ...] = ()
+    random_blocks: int = 0
+    layout_seed: int = 0
+    sigma: float = 1.0
+    padded: bool = False            # per-batch key valid length drawn after Q/K/V
+    routed_k: int = 0               # >0: routed-query variant (top-k rows attend to all keys)
+    band_tokens: int = 0            # routed variant: other rows see keys with |t-s| <= band
+
+    @property
+    def routed(self) -> bool:
+        return self.routed_k > 0
+
+    @property
+    def num_blocks(self) -> int:
+        return self.seq_len // self.block
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / (self.head_dim ** 0.5)
+
+    def with_(self, **kw) -> "Workload":
+        """A copy with some fields replaced (smaller test shapes of the same recipe)."""
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    # 8x8 blocks, fp32 end to end: window self+-1 (clipped), global block 0, one random block.
+    "tiny-f32-L512": Workload(
+        name="tiny-f32-L512", batch=1, heads=2, seq_len=512, head_dim=64, dtype="f32",
+        data_seed=0, window_blocks=3, global_blocks=(0,), random_blocks=1, layout_seed=0),
+    # BigBird layout at 2048 tokens: window 3, first/last block global, 3 random blocks.
+    "bigbird-L2048": Workload(
+        name="bigbird-L2048", batch=8, heads=12, seq_len=2048, head_dim=64, dtype="bf16",
+        data_seed=1, window_blocks=3, global_blocks=(0, 31), random_blocks=3, layout_seed=1),
+    # BigBird layout at 8192 tokens (128 blocks a side): the throughput workload.
+    "bigbird-L8192": Workload(
+        name="bigbird-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
+        data_seed=2, window_blocks=3, global_blocks=(0, 127), random_blocks=3, layout_seed=2),
+    # Sliding window of 5 blocks + global block 0, trailing keys padded per batch entry.
+    "window-pad-L16384": Workload(
+        name="window-pad-L16384", batch=4, heads=16, seq_len=16384, head_dim=128, dtype="bf16",
+        data_seed=3, window_blocks=5, global_blocks=(0,), random_blocks=0, layout_seed=3,
+        sigma=0.5, padded=True),
+    # Routed queries: per head the top-64 rows by q.w attend to every key, the rest to +-32 tokens.
+    "routed-L4096": Workload(
+        name="routed-L4096", batch=1, heads=32, seq_len=4096, head_dim=128, dtype="bf16",
+        data_seed=4, routed_k=64, band_tokens=32),
+}
+
+THROUGHPUT_WORKLOAD = "bigbird-L8192"
+
+
+def torch_dtype(wl: Workload) -> torch.dtype:
+    return torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+
+def make_inputs(wl: Workload, device: Optional[str] = None) -> dict:
+    """Draw the inputs of ``wl`` on the CPU (optionally moved to ``device``).
+
+    Returns a dict with ``q, k, v`` ([B, H, L, D], contiguous, the workload's
+    dtype), ``w`` ([D] fp32, routed workloads only) and ``valid_len``
+    ([B] int32, padded workloads only).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(wl.data_seed)
+    shape = (wl.batch, wl.heads, wl.seq_len, wl.head_dim)
+    dt = torch_dtype(wl)
+    out = {}
+    for name in ("q", "k", "v"):
+        x = torch.randn(shape, generator=g, dtype=torch.float32) * wl.sigma
+        out[name] = x.to(dt).contiguous()
+    if wl.routed:
+        out["w"] = torch.randn((wl.head_dim,), generator=g, dtype=torch.float32)
+    if wl.padded:
+        out["valid_len"] = torch.randint(wl.seq_len // 2, wl.seq_len + 1, (wl.batch,),
+                                         generator=g, dtype=torch.int64).to(torch.int32)
+    if device is not None:
+        out = {k: v.to(device) for k, v in out.items()}
+    return out
