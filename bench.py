@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Throughput of the block-sparse attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one full forward (``bsattn_forward``: every non-zero 64x64 tile of
+the layout, the split of the dense global rows and their log-sum-exp merge)
+over one batch of the workload, inputs already resident in HBM.  W untimed
+steps, then exactly K timed steps bracketed by device synchronisation; three
+copies of the inputs are rotated so that consecutive steps do not hit the
+256 MB last-level cache with the previous step's tensors.
+
+Prints ONE JSON line with the metric, ``roofline`` (the main attention
+kernel timed by HIP events around each of its launches inside the timed
+region, priced against the bf16 dense MFMA peak) and ``cpu_baseline`` (the
+fp64 oracle on a bounded sample of the same workload, on the host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn fwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), L=8192"
+# MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "fwd_bf16.hip")
+MAIN_KERNEL = "fwd_bf16_kernel"
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=None, help="default: the L=8192 BigBird workload")
+    p.add_argument("--rotate", type=int, default=3, help="input copies rotated across steps")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-heads", type=int, default=1,
+                   help="(batch, head) pairs the oracle runs for the CPU baseline")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="instead of the benchmark, run plain device copies of MIB MiB (counter calibration)")
+    return p.parse_args()
+
+
+def tile_stats(wl, row_ptr, col, valid_len=None):
+    """Non-zero 64x64 tiles computed per step (padding-aware when valid_len is given)."""
+    import numpy as np
+    per_head = np.diff(row_ptr).reshape(wl.heads, wl.num_blocks)
+    if valid_len is None:
+        return int(per_head.sum()) * wl.batch
+    total = 0
+    for b in range(wl.batch):
+        nvb = -(-int(valid_len[b]) // 64)
+        total += int((col < nvb).sum())
+    return total
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch of the main kernel from the committed counter summary, or None
+    when the summary is missing or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{MAIN_KERNEL}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b:
+        return None
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if sha != m_sha.group(1):
+        return None
+    return float(m_b.group(1))
+
+
+def calibrate_copy(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}))
+
+
+def cpu_baseline(wl, inp, layout_o, n_pairs: int):
+    """The oracle as it stands, on the first n_pairs (batch, head) pairs, all query rows."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as OA
+    pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)][:n_pairs]
+    vl = inp.get("valid_len")
+    t0 = time.perf_counter()
+    for b, h in pairs:
+        OA.attention_forward(inp["q"], inp["k"], inp["v"], layout_o, wl.scale,
+                             valid_len=None if vl is None else vl.tolist(), heads=[h], batches=[b])
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    full_s = dt * (wl.batch * wl.heads) / len(pairs)
+    return {"value": wl.batch * wl.seq_len / full_s, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(pairs)} of {wl.batch * wl.heads} (batch, head) pairs, all {wl.seq_len} query rows, "
+                      f"dense fp64 masked attention; {dt:.2f} s measured, scaled to the whole job",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "each (batch, head) pair is independent, so more GPUs would shard heads with no collective.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_transformer_amd as bs
+    from workloads import THROUGHPUT_WORKLOAD, WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
+    wl = WORKLOADS[args.workload or THROUGHPUT_WORKLOAD]
+    if wl.routed:
+        print("bench.py times the block-layout forward; routed workloads are parity cases", file=sys.stderr)
+        sys.exit(2)
+    inp = make_inputs(wl)
+
+    t0 = time.perf_counter()
+    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+                                wl.random_blocks, wl.layout_seed)
+    layout_host_us = (time.perf_counter() - t0) * 1e6
+    bs.bsattn_layout_upload(lay)
+    row_ptr, col = bs.bsattn_layout_csr(lay)
+    vl_host = inp.get("valid_len")
+    tiles = tile_stats(wl, row_ptr, col, None if vl_host is None else vl_host.tolist())
+    flops_per_step = tiles * 4.0 * 64 * 64 * wl.head_dim
+    elem = 2 if wl.dtype == "bf16" else 4
+    alg_bytes = wl.batch * wl.heads * wl.seq_len * (4 * wl.head_dim * elem + 4)
+
+    dev = torch.device("cuda:0")
+    sets = []
+    base = {k: v.to(dev) for k, v in inp.items()}
+    for r in range(max(1, args.rotate)):
+        sets.append({k: (v if r == 0 else v.clone()) for k, v in base.items()})
+    B, H, L, D = wl.batch, wl.heads, wl.seq_len, wl.head_dim
+    outs = [torch.empty((B, H, L, D), dtype=base["q"].dtype, device=dev) for _ in sets]
+    lses = [torch.empty((B, H, L), dtype=torch.float32, device=dev) for _ in sets]
+    ws_bytes = bs.bsattn_workspace_size(lay, B, D)
+    ws = torch.empty(max(1, (ws_bytes + 255) // 4), dtype=torch.float32, device=dev)
+
+    # Pre-marshalled C calls: the timed loop pays only the ctypes call itself.
+    L_ = bs.lib()
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    dtype_code = 1 if wl.dtype == "bf16" else 0
+    calls = []
+    for s, o, l in zip(sets, outs, lses):
+        vl = s.get("valid_len")
+        calls.append((lay.handle, dtype_code, B, H, L, D, s["q"].data_ptr(), s["k"].data_ptr(),
+                      s["v"].data_ptr(), o.data_ptr(), l.data_ptr(), None if vl is None else vl.data_ptr(),
+                      ctypes.c_float(wl.scale), ws.data_ptr(), ctypes.c_size_t(ws_bytes), sh))
+    fwd = L_.bsattn_forward
+
+    def step(i):
+        st = fwd(*calls[i % len(calls)])
+        if st != 0:
+            raise bs.BsattnError("bsattn_forward", st)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = bs.HipEvents(K)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    set_ev = L_.bsattn_set_profile_events
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        set_ev(ev.before[i], ev.after[i])
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    set_ev(None, None)
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / K
+    kern_ms = [ev.elapsed_ms(i) for i in range(K)]
+    ev.destroy()
+    kern_avg_ms = float(np.mean(kern_ms))
+
+    tokens = B * L
+    value = tokens / (ms_step / 1e3)
+    eff_tflops = flops_per_step / (ms_step / 1e3) / 1e12
+    kern_tflops = flops_per_step / (kern_avg_ms / 1e3) / 1e12
+    traffic = traffic_from_profile(wl.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded Gaussian Q/K/V of the workload's shape)",
+        "config": {
+            "workload": wl.name, "batch": B, "heads": H, "seq_len": L, "head_dim": D, "block": 64,
+            "window_blocks": wl.window_blocks, "global_blocks": list(wl.global_blocks),
+            "random_blocks": wl.random_blocks, "layout_seed": wl.layout_seed,
+            "nonzero_tiles": tiles, "layout_density": round(tiles / (B * H * (L // 64) ** 2), 5),
+        },
+        "eff_tflops": round(eff_tflops, 2),
+        "pct_bf16_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),
+        "hbm_alg_gbps": round(alg_bytes / (ms_step / 1e3) / 1e9, 1),
+        "layout_build_host_us": round(layout_host_us, 1),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": MAIN_KERNEL,
+            "achieved": round(kern_tflops, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
+            "flop_per_launch": flops_per_step,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import layout as OL
+        olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+                              wl.random_blocks, wl.layout_seed)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, olay, args.cpu_sample_heads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,34 @@
+"""block_sparse_transformer_amd -- block-sparse attention forward on AMD MI355X (gfx950).
+
+A thin ctypes binding of ``libbsattn.so`` (declared in ``include/bsattn.h``).
+Every function here only marshals arguments: tensors become device pointers,
+the current torch stream becomes the ``hipStream_t``.  All computation runs in
+the HIP kernels of the library; there is no CPU fallback, and every function
+raises if the library has not been built.
+
+Functions carry the C names (``bsattn_make_layout``, ``bsattn_forward``, ...)
+plus two conveniences, :func:`forward` and :func:`forward_routed`, that
+allocate outputs and workspace with torch.
+"""
+from ._binding import (  # noqa: F401
+    BsattnError,
+    Layout,
+    bsattn_forward,
+    bsattn_forward_routed,
+    bsattn_last_error,
+    bsattn_layout_build_device,
+    bsattn_layout_csr,
+    bsattn_layout_destroy,
+    bsattn_layout_upload,
+    bsattn_make_band_layout,
+    bsattn_make_layout,
+    bsattn_route_topk,
+    bsattn_set_profile_events,
+    bsattn_status_string,
+    bsattn_workspace_size,
+    forward,
+    forward_routed,
+    lib,
+    library_path,
+    HipEvents,
+)

@@ -1,0 +1,299 @@
+"""ctypes marshalling for libbsattn.so (see include/bsattn.h for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libbsattn.so")
+_lib = None
+
+BSATTN_F32 = 0
+BSATTN_BF16 = 1
+
+_c_int = ctypes.c_int32
+_c_vp = ctypes.c_void_p
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class BsattnError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func} failed: {bsattn_status_string(status)}: {bsattn_last_error()}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbsattn.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m block_sparse_transformer_amd.build` "
+            "(or __graft_entry__.build()). There is no CPU fallback.")
+    L = ctypes.CDLL(_LIB_PATH)
+    L.bsattn_make_layout.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_i32p, _c_int, _c_int,
+                                     ctypes.c_uint64, ctypes.POINTER(_c_vp)]
+    L.bsattn_make_band_layout.argtypes = [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_vp)]
+    L.bsattn_layout_csr.argtypes = [_c_vp, ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_i32p),
+                                    ctypes.POINTER(_c_int), ctypes.POINTER(ctypes.c_int64)]
+    L.bsattn_layout_upload.argtypes = [_c_vp, _c_vp]
+    L.bsattn_layout_build_device.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp]
+    L.bsattn_layout_destroy.argtypes = [_c_vp]
+    L.bsattn_layout_destroy.restype = None
+    L.bsattn_workspace_size.argtypes = [_c_vp, _c_int, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]
+    L.bsattn_forward.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
+                                 _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_size_t, _c_vp]
+    L.bsattn_route_topk.argtypes = [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp]
+    L.bsattn_forward_routed.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp,
+                                        _c_vp, _c_vp, _c_int, _c_vp, _c_vp, ctypes.c_float, _c_vp,
+                                        ctypes.c_size_t, _c_vp]
+    L.bsattn_set_profile_events.argtypes = [_c_vp, _c_vp]
+    L.bsattn_status_string.argtypes = [ctypes.c_int]
+    L.bsattn_status_string.restype = ctypes.c_char_p
+    L.bsattn_last_error.argtypes = []
+    L.bsattn_last_error.restype = ctypes.c_char_p
+    for name in ("bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr", "bsattn_layout_upload",
+                 "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
+                 "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def bsattn_status_string(status: int) -> str:
+    return lib().bsattn_status_string(int(status)).decode()
+
+
+def bsattn_last_error() -> str:
+    return lib().bsattn_last_error().decode()
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise BsattnError(func, status)
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class Layout:
+    """Owner of a ``bsattn_layout*``; freed on destroy() or garbage collection."""
+
+    def __init__(self, handle: int, num_heads: int, seq_len: int, band_tokens: Optional[int] = None):
+        self._h = handle
+        self.num_heads = num_heads
+        self.seq_len = seq_len
+        self.band_tokens = band_tokens
+
+    @property
+    def handle(self) -> int:
+        if not self._h:
+            raise ValueError("layout has been destroyed")
+        return self._h
+
+    def destroy(self) -> None:
+        if self._h:
+            lib().bsattn_layout_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def bsattn_make_layout(num_heads: int, seq_len: int, block: int, window_blocks: int,
+                       global_blocks: Sequence[int], random_blocks: int, seed: int) -> Layout:
+    g = (ctypes.c_int32 * max(1, len(global_blocks)))(*global_blocks)
+    out = _c_vp()
+    _check("bsattn_make_layout", lib().bsattn_make_layout(
+        num_heads, seq_len, block, window_blocks, g if len(global_blocks) else None, len(global_blocks),
+        random_blocks, ctypes.c_uint64(seed & ((1 << 64) - 1)), ctypes.byref(out)))
+    return Layout(out.value, num_heads, seq_len)
+
+
+def bsattn_make_band_layout(num_heads: int, seq_len: int, block: int, band_tokens: int) -> Layout:
+    out = _c_vp()
+    _check("bsattn_make_band_layout", lib().bsattn_make_band_layout(num_heads, seq_len, block, band_tokens,
+                                                                    ctypes.byref(out)))
+    return Layout(out.value, num_heads, seq_len, band_tokens=band_tokens)
+
+
+def bsattn_layout_csr(layout: Layout) -> Tuple[np.ndarray, np.ndarray]:
+    """Copies of the host CSR arrays (row_ptr [rows+1], col_idx [nnz]) as int32 numpy."""
+    rp, ci = _c_i32p(), _c_i32p()
+    nrows, nnz = _c_int(), ctypes.c_int64()
+    _check("bsattn_layout_csr", lib().bsattn_layout_csr(layout.handle, ctypes.byref(rp), ctypes.byref(ci),
+                                                        ctypes.byref(nrows), ctypes.byref(nnz)))
+    row_ptr = np.ctypeslib.as_array(rp, shape=(nrows.value + 1,)).copy()
+    col = np.ctypeslib.as_array(ci, shape=(max(1, nnz.value),))[: nnz.value].copy()
+    return row_ptr, col
+
+
+def bsattn_layout_upload(layout: Layout, stream=None) -> None:
+    _check("bsattn_layout_upload", lib().bsattn_layout_upload(layout.handle, _stream_handle(stream)))
+
+
+def bsattn_layout_build_device(layout: Layout, row_ptr_dev, col_idx_dev, stream=None) -> None:
+    _check("bsattn_layout_build_device", lib().bsattn_layout_build_device(
+        layout.handle, _ptr(row_ptr_dev), _ptr(col_idx_dev), _stream_handle(stream)))
+
+
+def bsattn_layout_destroy(layout: Layout) -> None:
+    layout.destroy()
+
+
+def bsattn_workspace_size(layout: Layout, batch: int, head_dim: int, num_routed: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check("bsattn_workspace_size", lib().bsattn_workspace_size(layout.handle, batch, head_dim, num_routed,
+                                                                ctypes.byref(n)))
+    return n.value
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BSATTN_BF16
+    if t.dtype == torch.float32:
+        return BSATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_qkv(q, k, v, out):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4 or tuple(t.shape) != tuple(q.shape):
+            raise ValueError(f"{name} must have the shape of q {tuple(q.shape)}")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q's dtype and device")
+
+
+def bsattn_forward(layout: Layout, q, k, v, out, lse, key_valid_len=None, scale: Optional[float] = None,
+                   workspace=None, stream=None) -> None:
+    """Enqueue the forward pass; all tensors are caller-allocated device tensors."""
+    import torch
+    _check_qkv(q, k, v, out)
+    B, H, L, D = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, L] tensor")
+    if key_valid_len is not None and (key_valid_len.dtype != torch.int32 or key_valid_len.numel() != B):
+        raise ValueError("key_valid_len must be int32 [B]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bsattn_forward", lib().bsattn_forward(
+        layout.handle, _dtype_code(q), B, H, L, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+        _ptr(key_valid_len), scale, _ptr(workspace), wbytes, _stream_handle(stream)))
+
+
+def bsattn_route_topk(q, w, k: int, routed_rows, stream=None) -> None:
+    import torch
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 4:
+        raise ValueError("q must be a contiguous bf16 [B, H, L, D] tensor")
+    B, H, L, D = q.shape
+    if w.dtype != torch.float32 or w.numel() != D:
+        raise ValueError("w must be fp32 [D]")
+    if routed_rows.dtype != torch.int32 or tuple(routed_rows.shape) != (B, H, k):
+        raise ValueError("routed_rows must be int32 [B, H, k]")
+    _check("bsattn_route_topk", lib().bsattn_route_topk(_ptr(q), _ptr(w), B, H, L, D, k, _ptr(routed_rows),
+                                                        _stream_handle(stream)))
+
+
+def bsattn_forward_routed(band_layout: Layout, q, k, v, routed_rows, out, lse, scale: Optional[float] = None,
+                          workspace=None, stream=None) -> None:
+    import torch
+    _check_qkv(q, k, v, out)
+    B, H, L, D = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, L] tensor")
+    if routed_rows.dtype != torch.int32 or routed_rows.dim() != 3 or tuple(routed_rows.shape[:2]) != (B, H):
+        raise ValueError("routed_rows must be int32 [B, H, k]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bsattn_forward_routed", lib().bsattn_forward_routed(
+        band_layout.handle, _dtype_code(q), B, H, L, D, _ptr(q), _ptr(k), _ptr(v), _ptr(routed_rows),
+        int(routed_rows.shape[2]), _ptr(out), _ptr(lse), scale, _ptr(workspace), wbytes,
+        _stream_handle(stream)))
+
+
+def bsattn_set_profile_events(before: Optional[int], after: Optional[int]) -> None:
+    _check("bsattn_set_profile_events", lib().bsattn_set_profile_events(before, after))
+
+
+def _workspace(layout: Layout, q, num_routed: int = 0):
+    import torch
+    n = bsattn_workspace_size(layout, q.shape[0], q.shape[3], num_routed)
+    if n == 0:
+        return None
+    return torch.empty((n + 255) // 4, dtype=torch.float32, device=q.device)
+
+
+def forward(q, k, v, layout: Layout, key_valid_len=None, scale: Optional[float] = None, workspace=None):
+    """Allocate (out, lse) with torch and run :func:`bsattn_forward` on the current stream."""
+    import torch
+    B, H, L, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(layout, q)
+    bsattn_forward(layout, q, k, v, out, lse, key_valid_len, scale, workspace)
+    return out, lse
+
+
+def forward_routed(q, k, v, band_layout: Layout, routed_rows, scale: Optional[float] = None, workspace=None):
+    import torch
+    B, H, L, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(band_layout, q, int(routed_rows.shape[2]))
+    bsattn_forward_routed(band_layout, q, k, v, routed_rows, out, lse, scale, workspace)
+    return out, lse
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs from the HIP runtime, for timing one kernel on a given stream."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(_c_vp)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _c_vp, _c_vp]
+        self._hip.hipEventSynchronize.argtypes = [_c_vp]
+        self._hip.hipEventDestroy.argtypes = [_c_vp]
+        self.before, self.after = [], []
+        for _ in range(n):
+            for lst in (self.before, self.after):
+                e = _c_vp()
+                if self._hip.hipEventCreate(ctypes.byref(e)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                lst.append(e.value)
+
+    def elapsed_ms(self, i: int) -> float:
+        ms = ctypes.c_float()
+        if self._hip.hipEventSynchronize(self.after[i]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.before[i], self.after[i]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self) -> None:
+        for e in self.before + self.after:
+            self._hip.hipEventDestroy(e)
+        self.before, self.after = [], []

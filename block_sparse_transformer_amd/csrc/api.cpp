@@ -1,0 +1,467 @@
+// api.cpp -- C ABI of libbsattn: validation, host layout build, scheduling, dispatch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+using namespace bsattn;
+
+namespace {
+
+thread_local std::string g_error;
+thread_local hipEvent_t g_ev_before = nullptr;
+thread_local hipEvent_t g_ev_after = nullptr;
+
+bsattn_status fail(bsattn_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+bsattn_status ok() {
+    g_error.clear();
+    return BSATTN_OK;
+}
+
+bsattn_status hip_fail(hipError_t e, const char* what) {
+    return fail(BSATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Work schedule: rows of <= kChunkTiles blocks become one item; longer rows are
+// split into balanced chunks whose partials are merged afterwards.  Items are
+// ordered longest first so the long chunks start before the short rows.
+void build_schedule(bsattn_layout* lay) {
+    lay->items.clear();
+    lay->merges.clear();
+    int32_t slot = 0;
+    const int32_t rows = lay->H * lay->nb;
+    for (int32_t r = 0; r < rows; ++r) {
+        const int32_t b0 = lay->row_ptr[r], b1 = lay->row_ptr[r + 1];
+        const int32_t len = b1 - b0;
+        if (len <= kChunkTiles) {
+            lay->items.push_back({r, b0, b1, -1});
+            continue;
+        }
+        int32_t nch, per;
+        split_row(len, &nch, &per);
+        lay->merges.push_back({r, slot, nch, 0});
+        for (int32_t c = 0; c < nch; ++c) {
+            const int32_t s = b0 + c * per;
+            const int32_t e = std::min(b1, s + per);
+            lay->items.push_back({r, s, e, slot++});
+        }
+    }
+    lay->n_slots = slot;
+    std::stable_sort(lay->items.begin(), lay->items.end(), [](const WorkItem& x, const WorkItem& y) {
+        return (x.col_end - x.col_begin) > (y.col_end - y.col_begin);
+    });
+}
+
+void free_device(bsattn_layout* lay) {
+    if (lay->device >= 0) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        if (cur != lay->device) (void)hipSetDevice(lay->device);
+        (void)hipFree(lay->d_row_ptr);
+        (void)hipFree(lay->d_col_idx);
+        (void)hipFree(lay->d_items);
+        (void)hipFree(lay->d_merges);
+        if (cur >= 0 && cur != lay->device) (void)hipSetDevice(cur);
+    }
+    lay->d_row_ptr = lay->d_col_idx = nullptr;
+    lay->d_items = nullptr;
+    lay->d_merges = nullptr;
+    lay->device = -1;
+}
+
+bsattn_status check_layout_dims(int32_t H, int32_t L, int32_t block) {
+    if (H < 1) return fail(BSATTN_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", H);
+    if (block != kBlock) return fail(BSATTN_ERR_UNSUPPORTED, "block must be 64 (got %d)", block);
+    if (L < block || L % block != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "seq_len must be a positive multiple of %d (got %d)", block, L);
+    if ((int64_t)H * (L / block) > (1 << 20))
+        return fail(BSATTN_ERR_UNSUPPORTED, "num_heads * seq_len/64 exceeds 2^20");
+    return BSATTN_OK;
+}
+
+bsattn_status finish_layout(bsattn_layout* lay) {
+    build_schedule(lay);
+    return ok();
+}
+
+// Shape/pointer checks shared by both forward entry points.
+bsattn_status check_forward_common(const bsattn_layout* lay, int32_t B, int32_t H, int32_t L,
+                                   int32_t D, const void* q, const void* k, const void* v,
+                                   void* out, float* lse, float scale) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (B < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", B);
+    if (H != lay->H || L != lay->L)
+        return fail(BSATTN_ERR_INVALID_ARG, "H=%d L=%d do not match the layout (H=%d L=%d)", H, L,
+                    lay->H, lay->L);
+    if (D != 64 && D != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+    if (!q || !k || !v || !out || !lse) return fail(BSATTN_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+        return fail(BSATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (out == q || out == k || out == v) return fail(BSATTN_ERR_INVALID_ARG, "out aliases an input");
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(BSATTN_ERR_INVALID_ARG, "scale must be positive and finite");
+    if ((int64_t)B * H * L * D >= (int64_t)1 << 40)
+        return fail(BSATTN_ERR_UNSUPPORTED, "tensor too large");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (lay->device < 0 || lay->device != dev)
+        return fail(BSATTN_ERR_STATE, "layout is not uploaded to the current device (%d)", dev);
+    return BSATTN_OK;
+}
+
+size_t slot_bytes(int32_t D) { return (size_t)kBlock * (size_t)(D + 1) * sizeof(float); }
+
+void routed_split(int32_t nb, int32_t k, int32_t* n_rt, int32_t* r_chunks, int32_t* per) {
+    *n_rt = (k + kBlock - 1) / kBlock;
+    split_row(nb, r_chunks, per);
+    *r_chunks = (nb + *per - 1) / *per;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsattn_status_string(bsattn_status st) {
+    switch (st) {
+        case BSATTN_OK: return "ok";
+        case BSATTN_ERR_INVALID_ARG: return "invalid argument";
+        case BSATTN_ERR_UNSUPPORTED: return "unsupported";
+        case BSATTN_ERR_HIP: return "HIP runtime error";
+        case BSATTN_ERR_NO_MEMORY: return "out of memory";
+        case BSATTN_ERR_STATE: return "layout not uploaded to this device";
+    }
+    return "unknown status";
+}
+
+const char* bsattn_last_error(void) { return g_error.c_str(); }
+
+bsattn_status bsattn_make_layout(int32_t num_heads, int32_t seq_len, int32_t block,
+                                 int32_t window_blocks, const int32_t* global_blocks,
+                                 int32_t num_global, int32_t random_blocks, uint64_t seed,
+                                 bsattn_layout** out) {
+    if (!out) return fail(BSATTN_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    bsattn_status st = check_layout_dims(num_heads, seq_len, block);
+    if (st != BSATTN_OK) return st;
+    const int32_t nb = seq_len / block;
+    if (window_blocks < 1 || window_blocks % 2 == 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "window_blocks must be odd and >= 1 (got %d)", window_blocks);
+    if (window_blocks > kMaxWindowBlocks)
+        return fail(BSATTN_ERR_UNSUPPORTED, "window_blocks > %d", kMaxWindowBlocks);
+    if (num_global < 0 || num_global > kMaxGlobal)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_global must be in [0, %d] (got %d)", kMaxGlobal, num_global);
+    if (num_global > 0 && !global_blocks) return fail(BSATTN_ERR_INVALID_ARG, "global_blocks is NULL");
+    if (random_blocks < 0 || random_blocks > kMaxRandom)
+        return fail(BSATTN_ERR_INVALID_ARG, "random_blocks must be in [0, %d] (got %d)", kMaxRandom,
+                    random_blocks);
+    RowRule rule{};
+    rule.nb = nb;
+    rule.wh = (window_blocks - 1) / 2;
+    rule.r = random_blocks;
+    rule.ng = num_global;
+    rule.seed = seed;
+    for (int32_t a = 0; a < num_global; ++a) {
+        const int32_t g = global_blocks[a];
+        if (g < 0 || g >= nb) return fail(BSATTN_ERR_INVALID_ARG, "global block %d out of [0, %d)", g, nb);
+        rule.g[a] = g;
+    }
+    std::sort(rule.g, rule.g + num_global);
+    for (int32_t a = 1; a < num_global; ++a)
+        if (rule.g[a] == rule.g[a - 1]) return fail(BSATTN_ERR_INVALID_ARG, "duplicate global block %d", rule.g[a]);
+
+    bsattn_layout* lay = new (std::nothrow) bsattn_layout();
+    if (!lay) return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    try {
+        lay->H = num_heads;
+        lay->L = seq_len;
+        lay->nb = nb;
+        lay->block = block;
+        lay->kind = 0;
+        lay->rule = rule;
+        const int32_t rows = num_heads * nb;
+        lay->row_ptr.assign((size_t)rows + 1, 0);
+        for (int32_t h = 0; h < num_heads; ++h)
+            for (int32_t i = 0; i < nb; ++i)
+                lay->row_ptr[(size_t)h * nb + i + 1] = rule_row_count(rule, h, i);
+        for (int32_t r = 0; r < rows; ++r) lay->row_ptr[r + 1] += lay->row_ptr[r];
+        lay->col_idx.assign((size_t)lay->row_ptr[rows], 0);
+        for (int32_t h = 0; h < num_heads; ++h)
+            for (int32_t i = 0; i < nb; ++i) {
+                const int32_t r = h * nb + i;
+                rule_row_fill(rule, h, i, lay->col_idx.data() + lay->row_ptr[r]);
+            }
+    } catch (const std::bad_alloc&) {
+        delete lay;
+        return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    }
+    *out = lay;
+    return finish_layout(lay);
+}
+
+bsattn_status bsattn_make_band_layout(int32_t num_heads, int32_t seq_len, int32_t block,
+                                      int32_t band_tokens, bsattn_layout** out) {
+    if (!out) return fail(BSATTN_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    bsattn_status st = check_layout_dims(num_heads, seq_len, block);
+    if (st != BSATTN_OK) return st;
+    if (band_tokens < 0 || band_tokens >= seq_len)
+        return fail(BSATTN_ERR_INVALID_ARG, "band_tokens must be in [0, seq_len) (got %d)", band_tokens);
+    const int32_t nb = seq_len / block;
+    bsattn_layout* lay = new (std::nothrow) bsattn_layout();
+    if (!lay) return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    try {
+        lay->H = num_heads;
+        lay->L = seq_len;
+        lay->nb = nb;
+        lay->block = block;
+        lay->kind = 1;
+        lay->band_tokens = band_tokens;
+        lay->rule.nb = nb;
+        const int32_t rows = num_heads * nb;
+        lay->row_ptr.assign((size_t)rows + 1, 0);
+        for (int32_t r = 0; r < rows; ++r)
+            lay->row_ptr[r + 1] = lay->row_ptr[r] + band_row_fill(nb, block, band_tokens, r % nb, nullptr);
+        lay->col_idx.assign((size_t)lay->row_ptr[rows], 0);
+        for (int32_t r = 0; r < rows; ++r)
+            band_row_fill(nb, block, band_tokens, r % nb, lay->col_idx.data() + lay->row_ptr[r]);
+    } catch (const std::bad_alloc&) {
+        delete lay;
+        return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    }
+    *out = lay;
+    return finish_layout(lay);
+}
+
+bsattn_status bsattn_layout_csr(const bsattn_layout* lay, const int32_t** row_ptr,
+                                const int32_t** col_idx, int32_t* num_rows, int64_t* nnz) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (row_ptr) *row_ptr = lay->row_ptr.data();
+    if (col_idx) *col_idx = lay->col_idx.data();
+    if (num_rows) *num_rows = lay->H * lay->nb;
+    if (nnz) *nnz = (int64_t)lay->col_idx.size();
+    return ok();
+}
+
+bsattn_status bsattn_layout_upload(bsattn_layout* lay, hipStream_t stream) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    free_device(lay);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    const size_t nrp = lay->row_ptr.size() * sizeof(int32_t);
+    const size_t ncol = std::max<size_t>(1, lay->col_idx.size()) * sizeof(int32_t);
+    const size_t nit = std::max<size_t>(1, lay->items.size()) * sizeof(WorkItem);
+    const size_t nmg = std::max<size_t>(1, lay->merges.size()) * sizeof(MergeItem);
+    void* p[4] = {nullptr, nullptr, nullptr, nullptr};
+    const size_t sz[4] = {nrp, ncol, nit, nmg};
+    for (int a = 0; a < 4; ++a) {
+        e = hipMalloc(&p[a], sz[a]);
+        if (e != hipSuccess) {
+            for (int c = 0; c < a; ++c) (void)hipFree(p[c]);
+            return fail(BSATTN_ERR_NO_MEMORY, "hipMalloc of %zu bytes failed: %s", sz[a], hipGetErrorString(e));
+        }
+    }
+    lay->device = dev;
+    lay->d_row_ptr = (int32_t*)p[0];
+    lay->d_col_idx = (int32_t*)p[1];
+    lay->d_items = (WorkItem*)p[2];
+    lay->d_merges = (MergeItem*)p[3];
+    const void* src[4] = {lay->row_ptr.data(), lay->col_idx.data(), lay->items.data(), lay->merges.data()};
+    const size_t cp[4] = {nrp, lay->col_idx.size() * sizeof(int32_t), lay->items.size() * sizeof(WorkItem),
+                          lay->merges.size() * sizeof(MergeItem)};
+    for (int a = 0; a < 4; ++a) {
+        if (cp[a] == 0) continue;
+        e = hipMemcpyAsync(p[a], src[a], cp[a], hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) {
+            free_device(lay);
+            return hip_fail(e, "hipMemcpyAsync (layout upload)");
+        }
+    }
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        free_device(lay);
+        return hip_fail(e, "hipStreamSynchronize (layout upload)");
+    }
+    return ok();
+}
+
+bsattn_status bsattn_layout_build_device(const bsattn_layout* lay, int32_t* row_ptr_dev,
+                                         int32_t* col_idx_dev, hipStream_t stream) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (!row_ptr_dev || (!col_idx_dev && !lay->col_idx.empty()))
+        return fail(BSATTN_ERR_INVALID_ARG, "NULL device array");
+    hipError_t e = launch_layout_build(lay->rule, lay->kind, lay->H, lay->nb, lay->band_tokens,
+                                       row_ptr_dev, col_idx_dev, stream);
+    if (e != hipSuccess) return hip_fail(e, "layout build launch");
+    return ok();
+}
+
+void bsattn_layout_destroy(bsattn_layout* lay) {
+    if (!lay) return;
+    free_device(lay);
+    delete lay;
+}
+
+bsattn_status bsattn_workspace_size(const bsattn_layout* lay, int32_t batch, int32_t head_dim,
+                                    int32_t num_routed, size_t* bytes) {
+    if (!lay || !bytes) return fail(BSATTN_ERR_INVALID_ARG, "NULL argument");
+    if (batch < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch must be >= 1");
+    if (head_dim != 64 && head_dim != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (num_routed < 0 || num_routed > lay->L)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_routed must be in [0, seq_len]");
+    size_t slots = (size_t)batch * lay->n_slots;
+    if (num_routed > 0) {
+        int32_t n_rt, rch, per;
+        routed_split(lay->nb, num_routed, &n_rt, &rch, &per);
+        slots += (size_t)batch * lay->H * n_rt * rch;
+    }
+    *bytes = slots * slot_bytes(head_dim);
+    return ok();
+}
+
+bsattn_status bsattn_set_profile_events(hipEvent_t before, hipEvent_t after) {
+    if ((before == nullptr) != (after == nullptr))
+        return fail(BSATTN_ERR_INVALID_ARG, "set both events or neither");
+    g_ev_before = before;
+    g_ev_after = after;
+    return ok();
+}
+
+bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32_t B, int32_t H,
+                             int32_t L, int32_t D, const void* q, const void* k, const void* v,
+                             void* out, float* lse, const int32_t* key_valid_len, float scale,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    bsattn_status st = check_forward_common(lay, B, H, L, D, q, k, v, out, lse, scale);
+    if (st != BSATTN_OK) return st;
+    if (lay->kind != 0) return fail(BSATTN_ERR_INVALID_ARG, "band layouts are used with bsattn_forward_routed");
+    if (dtype != BSATTN_BF16 && dtype != BSATTN_F32) return fail(BSATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    size_t need = 0;
+    st = bsattn_workspace_size(lay, B, D, 0, &need);
+    if (st != BSATTN_OK) return st;
+    if (dtype == BSATTN_BF16 && need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    }
+    if ((int64_t)lay->items.size() * B >= ((int64_t)1 << 31))
+        return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    const size_t total_slots = (size_t)B * lay->n_slots;
+    a.ws_o = (float*)workspace;
+    a.ws_lse = workspace ? (float*)workspace + total_slots * kBlock * D : nullptr;
+    a.items = lay->d_items;
+    a.merges = lay->d_merges;
+    a.col_idx = lay->d_col_idx;
+    a.valid_len = key_valid_len;
+    a.routed_rows = nullptr;
+    a.n_items = (int32_t)lay->items.size();
+    a.n_merges = (int32_t)lay->merges.size();
+    a.B = B; a.H = H; a.L = L; a.nb = lay->nb; a.n_slots = lay->n_slots;
+    a.n_routed = 0; a.n_rt = 0; a.r_chunks = 1; a.r_chunk_tiles = 1; a.r_slot_base = 0;
+    a.band = -1;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const int mask = key_valid_len ? MASK_PAD : MASK_NONE;
+
+    hipError_t e;
+    if (dtype == BSATTN_F32) {
+        e = launch_fwd_f32(a, lay->d_row_ptr, D, mask, stream, g_ev_before, g_ev_after);
+        if (e != hipSuccess) return hip_fail(e, "fp32 forward launch");
+        return ok();
+    }
+    e = launch_fwd_bf16(a, D, mask, stream, g_ev_before, g_ev_after);
+    if (e != hipSuccess) return hip_fail(e, "bf16 forward launch");
+    if (a.n_merges > 0) {
+        e = launch_merge_bf16(a, D, stream);
+        if (e != hipSuccess) return hip_fail(e, "merge launch");
+    }
+    return ok();
+}
+
+bsattn_status bsattn_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,
+                                int32_t D, int32_t k, int32_t* routed_rows, hipStream_t stream) {
+    if (!q || !w || !routed_rows) return fail(BSATTN_ERR_INVALID_ARG, "NULL pointer");
+    if (B < 1 || H < 1 || L < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch, heads and seq_len must be >= 1");
+    if (D != 64 && D != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+    if (L > 8192) return fail(BSATTN_ERR_UNSUPPORTED, "seq_len > 8192 in the router");
+    if (k < 1 || k > L) return fail(BSATTN_ERR_INVALID_ARG, "k must be in [1, seq_len] (got %d)", k);
+    if (!aligned16(q)) return fail(BSATTN_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if ((int64_t)B * H > 0x7fffffff) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+    hipError_t e = launch_route_topk(q, w, B, H, L, D, k, routed_rows, stream);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    return ok();
+}
+
+bsattn_status bsattn_forward_routed(const bsattn_layout* lay, bsattn_dtype dtype, int32_t B,
+                                    int32_t H, int32_t L, int32_t D, const void* q, const void* k,
+                                    const void* v, const int32_t* routed_rows, int32_t num_routed,
+                                    void* out, float* lse, float scale, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    bsattn_status st = check_forward_common(lay, B, H, L, D, q, k, v, out, lse, scale);
+    if (st != BSATTN_OK) return st;
+    if (lay->kind != 1) return fail(BSATTN_ERR_INVALID_ARG, "bsattn_forward_routed needs a band layout");
+    if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "the routed variant is bf16 only");
+    if (num_routed < 1 || num_routed > L)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_routed must be in [1, seq_len] (got %d)", num_routed);
+    if (!routed_rows) return fail(BSATTN_ERR_INVALID_ARG, "routed_rows is NULL");
+    size_t need = 0;
+    st = bsattn_workspace_size(lay, B, D, num_routed, &need);
+    if (st != BSATTN_OK) return st;
+    if (!workspace || workspace_bytes < need)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    int32_t n_rt, rch, per;
+    routed_split(lay->nb, num_routed, &n_rt, &rch, &per);
+    const int64_t grid = (int64_t)lay->items.size() * B + (int64_t)B * H * n_rt * rch;
+    if (grid >= ((int64_t)1 << 31)) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    const size_t total_slots = (size_t)B * lay->n_slots + (size_t)B * H * n_rt * rch;
+    a.ws_o = (float*)workspace;
+    a.ws_lse = (float*)workspace + total_slots * kBlock * D;
+    a.items = lay->d_items;
+    a.merges = lay->d_merges;
+    a.col_idx = lay->d_col_idx;
+    a.valid_len = nullptr;
+    a.routed_rows = routed_rows;
+    a.n_items = (int32_t)lay->items.size();
+    a.n_merges = (int32_t)lay->merges.size();
+    a.B = B; a.H = H; a.L = L; a.nb = lay->nb; a.n_slots = lay->n_slots;
+    a.n_routed = num_routed; a.n_rt = n_rt; a.r_chunks = rch; a.r_chunk_tiles = per;
+    a.r_slot_base = B * lay->n_slots;
+    a.band = lay->band_tokens;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+
+    hipError_t e = launch_fwd_bf16(a, D, MASK_BAND, stream, g_ev_before, g_ev_after);
+    if (e != hipSuccess) return hip_fail(e, "routed forward launch");
+    e = launch_merge_bf16(a, D, stream);
+    if (e != hipSuccess) return hip_fail(e, "routed merge launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// internal.h -- layout object, work schedule and kernel argument blocks of libbsattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "bsattn.h"
+#include "layout_rule.h"
+
+namespace bsattn {
+
+constexpr int kBlock = 64;        // tokens per block and rows per query tile
+constexpr int kChunkTiles = 16;   // a row longer than this is split across workgroups
+constexpr int kMaxChunks = 32;    // upper bound on the split of one row
+
+enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2 };
+
+// One workgroup's share: query block `row` (= h*nb + i) over key blocks
+// col_idx[col_begin, col_end).  slot < 0: the whole row, written straight to
+// O/LSE; slot >= 0: one chunk of a split row, written as a partial (O
+// normalised over the chunk, chunk LSE) to workspace slot b*n_slots + slot.
+struct WorkItem {
+    int32_t row, col_begin, col_end, slot;
+};
+
+// A split row: its chunks occupy slots [first_slot, first_slot + n_chunks).
+struct MergeItem {
+    int32_t row, first_slot, n_chunks, pad;
+};
+
+// Chunking of a row of `len` tiles: number of chunks and tiles per chunk.
+inline void split_row(int32_t len, int32_t* n_chunks, int32_t* per_chunk) {
+    int32_t per = kChunkTiles;
+    if ((len + per - 1) / per > kMaxChunks) per = (len + kMaxChunks - 1) / kMaxChunks;
+    const int32_t n = (len + per - 1) / per;
+    *n_chunks = n;
+    *per_chunk = (len + n - 1) / n;
+}
+
+// Everything a forward launch needs, passed by value to the kernels.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    float* ws_o;              // [total_slots][64][D] fp32
+    float* ws_lse;            // [total_slots][64]
+    const WorkItem* items;    // explicit items (CSR rows or chunks)
+    const MergeItem* merges;
+    const int32_t* col_idx;
+    const int32_t* valid_len; // [B] or null
+    const int32_t* routed_rows;
+    int32_t n_items, n_merges;
+    int32_t B, H, L, nb, n_slots;
+    // routed tiles (gathered query rows over all key blocks), placed first in the grid
+    int32_t n_routed;         // k rows per (b, h); 0 = no routed tiles
+    int32_t n_rt;             // ceil(k / 64) routed tiles per (b, h)
+    int32_t r_chunks;         // chunks per routed tile
+    int32_t r_chunk_tiles;    // key blocks per chunk
+    int32_t r_slot_base;      // first workspace slot of routed partials
+    int32_t band;             // token band of non-routed rows (MASK_BAND)
+    float scale;              // score scale
+    float scale_log2;         // scale * log2(e)
+};
+
+// ---- launchers (defined in kernels/*.hip) ----
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s,
+                           hipEvent_t before, hipEvent_t after);
+hipError_t launch_merge_bf16(const FwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, const int32_t* row_ptr, int head_dim, int mask,
+                          hipStream_t s, hipEvent_t before, hipEvent_t after);
+hipError_t launch_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,
+                             int32_t D, int32_t k, int32_t* out, hipStream_t s);
+hipError_t launch_layout_build(const RowRule& rule, int kind, int32_t H, int32_t nb,
+                               int32_t band, int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+
+}  // namespace bsattn
+
+// The opaque layout handle of the C ABI.
+struct bsattn_layout {
+    int32_t H = 0, L = 0, nb = 0, block = 0;
+    int32_t kind = 0;           // 0: window/global/random rule, 1: token band
+    int32_t band_tokens = -1;
+    bsattn::RowRule rule{};
+    std::vector<int32_t> row_ptr, col_idx;
+    std::vector<bsattn::WorkItem> items;
+    std::vector<bsattn::MergeItem> merges;
+    int32_t n_slots = 0;        // partial slots per batch entry
+    // device copy (after upload)
+    int device = -1;
+    int32_t* d_row_ptr = nullptr;
+    int32_t* d_col_idx = nullptr;
+    bsattn::WorkItem* d_items = nullptr;
+    bsattn::MergeItem* d_merges = nullptr;
+};

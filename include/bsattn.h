@@ -1,0 +1,196 @@
+/*
+ * bsattn.h -- block-sparse self-attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbsattn.so.  Plain pointers and sizes only; no C++ or framework
+ * types cross this boundary, and no C++ exception escapes it.
+ *
+ * The operation (Adaptive Sparse Transformer page, "Adapt or Perish: 新手入门指南 –
+ * Adaptive Sparse Transformer 核心原理与实战", the SparseAttention formula):
+ *   O = softmax(scale * Q K^T under a 0/1 mask M) V,
+ * with masked scores treated as -inf (the primer page's and the multi-head
+ * page's code fill masked scores with a large negative value) and one softmax
+ * over the union of all patterns.  M is given at 64x64 block granularity by a
+ * BigBird-style layout (BigBird page, "BigBird 稀疏注意力机制解析：如何突破
+ * Transformer 的序列长度限制", section 核心实现: global, sliding-window and random
+ * patterns) stored in block-CSR form (SQA page, "Transformer计算效率优化：SQA稀疏
+ * 注意力机制详解", section 3.1: block-sparse mask, attention only on non-zero
+ * blocks; section 5: 64x64 blocks), optionally refined per token by a key
+ * padding length or, in the routed-query variant (SQA page, section 2.1), by
+ * a token band.
+ *
+ * Tensor layout everywhere: [B, H, L, D] row-major, D innermost, contiguous.
+ * LSE is [B, H, L] fp32: the natural-log log-sum-exp of the scaled, masked
+ * scores of each query row (the normaliser of the softmax, kept for a
+ * backward pass).
+ *
+ * Errors: every function returns a bsattn_status.  Arguments are validated
+ * before anything is enqueued; on failure nothing is launched and
+ * bsattn_last_error() returns a thread-local description.  Launch failures
+ * are reported as BSATTN_ERR_HIP.  NaN inputs propagate to the outputs.  A
+ * query row with no allowed key gets O = 0 and LSE = -inf.
+ *
+ * Asynchrony: functions taking a hipStream_t enqueue work on that stream and
+ * return without synchronising; they are reentrant.  Calls that share a
+ * workspace must be ordered (same stream, or synchronised).
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSATTN_OK = 0,
+    BSATTN_ERR_INVALID_ARG = 1,   /* bad pointer, size, shape or layout mismatch */
+    BSATTN_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (e.g. D=96) */
+    BSATTN_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed */
+    BSATTN_ERR_NO_MEMORY = 4,     /* host or device allocation failed */
+    BSATTN_ERR_STATE = 5          /* layout not uploaded to the current device */
+} bsattn_status;
+
+typedef enum {
+    BSATTN_F32 = 0,               /* fp32 Q/K/V/O, fp32 arithmetic */
+    BSATTN_BF16 = 1               /* bf16 Q/K/V/O, bf16 MFMA with fp32 accumulation */
+} bsattn_dtype;
+
+/* Opaque, immutable once built.  Owns its host CSR arrays and, after
+ * bsattn_layout_upload, a device copy plus the scheduled work list. */
+typedef struct bsattn_layout bsattn_layout;
+
+/* Build a BigBird-style block layout on the host (no HIP call).
+ * BigBird page, section 核心实现 (global / sliding window / random patterns);
+ * SQA page, section 3.1 (block-sparse storage).
+ *   num_heads      H >= 1; the layout is per head and shared by the batch.
+ *   seq_len        L, a positive multiple of block.
+ *   block          must be 64 (the tile of the kernels).
+ *   window_blocks  odd >= 1: query block i sees key blocks j with
+ *                  |i-j| <= (window_blocks-1)/2, clipped to [0, L/block).
+ *   global_blocks  host array of num_global distinct block indices in range
+ *                  (may be NULL when num_global == 0).  A global block's row
+ *                  is every block, and every row contains every global block.
+ *   random_blocks  r >= 0 extra blocks per non-global row, drawn without
+ *                  replacement from the blocks not already in the row by a
+ *                  splitmix64-driven partial Fisher-Yates shuffle: row stream
+ *                  state s = sm(sm(sm(seed)^h)^i), sm(x) = first splitmix64
+ *                  output from state x; draw j swaps candidate j with
+ *                  candidate j + (u_j mod (n-j)), u_j the (j+1)-th output from
+ *                  state s, candidates in ascending order.  If r exceeds the
+ *                  candidates, all are taken.
+ *   seed           hash seed.
+ *   out            receives the new layout (caller frees with bsattn_layout_destroy).
+ * Rows are ascending and duplicate-free.  Limits: window_blocks <= 63,
+ * num_global <= 64, random_blocks <= 64, H * (L/block) <= 2^20. */
+bsattn_status bsattn_make_layout(int32_t num_heads, int32_t seq_len, int32_t block,
+                                 int32_t window_blocks, const int32_t* global_blocks,
+                                 int32_t num_global, int32_t random_blocks, uint64_t seed,
+                                 bsattn_layout** out);
+
+/* Build the block layout of a token band (routed-query variant, SQA page,
+ * section 2.1: non-routed queries see only a local window of keys), read as
+ * |t - s| <= band_tokens.  Row i lists every key block the band of query
+ * block i touches (i-1, i, i+1 for band_tokens <= 64), and the kernels mask
+ * the band per token.  band_tokens in [0, seq_len).  Host only. */
+bsattn_status bsattn_make_band_layout(int32_t num_heads, int32_t seq_len, int32_t block,
+                                      int32_t band_tokens, bsattn_layout** out);
+
+/* Borrowed host view of the block-CSR arrays (valid until destroy).
+ *   row_ptr [num_rows + 1], col_idx [nnz], num_rows = H * L / block, rows
+ *   ordered head-major (row h*nb + i).  Any output pointer may be NULL. */
+bsattn_status bsattn_layout_csr(const bsattn_layout* layout, const int32_t** row_ptr,
+                                const int32_t** col_idx, int32_t* num_rows, int64_t* nnz);
+
+/* Copy the CSR and the work schedule to the current HIP device (hipMalloc +
+ * copies enqueued on `stream`, then synchronised).  Must precede the forward
+ * calls that use the layout; calling it again re-uploads to the then-current
+ * device.  The device copy is freed by bsattn_layout_destroy. */
+bsattn_status bsattn_layout_upload(bsattn_layout* layout, hipStream_t stream);
+
+/* Rebuild the same layout on the device from its parameters (one thread per
+ * row runs the identical integer rule) into caller-owned device arrays
+ * row_ptr_dev [num_rows + 1] and col_idx_dev [nnz].  Exists to prove that
+ * the host and device evaluations of the rule agree bit for bit. */
+bsattn_status bsattn_layout_build_device(const bsattn_layout* layout, int32_t* row_ptr_dev,
+                                         int32_t* col_idx_dev, hipStream_t stream);
+
+/* Free a layout and its device copy.  NULL is a no-op. */
+void bsattn_layout_destroy(bsattn_layout* layout);
+
+/* Device workspace bytes needed by bsattn_forward (num_routed == 0) or
+ * bsattn_forward_routed (num_routed = k) for this layout, batch and head
+ * width: fp32 partial outputs of rows that are split across workgroups,
+ * merged by log-sum-exp.  Written to *bytes (0 when nothing is split). */
+bsattn_status bsattn_workspace_size(const bsattn_layout* layout, int32_t batch,
+                                    int32_t head_dim, int32_t num_routed, size_t* bytes);
+
+/* Block-sparse attention forward.
+ *   layout         uploaded layout with num_heads == H and seq_len == L.
+ *   dtype          element type of q, k, v and out.
+ *   batch..head_dim  B >= 1, H, L as in the layout, D in {64, 128}.
+ *   q, k, v        device [B, H, L, D], contiguous, 16-byte aligned.
+ *   out            device [B, H, L, D] of dtype; must not alias q, k or v.
+ *   lse            device [B, H, L] fp32 (natural log).
+ *   key_valid_len  device int32 [B] or NULL: keys s >= key_valid_len[b] are
+ *                  masked (the primer page's key mask); each value in [0, L].
+ *                  Query rows past the valid length are computed normally.
+ *   scale          score scale (1/sqrt(D) for the usual attention).
+ *   workspace      device buffer of at least bsattn_workspace_size() bytes,
+ *                  256-byte aligned (may be NULL if that size is 0).
+ * Enqueued on `stream`; no synchronisation. */
+bsattn_status bsattn_forward(const bsattn_layout* layout, bsattn_dtype dtype,
+                             int32_t batch, int32_t num_heads, int32_t seq_len, int32_t head_dim,
+                             const void* q, const void* k, const void* v,
+                             void* out, float* lse, const int32_t* key_valid_len, float scale,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Routed-query selection (SQA page, section 2.1: a learned linear router
+ * scores each query and keeps the top-k; section 3.2: the router runs in
+ * higher precision than the model).  For each (b, h):
+ *   score[t] = sum_{d=0}^{D-1} (double)q[b,h,t,d] * (double)w[d], summed left
+ *   to right in fp64 (every product is exact, so the score is reproducible
+ *   bit for bit), then the k rows with the largest score, ties to the lower
+ *   row index, written ascending to routed_rows.
+ *   q             device bf16 [B, H, L, D], D in {64, 128}.
+ *   w             device fp32 [D].
+ *   k             1 <= k <= L; L <= 8192.
+ *   routed_rows   device int32 [B, H, k].
+ * NaN scores give an unspecified (but valid, distinct) selection. */
+bsattn_status bsattn_route_topk(const void* q, const float* w, int32_t batch, int32_t num_heads,
+                                int32_t seq_len, int32_t head_dim, int32_t k,
+                                int32_t* routed_rows, hipStream_t stream);
+
+/* Routed-query attention forward (SQA page, section 2.1): rows listed in
+ * routed_rows [B, H, num_routed] (device int32, distinct, in [0, L)) attend to
+ * every key; all other rows attend to keys with |t - s| <= band, where
+ * `band_layout` comes from bsattn_make_band_layout (and is uploaded).
+ * dtype must be BSATTN_BF16.  Other arguments as bsattn_forward; the
+ * workspace is sized with num_routed. */
+bsattn_status bsattn_forward_routed(const bsattn_layout* band_layout, bsattn_dtype dtype,
+                                    int32_t batch, int32_t num_heads, int32_t seq_len,
+                                    int32_t head_dim, const void* q, const void* k,
+                                    const void* v, const int32_t* routed_rows,
+                                    int32_t num_routed, void* out, float* lse, float scale,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Measurement hook: while set (non-NULL), every forward call made from this
+ * thread records `before` on its stream immediately before the main attention
+ * kernel and `after` immediately after it, so a caller can time that kernel
+ * alone with hipEventElapsedTime.  Pass NULLs to clear.  Events are caller
+ * owned. */
+bsattn_status bsattn_set_profile_events(hipEvent_t before, hipEvent_t after);
+
+/* Static description of a status code; never NULL. */
+const char* bsattn_status_string(bsattn_status status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* bsattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

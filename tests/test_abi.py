@@ -1,0 +1,115 @@
+"""The C ABI loads, exports every declared symbol, and rejects bad arguments
+before touching the GPU (CPU only: no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_transformer_amd as bs
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "bsattn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsattn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert names == sorted([
+        "bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr", "bsattn_layout_upload",
+        "bsattn_layout_build_device", "bsattn_layout_destroy", "bsattn_workspace_size", "bsattn_forward",
+        "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
+        "bsattn_last_error"])
+    lib = bs.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_last_error():
+    for code in range(6):
+        assert bs.bsattn_status_string(code)
+    assert bs.bsattn_status_string(99) == "unknown status"
+    assert isinstance(bs.bsattn_last_error(), str)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block=32), 2),
+    (dict(seq_len=100), 1),
+    (dict(window_blocks=2), 1),
+    (dict(window_blocks=65), 2),
+    (dict(global_blocks=[0, 0]), 1),
+    (dict(global_blocks=[16]), 1),
+    (dict(random_blocks=-1), 1),
+    (dict(random_blocks=65), 1),
+    (dict(num_heads=0), 1),
+])
+def test_make_layout_rejects(kw, code):
+    args = dict(num_heads=2, seq_len=1024, block=64, window_blocks=3, global_blocks=[0], random_blocks=1, seed=0)
+    args.update(kw)
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_make_layout(**args)
+    assert e.value.status == code
+    assert bs.bsattn_last_error()
+
+
+def test_band_layout_rejects():
+    with pytest.raises(bs.BsattnError):
+        bs.bsattn_make_band_layout(2, 1024, 64, 1024)
+    with pytest.raises(bs.BsattnError):
+        bs.bsattn_make_band_layout(2, 1024, 64, -1)
+
+
+def test_workspace_size_and_destroy():
+    lay = bs.bsattn_make_layout(12, 8192, 64, 3, [0, 127], 3, 2)
+    n = bs.bsattn_workspace_size(lay, 2, 64)
+    # 2 dense rows per head, 128 blocks each -> 8 chunks of 16; slots of 64 x (64+1) floats
+    assert n == 2 * 12 * 2 * 8 * 64 * 65 * 4
+    assert bs.bsattn_workspace_size(lay, 2, 64, num_routed=64) > n
+    with pytest.raises(bs.BsattnError):
+        bs.bsattn_workspace_size(lay, 2, 96)
+    lay.destroy()
+    lay.destroy()                         # idempotent
+    bs.lib().bsattn_layout_destroy(None)  # NULL-safe
+
+
+def test_forward_rejects_before_any_hip_call():
+    L = bs.lib()
+    lay = bs.bsattn_make_layout(2, 1024, 64, 3, [0], 1, 0)
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    ws = ctypes.c_size_t(0)
+    # NULL layout
+    st = L.bsattn_forward(None, 1, 1, 2, 1024, 64, fake, fake, fake, ctypes.c_void_p(0x2000), fake, None,
+                          0.125, None, ws, None)
+    assert st == 1
+    # H mismatch
+    st = L.bsattn_forward(lay.handle, 1, 1, 3, 1024, 64, fake, fake, fake, ctypes.c_void_p(0x2000), fake, None,
+                          0.125, None, ws, None)
+    assert st == 1 and "match" in bs.bsattn_last_error()
+    # unsupported head_dim
+    st = L.bsattn_forward(lay.handle, 1, 1, 2, 1024, 96, fake, fake, fake, ctypes.c_void_p(0x2000), fake, None,
+                          0.125, None, ws, None)
+    assert st == 2
+    # misaligned pointer
+    st = L.bsattn_forward(lay.handle, 1, 1, 2, 1024, 64, ctypes.c_void_p(0x1002), fake, fake,
+                          ctypes.c_void_p(0x2000), fake, None, 0.125, None, ws, None)
+    assert st == 1 and "aligned" in bs.bsattn_last_error()
+    # out aliasing q
+    st = L.bsattn_forward(lay.handle, 1, 1, 2, 1024, 64, fake, fake, fake, fake, fake, None, 0.125, None, ws, None)
+    assert st == 1
+    # bad scale
+    st = L.bsattn_forward(lay.handle, 1, 1, 2, 1024, 64, fake, fake, fake, ctypes.c_void_p(0x2000), fake, None,
+                          -1.0, None, ws, None)
+    assert st == 1
+    # router argument checks
+    st = L.bsattn_route_topk(fake, fake, 1, 2, 1024, 64, 0, fake, None)
+    assert st == 1
+    st = L.bsattn_route_topk(fake, fake, 1, 2, 16384, 64, 4, fake, None)
+    assert st == 2
+    # profile events must be set in pairs
+    assert L.bsattn_set_profile_events(fake, None) == 1
+    assert L.bsattn_set_profile_events(None, None) == 0

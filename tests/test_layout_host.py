@@ -1,0 +1,65 @@
+"""The library's host layout builder equals the oracle's layout bit for bit
+(integer work: exact equality), on every workload and on random parameter
+tuples.  Host code only -- no GPU call."""
+import numpy as np
+import pytest
+
+import block_sparse_transformer_amd as bs
+from oracle import layout as OL
+from workloads import WORKLOADS
+
+
+def _both(H, L, w, G, r, seed):
+    lay = bs.bsattn_make_layout(H, L, 64, w, list(G), r, seed)
+    got = bs.bsattn_layout_csr(lay)
+    want = OL.make_layout(H, L, 64, w, list(G), r, seed).csr()
+    return got, want
+
+
+@pytest.mark.parametrize("name", [n for n, wl in WORKLOADS.items() if not wl.routed])
+def test_workload_layouts_bit_exact(name):
+    wl = WORKLOADS[name]
+    (rp, ci), (orp, oci) = _both(wl.heads, wl.seq_len, wl.window_blocks, wl.global_blocks,
+                                 wl.random_blocks, wl.layout_seed)
+    assert rp.dtype == np.int32 and ci.dtype == np.int32
+    assert np.array_equal(rp, orp)
+    assert np.array_equal(ci, oci)
+
+
+def test_band_layout_bit_exact():
+    wl = WORKLOADS["routed-L4096"]
+    lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+    rp, ci = bs.bsattn_layout_csr(lay)
+    orp, oci = OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens).csr()
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+    for band in (0, 1, 63, 64, 65, 200):
+        lay = bs.bsattn_make_band_layout(2, 16 * 64, 64, band)
+        rp, ci = bs.bsattn_layout_csr(lay)
+        orp, oci = OL.make_band_layout(2, 16 * 64, 64, band).csr()
+        assert np.array_equal(rp, orp) and np.array_equal(ci, oci), band
+
+
+def test_random_parameter_tuples_bit_exact():
+    g = np.random.default_rng(1234)
+    for _ in range(300):
+        nb = int(g.integers(1, 40))
+        H = int(g.integers(1, 4))
+        w = int(g.integers(0, 8)) * 2 + 1
+        ng = int(g.integers(0, min(nb, 5) + 1))
+        G = sorted(g.choice(nb, size=ng, replace=False).tolist())
+        r = int(g.integers(0, 12))
+        seed = int(g.integers(0, 2 ** 63)) * (1 if g.random() < 0.5 else 2) % (2 ** 64)
+        (rp, ci), (orp, oci) = _both(H, nb * 64, w, G, r, seed)
+        assert np.array_equal(rp, orp), (nb, H, w, G, r, seed)
+        assert np.array_equal(ci, oci), (nb, H, w, G, r, seed)
+
+
+def test_global_order_does_not_matter():
+    a = bs.bsattn_layout_csr(bs.bsattn_make_layout(2, 2048, 64, 3, [31, 0, 7], 2, 5))
+    b = bs.bsattn_layout_csr(bs.bsattn_make_layout(2, 2048, 64, 3, [0, 7, 31], 2, 5))
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_large_seed_and_head_values():
+    (rp, ci), (orp, oci) = _both(3, 64 * 64, 5, [0, 63], 7, (1 << 64) - 1)
+    assert np.array_equal(ci, oci)
