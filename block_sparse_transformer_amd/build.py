@@ -34,6 +34,7 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-I", INCLUDE, "-I", CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",   # MFMA accumulators in VGPRs: no AGPR copies around the softmax
     "-Wno-unused-command-line-argument",
 ]
 

@@ -40,33 +40,49 @@ bsattn_status hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Work schedule: rows of <= kChunkTiles blocks become one item; longer rows are
-// split into balanced chunks whose partials are merged afterwards.  Items are
-// ordered longest first so the long chunks start before the short rows.
+// split into balanced chunks whose partials are merged by the last chunk to
+// finish.  Each head's items are ordered longest first (so long chunks start
+// before short rows) and padded with no-op items to a common length; the
+// kernel deals whole (batch, head) groups to one XCD so their K/V stay in
+// that XCD's L2.
 void build_schedule(bsattn_layout* lay) {
     lay->items.clear();
     lay->merges.clear();
     int32_t slot = 0;
-    const int32_t rows = lay->H * lay->nb;
-    for (int32_t r = 0; r < rows; ++r) {
-        const int32_t b0 = lay->row_ptr[r], b1 = lay->row_ptr[r + 1];
-        const int32_t len = b1 - b0;
-        if (len <= kChunkTiles) {
-            lay->items.push_back({r, b0, b1, -1});
-            continue;
+    std::vector<std::vector<WorkItem>> per_head((size_t)lay->H);
+    for (int32_t h = 0; h < lay->H; ++h) {
+        auto& hi = per_head[(size_t)h];
+        for (int32_t i = 0; i < lay->nb; ++i) {
+            const int32_t r = h * lay->nb + i;
+            const int32_t b0 = lay->row_ptr[r], b1 = lay->row_ptr[r + 1];
+            const int32_t len = b1 - b0;
+            if (len <= kChunkTiles) {
+                hi.push_back({r, b0, b1, -1, -1, 0, 0, 0});
+                continue;
+            }
+            int32_t nch, per;
+            split_row(len, &nch, &per);
+            const int32_t m = (int32_t)lay->merges.size();
+            lay->merges.push_back({r, slot, nch, 0});
+            const int32_t first = slot;
+            for (int32_t c = 0; c < nch; ++c) {
+                const int32_t s0 = b0 + c * per;
+                const int32_t e0 = std::min(b1, s0 + per);
+                hi.push_back({r, s0, e0, slot++, m, first, nch, 0});
+            }
         }
-        int32_t nch, per;
-        split_row(len, &nch, &per);
-        lay->merges.push_back({r, slot, nch, 0});
-        for (int32_t c = 0; c < nch; ++c) {
-            const int32_t s = b0 + c * per;
-            const int32_t e = std::min(b1, s + per);
-            lay->items.push_back({r, s, e, slot++});
-        }
+        std::stable_sort(hi.begin(), hi.end(), [](const WorkItem& x, const WorkItem& y) {
+            return (x.col_end - x.col_begin) > (y.col_end - y.col_begin);
+        });
     }
+    size_t per = 0;
+    for (auto& hi : per_head) per = std::max(per, hi.size());
+    for (auto& hi : per_head) {
+        lay->items.insert(lay->items.end(), hi.begin(), hi.end());
+        for (size_t a = hi.size(); a < per; ++a) lay->items.push_back({-1, 0, 0, -1, -1, 0, 0, 0});
+    }
+    lay->items_per_head = (int32_t)per;
     lay->n_slots = slot;
-    std::stable_sort(lay->items.begin(), lay->items.end(), [](const WorkItem& x, const WorkItem& y) {
-        return (x.col_end - x.col_begin) > (y.col_end - y.col_begin);
-    });
 }
 
 void free_device(bsattn_layout* lay) {
@@ -128,6 +144,12 @@ bsattn_status check_forward_common(const bsattn_layout* lay, int32_t B, int32_t 
 }
 
 size_t slot_bytes(int32_t D) { return (size_t)kBlock * (size_t)(D + 1) * sizeof(float); }
+
+// Counter area at the start of the workspace, rounded up to 256 bytes.
+size_t counter_ints(const bsattn_layout* lay, int32_t B, int32_t n_rt) {
+    const size_t n = (size_t)B * lay->merges.size() + (size_t)B * lay->H * n_rt;
+    return (n + 63) / 64 * 64;
+}
 
 void routed_split(int32_t nb, int32_t k, int32_t* n_rt, int32_t* r_chunks, int32_t* per) {
     *n_rt = (k + kBlock - 1) / kBlock;
@@ -328,12 +350,32 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* lay, int32_t batch, int
     if (num_routed < 0 || num_routed > lay->L)
         return fail(BSATTN_ERR_INVALID_ARG, "num_routed must be in [0, seq_len]");
     size_t slots = (size_t)batch * lay->n_slots;
+    int32_t n_rt = 0;
     if (num_routed > 0) {
-        int32_t n_rt, rch, per;
+        int32_t rch, per;
         routed_split(lay->nb, num_routed, &n_rt, &rch, &per);
         slots += (size_t)batch * lay->H * n_rt * rch;
     }
-    *bytes = slots * slot_bytes(head_dim);
+    *bytes = slots == 0 ? 0 : counter_ints(lay, batch, n_rt) * sizeof(int32_t) + slots * slot_bytes(head_dim);
+    return ok();
+}
+
+bsattn_status bsattn_workspace_init(const bsattn_layout* lay, int32_t batch, int32_t head_dim,
+                                    int32_t num_routed, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    size_t need = 0;
+    bsattn_status st = bsattn_workspace_size(lay, batch, head_dim, num_routed, &need);
+    if (st != BSATTN_OK) return st;
+    if (need == 0) return ok();
+    if (!workspace || workspace_bytes < need)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    int32_t n_rt = 0;
+    if (num_routed > 0) {
+        int32_t rch, per;
+        routed_split(lay->nb, num_routed, &n_rt, &rch, &per);
+    }
+    hipError_t e = launch_zero_i32((int32_t*)workspace, (int64_t)counter_ints(lay, batch, n_rt), stream);
+    if (e != hipSuccess) return hip_fail(e, "workspace init launch");
     return ok();
 }
 
@@ -362,14 +404,16 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
             return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     }
-    if ((int64_t)lay->items.size() * B >= ((int64_t)1 << 31))
+    if ((int64_t)kXcds * (((int64_t)B * H + kXcds - 1) / kXcds) * lay->items_per_head >= ((int64_t)1 << 31))
         return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
 
     FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
     const size_t total_slots = (size_t)B * lay->n_slots;
-    a.ws_o = (float*)workspace;
-    a.ws_lse = workspace ? (float*)workspace + total_slots * kBlock * D : nullptr;
+    const size_t nci = total_slots ? counter_ints(lay, B, 0) : 0;
+    a.counters = (int32_t*)workspace;
+    a.ws_o = workspace ? (float*)workspace + nci : nullptr;
+    a.ws_lse = workspace ? a.ws_o + total_slots * kBlock * D : nullptr;
     a.items = lay->d_items;
     a.merges = lay->d_merges;
     a.col_idx = lay->d_col_idx;
@@ -377,6 +421,7 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     a.routed_rows = nullptr;
     a.n_items = (int32_t)lay->items.size();
     a.n_merges = (int32_t)lay->merges.size();
+    a.items_per_head = lay->items_per_head;
     a.B = B; a.H = H; a.L = L; a.nb = lay->nb; a.n_slots = lay->n_slots;
     a.n_routed = 0; a.n_rt = 0; a.r_chunks = 1; a.r_chunk_tiles = 1; a.r_slot_base = 0;
     a.band = -1;
@@ -392,10 +437,6 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     }
     e = launch_fwd_bf16(a, D, mask, stream, g_ev_before, g_ev_after);
     if (e != hipSuccess) return hip_fail(e, "bf16 forward launch");
-    if (a.n_merges > 0) {
-        e = launch_merge_bf16(a, D, stream);
-        if (e != hipSuccess) return hip_fail(e, "merge launch");
-    }
     return ok();
 }
 
@@ -435,14 +476,15 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* lay, bsattn_dtype dtype
 
     int32_t n_rt, rch, per;
     routed_split(lay->nb, num_routed, &n_rt, &rch, &per);
-    const int64_t grid = (int64_t)lay->items.size() * B + (int64_t)B * H * n_rt * rch;
+    const int64_t grid = (int64_t)kXcds * (((int64_t)B * H + kXcds - 1) / kXcds) * (lay->items_per_head + (int64_t)n_rt * rch);
     if (grid >= ((int64_t)1 << 31)) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
 
     FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
     const size_t total_slots = (size_t)B * lay->n_slots + (size_t)B * H * n_rt * rch;
-    a.ws_o = (float*)workspace;
-    a.ws_lse = (float*)workspace + total_slots * kBlock * D;
+    a.counters = (int32_t*)workspace;
+    a.ws_o = (float*)workspace + counter_ints(lay, B, n_rt);
+    a.ws_lse = a.ws_o + total_slots * kBlock * D;
     a.items = lay->d_items;
     a.merges = lay->d_merges;
     a.col_idx = lay->d_col_idx;
@@ -450,6 +492,7 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* lay, bsattn_dtype dtype
     a.routed_rows = routed_rows;
     a.n_items = (int32_t)lay->items.size();
     a.n_merges = (int32_t)lay->merges.size();
+    a.items_per_head = lay->items_per_head;
     a.B = B; a.H = H; a.L = L; a.nb = lay->nb; a.n_slots = lay->n_slots;
     a.n_routed = num_routed; a.n_rt = n_rt; a.r_chunks = rch; a.r_chunk_tiles = per;
     a.r_slot_base = B * lay->n_slots;
@@ -459,8 +502,6 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* lay, bsattn_dtype dtype
 
     hipError_t e = launch_fwd_bf16(a, D, MASK_BAND, stream, g_ev_before, g_ev_after);
     if (e != hipSuccess) return hip_fail(e, "routed forward launch");
-    e = launch_merge_bf16(a, D, stream);
-    if (e != hipSuccess) return hip_fail(e, "routed merge launch");
     return ok();
 }
 

@@ -21,8 +21,12 @@ enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2 };
 // col_idx[col_begin, col_end).  slot < 0: the whole row, written straight to
 // O/LSE; slot >= 0: one chunk of a split row, written as a partial (O
 // normalised over the chunk, chunk LSE) to workspace slot b*n_slots + slot.
+// The chunks of split row `merge` occupy slots [first_slot, first_slot +
+// n_chunks); the last chunk to finish merges them.  row < 0: no work
+// (padding of a head's item list).
 struct WorkItem {
     int32_t row, col_begin, col_end, slot;
+    int32_t merge, first_slot, n_chunks, pad;
 };
 
 // A split row: its chunks occupy slots [first_slot, first_slot + n_chunks).
@@ -30,10 +34,14 @@ struct MergeItem {
     int32_t row, first_slot, n_chunks, pad;
 };
 
-// Chunking of a row of `len` tiles: number of chunks and tiles per chunk.
+constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+
+// Chunking of a row of `len` tiles: number of chunks and tiles per chunk
+// (at most 64 tiles per chunk: a chunk's key-block list fits one wave's lanes).
 inline void split_row(int32_t len, int32_t* n_chunks, int32_t* per_chunk) {
     int32_t per = kChunkTiles;
     if ((len + per - 1) / per > kMaxChunks) per = (len + kMaxChunks - 1) / kMaxChunks;
+    if (per > 64) per = 64;
     const int32_t n = (len + per - 1) / per;
     *n_chunks = n;
     *per_chunk = (len + n - 1) / n;
@@ -48,12 +56,14 @@ struct FwdArgs {
     float* lse;
     float* ws_o;              // [total_slots][64][D] fp32
     float* ws_lse;            // [total_slots][64]
-    const WorkItem* items;    // explicit items (CSR rows or chunks)
+    int32_t* counters;        // [n_counters] arrival counts of split rows (zero between calls)
+    const WorkItem* items;    // [H][n_item_per_head] explicit items, longest first per head
     const MergeItem* merges;
     const int32_t* col_idx;
     const int32_t* valid_len; // [B] or null
     const int32_t* routed_rows;
     int32_t n_items, n_merges;
+    int32_t items_per_head;   // explicit items per head (NOP-padded to equal length)
     int32_t B, H, L, nb, n_slots;
     // routed tiles (gathered query rows over all key blocks), placed first in the grid
     int32_t n_routed;         // k rows per (b, h); 0 = no routed tiles
@@ -69,7 +79,7 @@ struct FwdArgs {
 // ---- launchers (defined in kernels/*.hip) ----
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s,
                            hipEvent_t before, hipEvent_t after);
-hipError_t launch_merge_bf16(const FwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, const int32_t* row_ptr, int head_dim, int mask,
                           hipStream_t s, hipEvent_t before, hipEvent_t after);
 hipError_t launch_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,
@@ -91,6 +101,7 @@ struct bsattn_layout {
     int32_t n_slots = 0;        // partial slots per batch entry
     // device copy (after upload)
     int device = -1;
+    int32_t items_per_head = 0;
     int32_t* d_row_ptr = nullptr;
     int32_t* d_col_idx = nullptr;
     bsattn::WorkItem* d_items = nullptr;

@@ -1,32 +1,52 @@
 // fwd_bf16.hip -- block-sparse attention forward, bf16 in/out, bf16 MFMA with fp32 accumulation.
 //
-// What is computed (Adaptive Sparse Transformer page, the SparseAttention
-// formula; masked scores are -inf): for every query row, softmax over the
-// allowed keys of scale * q.k, times V.  Attention runs only on the non-zero
-// 64x64 blocks of the block-CSR layout (SQA page, "Transformer计算效率优化：SQA稀疏
-// 注意力机制详解", section 3.1: FlashAttention-style computation restricted to
-// non-zero blocks; section 5: 64x64 blocks held in on-chip memory).
+// What is computed (Adaptive Sparse Transformer page, "Adapt or Perish: 新手入门指南 –
+// Adaptive Sparse Transformer 核心原理与实战", the SparseAttention formula; masked
+// scores are -inf): for every query row, softmax over the allowed keys of
+// scale * q.k, times V.  Attention runs only on the non-zero 64x64 blocks of
+// the block-CSR layout (SQA page, "Transformer计算效率优化：SQA稀疏注意力机制详解",
+// section 3.1: FlashAttention-style computation restricted to non-zero
+// blocks; section 5: 64x64 blocks staged in on-chip memory).
 //
-// Design for gfx950 (CDNA4, wave64, 160 KB LDS per CU):
-//  * One workgroup = 2 waves = one 64-row query tile; wave w owns rows
-//    32w..32w+31.  The tile walks its CSR row of key blocks.
-//  * K and V tiles are double-buffered in LDS: the global loads of tile t+1
-//    are issued into registers before tile t is computed, and written to the
-//    other LDS buffer afterwards; one barrier per tile.  K is stored
-//    row-major (padded rows, conflict-free 16-byte reads); V is stored
-//    transposed (Vt[d][key]) so that the PV contraction over keys reads
-//    contiguous keys.
-//  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: the 32x32 accumulator gives each lane 16
-//    keys of ONE query, so the row max/sum are in-lane reductions plus a
-//    single exchange between the two half-waves.  The same registers,
-//    rounded to bf16, are directly the B operand of O^T = V^T P^T (the order
-//    of the contraction index is free as long as A and B agree).
-//  * Online softmax in the log2 domain: p = exp2(s*scale*log2e - m) with a
-//    single FMA feeding v_exp_f32; running max m and per-half partial sums.
+// Design for gfx950 (CDNA4: wave64, 4 SIMDs and 160 KB LDS per CU, 8 XCDs):
+//  * One workgroup = 2 waves = one 64-row query tile walking its list of key
+//    blocks; wave w owns query rows 32w..32w+31 against all 64 keys of every
+//    key tile.  The list (at most 64 blocks) is read once into a VGPR and
+//    each step takes its block index with v_readlane.
+//  * K and V tiles travel global -> LDS by direct LDS loads
+//    (global_load_lds_dwordx4, issued from inline asm so that only the
+//    pipeline's explicit waits govern them): no staging registers, no LDS
+//    store instructions.  Tiles are row-major in LDS with the 16-byte pieces of
+//    every row XOR-swizzled so that both readers are bank-conflict free:
+//    K through ds_read_b128 (A operand of S^T = K Q^T), V through
+//    ds_read_b64_tr_b16, whose 16-lane transpose hands each lane 4
+//    consecutive keys of one d column -- exactly the A operand of
+//    O^T = V^T P^T, with no transpose pass over V.
+//  * Two LDS stages: the loads of the next tile are in flight while the
+//    current one is computed (a third stage cost more in occupancy than it
+//    gained in latency hiding).  Every step waits
+//    with an explicit vmcnt for its own tile only and passes a plain
+//    s_barrier (a fenced __syncthreads would wait for all loads in flight).
+//  * Scores are computed transposed with v_mfma_f32_32x32x16_bf16: each lane
+//    holds 16 keys of ONE query per 32x32 block, so row reductions are in-lane
+//    plus one v_permlane32_swap between half-waves.  The same registers,
+//    rounded to bf16, are the B operand of the PV product (the order of a
+//    contraction index is free as long as both operands agree).
+//  * Online softmax in the log2 domain, p = exp2(s*scale*log2e - m): one FMA
+//    into v_exp_f32 (half rate on gfx950).  The running max m is only raised
+//    when a tile's max exceeds it by more than kLazyMax (so p <= 2^kLazyMax,
+//    harmless in fp32 and bf16), which skips the O rescale on almost every
+//    tile.  Row sums add the fp32 probabilities (v_dot2c_f32_bf16 on the bf16
+//    P gave wrong sums on gfx950 in testing, so it is not used).
 //  * Rows longer than 16 blocks (global rows, routed tiles) are split into
-//    chunks; each chunk writes a normalised fp32 partial and its LSE, and
-//    merge_kernel combines them by log-sum-exp.
+//    chunks run by different workgroups; each writes a normalised fp32
+//    partial and its LSE, and the last chunk to arrive (atomic counter,
+//    release/acquire fences) merges them by log-sum-exp and resets the
+//    counter -- the whole forward is one launch.
+//  * Scheduling: workgroups are dealt round-robin to the 8 XCDs; workgroup i
+//    runs on XCD i%8, and the kernel maps it to the (i/8)-th unit of the
+//    (batch, head) groups assigned to that XCD, so every group's K/V is read
+//    by one XCD and stays in its L2.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -37,161 +57,193 @@ namespace bsattn {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // native vector: stays in registers
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // native vectors stay in registers
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.0f;   // log2 units: p never exceeds 2^8
+constexpr int kThreads = 128;      // 2 waves per workgroup
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     bf16x2_t r = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ bf16x8_t pack_bf16x8(const f32x16_t& s, int base) {
-    u32x4_t u;
-    u.x = pack_bf16x2(s[base + 0], s[base + 1]);
-    u.y = pack_bf16x2(s[base + 2], s[base + 3]);
-    u.z = pack_bf16x2(s[base + 4], s[base + 5]);
-    u.w = pack_bf16x2(s[base + 6], s[base + 7]);
-    return as_bf16x8(u);
+// Combine a value across the two half-waves (lanes l and l^32).
+// v_permlane32_swap exchanges one half of its first operand with the other
+// half of its second; with x in both, the two results hold x from the lower
+// and from the upper half-wave in every lane, in some order -- so their max
+// and their sum are the pairwise max and sum whatever the order.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
-// Layout constants shared by the kernel and its tile helpers.
+// Workgroup barrier without a memory fence: outstanding direct-to-LDS loads
+// of later tiles stay in flight (each wave has already waited for its own
+// loads of the tile about to be read).  The empty asm keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <int D>
-struct Tile {
-    static constexpr int KS = D + 8;     // LDS K row stride (bf16 elements): conflict-free 16-byte reads
-    static constexpr int VS = 64 + 4;    // LDS Vt row stride (bf16 elements): conflict-free 8-byte reads
-    static constexpr int KT = 64 * KS;   // K tile (elements)
-    static constexpr int VT = D * VS;    // Vt tile (elements)
-    static constexpr int KLD = D / 16;   // 16-byte K pieces per thread per tile (128 threads)
-    static constexpr int VLD = D / 64;   // (4 keys x 8 d) V units per thread per tile
+struct Geo {
+    static constexpr int PIECES = D / 8;                 // 16-byte pieces per K/V row
+    static constexpr int TILE = 64 * D;                  // bf16 elements of one K or V tile
+    static constexpr int LPT = 64 * PIECES / kThreads;   // direct loads per thread per K (or V) tile
+    static constexpr int NC = D / 16;                    // 16-wide contraction chunks of S^T
+    static constexpr int NDB = D / 32;                   // 32-row blocks of O^T
 };
 
-// Issue the global loads of key block j into registers.  K: 16-byte pieces,
-// consecutive threads on consecutive pieces of a row.  V: thread owns 4
-// consecutive keys x 8 consecutive d, ready for the transposed LDS store.
-template <int D>
-__device__ __forceinline__ void tile_gload(const uint16_t* kp, const uint16_t* vp, int j, int tid,
-                                           u32x4_t (&kr)[Tile<D>::KLD], u32x4_t (&vr)[Tile<D>::VLD][4]) {
-    const uint16_t* kt = kp + (size_t)j * 64 * D;
-#pragma unroll
-    for (int r = 0; r < Tile<D>::KLD; ++r) {
-        const int id = tid + 128 * r;
-        const int row = id / (D / 8), cc = id % (D / 8);
-        kr[r] = *(const u32x4_t*)(kt + row * D + cc * 8);
-    }
-    const uint16_t* vt = vp + (size_t)j * 64 * D;
-#pragma unroll
-    for (int u = 0; u < Tile<D>::VLD; ++u) {
-        const int uid = tid + 128 * u;
-        const int kg = uid % 16, dc = uid / 16;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) vr[u][rr] = *(const u32x4_t*)(vt + (4 * kg + rr) * D + 8 * dc);
-    }
+// One direct global -> LDS load of 16 bytes per lane from sbase + voff: lane
+// i's bytes land at LDS byte address lds + 16 i (sbase and lds are
+// wave-uniform SGPR values, voff a per-lane byte offset).  Written as inline
+// asm so that the compiler does not track it: the only waits on these loads
+// are the explicit vmcnt waits of the pipeline (the compiler's own LDS-DMA
+// alias tracking inserts full drains at loop headers).  The instruction
+// writes no register; M0 is saved and restored around it, with the wait
+// state M0 needs before an LDS load.
+__device__ __forceinline__ void lds_load16(uint32_t voff, const void* sbase, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
 }
 
-// Write the staged tile to one LDS buffer: K row-major, V transposed (Vt[d][key]).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)LDS_PTR(p);
+}
+
+// Physical position of a 16-byte piece inside its row (XOR is an involution,
+// so the same map converts logical <-> physical).
+__device__ __forceinline__ int swz_k(int row, int piece) { return piece ^ (row & 7); }
+__device__ __forceinline__ int swz_v(int row, int piece) { return piece ^ ((row & 3) << 1); }
+
+// Direct loads of key block j into one LDS stage [K tile | V tile].  Each wave
+// instruction fills 1 KB of LDS contiguously (lane i -> +16 i); lane i loads
+// the global piece that the swizzle places at that slot, and the 8 (16) lanes
+// covering one row read the whole 128 (256) byte row.  Per-lane byte offsets
+// are fixed for the whole walk (koffs/voffs); the tile base and the LDS
+// destination are scalars, so a load costs no vector ALU work.
 template <int D>
-__device__ __forceinline__ void tile_lstore(uint16_t* Ks, int tid, const u32x4_t (&kr)[Tile<D>::KLD],
-                                            const u32x4_t (&vr)[Tile<D>::VLD][4]) {
-    uint16_t* Vt = Ks + Tile<D>::KT;
+__device__ __forceinline__ void issue_tile(const uint16_t* kp, const uint16_t* vp, int j,
+                                           const uint32_t (&koffs)[Geo<D>::LPT],
+                                           const uint32_t (&voffs)[Geo<D>::LPT], uint32_t lds_wave) {
+    using Gm = Geo<D>;
+    const uint16_t* kt = kp + (size_t)j * 64 * D;
+    const uint16_t* vt = vp + (size_t)j * 64 * D;
 #pragma unroll
-    for (int r = 0; r < Tile<D>::KLD; ++r) {
-        const int id = tid + 128 * r;
-        const int row = id / (D / 8), cc = id % (D / 8);
-        *(u32x4_t*)(Ks + row * Tile<D>::KS + cc * 8) = kr[r];
-    }
-#pragma unroll
-    for (int u = 0; u < Tile<D>::VLD; ++u) {
-        const int uid = tid + 128 * u;
-        const int kg = uid % 16, dc = uid / 16;
-#pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-            // dword m4 of key row rr holds d = 8dc+2m4 (low half) and 8dc+2m4+1 (high half)
-            const uint32_t w0 = vr[u][0][m4], w1 = vr[u][1][m4];
-            const uint32_t w2 = vr[u][2][m4], w3 = vr[u][3][m4];
-            u32x2_t lo, hi;
-            lo.x = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-            lo.y = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-            hi.x = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-            hi.y = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-            *(u32x2_t*)(Vt + (8 * dc + 2 * m4) * Tile<D>::VS + 4 * kg) = lo;
-            *(u32x2_t*)(Vt + (8 * dc + 2 * m4 + 1) * Tile<D>::VS + 4 * kg) = hi;
-        }
+    for (int r = 0; r < Gm::LPT; ++r) {
+        lds_load16(koffs[r], kt, lds_wave + r * kThreads * 16);
+        lds_load16(voffs[r], vt, lds_wave + 2 * Gm::TILE + r * kThreads * 16);
     }
 }
 
 template <int D, int MASK>
-__global__ __launch_bounds__(128) void fwd_bf16_kernel(const FwdArgs a) {
-    constexpr int KS = Tile<D>::KS, VS = Tile<D>::VS, KT = Tile<D>::KT, VT = Tile<D>::VT;
-    constexpr int KLD = Tile<D>::KLD, VLD = Tile<D>::VLD;
-    constexpr int NC = D / 16;       // 16-wide contraction chunks of Q K^T
-    constexpr int NDB = D / 32;      // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
+__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
+    using Gm = Geo<D>;
+    constexpr int NC = Gm::NC, NDB = Gm::NDB, TILE = Gm::TILE;
+    __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * TILE];
+    int* s_last = (int*)st0;   // merge flag; the stages are idle once the walk is done
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int ql = lane & 31;
     const int hh = lane >> 5;
-    const int rloc = wave * 32 + ql;
+    const int rloc = wave * 32 + ql;  // this lane's query row within the tile
 
-    // ---- decode the work unit: routed tiles first, then the explicit items ----
-    int b, h, qblk = 0, cb, ce, slot, rt = 0;
+    // ---- decode: XCD x = blockIdx % 8 runs groups g = x, x+8, ... in order ----
+    const int G = a.B * a.H;
+    const int nru = a.n_routed > 0 ? a.n_rt * a.r_chunks : 0;   // routed units per group
+    const int per_group = nru + a.items_per_head;
+    const int x = blockIdx.x % kXcds;
+    const int p = blockIdx.x / kXcds;
+    const int g = x + kXcds * (p / per_group);
+    const int it = p % per_group;
+    if (g >= G) return;
+    const int b = g / a.H, h = g % a.H;
+
+    int qblk = 0, cb, ce, slot, rt = 0, cidx = -1, first = 0, nch = 0;
     bool routed;
-    const int n_routed_units = a.n_routed > 0 ? a.B * a.H * a.n_rt * a.r_chunks : 0;
-    if ((int)blockIdx.x < n_routed_units) {
-        int r = blockIdx.x;
-        const int c = r % a.r_chunks;
-        r /= a.r_chunks;
-        rt = r % a.n_rt;
-        r /= a.n_rt;
-        h = r % a.H;
-        b = r / a.H;
+    if (it < nru) {
+        rt = it / a.r_chunks;
+        const int c = it % a.r_chunks;
         cb = c * a.r_chunk_tiles;
         ce = min(a.nb, cb + a.r_chunk_tiles);
-        slot = a.r_slot_base + ((b * a.H + h) * a.n_rt + rt) * a.r_chunks + c;
+        first = a.r_slot_base + (g * a.n_rt + rt) * a.r_chunks;
+        slot = first + c;
+        nch = a.r_chunks;
+        cidx = a.B * a.n_merges + g * a.n_rt + rt;
         routed = true;
     } else {
-        const int u = blockIdx.x - n_routed_units;
-        const WorkItem it = a.items[u / a.B];
-        b = u % a.B;
-        h = it.row / a.nb;
-        qblk = it.row % a.nb;
-        cb = it.col_begin;
-        ce = it.col_end;
-        slot = it.slot < 0 ? -1 : b * a.n_slots + it.slot;
+        const WorkItem wi = a.items[h * a.items_per_head + (it - nru)];
+        if (wi.row < 0) return;
+        qblk = wi.row % a.nb;
+        cb = wi.col_begin;
+        ce = wi.col_end;
+        slot = wi.slot < 0 ? -1 : b * a.n_slots + wi.slot;
+        if (wi.slot >= 0) {
+            first = b * a.n_slots + wi.first_slot;
+            nch = wi.n_chunks;
+            cidx = b * a.n_merges + wi.merge;
+        }
         routed = false;
     }
-    const size_t bh = (size_t)b * a.H + h;
+    const size_t bh = (size_t)g;
 
-    int tq;   // query token of this lane's row (-1: unused row of a ragged routed tile)
-    if (!routed) {
-        tq = qblk * 64 + rloc;
-    } else {
-        const int kk = rt * 64 + rloc;
-        tq = kk < a.n_routed ? a.routed_rows[bh * a.n_routed + kk] : -1;
-        if (tq >= a.L) tq = -1;   // out-of-range routed rows are skipped, never dereferenced
-    }
+    auto query_token = [&](int r) -> int {   // token of tile row r (-1: unused routed row)
+        if (!routed) return qblk * 64 + r;
+        const int kk = rt * 64 + r;
+        const int t = kk < a.n_routed ? a.routed_rows[bh * a.n_routed + kk] : -1;
+        return (t >= a.L) ? -1 : t;          // out-of-range rows are skipped, never dereferenced
+    };
+    const int tq = query_token(rloc);
 
+    // Key blocks of this item, one per lane (<= 64 by construction of the schedule).
+    int n = ce - cb;
+    const int colv = lane < n ? (routed ? cb + lane : a.col_idx[cb + lane]) : 0;
     int valid = a.L;
     if (MASK == MASK_PAD) {
         valid = min(max(a.valid_len[b], 0), a.L);
-        // rows are ascending: drop the trailing blocks that start at or past the valid length
-        while (ce > cb && a.col_idx[ce - 1] * 64 >= valid) --ce;
+        // ascending blocks: keep those that start before the valid length
+        n = __builtin_popcountll(__ballot(lane < n && colv * 64 < valid));
     }
+    auto tile_of = [&](int t) -> int { return __builtin_amdgcn_readlane(colv, t); };
 
     const uint16_t* qp = (const uint16_t*)a.q + bh * (size_t)a.L * D;
     const uint16_t* kp = (const uint16_t*)a.k + bh * (size_t)a.L * D;
     const uint16_t* vp = (const uint16_t*)a.v + bh * (size_t)a.L * D;
 
-    // Q^T fragments, the B operand of S^T = K Q^T: lane (ql, hh) holds Q[row][16c + 8hh .. +7].
+    // Q^T fragments (B operand of S^T): lane (ql, hh) holds Q[row][16c + 8hh .. +7].
     bf16x8_t qf[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -205,203 +257,258 @@ __global__ __launch_bounds__(128) void fwd_bf16_kernel(const FwdArgs a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    float m = -INFINITY;   // running max of scaled scores (log2 units)
-    float l = 0.f;         // running partial sum over this half-wave's keys
+    float m = -INFINITY;   // running (lazily raised) max of scaled scores, log2 units
+    float l = 0.f;         // sum of this lane's probabilities
+    const float c2 = a.scale_log2;
 
-    u32x4_t kr[KLD];
-    u32x4_t vr[VLD][4];
-    const int n = ce - cb;
-    if (n > 0) {
-        tile_gload<D>(kp, vp, routed ? cb : a.col_idx[cb], tid, kr, vr);
-        tile_lstore<D>(smem, tid, kr, vr);
-    }
-    __syncthreads();
-
-    for (int t = 0; t < n; ++t) {
-        const int j = routed ? cb + t : a.col_idx[cb + t];
-        if (t + 1 < n) tile_gload<D>(kp, vp, routed ? cb + t + 1 : a.col_idx[cb + t + 1], tid, kr, vr);
-        const uint16_t* Ks = smem + (t & 1) * (KT + VT);
-        const uint16_t* Vt = Ks + KT;
-
-        // S^T (keys x queries): s0 keys 0..31, s1 keys 32..63 of the tile.
-        f32x16_t s0, s1;
+    // Per-lane LDS offsets (elements) of the fragment reads, fixed for the whole walk.
+    int koff[2][NC];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const bf16x8_t k0 = as_bf16x8(*(const u32x4_t*)(Ks + ql * KS + 16 * c + 8 * hh));
-            const bf16x8_t k1 = as_bf16x8(*(const u32x4_t*)(Ks + (32 + ql) * KS + 16 * c + 8 * hh));
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[c], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[c], s1, 0, 0, 0);
+            const int row = 32 * kb + ql;
+            koff[kb][c] = row * D + swz_k(row, 2 * c + hh) * 8;
         }
-        // accumulator register i holds key 8*(i/4) + 4*hh + (i%4) (+32 for s1)
+    // V: the 16-lane transpose read gives lane i of group G, value e, the
+    // element (i & 3) of source lane 4e + (i >> 2).  Source lane i therefore
+    // points at key row 16c + 8e2 + 4hh + (i >> 2), columns 32db + 16(G & 1) + 4(i & 3) .. +3,
+    // and receives V[16c + 8e2 + 4hh + e][32db + ql] for e = 0..3.
+    const int gi = lane & 15, gsel = (lane >> 4) & 1;
+    int voff[4][NDB][2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                const int row = 16 * c + 8 * e2 + 4 * hh + (gi >> 2);
+                const int d0 = 32 * db + 16 * gsel + 4 * (gi & 3);
+                voff[c][db][e2] = row * D + swz_v(row, d0 >> 3) * 8 + (d0 & 7);
+            }
+
+    // Direct-load byte offsets of this thread's pieces (fixed for the whole walk)
+    // and the wave's LDS destinations in each stage.
+    uint32_t koffs[Gm::LPT], voffs[Gm::LPT];
+#pragma unroll
+    for (int r = 0; r < Gm::LPT; ++r) {
+        const int slot = r * kThreads + tid;
+        const int row = slot / Gm::PIECES, q = slot % Gm::PIECES;
+        koffs[r] = (uint32_t)(row * D + swz_k(row, q) * 8) * 2u;
+        voffs[r] = (uint32_t)(row * D + swz_v(row, q) * 8) * 2u;
+    }
+    const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(wave * 64 * 16);
+    const uint32_t lds0 = lds_addr(st0) + wave_lds, lds1 = lds_addr(st1) + wave_lds;
+
+    auto compute = [&](int t, const uint16_t* Ks) {
+        const uint16_t* Vs = Ks + TILE;
+        const int j = tile_of(t);
+        // S^T (keys x queries): s[kb] register i <-> key 32kb + 8(i/4) + 4hh + i%4.
+        bf16x8_t kf[2][NC];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) kf[kb][c] = as_bf16x8(*(const u32x4_t*)(Ks + koff[kb][c]));
+        f32x16_t s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][c], qf[c], s[kb], 0, 0, 0);
         if (MASK == MASK_PAD) {
             if (j * 64 + 64 > valid) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = j * 64 + 8 * (i / 4) + 4 * hh + (i % 4);
-                    if (key >= valid) s0[i] = -INFINITY;
-                    if (key + 32 >= valid) s1[i] = -INFINITY;
-                }
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) s[kb][i] = -INFINITY;
             }
         }
         if (MASK == MASK_BAND) {
             if (!routed) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = j * 64 + 8 * (i / 4) + 4 * hh + (i % 4);
-                    if (abs(tq - key) > a.band) s0[i] = -INFINITY;
-                    if (abs(tq - key - 32) > a.band) s1[i] = -INFINITY;
-                }
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (abs(tq - (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4))) > a.band)
+                            s[kb][i] = -INFINITY;
             }
         }
-
-        float mx = fmaxf(s0[0], s1[0]);
+        // V^T fragments for the PV product, read while the softmax runs.
+        bf16x8_t va[4][NDB];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m, mx * a.scale_log2);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m - muse);
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.scale_log2, -muse));
-            s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.scale_log2, -muse));
-            ps += s0[i] + s1[i];
-        }
-        l = l * alpha + ps;
-        m = mnew;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-
-        // P^T fragments: MFMA c2 covers keys 16c2..16c2+15; element e of lane half hh is
-        // key 16c2 + 8(e/4) + 4hh + e%4.
-        bf16x8_t pf[4];
-        pf[0] = pack_bf16x8(s0, 0);
-        pf[1] = pack_bf16x8(s0, 8);
-        pf[2] = pack_bf16x8(s1, 0);
-        pf[3] = pack_bf16x8(s1, 8);
-#pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) {
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const uint16_t* vrow = Vt + (32 * db + ql) * VS + 16 * c2 + 4 * hh;
-                const u32x2_t lo = *(const u32x2_t*)vrow;
-                const u32x2_t hi = *(const u32x2_t*)(vrow + 8);
-                const u32x4_t lh = {lo.x, lo.y, hi.x, hi.y};
-                const bf16x8_t va = as_bf16x8(lh);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[c2], o[db], 0, 0, 0);
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t*)(Vs + voff[c][db][0]));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t*)(Vs + voff[c][db][1]));
+                const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+                const u32x4_t lh = {l2.x, l2.y, h2.x, h2.y};
+                va[c][db] = as_bf16x8(lh);
             }
+
+        float mx = __builtin_fmaxf(__builtin_fmaxf(s[0][0], s[0][1]), s[1][0]);
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][i]), s[0][i + 1]);
+#pragma unroll
+        for (int i = 1; i < 15; i += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[1][i]), s[1][i + 1]);
+        mx = __builtin_fmaxf(mx, s[1][15]);
+        mx = pair_max(mx) * c2;
+        const bool raise = mx > m + kLazyMax;
+        if (__ballot(raise) != 0) {          // wave-uniform: rescale only when some row's max jumped
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m - mx) : 1.f;   // 0 when m was -inf
+            const float mn = raise ? mx : m;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+            m = mn;
         }
-        if (t + 1 < n) tile_lstore<D>(smem + ((t + 1) & 1) * (KT + VT), tid, kr, vr);
-        __syncthreads();
+        const float muse = m == -INFINITY ? 0.f : m;
+
+        // P^T fragments: pf[c] (c = 0..3) element e <-> key 16c + 8(e/4) + 4hh + e%4.
+        bf16x8_t pf[4];
+        float ls[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            u32x4_t u;
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][8 * (c % 2) + 2 * e], c2, -muse));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][8 * (c % 2) + 2 * e + 1], c2, -muse));
+                u[e] = pack_bf16x2(p0, p1);
+                acc += p0 + p1;
+            }
+            ls[c] = acc;
+            pf[c] = as_bf16x8(u);
+        }
+        l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c][db], pf[c], o[db], 0, 0, 0);
+    };
+
+    // ---- pipelined walk over the key blocks ----
+    // The block list and Q must be in registers before the first load
+    // addresses and MFMAs; waiting here once keeps the compiler from placing
+    // conservative full waits inside the pipeline.  The prologue loads are
+    // unconditional (lanes past the list hold block 0, a valid address).
+    wait_vmcnt<0>();
+    issue_tile<D>(kp, vp, tile_of(0), koffs, voffs, lds0);
+    // step t: tile t sits in stage t%2; the loads of tile t+1 go to the other
+    // stage, whose last reader (step t-1) is behind the barrier.
+    auto step = [&](int t, const uint16_t* cur, uint32_t nxt) {
+        wait_vmcnt<0>();
+        stage_barrier();
+        if (t + 1 < n) issue_tile<D>(kp, vp, tile_of(t + 1), koffs, voffs, nxt);
+        compute(t, cur);
+    };
+    for (int t = 0; t < n; t += 2) {
+        step(t, st0, lds1);
+        if (t + 1 < n) step(t + 1, st1, lds0);
     }
+    wait_vmcnt<0>();   // no direct-to-LDS load may outlive the workgroup
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
-    const float lt = l + __shfl_xor(l, 32);
+    const float lt = pair_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse_v = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
-    if (tq < 0) return;
-    if (slot < 0) {
-        uint16_t* orow = (uint16_t*)a.out + (bh * a.L + tq) * D;
+    if (tq >= 0) {
+        // O^T register i of block db <-> d = 32db + 8(i/4) + 4hh + i%4
+        if (slot < 0) {
+            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + tq) * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * db + 8 * g + 4 * hh;
-                u32x2_t w;
-                w.x = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
-                w.y = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                *(u32x2_t*)(orow + d0) = w;
-            }
-        if (hh == 0) a.lse[bh * a.L + tq] = lse_v;
-    } else {
-        float* orow = a.ws_o + ((size_t)slot * 64 + rloc) * D;
+                for (int gq = 0; gq < 4; ++gq) {
+                    u32x2_t w;
+                    w.x = pack_bf16x2(o[db][4 * gq + 0] * inv, o[db][4 * gq + 1] * inv);
+                    w.y = pack_bf16x2(o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv);
+                    *(u32x2_t*)(orow + 32 * db + 8 * gq + 4 * hh) = w;
+                }
+            if (hh == 0) a.lse[bh * a.L + tq] = lse_v;
+        } else {
+            float* orow = a.ws_o + ((size_t)slot * 64 + rloc) * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * db + 8 * g + 4 * hh;
-                *(float4*)(orow + d0) = make_float4(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv,
-                                                    o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-            }
-        if (hh == 0) a.ws_lse[(size_t)slot * 64 + rloc] = lse_v;
-    }
-}
-
-// Combine the chunk partials of split rows: LSE = logsumexp_c LSE_c,
-// O = sum_c exp(LSE_c - LSE) O_c.  A chunk with no allowed key has LSE_c = -inf
-// and weight 0; a row with none at all gets O = 0, LSE = -inf.
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const FwdArgs a) {
-    constexpr int DP = D / 4;   // d values per thread
-    const int row = threadIdx.x >> 2;
-    const int part = threadIdx.x & 3;
-    int b, h, first, nch, tq;
-    const int n_routed_units = a.n_routed > 0 ? a.B * a.H * a.n_rt : 0;
-    if ((int)blockIdx.x < n_routed_units) {
-        int r = blockIdx.x;
-        const int rt = r % a.n_rt;
-        r /= a.n_rt;
-        h = r % a.H;
-        b = r / a.H;
-        first = a.r_slot_base + ((b * a.H + h) * a.n_rt + rt) * a.r_chunks;
-        nch = a.r_chunks;
-        const int kk = rt * 64 + row;
-        tq = kk < a.n_routed ? a.routed_rows[((size_t)b * a.H + h) * a.n_routed + kk] : -1;
-        if (tq >= a.L) tq = -1;
-    } else {
-        const int u = blockIdx.x - n_routed_units;
-        const MergeItem mi = a.merges[u / a.B];
-        b = u % a.B;
-        h = mi.row / a.nb;
-        first = b * a.n_slots + mi.first_slot;
-        nch = mi.n_chunks;
-        tq = (mi.row % a.nb) * 64 + row;
-    }
-    if (tq < 0) return;
-    const size_t bh = (size_t)b * a.H + h;
-    float mx = -INFINITY;
-    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.ws_lse[(size_t)(first + c) * 64 + row]);
-    uint16_t* orow = (uint16_t*)a.out + (bh * a.L + tq) * D + part * DP;
-    if (mx == -INFINITY) {
-#pragma unroll
-        for (int d = 0; d < DP; d += 2) *(uint32_t*)(orow + d) = 0u;
-        if (part == 0) a.lse[bh * a.L + tq] = -INFINITY;
-        return;
-    }
-    float acc[DP];
-#pragma unroll
-    for (int d = 0; d < DP; ++d) acc[d] = 0.f;
-    float wsum = 0.f;
-    for (int c = 0; c < nch; ++c) {
-        const float w = expf(a.ws_lse[(size_t)(first + c) * 64 + row] - mx);
-        wsum += w;
-        const float* src = a.ws_o + ((size_t)(first + c) * 64 + row) * D + part * DP;
-#pragma unroll
-        for (int d = 0; d < DP; d += 4) {
-            const float4 x = *(const float4*)(src + d);
-            acc[d + 0] += w * x.x;
-            acc[d + 1] += w * x.y;
-            acc[d + 2] += w * x.z;
-            acc[d + 3] += w * x.w;
+                for (int gq = 0; gq < 4; ++gq)
+                    *(float4*)(orow + 32 * db + 8 * gq + 4 * hh) =
+                        make_float4(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
+                                    o[db][4 * gq + 3] * inv);
+            if (hh == 0) a.ws_lse[(size_t)slot * 64 + rloc] = lse_v;
         }
     }
-    const float inv = 1.f / wsum;
+    if (slot < 0) return;
+
+    // ---- split row: the last chunk to arrive merges all partials ----
+    __threadfence();      // release this chunk's partial
+    __syncthreads();
+    if (tid == 0) *s_last = atomicAdd(&a.counters[cidx], 1) == nch - 1;
+    __syncthreads();
+    if (!*s_last) return;
+    __threadfence();      // acquire the other chunks' partials
+    {
+        constexpr int DP = D / 2;
+        const int row = tid >> 1, part = tid & 1;
+        const int t2 = query_token(row);
+        if (t2 >= 0) {
+            float mxl = -INFINITY;
+            for (int c = 0; c < nch; ++c) mxl = __builtin_fmaxf(mxl, a.ws_lse[(size_t)(first + c) * 64 + row]);
+            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t2) * D + part * DP;
+            if (mxl == -INFINITY) {
 #pragma unroll
-    for (int d = 0; d < DP; d += 2) *(uint32_t*)(orow + d) = pack_bf16x2(acc[d] * inv, acc[d + 1] * inv);
-    if (part == 0) a.lse[bh * a.L + tq] = mx + logf(wsum);
+                for (int d = 0; d < DP; d += 2) *(uint32_t*)(orow + d) = 0u;
+                if (part == 0) a.lse[bh * a.L + t2] = -INFINITY;
+            } else {
+                float acc[DP];
+#pragma unroll
+                for (int d = 0; d < DP; ++d) acc[d] = 0.f;
+                float wsum = 0.f;
+                for (int c = 0; c < nch; ++c) {
+                    const float w = expf(a.ws_lse[(size_t)(first + c) * 64 + row] - mxl);
+                    wsum += w;
+                    const float* src = a.ws_o + ((size_t)(first + c) * 64 + row) * D + part * DP;
+#pragma unroll
+                    for (int d = 0; d < DP; d += 4) {
+                        const float4 v4 = *(const float4*)(src + d);
+                        acc[d] += w * v4.x;
+                        acc[d + 1] += w * v4.y;
+                        acc[d + 2] += w * v4.z;
+                        acc[d + 3] += w * v4.w;
+                    }
+                }
+                const float inv2 = 1.f / wsum;
+#pragma unroll
+                for (int d = 0; d < DP; d += 2) *(uint32_t*)(orow + d) = pack_bf16x2(acc[d] * inv2, acc[d + 1] * inv2);
+                if (part == 0) a.lse[bh * a.L + t2] = mxl + logf(wsum);
+            }
+        }
+    }
+    if (tid == 0) a.counters[cidx] = 0;   // ready for the next call on this workspace
+}
+
+__global__ void zero_i32_kernel(int32_t* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
 }
 
 template <int D, int MASK>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-    const int64_t n_routed_units = a.n_routed > 0 ? (int64_t)a.B * a.H * a.n_rt * a.r_chunks : 0;
-    const int64_t grid = (int64_t)a.n_items * a.B + n_routed_units;
+    const int64_t G = (int64_t)a.B * a.H;
+    const int64_t nru = a.n_routed > 0 ? (int64_t)a.n_rt * a.r_chunks : 0;
+    const int64_t grid = kXcds * ((G + kXcds - 1) / kXcds) * (nru + a.items_per_head);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK>), dim3((unsigned)grid), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -425,14 +532,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
     return hipSuccess;
 }
 
-hipError_t launch_merge_bf16(const FwdArgs& a, int head_dim, hipStream_t s) {
-    const int64_t n_routed_units = a.n_routed > 0 ? (int64_t)a.B * a.H * a.n_rt : 0;
-    const int64_t grid = (int64_t)a.n_merges * a.B + n_routed_units;
-    if (grid == 0) return hipSuccess;
-    if (head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<64>), dim3((unsigned)grid), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((merge_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, a);
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

@@ -315,3 +315,27 @@ def test_edge_long_global_rows_many_chunks():
     L = 600 * 64
     rows = [(0, 0, t) for t in (0, 1, 31, 63, L - 64, L - 1, 64, 5000, 20000, 38000)]
     _edge(1, L, 64, "bf16", 3, [0, 599], 1, 9, tag="nb=600 global rows", rows=rows)
+
+
+def test_workspace_reused_across_calls_and_init():
+    """Split-row counters return to zero after every call: one workspace serves many calls,
+    and bsattn_workspace_init makes a dirty buffer usable."""
+    wl = WORKLOADS["bigbird-L2048"].with_(batch=2, heads=2)
+    _say("workspace reuse", wl)
+    inp = make_inputs(wl)
+    lay, olay = _layouts(wl)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    n = bs.bsattn_workspace_size(lay, wl.batch, wl.head_dim)
+    ws = torch.full(((n + 255) // 4,), 7.0, dtype=torch.float32, device="cuda")   # dirty
+    bs.bsattn_workspace_init(lay, wl.batch, wl.head_dim, 0, ws)
+    outs = []
+    for _ in range(3):
+        out, lse = bs.forward(dev["q"], dev["k"], dev["v"], lay, scale=wl.scale, workspace=ws)
+        outs.append((out.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l.view(torch.int32), outs[0][1].view(torch.int32))
+    ro, rl = OA.attention_forward(inp["q"], inp["k"], inp["v"], olay, wl.scale)
+    _compare(outs[-1][0].float().cpu().numpy().astype(np.float64), outs[-1][1].cpu().numpy().astype(np.float64),
+             ro, rl, "bf16", "workspace reuse")
