@@ -45,8 +45,8 @@ def parse_args():
     p.add_argument("--workload", default=None, help="default: the L=8192 BigBird workload")
     p.add_argument("--rotate", type=int, default=3, help="input copies rotated across steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-heads", type=int, default=1,
-                   help="(batch, head) pairs the oracle runs for the CPU baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="the CPU baseline runs whole (batch, head) pairs until this much time has passed")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="instead of the benchmark, run plain device copies of MIB MiB (counter calibration)")
     return p.parse_args()
@@ -93,17 +93,22 @@ def calibrate_copy(mib: int) -> None:
     print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}))
 
 
-def cpu_baseline(wl, inp, layout_o, n_pairs: int):
-    """The oracle as it stands, on the first n_pairs (batch, head) pairs, all query rows."""
+def cpu_baseline(wl, inp, layout_o, seconds: float):
+    """The oracle as it stands, on whole (batch, head) pairs (all query rows) taken in order
+    until ``seconds`` have passed, scaled to the whole job."""
     from threadpoolctl import threadpool_info
 
     from oracle import attention as OA
-    pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)][:n_pairs]
+    all_pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)]
     vl = inp.get("valid_len")
+    pairs = []
     t0 = time.perf_counter()
-    for b, h in pairs:
+    for b, h in all_pairs:
         OA.attention_forward(inp["q"], inp["k"], inp["v"], layout_o, wl.scale,
                              valid_len=None if vl is None else vl.tolist(), heads=[h], batches=[b])
+        pairs.append((b, h))
+        if time.perf_counter() - t0 >= seconds:
+            break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     full_s = dt * (wl.batch * wl.heads) / len(pairs)
@@ -252,7 +257,7 @@ def main():
         from oracle import layout as OL
         olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
                               wl.random_blocks, wl.layout_seed)
-        result["cpu_baseline"] = cpu_baseline(wl, inp, olay, args.cpu_sample_heads)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, olay, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
