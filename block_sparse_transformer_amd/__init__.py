@@ -25,7 +25,6 @@ from ._binding import (  # noqa: F401
     bsattn_route_topk,
     bsattn_set_profile_events,
     bsattn_status_string,
-    bsattn_workspace_init,
     bsattn_workspace_size,
     forward,
     forward_routed,

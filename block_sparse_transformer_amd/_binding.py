@@ -49,7 +49,6 @@ def lib() -> ctypes.CDLL:
     L.bsattn_layout_destroy.argtypes = [_c_vp]
     L.bsattn_layout_destroy.restype = None
     L.bsattn_workspace_size.argtypes = [_c_vp, _c_int, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]
-    L.bsattn_workspace_init.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_vp, ctypes.c_size_t, _c_vp]
     L.bsattn_forward.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
                                  _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_size_t, _c_vp]
     L.bsattn_route_topk.argtypes = [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp]
@@ -62,7 +61,7 @@ def lib() -> ctypes.CDLL:
     L.bsattn_last_error.argtypes = []
     L.bsattn_last_error.restype = ctypes.c_char_p
     for name in ("bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr", "bsattn_layout_upload",
-                 "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_workspace_init", "bsattn_forward",
+                 "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
                  "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -168,14 +167,6 @@ def bsattn_workspace_size(layout: Layout, batch: int, head_dim: int, num_routed:
     return n.value
 
 
-def bsattn_workspace_init(layout: Layout, batch: int, head_dim: int, num_routed: int, workspace,
-                          stream=None) -> None:
-    """Zero the workspace's counter area on the stream (needed once before first use)."""
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("bsattn_workspace_init", lib().bsattn_workspace_init(
-        layout.handle, batch, head_dim, num_routed, _ptr(workspace), wbytes, _stream_handle(stream)))
-
-
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -251,8 +242,7 @@ def _workspace(layout: Layout, q, num_routed: int = 0):
     n = bsattn_workspace_size(layout, q.shape[0], q.shape[3], num_routed)
     if n == 0:
         return None
-    # zero-filled: the split-row arrival counters at its start must begin at zero
-    return torch.zeros((n + 255) // 4, dtype=torch.float32, device=q.device)
+    return torch.empty((n + 255) // 4, dtype=torch.float32, device=q.device)
 
 
 def forward(q, k, v, layout: Layout, key_valid_len=None, scale: Optional[float] = None, workspace=None):

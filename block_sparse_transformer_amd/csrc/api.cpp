@@ -40,8 +40,7 @@ bsattn_status hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Work schedule: rows of <= kChunkTiles blocks become one item; longer rows are
-// split into balanced chunks whose partials are merged by the last chunk to
-// finish.  Each head's items are ordered longest first (so long chunks start
+// split into balanced chunks whose partials the merge kernel combines.  Each head's items are ordered longest first (so long chunks start
 // before short rows) and padded with no-op items to a common length; the
 // kernel deals whole (batch, head) groups to one XCD so their K/V stay in
 // that XCD's L2.
@@ -144,12 +143,6 @@ bsattn_status check_forward_common(const bsattn_layout* lay, int32_t B, int32_t 
 }
 
 size_t slot_bytes(int32_t D) { return (size_t)kBlock * (size_t)(D + 1) * sizeof(float); }
-
-// Counter area at the start of the workspace, rounded up to 256 bytes.
-size_t counter_ints(const bsattn_layout* lay, int32_t B, int32_t n_rt) {
-    const size_t n = (size_t)B * lay->merges.size() + (size_t)B * lay->H * n_rt;
-    return (n + 63) / 64 * 64;
-}
 
 void routed_split(int32_t nb, int32_t k, int32_t* n_rt, int32_t* r_chunks, int32_t* per) {
     *n_rt = (k + kBlock - 1) / kBlock;
@@ -356,26 +349,7 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* lay, int32_t batch, int
         routed_split(lay->nb, num_routed, &n_rt, &rch, &per);
         slots += (size_t)batch * lay->H * n_rt * rch;
     }
-    *bytes = slots == 0 ? 0 : counter_ints(lay, batch, n_rt) * sizeof(int32_t) + slots * slot_bytes(head_dim);
-    return ok();
-}
-
-bsattn_status bsattn_workspace_init(const bsattn_layout* lay, int32_t batch, int32_t head_dim,
-                                    int32_t num_routed, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
-    size_t need = 0;
-    bsattn_status st = bsattn_workspace_size(lay, batch, head_dim, num_routed, &need);
-    if (st != BSATTN_OK) return st;
-    if (need == 0) return ok();
-    if (!workspace || workspace_bytes < need)
-        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
-    int32_t n_rt = 0;
-    if (num_routed > 0) {
-        int32_t rch, per;
-        routed_split(lay->nb, num_routed, &n_rt, &rch, &per);
-    }
-    hipError_t e = launch_zero_i32((int32_t*)workspace, (int64_t)counter_ints(lay, batch, n_rt), stream);
-    if (e != hipSuccess) return hip_fail(e, "workspace init launch");
+    *bytes = slots * slot_bytes(head_dim);
     return ok();
 }
 
@@ -410,9 +384,7 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
     const size_t total_slots = (size_t)B * lay->n_slots;
-    const size_t nci = total_slots ? counter_ints(lay, B, 0) : 0;
-    a.counters = (int32_t*)workspace;
-    a.ws_o = workspace ? (float*)workspace + nci : nullptr;
+    a.ws_o = workspace ? (float*)workspace : nullptr;
     a.ws_lse = workspace ? a.ws_o + total_slots * kBlock * D : nullptr;
     a.items = lay->d_items;
     a.merges = lay->d_merges;
@@ -482,8 +454,7 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* lay, bsattn_dtype dtype
     FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
     const size_t total_slots = (size_t)B * lay->n_slots + (size_t)B * H * n_rt * rch;
-    a.counters = (int32_t*)workspace;
-    a.ws_o = (float*)workspace + counter_ints(lay, B, n_rt);
+    a.ws_o = (float*)workspace;
     a.ws_lse = a.ws_o + total_slots * kBlock * D;
     a.items = lay->d_items;
     a.merges = lay->d_merges;

@@ -22,8 +22,8 @@ enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2 };
 // O/LSE; slot >= 0: one chunk of a split row, written as a partial (O
 // normalised over the chunk, chunk LSE) to workspace slot b*n_slots + slot.
 // The chunks of split row `merge` occupy slots [first_slot, first_slot +
-// n_chunks); the last chunk to finish merges them.  row < 0: no work
-// (padding of a head's item list).
+// n_chunks); the merge kernel combines them.  row < 0: no work (padding of a
+// head's item list).
 struct WorkItem {
     int32_t row, col_begin, col_end, slot;
     int32_t merge, first_slot, n_chunks, pad;
@@ -56,7 +56,6 @@ struct FwdArgs {
     float* lse;
     float* ws_o;              // [total_slots][64][D] fp32
     float* ws_lse;            // [total_slots][64]
-    int32_t* counters;        // [n_counters] arrival counts of split rows (zero between calls)
     const WorkItem* items;    // [H][n_item_per_head] explicit items, longest first per head
     const MergeItem* merges;
     const int32_t* col_idx;
@@ -79,7 +78,6 @@ struct FwdArgs {
 // ---- launchers (defined in kernels/*.hip) ----
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s,
                            hipEvent_t before, hipEvent_t after);
-hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, const int32_t* row_ptr, int head_dim, int mask,
                           hipStream_t s, hipEvent_t before, hipEvent_t after);
 hipError_t launch_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,

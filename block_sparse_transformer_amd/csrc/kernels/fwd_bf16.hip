@@ -40,9 +40,10 @@
 //    P gave wrong sums on gfx950 in testing, so it is not used).
 //  * Rows longer than 16 blocks (global rows, routed tiles) are split into
 //    chunks run by different workgroups; each writes a normalised fp32
-//    partial and its LSE, and the last chunk to arrive (atomic counter,
-//    release/acquire fences) merges them by log-sum-exp and resets the
-//    counter -- the whole forward is one launch.
+//    partial and its LSE, and a small second launch merges them by
+//    log-sum-exp.  (Merging inside the attention kernel by the last chunk to
+//    arrive needs device-scope release/acquire fences, which on gfx950 write
+//    back and invalidate the XCD's L2 and slowed every resident workgroup.)
 //  * Scheduling: workgroups are dealt round-robin to the 8 XCDs; workgroup i
 //    runs on XCD i%8, and the kernel maps it to the (i/8)-th unit of the
 //    (batch, head) groups assigned to that XCD, so every group's K/V is read
@@ -172,7 +173,6 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     constexpr int NC = Gm::NC, NDB = Gm::NDB, TILE = Gm::TILE;
     __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * TILE];
-    int* s_last = (int*)st0;   // merge flag; the stages are idle once the walk is done
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -192,17 +192,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     if (g >= G) return;
     const int b = g / a.H, h = g % a.H;
 
-    int qblk = 0, cb, ce, slot, rt = 0, cidx = -1, first = 0, nch = 0;
+    int qblk = 0, cb, ce, slot, rt = 0;
     bool routed;
     if (it < nru) {
         rt = it / a.r_chunks;
         const int c = it % a.r_chunks;
         cb = c * a.r_chunk_tiles;
         ce = min(a.nb, cb + a.r_chunk_tiles);
-        first = a.r_slot_base + (g * a.n_rt + rt) * a.r_chunks;
-        slot = first + c;
-        nch = a.r_chunks;
-        cidx = a.B * a.n_merges + g * a.n_rt + rt;
+        slot = a.r_slot_base + (g * a.n_rt + rt) * a.r_chunks + c;
         routed = true;
     } else {
         const WorkItem wi = a.items[h * a.items_per_head + (it - nru)];
@@ -211,11 +208,6 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         cb = wi.col_begin;
         ce = wi.col_end;
         slot = wi.slot < 0 ? -1 : b * a.n_slots + wi.slot;
-        if (wi.slot >= 0) {
-            first = b * a.n_slots + wi.first_slot;
-            nch = wi.n_chunks;
-            cidx = b * a.n_merges + wi.merge;
-        }
         routed = false;
     }
     const size_t bh = (size_t)g;
@@ -448,58 +440,78 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
             if (hh == 0) a.ws_lse[(size_t)slot * 64 + rloc] = lse_v;
         }
     }
-    if (slot < 0) return;
-
-    // ---- split row: the last chunk to arrive merges all partials ----
-    __threadfence();      // release this chunk's partial
-    __syncthreads();
-    if (tid == 0) *s_last = atomicAdd(&a.counters[cidx], 1) == nch - 1;
-    __syncthreads();
-    if (!*s_last) return;
-    __threadfence();      // acquire the other chunks' partials
-    {
-        constexpr int DP = D / 2;
-        const int row = tid >> 1, part = tid & 1;
-        const int t2 = query_token(row);
-        if (t2 >= 0) {
-            float mxl = -INFINITY;
-            for (int c = 0; c < nch; ++c) mxl = __builtin_fmaxf(mxl, a.ws_lse[(size_t)(first + c) * 64 + row]);
-            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t2) * D + part * DP;
-            if (mxl == -INFINITY) {
-#pragma unroll
-                for (int d = 0; d < DP; d += 2) *(uint32_t*)(orow + d) = 0u;
-                if (part == 0) a.lse[bh * a.L + t2] = -INFINITY;
-            } else {
-                float acc[DP];
-#pragma unroll
-                for (int d = 0; d < DP; ++d) acc[d] = 0.f;
-                float wsum = 0.f;
-                for (int c = 0; c < nch; ++c) {
-                    const float w = expf(a.ws_lse[(size_t)(first + c) * 64 + row] - mxl);
-                    wsum += w;
-                    const float* src = a.ws_o + ((size_t)(first + c) * 64 + row) * D + part * DP;
-#pragma unroll
-                    for (int d = 0; d < DP; d += 4) {
-                        const float4 v4 = *(const float4*)(src + d);
-                        acc[d] += w * v4.x;
-                        acc[d + 1] += w * v4.y;
-                        acc[d + 2] += w * v4.z;
-                        acc[d + 3] += w * v4.w;
-                    }
-                }
-                const float inv2 = 1.f / wsum;
-#pragma unroll
-                for (int d = 0; d < DP; d += 2) *(uint32_t*)(orow + d) = pack_bf16x2(acc[d] * inv2, acc[d + 1] * inv2);
-                if (part == 0) a.lse[bh * a.L + t2] = mxl + logf(wsum);
-            }
-        }
-    }
-    if (tid == 0) a.counters[cidx] = 0;   // ready for the next call on this workspace
 }
 
-__global__ void zero_i32_kernel(int32_t* p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0;
+// Merge of a split row (global rows, routed tiles): the chunks of the row
+// wrote fp32 partials normalised over their own keys plus their LSE; the row's
+// LSE is the log-sum-exp of the chunk LSEs and O the LSE-weighted mean of the
+// partial outputs.  A chunk with no allowed key has LSE -inf and weight 0; a
+// row with no allowed key at all gets O = 0, LSE = -inf.  Runs as its own
+// launch after the attention kernel, so stream order makes the partials
+// visible without any device-scope fence.  One workgroup per split row,
+// four threads per query row, each owning D/4 columns.
+template <int D>
+__global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
+    constexpr int DP = D / 4;
+    const int u = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int row = tid >> 2, part = tid & 3;
+    int first, nch, t;
+    size_t bh;
+    if (u < a.B * a.n_merges) {
+        const int b = u / a.n_merges;
+        const MergeItem mi = a.merges[u % a.n_merges];
+        bh = (size_t)b * a.H + mi.row / a.nb;
+        first = b * a.n_slots + mi.first_slot;
+        nch = mi.n_chunks;
+        t = (mi.row % a.nb) * 64 + row;
+    } else {
+        const int v = u - a.B * a.n_merges;
+        const int g = v / a.n_rt, rt = v % a.n_rt;
+        bh = (size_t)g;
+        first = a.r_slot_base + (g * a.n_rt + rt) * a.r_chunks;
+        nch = a.r_chunks;
+        const int kk = rt * 64 + row;
+        t = kk < a.n_routed ? a.routed_rows[bh * a.n_routed + kk] : -1;
+        if (t >= a.L) t = -1;   // out-of-range rows are skipped, never dereferenced
+    }
+    if (t < 0) return;
+    const float* lse_p = a.ws_lse + (size_t)first * 64 + row;
+    float mxl = -INFINITY;
+    for (int c = 0; c < nch; ++c) mxl = __builtin_fmaxf(mxl, lse_p[(size_t)c * 64]);
+    uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * DP;
+    if (mxl == -INFINITY) {
+#pragma unroll
+        for (int d = 0; d < DP; d += 2) *(uint32_t*)(orow + d) = 0u;
+        if (part == 0) a.lse[bh * a.L + t] = -INFINITY;
+        return;
+    }
+    float acc[DP];
+#pragma unroll
+    for (int d = 0; d < DP; ++d) acc[d] = 0.f;
+    float wsum = 0.f;
+    for (int c = 0; c < nch; ++c) {
+        const float w = expf(lse_p[(size_t)c * 64] - mxl);
+        wsum += w;
+        const float* src = a.ws_o + ((size_t)(first + c) * 64 + row) * D + part * DP;
+#pragma unroll
+        for (int d = 0; d < DP; d += 4) {
+            const float4 v4 = *(const float4*)(src + d);
+            acc[d] += w * v4.x;
+            acc[d + 1] += w * v4.y;
+            acc[d + 2] += w * v4.z;
+            acc[d + 3] += w * v4.w;
+        }
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int d = 0; d < DP; d += 4) {
+        u32x2_t w2;
+        w2.x = pack_bf16x2(acc[d] * inv, acc[d + 1] * inv);
+        w2.y = pack_bf16x2(acc[d + 2] * inv, acc[d + 3] * inv);
+        *(u32x2_t*)(orow + d) = w2;
+    }
+    if (part == 0) a.lse[bh * a.L + t] = mxl + logf(wsum);
 }
 
 template <int D, int MASK>
@@ -529,12 +541,12 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
     }
     if (e != hipSuccess) return e;
     if (after && (e = hipEventRecord(after, s)) != hipSuccess) return e;
-    return hipSuccess;
-}
-
-hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+    const int64_t units = (int64_t)a.B * a.n_merges + (a.n_routed > 0 ? (int64_t)a.B * a.H * a.n_rt : 0);
+    if (units == 0) return hipSuccess;
+    if (head_dim == 64)
+        hipLaunchKernelGGL(merge_bf16_kernel<64>, dim3((unsigned)units), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(merge_bf16_kernel<128>, dim3((unsigned)units), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -122,23 +122,13 @@ void bsattn_layout_destroy(bsattn_layout* layout);
 
 /* Device workspace bytes needed by bsattn_forward (num_routed == 0) or
  * bsattn_forward_routed (num_routed = k) for this layout, batch and head
- * width: arrival counters and fp32 partial outputs of rows that are split
- * across workgroups (global rows, routed tiles) and merged by log-sum-exp
- * by the last of their chunks to finish.  Written to *bytes (0 when nothing
- * is split).
- * The counters live at the start of the workspace and must be zero when a
- * forward call starts: zero the workspace once (bsattn_workspace_init, or
- * any zero fill) before its first use with a given (layout, batch,
- * head_dim, num_routed); every completed forward call leaves them zero
- * again.  Forward calls sharing a workspace must not overlap in time. */
+ * width: the fp32 partial outputs and partial LSEs of rows that are split
+ * across workgroups (global rows, routed tiles), which a second kernel of the
+ * same call merges by log-sum-exp.  Written to *bytes (0 when nothing is
+ * split).  The workspace needs no initialisation and holds nothing between
+ * calls; calls that share one must not overlap in time. */
 bsattn_status bsattn_workspace_size(const bsattn_layout* layout, int32_t batch,
                                     int32_t head_dim, int32_t num_routed, size_t* bytes);
-
-/* Zero the counter area of `workspace` on `stream` (a fill kernel, no
- * hipMemset).  Same size arguments as bsattn_workspace_size. */
-bsattn_status bsattn_workspace_init(const bsattn_layout* layout, int32_t batch, int32_t head_dim,
-                                    int32_t num_routed, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream);
 
 /* Block-sparse attention forward.
  *   layout         uploaded layout with num_heads == H and seq_len == L.
@@ -152,8 +142,8 @@ bsattn_status bsattn_workspace_init(const bsattn_layout* layout, int32_t batch, 
  *                  Query rows past the valid length are computed normally.
  *   scale          score scale (1/sqrt(D) for the usual attention).
  *   workspace      device buffer of at least bsattn_workspace_size() bytes,
- *                  256-byte aligned, counters zeroed (see bsattn_workspace_size;
- *                  may be NULL if that size is 0).
+ *                  256-byte aligned, any contents (may be NULL if that size
+ *                  is 0).
  * Enqueued on `stream`; no synchronisation. */
 bsattn_status bsattn_forward(const bsattn_layout* layout, bsattn_dtype dtype,
                              int32_t batch, int32_t num_heads, int32_t seq_len, int32_t head_dim,

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert names == sorted([
         "bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr", "bsattn_layout_upload",
-        "bsattn_layout_build_device", "bsattn_layout_destroy", "bsattn_workspace_size", "bsattn_workspace_init",
+        "bsattn_layout_build_device", "bsattn_layout_destroy", "bsattn_workspace_size",
         "bsattn_forward",
         "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
         "bsattn_last_error"])
@@ -68,9 +68,8 @@ def test_band_layout_rejects():
 def test_workspace_size_and_destroy():
     lay = bs.bsattn_make_layout(12, 8192, 64, 3, [0, 127], 3, 2)
     n = bs.bsattn_workspace_size(lay, 2, 64)
-    # 2 dense rows per head, 128 blocks each -> 8 chunks of 16; slots of 64 x (64+1) floats,
-    # after 2 x 24 split-row counters rounded up to 64 ints
-    assert n == 64 * 4 + 2 * 12 * 2 * 8 * 64 * 65 * 4
+    # 2 dense rows per head, 128 blocks each -> 8 chunks of 16; slots of 64 x (64+1) floats
+    assert n == 2 * 12 * 2 * 8 * 64 * 65 * 4
     assert bs.bsattn_workspace_size(lay, 2, 64, num_routed=64) > n
     with pytest.raises(bs.BsattnError):
         bs.bsattn_workspace_size(lay, 2, 96)

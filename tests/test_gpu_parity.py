@@ -317,17 +317,16 @@ def test_edge_long_global_rows_many_chunks():
     _edge(1, L, 64, "bf16", 3, [0, 599], 1, 9, tag="nb=600 global rows", rows=rows)
 
 
-def test_workspace_reused_across_calls_and_init():
-    """Split-row counters return to zero after every call: one workspace serves many calls,
-    and bsattn_workspace_init makes a dirty buffer usable."""
+def test_workspace_dirty_and_reused():
+    """The workspace needs no initialisation: a buffer full of NaN serves, and one buffer
+    serves consecutive calls with identical results."""
     wl = WORKLOADS["bigbird-L2048"].with_(batch=2, heads=2)
     _say("workspace reuse", wl)
     inp = make_inputs(wl)
     lay, olay = _layouts(wl)
     dev = {k: v.cuda() for k, v in inp.items()}
     n = bs.bsattn_workspace_size(lay, wl.batch, wl.head_dim)
-    ws = torch.full(((n + 255) // 4,), 7.0, dtype=torch.float32, device="cuda")   # dirty
-    bs.bsattn_workspace_init(lay, wl.batch, wl.head_dim, 0, ws)
+    ws = torch.full(((n + 255) // 4,), float("nan"), dtype=torch.float32, device="cuda")   # dirty
     outs = []
     for _ in range(3):
         out, lse = bs.forward(dev["q"], dev["k"], dev["v"], lay, scale=wl.scale, workspace=ws)
