@@ -3,6 +3,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <functional>
+#include <queue>
 #include <cstdarg>
 #include <cstdio>
 #include <new>
@@ -93,8 +95,15 @@ void free_device(bsattn_layout* lay) {
         (void)hipFree(lay->d_col_idx);
         (void)hipFree(lay->d_items);
         (void)hipFree(lay->d_merges);
+        for (auto& sc : lay->scheds) {
+            (void)hipFree(sc.d_units);
+            (void)hipFree(sc.d_unit_ptr);
+            (void)hipFree(sc.d_tiles);
+            (void)hipFree(sc.d_tile_ptr);
+        }
         if (cur >= 0 && cur != lay->device) (void)hipSetDevice(cur);
     }
+    lay->scheds.clear();
     lay->d_row_ptr = lay->d_col_idx = nullptr;
     lay->d_items = nullptr;
     lay->d_merges = nullptr;
@@ -148,6 +157,153 @@ void routed_split(int32_t nb, int32_t k, int32_t* n_rt, int32_t* r_chunks, int32
     *n_rt = (k + kBlock - 1) / kBlock;
     split_row(nb, r_chunks, per);
     *r_chunks = (nb + *per - 1) / *per;
+}
+
+// Workgroups of the bf16 kernel that one device holds at once (CUs x
+// resident workgroups per CU), cached per device and head width.
+int device_capacity(int dev, int32_t D) {
+    static std::mutex mu;
+    static std::vector<int> cache;   // index 2 * dev + (D == 128)
+    std::lock_guard<std::mutex> g(mu);
+    const size_t idx = 2 * (size_t)dev + (D == 128 ? 1 : 0);
+    if (cache.size() <= idx) cache.resize(idx + 1, 0);
+    if (cache[idx] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 1;
+        cache[idx] = cus * fwd_bf16_ctas_per_cu(D);
+    }
+    return cache[idx];
+}
+
+// Persistent schedule for one call shape.  Each (batch, head) group gets
+// n_bins workgroups -- as many as fill the device once, when the groups are
+// dealt 8 per XCD -- and the group's units (the head's items, plus the routed
+// chunks) are packed into the bins longest-processing-time first: each unit,
+// by decreasing cost, goes to the least loaded bin.  A unit's cost is its
+// tile count plus a fixed overhead for loading Q and writing O.  Row lengths
+// do not depend on the head for the supported layouts, so one packing serves
+// every head (the cost of position k is the longest item at k over all heads;
+// positions empty in every head are dropped).  For every (head, bin) the
+// device gets the unit records and the flat list of the units' key blocks in
+// order, at most kMaxBinUnits units and kMaxBinTiles tiles per bin.
+bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32_t nru, int32_t rct,
+                           int32_t r_chunks, hipStream_t stream, bsattn_layout::Sched* out) {
+    const int32_t ipH = lay->items_per_head;
+    std::vector<int32_t> unit_id, cost;
+    for (int32_t k = 0; k < ipH; ++k) {
+        int32_t len = 0;
+        for (int32_t h = 0; h < lay->H; ++h) {
+            const WorkItem& wi = lay->items[(size_t)h * ipH + k];
+            if (wi.row >= 0) len = std::max(len, wi.col_end - wi.col_begin);
+        }
+        if (len == 0) continue;
+        unit_id.push_back(k);
+        cost.push_back(len + 2);
+    }
+    auto routed_len = [&](int32_t v) {
+        const int32_t c = v % r_chunks;
+        return std::min(lay->nb, c * rct + rct) - c * rct;
+    };
+    for (int32_t v = 0; v < nru; ++v) {
+        unit_id.push_back(-1 - v);
+        cost.push_back(routed_len(v) + 2);
+    }
+    const int32_t U = (int32_t)unit_id.size();
+    int64_t tiles_head = 0;
+    for (int32_t c : cost) tiles_head += c - 2;
+    const int64_t G8 = (int64_t)kXcds * (((int64_t)B * lay->H + kXcds - 1) / kXcds);
+    int64_t q = device_capacity(lay->device, D) / G8;
+    q = std::max<int64_t>(q, (U + kMaxBinUnits - 1) / kMaxBinUnits);
+    q = std::max<int64_t>(q, (tiles_head + kMaxBinTiles / 2 - 1) / (kMaxBinTiles / 2));
+    q = std::min<int64_t>(q, std::max<int32_t>(U, 1));
+    int32_t n_bins = (int32_t)std::max<int64_t>(q, 1);
+
+    std::lock_guard<std::mutex> guard(*lay->sched_mu);
+    for (const auto& sc : lay->scheds)
+        if (sc.n_bins == n_bins && sc.nru == nru && sc.rct == rct) {
+            *out = sc;
+            return BSATTN_OK;
+        }
+    std::vector<int32_t> order((size_t)U);
+    for (int32_t u = 0; u < U; ++u) order[(size_t)u] = u;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return cost[(size_t)x] > cost[(size_t)y]; });
+    std::vector<std::vector<int32_t>> bins;
+    for (;;) {
+        bins.assign((size_t)n_bins, {});
+        std::vector<int64_t> tiles_in((size_t)n_bins, 0);
+        using Load = std::pair<int64_t, int32_t>;   // (load, bin), least loaded first, then lowest bin
+        std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+        for (int32_t i = 0; i < n_bins; ++i) heap.push({0, i});
+        for (int32_t u : order) {
+            Load t = heap.top();
+            heap.pop();
+            bins[(size_t)t.second].push_back(u);
+            tiles_in[(size_t)t.second] += cost[(size_t)u] - 2;
+            heap.push({t.first + cost[(size_t)u], t.second});
+        }
+        bool fits = true;
+        for (int32_t i = 0; i < n_bins; ++i)
+            fits = fits && bins[(size_t)i].size() <= (size_t)kMaxBinUnits && tiles_in[(size_t)i] <= kMaxBinTiles;
+        if (fits) break;
+        if (n_bins >= U) return fail(BSATTN_ERR_UNSUPPORTED, "a single row exceeds the per-workgroup tile list");
+        n_bins = std::min(U, n_bins * 2);
+    }
+    // per (head, bin): unit records and flat tile lists
+    std::vector<int2> units;
+    std::vector<int32_t> unit_ptr(1, 0), tiles, tile_ptr(1, 0);
+    for (int32_t h = 0; h < lay->H; ++h)
+        for (int32_t i = 0; i < n_bins; ++i) {
+            int32_t k = 0;
+            for (int32_t u : bins[(size_t)i]) {
+                const int32_t id = unit_id[(size_t)u];
+                int32_t n = 0, first = 0;
+                bool routed = id < 0;
+                if (!routed) {
+                    const WorkItem& wi = lay->items[(size_t)h * ipH + id];
+                    if (wi.row < 0) continue;   // empty in this head
+                    units.push_back(make_int2(wi.row % lay->nb, wi.slot));
+                    n = wi.col_end - wi.col_begin;
+                    first = wi.col_begin;
+                } else {
+                    const int32_t v = -1 - id;
+                    units.push_back(make_int2(-1 - v / r_chunks, v % r_chunks));
+                    n = routed_len(v);
+                    first = (v % r_chunks) * rct;
+                }
+                for (int32_t t = 0; t < n; ++t) {
+                    const int32_t j = routed ? first + t : lay->col_idx[(size_t)first + t];
+                    tiles.push_back(j | (k << kTileUnitShift) | (t == 0 ? kTileFirst : 0) | (t == n - 1 ? kTileLast : 0));
+                }
+                ++k;
+            }
+            unit_ptr.push_back((int32_t)units.size());
+            tile_ptr.push_back((int32_t)tiles.size());
+        }
+    if (units.empty()) units.push_back(make_int2(0, -1));
+    if (tiles.empty()) tiles.push_back(0);
+    bsattn_layout::Sched sc{n_bins, nru, rct, nullptr, nullptr, nullptr, nullptr};
+    void* p[4] = {nullptr, nullptr, nullptr, nullptr};
+    const void* src[4] = {units.data(), unit_ptr.data(), tiles.data(), tile_ptr.data()};
+    const size_t sz[4] = {units.size() * sizeof(int2), unit_ptr.size() * sizeof(int32_t),
+                          tiles.size() * sizeof(int32_t), tile_ptr.size() * sizeof(int32_t)};
+    hipError_t e = hipSuccess;
+    for (int a = 0; a < 4 && e == hipSuccess; ++a) {
+        e = hipMalloc(&p[a], sz[a]);
+        if (e == hipSuccess) e = hipMemcpyAsync(p[a], src[a], sz[a], hipMemcpyHostToDevice, stream);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        for (int a = 0; a < 4; ++a) (void)hipFree(p[a]);
+        return fail(BSATTN_ERR_NO_MEMORY, "schedule upload: %s", hipGetErrorString(e));
+    }
+    sc.d_units = (int2*)p[0];
+    sc.d_unit_ptr = (int32_t*)p[1];
+    sc.d_tiles = (int32_t*)p[2];
+    sc.d_tile_ptr = (int32_t*)p[3];
+    lay->scheds.push_back(sc);
+    *out = sc;
+    return BSATTN_OK;
 }
 
 }  // namespace
@@ -378,8 +534,6 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
             return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     }
-    if ((int64_t)kXcds * (((int64_t)B * H + kXcds - 1) / kXcds) * lay->items_per_head >= ((int64_t)1 << 31))
-        return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
 
     FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
@@ -407,6 +561,14 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
         if (e != hipSuccess) return hip_fail(e, "fp32 forward launch");
         return ok();
     }
+    bsattn_layout::Sched sc{};
+    st = get_schedule(lay, B, D, 0, 1, 1, stream, &sc);
+    if (st != BSATTN_OK) return st;
+    a.n_bins = sc.n_bins;
+    a.units = sc.d_units;
+    a.unit_ptr = sc.d_unit_ptr;
+    a.tiles = sc.d_tiles;
+    a.tile_ptr = sc.d_tile_ptr;
     e = launch_fwd_bf16(a, D, mask, stream, g_ev_before, g_ev_after);
     if (e != hipSuccess) return hip_fail(e, "bf16 forward launch");
     return ok();
@@ -448,8 +610,7 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* lay, bsattn_dtype dtype
 
     int32_t n_rt, rch, per;
     routed_split(lay->nb, num_routed, &n_rt, &rch, &per);
-    const int64_t grid = (int64_t)kXcds * (((int64_t)B * H + kXcds - 1) / kXcds) * (lay->items_per_head + (int64_t)n_rt * rch);
-    if (grid >= ((int64_t)1 << 31)) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+    if ((int64_t)n_rt * rch > (1 << 24)) return fail(BSATTN_ERR_UNSUPPORTED, "too many routed tiles");
 
     FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
@@ -471,6 +632,14 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* lay, bsattn_dtype dtype
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
 
+    bsattn_layout::Sched sc{};
+    st = get_schedule(lay, B, D, n_rt * rch, per, rch, stream, &sc);
+    if (st != BSATTN_OK) return st;
+    a.n_bins = sc.n_bins;
+    a.units = sc.d_units;
+    a.unit_ptr = sc.d_unit_ptr;
+    a.tiles = sc.d_tiles;
+    a.tile_ptr = sc.d_tile_ptr;
     hipError_t e = launch_fwd_bf16(a, D, MASK_BAND, stream, g_ev_before, g_ev_after);
     if (e != hipSuccess) return hip_fail(e, "routed forward launch");
     return ok();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <memory>
+#include <mutex>
 #include <vector>
 
 #include "bsattn.h"
@@ -34,7 +36,14 @@ struct MergeItem {
     int32_t row, first_slot, n_chunks, pad;
 };
 
-constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+constexpr int kXcds = 8;
+constexpr int kMaxBinUnits = 64;     // units of one workgroup (one per lane)
+constexpr int kMaxBinTiles = 1024;   // tiles of one workgroup (its list lives in LDS)
+// Flat tile entry of a workgroup's list: key block | unit << 20 | first | last.
+constexpr int kTileJ = (1 << 20) - 1;
+constexpr int kTileUnitShift = 20;
+constexpr int kTileFirst = 1 << 29;
+constexpr int kTileLast = 1 << 30;   // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 
 // Chunking of a row of `len` tiles: number of chunks and tiles per chunk
 // (at most 64 tiles per chunk: a chunk's key-block list fits one wave's lanes).
@@ -63,6 +72,17 @@ struct FwdArgs {
     const int32_t* routed_rows;
     int32_t n_items, n_merges;
     int32_t items_per_head;   // explicit items per head (NOP-padded to equal length)
+    // persistent schedule: n_bins workgroups per group.  Workgroup (h, bin)
+    // runs units units[unit_ptr[h*n_bins+bin] ..) -- {kind, slot}: kind >= 0
+    // the query block of a layout row (slot: partial slot within a batch
+    // entry, -1 for a whole row), kind < 0 routed tile -1-kind (slot: chunk)
+    // -- over the flat tile list tiles[tile_ptr[h*n_bins+bin] ..), entries
+    // key block | unit << 20 | kTileFirst | kTileLast.
+    int32_t n_bins;
+    const int2* units;
+    const int32_t* unit_ptr;
+    const int32_t* tiles;
+    const int32_t* tile_ptr;
     int32_t B, H, L, nb, n_slots;
     // routed tiles (gathered query rows over all key blocks), placed first in the grid
     int32_t n_routed;         // k rows per (b, h); 0 = no routed tiles
@@ -78,6 +98,7 @@ struct FwdArgs {
 // ---- launchers (defined in kernels/*.hip) ----
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s,
                            hipEvent_t before, hipEvent_t after);
+int fwd_bf16_ctas_per_cu(int head_dim);   // workgroups of the bf16 kernel resident per CU
 hipError_t launch_fwd_f32(const FwdArgs& a, const int32_t* row_ptr, int head_dim, int mask,
                           hipStream_t s, hipEvent_t before, hipEvent_t after);
 hipError_t launch_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,
@@ -104,4 +125,15 @@ struct bsattn_layout {
     int32_t* d_col_idx = nullptr;
     bsattn::WorkItem* d_items = nullptr;
     bsattn::MergeItem* d_merges = nullptr;
+    // persistent schedules built on first use, keyed by (bins per group,
+    // routed units per group, tiles per routed unit); device arrays
+    struct Sched {
+        int32_t n_bins, nru, rct;
+        int2* d_units;
+        int32_t* d_unit_ptr;
+        int32_t* d_tiles;
+        int32_t* d_tile_ptr;
+    };
+    mutable std::vector<Sched> scheds;
+    mutable std::unique_ptr<std::mutex> sched_mu{new std::mutex};
 };

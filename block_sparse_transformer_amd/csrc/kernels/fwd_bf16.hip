@@ -51,6 +51,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "../internal.h"
 
@@ -117,24 +118,28 @@ struct Geo {
     static constexpr int NDB = D / 32;                   // 32-row blocks of O^T
 };
 
-// One direct global -> LDS load of 16 bytes per lane from sbase + voff: lane
-// i's bytes land at LDS byte address lds + 16 i (sbase and lds are
-// wave-uniform SGPR values, voff a per-lane byte offset).  Written as inline
-// asm so that the compiler does not track it: the only waits on these loads
-// are the explicit vmcnt waits of the pipeline (the compiler's own LDS-DMA
-// alias tracking inserts full drains at loop headers).  The instruction
-// writes no register; M0 is saved and restored around it, with the wait
-// state M0 needs before an LDS load.
-__device__ __forceinline__ void lds_load16(uint32_t voff, const void* sbase, uint32_t lds) {
+// Four direct global -> LDS loads of 16 bytes per lane: load r reads
+// sbase + voff[r] + imm_r and writes LDS byte address m0v + imm_r + 16 lane,
+// imm_r = 2048 r - 4096 (the instruction offset moves both addresses, so the
+// four 2 KB pieces land at m0v - 4096 .. m0v + 4095 with one M0 setting).
+// Written as inline asm so that the compiler does not track the loads: the
+// only waits on them are the explicit vmcnt waits of the pipeline (the
+// compiler's own LDS-DMA alias tracking inserts full drains at loop headers).
+// The instructions write no register; M0 is saved and restored around them,
+// with the wait state M0 needs before an LDS load.
+__device__ __forceinline__ void lds_load16x4(const uint32_t (&voff)[4], const void* sbase, uint32_t m0v) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
+        "s_mov_b32 m0, %5\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
+        "global_load_lds_dwordx4 %1, %6 offset:-4096\n\t"
+        "global_load_lds_dwordx4 %2, %6 offset:-2048\n\t"
+        "global_load_lds_dwordx4 %3, %6\n\t"
+        "global_load_lds_dwordx4 %4, %6 offset:2048\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(voff), "s"(sbase), "s"(lds)
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(m0v), "s"(sbase)
         : "memory");
 }
 
@@ -147,32 +152,37 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ int swz_k(int row, int piece) { return piece ^ (row & 7); }
 __device__ __forceinline__ int swz_v(int row, int piece) { return piece ^ ((row & 3) << 1); }
 
-// Direct loads of key block j into one LDS stage [K tile | V tile].  Each wave
-// instruction fills 1 KB of LDS contiguously (lane i -> +16 i); lane i loads
-// the global piece that the swizzle places at that slot, and the 8 (16) lanes
-// covering one row read the whole 128 (256) byte row.  Per-lane byte offsets
-// are fixed for the whole walk (koffs/voffs); the tile base and the LDS
-// destination are scalars, so a load costs no vector ALU work.
+// Direct loads of one K (or V) tile -- key block j -- into an LDS buffer.
+// Each wave instruction fills 2 KB of LDS contiguously (lane i -> +16 i,
+// the two waves interleaved 1 KB apart); lane i loads the global piece that
+// the swizzle places at that slot, so the lanes covering one row read the
+// whole 128 (256) byte row.  Per-lane byte offsets are fixed for the whole
+// walk; the tile base and the LDS destination are scalars, so a tile costs
+// no vector ALU work.
 template <int D>
-__device__ __forceinline__ void issue_tile(const uint16_t* kp, const uint16_t* vp, int j,
-                                           const uint32_t (&koffs)[Geo<D>::LPT],
-                                           const uint32_t (&voffs)[Geo<D>::LPT], uint32_t lds_wave) {
-    using Gm = Geo<D>;
-    const uint16_t* kt = kp + (size_t)j * 64 * D;
-    const uint16_t* vt = vp + (size_t)j * 64 * D;
+__device__ __forceinline__ void issue_half(const uint16_t* base, int j, const uint32_t (&offs)[Geo<D>::LPT],
+                                           uint32_t lds_wave) {
+    static_assert(Geo<D>::LPT % 4 == 0, "loads come in groups of four");
+    const uint16_t* t = base + (size_t)j * 64 * D;
 #pragma unroll
-    for (int r = 0; r < Gm::LPT; ++r) {
-        lds_load16(koffs[r], kt, lds_wave + r * kThreads * 16);
-        lds_load16(voffs[r], vt, lds_wave + 2 * Gm::TILE + r * kThreads * 16);
+    for (int r = 0; r < Geo<D>::LPT; r += 4) {
+        const uint32_t o4[4] = {offs[r], offs[r + 1], offs[r + 2], offs[r + 3]};
+        lds_load16x4(o4, t, lds_wave + r * kThreads * 16 + 4096);
     }
 }
+
+__device__ __forceinline__ int tile_j(int e) { return e & kTileJ; }
+__device__ __forceinline__ int tile_unit(int e) { return (e >> kTileUnitShift) & (kMaxBinUnits - 1); }
 
 template <int D, int MASK>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     using Gm = Geo<D>;
     constexpr int NC = Gm::NC, NDB = Gm::NDB, TILE = Gm::TILE;
-    __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * TILE];
+    // K ring and V ring, two tiles each, and the workgroup's tile list.
+    __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2 * TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vbuf[2 * TILE];
+    __shared__ int flat[kMaxBinTiles];
+    __shared__ int s_count;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -181,77 +191,120 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     const int hh = lane >> 5;
     const int rloc = wave * 32 + ql;  // this lane's query row within the tile
 
-    // ---- decode: XCD x = blockIdx % 8 runs groups g = x, x+8, ... in order ----
+    // ---- this workgroup: bin `bin` of group g = (b, h).  Workgroup i runs on
+    // XCD i % 8, which serves groups x, x + 8, ... so a group's K/V stays in
+    // one XCD's L2.  The grid is sized to be resident at once; every bin holds
+    // a balanced list of units (rows, chunks of split rows, routed tiles).
     const int G = a.B * a.H;
-    const int nru = a.n_routed > 0 ? a.n_rt * a.r_chunks : 0;   // routed units per group
-    const int per_group = nru + a.items_per_head;
     const int x = blockIdx.x % kXcds;
     const int p = blockIdx.x / kXcds;
-    const int g = x + kXcds * (p / per_group);
-    const int it = p % per_group;
+    const int g = x + kXcds * (p / a.n_bins);
+    const int bin = p % a.n_bins;
     if (g >= G) return;
     const int b = g / a.H, h = g % a.H;
-
-    int qblk = 0, cb, ce, slot, rt = 0;
-    bool routed;
-    if (it < nru) {
-        rt = it / a.r_chunks;
-        const int c = it % a.r_chunks;
-        cb = c * a.r_chunk_tiles;
-        ce = min(a.nb, cb + a.r_chunk_tiles);
-        slot = a.r_slot_base + (g * a.n_rt + rt) * a.r_chunks + c;
-        routed = true;
-    } else {
-        const WorkItem wi = a.items[h * a.items_per_head + (it - nru)];
-        if (wi.row < 0) return;
-        qblk = wi.row % a.nb;
-        cb = wi.col_begin;
-        ce = wi.col_end;
-        slot = wi.slot < 0 ? -1 : b * a.n_slots + wi.slot;
-        routed = false;
-    }
     const size_t bh = (size_t)g;
+    const int hb = h * a.n_bins + bin;
+    const int up0 = a.unit_ptr[hb], nu = a.unit_ptr[hb + 1] - up0;   // <= 64
+    const int tp0 = a.tile_ptr[hb], nt = a.tile_ptr[hb + 1] - tp0;   // <= kMaxBinTiles
 
-    auto query_token = [&](int r) -> int {   // token of tile row r (-1: unused routed row)
-        if (!routed) return qblk * 64 + r;
-        const int kk = rt * 64 + r;
-        const int t = kk < a.n_routed ? a.routed_rows[bh * a.n_routed + kk] : -1;
-        return (t >= a.L) ? -1 : t;          // out-of-range rows are skipped, never dereferenced
-    };
-    const int tq = query_token(rloc);
-
-    // Key blocks of this item, one per lane (<= 64 by construction of the schedule).
-    int n = ce - cb;
-    const int colv = lane < n ? (routed ? cb + lane : a.col_idx[cb + lane]) : 0;
-    int valid = a.L;
-    if (MASK == MASK_PAD) {
-        valid = min(max(a.valid_len[b], 0), a.L);
-        // ascending blocks: keep those that start before the valid length
-        n = __builtin_popcountll(__ballot(lane < n && colv * 64 < valid));
+    // Unit table, lane k describing unit k: kind >= 0 query block of a layout
+    // row, kind < 0 routed tile -1-kind; slot -1 writes O/LSE, >= 0 a partial.
+    int u_kind = 0, u_slot = -1;
+    if (lane < nu) {
+        const int2 r = a.units[up0 + lane];
+        u_kind = r.x;
+        if (r.x >= 0) u_slot = r.y < 0 ? -1 : b * a.n_slots + r.y;
+        else u_slot = a.r_slot_base + (g * a.n_rt + (-1 - r.x)) * a.r_chunks + r.y;
     }
-    auto tile_of = [&](int t) -> int { return __builtin_amdgcn_readlane(colv, t); };
+    auto rd = [](int v, int k) -> int { return __builtin_amdgcn_readlane(v, k); };
+
+    int valid = a.L;
+    if (MASK == MASK_PAD) valid = min(max(a.valid_len[b], 0), a.L);
 
     const uint16_t* qp = (const uint16_t*)a.q + bh * (size_t)a.L * D;
     const uint16_t* kp = (const uint16_t*)a.k + bh * (size_t)a.L * D;
     const uint16_t* vp = (const uint16_t*)a.v + bh * (size_t)a.L * D;
 
-    // Q^T fragments (B operand of S^T): lane (ql, hh) holds Q[row][16c + 8hh .. +7].
-    bf16x8_t qf[NC];
+    // token of this lane's query row in a unit of kind `kind` (-1: unused routed row)
+    auto query_token = [&](int kind) -> int {
+        if (kind >= 0) return kind * 64 + rloc;
+        const int kk = (-1 - kind) * 64 + rloc;
+        const int t = kk < a.n_routed ? a.routed_rows[bh * a.n_routed + kk] : -1;
+        return (t >= a.L) ? -1 : t;          // out-of-range rows are skipped, never dereferenced
+    };
+    // Q^T fragments of a row (B operand of S^T): lane (ql, hh) holds Q[t][16c + 8hh .. +7].
+    auto load_q = [&](int t, bf16x8_t (&qf)[NC]) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        u32x4_t u = {0u, 0u, 0u, 0u};
-        if (tq >= 0) u = *(const u32x4_t*)(qp + (size_t)tq * D + 16 * c + 8 * hh);
-        qf[c] = as_bf16x8(u);
-    }
+        for (int c = 0; c < NC; ++c) {
+            u32x4_t u = {0u, 0u, 0u, 0u};
+            if (t >= 0) u = *(const u32x4_t*)(qp + (size_t)t * D + 16 * c + 8 * hh);
+            qf[c] = as_bf16x8(u);
+        }
+    };
+    // Write a unit's result: O row (bf16) and LSE, or an fp32 partial and its LSE.
+    auto store_unit = [&](int slot, int t, int r, const f32x16_t (&ov)[NDB], float inv, float lse_v) {
+        if (t < 0) return;
+        // O^T register i of block db <-> d = 32db + 8(i/4) + 4hh + i%4
+        if (slot < 0) {
+            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    u32x2_t w;
+                    w.x = pack_bf16x2(ov[db][4 * gq + 0] * inv, ov[db][4 * gq + 1] * inv);
+                    w.y = pack_bf16x2(ov[db][4 * gq + 2] * inv, ov[db][4 * gq + 3] * inv);
+                    *(u32x2_t*)(orow + 32 * db + 8 * gq + 4 * hh) = w;
+                }
+            if (hh == 0) a.lse[bh * a.L + t] = lse_v;
+        } else {
+            float* orow = a.ws_o + ((size_t)slot * 64 + r) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    *(float4*)(orow + 32 * db + 8 * gq + 4 * hh) =
+                        make_float4(ov[db][4 * gq] * inv, ov[db][4 * gq + 1] * inv, ov[db][4 * gq + 2] * inv,
+                                    ov[db][4 * gq + 3] * inv);
+            if (hh == 0) a.ws_lse[(size_t)slot * 64 + r] = lse_v;
+        }
+    };
 
-    f32x16_t o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    float m = -INFINITY;   // running (lazily raised) max of scaled scores, log2 units
-    float l = 0.f;         // sum of this lane's probabilities
-    const float c2 = a.scale_log2;
+    // ---- the bin's tile list -> LDS.  With a key-padding mask, tiles that
+    // start at or past the valid length are dropped (a unit's blocks ascend, so
+    // it keeps a prefix) and a unit left with no tile is written as empty
+    // (O = 0, LSE = -inf) right here.
+    int F = nt;
+    uint64_t empty_units = 0;
+    if (MASK != MASK_PAD) {
+        for (int i = tid; i < nt; i += kThreads) flat[i] = a.tiles[tp0 + i];
+    } else {
+        // both waves scan the list (wave 0 writes it) and write their half of empty units
+        int kept_total = 0;
+        for (int base = 0; base < nt; base += 64) {
+            const int i = base + lane;
+            const int e = i < nt ? a.tiles[tp0 + i] : 0;
+            const int en = i + 1 < nt ? a.tiles[tp0 + i + 1] : 0;
+            const bool keep = i < nt && tile_j(e) * 64 < valid;
+            const bool keep_next = i + 1 < nt && !(e & kTileLast) && tile_j(en) * 64 < valid;
+            const uint64_t km = __ballot(keep);
+            const int pos = kept_total + __builtin_popcountll(km & ((1ull << lane) - 1ull));
+            if (wave == 0 && keep) flat[pos] = keep_next ? (e & ~kTileLast) : (e | kTileLast);
+            const uint64_t em = __ballot(i < nt && (e & kTileFirst) && !keep);
+            for (uint64_t mm = em; mm; mm &= mm - 1) empty_units |= 1ull << tile_unit(rd(e, __builtin_ctzll(mm)));
+            kept_total += __builtin_popcountll(km);
+        }
+        F = kept_total;
+        const f32x16_t zero[NDB] = {};
+        for (uint64_t mm = empty_units; mm; mm &= mm - 1) {
+            const int u = __builtin_ctzll(mm);
+            store_unit(rd(u_slot, u), query_token(rd(u_kind, u)), rloc, zero, 0.f, -INFINITY);
+        }
+    }
+    __syncthreads();
+    if (F == 0) return;
+    // units with at least one tile (those without were written above)
+    const uint64_t live_units = (nu >= 64 ? ~0ull : ((1ull << nu) - 1ull)) & ~empty_units;
 
     // Per-lane LDS offsets (elements) of the fragment reads, fixed for the whole walk.
     int koff[2][NC];
@@ -278,30 +331,42 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                 const int d0 = 32 * db + 16 * gsel + 4 * (gi & 3);
                 voff[c][db][e2] = row * D + swz_v(row, d0 >> 3) * 8 + (d0 & 7);
             }
-
-    // Direct-load byte offsets of this thread's pieces (fixed for the whole walk)
-    // and the wave's LDS destinations in each stage.
+    // Direct-load byte offsets of this thread's pieces, and the wave's LDS
+    // destinations in each ring buffer.
     uint32_t koffs[Gm::LPT], voffs[Gm::LPT];
 #pragma unroll
     for (int r = 0; r < Gm::LPT; ++r) {
-        const int slot = r * kThreads + tid;
-        const int row = slot / Gm::PIECES, q = slot % Gm::PIECES;
-        koffs[r] = (uint32_t)(row * D + swz_k(row, q) * 8) * 2u;
-        voffs[r] = (uint32_t)(row * D + swz_v(row, q) * 8) * 2u;
+        const int sl = r * kThreads + tid;
+        const int row = sl / Gm::PIECES, q = sl % Gm::PIECES;
+        // minus the instruction offset 2048 (r % 4) - 4096 that the load adds
+        koffs[r] = (uint32_t)(row * D + swz_k(row, q) * 8) * 2u + 4096u - 2048u * (r % 4);
+        voffs[r] = (uint32_t)(row * D + swz_v(row, q) * 8) * 2u + 4096u - 2048u * (r % 4);
     }
     const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(wave * 64 * 16);
-    const uint32_t lds0 = lds_addr(st0) + wave_lds, lds1 = lds_addr(st1) + wave_lds;
+    const uint32_t kl0 = lds_addr(kbuf) + wave_lds, vl0 = lds_addr(vbuf) + wave_lds;
 
-    auto compute = [&](int t, const uint16_t* Ks) {
-        const uint16_t* Vs = Ks + TILE;
-        const int j = tile_of(t);
-        // S^T (keys x queries): s[kb] register i <-> key 32kb + 8(i/4) + 4hh + i%4.
-        bf16x8_t kf[2][NC];
+    const float c2 = a.scale_log2;
+    f32x16_t o[NDB];
+    float m = -INFINITY;   // running (lazily raised) max of scaled scores, log2 units
+    float l = 0.f;         // sum of this lane's probabilities
+    auto reset = [&]() {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+        m = -INFINITY;
+        l = 0.f;
+    };
+
+    // K fragments of the tile at Ks (A operand of S^T = K Q^T).
+    auto kread = [&](const uint16_t* Ks, bf16x8_t (&kf)[2][NC]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int c = 0; c < NC; ++c) kf[kb][c] = as_bf16x8(*(const u32x4_t*)(Ks + koff[kb][c]));
-        f32x16_t s[2];
+    };
+    // S^T = K Q^T: s[kb] register i <-> key 32kb + 8(i/4) + 4hh + i%4.
+    auto smma = [&](const bf16x8_t (&kf)[2][NC], const bf16x8_t (&q)[NC], f32x16_t (&s)[2]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -309,28 +374,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][c], qf[c], s[kb], 0, 0, 0);
-        if (MASK == MASK_PAD) {
-            if (j * 64 + 64 > valid) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) s[kb][i] = -INFINITY;
-            }
-        }
-        if (MASK == MASK_BAND) {
-            if (!routed) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (abs(tq - (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4))) > a.band)
-                            s[kb][i] = -INFINITY;
-            }
-        }
-        // V^T fragments for the PV product, read while the softmax runs.
-        bf16x8_t va[4][NDB];
+            for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][c], q[c], s[kb], 0, 0, 0);
+    };
+    // V^T fragments of the tile at Vs (A operand of O^T = V^T P^T).
+    auto vread = [&](const uint16_t* Vs, bf16x8_t (&va)[4][NDB]) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -343,7 +390,29 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                 const u32x4_t lh = {l2.x, l2.y, h2.x, h2.y};
                 va[c][db] = as_bf16x8(lh);
             }
-
+    };
+    // Online softmax, first half: mask the tile's scores (key block j), raise
+    // the running max lazily (rescaling O and l), return the max to subtract.
+    auto softmax_max = [&](int j, int kind, int tq, f32x16_t (&s)[2]) -> float {
+        if (MASK == MASK_PAD) {
+            if (j * 64 + 64 > valid) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) s[kb][i] = -INFINITY;
+            }
+        }
+        if (MASK == MASK_BAND) {
+            if (kind >= 0) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (abs(tq - (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4))) > a.band)
+                            s[kb][i] = -INFINITY;
+            }
+        }
         float mx = __builtin_fmaxf(__builtin_fmaxf(s[0][0], s[0][1]), s[1][0]);
 #pragma unroll
         for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][i]), s[0][i + 1]);
@@ -362,10 +431,12 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                 for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
             m = mn;
         }
-        const float muse = m == -INFINITY ? 0.f : m;
-
-        // P^T fragments: pf[c] (c = 0..3) element e <-> key 16c + 8(e/4) + 4hh + e%4.
-        bf16x8_t pf[4];
+        return m == -INFINITY ? 0.f : m;
+    };
+    // Online softmax, second half: P = exp2(s * c2 - muse) as the bf16 B
+    // operand of the PV product (pf[c] element e <-> key 16c + 8(e/4) + 4hh + e%4),
+    // row sums in fp32, and O^T += V^T P^T.
+    auto softmax_pv = [&](const f32x16_t (&s)[2], float muse, const bf16x8_t (&va)[4][NDB]) {
         float ls[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -379,66 +450,111 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                 acc += p0 + p1;
             }
             ls[c] = acc;
-            pf[c] = as_bf16x8(u);
+            const bf16x8_t pf = as_bf16x8(u);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c][db], pf, o[db], 0, 0, 0);
         }
         l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c][db], pf[c], o[db], 0, 0, 0);
     };
 
-    // ---- pipelined walk over the key blocks ----
-    // The block list and Q must be in registers before the first load
-    // addresses and MFMAs; waiting here once keeps the compiler from placing
-    // conservative full waits inside the pipeline.  The prologue loads are
-    // unconditional (lanes past the list hold block 0, a valid address).
+    // ---- software pipeline over the flat tile list ----
+    // Tile f's K sits in K buffer f & 1 and its V in V buffer f & 1.  Step f
+    // computes the scores of tile f + 1 (MFMA) while it runs the softmax of
+    // tile f (VALU), then accumulates tile f's PV product.  During step f the
+    // direct loads of K(f + 2) and V(f + 1) are in flight, into the buffers
+    // whose last readers (step f - 1) are behind the step's barrier.  A unit's
+    // Q is loaded during the first step of the unit before it, so a unit
+    // boundary costs no load latency.
+    int e0 = flat[0];
+    int e1 = F > 1 ? flat[1] : 0;
+    int e2 = F > 2 ? flat[2] : 0;
+    int u_cur = tile_unit(e0);
+    int kind_cur = rd(u_kind, u_cur), slot_cur = rd(u_slot, u_cur);
+    int tq_cur = query_token(kind_cur);
+    int kind_n = 0, slot_n = -1, tq_n = -1, u_n = 0;
+    bf16x8_t qf[NC], qf_n[NC];
+    load_q(tq_cur, qf);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf_n[c] = qf[c];
+
     wait_vmcnt<0>();
-    issue_tile<D>(kp, vp, tile_of(0), koffs, voffs, lds0);
-    // step t: tile t sits in stage t%2; the loads of tile t+1 go to the other
-    // stage, whose last reader (step t-1) is behind the barrier.
-    auto step = [&](int t, const uint16_t* cur, uint32_t nxt) {
+    issue_half<D>(kp, tile_j(e0), koffs, kl0);
+    issue_half<D>(vp, tile_j(e0), voffs, vl0);
+    if (F > 1) {
+        issue_half<D>(kp, tile_j(e1), koffs, kl0 + TILE * 2);
+        wait_vmcnt<2 * Gm::LPT>();   // K(0) landed; V(0) and K(1) may still fly
+    } else {
+        wait_vmcnt<Gm::LPT>();
+    }
+    stage_barrier();
+    f32x16_t s_cur[2], s_nxt[2];
+    {
+        bf16x8_t kf[2][NC];
+        kread(kbuf, kf);
+        smma(kf, qf, s_cur);
+    }
+    reset();
+
+
+    // One step, written for a compile-time parity P = f & 1 so that the ring
+    // buffers' addresses fold into instruction offsets; the loop runs steps in
+    // pairs, swapping the roles of the two score register sets.  The running
+    // max of tile f is taken before the step's wait: it needs only registers,
+    // and it covers the latency of the previous step's output stores.
+    auto step = [&](auto parity, int f, f32x16_t (&s_now)[2], f32x16_t (&s_next)[2]) {
+        constexpr int P = decltype(parity)::value;
+        const float muse = softmax_max(tile_j(e0), kind_cur, tq_cur, s_now);
         wait_vmcnt<0>();
         stage_barrier();
-        if (t + 1 < n) issue_tile<D>(kp, vp, tile_of(t + 1), koffs, voffs, nxt);
-        compute(t, cur);
-    };
-    for (int t = 0; t < n; t += 2) {
-        step(t, st0, lds1);
-        if (t + 1 < n) step(t + 1, st1, lds0);
-    }
-    wait_vmcnt<0>();   // no direct-to-LDS load may outlive the workgroup
-
-    // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
-    const float lt = pair_sum(l);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse_v = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
-    if (tq >= 0) {
-        // O^T register i of block db <-> d = 32db + 8(i/4) + 4hh + i%4
-        if (slot < 0) {
-            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + tq) * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    u32x2_t w;
-                    w.x = pack_bf16x2(o[db][4 * gq + 0] * inv, o[db][4 * gq + 1] * inv);
-                    w.y = pack_bf16x2(o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv);
-                    *(u32x2_t*)(orow + 32 * db + 8 * gq + 4 * hh) = w;
-                }
-            if (hh == 0) a.lse[bh * a.L + tq] = lse_v;
-        } else {
-            float* orow = a.ws_o + ((size_t)slot * 64 + rloc) * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq)
-                    *(float4*)(orow + 32 * db + 8 * gq + 4 * hh) =
-                        make_float4(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
-                                    o[db][4 * gq + 3] * inv);
-            if (hh == 0) a.ws_lse[(size_t)slot * 64 + rloc] = lse_v;
+        if (f + 2 < F) issue_half<D>(kp, tile_j(e2), koffs, kl0 + P * TILE * 2);
+        if (f + 1 < F) issue_half<D>(vp, tile_j(e1), voffs, vl0 + (1 - P) * TILE * 2);
+        const int e3 = f + 3 < F ? flat[f + 3] : 0;
+        if (e0 & kTileFirst) {             // prefetch the next unit's Q
+            const uint64_t rest = u_cur >= 63 ? 0ull : (live_units & ~((2ull << u_cur) - 1ull));
+            if (rest != 0) {
+                u_n = __builtin_ctzll(rest);
+                kind_n = rd(u_kind, u_n);
+                slot_n = rd(u_slot, u_n);
+                tq_n = query_token(kind_n);
+                load_q(tq_n, qf_n);
+            }
         }
+        if (e0 & kTileLast) {              // tile f + 1 (if any) opens the next unit
+#pragma unroll
+            for (int c = 0; c < NC; ++c) qf[c] = qf_n[c];
+        }
+        // Scores of tile f + 1 (past the end they read a stale buffer and are
+        // discarded), interleaved by the scheduler with the softmax of tile f.
+        bf16x8_t kf[2][NC], va[4][NDB];
+        kread(kbuf + (1 - P) * TILE, kf);
+        vread(vbuf + P * TILE, va);
+        smma(kf, qf, s_next);
+        softmax_pv(s_now, muse, va);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // then six VALU
+        }
+        if (e0 & kTileLast) {
+            // ---- unit done: O = acc / l, LSE = (m + log2 l) ln 2 ----
+            const float lt = pair_sum(l);
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            const float lse_v = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+            store_unit(slot_cur, tq_cur, rloc, o, inv, lse_v);
+            reset();
+            u_cur = u_n;
+            kind_cur = kind_n;
+            slot_cur = slot_n;
+            tq_cur = tq_n;
+        }
+        e0 = e1;
+        e1 = e2;
+        e2 = e3;
+    };
+    for (int f = 0; f < F; f += 2) {
+        step(std::integral_constant<int, 0>(), f, s_cur, s_nxt);
+        if (f + 1 < F) step(std::integral_constant<int, 1>(), f + 1, s_nxt, s_cur);
     }
 }
 
@@ -517,14 +633,25 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
 template <int D, int MASK>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
     const int64_t G = (int64_t)a.B * a.H;
-    const int64_t nru = a.n_routed > 0 ? (int64_t)a.n_rt * a.r_chunks : 0;
-    const int64_t grid = kXcds * ((G + kXcds - 1) / kXcds) * (nru + a.items_per_head);
+    const int64_t grid = kXcds * ((G + kXcds - 1) / kXcds) * a.n_bins;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+int fwd_bf16_ctas_per_cu(int head_dim) {
+    int n = 0;
+    hipError_t e = head_dim == 64
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<64, MASK_NONE>, kThreads, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<128, MASK_NONE>, kThreads, 0);
+    if (e != hipSuccess || n < 1) n = 1;
+    // Measured on MI355X: with 32 KiB of LDS per workgroup only 4 workgroups
+    // are resident per CU (the occupancy query reports 5); 64 KiB gives 2.
+    const int lds_cap = head_dim == 64 ? 4 : 2;
+    return n < lds_cap ? n : lds_cap;
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
                            hipEvent_t after) {
