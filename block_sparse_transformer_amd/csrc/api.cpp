@@ -176,116 +176,130 @@ int device_capacity(int dev, int32_t D) {
     return cache[idx];
 }
 
-// Persistent schedule for one call shape.  Each (batch, head) group gets
-// n_bins workgroups -- as many as fill the device once, when the groups are
-// dealt 8 per XCD -- and the group's units (the head's items, plus the routed
-// chunks) are packed into the bins longest-processing-time first: each unit,
-// by decreasing cost, goes to the least loaded bin.  A unit's cost is its
-// tile count plus a fixed overhead for loading Q and writing O.  Row lengths
-// do not depend on the head for the supported layouts, so one packing serves
-// every head (the cost of position k is the longest item at k over all heads;
-// positions empty in every head are dropped).  For every (head, bin) the
-// device gets the unit records and the flat list of the units' key blocks in
-// order, at most kMaxBinUnits units and kMaxBinTiles tiles per bin.
+// Persistent schedule for one call shape.  Workgroup i runs on XCD i % 8
+// (workgroups are dealt round-robin), and XCD x serves the (batch, head)
+// groups g = x, x + 8, ...  The units of those groups -- each head's items
+// (rows of at most kChunkTiles blocks, chunks of split rows) plus the routed
+// chunks -- are packed into the XCD's n_bins bins longest-processing-time
+// first: each unit, by decreasing cost, goes to the least loaded bin, cost =
+// tile count + a fixed overhead for loading Q and writing O.  n_bins is the
+// number of workgroups per XCD that the device holds at once.  Within a bin
+// the units are then ordered by group, so that all bins of an XCD walk its
+// groups in the same order and the XCD's K/V working set stays near one
+// group (which fits in its L2).  For every bin the device gets the unit
+// records and the flat list of the units' key blocks in order, at most
+// kMaxBinUnits units and kMaxBinTiles tiles per bin.
 bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32_t nru, int32_t rct,
                            int32_t r_chunks, hipStream_t stream, bsattn_layout::Sched* out) {
     const int32_t ipH = lay->items_per_head;
-    std::vector<int32_t> unit_id, cost;
-    for (int32_t k = 0; k < ipH; ++k) {
-        int32_t len = 0;
-        for (int32_t h = 0; h < lay->H; ++h) {
-            const WorkItem& wi = lay->items[(size_t)h * ipH + k];
-            if (wi.row >= 0) len = std::max(len, wi.col_end - wi.col_begin);
-        }
-        if (len == 0) continue;
-        unit_id.push_back(k);
-        cost.push_back(len + 2);
-    }
+    const int64_t G = (int64_t)B * lay->H;
     auto routed_len = [&](int32_t v) {
         const int32_t c = v % r_chunks;
         return std::min(lay->nb, c * rct + rct) - c * rct;
     };
-    for (int32_t v = 0; v < nru; ++v) {
-        unit_id.push_back(-1 - v);
-        cost.push_back(routed_len(v) + 2);
+    struct Unit {
+        int32_t g, id, tiles, order;   // id >= 0: item position in the head; < 0: routed -1-v
+    };
+    // units of each XCD, in group order
+    std::vector<std::vector<Unit>> xu((size_t)kXcds);
+    for (int64_t g = 0; g < G; ++g) {
+        auto& v = xu[(size_t)(g % kXcds)];
+        const int32_t h = (int32_t)(g % lay->H);
+        for (int32_t k = 0; k < ipH; ++k) {
+            const WorkItem& wi = lay->items[(size_t)h * ipH + k];
+            if (wi.row >= 0) v.push_back({(int32_t)g, k, wi.col_end - wi.col_begin, (int32_t)v.size()});
+        }
+        for (int32_t r = 0; r < nru; ++r) v.push_back({(int32_t)g, -1 - r, routed_len(r), (int32_t)v.size()});
     }
-    const int32_t U = (int32_t)unit_id.size();
-    int64_t tiles_head = 0;
-    for (int32_t c : cost) tiles_head += c - 2;
-    const int64_t G8 = (int64_t)kXcds * (((int64_t)B * lay->H + kXcds - 1) / kXcds);
-    int64_t q = device_capacity(lay->device, D) / G8;
-    q = std::max<int64_t>(q, (U + kMaxBinUnits - 1) / kMaxBinUnits);
-    q = std::max<int64_t>(q, (tiles_head + kMaxBinTiles / 2 - 1) / (kMaxBinTiles / 2));
-    q = std::min<int64_t>(q, std::max<int32_t>(U, 1));
-    int32_t n_bins = (int32_t)std::max<int64_t>(q, 1);
+    int64_t need = 1;
+    for (const auto& v : xu) {
+        int64_t t = 0;
+        for (const auto& u : v) t += u.tiles;
+        need = std::max<int64_t>(need, ((int64_t)v.size() + kMaxBinUnits - 1) / kMaxBinUnits);
+        need = std::max<int64_t>(need, (t + kMaxBinTiles / 2 - 1) / (kMaxBinTiles / 2));
+    }
+    size_t max_units = 1;
+    for (const auto& v : xu) max_units = std::max(max_units, v.size());
+    int64_t nb64 = std::max<int64_t>(device_capacity(lay->device, D) / kXcds, need);
+    nb64 = std::min<int64_t>(nb64, (int64_t)max_units);
+    if (nb64 * kXcds >= ((int64_t)1 << 31)) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+    int32_t n_bins = (int32_t)std::max<int64_t>(nb64, 1);
 
     std::lock_guard<std::mutex> guard(*lay->sched_mu);
     for (const auto& sc : lay->scheds)
-        if (sc.n_bins == n_bins && sc.nru == nru && sc.rct == rct) {
+        if (sc.batch == B && sc.head_dim == D && sc.nru == nru && sc.rct == rct) {
             *out = sc;
             return BSATTN_OK;
         }
-    std::vector<int32_t> order((size_t)U);
-    for (int32_t u = 0; u < U; ++u) order[(size_t)u] = u;
-    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return cost[(size_t)x] > cost[(size_t)y]; });
-    std::vector<std::vector<int32_t>> bins;
-    for (;;) {
-        bins.assign((size_t)n_bins, {});
-        std::vector<int64_t> tiles_in((size_t)n_bins, 0);
-        using Load = std::pair<int64_t, int32_t>;   // (load, bin), least loaded first, then lowest bin
-        std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
-        for (int32_t i = 0; i < n_bins; ++i) heap.push({0, i});
-        for (int32_t u : order) {
-            Load t = heap.top();
-            heap.pop();
-            bins[(size_t)t.second].push_back(u);
-            tiles_in[(size_t)t.second] += cost[(size_t)u] - 2;
-            heap.push({t.first + cost[(size_t)u], t.second});
-        }
-        bool fits = true;
-        for (int32_t i = 0; i < n_bins; ++i)
-            fits = fits && bins[(size_t)i].size() <= (size_t)kMaxBinUnits && tiles_in[(size_t)i] <= kMaxBinTiles;
-        if (fits) break;
-        if (n_bins >= U) return fail(BSATTN_ERR_UNSUPPORTED, "a single row exceeds the per-workgroup tile list");
-        n_bins = std::min(U, n_bins * 2);
-    }
-    // per (head, bin): unit records and flat tile lists
-    std::vector<int2> units;
-    std::vector<int32_t> unit_ptr(1, 0), tiles, tile_ptr(1, 0);
-    for (int32_t h = 0; h < lay->H; ++h)
-        for (int32_t i = 0; i < n_bins; ++i) {
-            int32_t k = 0;
-            for (int32_t u : bins[(size_t)i]) {
-                const int32_t id = unit_id[(size_t)u];
-                int32_t n = 0, first = 0;
-                bool routed = id < 0;
-                if (!routed) {
-                    const WorkItem& wi = lay->items[(size_t)h * ipH + id];
-                    if (wi.row < 0) continue;   // empty in this head
-                    units.push_back(make_int2(wi.row % lay->nb, wi.slot));
-                    n = wi.col_end - wi.col_begin;
-                    first = wi.col_begin;
-                } else {
-                    const int32_t v = -1 - id;
-                    units.push_back(make_int2(-1 - v / r_chunks, v % r_chunks));
-                    n = routed_len(v);
-                    first = (v % r_chunks) * rct;
-                }
-                for (int32_t t = 0; t < n; ++t) {
-                    const int32_t j = routed ? first + t : lay->col_idx[(size_t)first + t];
-                    tiles.push_back(j | (k << kTileUnitShift) | (t == 0 ? kTileFirst : 0) | (t == n - 1 ? kTileLast : 0));
-                }
-                ++k;
+    std::vector<int4> units;
+    std::vector<int32_t> unit_ptr, tiles, tile_ptr;
+    // pack every XCD's units into nbins bins; false if some bin overflows its lists
+    auto pack = [&](int32_t nbins) -> bool {
+        units.clear();
+        tiles.clear();
+        unit_ptr.assign(1, 0);
+        tile_ptr.assign(1, 0);
+        for (int32_t x = 0; x < kXcds; ++x) {
+            const auto& v = xu[(size_t)x];
+            std::vector<std::vector<int32_t>> bins((size_t)nbins);
+            std::vector<int64_t> tiles_in((size_t)nbins, 0);
+            std::vector<int32_t> order(v.size());
+            for (size_t u = 0; u < v.size(); ++u) order[u] = (int32_t)u;
+            std::stable_sort(order.begin(), order.end(),
+                             [&](int32_t a2, int32_t b2) { return v[(size_t)a2].tiles > v[(size_t)b2].tiles; });
+            using Load = std::pair<int64_t, int32_t>;   // (load, bin), least loaded first, then lowest bin
+            std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+            for (int32_t i = 0; i < nbins; ++i) heap.push({0, i});
+            for (int32_t u : order) {
+                Load t = heap.top();
+                heap.pop();
+                bins[(size_t)t.second].push_back(u);
+                tiles_in[(size_t)t.second] += v[(size_t)u].tiles;
+                heap.push({t.first + v[(size_t)u].tiles + 2, t.second});
             }
-            unit_ptr.push_back((int32_t)units.size());
-            tile_ptr.push_back((int32_t)tiles.size());
+            for (int32_t i = 0; i < nbins; ++i)
+                if (bins[(size_t)i].size() > (size_t)kMaxBinUnits || tiles_in[(size_t)i] > kMaxBinTiles) return false;
+            for (auto& bn : bins) {
+                std::sort(bn.begin(), bn.end(),
+                          [&](int32_t a2, int32_t b2) { return v[(size_t)a2].order < v[(size_t)b2].order; });
+                int32_t k = 0;
+                for (int32_t u : bn) {
+                    const Unit& un = v[(size_t)u];
+                    const int32_t h = un.g % lay->H;
+                    int32_t first = 0;
+                    const bool routed = un.id < 0;
+                    if (!routed) {
+                        const WorkItem& wi = lay->items[(size_t)h * ipH + un.id];
+                        units.push_back(make_int4(wi.row % lay->nb, wi.slot, un.g, 0));
+                        first = wi.col_begin;
+                    } else {
+                        const int32_t r = -1 - un.id;
+                        units.push_back(make_int4(-1 - r / r_chunks, r % r_chunks, un.g, 0));
+                        first = (r % r_chunks) * rct;
+                    }
+                    for (int32_t t = 0; t < un.tiles; ++t) {
+                        const int32_t j = routed ? first + t : lay->col_idx[(size_t)first + t];
+                        tiles.push_back(j | (k << kTileUnitShift) | (t == 0 ? kTileFirst : 0) |
+                                        (t == un.tiles - 1 ? kTileLast : 0));
+                    }
+                    ++k;
+                }
+                unit_ptr.push_back((int32_t)units.size());
+                tile_ptr.push_back((int32_t)tiles.size());
+            }
         }
-    if (units.empty()) units.push_back(make_int2(0, -1));
+        return true;
+    };
+    while (!pack(n_bins)) {
+        if ((size_t)n_bins >= max_units) return fail(BSATTN_ERR_UNSUPPORTED, "a unit exceeds the per-workgroup tile list");
+        n_bins = (int32_t)std::min<size_t>(max_units, (size_t)n_bins * 2);
+    }
+    if (units.empty()) units.push_back(make_int4(0, -1, 0, 0));
     if (tiles.empty()) tiles.push_back(0);
-    bsattn_layout::Sched sc{n_bins, nru, rct, nullptr, nullptr, nullptr, nullptr};
+    bsattn_layout::Sched sc{B, D, n_bins, nru, rct, nullptr, nullptr, nullptr, nullptr};
     void* p[4] = {nullptr, nullptr, nullptr, nullptr};
     const void* src[4] = {units.data(), unit_ptr.data(), tiles.data(), tile_ptr.data()};
-    const size_t sz[4] = {units.size() * sizeof(int2), unit_ptr.size() * sizeof(int32_t),
+    const size_t sz[4] = {units.size() * sizeof(int4), unit_ptr.size() * sizeof(int32_t),
                           tiles.size() * sizeof(int32_t), tile_ptr.size() * sizeof(int32_t)};
     hipError_t e = hipSuccess;
     for (int a = 0; a < 4 && e == hipSuccess; ++a) {
@@ -297,7 +311,7 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
         for (int a = 0; a < 4; ++a) (void)hipFree(p[a]);
         return fail(BSATTN_ERR_NO_MEMORY, "schedule upload: %s", hipGetErrorString(e));
     }
-    sc.d_units = (int2*)p[0];
+    sc.d_units = (int4*)p[0];
     sc.d_unit_ptr = (int32_t*)p[1];
     sc.d_tiles = (int32_t*)p[2];
     sc.d_tile_ptr = (int32_t*)p[3];

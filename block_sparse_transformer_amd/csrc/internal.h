@@ -72,14 +72,15 @@ struct FwdArgs {
     const int32_t* routed_rows;
     int32_t n_items, n_merges;
     int32_t items_per_head;   // explicit items per head (NOP-padded to equal length)
-    // persistent schedule: n_bins workgroups per group.  Workgroup (h, bin)
-    // runs units units[unit_ptr[h*n_bins+bin] ..) -- {kind, slot}: kind >= 0
-    // the query block of a layout row (slot: partial slot within a batch
-    // entry, -1 for a whole row), kind < 0 routed tile -1-kind (slot: chunk)
-    // -- over the flat tile list tiles[tile_ptr[h*n_bins+bin] ..), entries
-    // key block | unit << 20 | kTileFirst | kTileLast.
+    // persistent schedule: n_bins workgroups per XCD.  Workgroup (x, bin)
+    // runs units units[unit_ptr[x*n_bins+bin] ..) -- {kind, slot, group}:
+    // kind >= 0 the query block of a layout row (slot: partial slot within a
+    // batch entry, -1 for a whole row), kind < 0 routed tile -1-kind (slot:
+    // chunk); group = b * H + h -- over the flat tile list
+    // tiles[tile_ptr[x*n_bins+bin] ..), entries key block | unit << 20 |
+    // kTileFirst | kTileLast.
     int32_t n_bins;
-    const int2* units;
+    const int4* units;
     const int32_t* unit_ptr;
     const int32_t* tiles;
     const int32_t* tile_ptr;
@@ -125,11 +126,11 @@ struct bsattn_layout {
     int32_t* d_col_idx = nullptr;
     bsattn::WorkItem* d_items = nullptr;
     bsattn::MergeItem* d_merges = nullptr;
-    // persistent schedules built on first use, keyed by (bins per group,
+    // persistent schedules built on first use, keyed by (batch, head width,
     // routed units per group, tiles per routed unit); device arrays
     struct Sched {
-        int32_t n_bins, nru, rct;
-        int2* d_units;
+        int32_t batch, head_dim, n_bins, nru, rct;
+        int4* d_units;
         int32_t* d_unit_ptr;
         int32_t* d_tiles;
         int32_t* d_tile_ptr;

@@ -191,49 +191,47 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     const int hh = lane >> 5;
     const int rloc = wave * 32 + ql;  // this lane's query row within the tile
 
-    // ---- this workgroup: bin `bin` of group g = (b, h).  Workgroup i runs on
-    // XCD i % 8, which serves groups x, x + 8, ... so a group's K/V stays in
-    // one XCD's L2.  The grid is sized to be resident at once; every bin holds
-    // a balanced list of units (rows, chunks of split rows, routed tiles).
-    const int G = a.B * a.H;
+    // ---- this workgroup: bin `bin` of XCD x = blockIdx % 8 (workgroups are
+    // dealt round-robin to the XCDs).  The bins of an XCD share the units --
+    // rows, chunks of split rows, routed tiles -- of the (batch, head) groups
+    // that XCD serves, packed so that all bins walk the groups in the same
+    // order: the K/V working set of the XCD stays near one group and hits in
+    // its L2.  The grid is sized to be resident at once.
     const int x = blockIdx.x % kXcds;
-    const int p = blockIdx.x / kXcds;
-    const int g = x + kXcds * (p / a.n_bins);
-    const int bin = p % a.n_bins;
-    if (g >= G) return;
-    const int b = g / a.H, h = g % a.H;
-    const size_t bh = (size_t)g;
-    const int hb = h * a.n_bins + bin;
-    const int up0 = a.unit_ptr[hb], nu = a.unit_ptr[hb + 1] - up0;   // <= 64
-    const int tp0 = a.tile_ptr[hb], nt = a.tile_ptr[hb + 1] - tp0;   // <= kMaxBinTiles
+    const int bin = blockIdx.x / kXcds;
+    const int bi = x * a.n_bins + bin;
+    const int up0 = a.unit_ptr[bi], nu = a.unit_ptr[bi + 1] - up0;   // <= 64
+    const int tp0 = a.tile_ptr[bi], nt = a.tile_ptr[bi + 1] - tp0;   // <= kMaxBinTiles
+    if (nu <= 0) return;
 
     // Unit table, lane k describing unit k: kind >= 0 query block of a layout
-    // row, kind < 0 routed tile -1-kind; slot -1 writes O/LSE, >= 0 a partial.
-    int u_kind = 0, u_slot = -1;
+    // row, kind < 0 routed tile -1-kind; slot -1 writes O/LSE, >= 0 a partial;
+    // g its (batch, head) group; valid its batch entry's key length.
+    int u_kind = 0, u_slot = -1, u_g = 0, u_valid = a.L;
     if (lane < nu) {
-        const int2 r = a.units[up0 + lane];
+        const int4 r = a.units[up0 + lane];
+        const int ub = r.z / a.H;
         u_kind = r.x;
-        if (r.x >= 0) u_slot = r.y < 0 ? -1 : b * a.n_slots + r.y;
-        else u_slot = a.r_slot_base + (g * a.n_rt + (-1 - r.x)) * a.r_chunks + r.y;
+        u_g = r.z;
+        if (r.x >= 0) u_slot = r.y < 0 ? -1 : ub * a.n_slots + r.y;
+        else u_slot = a.r_slot_base + (r.z * a.n_rt + (-1 - r.x)) * a.r_chunks + r.y;
+        if (MASK == MASK_PAD) u_valid = min(max(a.valid_len[ub], 0), a.L);
     }
     auto rd = [](int v, int k) -> int { return __builtin_amdgcn_readlane(v, k); };
+    auto gbase = [&](const void* t, int g) -> const uint16_t* {
+        return (const uint16_t*)t + (size_t)g * a.L * D;
+    };
 
-    int valid = a.L;
-    if (MASK == MASK_PAD) valid = min(max(a.valid_len[b], 0), a.L);
-
-    const uint16_t* qp = (const uint16_t*)a.q + bh * (size_t)a.L * D;
-    const uint16_t* kp = (const uint16_t*)a.k + bh * (size_t)a.L * D;
-    const uint16_t* vp = (const uint16_t*)a.v + bh * (size_t)a.L * D;
-
-    // token of this lane's query row in a unit of kind `kind` (-1: unused routed row)
-    auto query_token = [&](int kind) -> int {
+    // token of this lane's query row in a unit of kind `kind`, group g (-1: unused routed row)
+    auto query_token = [&](int kind, int g) -> int {
         if (kind >= 0) return kind * 64 + rloc;
         const int kk = (-1 - kind) * 64 + rloc;
-        const int t = kk < a.n_routed ? a.routed_rows[bh * a.n_routed + kk] : -1;
+        const int t = kk < a.n_routed ? a.routed_rows[(size_t)g * a.n_routed + kk] : -1;
         return (t >= a.L) ? -1 : t;          // out-of-range rows are skipped, never dereferenced
     };
     // Q^T fragments of a row (B operand of S^T): lane (ql, hh) holds Q[t][16c + 8hh .. +7].
-    auto load_q = [&](int t, bf16x8_t (&qf)[NC]) {
+    auto load_q = [&](int t, int g, bf16x8_t (&qf)[NC]) {
+        const uint16_t* qp = gbase(a.q, g);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             u32x4_t u = {0u, 0u, 0u, 0u};
@@ -242,8 +240,9 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         }
     };
     // Write a unit's result: O row (bf16) and LSE, or an fp32 partial and its LSE.
-    auto store_unit = [&](int slot, int t, int r, const f32x16_t (&ov)[NDB], float inv, float lse_v) {
+    auto store_unit = [&](int slot, int t, int g, int r, const f32x16_t (&ov)[NDB], float inv, float lse_v) {
         if (t < 0) return;
+        const size_t bh = (size_t)g;
         // O^T register i of block db <-> d = 32db + 8(i/4) + 4hh + i%4
         if (slot < 0) {
             uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D;
@@ -285,6 +284,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
             const int i = base + lane;
             const int e = i < nt ? a.tiles[tp0 + i] : 0;
             const int en = i + 1 < nt ? a.tiles[tp0 + i + 1] : 0;
+            const int valid = __shfl(u_valid, tile_unit(e));   // the tile's unit's key length
             const bool keep = i < nt && tile_j(e) * 64 < valid;
             const bool keep_next = i + 1 < nt && !(e & kTileLast) && tile_j(en) * 64 < valid;
             const uint64_t km = __ballot(keep);
@@ -298,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         const f32x16_t zero[NDB] = {};
         for (uint64_t mm = empty_units; mm; mm &= mm - 1) {
             const int u = __builtin_ctzll(mm);
-            store_unit(rd(u_slot, u), query_token(rd(u_kind, u)), rloc, zero, 0.f, -INFINITY);
+            const int g = rd(u_g, u);
+            store_unit(rd(u_slot, u), query_token(rd(u_kind, u), g), g, rloc, zero, 0.f, -INFINITY);
         }
     }
     __syncthreads();
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     };
     // Online softmax, first half: mask the tile's scores (key block j), raise
     // the running max lazily (rescaling O and l), return the max to subtract.
-    auto softmax_max = [&](int j, int kind, int tq, f32x16_t (&s)[2]) -> float {
+    auto softmax_max = [&](int j, int kind, int tq, int valid, f32x16_t (&s)[2]) -> float {
         if (MASK == MASK_PAD) {
             if (j * 64 + 64 > valid) {
 #pragma unroll
@@ -436,26 +437,27 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     // Online softmax, second half: P = exp2(s * c2 - muse) as the bf16 B
     // operand of the PV product (pf[c] element e <-> key 16c + 8(e/4) + 4hh + e%4),
     // row sums in fp32, and O^T += V^T P^T.
-    auto softmax_pv = [&](const f32x16_t (&s)[2], float muse, const bf16x8_t (&va)[4][NDB]) {
-        float ls[4];
+    // Key chunks c0 .. c1 - 1 (16 keys each) of the tile.
+    auto softmax_pv = [&](const f32x16_t (&s)[2], float muse, const bf16x8_t (&va)[4][NDB], auto c0, auto c1) {
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = decltype(c0)::value; c < decltype(c1)::value; ++c) {
             u32x4_t u;
-            float acc = 0.f;
+            float acc[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][8 * (c % 2) + 2 * e], c2, -muse));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][8 * (c % 2) + 2 * e + 1], c2, -muse));
                 u[e] = pack_bf16x2(p0, p1);
-                acc += p0 + p1;
+                acc[e] = p0 + p1;
             }
-            ls[c] = acc;
+            ls[c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             const bf16x8_t pf = as_bf16x8(u);
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c][db], pf, o[db], 0, 0, 0);
         }
-        l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        l += (ls[decltype(c0)::value] + ls[decltype(c0)::value + 1]);
     };
 
     // ---- software pipeline over the flat tile list ----
@@ -469,20 +471,23 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     int e0 = flat[0];
     int e1 = F > 1 ? flat[1] : 0;
     int e2 = F > 2 ? flat[2] : 0;
+    // group of a flat tile entry's unit
+    auto tile_g = [&](int e) -> int { return rd(u_g, tile_unit(e)); };
     int u_cur = tile_unit(e0);
-    int kind_cur = rd(u_kind, u_cur), slot_cur = rd(u_slot, u_cur);
-    int tq_cur = query_token(kind_cur);
-    int kind_n = 0, slot_n = -1, tq_n = -1, u_n = 0;
+    int kind_cur = rd(u_kind, u_cur), slot_cur = rd(u_slot, u_cur), g_cur = rd(u_g, u_cur);
+    int valid_cur = rd(u_valid, u_cur);
+    int tq_cur = query_token(kind_cur, g_cur);
+    int kind_n = 0, slot_n = -1, tq_n = -1, u_n = 0, g_n = 0, valid_n = a.L;
     bf16x8_t qf[NC], qf_n[NC];
-    load_q(tq_cur, qf);
+    load_q(tq_cur, g_cur, qf);
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf_n[c] = qf[c];
 
     wait_vmcnt<0>();
-    issue_half<D>(kp, tile_j(e0), koffs, kl0);
-    issue_half<D>(vp, tile_j(e0), voffs, vl0);
+    issue_half<D>(gbase(a.k, g_cur), tile_j(e0), koffs, kl0);
+    issue_half<D>(gbase(a.v, g_cur), tile_j(e0), voffs, vl0);
     if (F > 1) {
-        issue_half<D>(kp, tile_j(e1), koffs, kl0 + TILE * 2);
+        issue_half<D>(gbase(a.k, tile_g(e1)), tile_j(e1), koffs, kl0 + TILE * 2);
         wait_vmcnt<2 * Gm::LPT>();   // K(0) landed; V(0) and K(1) may still fly
     } else {
         wait_vmcnt<Gm::LPT>();
@@ -504,49 +509,73 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     // and it covers the latency of the previous step's output stores.
     auto step = [&](auto parity, int f, f32x16_t (&s_now)[2], f32x16_t (&s_next)[2]) {
         constexpr int P = decltype(parity)::value;
-        const float muse = softmax_max(tile_j(e0), kind_cur, tq_cur, s_now);
+        const float muse = softmax_max(tile_j(e0), kind_cur, tq_cur, valid_cur, s_now);
         wait_vmcnt<0>();
         stage_barrier();
-        if (f + 2 < F) issue_half<D>(kp, tile_j(e2), koffs, kl0 + P * TILE * 2);
-        if (f + 1 < F) issue_half<D>(vp, tile_j(e1), voffs, vl0 + (1 - P) * TILE * 2);
-        const int e3 = f + 3 < F ? flat[f + 3] : 0;
-        if (e0 & kTileFirst) {             // prefetch the next unit's Q
+        // Q of the next unit: loaded during the first step of the current unit
+        // and, when the current unit ends here, moved in place for the scores
+        // of tile f + 1 -- before this step's direct loads are issued, so that
+        // any wait the compiler places for the Q loads cannot also wait for
+        // the direct loads in flight.
+        if (e0 & kTileFirst) {
             const uint64_t rest = u_cur >= 63 ? 0ull : (live_units & ~((2ull << u_cur) - 1ull));
             if (rest != 0) {
                 u_n = __builtin_ctzll(rest);
                 kind_n = rd(u_kind, u_n);
                 slot_n = rd(u_slot, u_n);
-                tq_n = query_token(kind_n);
-                load_q(tq_n, qf_n);
+                g_n = rd(u_g, u_n);
+                valid_n = rd(u_valid, u_n);
+                tq_n = query_token(kind_n, g_n);
+                load_q(tq_n, g_n, qf_n);
             }
         }
-        if (e0 & kTileLast) {              // tile f + 1 (if any) opens the next unit
+        if (e0 & kTileLast) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) qf[c] = qf_n[c];
         }
-        // Scores of tile f + 1 (past the end they read a stale buffer and are
-        // discarded), interleaved by the scheduler with the softmax of tile f.
+#pragma unroll
+        for (int c = 0; c < NC; ++c) asm volatile("" ::"v"(qf[c]));   // materialise qf here
+        const int e3 = f + 3 < F ? flat[f + 3] : 0;
+        // Fragment reads first; the direct loads of K(f + 2) and V(f + 1) are
+        // spread over the step (a burst of them right after the barrier makes
+        // every wave queue at the texture unit with nothing else to issue).
         bf16x8_t kf[2][NC], va[4][NDB];
         kread(kbuf + (1 - P) * TILE, kf);
         vread(vbuf + P * TILE, va);
+        if (f + 2 < F) issue_half<D>(gbase(a.k, tile_g(e2)), tile_j(e2), koffs, kl0 + P * TILE * 2);
+        // Scores of tile f + 1 (past the end they read a stale buffer and are
+        // discarded), interleaved by the scheduler with the softmax of tile f.
+        using C0 = std::integral_constant<int, 0>;
+        using C2 = std::integral_constant<int, 2>;
+        using C4 = std::integral_constant<int, 4>;
         smma(kf, qf, s_next);
-        softmax_pv(s_now, muse, va);
+        softmax_pv(s_now, muse, va, C0(), C2());
+        __builtin_amdgcn_sched_group_barrier(0x100, 8 + 8 * NDB, 0);   // LDS reads first
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // then six VALU
+        for (int i = 0; i < 8 + 2 * NDB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
+        }
+        if (f + 1 < F) issue_half<D>(gbase(a.v, tile_g(e1)), tile_j(e1), voffs, vl0 + (1 - P) * TILE * 2);
+        softmax_pv(s_now, muse, va, C2(), C4());
+#pragma unroll
+        for (int i = 0; i < 2 * NDB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
         }
         if (e0 & kTileLast) {
             // ---- unit done: O = acc / l, LSE = (m + log2 l) ln 2 ----
             const float lt = pair_sum(l);
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             const float lse_v = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
-            store_unit(slot_cur, tq_cur, rloc, o, inv, lse_v);
+            store_unit(slot_cur, tq_cur, g_cur, rloc, o, inv, lse_v);
             reset();
             u_cur = u_n;
             kind_cur = kind_n;
             slot_cur = slot_n;
             tq_cur = tq_n;
+            g_cur = g_n;
+            valid_cur = valid_n;
         }
         e0 = e1;
         e1 = e2;
@@ -564,14 +593,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
 // partial outputs.  A chunk with no allowed key has LSE -inf and weight 0; a
 // row with no allowed key at all gets O = 0, LSE = -inf.  Runs as its own
 // launch after the attention kernel, so stream order makes the partials
-// visible without any device-scope fence.  One workgroup per split row,
-// four threads per query row, each owning D/4 columns.
+// visible without any device-scope fence.  Four workgroups per split row, 16
+// query rows each; 16 threads per row, each owning D/16 columns.  All loads
+// of a thread are issued before their results are used.
 template <int D>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
-    constexpr int DP = D / 4;
-    const int u = blockIdx.x;
+    constexpr int DP = D / 16;   // columns per thread: 4 or 8
+    const int u = blockIdx.x >> 2;
     const int tid = threadIdx.x;
-    const int row = tid >> 2, part = tid & 3;
+    const int row = (blockIdx.x & 3) * 16 + (tid >> 4), part = tid & 15;
     int first, nch, t;
     size_t bh;
     if (u < a.B * a.n_merges) {
@@ -593,8 +623,12 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
     }
     if (t < 0) return;
     const float* lse_p = a.ws_lse + (size_t)first * 64 + row;
+    float lsev[kMaxChunks];
     float mxl = -INFINITY;
-    for (int c = 0; c < nch; ++c) mxl = __builtin_fmaxf(mxl, lse_p[(size_t)c * 64]);
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) lsev[c] = c < nch ? lse_p[(size_t)c * 64] : -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) mxl = __builtin_fmaxf(mxl, lsev[c]);
     uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * DP;
     if (mxl == -INFINITY) {
 #pragma unroll
@@ -606,17 +640,28 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
 #pragma unroll
     for (int d = 0; d < DP; ++d) acc[d] = 0.f;
     float wsum = 0.f;
-    for (int c = 0; c < nch; ++c) {
-        const float w = expf(lse_p[(size_t)c * 64] - mxl);
-        wsum += w;
-        const float* src = a.ws_o + ((size_t)(first + c) * 64 + row) * D + part * DP;
+    const float* src = a.ws_o + ((size_t)first * 64 + row) * D + part * DP;
 #pragma unroll
-        for (int d = 0; d < DP; d += 4) {
-            const float4 v4 = *(const float4*)(src + d);
-            acc[d] += w * v4.x;
-            acc[d + 1] += w * v4.y;
-            acc[d + 2] += w * v4.z;
-            acc[d + 3] += w * v4.w;
+    for (int c0 = 0; c0 < kMaxChunks; c0 += 8) {
+        if (c0 >= nch) break;
+        float4 v4[8][DP / 4];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int d = 0; d < DP / 4; ++d)
+                v4[c][d] = c0 + c < nch ? *(const float4*)(src + (size_t)(c0 + c) * 64 * D + 4 * d)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float w = expf(lsev[c0 + c] - mxl);   // 0 past nch (lse -inf)
+            wsum += w;
+#pragma unroll
+            for (int d = 0; d < DP / 4; ++d) {
+                acc[4 * d] += w * v4[c][d].x;
+                acc[4 * d + 1] += w * v4[c][d].y;
+                acc[4 * d + 2] += w * v4[c][d].z;
+                acc[4 * d + 3] += w * v4[c][d].w;
+            }
         }
     }
     const float inv = 1.f / wsum;
@@ -632,8 +677,7 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
 
 template <int D, int MASK>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-    const int64_t G = (int64_t)a.B * a.H;
-    const int64_t grid = kXcds * ((G + kXcds - 1) / kXcds) * a.n_bins;
+    const int64_t grid = (int64_t)kXcds * a.n_bins;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
@@ -671,9 +715,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
     const int64_t units = (int64_t)a.B * a.n_merges + (a.n_routed > 0 ? (int64_t)a.B * a.H * a.n_rt : 0);
     if (units == 0) return hipSuccess;
     if (head_dim == 64)
-        hipLaunchKernelGGL(merge_bf16_kernel<64>, dim3((unsigned)units), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(merge_bf16_kernel<64>, dim3((unsigned)(4 * units)), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(merge_bf16_kernel<128>, dim3((unsigned)units), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(merge_bf16_kernel<128>, dim3((unsigned)(4 * units)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
