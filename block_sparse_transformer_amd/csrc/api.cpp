@@ -161,18 +161,23 @@ void routed_split(int32_t nb, int32_t k, int32_t* n_rt, int32_t* r_chunks, int32
 
 // Workgroups of the bf16 kernel that one device holds at once (CUs x
 // resident workgroups per CU), cached per device and head width.
-int device_capacity(int dev, int32_t D) {
+int device_capacity(int dev, int32_t D, int* cus_out = nullptr) {
     static std::mutex mu;
-    static std::vector<int> cache;   // index 2 * dev + (D == 128)
+    static std::vector<int> cache, cus_cache;   // index 2 * dev + (D == 128)
     std::lock_guard<std::mutex> g(mu);
     const size_t idx = 2 * (size_t)dev + (D == 128 ? 1 : 0);
-    if (cache.size() <= idx) cache.resize(idx + 1, 0);
+    if (cache.size() <= idx) {
+        cache.resize(idx + 1, 0);
+        cus_cache.resize(idx + 1, 0);
+    }
     if (cache[idx] == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             cus = 1;
+        cus_cache[idx] = cus;
         cache[idx] = cus * fwd_bf16_ctas_per_cu(D);
     }
+    if (cus_out) *cus_out = cus_cache[idx];
     return cache[idx];
 }
 
@@ -220,7 +225,10 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
     }
     size_t max_units = 1;
     for (const auto& v : xu) max_units = std::max(max_units, v.size());
-    int64_t nb64 = std::max<int64_t>(device_capacity(lay->device, D) / kXcds, need);
+    int cus = 1;
+    const int capacity = device_capacity(lay->device, D, &cus);
+    const int32_t cus_per_xcd = std::max(1, cus / kXcds);
+    int64_t nb64 = std::max<int64_t>(capacity / kXcds, need);
     nb64 = std::min<int64_t>(nb64, (int64_t)max_units);
     if (nb64 * kXcds >= ((int64_t)1 << 31)) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
     int32_t n_bins = (int32_t)std::max<int64_t>(nb64, 1);
@@ -247,16 +255,35 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
             for (size_t u = 0; u < v.size(); ++u) order[u] = (int32_t)u;
             std::stable_sort(order.begin(), order.end(),
                              [&](int32_t a2, int32_t b2) { return v[(size_t)a2].tiles > v[(size_t)b2].tiles; });
-            using Load = std::pair<int64_t, int32_t>;   // (load, bin), least loaded first, then lowest bin
-            std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
-            for (int32_t i = 0; i < nbins; ++i) heap.push({0, i});
-            for (int32_t u : order) {
-                Load t = heap.top();
-                heap.pop();
-                bins[(size_t)t.second].push_back(u);
-                tiles_in[(size_t)t.second] += v[(size_t)u].tiles;
-                heap.push({t.first + v[(size_t)u].tiles + 2, t.second});
+            using Load = std::pair<int64_t, int32_t>;   // (load, index), least loaded first, then lowest
+            // Least-loaded-first packing of `items` (indices into v, by decreasing cost) into n slots.
+            auto lpt = [&](const std::vector<int32_t>& items, int32_t n) {
+                std::vector<std::vector<int32_t>> out((size_t)n);
+                std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+                for (int32_t i = 0; i < n; ++i) heap.push({0, i});
+                for (int32_t u : items) {
+                    Load t = heap.top();
+                    heap.pop();
+                    out[(size_t)t.second].push_back(u);
+                    heap.push({t.first + v[(size_t)u].tiles + 2, t.second});
+                }
+                return out;
+            };
+            if (nbins % cus_per_xcd == 0 && nbins > cus_per_xcd) {
+                // Workgroups b, b + cus_per_xcd, b + 2 cus_per_xcd, ... of an XCD share a
+                // CU (measured dispatch order), and co-resident workgroups share its
+                // SIMDs: balance the work per CU first, then split each CU's share.
+                const auto per_cu = lpt(order, cus_per_xcd);
+                const int32_t per = nbins / cus_per_xcd;
+                for (int32_t c = 0; c < cus_per_xcd; ++c) {
+                    const auto split = lpt(per_cu[(size_t)c], per);
+                    for (int32_t m = 0; m < per; ++m) bins[(size_t)(c + m * cus_per_xcd)] = split[(size_t)m];
+                }
+            } else {
+                bins = lpt(order, nbins);
             }
+            for (int32_t i = 0; i < nbins; ++i)
+                for (int32_t u : bins[(size_t)i]) tiles_in[(size_t)i] += v[(size_t)u].tiles;
             for (int32_t i = 0; i < nbins; ++i)
                 if (bins[(size_t)i].size() > (size_t)kMaxBinUnits || tiles_in[(size_t)i] > kMaxBinTiles) return false;
             for (auto& bn : bins) {
