@@ -33,11 +33,13 @@
 //    rounded to bf16, are the B operand of the PV product (the order of a
 //    contraction index is free as long as both operands agree).
 //  * Online softmax in the log2 domain, p = exp2(s*scale*log2e - m): one FMA
-//    into v_exp_f32 (half rate on gfx950).  The running max m is only raised
-//    when a tile's max exceeds it by more than kLazyMax (so p <= 2^kLazyMax,
-//    harmless in fp32 and bf16), which skips the O rescale on almost every
-//    tile.  Row sums add the fp32 probabilities (v_dot2c_f32_bf16 on the bf16
-//    P gave wrong sums on gfx950 in testing, so it is not used).
+//    into v_exp_f32 (half rate on gfx950).  The running max m is taken from
+//    the first tile of a unit and afterwards raised only when half a tile's
+//    probabilities sum past kSumCap in some lane (then O and l are rescaled
+//    and that half is redone), so the per-tile row max and the O rescale are
+//    skipped on almost every tile and no probability overflows.  Row sums add
+//    the fp32 probabilities (a chained v_dot2c_f32_bf16 over the bf16 P gave
+//    wrong sums on gfx950 in testing, so it is not used).
 //  * Rows longer than 16 blocks (global rows, routed tiles) are split into
 //    chunks run by different workgroups; each writes a normalised fp32
 //    partial and its LSE, and a small second launch merges them by
@@ -68,7 +70,10 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazyMax = 8.0f;   // log2 units: p never exceeds 2^8
+// A lane's 16 probabilities of half a tile may sum to at most this before the
+// running max is raised.  Besides preventing overflow it keeps a dominant
+// probability near 1, where its bf16 rounding is exact or small.
+constexpr float kSumCap = 256.0f;
 constexpr int kThreads = 128;      // 2 waves per workgroup
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -392,9 +397,22 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                 va[c][db] = as_bf16x8(lh);
             }
     };
-    // Online softmax, first half: mask the tile's scores (key block j), raise
-    // the running max lazily (rescaling O and l), return the max to subtract.
-    auto softmax_max = [&](int j, int kind, int tq, int valid, f32x16_t (&s)[2]) -> float {
+    // Row max of a tile's scores in log2 units (pair of lanes = one query row).
+    auto tile_max = [&](const f32x16_t (&s)[2]) -> float {
+        float mx = __builtin_fmaxf(__builtin_fmaxf(s[0][0], s[0][1]), s[1][0]);
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][i]), s[0][i + 1]);
+#pragma unroll
+        for (int i = 1; i < 15; i += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[1][i]), s[1][i + 1]);
+        mx = __builtin_fmaxf(mx, s[1][15]);
+        return pair_max(mx) * c2;
+    };
+    // Online softmax, first half: mask the tile's scores (key block j); on the
+    // first tile of a unit take the running max from the tile itself.  Later
+    // tiles keep the running max m as it is: the max is raised only when a
+    // tile's probabilities grow too large (see softmax_pv), which on typical
+    // rows happens rarely -- so no per-tile max is computed.
+    auto softmax_prep = [&](int j, int kind, int tq, int valid, f32x16_t (&s)[2], bool first) {
         if (MASK == MASK_PAD) {
             if (j * 64 + 64 > valid) {
 #pragma unroll
@@ -414,50 +432,58 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                             s[kb][i] = -INFINITY;
             }
         }
-        float mx = __builtin_fmaxf(__builtin_fmaxf(s[0][0], s[0][1]), s[1][0]);
+        if (first) m = tile_max(s);   // o = 0 and l = 0 here
+    };
+    // Online softmax, second half, for the key chunks c0, c0 + 1 (16 keys each):
+    // P = exp2(s * c2 - m) as the bf16 B operand of the PV product (pf[c]
+    // element e <-> key 16c + 8(e/4) + 4hh + e%4), row sums in fp32.  If the
+    // chunks' probabilities sum past kSumCap in some lane (or a row whose max
+    // is still -inf meets a finite score), the running max is raised to the
+    // tile's max, O and l are rescaled -- they hold only contributions made
+    // with the old max -- and the chunks are redone.  So every probability
+    // stays below kSumCap and nothing overflows.
+    auto softmax_exp = [&](const f32x16_t (&s)[2], auto c0, u32x4_t (&u)[2]) {
+        constexpr int C0 = decltype(c0)::value;
+        float lsum;
+        auto chunks = [&]() {
+            const float muse = m == -INFINITY ? 0.f : m;
+            float acc[8];
 #pragma unroll
-        for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][i]), s[0][i + 1]);
+            for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int i = 1; i < 15; i += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[1][i]), s[1][i + 1]);
-        mx = __builtin_fmaxf(mx, s[1][15]);
-        mx = pair_max(mx) * c2;
-        const bool raise = mx > m + kLazyMax;
-        if (__ballot(raise) != 0) {          // wave-uniform: rescale only when some row's max jumped
+                for (int e = 0; e < 4; ++e) {
+                    const int c = C0 + k;
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][8 * (c % 2) + 2 * e], c2, -muse));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][8 * (c % 2) + 2 * e + 1], c2, -muse));
+                    u[k][e] = pack_bf16x2(p0, p1);
+                    acc[4 * k + e] = p0 + p1;
+                }
+            lsum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+        };
+        chunks();
+        const bool bad = lsum > kSumCap || (m == -INFINITY && lsum > 0.f);
+        if (__ballot(bad) != 0) {          // wave-uniform, rare
+            const float mx = tile_max(s);
+            const bool raise = mx > m;
             const float alpha = raise ? __builtin_amdgcn_exp2f(m - mx) : 1.f;   // 0 when m was -inf
-            const float mn = raise ? mx : m;
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-            m = mn;
+            m = raise ? mx : m;
+            chunks();
         }
-        return m == -INFINITY ? 0.f : m;
+        l += lsum;
     };
-    // Online softmax, second half: P = exp2(s * c2 - muse) as the bf16 B
-    // operand of the PV product (pf[c] element e <-> key 16c + 8(e/4) + 4hh + e%4),
-    // row sums in fp32, and O^T += V^T P^T.
-    // Key chunks c0 .. c1 - 1 (16 keys each) of the tile.
-    auto softmax_pv = [&](const f32x16_t (&s)[2], float muse, const bf16x8_t (&va)[4][NDB], auto c0, auto c1) {
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    // O^T += V^T P^T for the key chunks c0, c0 + 1.
+    auto pv = [&](const bf16x8_t (&va)[4][NDB], auto c0, const u32x4_t (&u)[2]) {
+        constexpr int C0 = decltype(c0)::value;
 #pragma unroll
-        for (int c = decltype(c0)::value; c < decltype(c1)::value; ++c) {
-            u32x4_t u;
-            float acc[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][8 * (c % 2) + 2 * e], c2, -muse));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][8 * (c % 2) + 2 * e + 1], c2, -muse));
-                u[e] = pack_bf16x2(p0, p1);
-                acc[e] = p0 + p1;
-            }
-            ls[c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            const bf16x8_t pf = as_bf16x8(u);
+        for (int k = 0; k < 2; ++k)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c][db], pf, o[db], 0, 0, 0);
-        }
-        l += (ls[decltype(c0)::value] + ls[decltype(c0)::value + 1]);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[C0 + k][db], as_bf16x8(u[k]), o[db], 0, 0, 0);
     };
 
     // ---- software pipeline over the flat tile list ----
@@ -509,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     // and it covers the latency of the previous step's output stores.
     auto step = [&](auto parity, int f, f32x16_t (&s_now)[2], f32x16_t (&s_next)[2]) {
         constexpr int P = decltype(parity)::value;
-        const float muse = softmax_max(tile_j(e0), kind_cur, tq_cur, valid_cur, s_now);
+        softmax_prep(tile_j(e0), kind_cur, tq_cur, valid_cur, s_now, (e0 & kTileFirst) != 0);
         wait_vmcnt<0>();
         stage_barrier();
         // Q of the next unit: loaded during the first step of the current unit
@@ -547,22 +573,24 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         // discarded), interleaved by the scheduler with the softmax of tile f.
         using C0 = std::integral_constant<int, 0>;
         using C2 = std::integral_constant<int, 2>;
-        using C4 = std::integral_constant<int, 4>;
+        u32x4_t pA[2], pB[2];
         smma(kf, qf, s_next);
-        softmax_pv(s_now, muse, va, C0(), C2());
+        softmax_exp(s_now, C0(), pA);
         __builtin_amdgcn_sched_group_barrier(0x100, 8 + 8 * NDB, 0);   // LDS reads first
 #pragma unroll
-        for (int i = 0; i < 8 + 2 * NDB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
         }
         if (f + 1 < F) issue_half<D>(gbase(a.v, tile_g(e1)), tile_j(e1), voffs, vl0 + (1 - P) * TILE * 2);
-        softmax_pv(s_now, muse, va, C2(), C4());
+        pv(va, C0(), pA);
+        softmax_exp(s_now, C2(), pB);
 #pragma unroll
         for (int i = 0; i < 2 * NDB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // then eight VALU
         }
+        pv(va, C2(), pB);
         if (e0 & kTileLast) {
             // ---- unit done: O = acc / l, LSE = (m + log2 l) ln 2 ----
             const float lt = pair_sum(l);
