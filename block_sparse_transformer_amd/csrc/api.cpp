@@ -193,7 +193,7 @@ int device_capacity(int dev, int32_t D, int* cus_out = nullptr) {
 // groups in the same order and the XCD's K/V working set stays near one
 // group (which fits in its L2).  For every bin the device gets the unit
 // records and the flat list of the units' key blocks in order, at most
-// kMaxBinUnits units and kMaxBinTiles tiles per bin.
+// max_bin_units units and max_bin_tiles tiles per bin.
 bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32_t nru, int32_t rct,
                            int32_t r_chunks, hipStream_t stream, bsattn_layout::Sched* out) {
     const int32_t ipH = lay->items_per_head;
@@ -216,20 +216,27 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
         }
         for (int32_t r = 0; r < nru; ++r) v.push_back({(int32_t)g, -1 - r, routed_len(r), (int32_t)v.size()});
     }
+    // D = 64 runs one workgroup of kQWaves waves per CU, one list (bin) per
+    // wave; D = 128 one list per workgroup.
+    const bool per_wave = D == 64;
+    const int32_t max_bin_units = kMaxBinUnits;
+    const int32_t max_bin_tiles = kMaxBinTiles;
     int64_t need = 1;
     for (const auto& v : xu) {
         int64_t t = 0;
         for (const auto& u : v) t += u.tiles;
-        need = std::max<int64_t>(need, ((int64_t)v.size() + kMaxBinUnits - 1) / kMaxBinUnits);
-        need = std::max<int64_t>(need, (t + kMaxBinTiles / 2 - 1) / (kMaxBinTiles / 2));
+        need = std::max<int64_t>(need, ((int64_t)v.size() + max_bin_units - 1) / max_bin_units);
+        need = std::max<int64_t>(need, (t + max_bin_tiles / 2 - 1) / (max_bin_tiles / 2));
     }
     size_t max_units = 1;
     for (const auto& v : xu) max_units = std::max(max_units, v.size());
     int cus = 1;
     const int capacity = device_capacity(lay->device, D, &cus);
     const int32_t cus_per_xcd = std::max(1, cus / kXcds);
-    int64_t nb64 = std::max<int64_t>(capacity / kXcds, need);
+    const int32_t lists_per_wg = per_wave ? kQWaves : 1;
+    int64_t nb64 = std::max<int64_t>((int64_t)capacity * lists_per_wg / kXcds, need);
     nb64 = std::min<int64_t>(nb64, (int64_t)max_units);
+    nb64 = (nb64 + lists_per_wg - 1) / lists_per_wg * lists_per_wg;   // whole workgroups
     if (nb64 * kXcds >= ((int64_t)1 << 31)) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
     int32_t n_bins = (int32_t)std::max<int64_t>(nb64, 1);
 
@@ -270,13 +277,22 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
                 return out;
             };
             if (nbins % cus_per_xcd == 0 && nbins > cus_per_xcd) {
-                // Workgroups b, b + cus_per_xcd, b + 2 cus_per_xcd, ... of an XCD share a
-                // CU (measured dispatch order), and co-resident workgroups share its
-                // SIMDs: balance the work per CU first, then split each CU's share.
+                // Bins b, b + cus_per_xcd, b + 2 cus_per_xcd, ... of an XCD run on one
+                // CU (workgroups of one CU, measured dispatch order; or the waves of
+                // one workgroup), and they share its SIMDs: balance the work per CU
+                // first, then split each CU's share -- in pairs of equal load when
+                // the waves of a SIMD pair up (lists 2s and 2s + 1).
                 const auto per_cu = lpt(order, cus_per_xcd);
                 const int32_t per = nbins / cus_per_xcd;
+                const bool pairs = per_wave && per % 2 == 0;
                 for (int32_t c = 0; c < cus_per_xcd; ++c) {
-                    const auto split = lpt(per_cu[(size_t)c], per);
+                    std::vector<std::vector<int32_t>> split;
+                    if (pairs) {
+                        for (const auto& pr : lpt(per_cu[(size_t)c], per / 2))
+                            for (auto& one : lpt(pr, 2)) split.push_back(std::move(one));
+                    } else {
+                        split = lpt(per_cu[(size_t)c], per);
+                    }
                     for (int32_t m = 0; m < per; ++m) bins[(size_t)(c + m * cus_per_xcd)] = split[(size_t)m];
                 }
             } else {
@@ -285,11 +301,12 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
             for (int32_t i = 0; i < nbins; ++i)
                 for (int32_t u : bins[(size_t)i]) tiles_in[(size_t)i] += v[(size_t)u].tiles;
             for (int32_t i = 0; i < nbins; ++i)
-                if (bins[(size_t)i].size() > (size_t)kMaxBinUnits || tiles_in[(size_t)i] > kMaxBinTiles) return false;
+                if (bins[(size_t)i].size() > (size_t)max_bin_units || tiles_in[(size_t)i] > max_bin_tiles) return false;
             for (auto& bn : bins) {
                 std::sort(bn.begin(), bn.end(),
                           [&](int32_t a2, int32_t b2) { return v[(size_t)a2].order < v[(size_t)b2].order; });
                 int32_t k = 0;
+                const size_t bin_tile0 = tiles.size();
                 for (int32_t u : bn) {
                     const Unit& un = v[(size_t)u];
                     const int32_t h = un.g % lay->H;
@@ -297,11 +314,11 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
                     const bool routed = un.id < 0;
                     if (!routed) {
                         const WorkItem& wi = lay->items[(size_t)h * ipH + un.id];
-                        units.push_back(make_int4(wi.row % lay->nb, wi.slot, un.g, 0));
+                        units.push_back(make_int4(wi.row % lay->nb, wi.slot, un.g, (int32_t)(tiles.size() - bin_tile0)));
                         first = wi.col_begin;
                     } else {
                         const int32_t r = -1 - un.id;
-                        units.push_back(make_int4(-1 - r / r_chunks, r % r_chunks, un.g, 0));
+                        units.push_back(make_int4(-1 - r / r_chunks, r % r_chunks, un.g, (int32_t)(tiles.size() - bin_tile0)));
                         first = (r % r_chunks) * rct;
                     }
                     for (int32_t t = 0; t < un.tiles; ++t) {
@@ -319,7 +336,8 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
     };
     while (!pack(n_bins)) {
         if ((size_t)n_bins >= max_units) return fail(BSATTN_ERR_UNSUPPORTED, "a unit exceeds the per-workgroup tile list");
-        n_bins = (int32_t)std::min<size_t>(max_units, (size_t)n_bins * 2);
+        const int64_t nn = std::min<int64_t>((int64_t)max_units, (int64_t)n_bins * 2);
+        n_bins = (int32_t)((nn + lists_per_wg - 1) / lists_per_wg * lists_per_wg);
     }
     if (units.empty()) units.push_back(make_int4(0, -1, 0, 0));
     if (tiles.empty()) tiles.push_back(0);

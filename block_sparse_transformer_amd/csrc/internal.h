@@ -38,7 +38,9 @@ struct MergeItem {
 
 constexpr int kXcds = 8;
 constexpr int kMaxBinUnits = 64;     // units of one workgroup (one per lane)
-constexpr int kMaxBinTiles = 1024;   // tiles of one workgroup (its list lives in LDS)
+constexpr int kMaxBinTiles = 512;    // tiles of one workgroup (its list lives in LDS)
+// D = 64 kernel: one workgroup of kQWaves waves per CU, one unit/tile list per wave
+constexpr int kQWaves = 8;
 // Flat tile entry of a workgroup's list: key block | unit << 20 | first | last.
 constexpr int kTileJ = (1 << 20) - 1;
 constexpr int kTileUnitShift = 20;
@@ -73,12 +75,13 @@ struct FwdArgs {
     int32_t n_items, n_merges;
     int32_t items_per_head;   // explicit items per head (NOP-padded to equal length)
     // persistent schedule: n_bins workgroups per XCD.  Workgroup (x, bin)
-    // runs units units[unit_ptr[x*n_bins+bin] ..) -- {kind, slot, group}:
-    // kind >= 0 the query block of a layout row (slot: partial slot within a
-    // batch entry, -1 for a whole row), kind < 0 routed tile -1-kind (slot:
-    // chunk); group = b * H + h -- over the flat tile list
+    // runs units units[unit_ptr[x*n_bins+bin] ..) -- {kind, slot, group,
+    // first tile}: kind >= 0 the query block of a layout row (slot: partial
+    // slot within a batch entry, -1 for a whole row), kind < 0 routed tile
+    // -1-kind (slot: chunk); group = b * H + h; first tile: offset of the
+    // unit's tiles in the bin's list -- over the flat tile list
     // tiles[tile_ptr[x*n_bins+bin] ..), entries key block | unit << 20 |
-    // kTileFirst | kTileLast.
+    // kTileFirst | kTileLast (unit: index within the bin).
     int32_t n_bins;
     const int4* units;
     const int32_t* unit_ptr;

@@ -615,6 +615,457 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// D = 64: one workgroup of eight waves per CU, two waves per SIMD.  A wave owns
+// a whole 64-row query tile, so each K and V fragment it reads from LDS feeds
+// both 32-row halves, and it walks its own list of tiles with no barrier:
+// every wave has its own single K and V buffer (16 KB).  Within a step the
+// wave reads the tile's fragments first; the loads of its next tile then go
+// into the same buffers while it runs the softmax and the PV products.
+//
+// The two waves that share a SIMD get lists of equal length, and they keep
+// pace with each other: the SIMD's issue arbiter favours the older wave, so
+// left alone the younger one would fall behind and finish long after it,
+// running by itself with nothing to hide its latencies.  Each wave posts the
+// tiles it has left in LDS and, while it has more left than its partner,
+// raises its issue priority.
+constexpr int kQThreads = 64 * kQWaves;
+
+// Four direct loads of one wave, 1 KB apart: load r lands at m0v + 1024 r - 2048 + 16 lane.
+__device__ __forceinline__ void lds_load16x4_1k(uint32_t voff, const void* sbase, uint32_t m0v) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3 offset:-2048\n\t"
+        "global_load_lds_dwordx4 %1, %3 offset:-1024\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "global_load_lds_dwordx4 %1, %3 offset:1024\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(m0v), "s"(sbase)
+        : "memory");
+}
+
+// A whole 64x64 bf16 tile (8 KB) by one wave: 8 loads of 1 KB, rows in order,
+// in two groups of four (rows 0..31, 32..63).  voff is the lane's byte offset
+// within a group (rows 0..7) plus 2 KB; one register serves both groups.
+__device__ __forceinline__ void issue_tile1(const uint16_t* base, int j, uint32_t voff, uint32_t lds) {
+    const uint16_t* t = base + (size_t)j * 64 * 64;
+    lds_load16x4_1k(voff, t, lds + 2048);
+    lds_load16x4_1k(voff, t + 32 * 64, lds + 4096 + 2048);
+}
+
+template <int MASK>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_q_kernel(const FwdArgs a) {
+    constexpr int D = 64, NC = 4, NDB = 2, TILE = 64 * 64;
+    __shared__ __attribute__((aligned(1024))) uint16_t kvbuf[kQWaves][2][TILE];
+    __shared__ int flats[kQWaves][kMaxBinTiles];   // each wave's tile list
+    __shared__ int simd_of[kQWaves];
+    __shared__ int left[kQWaves];                  // tiles each wave has not finished
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in a scalar register
+    const int ql = lane & 31;
+    const int hh = lane >> 5;
+
+    // Which waves share a SIMD (HW_ID bits 5:4).  With two waves on every
+    // SIMD, the waves of SIMD s run lists 2s and 2s + 1 and pace each other;
+    // otherwise wave w runs list w on its own.
+    const int my_simd = (__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3;
+    if (lane == 0) {
+        simd_of[wv] = my_simd;
+        left[wv] = 0;
+    }
+    __syncthreads();
+    int rank = 0, partner = -1;
+    bool paired = true;
+    for (int s2 = 0; s2 < 4; ++s2) {
+        int n_on = 0;
+        for (int w = 0; w < kQWaves; ++w) n_on += simd_of[w] == s2;
+        paired = paired && n_on == 2;
+    }
+    for (int w = 0; w < kQWaves; ++w)
+        if (w != wv && simd_of[w] == my_simd) {
+            partner = w;
+            rank += w < wv;
+        }
+    const int list = paired ? 2 * my_simd + rank : wv;
+    if (!paired) partner = -1;
+    int* const flat = flats[wv];
+
+    const int x = blockIdx.x % kXcds;
+    const int bin = blockIdx.x / kXcds + list * (a.n_bins / kQWaves);
+    const int bi = x * a.n_bins + bin;
+    const int up0 = a.unit_ptr[bi], nu = a.unit_ptr[bi + 1] - up0;   // <= kMaxBinUnits
+    const int tp0 = a.tile_ptr[bi], nt = a.tile_ptr[bi + 1] - tp0;   // <= kMaxBinTiles
+    if (nu <= 0) return;
+
+    int u_kind = 0, u_slot = -1, u_g = 0, u_valid = a.L;
+    if (lane < nu) {
+        const int4 r = a.units[up0 + lane];
+        const int ub = r.z / a.H;
+        u_kind = r.x;
+        u_g = r.z;
+        if (r.x >= 0) u_slot = r.y < 0 ? -1 : ub * a.n_slots + r.y;
+        else u_slot = a.r_slot_base + (r.z * a.n_rt + (-1 - r.x)) * a.r_chunks + r.y;
+        if (MASK == MASK_PAD) u_valid = min(max(a.valid_len[ub], 0), a.L);
+    }
+    auto rd = [](int v, int k) -> int { return __builtin_amdgcn_readlane(v, k); };
+    auto gbase = [&](const void* t, int g) -> const uint16_t* {
+        return (const uint16_t*)t + (size_t)g * a.L * D;
+    };
+    // token of query row r (0..63) of a unit (-1: unused routed row)
+    auto query_token = [&](int kind, int g, int r) -> int {
+        if (kind >= 0) return kind * 64 + r;
+        const int kk = (-1 - kind) * 64 + r;
+        const int t = kk < a.n_routed ? a.routed_rows[(size_t)g * a.n_routed + kk] : -1;
+        return (t >= a.L) ? -1 : t;
+    };
+    // Q^T fragments of both halves: qf[qb][c] holds Q[row 32qb + ql][16c + 8hh .. +7].
+    auto load_q = [&](int kind, int g, bf16x8_t (&qf)[2][NC], int (&tq)[2]) {
+        const uint16_t* qp = gbase(a.q, g);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            tq[qb] = query_token(kind, g, 32 * qb + ql);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                u32x4_t u = {0u, 0u, 0u, 0u};
+                if (tq[qb] >= 0) u = *(const u32x4_t*)(qp + (size_t)tq[qb] * D + 16 * c + 8 * hh);
+                qf[qb][c] = as_bf16x8(u);
+            }
+        }
+    };
+    auto store_half = [&](int slot, int t, int g, int r, const f32x16_t (&ov)[NDB], float inv, float lse_v) {
+        if (t < 0) return;
+        const size_t bh = (size_t)g;
+        // O^T register i of block db <-> d = 32db + 8(i/4) + 4hh + i%4
+        if (slot < 0) {
+            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D;
+            // Lanes l and l + 32 hold d = 8gq + 0..3 and 8gq + 4..7 of the same
+            // row: swapping halves (v_permlane32_swap moves the upper half-wave's
+            // first operand to the lower half-wave's second, and back) leaves
+            // each lane 8 consecutive d, 16 bytes: even gq in the lower
+            // half-wave, odd gq in the upper.
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int ge = 2 * pr, go = 2 * pr + 1;
+                    const uint32_t e0 = pack_bf16x2(ov[db][4 * ge + 0] * inv, ov[db][4 * ge + 1] * inv);
+                    const uint32_t e1 = pack_bf16x2(ov[db][4 * ge + 2] * inv, ov[db][4 * ge + 3] * inv);
+                    const uint32_t o0 = pack_bf16x2(ov[db][4 * go + 0] * inv, ov[db][4 * go + 1] * inv);
+                    const uint32_t o1 = pack_bf16x2(ov[db][4 * go + 2] * inv, ov[db][4 * go + 3] * inv);
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(e0, o0, false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(e1, o1, false, false);
+                    const u32x4_t w4 = {s0[0], s1[0], s0[1], s1[1]};
+                    *(u32x4_t*)(orow + 32 * db + 16 * pr + 8 * hh) = w4;
+                }
+            if (hh == 0) a.lse[bh * a.L + t] = lse_v;
+        } else {
+            float* orow = a.ws_o + ((size_t)slot * 64 + r) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    *(float4*)(orow + 32 * db + 8 * gq + 4 * hh) =
+                        make_float4(ov[db][4 * gq] * inv, ov[db][4 * gq + 1] * inv, ov[db][4 * gq + 2] * inv,
+                                    ov[db][4 * gq + 3] * inv);
+            if (hh == 0) a.ws_lse[(size_t)slot * 64 + r] = lse_v;
+        }
+    };
+    // ---- tile list -> LDS (key padding: drop tiles past the valid length) ----
+    int F = nt;
+    uint64_t empty_units = 0;
+    if (MASK != MASK_PAD) {
+        for (int i = lane; i < nt; i += 64) flat[i] = a.tiles[tp0 + i];
+    } else {
+        int kept_total = 0;
+        for (int base = 0; base < nt; base += 64) {
+            const int i = base + lane;
+            const int e = i < nt ? a.tiles[tp0 + i] : 0;
+            const int en = i + 1 < nt ? a.tiles[tp0 + i + 1] : 0;
+            const int valid = __shfl(u_valid, tile_unit(e));
+            const bool keep = i < nt && tile_j(e) * 64 < valid;
+            const bool keep_next = i + 1 < nt && !(e & kTileLast) && tile_j(en) * 64 < valid;
+            const uint64_t km = __ballot(keep);
+            const int pos = kept_total + __builtin_popcountll(km & ((1ull << lane) - 1ull));
+            if (keep) flat[pos] = keep_next ? (e & ~kTileLast) : (e | kTileLast);
+            const uint64_t em = __ballot(i < nt && (e & kTileFirst) && !keep);
+            for (uint64_t mm = em; mm; mm &= mm - 1) empty_units |= 1ull << tile_unit(rd(e, __builtin_ctzll(mm)));
+            kept_total += __builtin_popcountll(km);
+        }
+        F = kept_total;
+        const f32x16_t zero[NDB] = {};
+        for (uint64_t mm = empty_units; mm; mm &= mm - 1) {
+            const int u = __builtin_ctzll(mm);
+            const int g = rd(u_g, u), kind = rd(u_kind, u), slot = rd(u_slot, u);
+            for (int qb = 0; qb < 2; ++qb)
+                store_half(slot, query_token(kind, g, 32 * qb + ql), g, 32 * qb + ql, zero, 0.f, -INFINITY);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the list is in LDS
+    if (F == 0) return;
+
+    // Fragment read offsets (elements), as in the two-wave kernel.  The
+    // swizzles depend on the row only through row & 7 (K) and row & 3 (V), so
+    // rows 32 apart (K) and 8 apart (V) share a lane offset and differ by a
+    // constant that goes into the read instruction.
+    int koff[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) koff[c] = ql * D + swz_k(ql, 2 * c + hh) * 8;
+    const int gi = lane & 15, gsel = (lane >> 4) & 1;
+    int voff[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int row = 4 * hh + (gi >> 2);
+        const int d0 = 32 * db + 16 * gsel + 4 * (gi & 3);
+        voff[db] = row * D + swz_v(row, d0 >> 3) * 8 + (d0 & 7);
+    }
+    // Direct-load offsets: load r covers rows 8r .. 8r + 7, lane -> row 8r + lane/8,
+    // piece lane%8; the swizzle depends on the row only through lane/8.
+    uint32_t kdo, vdo;
+    {
+        const int row0 = lane >> 3, q = lane & 7;
+        kdo = (uint32_t)(row0 * D + swz_k(row0, q) * 8) * 2u + 2048u;
+        vdo = (uint32_t)(row0 * D + swz_v(row0, q) * 8) * 2u + 2048u;
+    }
+    const uint16_t* kbuf = kvbuf[wv][0];
+    const uint16_t* vbuf = kvbuf[wv][1];
+    const uint32_t kl = lds_addr(kbuf), vl = lds_addr(vbuf);
+
+    auto kread = [&](const uint16_t* Ks, bf16x8_t (&kf)[2][NC]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) kf[kb][c] = as_bf16x8(*(const u32x4_t*)(Ks + koff[c] + 32 * kb * D));
+    };
+    // S^T = K Q^T for both halves: s[kb][qb] register i <-> key 32kb + 8(i/4) + 4hh + i%4.
+    auto smma = [&](const bf16x8_t (&kf)[2][NC], const bf16x8_t (&q)[2][NC], f32x16_t (&s)[2][2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][c], q[qb][c], s[kb][qb], 0, 0, 0);
+    };
+    // V^T fragments (A operand of O^T = V^T P^T), transposed on read.
+    auto vread = [&](const uint16_t* Vs, bf16x8_t (&va)[4][NDB]) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t*)(Vs + voff[db] + 16 * c * D));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t*)(Vs + voff[db] + (16 * c + 8) * D));
+                const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+                const u32x4_t lh = {l2.x, l2.y, h2.x, h2.y};
+                va[c][db] = as_bf16x8(lh);
+            }
+    };
+
+    const float c2 = a.scale_log2;
+    f32x16_t o[NDB][2];
+    float m[2], l[2];
+    auto reset = [&]() {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][qb][i] = 0.f;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            m[qb] = -INFINITY;
+            l[qb] = 0.f;
+        }
+    };
+    // row max (log2 units) of one half
+    auto tile_max = [&](const f32x16_t (&s)[2][2], int qb) -> float {
+        float v = __builtin_fmaxf(__builtin_fmaxf(s[0][qb][0], s[0][qb][1]), s[1][qb][0]);
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) v = __builtin_fmaxf(__builtin_fmaxf(v, s[0][qb][i]), s[0][qb][i + 1]);
+#pragma unroll
+        for (int i = 1; i < 15; i += 2) v = __builtin_fmaxf(__builtin_fmaxf(v, s[1][qb][i]), s[1][qb][i + 1]);
+        return pair_max(__builtin_fmaxf(v, s[1][qb][15])) * c2;
+    };
+    // masks; on a unit's first tile, the running max is the tile's max
+    auto softmax_prep = [&](int j, int kind, const int (&tq)[2], int valid, f32x16_t (&s)[2][2], bool first) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            if (MASK == MASK_PAD) {
+                if (j * 64 + 64 > valid) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            if (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) s[kb][qb][i] = -INFINITY;
+                }
+            }
+            if (MASK == MASK_BAND) {
+                if (kind >= 0) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            if (abs(tq[qb] - (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4))) > a.band)
+                                s[kb][qb][i] = -INFINITY;
+                }
+            }
+            if (first) m[qb] = tile_max(s, qb);
+        }
+    };
+    // Probabilities of half qb, key chunks c0 and c0 + 1.  The running max is
+    // raised only when a lane's probabilities would sum past kSumCap (or a
+    // -inf max meets a finite score): then O and l are rescaled to the tile's
+    // max and the chunk pair is redone.
+    auto softmax_exp = [&](const f32x16_t (&s)[2][2], int qb, auto c0, u32x4_t (&u)[2]) {
+        constexpr int C0 = decltype(c0)::value;
+        float lsum;
+        auto chunks = [&]() {
+            const float muse = m[qb] == -INFINITY ? 0.f : m[qb];
+            float acc[8];
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = C0 + k;
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][qb][8 * (c % 2) + 2 * e], c2, -muse));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][qb][8 * (c % 2) + 2 * e + 1], c2, -muse));
+                    u[k][e] = pack_bf16x2(p0, p1);
+                    acc[4 * k + e] = p0 + p1;
+                }
+            lsum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+        };
+        chunks();
+        const bool bad = lsum > kSumCap || (m[qb] == -INFINITY && lsum > 0.f);
+        if (__ballot(bad) != 0) {          // wave-uniform, rare
+            const float mx = tile_max(s, qb);
+            const bool raise = mx > m[qb];
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m[qb] - mx) : 1.f;
+            l[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha;
+            m[qb] = raise ? mx : m[qb];
+            chunks();
+        }
+        l[qb] += lsum;
+    };
+    auto pv = [&](const bf16x8_t (&va)[4][NDB], int qb, auto c0, const u32x4_t (&u)[2]) {
+        constexpr int C0 = decltype(c0)::value;
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[C0 + k][db], as_bf16x8(u[k]), o[db][qb], 0, 0, 0);
+    };
+
+    // ---- walk the tile list ----
+    int e0 = __builtin_amdgcn_readfirstlane(flat[0]);
+    auto tile_g = [&](int e) -> int { return rd(u_g, tile_unit(e)); };
+    int u_cur = tile_unit(e0);
+    int kind_cur = rd(u_kind, u_cur), slot_cur = rd(u_slot, u_cur), g_cur = rd(u_g, u_cur);
+    int valid_cur = rd(u_valid, u_cur);
+    int tq_cur[2];
+    bf16x8_t qf[2][NC];
+    load_q(kind_cur, g_cur, qf, tq_cur);
+    issue_tile1(gbase(a.k, g_cur), tile_j(e0), kdo, kl);
+    issue_tile1(gbase(a.v, g_cur), tile_j(e0), vdo, vl);
+    reset();
+
+    // A unit's epilogue (normalise, store O and LSE, reset) runs in the next
+    // step, after that step's first loads are issued: the stores then have a
+    // whole step to drain before the wave next waits on its memory counter.
+    bool pend = false;
+    int p_slot = -1, p_g = 0, p_tq[2] = {-1, -1};
+    auto finish = [&]() {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float lt = pair_sum(l[qb]);
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            const float lse_v = lt > 0.f ? (m[qb] + log2f(lt)) * kLn2 : -INFINITY;
+            const f32x16_t oq[NDB] = {o[0][qb], o[1][qb]};
+            store_half(p_slot, p_tq[qb], p_g, 32 * qb + ql, oq, inv, lse_v);
+        }
+        reset();
+    };
+
+    using C0 = std::integral_constant<int, 0>;
+    using C2 = std::integral_constant<int, 2>;
+    for (int f = 0; f < F; ++f) {
+        const int e1 = f + 1 < F ? __builtin_amdgcn_readfirstlane(flat[f + 1]) : 0;
+        if (lane == 0) left[wv] = F - f;
+        const int partner_left = partner >= 0 ? __builtin_amdgcn_readfirstlane(left[partner]) : 0;
+        if ((e0 & kTileFirst) && f > 0) {   // a new unit: its Q (the load's latency is covered by the other wave)
+            u_cur = tile_unit(e0);
+            kind_cur = rd(u_kind, u_cur);
+            slot_cur = rd(u_slot, u_cur);
+            g_cur = rd(u_g, u_cur);
+            valid_cur = rd(u_valid, u_cur);
+            load_q(kind_cur, g_cur, qf, tq_cur);
+        }
+        wait_vmcnt<0>();                   // K(f), V(f) and Q in place
+        asm volatile("" ::: "memory");
+        bf16x8_t kf[2][NC];
+        kread(kbuf, kf);
+        f32x16_t sc[2][2];
+        smma(kf, qf, sc);
+        bf16x8_t va[4][NDB];
+        vread(vbuf, va);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): every fragment read returned
+        asm volatile("" ::: "memory");
+        // behind the partner wave: issue first until caught up
+        if (F - f > partner_left) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+        // The buffers are free: the loads of tile f + 1 go out in four groups
+        // spread over the softmax, so that no long burst stalls the wave.
+        const bool more = f + 1 < F;
+        const uint16_t* kn = gbase(a.k, tile_g(e1)) + (size_t)tile_j(e1) * 64 * 64;
+        const uint16_t* vn = gbase(a.v, tile_g(e1)) + (size_t)tile_j(e1) * 64 * 64;
+        if (more) lds_load16x4_1k(kdo, kn, kl + 2048);
+        if (pend) {                         // the previous unit's epilogue
+            finish();
+            pend = false;
+        }
+        softmax_prep(tile_j(e0), kind_cur, tq_cur, valid_cur, sc, (e0 & kTileFirst) != 0);
+        u32x4_t p0[2], p1[2], p2[2], p3[2];
+        softmax_exp(sc, 0, C0(), p0);
+        if (more) lds_load16x4_1k(kdo, kn + 32 * 64, kl + 4096 + 2048);
+        softmax_exp(sc, 1, C0(), p1);
+        pv(va, 0, C0(), p0);
+        if (more) lds_load16x4_1k(vdo, vn, vl + 2048);
+        softmax_exp(sc, 0, C2(), p2);
+        pv(va, 1, C0(), p1);
+        if (more) lds_load16x4_1k(vdo, vn + 32 * 64, vl + 4096 + 2048);
+        softmax_exp(sc, 1, C2(), p3);
+        pv(va, 0, C2(), p2);
+        pv(va, 1, C2(), p3);
+        if (e0 & kTileLast) {               // finished once the next tile's loads are out
+            pend = true;
+            p_slot = slot_cur;
+            p_g = g_cur;
+            p_tq[0] = tq_cur[0];
+            p_tq[1] = tq_cur[1];
+        }
+        e0 = e1;
+    }
+    if (pend) finish();
+    if (lane == 0) left[wv] = 0;
+    wait_vmcnt<0>();
+}
+
 // Merge of a split row (global rows, routed tiles): the chunks of the row
 // wrote fp32 partials normalised over their own keys plus their LSE; the row's
 // LSE is the log-sum-exp of the chunk LSEs and O the LSE-weighted mean of the
@@ -711,18 +1162,27 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int MASK>
+hipError_t launch_q(const FwdArgs& a, hipStream_t s) {
+    // kQWaves lists (bins) per workgroup
+    if (a.n_bins % kQWaves != 0) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)kXcds * (a.n_bins / kQWaves);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_bf16_q_kernel<MASK>), dim3((unsigned)grid), dim3(kQThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int fwd_bf16_ctas_per_cu(int head_dim) {
+    // D = 64: one workgroup holds the whole CU.
+    if (head_dim == 64) return 1;
     int n = 0;
-    hipError_t e = head_dim == 64
-        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<64, MASK_NONE>, kThreads, 0)
-        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<128, MASK_NONE>, kThreads, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<128, MASK_NONE>, kThreads, 0);
     if (e != hipSuccess || n < 1) n = 1;
     // Measured on MI355X: with 32 KiB of LDS per workgroup only 4 workgroups
     // are resident per CU (the occupancy query reports 5); 64 KiB gives 2.
-    const int lds_cap = head_dim == 64 ? 4 : 2;
-    return n < lds_cap ? n : lds_cap;
+    return n < 2 ? n : 2;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
@@ -730,9 +1190,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
     hipError_t e;
     if (before && (e = hipEventRecord(before, s)) != hipSuccess) return e;
     if (head_dim == 64) {
-        e = mask == MASK_PAD ? launch_fwd_t<64, MASK_PAD>(a, s)
-          : mask == MASK_BAND ? launch_fwd_t<64, MASK_BAND>(a, s)
-                              : launch_fwd_t<64, MASK_NONE>(a, s);
+        e = mask == MASK_PAD ? launch_q<MASK_PAD>(a, s)
+          : mask == MASK_BAND ? launch_q<MASK_BAND>(a, s)
+                              : launch_q<MASK_NONE>(a, s);
     } else {
         e = mask == MASK_PAD ? launch_fwd_t<128, MASK_PAD>(a, s)
           : mask == MASK_BAND ? launch_fwd_t<128, MASK_BAND>(a, s)
