@@ -733,7 +733,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 u32x4_t u = {0u, 0u, 0u, 0u};
-                if (tq[qb] >= 0) u = *(const u32x4_t*)(qp + (size_t)tq[qb] * D + 16 * c + 8 * hh);
+                if (tq[qb] >= 0) u = *(const u32x4_t*)(qp + (uint32_t)(tq[qb] * D + 16 * c + 8 * hh));
                 qf[qb][c] = as_bf16x8(u);
             }
         }
@@ -742,8 +742,9 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         if (t < 0) return;
         const size_t bh = (size_t)g;
         // O^T register i of block db <-> d = 32db + 8(i/4) + 4hh + i%4
+        // group / slot bases are uniform (scalar), the lane offsets 32-bit
         if (slot < 0) {
-            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D;
+            uint16_t* orow = (uint16_t*)a.out + bh * a.L * D + (uint32_t)(t * D);
             // Lanes l and l + 32 hold d = 8gq + 0..3 and 8gq + 4..7 of the same
             // row: swapping halves (v_permlane32_swap moves the upper half-wave's
             // first operand to the lower half-wave's second, and back) leaves
@@ -763,9 +764,11 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     const u32x4_t w4 = {s0[0], s1[0], s0[1], s1[1]};
                     *(u32x4_t*)(orow + 32 * db + 16 * pr + 8 * hh) = w4;
                 }
-            if (hh == 0) a.lse[bh * a.L + t] = lse_v;
+            if (hh == 0) (a.lse + bh * a.L)[(uint32_t)t] = lse_v;
         } else {
-            float* orow = a.ws_o + ((size_t)slot * 64 + r) * D;
+            uint32_t roff = (uint32_t)(r * D);
+            asm volatile("" : "+v"(roff));   // keep the lane offset 32-bit and local (no 64-bit address held across the loop)
+            float* orow = a.ws_o + (size_t)slot * 64 * D + roff;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -773,7 +776,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     *(float4*)(orow + 32 * db + 8 * gq + 4 * hh) =
                         make_float4(ov[db][4 * gq] * inv, ov[db][4 * gq + 1] * inv, ov[db][4 * gq + 2] * inv,
                                     ov[db][4 * gq + 3] * inv);
-            if (hh == 0) a.ws_lse[(size_t)slot * 64 + r] = lse_v;
+            if (hh == 0) (a.ws_lse + (size_t)slot * 64)[(uint32_t)r] = lse_v;
         }
     };
     // ---- tile list -> LDS (key padding: drop tiles past the valid length) ----
@@ -978,7 +981,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     int u_cur = tile_unit(e0);
     int kind_cur = rd(u_kind, u_cur), slot_cur = rd(u_slot, u_cur), g_cur = rd(u_g, u_cur);
     int valid_cur = rd(u_valid, u_cur);
-    int tq_cur[2];
+    int tq_cur[2], tq_next[2] = {-1, -1};
     bf16x8_t qf[2][NC];
     load_q(kind_cur, g_cur, qf, tq_cur);
     issue_tile1(gbase(a.k, g_cur), tile_j(e0), kdo, kl);
@@ -1008,13 +1011,14 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int e1 = f + 1 < F ? __builtin_amdgcn_readfirstlane(flat[f + 1]) : 0;
         if (lane == 0) left[wv] = F - f;
         const int partner_left = partner >= 0 ? __builtin_amdgcn_readfirstlane(left[partner]) : 0;
-        if ((e0 & kTileFirst) && f > 0) {   // a new unit: its Q (the load's latency is covered by the other wave)
+        if ((e0 & kTileFirst) && f > 0) {   // a new unit (its Q was loaded during the last step)
             u_cur = tile_unit(e0);
             kind_cur = rd(u_kind, u_cur);
             slot_cur = rd(u_slot, u_cur);
             g_cur = rd(u_g, u_cur);
             valid_cur = rd(u_valid, u_cur);
-            load_q(kind_cur, g_cur, qf, tq_cur);
+            tq_cur[0] = tq_next[0];
+            tq_cur[1] = tq_next[1];
         }
         wait_vmcnt<0>();                   // K(f), V(f) and Q in place
         asm volatile("" ::: "memory");
@@ -1022,6 +1026,12 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         kread(kbuf, kf);
         f32x16_t sc[2][2];
         smma(kf, qf, sc);
+        // On a unit's last tile Q is free once the products are issued: load
+        // the next unit's, so that its latency hides behind this step.
+        if ((e0 & kTileLast) && f + 1 < F) {
+            const int un = tile_unit(e1);
+            load_q(rd(u_kind, un), rd(u_g, un), qf, tq_next);
+        }
         bf16x8_t va[4][NDB];
         vread(vbuf, va);
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): every fragment read returned
