@@ -34,7 +34,9 @@ METRIC = "block-sparse attn fwd tokens/s and effective TFLOP/s (% bf16 MFMA peak
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "fwd_bf16.hip")
-MAIN_KERNEL = "fwd_bf16_kernel"
+# the attention kernel that dominates a bf16 forward: one for D = 64, one for D = 128
+def main_kernel(head_dim: int) -> str:
+    return "fwd_bf16_d64_kernel" if head_dim == 64 else "fwd_bf16_kernel"
 
 
 def parse_args():
@@ -65,10 +67,10 @@ def tile_stats(wl, row_ptr, col, valid_len=None):
     return total
 
 
-def traffic_from_profile(workload: str):
+def traffic_from_profile(workload: str, kernel: str):
     """HBM bytes per launch of the main kernel from the committed counter summary, or None
     when the summary is missing or the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{MAIN_KERNEL}_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -215,7 +217,7 @@ def main():
     value = tokens / (ms_step / 1e3)
     eff_tflops = flops_per_step / (ms_step / 1e3) / 1e12
     kern_tflops = flops_per_step / (kern_avg_ms / 1e3) / 1e12
-    traffic = traffic_from_profile(wl.name)
+    traffic = traffic_from_profile(wl.name, main_kernel(D))
 
     result = {
         "metric": METRIC,
@@ -242,7 +244,7 @@ def main():
         "layout_build_host_us": round(layout_host_us, 1),
         "roofline": {
             "bound": "mfma",
-            "kernel": MAIN_KERNEL,
+            "kernel": main_kernel(D),
             "achieved": round(kern_tflops, 2),
             "peak": round(PEAK_BF16_TFLOPS, 1),
             "unit": "TFLOP/s",

@@ -188,7 +188,8 @@ int device_capacity(int dev, int32_t D, int* cus_out = nullptr) {
 // chunks -- are packed into the XCD's n_bins bins longest-processing-time
 // first: each unit, by decreasing cost, goes to the least loaded bin, cost =
 // tile count + a fixed overhead for loading Q and writing O.  n_bins is the
-// number of workgroups per XCD that the device holds at once.  Within a bin
+// number of lists per XCD that the device runs at once: one per workgroup
+// (D = 128), or one per wave of the CU-wide workgroups (D = 64).  Within a bin
 // the units are then ordered by group, so that all bins of an XCD walk its
 // groups in the same order and the XCD's K/V working set stays near one
 // group (which fits in its L2).  For every bin the device gets the unit

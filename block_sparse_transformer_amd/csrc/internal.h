@@ -74,8 +74,8 @@ struct FwdArgs {
     const int32_t* routed_rows;
     int32_t n_items, n_merges;
     int32_t items_per_head;   // explicit items per head (NOP-padded to equal length)
-    // persistent schedule: n_bins workgroups per XCD.  Workgroup (x, bin)
-    // runs units units[unit_ptr[x*n_bins+bin] ..) -- {kind, slot, group,
+    // persistent schedule: n_bins lists per XCD (one per workgroup, or one
+    // per wave for D = 64, kQWaves per workgroup).  List (x, bin) runs units units[unit_ptr[x*n_bins+bin] ..) -- {kind, slot, group,
     // first tile}: kind >= 0 the query block of a layout row (slot: partial
     // slot within a batch entry, -1 for a whole row), kind < 0 routed tile
     // -1-kind (slot: chunk); group = b * H + h; first tile: offset of the

@@ -658,7 +658,7 @@ __device__ __forceinline__ void issue_tile1(const uint16_t* base, int j, uint32_
 }
 
 template <int MASK>
-__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_q_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_d64_kernel(const FwdArgs a) {
     constexpr int D = 64, NC = 4, NDB = 2, TILE = 64 * 64;
     __shared__ __attribute__((aligned(1024))) uint16_t kvbuf[kQWaves][2][TILE];
     __shared__ int flats[kQWaves][kMaxBinTiles];   // each wave's tile list
@@ -1173,12 +1173,12 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
 }
 
 template <int MASK>
-hipError_t launch_q(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_d64(const FwdArgs& a, hipStream_t s) {
     // kQWaves lists (bins) per workgroup
     if (a.n_bins % kQWaves != 0) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)kXcds * (a.n_bins / kQWaves);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_bf16_q_kernel<MASK>), dim3((unsigned)grid), dim3(kQThreads), 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_d64_kernel<MASK>), dim3((unsigned)grid), dim3(kQThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1200,9 +1200,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
     hipError_t e;
     if (before && (e = hipEventRecord(before, s)) != hipSuccess) return e;
     if (head_dim == 64) {
-        e = mask == MASK_PAD ? launch_q<MASK_PAD>(a, s)
-          : mask == MASK_BAND ? launch_q<MASK_BAND>(a, s)
-                              : launch_q<MASK_NONE>(a, s);
+        e = mask == MASK_PAD ? launch_d64<MASK_PAD>(a, s)
+          : mask == MASK_BAND ? launch_d64<MASK_BAND>(a, s)
+                              : launch_d64<MASK_NONE>(a, s);
     } else {
         e = mask == MASK_PAD ? launch_fwd_t<128, MASK_PAD>(a, s)
           : mask == MASK_BAND ? launch_fwd_t<128, MASK_BAND>(a, s)
