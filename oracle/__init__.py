@@ -14,13 +14,16 @@ Modules
               0/1 token mask.
 ``attention`` dense masked softmax attention in fp64 from that mask.
 ``router``    the routed-query selection: exact fp64 score q.w and top-k.
+``attention_grad``  the gradients (dQ, dK, dV) of the masked attention for
+              an upstream dO: the softmax Jacobian written out in fp64.
 
 Parity pins (see ``tests/test_oracle_*.py``): every function is checked
 against something other than itself -- published splitmix64 outputs, closed
-form layout counts, library routines (``scaled_dot_product_attention`` in
-fp64), brute-force loops, exact rational arithmetic and closed forms of the
-softmax.  Parity unpinned: the concrete choice of random blocks beyond the
+form layout counts, library routines (``scaled_dot_product_attention`` and
+torch autograd in fp64), brute-force loops, central finite differences,
+exact rational arithmetic and closed forms and invariants of the softmax.
+Parity unpinned: the concrete choice of random blocks beyond the
 hash stream itself (the composition of the per-row seed and the shuffle are
 this library's own specification; any uniform draw satisfies the pages).
 """
-from . import layout, attention, router  # noqa: F401
+from . import layout, attention, attention_grad, router  # noqa: F401
