@@ -1,4 +1,4 @@
-"""block_sparse_transformer_amd -- block-sparse attention forward on AMD MI355X (gfx950).
+"""block_sparse_transformer_amd -- block-sparse attention forward and backward on AMD MI355X (gfx950).
 
 A thin ctypes binding of ``libbsattn.so`` (declared in ``include/bsattn.h``).
 Every function here only marshals arguments: tensors become device pointers,
@@ -7,12 +7,15 @@ the HIP kernels of the library; there is no CPU fallback, and every function
 raises if the library has not been built.
 
 Functions carry the C names (``bsattn_make_layout``, ``bsattn_forward``, ...)
-plus two conveniences, :func:`forward` and :func:`forward_routed`, that
-allocate outputs and workspace with torch.
+plus conveniences, :func:`forward`, :func:`forward_routed` and
+:func:`backward`, that allocate outputs and workspace with torch.
 """
 from ._binding import (  # noqa: F401
     BsattnError,
     Layout,
+    backward,
+    bsattn_backward,
+    bsattn_backward_workspace_size,
     bsattn_forward,
     bsattn_forward_routed,
     bsattn_last_error,

@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
     L.bsattn_forward_routed.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp,
                                         _c_vp, _c_vp, _c_int, _c_vp, _c_vp, ctypes.c_float, _c_vp,
                                         ctypes.c_size_t, _c_vp]
+    L.bsattn_backward_workspace_size.argtypes = [_c_vp, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]
+    L.bsattn_backward.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
+                                  _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp,
+                                  ctypes.c_size_t, _c_vp]
     L.bsattn_set_profile_events.argtypes = [_c_vp, _c_vp]
     L.bsattn_status_string.argtypes = [ctypes.c_int]
     L.bsattn_status_string.restype = ctypes.c_char_p
@@ -233,6 +237,33 @@ def bsattn_forward_routed(band_layout: Layout, q, k, v, routed_rows, out, lse, s
         _stream_handle(stream)))
 
 
+def bsattn_backward_workspace_size(layout: Layout, batch: int, head_dim: int) -> int:
+    n = ctypes.c_size_t()
+    _check("bsattn_backward_workspace_size",
+           lib().bsattn_backward_workspace_size(layout.handle, batch, head_dim, ctypes.byref(n)))
+    return n.value
+
+
+def bsattn_backward(layout: Layout, q, k, v, out, lse, dout, dq, dk, dv, key_valid_len=None,
+                    scale: Optional[float] = None, workspace=None, stream=None) -> None:
+    """Enqueue the backward pass; all tensors are caller-allocated device tensors."""
+    import torch
+    _check_qkv(q, k, v, out)
+    _check_qkv(q, dout, dq, dk)
+    _check_qkv(q, dv, dv, dv)
+    B, H, L, D = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, L] tensor")
+    if key_valid_len is not None and (key_valid_len.dtype != torch.int32 or key_valid_len.numel() != B):
+        raise ValueError("key_valid_len must be int32 [B]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bsattn_backward", lib().bsattn_backward(
+        layout.handle, _dtype_code(q), B, H, L, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(key_valid_len), scale, _ptr(workspace), wbytes,
+        _stream_handle(stream)))
+
+
 def bsattn_set_profile_events(before: Optional[int], after: Optional[int]) -> None:
     _check("bsattn_set_profile_events", lib().bsattn_set_profile_events(before, after))
 
@@ -255,6 +286,18 @@ def forward(q, k, v, layout: Layout, key_valid_len=None, scale: Optional[float] 
         workspace = _workspace(layout, q)
     bsattn_forward(layout, q, k, v, out, lse, key_valid_len, scale, workspace)
     return out, lse
+
+
+def backward(q, k, v, out, lse, dout, layout: Layout, key_valid_len=None, scale: Optional[float] = None,
+             workspace=None):
+    """Allocate (dq, dk, dv) and workspace with torch and run :func:`bsattn_backward`."""
+    import torch
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if workspace is None:
+        n = bsattn_backward_workspace_size(layout, q.shape[0], q.shape[3])
+        workspace = torch.empty((n + 255) // 4, dtype=torch.float32, device=q.device)
+    bsattn_backward(layout, q, k, v, out, lse, dout, dq, dk, dv, key_valid_len, scale, workspace)
+    return dq, dk, dv
 
 
 def forward_routed(q, k, v, band_layout: Layout, routed_rows, scale: Optional[float] = None, workspace=None):

@@ -23,6 +23,7 @@ LIB = os.path.join(PKG, "libbsattn.so")
 SOURCES = [
     "api.cpp",
     "kernels/fwd_bf16.hip",
+    "kernels/bwd_bf16.hip",
     "kernels/fwd_f32.hip",
     "kernels/router.hip",
     "kernels/layout_build.hip",

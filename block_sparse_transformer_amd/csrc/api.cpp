@@ -86,6 +86,70 @@ void build_schedule(bsattn_layout* lay) {
     lay->n_slots = slot;
 }
 
+// Backward work lists.  dQ: every query block against the key blocks of its
+// row; dK/dV: every key block against the query blocks whose rows hold it
+// (the layout transposed, per head).  Lists longer than kChunkTiles are
+// split into chunks whose fp32 partials a summing launch adds up.  Items go
+// longest first so that long chunks start before short lists.
+void build_bwd(bsattn_layout* lay) {
+    auto& bw = lay->bwd;
+    bw = bsattn_layout::Bwd{};
+    const int32_t H = lay->H, nb = lay->nb;
+    // transpose: for each (h, key block j) the query blocks i whose row holds j, ascending
+    std::vector<int32_t> cptr((size_t)H * nb + 1, 0);
+    for (int32_t h = 0; h < H; ++h)
+        for (int32_t i = 0; i < nb; ++i) {
+            const int32_t r = h * nb + i;
+            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a) ++cptr[(size_t)h * nb + lay->col_idx[a] + 1];
+        }
+    for (size_t c = 0; c + 1 < cptr.size(); ++c) cptr[c + 1] += cptr[c];
+    bw.k_idx.assign((size_t)cptr.back(), 0);
+    std::vector<int32_t> fill(cptr.begin(), cptr.end() - 1);
+    for (int32_t h = 0; h < H; ++h)
+        for (int32_t i = 0; i < nb; ++i) {
+            const int32_t r = h * nb + i;
+            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a)
+                bw.k_idx[(size_t)fill[(size_t)h * nb + lay->col_idx[a]]++] = i;
+        }
+    auto make = [&](const std::vector<int32_t>& ptr, std::vector<BwdItem>& items, std::vector<BwdSum>& sums,
+                    int32_t& n_slots) {
+        n_slots = 0;
+        for (int32_t hb = 0; hb < H * nb; ++hb) {
+            const int32_t b0 = ptr[(size_t)hb], b1 = ptr[(size_t)hb + 1];
+            const int32_t len = b1 - b0;
+            if (len <= kChunkTiles) {
+                items.push_back({hb, b0, b1, -1});
+                continue;
+            }
+            int32_t nch, per;
+            split_row(len, &nch, &per);
+            sums.push_back({hb, n_slots, nch, 0});
+            for (int32_t c = 0; c < nch; ++c) {
+                const int32_t s0 = b0 + c * per;
+                items.push_back({hb, s0, std::min(b1, s0 + per), n_slots++});
+            }
+        }
+        std::stable_sort(items.begin(), items.end(),
+                         [](const BwdItem& x, const BwdItem& y) { return (x.end - x.begin) > (y.end - y.begin); });
+    };
+    make(lay->row_ptr, bw.q_items, bw.q_sums, bw.n_qslots);
+    make(cptr, bw.k_items, bw.k_sums, bw.n_kslots);
+    bw.built = true;
+}
+
+void free_bwd_device(bsattn_layout* lay) {
+    auto& bw = lay->bwd;
+    (void)hipFree(bw.d_q_items);
+    (void)hipFree(bw.d_k_items);
+    (void)hipFree(bw.d_q_sums);
+    (void)hipFree(bw.d_k_sums);
+    (void)hipFree(bw.d_k_idx);
+    bw.d_q_items = bw.d_k_items = nullptr;
+    bw.d_q_sums = bw.d_k_sums = nullptr;
+    bw.d_k_idx = nullptr;
+    bw.uploaded = false;
+}
+
 void free_device(bsattn_layout* lay) {
     if (lay->device >= 0) {
         int cur = -1;
@@ -101,6 +165,7 @@ void free_device(bsattn_layout* lay) {
             (void)hipFree(sc.d_tiles);
             (void)hipFree(sc.d_tile_ptr);
         }
+        free_bwd_device(lay);
         if (cur >= 0 && cur != lay->device) (void)hipSetDevice(cur);
     }
     lay->scheds.clear();
@@ -122,7 +187,55 @@ bsattn_status check_layout_dims(int32_t H, int32_t L, int32_t block) {
 
 bsattn_status finish_layout(bsattn_layout* lay) {
     build_schedule(lay);
+    try {
+        build_bwd(lay);
+    } catch (const std::bad_alloc&) {
+        return fail(BSATTN_ERR_NO_MEMORY, "backward work list allocation failed");
+    }
     return ok();
+}
+
+// Device copies of the backward lists (first backward call on the device).
+bsattn_status upload_bwd(const bsattn_layout* lay, hipStream_t stream) {
+    auto& bw = lay->bwd;
+    if (bw.uploaded) return BSATTN_OK;
+    void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    const void* src[5] = {bw.q_items.data(), bw.k_items.data(), bw.q_sums.data(), bw.k_sums.data(),
+                          bw.k_idx.data()};
+    const size_t sz[5] = {bw.q_items.size() * sizeof(BwdItem), bw.k_items.size() * sizeof(BwdItem),
+                          bw.q_sums.size() * sizeof(BwdSum), bw.k_sums.size() * sizeof(BwdSum),
+                          bw.k_idx.size() * sizeof(int32_t)};
+    hipError_t e = hipSuccess;
+    for (int a = 0; a < 5 && e == hipSuccess; ++a) {
+        e = hipMalloc(&p[a], std::max<size_t>(sz[a], 16));
+        if (e == hipSuccess && sz[a] > 0) e = hipMemcpyAsync(p[a], src[a], sz[a], hipMemcpyHostToDevice, stream);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        for (int a = 0; a < 5; ++a) (void)hipFree(p[a]);
+        return fail(BSATTN_ERR_NO_MEMORY, "backward list upload: %s", hipGetErrorString(e));
+    }
+    bw.d_q_items = (BwdItem*)p[0];
+    bw.d_k_items = (BwdItem*)p[1];
+    bw.d_q_sums = (BwdSum*)p[2];
+    bw.d_k_sums = (BwdSum*)p[3];
+    bw.d_k_idx = (int32_t*)p[4];
+    bw.uploaded = true;
+    return BSATTN_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace of bsattn_backward: delta, then the dQ, dK and dV partial slots.
+void bwd_workspace_parts(const bsattn_layout* lay, int32_t B, int32_t D, size_t* off_dq, size_t* off_dk,
+                         size_t* off_dv, size_t* total) {
+    const size_t delta = align256((size_t)B * lay->H * lay->L * sizeof(float));
+    const size_t qs = align256((size_t)B * lay->bwd.n_qslots * kBlock * D * sizeof(float));
+    const size_t ks = align256((size_t)B * lay->bwd.n_kslots * kBlock * D * sizeof(float));
+    *off_dq = delta;
+    *off_dk = delta + qs;
+    *off_dv = delta + qs + ks;
+    *total = delta + qs + 2 * ks;
 }
 
 // Shape/pointer checks shared by both forward entry points.
@@ -702,6 +815,89 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* lay, bsattn_dtype dtype
     a.tile_ptr = sc.d_tile_ptr;
     hipError_t e = launch_fwd_bf16(a, D, MASK_BAND, stream, g_ev_before, g_ev_after);
     if (e != hipSuccess) return hip_fail(e, "routed forward launch");
+    return ok();
+}
+
+bsattn_status bsattn_backward_workspace_size(const bsattn_layout* lay, int32_t batch, int32_t head_dim,
+                                             size_t* bytes) {
+    if (!lay || !bytes) return fail(BSATTN_ERR_INVALID_ARG, "NULL argument");
+    if (batch < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch must be >= 1");
+    if (head_dim != 64 && head_dim != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    size_t a, b, c;
+    bwd_workspace_parts(lay, batch, head_dim, &a, &b, &c, bytes);
+    return ok();
+}
+
+bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int32_t B, int32_t H,
+                              int32_t L, int32_t D, const void* q, const void* k, const void* v,
+                              const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                              void* dv, const int32_t* key_valid_len, float scale, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (lay->kind != 0) return fail(BSATTN_ERR_UNSUPPORTED, "the backward takes window/global/random layouts");
+    if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "the backward is bf16 only");
+    if (!dout || !dq || !dk || !dv) return fail(BSATTN_ERR_INVALID_ARG, "NULL gradient pointer");
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return fail(BSATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const void* ins[6] = {q, k, v, out, lse, dout};
+    const void* outs[3] = {dq, dk, dv};
+    for (const void* o : outs) {
+        for (const void* in : ins)
+            if (o == in) return fail(BSATTN_ERR_INVALID_ARG, "a gradient output aliases an input");
+    }
+    if (dq == dk || dq == dv || dk == dv) return fail(BSATTN_ERR_INVALID_ARG, "gradient outputs alias");
+    // the forward's checks: shapes against the layout, q, k, v, out, lse, scale, the device
+    bsattn_status st = check_forward_common(lay, B, H, L, D, q, k, v, const_cast<void*>(out),
+                                            const_cast<float*>(lse), scale);
+    if (st != BSATTN_OK) return st;
+    size_t off_dq, off_dk, off_dv, need;
+    bwd_workspace_parts(lay, B, D, &off_dq, &off_dk, &off_dv, &need);
+    if (!workspace || workspace_bytes < need)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const auto& bw = lay->bwd;
+    if ((int64_t)B * std::max(bw.q_items.size(), bw.k_items.size()) >= ((int64_t)1 << 31))
+        return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+    {
+        std::lock_guard<std::mutex> guard(*lay->sched_mu);
+        st = upload_bwd(lay, stream);
+        if (st != BSATTN_OK) return st;
+    }
+
+    BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    char* ws = (char*)workspace;
+    a.delta = (float*)ws;
+    a.ws_dq = (float*)(ws + off_dq);
+    a.ws_dk = (float*)(ws + off_dk);
+    a.ws_dv = (float*)(ws + off_dv);
+    a.valid_len = key_valid_len;
+    a.B = B; a.H = H; a.L = L; a.nb = lay->nb;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const int mask = key_valid_len ? MASK_PAD : MASK_NONE;
+
+    hipError_t e = launch_bwd_delta(a, D, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward delta launch");
+
+    a.items = bw.d_q_items; a.n_items = (int32_t)bw.q_items.size();
+    a.sums = bw.d_q_sums; a.n_sums = (int32_t)bw.q_sums.size();
+    a.idx = lay->d_col_idx; a.n_slots = bw.n_qslots;
+    e = launch_bwd_dq(a, D, mask, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward dQ launch");
+    if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 0, stream)) != hipSuccess) return hip_fail(e, "backward dQ sum launch");
+
+    a.items = bw.d_k_items; a.n_items = (int32_t)bw.k_items.size();
+    a.sums = bw.d_k_sums; a.n_sums = (int32_t)bw.k_sums.size();
+    a.idx = bw.d_k_idx; a.n_slots = bw.n_kslots;
+    if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    e = launch_bwd_dkdv(a, D, mask, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward dK/dV launch");
+    if (g_ev_after && (e = hipEventRecord(g_ev_after, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 1, stream)) != hipSuccess)
+        return hip_fail(e, "backward dK/dV sum launch");
     return ok();
 }
 

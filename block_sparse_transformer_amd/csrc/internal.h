@@ -75,8 +75,8 @@ struct FwdArgs {
     int32_t n_items, n_merges;
     int32_t items_per_head;   // explicit items per head (NOP-padded to equal length)
     // persistent schedule: n_bins lists per XCD (one per workgroup, or one
-    // per wave for D = 64, kQWaves per workgroup).  List (x, bin) runs units units[unit_ptr[x*n_bins+bin] ..) -- {kind, slot, group,
-    // first tile}: kind >= 0 the query block of a layout row (slot: partial
+    // per wave for D = 64, kQWaves per workgroup).  List (x, bin) runs units
+    // units[unit_ptr[x*n_bins+bin] ..) -- {kind, slot, group, first tile}: kind >= 0 the query block of a layout row (slot: partial
     // slot within a batch entry, -1 for a whole row), kind < 0 routed tile
     // -1-kind (slot: chunk); group = b * H + h; first tile: offset of the
     // unit's tiles in the bin's list -- over the flat tile list
@@ -99,6 +99,45 @@ struct FwdArgs {
     float scale_log2;         // scale * log2(e)
 };
 
+// ---- backward ----
+// One workgroup's share of a backward kernel: block `head_blk` (= h*nb + blk)
+// -- the query block for dQ, the key block for dK/dV -- against the blocks
+// idx[begin, end) of the other side (the layout's key blocks of the row for
+// dQ; the query blocks whose rows hold the key block for dK/dV).  slot < 0:
+// the whole row/column, written straight to the bf16 output; slot >= 0: one
+// chunk, written as an fp32 partial to workspace slot b*n_slots + slot.
+struct BwdItem {
+    int32_t head_blk, begin, end, slot;
+};
+// A split row/column: its chunks' partials occupy slots [first_slot, first_slot + n_chunks).
+struct BwdSum {
+    int32_t head_blk, first_slot, n_chunks, pad;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;             // [B*H*L] rowsum(dO * O)
+    float* ws_dq;             // [B*n_qslots][64][D] fp32 partials
+    float* ws_dk;             // [B*n_kslots][64][D]
+    float* ws_dv;             // [B*n_kslots][64][D]
+    const BwdItem* items;     // this launch's items (dQ or dK/dV)
+    const int32_t* idx;       // this launch's block lists
+    const BwdSum* sums;
+    int32_t n_items, n_sums;
+    const int32_t* valid_len; // [B] or null
+    int32_t B, H, L, nb, n_slots;
+    float scale;              // score scale
+    float scale_log2;         // scale * log2(e)
+};
+
 // ---- launchers (defined in kernels/*.hip) ----
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s,
                            hipEvent_t before, hipEvent_t after);
@@ -107,6 +146,11 @@ hipError_t launch_fwd_f32(const FwdArgs& a, const int32_t* row_ptr, int head_dim
                           hipStream_t s, hipEvent_t before, hipEvent_t after);
 hipError_t launch_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,
                              int32_t D, int32_t k, int32_t* out, hipStream_t s);
+hipError_t launch_bwd_delta(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s);
+// sum split partials into the bf16 output(s): which = 0 dQ, 1 dK and dV
+hipError_t launch_bwd_sum(const BwdArgs& a, int head_dim, int which, hipStream_t s);
 hipError_t launch_layout_build(const RowRule& rule, int kind, int32_t H, int32_t nb,
                                int32_t band, int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
 
@@ -140,4 +184,18 @@ struct bsattn_layout {
     };
     mutable std::vector<Sched> scheds;
     mutable std::unique_ptr<std::mutex> sched_mu{new std::mutex};
+    // backward work lists, built and uploaded on the first backward call
+    struct Bwd {
+        int32_t n_qslots = 0, n_kslots = 0;
+        std::vector<bsattn::BwdItem> q_items, k_items;   // longest first
+        std::vector<bsattn::BwdSum> q_sums, k_sums;
+        std::vector<int32_t> k_idx;                      // query blocks per key block (CSC)
+        bsattn::BwdItem* d_q_items = nullptr;
+        bsattn::BwdItem* d_k_items = nullptr;
+        bsattn::BwdSum* d_q_sums = nullptr;
+        bsattn::BwdSum* d_k_sums = nullptr;
+        int32_t* d_k_idx = nullptr;
+        bool built = false, uploaded = false;
+    };
+    mutable Bwd bwd;
 };

@@ -180,11 +180,52 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* band_layout, bsattn_dty
                                     int32_t num_routed, void* out, float* lse, float scale,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Device workspace bytes needed by bsattn_backward for this layout, batch and
+ * head width: delta = rowsum(dO * O) per query row (fp32 [B, H, L]), then the
+ * fp32 partial gradients of rows and columns of the layout that are split
+ * across workgroups (global rows and the key blocks every row attends).
+ * Written to *bytes.  The workspace needs no initialisation and holds nothing
+ * between calls; calls that share one must not overlap in time. */
+bsattn_status bsattn_backward_workspace_size(const bsattn_layout* layout, int32_t batch,
+                                             int32_t head_dim, size_t* bytes);
+
+/* Block-sparse attention backward: the gradients of bsattn_forward (same
+ * layout, key padding and scale) with respect to q, k and v for an upstream
+ * gradient dout of the output.  The models on the pages are trained (SQA
+ * page, sections 2.2 and 3.2; BigBird page, the pitfall guide on mixed
+ * precision training); the backward is the derivative of the forward:
+ *   P = exp(scale * q.k - lse) on allowed keys, delta = rowsum(dout * out),
+ *   dv = P^T dout,  ds = P * (dout v^T - delta),
+ *   dq = scale * ds k,  dk = scale * ds^T q.
+ *   layout          uploaded window/global/random layout (band layouts: UNSUPPORTED).
+ *   dtype           BSATTN_BF16 (others: UNSUPPORTED).
+ *   batch..head_dim as bsattn_forward.
+ *   q, k, v         the forward's inputs, device bf16 [B, H, L, D].
+ *   out, lse        the forward's outputs for these inputs: bf16 [B, H, L, D]
+ *                   and fp32 [B, H, L] (a row with lse = -inf has no allowed
+ *                   key and gets zero gradient).
+ *   dout            device bf16 [B, H, L, D].
+ *   dq, dk, dv      device bf16 [B, H, L, D], written completely; must not
+ *                   alias any input or each other.
+ *   key_valid_len   as bsattn_forward.
+ *   workspace       device buffer of at least bsattn_backward_workspace_size()
+ *                   bytes, 256-byte aligned, any contents.
+ * All pointers 16-byte aligned.  Enqueued on `stream`; no synchronisation.
+ * The first call on a device uploads the layout's backward work lists
+ * (hipMalloc and a synchronous copy); later calls allocate nothing. */
+bsattn_status bsattn_backward(const bsattn_layout* layout, bsattn_dtype dtype,
+                              int32_t batch, int32_t num_heads, int32_t seq_len, int32_t head_dim,
+                              const void* q, const void* k, const void* v,
+                              const void* out, const float* lse, const void* dout,
+                              void* dq, void* dk, void* dv, const int32_t* key_valid_len,
+                              float scale, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /* Measurement hook: while set (non-NULL), every forward call made from this
  * thread records `before` on its stream immediately before the main attention
- * kernel and `after` immediately after it, so a caller can time that kernel
- * alone with hipEventElapsedTime.  Pass NULLs to clear.  Events are caller
- * owned. */
+ * kernel and `after` immediately after it, and every backward call does the
+ * same around its dK/dV kernel, so a caller can time that kernel alone with
+ * hipEventElapsedTime.  Pass NULLs to clear.  Events are caller owned. */
 bsattn_status bsattn_set_profile_events(hipEvent_t before, hipEvent_t after);
 
 /* Static description of a status code; never NULL. */

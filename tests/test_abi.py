@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted([
         "bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr", "bsattn_layout_upload",
         "bsattn_layout_build_device", "bsattn_layout_destroy", "bsattn_workspace_size",
-        "bsattn_forward",
+        "bsattn_forward", "bsattn_backward_workspace_size", "bsattn_backward",
         "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
         "bsattn_last_error"])
     lib = bs.lib()
@@ -114,3 +114,38 @@ def test_forward_rejects_before_any_hip_call():
     # profile events must be set in pairs
     assert L.bsattn_set_profile_events(fake, None) == 1
     assert L.bsattn_set_profile_events(None, None) == 0
+
+
+def test_backward_workspace_size_and_lists():
+    """Host-side backward work lists: sizes follow the layout's split rows and columns."""
+    lay = bs.bsattn_make_layout(12, 8192, 64, 3, [0, 127], 3, 2)
+    n = bs.bsattn_backward_workspace_size(lay, 2, 64)
+    delta = 2 * 12 * 8192 * 4
+    # 2 global rows and 2 global columns per head, each 128 blocks -> 8 chunks of 16
+    part = 2 * 12 * 2 * 8 * 64 * 64 * 4
+    assert n == delta + part + 2 * part
+    assert bs.bsattn_backward_workspace_size(lay, 2, 128) == delta + 3 * 2 * part
+    with pytest.raises(bs.BsattnError):
+        bs.bsattn_backward_workspace_size(lay, 2, 96)
+
+
+def test_backward_rejects_before_any_hip_call():
+    L = bs.lib()
+    lay = bs.bsattn_make_layout(2, 1024, 64, 3, [0], 1, 0)
+    band = bs.bsattn_make_band_layout(2, 1024, 64, 32)
+    f = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(10)]
+    ws = ctypes.c_size_t(0)
+
+    def call(layout, dtype=1, D=64, q=f[0], dq=f[6], dk=f[7], dv=f[8], dout=f[5], scale=0.125):
+        return L.bsattn_backward(layout, dtype, 1, 2, 1024, D, q, f[1], f[2], f[3], f[4], dout, dq, dk, dv,
+                                 None, scale, None, ws, None)
+
+    assert call(None) == 1
+    assert call(band.handle) == 2 and "layout" in bs.bsattn_last_error()
+    assert call(lay.handle, dtype=0) == 2 and "bf16" in bs.bsattn_last_error()
+    assert call(lay.handle, dout=None) == 1
+    assert call(lay.handle, dq=f[0]) == 1 and "alias" in bs.bsattn_last_error()
+    assert call(lay.handle, dk=f[6]) == 1 and "alias" in bs.bsattn_last_error()
+    assert call(lay.handle, dv=ctypes.c_void_p(0x9002)) == 1 and "aligned" in bs.bsattn_last_error()
+    assert call(lay.handle, D=96) == 2
+    assert call(lay.handle, scale=0.0) == 1

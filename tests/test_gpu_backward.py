@@ -1,0 +1,175 @@
+"""GPU parity of the backward pass: the HIP path through the C ABI against the
+fp64 oracle gradients (oracle.attention_grad).
+
+Inputs Q, K, V and dO are seeded bf16 draws (workloads.make_inputs,
+make_grad_output).  The HIP backward runs on the HIP forward's O and LSE, as a
+training step would; one case instead feeds the oracle's own O (rounded to
+bf16) and LSE (rounded to fp32) to test the backward alone.
+
+Tolerance: every element of dQ, dK and dV within TOL_REL of the largest
+magnitude of that reference tensor (bf16 rounding of P, dS, O and the outputs
+each contribute about 2^-9 relative; see the backward tolerance derivation in
+the design notes).  Small shapes are compared everywhere; the benchmark shape
+(B=2, H=12, L=8192) is compared on one whole (batch, head) pair.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_transformer_amd as bs
+from oracle import attention as OA
+from oracle import attention_grad as OG
+from oracle import layout as OL
+from workloads import WORKLOADS, make_grad_output, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL = 2e-2
+
+
+def _say(*a):
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bs.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _layouts(wl):
+    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+                                wl.random_blocks, wl.layout_seed)
+    bs.bsattn_layout_upload(lay)
+    olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+                          wl.random_blocks, wl.layout_seed)
+    return lay, olay
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _compare(got, ref, what):
+    errs = []
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.isfinite(g).all(), f"{what}: non-finite {name}"
+        scale = max(np.abs(r).max(), 1e-6)
+        e = np.abs(g - r).max() / scale
+        errs.append(e)
+        _say(what, name, "max|ref| %.4g  max|err|/max|ref| %.3e" % (scale, e))
+        assert e <= TOL_REL, f"{what}: {name} relative error {e}"
+    return errs
+
+
+def _hip_backward(wl, inp, do, lay, o=None, lse=None):
+    dev = {k: v.cuda() for k, v in inp.items()}
+    vl = dev.get("valid_len")
+    if o is None:
+        o, lse = bs.forward(dev["q"], dev["k"], dev["v"], lay, key_valid_len=vl, scale=wl.scale)
+    dq, dk, dv = bs.backward(dev["q"], dev["k"], dev["v"], o, lse, do.cuda(), lay, key_valid_len=vl,
+                             scale=wl.scale)
+    torch.cuda.synchronize()
+    return _f64(dq), _f64(dk), _f64(dv)
+
+
+def _case(wl, tag, heads=None, batches=None):
+    _say(tag, wl)
+    inp = make_inputs(wl)
+    do = make_grad_output(wl)
+    lay, olay = _layouts(wl)
+    got = _hip_backward(wl, inp, do, lay)
+    vl = inp.get("valid_len")
+    ref = OG.attention_backward(inp["q"], inp["k"], inp["v"], do, olay, wl.scale,
+                                valid_len=None if vl is None else vl.tolist(), heads=heads, batches=batches)
+    if heads is not None or batches is not None:
+        bsel = list(range(wl.batch)) if batches is None else list(batches)
+        hsel = list(range(wl.heads)) if heads is None else list(heads)
+        got = tuple(x[np.ix_(bsel, hsel)] for x in got)
+        ref = tuple(x[np.ix_(bsel, hsel)] for x in ref)
+    return _compare(got, ref, tag)
+
+
+def test_backward_d64_split_rows_and_columns():
+    # 32 blocks a side: the global rows and columns (32 blocks) are split in two chunks
+    wl = WORKLOADS["bigbird-L2048"].with_(batch=2, heads=2)
+    _case(wl, "bwd d64 L2048")
+
+
+def test_backward_d128():
+    wl = WORKLOADS["bigbird-L2048"].with_(batch=1, heads=2, head_dim=128, data_seed=7)
+    _case(wl, "bwd d128 L2048")
+
+
+def test_backward_key_padding_d128():
+    wl = WORKLOADS["window-pad-L16384"].with_(batch=2, heads=2, seq_len=2048)
+    _case(wl, "bwd pad d128 L2048")
+
+
+def test_backward_key_padding_d64():
+    wl = WORKLOADS["bigbird-L2048"].with_(batch=3, heads=1, padded=True, data_seed=11)
+    _case(wl, "bwd pad d64 L2048")
+
+
+def test_backward_alone_on_oracle_forward():
+    """The backward fed the oracle's O (bf16) and LSE (fp32) instead of the HIP forward's."""
+    wl = WORKLOADS["bigbird-L2048"].with_(batch=1, heads=2, data_seed=5)
+    _say("bwd alone", wl)
+    inp = make_inputs(wl)
+    do = make_grad_output(wl)
+    lay, olay = _layouts(wl)
+    ro, rl = OA.attention_forward(inp["q"], inp["k"], inp["v"], olay, wl.scale)
+    o = torch.from_numpy(ro).to(torch.bfloat16).cuda()
+    lse = torch.from_numpy(rl).to(torch.float32).cuda()
+    got = _hip_backward(wl, inp, do, lay, o=o, lse=lse)
+    ref = OG.attention_backward(inp["q"], inp["k"], inp["v"], do, olay, wl.scale)
+    _compare(got, ref, "bwd alone")
+
+
+def test_backward_workspace_dirty_and_reused():
+    wl = WORKLOADS["bigbird-L2048"].with_(batch=1, heads=2, data_seed=9)
+    _say("bwd dirty workspace", wl)
+    inp = make_inputs(wl)
+    do = make_grad_output(wl).cuda()
+    lay, olay = _layouts(wl)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    o, lse = bs.forward(dev["q"], dev["k"], dev["v"], lay, scale=wl.scale)
+    n = bs.bsattn_backward_workspace_size(lay, wl.batch, wl.head_dim)
+    ws = torch.full(((n + 255) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    outs = []
+    for _ in range(2):
+        dq, dk, dv = bs.backward(dev["q"], dev["k"], dev["v"], o, lse, do, lay, scale=wl.scale, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((_f64(dq), _f64(dk), _f64(dv)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    ref = OG.attention_backward(inp["q"], inp["k"], inp["v"], do.cpu(), olay, wl.scale)
+    _compare(outs[0], ref, "bwd dirty workspace")
+
+
+def test_backward_benchmark_shape_one_head():
+    wl = WORKLOADS["bigbird-L8192"]
+    _case(wl, "bwd bigbird-L8192 (b=1, h=5)", heads=[5], batches=[1])
+
+
+def test_backward_rows_with_no_key():
+    """Window-only layout with heavy padding: rows past the window of the valid
+    keys see no key (LSE = -inf) and must get zero dQ; keys past the valid
+    length get zero dK and dV."""
+    wl = WORKLOADS["bigbird-L2048"].with_(batch=2, heads=2, seq_len=1024, global_blocks=(), random_blocks=0,
+                                          padded=True, data_seed=13)
+    _say("bwd empty rows", wl)
+    inp = make_inputs(wl)
+    inp["valid_len"] = torch.tensor([100, 1024], dtype=torch.int32)
+    do = make_grad_output(wl)
+    lay, olay = _layouts(wl)
+    got = _hip_backward(wl, inp, do, lay)
+    ref = OG.attention_backward(inp["q"], inp["k"], inp["v"], do, olay, wl.scale, valid_len=[100, 1024])
+    assert (got[0][0, :, 3 * 64:] == 0).all()          # rows of blocks >= 3 see no valid key
+    assert (got[1][0, :, 100:] == 0).all() and (got[2][0, :, 100:] == 0).all()
+    _compare(got, ref, "bwd empty rows")

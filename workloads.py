@@ -125,3 +125,14 @@ def make_inputs(wl: Workload, device: Optional[str] = None) -> dict:
     if device is not None:
         out = {k: v.to(device) for k, v in out.items()}
     return out
+
+
+def make_grad_output(wl: Workload, device: Optional[str] = None) -> torch.Tensor:
+    """The upstream gradient dO for a backward pass over ``wl``: [B, H, L, D]
+    standard normal (fp32 ``randn``, cast like Q/K/V), from its own generator
+    seeded with ``data_seed + 1000`` so that the forward inputs are unchanged."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(wl.data_seed + 1000)
+    shape = (wl.batch, wl.heads, wl.seq_len, wl.head_dim)
+    x = torch.randn(shape, generator=g, dtype=torch.float32).to(torch_dtype(wl)).contiguous()
+    return x if device is None else x.to(device)
