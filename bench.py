@@ -5,7 +5,10 @@
 
 One step = one full forward (``bsattn_forward``: every non-zero 64x64 tile of
 the layout, the split of the dense global rows and their log-sum-exp merge)
-over one batch of the workload, inputs already resident in HBM.  W untimed
+over one batch of the workload, inputs already resident in HBM.  With
+``--pass backward`` a step is one full backward (``bsattn_backward``: delta,
+the dQ pass, the dK/dV pass and the sums of split rows and columns) on the
+forward's outputs and a seeded upstream gradient.  W untimed
 steps, then exactly K timed steps bracketed by device synchronisation; three
 copies of the inputs are rotated so that consecutive steps do not hit the
 256 MB last-level cache with the previous step's tensors.
@@ -31,9 +34,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "block-sparse attn fwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), L=8192"
+METRIC_BWD = "block-sparse attn bwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), L=8192"
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "fwd_bf16.hip")
+BWD_KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "bwd_bf16.hip")
 # the attention kernel that dominates a bf16 forward: one for D = 64, one for D = 128
 def main_kernel(head_dim: int) -> str:
     return "fwd_bf16_d64_kernel" if head_dim == 64 else "fwd_bf16_kernel"
@@ -46,6 +51,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default=None, help="default: the L=8192 BigBird workload")
     p.add_argument("--rotate", type=int, default=3, help="input copies rotated across steps")
+    p.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+                   help="time the forward (default) or the backward")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="the CPU baseline runs whole (batch, head) pairs until this much time has passed")
@@ -67,7 +74,7 @@ def tile_stats(wl, row_ptr, col, valid_len=None):
     return total
 
 
-def traffic_from_profile(workload: str, kernel: str):
+def traffic_from_profile(workload: str, kernel: str, source: str = KERNEL_SOURCE):
     """HBM bytes per launch of the main kernel from the committed counter summary, or None
     when the summary is missing or the kernel source changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
@@ -78,7 +85,7 @@ def traffic_from_profile(workload: str, kernel: str):
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_sha or not m_b:
         return None
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
     if sha != m_sha.group(1):
         return None
     return float(m_b.group(1))
@@ -118,6 +125,32 @@ def cpu_baseline(wl, inp, layout_o, seconds: float):
             "kind": "oracle",
             "sample": f"{len(pairs)} of {wl.batch * wl.heads} (batch, head) pairs, all {wl.seq_len} query rows, "
                       f"dense fp64 masked attention; {dt:.2f} s measured, scaled to the whole job",
+            "seconds": round(dt, 3)}
+
+
+def cpu_baseline_bwd(wl, inp, do, layout_o, seconds: float):
+    """The oracle backward as it stands, on whole (batch, head) pairs taken in order until
+    ``seconds`` have passed, scaled to the whole job."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_grad as OG
+    all_pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)]
+    vl = inp.get("valid_len")
+    pairs = []
+    t0 = time.perf_counter()
+    for b, h in all_pairs:
+        OG.attention_backward(inp["q"], inp["k"], inp["v"], do, layout_o, wl.scale,
+                              valid_len=None if vl is None else vl.tolist(), heads=[h], batches=[b])
+        pairs.append((b, h))
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    full_s = dt * (wl.batch * wl.heads) / len(pairs)
+    return {"value": wl.batch * wl.seq_len / full_s, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(pairs)} of {wl.batch * wl.heads} (batch, head) pairs, all {wl.seq_len} query rows, "
+                      f"dense fp64 masked attention gradients; {dt:.2f} s measured, scaled to the whole job",
             "seconds": round(dt, 3)}
 
 
@@ -184,11 +217,45 @@ def main():
                       s["v"].data_ptr(), o.data_ptr(), l.data_ptr(), None if vl is None else vl.data_ptr(),
                       ctypes.c_float(wl.scale), ws.data_ptr(), ctypes.c_size_t(ws_bytes), sh))
     fwd = L_.bsattn_forward
+    backward = args.which == "backward"
+    if backward:
+        from workloads import make_grad_output
+        for c in calls:                          # the forward's outputs, once, untimed
+            st = fwd(*c)
+            if st != 0:
+                raise bs.BsattnError("bsattn_forward", st)
+        do_host = make_grad_output(wl)
+        dos = [do_host.to(dev) if r == 0 else do_host.to(dev).clone() for r in range(len(sets))]
+        grads = [[torch.empty((B, H, L, D), dtype=base["q"].dtype, device=dev) for _ in range(3)] for _ in sets]
+        wsb_bytes = bs.bsattn_backward_workspace_size(lay, B, D)
+        wsb = torch.empty(max(1, (wsb_bytes + 255) // 4), dtype=torch.float32, device=dev)
+        bcalls = []
+        for s, o, l, g, dd in zip(sets, outs, lses, grads, dos):
+            vl = s.get("valid_len")
+            bcalls.append((lay.handle, dtype_code, B, H, L, D, s["q"].data_ptr(), s["k"].data_ptr(),
+                           s["v"].data_ptr(), o.data_ptr(), l.data_ptr(), dd.data_ptr(), g[0].data_ptr(),
+                           g[1].data_ptr(), g[2].data_ptr(), None if vl is None else vl.data_ptr(),
+                           ctypes.c_float(wl.scale), wsb.data_ptr(), ctypes.c_size_t(wsb_bytes), sh))
+        bwd = L_.bsattn_backward
+        torch.cuda.synchronize()
+        # algorithmic work: the five products of a backward that recomputes P
+        # (S, dP, dV, dK, dQ), 2 * 64 * 64 * D flop each per tile; the dK/dV
+        # kernel does the first four of them
+        flops_per_step = tiles * 10.0 * 64 * 64 * wl.head_dim
+        kernel_flops = tiles * 8.0 * 64 * 64 * wl.head_dim
+        alg_bytes = wl.batch * wl.heads * wl.seq_len * (8 * wl.head_dim * elem + 4)
 
-    def step(i):
-        st = fwd(*calls[i % len(calls)])
-        if st != 0:
-            raise bs.BsattnError("bsattn_forward", st)
+        def step(i):
+            st = bwd(*bcalls[i % len(bcalls)])
+            if st != 0:
+                raise bs.BsattnError("bsattn_backward", st)
+    else:
+        kernel_flops = flops_per_step
+
+        def step(i):
+            st = fwd(*calls[i % len(calls)])
+            if st != 0:
+                raise bs.BsattnError("bsattn_forward", st)
 
     for i in range(args.warmup):
         step(i)
@@ -216,11 +283,12 @@ def main():
     tokens = B * L
     value = tokens / (ms_step / 1e3)
     eff_tflops = flops_per_step / (ms_step / 1e3) / 1e12
-    kern_tflops = flops_per_step / (kern_avg_ms / 1e3) / 1e12
-    traffic = traffic_from_profile(wl.name, main_kernel(D))
+    kern_tflops = kernel_flops / (kern_avg_ms / 1e3) / 1e12
+    kname = "bwd_dkdv_kernel" if backward else main_kernel(D)
+    traffic = traffic_from_profile(wl.name, kname, BWD_KERNEL_SOURCE if backward else KERNEL_SOURCE)
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if backward else METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -231,9 +299,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded Gaussian Q/K/V of the workload's shape)",
+        "data": "synthetic (seeded Gaussian Q/K/V" + (" and dO" if backward else "") + " of the workload's shape)",
         "config": {
-            "workload": wl.name, "batch": B, "heads": H, "seq_len": L, "head_dim": D, "block": 64,
+            "workload": wl.name, "pass": args.which, "batch": B, "heads": H, "seq_len": L, "head_dim": D, "block": 64,
             "window_blocks": wl.window_blocks, "global_blocks": list(wl.global_blocks),
             "random_blocks": wl.random_blocks, "layout_seed": wl.layout_seed,
             "nonzero_tiles": tiles, "layout_density": round(tiles / (B * H * (L // 64) ** 2), 5),
@@ -244,14 +312,14 @@ def main():
         "layout_build_host_us": round(layout_host_us, 1),
         "roofline": {
             "bound": "mfma",
-            "kernel": main_kernel(D),
+            "kernel": kname,
             "achieved": round(kern_tflops, 2),
             "peak": round(PEAK_BF16_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
-            "flop_per_launch": flops_per_step,
+            "flop_per_launch": kernel_flops,
         },
         "cpu_baseline": None,
     }
@@ -259,7 +327,10 @@ def main():
         from oracle import layout as OL
         olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
                               wl.random_blocks, wl.layout_seed)
-        result["cpu_baseline"] = cpu_baseline(wl, inp, olay, args.cpu_seconds)
+        if backward:
+            result["cpu_baseline"] = cpu_baseline_bwd(wl, inp, do_host, olay, args.cpu_seconds)
+        else:
+            result["cpu_baseline"] = cpu_baseline(wl, inp, olay, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -69,16 +69,32 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 // Physical 16-byte piece of logical piece `piece` in row `row` (an involution).
 __device__ __forceinline__ int swz(int row, int piece) { return piece ^ (row & 7); }
 
-// Copy a 64 x D bf16 tile (row-major, contiguous) into LDS, swizzled.
+// Copy of a 64 x D bf16 tile (row-major, contiguous) into LDS, swizzled, in
+// two halves: load the tile's pieces into registers (issued before the
+// current tile's products, so the loads run behind them), then store them to
+// LDS once the current tile is done.
 template <int D>
-__device__ __forceinline__ void stage(uint16_t* lds, const uint16_t* src, int tid) {
+struct TileRegs {
+    static constexpr int R = 64 * (D / 8) / kBT;
+    u32x4_t v[R];
+};
+template <int D>
+__device__ __forceinline__ void fetch_tile(TileRegs<D>& t, const uint16_t* src, int tid) {
     constexpr int P = D / 8;
 #pragma unroll
-    for (int r = 0; r < 64 * P / kBT; ++r) {
+    for (int r = 0; r < TileRegs<D>::R; ++r) {
+        const int p = tid + r * kBT;
+        t.v[r] = *(const u32x4_t*)(src + (p / P) * D + (p % P) * 8);
+    }
+}
+template <int D>
+__device__ __forceinline__ void commit_tile(uint16_t* lds, const TileRegs<D>& t, int tid) {
+    constexpr int P = D / 8;
+#pragma unroll
+    for (int r = 0; r < TileRegs<D>::R; ++r) {
         const int p = tid + r * kBT;
         const int row = p / P, c = p % P;
-        const u32x4_t v = *(const u32x4_t*)(src + row * D + c * 8);
-        *(u32x4_t*)(lds + row * D + swz(row, c) * 8) = v;
+        *(u32x4_t*)(lds + row * D + swz(row, c) * 8) = t.v[r];
     }
 }
 
@@ -139,25 +155,28 @@ __device__ __forceinline__ void store_row(const f32x16_t (&acc)[D / 32], float m
         }
 }
 
-// delta[row] = sum_d dO[row, d] * O[row, d], one thread per row.
+// delta[row] = sum_d dO[row, d] * O[row, d].  D/8 lanes per row, 16 bytes
+// each, so a wave reads whole rows contiguously; reduced with lane shuffles.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdArgs a) {
-    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (row >= (size_t)a.B * a.H * a.L) return;
-    const uint16_t* o = (const uint16_t*)a.out + row * D;
-    const uint16_t* g = (const uint16_t*)a.dout + row * D;
+    constexpr int LPR = D / 8;   // lanes per row
+    const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t row = gid / LPR;
+    const int c = (int)(gid % LPR);
+    const size_t rows = (size_t)a.B * a.H * a.L;
     float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-        const u32x4_t uo = *(const u32x4_t*)(o + 8 * c);
-        const u32x4_t ug = *(const u32x4_t*)(g + 8 * c);
+    if (row < rows) {
+        const u32x4_t uo = *(const u32x4_t*)((const uint16_t*)a.out + row * D + 8 * c);
+        const u32x4_t ug = *(const u32x4_t*)((const uint16_t*)a.dout + row * D + 8 * c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             acc = fmaf(bf16_to_f32(uo[e] & 0xffffu), bf16_to_f32(ug[e] & 0xffffu), acc);
             acc = fmaf(bf16_to_f32(uo[e] >> 16), bf16_to_f32(ug[e] >> 16), acc);
         }
     }
-    a.delta[row] = acc;
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < rows && c == 0) a.delta[row] = acc;
 }
 
 // dQ pass: workgroup = (item, batch entry); wave w owns queries 32w .. 32w + 31
@@ -195,12 +214,23 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) dqa[db][i] = 0.f;
 
+    TileRegs<D> kr, vr;
+    if (item.begin < item.end) {
+        const int j0 = a.idx[item.begin];
+        fetch_tile<D>(kr, (const uint16_t*)a.k + gbase + (size_t)j0 * TILE, tid);
+        fetch_tile<D>(vr, (const uint16_t*)a.v + gbase + (size_t)j0 * TILE, tid);
+    }
     for (int e = item.begin; e < item.end; ++e) {
         const int j = a.idx[e];
         __syncthreads();   // the previous tile's reads are done
-        stage<D>(kt, (const uint16_t*)a.k + gbase + (size_t)j * TILE, tid);
-        stage<D>(vt, (const uint16_t*)a.v + gbase + (size_t)j * TILE, tid);
+        commit_tile<D>(kt, kr, tid);
+        commit_tile<D>(vt, vr, tid);
         __syncthreads();
+        if (e + 1 < item.end) {   // the next tile's loads run behind this tile's products
+            const int jn = a.idx[e + 1];
+            fetch_tile<D>(kr, (const uint16_t*)a.k + gbase + (size_t)jn * TILE, tid);
+            fetch_tile<D>(vr, (const uint16_t*)a.v + gbase + (size_t)jn * TILE, tid);
+        }
         // S^T = K Q^T and dP^T = V dO^T: block kb holds keys 32kb .. 32kb + 31
         f32x16_t s[2], dp[2];
 #pragma unroll
@@ -273,18 +303,28 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) dka[db][i] = dva[db][i] = 0.f;
 
-    for (int e = item.begin; e < item.end; ++e) {
-        const int i_blk = a.idx[e];
-        __syncthreads();
-        stage<D>(qt, (const uint16_t*)a.q + gbase + (size_t)i_blk * TILE, tid);
-        stage<D>(ot, (const uint16_t*)a.dout + gbase + (size_t)i_blk * TILE, tid);
+    TileRegs<D> qr, orr;
+    float lse_r = 0.f, del_r = 0.f;
+    auto fetch = [&](int ib) {
+        fetch_tile<D>(qr, (const uint16_t*)a.q + gbase + (size_t)ib * TILE, tid);
+        fetch_tile<D>(orr, (const uint16_t*)a.dout + gbase + (size_t)ib * TILE, tid);
         if (tid < 64) {
-            const size_t r = grp * a.L + (size_t)i_blk * 64 + tid;
-            const float lse = a.lse[r];
-            nlse[tid] = lse == -INFINITY ? -INFINITY : -lse / a.scale;
-            ndel[tid] = -a.delta[r];
+            const size_t r = grp * a.L + (size_t)ib * 64 + tid;
+            lse_r = a.lse[r];
+            del_r = a.delta[r];
+        }
+    };
+    if (item.begin < item.end) fetch(a.idx[item.begin]);
+    for (int e = item.begin; e < item.end; ++e) {
+        __syncthreads();
+        commit_tile<D>(qt, qr, tid);
+        commit_tile<D>(ot, orr, tid);
+        if (tid < 64) {
+            nlse[tid] = lse_r == -INFINITY ? -INFINITY : -lse_r / a.scale;
+            ndel[tid] = -del_r;
         }
         __syncthreads();
+        if (e + 1 < item.end) fetch(a.idx[e + 1]);   // behind this tile's products
         // S = Q K^T - LSE/scale and dP = dO V^T - delta: block qb holds queries 32qb .. 32qb + 31,
         // register i <-> query 32qb + 8(i/4) + 4hh + i%4
         f32x16_t s[2], dp[2];
@@ -336,27 +376,42 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
 }
 
 // Sum of a split row's (column's) fp32 partials into the bf16 output block.
+// One workgroup per (split, batch entry, 1024-element slice of the 64 x D
+// block); each thread owns 4 elements and issues its chunks' loads together.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_sum_kernel(const BwdArgs a, int which) {
-    const int si = blockIdx.x / a.B, b = blockIdx.x % a.B;
+    constexpr int SLICES = 64 * D / 1024;
+    const int slice = blockIdx.x % SLICES;
+    const int rest = blockIdx.x / SLICES;
+    const int si = rest / a.B, b = rest % a.B;
     const BwdSum sm = a.sums[si];
     const int h = sm.head_blk / a.nb, blk = sm.head_blk % a.nb;
     const size_t out_base = (((size_t)b * a.H + h) * a.L + (size_t)blk * 64) * D;
+    const int x = slice * 1024 + threadIdx.x * 4;
     const int n_out = which == 0 ? 1 : 2;
     for (int o = 0; o < n_out; ++o) {
         const float* ws = which == 0 ? a.ws_dq : (o == 0 ? a.ws_dk : a.ws_dv);
         uint16_t* dst = (uint16_t*)(which == 0 ? a.dq : (o == 0 ? a.dk : a.dv)) + out_base;
-        for (int x = threadIdx.x * 4; x < 64 * D; x += 256 * 4) {
-            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int ch = 0; ch < sm.n_chunks; ++ch) {
-                const float4 v = *(const float4*)(ws + ((size_t)b * a.n_slots + sm.first_slot + ch) * 64 * D + x);
-                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        const float* src = ws + ((size_t)b * a.n_slots + sm.first_slot) * 64 * D + x;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        int ch = 0;
+        for (; ch + 4 <= sm.n_chunks; ch += 4) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *(const float4*)(src + (size_t)(ch + u) * 64 * D);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
             }
-            u32x2_t w;
-            w.x = pack_bf16x2(acc.x, acc.y);
-            w.y = pack_bf16x2(acc.z, acc.w);
-            *(u32x2_t*)(dst + x) = w;
         }
+        for (; ch < sm.n_chunks; ++ch) {
+            const float4 v = *(const float4*)(src + (size_t)ch * 64 * D);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        u32x2_t w;
+        w.x = pack_bf16x2(acc.x, acc.y);
+        w.y = pack_bf16x2(acc.z, acc.w);
+        *(u32x2_t*)(dst + x) = w;
     }
 }
 
@@ -379,8 +434,8 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd_delta(const BwdArgs& a, int head_dim, hipStream_t s) {
-    const int64_t rows = (int64_t)a.B * a.H * a.L;
-    const int64_t grid = (rows + 255) / 256;
+    const int64_t threads = (int64_t)a.B * a.H * a.L * (head_dim / 8);
+    const int64_t grid = (threads + 255) / 256;
     if (grid == 0) return hipSuccess;
     if (head_dim == 64) hipLaunchKernelGGL((bwd_delta_kernel<64>), dim3((unsigned)grid), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((bwd_delta_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, a);
@@ -398,7 +453,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t
 }
 
 hipError_t launch_bwd_sum(const BwdArgs& a, int head_dim, int which, hipStream_t s) {
-    const int64_t grid = (int64_t)a.n_sums * a.B;
+    const int64_t grid = (int64_t)a.n_sums * a.B * (64 * head_dim / 1024);
     if (grid == 0) return hipSuccess;
     if (head_dim == 64) hipLaunchKernelGGL((bwd_sum_kernel<64>), dim3((unsigned)grid), dim3(256), 0, s, a, which);
     else hipLaunchKernelGGL((bwd_sum_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, a, which);
