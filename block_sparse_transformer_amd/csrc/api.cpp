@@ -111,14 +111,17 @@ void build_bwd(bsattn_layout* lay) {
             for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a)
                 bw.k_idx[(size_t)fill[(size_t)h * nb + lay->col_idx[a]]++] = i;
         }
+    // per head, longest first, padded with empty items (head_blk -1) to a common length
     auto make = [&](const std::vector<int32_t>& ptr, std::vector<BwdItem>& items, std::vector<BwdSum>& sums,
-                    int32_t& n_slots) {
+                    int32_t& n_slots, int32_t& per_head) {
         n_slots = 0;
+        std::vector<std::vector<BwdItem>> heads((size_t)H);
         for (int32_t hb = 0; hb < H * nb; ++hb) {
+            auto& hi = heads[(size_t)(hb / nb)];
             const int32_t b0 = ptr[(size_t)hb], b1 = ptr[(size_t)hb + 1];
             const int32_t len = b1 - b0;
             if (len <= kChunkTiles) {
-                items.push_back({hb, b0, b1, -1});
+                hi.push_back({hb, b0, b1, -1});
                 continue;
             }
             int32_t nch, per;
@@ -126,14 +129,22 @@ void build_bwd(bsattn_layout* lay) {
             sums.push_back({hb, n_slots, nch, 0});
             for (int32_t c = 0; c < nch; ++c) {
                 const int32_t s0 = b0 + c * per;
-                items.push_back({hb, s0, std::min(b1, s0 + per), n_slots++});
+                hi.push_back({hb, s0, std::min(b1, s0 + per), n_slots++});
             }
         }
-        std::stable_sort(items.begin(), items.end(),
-                         [](const BwdItem& x, const BwdItem& y) { return (x.end - x.begin) > (y.end - y.begin); });
+        per_head = 0;
+        for (auto& hi : heads) {
+            std::stable_sort(hi.begin(), hi.end(),
+                             [](const BwdItem& x, const BwdItem& y) { return (x.end - x.begin) > (y.end - y.begin); });
+            per_head = std::max<int32_t>(per_head, (int32_t)hi.size());
+        }
+        for (auto& hi : heads) {
+            items.insert(items.end(), hi.begin(), hi.end());
+            for (size_t a = hi.size(); a < (size_t)per_head; ++a) items.push_back({-1, 0, 0, -1});
+        }
     };
-    make(lay->row_ptr, bw.q_items, bw.q_sums, bw.n_qslots);
-    make(cptr, bw.k_items, bw.k_sums, bw.n_kslots);
+    make(lay->row_ptr, bw.q_items, bw.q_sums, bw.n_qslots, bw.q_per_head);
+    make(cptr, bw.k_items, bw.k_sums, bw.n_kslots, bw.k_per_head);
     bw.built = true;
 }
 
@@ -857,7 +868,7 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     const auto& bw = lay->bwd;
-    if ((int64_t)B * std::max(bw.q_items.size(), bw.k_items.size()) >= ((int64_t)1 << 31))
+    if (((int64_t)B * H + kXcds) * std::max(bw.q_per_head, bw.k_per_head) >= ((int64_t)1 << 31))
         return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
     {
         std::lock_guard<std::mutex> guard(*lay->sched_mu);
@@ -882,14 +893,14 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
     hipError_t e = launch_bwd_delta(a, D, stream);
     if (e != hipSuccess) return hip_fail(e, "backward delta launch");
 
-    a.items = bw.d_q_items; a.n_items = (int32_t)bw.q_items.size();
+    a.items = bw.d_q_items; a.n_items = (int32_t)bw.q_items.size(); a.items_per_head = bw.q_per_head;
     a.sums = bw.d_q_sums; a.n_sums = (int32_t)bw.q_sums.size();
     a.idx = lay->d_col_idx; a.n_slots = bw.n_qslots;
     e = launch_bwd_dq(a, D, mask, stream);
     if (e != hipSuccess) return hip_fail(e, "backward dQ launch");
     if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 0, stream)) != hipSuccess) return hip_fail(e, "backward dQ sum launch");
 
-    a.items = bw.d_k_items; a.n_items = (int32_t)bw.k_items.size();
+    a.items = bw.d_k_items; a.n_items = (int32_t)bw.k_items.size(); a.items_per_head = bw.k_per_head;
     a.sums = bw.d_k_sums; a.n_sums = (int32_t)bw.k_sums.size();
     a.idx = bw.d_k_idx; a.n_slots = bw.n_kslots;
     if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -128,10 +128,11 @@ struct BwdArgs {
     float* ws_dq;             // [B*n_qslots][64][D] fp32 partials
     float* ws_dk;             // [B*n_kslots][64][D]
     float* ws_dv;             // [B*n_kslots][64][D]
-    const BwdItem* items;     // this launch's items (dQ or dK/dV)
+    const BwdItem* items;     // this launch's items (dQ or dK/dV), [H][items_per_head]
     const int32_t* idx;       // this launch's block lists
     const BwdSum* sums;
     int32_t n_items, n_sums;
+    int32_t items_per_head;   // per-head item lists padded to this length (head_blk < 0: none)
     const int32_t* valid_len; // [B] or null
     int32_t B, H, L, nb, n_slots;
     float scale;              // score scale
@@ -187,7 +188,8 @@ struct bsattn_layout {
     // backward work lists, built and uploaded on the first backward call
     struct Bwd {
         int32_t n_qslots = 0, n_kslots = 0;
-        std::vector<bsattn::BwdItem> q_items, k_items;   // longest first
+        int32_t q_per_head = 0, k_per_head = 0;
+        std::vector<bsattn::BwdItem> q_items, k_items;   // [H][per_head], longest first
         std::vector<bsattn::BwdSum> q_sums, k_sums;
         std::vector<int32_t> k_idx;                      // query blocks per key block (CSC)
         bsattn::BwdItem* d_q_items = nullptr;

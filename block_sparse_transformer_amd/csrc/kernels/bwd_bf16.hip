@@ -155,6 +155,22 @@ __device__ __forceinline__ void store_row(const f32x16_t (&acc)[D / 32], float m
         }
 }
 
+// Workgroup -> (batch entry, head, item).  Workgroups are dealt round-robin
+// to the 8 XCDs; XCD x takes the (b, h) groups x, x + 8, ... one after the
+// other, so that the tiles a group's items read stay in that XCD's L2.
+__device__ __forceinline__ bool take_item(const BwdArgs& a, int& b, int& h, int& blk, BwdItem& item) {
+    const int x = blockIdx.x % kXcds;
+    const int k = blockIdx.x / kXcds;
+    const int g = x + kXcds * (k / a.items_per_head);
+    if (g >= a.B * a.H) return false;
+    b = g / a.H;
+    h = g % a.H;
+    item = a.items[(size_t)h * a.items_per_head + k % a.items_per_head];
+    if (item.head_blk < 0) return false;
+    blk = item.head_blk % a.nb;
+    return true;
+}
+
 // delta[row] = sum_d dO[row, d] * O[row, d].  D/8 lanes per row, 16 bytes
 // each, so a wave reads whole rows contiguously; reduced with lane shuffles.
 template <int D>
@@ -189,9 +205,9 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ql = lane & 31, hh = lane >> 5, gi = lane & 15, gsel = (lane >> 4) & 1;
-    const int it = blockIdx.x / a.B, b = blockIdx.x % a.B;
-    const BwdItem item = a.items[it];
-    const int h = item.head_blk / a.nb, blk = item.head_blk % a.nb;
+    int b, h, blk;
+    BwdItem item;
+    if (!take_item(a, b, h, blk, item)) return;
     const size_t grp = (size_t)b * a.H + h;
     const size_t gbase = grp * a.L * D;
     const int t = blk * 64 + wave * 32 + ql;
@@ -281,9 +297,9 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int kl = lane & 31, hh = lane >> 5, gi = lane & 15, gsel = (lane >> 4) & 1;
-    const int it = blockIdx.x / a.B, b = blockIdx.x % a.B;
-    const BwdItem item = a.items[it];
-    const int h = item.head_blk / a.nb, blk = item.head_blk % a.nb;
+    int b, h, blk;
+    BwdItem item;
+    if (!take_item(a, b, h, blk, item)) return;
     const size_t grp = (size_t)b * a.H + h;
     const size_t gbase = grp * a.L * D;
     const int key = blk * 64 + wave * 32 + kl;
@@ -417,7 +433,8 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(const BwdArgs a, int which
 
 template <int D, int MASK>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
-    const int64_t grid = (int64_t)a.n_items * a.B;
+    const int64_t groups = (int64_t)a.B * a.H;
+    const int64_t grid = (groups + kXcds - 1) / kXcds * kXcds * a.items_per_head;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dq_kernel<D, MASK>), dim3((unsigned)grid), dim3(kBT), 0, s, a);
     return hipGetLastError();
@@ -425,7 +442,8 @@ hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
 
 template <int D, int MASK>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
-    const int64_t grid = (int64_t)a.n_items * a.B;
+    const int64_t groups = (int64_t)a.B * a.H;
+    const int64_t grid = (groups + kXcds - 1) / kXcds * kXcds * a.items_per_head;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK>), dim3((unsigned)grid), dim3(kBT), 0, s, a);
     return hipGetLastError();
