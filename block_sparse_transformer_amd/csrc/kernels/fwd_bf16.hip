@@ -1083,8 +1083,9 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // row with no allowed key at all gets O = 0, LSE = -inf.  Runs as its own
 // launch after the attention kernel, so stream order makes the partials
 // visible without any device-scope fence.  Four workgroups per split row, 16
-// query rows each; 16 threads per row, each owning D/16 columns.  All loads
-// of a thread are issued before their results are used.
+// query rows each; 16 threads per row, each owning D/16 columns.  The chunk
+// LSEs and the first 8 chunks' partials are loaded in one batch, before any
+// of them is used.
 template <int D>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
     constexpr int DP = D / 16;   // columns per thread: 4 or 8
@@ -1112,10 +1113,19 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
     }
     if (t < 0) return;
     const float* lse_p = a.ws_lse + (size_t)first * 64 + row;
+    const float* src = a.ws_o + ((size_t)first * 64 + row) * D + part * DP;
+    // the chunk LSEs and the first 8 chunks' partials are loaded together:
+    // one memory round trip for the common case of at most 8 chunks
     float lsev[kMaxChunks];
-    float mxl = -INFINITY;
+    float4 v4[8][DP / 4];
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) lsev[c] = c < nch ? lse_p[(size_t)c * 64] : -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int d = 0; d < DP / 4; ++d)
+            v4[c][d] = c < nch ? *(const float4*)(src + (size_t)c * 64 * D + 4 * d) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float mxl = -INFINITY;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) mxl = __builtin_fmaxf(mxl, lsev[c]);
     uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * DP;
@@ -1129,17 +1139,17 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
 #pragma unroll
     for (int d = 0; d < DP; ++d) acc[d] = 0.f;
     float wsum = 0.f;
-    const float* src = a.ws_o + ((size_t)first * 64 + row) * D + part * DP;
 #pragma unroll
     for (int c0 = 0; c0 < kMaxChunks; c0 += 8) {
         if (c0 >= nch) break;
-        float4 v4[8][DP / 4];
+        if (c0 > 0) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
+            for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int d = 0; d < DP / 4; ++d)
-                v4[c][d] = c0 + c < nch ? *(const float4*)(src + (size_t)(c0 + c) * 64 * D + 4 * d)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int d = 0; d < DP / 4; ++d)
+                    v4[c][d] = c0 + c < nch ? *(const float4*)(src + (size_t)(c0 + c) * 64 * D + 4 * d)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const float w = expf(lsev[c0 + c] - mxl);   // 0 past nch (lse -inf)
