@@ -16,6 +16,8 @@ Modules
 ``router``    the routed-query selection: exact fp64 score q.w and top-k.
 ``attention_grad``  the gradients (dQ, dK, dV) of the masked attention for
               an upstream dO: the softmax Jacobian written out in fp64.
+``layer``     the attention layer around it: qkv projection, head split,
+              attention, head concatenation, output projection.
 
 Parity pins (see ``tests/test_oracle_*.py``): every function is checked
 against something other than itself -- published splitmix64 outputs, closed
@@ -26,4 +28,4 @@ Parity unpinned: the concrete choice of random blocks beyond the
 hash stream itself (the composition of the per-row seed and the shuffle are
 this library's own specification; any uniform draw satisfies the pages).
 """
-from . import layout, attention, attention_grad, router  # noqa: F401
+from . import layout, attention, attention_grad, layer, router  # noqa: F401
