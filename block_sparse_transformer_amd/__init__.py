@@ -7,8 +7,8 @@ the HIP kernels of the library; there is no CPU fallback, and every function
 raises if the library has not been built.
 
 Functions carry the C names (``bsattn_make_layout``, ``bsattn_forward``, ...)
-plus conveniences, :func:`forward`, :func:`forward_routed` and
-:func:`backward`, that allocate outputs and workspace with torch.
+plus conveniences, :func:`forward`, :func:`forward_routed`, :func:`backward`
+and :func:`layer_forward`, that allocate outputs and workspace with torch.
 """
 from ._binding import (  # noqa: F401
     BsattnError,
@@ -19,6 +19,8 @@ from ._binding import (  # noqa: F401
     bsattn_forward,
     bsattn_forward_routed,
     bsattn_last_error,
+    bsattn_layer_forward,
+    bsattn_layer_workspace_size,
     bsattn_layout_build_device,
     bsattn_layout_csr,
     bsattn_layout_destroy,
@@ -31,6 +33,7 @@ from ._binding import (  # noqa: F401
     bsattn_workspace_size,
     forward,
     forward_routed,
+    layer_forward,
     lib,
     library_path,
     HipEvents,

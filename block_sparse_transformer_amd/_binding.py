@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_backward.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
                                   _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp,
                                   ctypes.c_size_t, _c_vp]
+    L.bsattn_layer_workspace_size.argtypes = [_c_vp, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]
+    L.bsattn_layer_forward.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                       _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_size_t, _c_vp]
     L.bsattn_set_profile_events.argtypes = [_c_vp, _c_vp]
     L.bsattn_status_string.argtypes = [ctypes.c_int]
     L.bsattn_status_string.restype = ctypes.c_char_p
@@ -262,6 +265,45 @@ def bsattn_backward(layout: Layout, q, k, v, out, lse, dout, dq, dk, dv, key_val
         layout.handle, _dtype_code(q), B, H, L, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(key_valid_len), scale, _ptr(workspace), wbytes,
         _stream_handle(stream)))
+
+
+def bsattn_layer_workspace_size(layout: Layout, batch: int, head_dim: int) -> int:
+    n = ctypes.c_size_t()
+    _check("bsattn_layer_workspace_size",
+           lib().bsattn_layer_workspace_size(layout.handle, batch, head_dim, ctypes.byref(n)))
+    return n.value
+
+
+def bsattn_layer_forward(layout: Layout, x, w_qkv, b_qkv, w_proj, b_proj, out, num_heads: int,
+                         key_valid_len=None, scale: Optional[float] = None, workspace=None, stream=None) -> None:
+    """Enqueue the attention layer; all tensors are caller-allocated bf16 device tensors."""
+    import torch
+    B, L, C = x.shape
+    D = C // num_heads
+    shapes = {"x": (x, (B, L, C)), "w_qkv": (w_qkv, (3 * C, C)), "b_qkv": (b_qkv, (3 * C,)),
+              "w_proj": (w_proj, (C, C)), "b_proj": (b_proj, (C,)), "out": (out, (B, L, C))}
+    for name, (t, shape) in shapes.items():
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+    if key_valid_len is not None and (key_valid_len.dtype != torch.int32 or key_valid_len.numel() != B):
+        raise ValueError("key_valid_len must be int32 [B]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bsattn_layer_forward", lib().bsattn_layer_forward(
+        layout.handle, B, num_heads, L, D, _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj), _ptr(b_proj),
+        _ptr(out), _ptr(key_valid_len), scale, _ptr(workspace), wbytes, _stream_handle(stream)))
+
+
+def layer_forward(x, w_qkv, b_qkv, w_proj, b_proj, layout: Layout, num_heads: int, key_valid_len=None,
+                  scale: Optional[float] = None, workspace=None):
+    """Allocate out and workspace with torch and run :func:`bsattn_layer_forward`."""
+    import torch
+    out = torch.empty_like(x)
+    if workspace is None:
+        n = bsattn_layer_workspace_size(layout, x.shape[0], x.shape[2] // num_heads)
+        workspace = torch.empty((n + 255) // 4, dtype=torch.float32, device=x.device)
+    bsattn_layer_forward(layout, x, w_qkv, b_qkv, w_proj, b_proj, out, num_heads, key_valid_len, scale, workspace)
+    return out
 
 
 def bsattn_set_profile_events(before: Optional[int], after: Optional[int]) -> None:

@@ -24,6 +24,7 @@ SOURCES = [
     "api.cpp",
     "kernels/fwd_bf16.hip",
     "kernels/bwd_bf16.hip",
+    "kernels/layer.hip",
     "kernels/fwd_f32.hip",
     "kernels/router.hip",
     "kernels/layout_build.hip",
@@ -58,7 +59,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+           "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -10,6 +10,8 @@
 #include <new>
 #include <string>
 
+#include <rocblas/rocblas.h>
+
 #include "internal.h"
 
 using namespace bsattn;
@@ -490,6 +492,52 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
     return BSATTN_OK;
 }
 
+// ---- attention layer ----
+
+// rocBLAS handles, one per (thread, device); created on first use.
+rocblas_handle blas_handle(int dev) {
+    thread_local std::vector<rocblas_handle> handles;
+    if (handles.size() <= (size_t)dev) handles.resize((size_t)dev + 1, nullptr);
+    if (!handles[(size_t)dev] && rocblas_create_handle(&handles[(size_t)dev]) != rocblas_status_success)
+        handles[(size_t)dev] = nullptr;
+    return handles[(size_t)dev];
+}
+
+// Row-major C[M, N] (fp32) = A[M, K] (bf16) * W[N, K]^T (bf16): in rocBLAS's
+// column-major terms C^T = W * A^T, i.e. op(W) = transpose, op(A) = none.
+rocblas_status gemm_xwt(rocblas_handle h, const void* A, const void* W, float* C, int M, int N, int K) {
+    const float one = 1.f, zero = 0.f;
+    return rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &one, W,
+                           rocblas_datatype_bf16_r, K, A, rocblas_datatype_bf16_r, K, &zero, C,
+                           rocblas_datatype_f32_r, N, C, rocblas_datatype_f32_r, N, rocblas_datatype_f32_r,
+                           rocblas_gemm_algo_standard, 0, 0);
+}
+
+// Workspace of bsattn_layer_forward: [qkv32 | out32] [q | o2] [k] [v] [o] [lse] [attention workspace].
+struct LayerWs {
+    size_t qkv32, q, k, v, o, lse, attn, total;
+};
+LayerWs layer_workspace(const bsattn_layout* lay, int32_t B, int32_t D, size_t attn_bytes) {
+    const size_t rows = (size_t)B * lay->L;
+    const size_t C = (size_t)lay->H * D;
+    LayerWs w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    w.qkv32 = take(rows * 3 * C * sizeof(float));
+    w.q = take(rows * C * 2);
+    w.k = take(rows * C * 2);
+    w.v = take(rows * C * 2);
+    w.o = take(rows * C * 2);
+    w.lse = take(rows * lay->H * sizeof(float));
+    w.attn = take(attn_bytes);
+    w.total = off;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -909,6 +957,71 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
     if (g_ev_after && (e = hipEventRecord(g_ev_after, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 1, stream)) != hipSuccess)
         return hip_fail(e, "backward dK/dV sum launch");
+    return ok();
+}
+
+bsattn_status bsattn_layer_workspace_size(const bsattn_layout* lay, int32_t batch, int32_t head_dim,
+                                          size_t* bytes) {
+    if (!lay || !bytes) return fail(BSATTN_ERR_INVALID_ARG, "NULL argument");
+    size_t attn = 0;
+    bsattn_status st = bsattn_workspace_size(lay, batch, head_dim, 0, &attn);
+    if (st != BSATTN_OK) return st;
+    *bytes = layer_workspace(lay, batch, head_dim, attn).total;
+    return ok();
+}
+
+bsattn_status bsattn_layer_forward(const bsattn_layout* lay, int32_t B, int32_t H, int32_t L, int32_t D,
+                                   const void* x, const void* w_qkv, const void* b_qkv, const void* w_proj,
+                                   const void* b_proj, void* out, const int32_t* key_valid_len, float scale,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (lay->kind != 0) return fail(BSATTN_ERR_UNSUPPORTED, "the layer takes window/global/random layouts");
+    if (!x || !w_qkv || !b_qkv || !w_proj || !b_proj || !out) return fail(BSATTN_ERR_INVALID_ARG, "NULL pointer");
+    const void* ps[6] = {x, w_qkv, b_qkv, w_proj, b_proj, out};
+    for (const void* p : ps)
+        if (!aligned16(p)) return fail(BSATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    if (out == x || out == w_qkv || out == b_qkv || out == w_proj || out == b_proj)
+        return fail(BSATTN_ERR_INVALID_ARG, "out aliases an input");
+    if (H != lay->H || L != lay->L) return fail(BSATTN_ERR_INVALID_ARG, "H=%d L=%d do not match the layout", H, L);
+    if (B < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch must be >= 1");
+    if (D != 64 && D != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+    const int64_t rows = (int64_t)B * L, C = (int64_t)H * D;
+    if (rows * 3 * C >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31))
+        return fail(BSATTN_ERR_UNSUPPORTED, "layer too large for 32-bit GEMM sizes");
+    size_t attn_bytes = 0;
+    bsattn_status st = bsattn_workspace_size(lay, B, D, 0, &attn_bytes);
+    if (st != BSATTN_OK) return st;
+    const LayerWs w = layer_workspace(lay, B, D, attn_bytes);
+    if (!workspace || workspace_bytes < w.total)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", w.total, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    rocblas_handle hb = blas_handle(dev);
+    if (!hb) return fail(BSATTN_ERR_HIP, "rocblas_create_handle failed");
+    if (rocblas_set_stream(hb, stream) != rocblas_status_success) return fail(BSATTN_ERR_HIP, "rocblas_set_stream failed");
+
+    char* ws = (char*)workspace;
+    float* qkv32 = (float*)(ws + w.qkv32);
+    void *q = ws + w.q, *k = ws + w.k, *v = ws + w.v, *o = ws + w.o;
+    float* lse = (float*)(ws + w.lse);
+    // 1. qkv = x W_qkv^T (fp32), then + bias, rounded, split into heads
+    if (gemm_xwt(hb, x, w_qkv, qkv32, (int)rows, (int)(3 * C), (int)C) != rocblas_status_success)
+        return fail(BSATTN_ERR_HIP, "qkv GEMM failed");
+    if ((e = launch_split_heads(qkv32, b_qkv, q, k, v, B, L, H, D, stream)) != hipSuccess)
+        return hip_fail(e, "split heads launch");
+    // 2. block-sparse attention
+    st = bsattn_forward(lay, BSATTN_BF16, B, H, L, D, q, k, v, o, lse, key_valid_len, scale,
+                        attn_bytes ? ws + w.attn : nullptr, attn_bytes, stream);
+    if (st != BSATTN_OK) return st;
+    // 3. heads concatenated (into q's space), out = o2 W_proj^T + bias (fp32 in qkv32's space)
+    if ((e = launch_merge_heads(o, q, B, L, H, D, stream)) != hipSuccess) return hip_fail(e, "merge heads launch");
+    if (gemm_xwt(hb, q, w_proj, qkv32, (int)rows, (int)C, (int)C) != rocblas_status_success)
+        return fail(BSATTN_ERR_HIP, "output GEMM failed");
+    if ((e = launch_bias_out(qkv32, b_proj, out, (size_t)rows, (int)C, stream)) != hipSuccess)
+        return hip_fail(e, "output bias launch");
     return ok();
 }
 

@@ -152,6 +152,11 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s);
 // sum split partials into the bf16 output(s): which = 0 dQ, 1 dK and dV
 hipError_t launch_bwd_sum(const BwdArgs& a, int head_dim, int which, hipStream_t s);
+// attention layer (kernels/layer.hip)
+hipError_t launch_split_heads(const float* qkv32, const void* b_qkv, void* q, void* k, void* v, int B, int L,
+                              int H, int D, hipStream_t s);
+hipError_t launch_merge_heads(const void* o, void* o2, int B, int L, int H, int D, hipStream_t s);
+hipError_t launch_bias_out(const float* out32, const void* b_proj, void* out, size_t rows, int C, hipStream_t s);
 hipError_t launch_layout_build(const RowRule& rule, int kind, int32_t H, int32_t nb,
                                int32_t band, int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
 

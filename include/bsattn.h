@@ -221,6 +221,35 @@ bsattn_status bsattn_backward(const bsattn_layout* layout, bsattn_dtype dtype,
                               float scale, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* Device workspace bytes needed by bsattn_layer_forward: the fp32 qkv
+ * projection, the per-head Q, K, V, O (bf16), LSE and the attention's own
+ * workspace.  Written to *bytes. */
+bsattn_status bsattn_layer_workspace_size(const bsattn_layout* layout, int32_t batch,
+                                          int32_t head_dim, size_t* bytes);
+
+/* The attention layer around the block-sparse attention (primer page, section
+ * PyTorch 实现基础稀疏注意力, the SparseAttention module):
+ *   qkv = x w_qkv^T + b_qkv            (width 3C, C = H * D; rows read as (3, H, D))
+ *   O   = block-sparse attention of each head's q, k, v (bsattn_forward)
+ *   out = concat_heads(O) w_proj^T + b_proj
+ *   x        device bf16 [B, L, C], row-major.
+ *   w_qkv    device bf16 [3C, C] (an nn.Linear weight: out x in); b_qkv bf16 [3C].
+ *   w_proj   device bf16 [C, C]; b_proj bf16 [C].
+ *   out      device bf16 [B, L, C]; must not alias an input.
+ *   layout, key_valid_len, scale as bsattn_forward (the page divides by sqrt(C);
+ *   pass the scale wanted).
+ * The two projections are rocBLAS GEMMs (bf16 inputs, fp32 accumulation and
+ * output); the bias adds, the head split and concatenation and the attention
+ * are this library's kernels.  q, k, v and the projections are rounded to
+ * bf16 once each.  Pointers 16-byte aligned, workspace 256-byte aligned.
+ * Enqueued on `stream`; the first call on a thread creates a rocBLAS handle. */
+bsattn_status bsattn_layer_forward(const bsattn_layout* layout, int32_t batch, int32_t num_heads,
+                                   int32_t seq_len, int32_t head_dim, const void* x,
+                                   const void* w_qkv, const void* b_qkv, const void* w_proj,
+                                   const void* b_proj, void* out, const int32_t* key_valid_len,
+                                   float scale, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* Measurement hook: while set (non-NULL), every forward call made from this
  * thread records `before` on its stream immediately before the main attention
  * kernel and `after` immediately after it, and every backward call does the

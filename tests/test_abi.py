@@ -24,6 +24,7 @@ def test_library_exports_every_declared_symbol():
         "bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr", "bsattn_layout_upload",
         "bsattn_layout_build_device", "bsattn_layout_destroy", "bsattn_workspace_size",
         "bsattn_forward", "bsattn_backward_workspace_size", "bsattn_backward",
+        "bsattn_layer_workspace_size", "bsattn_layer_forward",
         "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
         "bsattn_last_error"])
     lib = bs.lib()
@@ -149,3 +150,25 @@ def test_backward_rejects_before_any_hip_call():
     assert call(lay.handle, dv=ctypes.c_void_p(0x9002)) == 1 and "aligned" in bs.bsattn_last_error()
     assert call(lay.handle, D=96) == 2
     assert call(lay.handle, scale=0.0) == 1
+
+
+def test_layer_rejects_before_any_hip_call():
+    L = bs.lib()
+    lay = bs.bsattn_make_layout(2, 1024, 64, 3, [0], 1, 0)
+    band = bs.bsattn_make_band_layout(2, 1024, 64, 32)
+    f = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(8)]
+    ws = ctypes.c_size_t(0)
+
+    def call(layout, H=2, D=64, x=f[0], out=f[5], b_qkv=f[2]):
+        return L.bsattn_layer_forward(layout, 1, H, 1024, D, x, f[1], b_qkv, f[3], f[4], out, None, 0.125,
+                                      None, ws, None)
+
+    assert call(None) == 1
+    assert call(band.handle) == 2
+    assert call(lay.handle, out=f[0]) == 1 and "alias" in bs.bsattn_last_error()
+    assert call(lay.handle, b_qkv=ctypes.c_void_p(0x3008)) == 1 and "aligned" in bs.bsattn_last_error()
+    assert call(lay.handle, H=3) == 1
+    assert call(lay.handle, D=96) == 2
+    assert call(lay.handle) == 1 and "workspace" in bs.bsattn_last_error()
+    n = bs.bsattn_layer_workspace_size(lay, 1, 64)
+    assert n >= 1024 * 128 * (3 * 4 + 4 * 2)

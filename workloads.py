@@ -136,3 +136,27 @@ def make_grad_output(wl: Workload, device: Optional[str] = None) -> torch.Tensor
     shape = (wl.batch, wl.heads, wl.seq_len, wl.head_dim)
     x = torch.randn(shape, generator=g, dtype=torch.float32).to(torch_dtype(wl)).contiguous()
     return x if device is None else x.to(device)
+
+
+def make_layer_params(wl: Workload, device: Optional[str] = None) -> dict:
+    """Input and parameters of the attention layer around ``wl``'s attention:
+    x [B, L, C] standard normal, w_qkv [3C, C] and w_proj [C, C] normal with
+    standard deviation 1/sqrt(C) (so projections keep unit scale), biases
+    b_qkv [3C] and b_proj [C] normal with standard deviation 0.1; C = H * D.
+    Drawn in that order, cast to the workload's dtype, from a generator seeded
+    with ``data_seed + 2000``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(wl.data_seed + 2000)
+    C = wl.heads * wl.head_dim
+    dt = torch_dtype(wl)
+    out = {
+        "x": torch.randn((wl.batch, wl.seq_len, C), generator=g, dtype=torch.float32),
+        "w_qkv": torch.randn((3 * C, C), generator=g, dtype=torch.float32) / C ** 0.5,
+        "w_proj": torch.randn((C, C), generator=g, dtype=torch.float32) / C ** 0.5,
+        "b_qkv": torch.randn((3 * C,), generator=g, dtype=torch.float32) * 0.1,
+        "b_proj": torch.randn((C,), generator=g, dtype=torch.float32) * 0.1,
+    }
+    out = {k: v.to(dt).contiguous() for k, v in out.items()}
+    if device is not None:
+        out = {k: v.to(device) for k, v in out.items()}
+    return out
