@@ -8,7 +8,9 @@ the layout, the split of the dense global rows and their log-sum-exp merge)
 over one batch of the workload, inputs already resident in HBM.  With
 ``--pass backward`` a step is one full backward (``bsattn_backward``: delta,
 the dQ pass, the dK/dV pass and the sums of split rows and columns) on the
-forward's outputs and a seeded upstream gradient.  W untimed
+forward's outputs and a seeded upstream gradient; with ``--pass layer`` a
+step is one ``bsattn_layer_forward`` (qkv projection, head split, attention,
+head concatenation, output projection; no CPU baseline).  W untimed
 steps, then exactly K timed steps bracketed by device synchronisation; three
 copies of the inputs are rotated so that consecutive steps do not hit the
 256 MB last-level cache with the previous step's tensors.
@@ -35,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "block-sparse attn fwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), L=8192"
 METRIC_BWD = "block-sparse attn bwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), L=8192"
+METRIC_LAYER = "block-sparse attn layer fwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), L=8192"
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "fwd_bf16.hip")
@@ -51,8 +54,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default=None, help="default: the L=8192 BigBird workload")
     p.add_argument("--rotate", type=int, default=3, help="input copies rotated across steps")
-    p.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
-                   help="time the forward (default) or the backward")
+    p.add_argument("--pass", dest="which", choices=("forward", "backward", "layer"), default="forward",
+                   help="time the forward (default), the backward, or the whole attention layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="the CPU baseline runs whole (batch, head) pairs until this much time has passed")
@@ -249,6 +252,33 @@ def main():
             st = bwd(*bcalls[i % len(bcalls)])
             if st != 0:
                 raise bs.BsattnError("bsattn_backward", st)
+    elif args.which == "layer":
+        from workloads import make_layer_params
+        C = H * D
+        lp = make_layer_params(wl)
+        lsets = [{k: v.to(dev) for k, v in lp.items()}]
+        for _ in range(1, len(sets)):
+            lsets.append({k: (v if k != "x" else v.clone()) for k, v in lsets[0].items()})
+        louts = [torch.empty((B, L, C), dtype=torch.bfloat16, device=dev) for _ in lsets]
+        wsl_bytes = bs.bsattn_layer_workspace_size(lay, B, D)
+        wsl = torch.empty(max(1, (wsl_bytes + 255) // 4), dtype=torch.float32, device=dev)
+        lcalls = []
+        for ls_, lo, s in zip(lsets, louts, sets):
+            vl = s.get("valid_len")
+            lcalls.append((lay.handle, B, H, L, D, ls_["x"].data_ptr(), ls_["w_qkv"].data_ptr(),
+                           ls_["b_qkv"].data_ptr(), ls_["w_proj"].data_ptr(), ls_["b_proj"].data_ptr(),
+                           lo.data_ptr(), None if vl is None else vl.data_ptr(), ctypes.c_float(wl.scale),
+                           wsl.data_ptr(), ctypes.c_size_t(wsl_bytes), sh))
+        lfwd = L_.bsattn_layer_forward
+        # the two projections (2 * rows * C * 4C flop) plus the attention's tiles
+        kernel_flops = flops_per_step
+        flops_per_step = flops_per_step + 2.0 * B * L * C * 4 * C
+        alg_bytes = alg_bytes + B * L * C * 2 * 2 + 4 * C * C * 2
+
+        def step(i):
+            st = lfwd(*lcalls[i % len(lcalls)])
+            if st != 0:
+                raise bs.BsattnError("bsattn_layer_forward", st)
     else:
         kernel_flops = flops_per_step
 
@@ -288,7 +318,7 @@ def main():
     traffic = traffic_from_profile(wl.name, kname, BWD_KERNEL_SOURCE if backward else KERNEL_SOURCE)
 
     result = {
-        "metric": METRIC_BWD if backward else METRIC,
+        "metric": METRIC_BWD if backward else (METRIC_LAYER if args.which == "layer" else METRIC),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -299,7 +329,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded Gaussian Q/K/V" + (" and dO" if backward else "") + " of the workload's shape)",
+        "data": ("synthetic (seeded Gaussian x and layer weights of the workload's shape)" if args.which == "layer"
+                 else "synthetic (seeded Gaussian Q/K/V" + (" and dO" if backward else "") + " of the workload's shape)"),
         "config": {
             "workload": wl.name, "pass": args.which, "batch": B, "heads": H, "seq_len": L, "head_dim": D, "block": 64,
             "window_blocks": wl.window_blocks, "global_blocks": list(wl.global_blocks),
@@ -323,7 +354,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.which != "layer":
         from oracle import layout as OL
         olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
                               wl.random_blocks, wl.layout_seed)
