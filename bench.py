@@ -185,9 +185,15 @@ def main():
         sys.exit(2)
     inp = make_inputs(wl)
 
+    if wl.band and args.which != "forward":
+        print("band workloads are timed in the forward only", file=sys.stderr)
+        sys.exit(2)
     t0 = time.perf_counter()
-    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
-                                wl.random_blocks, wl.layout_seed)
+    if wl.band:
+        lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+    else:
+        lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+                                    wl.random_blocks, wl.layout_seed)
     layout_host_us = (time.perf_counter() - t0) * 1e6
     bs.bsattn_layout_upload(lay)
     row_ptr, col = bs.bsattn_layout_csr(lay)
@@ -334,7 +340,7 @@ def main():
         "config": {
             "workload": wl.name, "pass": args.which, "batch": B, "heads": H, "seq_len": L, "head_dim": D, "block": 64,
             "window_blocks": wl.window_blocks, "global_blocks": list(wl.global_blocks),
-            "random_blocks": wl.random_blocks, "layout_seed": wl.layout_seed,
+            "random_blocks": wl.random_blocks, "layout_seed": wl.layout_seed, "band_tokens": wl.band_tokens,
             "nonzero_tiles": tiles, "layout_density": round(tiles / (B * H * (L // 64) ** 2), 5),
         },
         "eff_tflops": round(eff_tflops, 2),
@@ -356,8 +362,11 @@ def main():
     }
     if not args.no_cpu_baseline and args.which != "layer":
         from oracle import layout as OL
-        olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
-                              wl.random_blocks, wl.layout_seed)
+        if wl.band:
+            olay = OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+        else:
+            olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+                                  wl.random_blocks, wl.layout_seed)
         if backward:
             result["cpu_baseline"] = cpu_baseline_bwd(wl, inp, do_host, olay, args.cpu_seconds)
         else:

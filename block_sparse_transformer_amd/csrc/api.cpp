@@ -755,8 +755,10 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
     bsattn_status st = check_forward_common(lay, B, H, L, D, q, k, v, out, lse, scale);
     if (st != BSATTN_OK) return st;
-    if (lay->kind != 0) return fail(BSATTN_ERR_INVALID_ARG, "band layouts are used with bsattn_forward_routed");
     if (dtype != BSATTN_BF16 && dtype != BSATTN_F32) return fail(BSATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    const bool band = lay->kind == 1;   // token band |t - s| <= band_tokens (a token-granular window)
+    if (band && dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "band layouts are bf16 only");
+    if (band && key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "band layouts take no key padding");
     size_t need = 0;
     st = bsattn_workspace_size(lay, B, D, 0, &need);
     if (st != BSATTN_OK) return st;
@@ -782,10 +784,10 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     a.items_per_head = lay->items_per_head;
     a.B = B; a.H = H; a.L = L; a.nb = lay->nb; a.n_slots = lay->n_slots;
     a.n_routed = 0; a.n_rt = 0; a.r_chunks = 1; a.r_chunk_tiles = 1; a.r_slot_base = 0;
-    a.band = -1;
+    a.band = band ? lay->band_tokens : -1;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const int mask = key_valid_len ? MASK_PAD : MASK_NONE;
+    const int mask = band ? MASK_BAND : (key_valid_len ? MASK_PAD : MASK_NONE);
 
     hipError_t e;
     if (dtype == BSATTN_F32) {

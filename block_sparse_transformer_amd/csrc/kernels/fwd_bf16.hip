@@ -423,7 +423,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
             }
         }
         if (MASK == MASK_BAND) {
-            if (kind >= 0) {
+            // a tile whose farthest (query, key) pair is inside the band needs no mask
+            if (kind >= 0 && 64 * abs(kind - j) + 63 > a.band) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -916,7 +917,8 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 }
             }
             if (MASK == MASK_BAND) {
-                if (kind >= 0) {
+                // a tile whose farthest (query, key) pair is inside the band needs no mask
+                if (kind >= 0 && 64 * abs(kind - j) + 63 > a.band) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

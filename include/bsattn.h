@@ -131,7 +131,12 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* layout, int32_t batch,
                                     int32_t head_dim, int32_t num_routed, size_t* bytes);
 
 /* Block-sparse attention forward.
- *   layout         uploaded layout with num_heads == H and seq_len == L.
+ *   layout         uploaded layout with num_heads == H and seq_len == L.  A
+ *                  band layout (bsattn_make_band_layout) gives the
+ *                  token-granular sliding window |t - s| <= band_tokens (the
+ *                  primer page's window_size loop, the BigBird page's 64-256
+ *                  token windows); it is bf16 only and takes no key padding
+ *                  (BSATTN_ERR_UNSUPPORTED otherwise).
  *   dtype          element type of q, k, v and out.
  *   batch..head_dim  B >= 1, H, L as in the layout, D in {64, 128}.
  *   q, k, v        device [B, H, L, D], contiguous, 16-byte aligned.

@@ -206,7 +206,7 @@ def test_routed_head_dim_64():
 def test_device_layout_equals_host(name):
     wl = WORKLOADS[name]
     _say("device layout", name)
-    if wl.routed:
+    if wl.routed or wl.band:
         lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
     else:
         lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
@@ -338,3 +338,48 @@ def test_workspace_dirty_and_reused():
     ro, rl = OA.attention_forward(inp["q"], inp["k"], inp["v"], olay, wl.scale)
     _compare(outs[-1][0].float().cpu().numpy().astype(np.float64), outs[-1][1].cpu().numpy().astype(np.float64),
              ro, rl, "bf16", "workspace reuse")
+
+
+# ---------------- token-granular window (band layout through the plain forward) ----------------
+
+def _band_layouts(wl):
+    lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+    bs.bsattn_layout_upload(lay)
+    return lay, OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+
+
+@pytest.mark.parametrize("band,D", [(128, 64), (256, 64), (37, 64), (64, 128), (200, 128)])
+def test_band_window_full(band, D):
+    wl = WORKLOADS["band256-L8192"].with_(batch=2, heads=2, seq_len=1024 + 512, head_dim=D, band_tokens=band)
+    _say("band window", band, D)
+    inp = make_inputs(wl)
+    lay, olay = _band_layouts(wl)
+    o, l = _run(wl, inp, lay)
+    ro, rl = OA.attention_forward(inp["q"], inp["k"], inp["v"], olay, wl.scale)
+    _compare(o, l, ro, rl, wl.dtype, f"band {band} D={D}")
+
+
+def test_band_window_benchmark_shape_sampled():
+    wl = WORKLOADS["band256-L8192"]
+    _say("band window bench shape", wl)
+    inp = make_inputs(wl)
+    lay, olay = _band_layouts(wl)
+    o, l = _run(wl, inp, lay)
+    g = np.random.default_rng(3)
+    rows = [(int(g.integers(wl.batch)), int(g.integers(wl.heads)), int(t))
+            for t in list(g.integers(0, wl.seq_len, 60)) + [0, 255, 256, wl.seq_len - 1]]
+    ro, rl = OA.attention_rows(inp["q"], inp["k"], inp["v"], olay, wl.scale, rows)
+    go = np.stack([o[b, h, t] for b, h, t in rows])
+    gl = np.array([l[b, h, t] for b, h, t in rows])
+    _compare(go, gl, ro, rl, wl.dtype, "band bench shape")
+
+
+def test_band_rejects_padding_and_fp32():
+    wl = WORKLOADS["band256-L8192"].with_(batch=1, heads=1, seq_len=512)
+    lay, _ = _band_layouts(wl)
+    inp = {k: v.cuda() for k, v in make_inputs(wl).items()}
+    with pytest.raises(bs.BsattnError):
+        bs.forward(inp["q"], inp["k"], inp["v"], lay, key_valid_len=torch.tensor([300], dtype=torch.int32,
+                   device="cuda"))
+    with pytest.raises(bs.BsattnError):
+        bs.forward(inp["q"].float(), inp["k"].float(), inp["v"].float(), lay)

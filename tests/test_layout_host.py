@@ -16,7 +16,7 @@ def _both(H, L, w, G, r, seed):
     return got, want
 
 
-@pytest.mark.parametrize("name", [n for n, wl in WORKLOADS.items() if not wl.routed])
+@pytest.mark.parametrize("name", [n for n, wl in WORKLOADS.items() if not (wl.routed or wl.band)])
 def test_workload_layouts_bit_exact(name):
     wl = WORKLOADS[name]
     (rp, ci), (orp, oci) = _both(wl.heads, wl.seq_len, wl.window_blocks, wl.global_blocks,
@@ -28,6 +28,11 @@ def test_workload_layouts_bit_exact(name):
 
 def test_band_layout_bit_exact():
     wl = WORKLOADS["routed-L4096"]
+    lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+    rp, ci = bs.bsattn_layout_csr(lay)
+    orp, oci = OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens).csr()
+    assert np.array_equal(rp, orp) and np.array_equal(ci, oci)
+    wl = WORKLOADS["band256-L8192"]
     lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
     rp, ci = bs.bsattn_layout_csr(lay)
     orp, oci = OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens).csr()

@@ -59,6 +59,11 @@ class Workload:
         return self.routed_k > 0
 
     @property
+    def band(self) -> bool:
+        """A token-band layout without routed rows (the plain forward on a band layout)."""
+        return self.band_tokens > 0 and not self.routed
+
+    @property
     def num_blocks(self) -> int:
         return self.seq_len // self.block
 
@@ -90,6 +95,11 @@ WORKLOADS = {
         data_seed=3, window_blocks=5, global_blocks=(0,), random_blocks=0, layout_seed=3,
         sigma=0.5, padded=True),
     # Routed queries: per head the top-64 rows by q.w attend to every key, the rest to +-32 tokens.
+    # Token-granular sliding window |t - s| <= 256 (the BigBird page's 64-256 token windows)
+    # at the throughput shape: a band layout through the plain forward.
+    "band256-L8192": Workload(
+        name="band256-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
+        data_seed=5, band_tokens=256),
     "routed-L4096": Workload(
         name="routed-L4096", batch=1, heads=32, seq_len=4096, head_dim=128, dtype="bf16",
         data_seed=4, routed_k=64, band_tokens=32),
