@@ -67,7 +67,7 @@ def parse_args():
 def tile_stats(wl, row_ptr, col, valid_len=None):
     """Non-zero 64x64 tiles computed per step (padding-aware when valid_len is given)."""
     import numpy as np
-    per_head = np.diff(row_ptr).reshape(wl.heads, wl.num_blocks)
+    per_head = np.diff(row_ptr).reshape(wl.heads, wl.seq_len // 64)   # rows of 64-token tiles
     if valid_len is None:
         return int(per_head.sum()) * wl.batch
     total = 0
@@ -192,7 +192,7 @@ def main():
     if wl.band:
         lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
     else:
-        lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+        lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                     wl.random_blocks, wl.layout_seed)
     layout_host_us = (time.perf_counter() - t0) * 1e6
     bs.bsattn_layout_upload(lay)
@@ -365,7 +365,7 @@ def main():
         if wl.band:
             olay = OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
         else:
-            olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+            olay = OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                   wl.random_blocks, wl.layout_seed)
         if backward:
             result["cpu_baseline"] = cpu_baseline_bwd(wl, inp, do_host, olay, args.cpu_seconds)

@@ -188,12 +188,13 @@ void free_device(bsattn_layout* lay) {
     lay->device = -1;
 }
 
-bsattn_status check_layout_dims(int32_t H, int32_t L, int32_t block) {
+bsattn_status check_layout_dims(int32_t H, int32_t L, int32_t block, bool allow_128 = false) {
     if (H < 1) return fail(BSATTN_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", H);
-    if (block != kBlock) return fail(BSATTN_ERR_UNSUPPORTED, "block must be 64 (got %d)", block);
+    if (block != kBlock && !(allow_128 && block == 2 * kBlock))
+        return fail(BSATTN_ERR_UNSUPPORTED, "block must be 64%s (got %d)", allow_128 ? " or 128" : "", block);
     if (L < block || L % block != 0)
         return fail(BSATTN_ERR_INVALID_ARG, "seq_len must be a positive multiple of %d (got %d)", block, L);
-    if ((int64_t)H * (L / block) > (1 << 20))
+    if ((int64_t)H * (L / kBlock) > (1 << 20))
         return fail(BSATTN_ERR_UNSUPPORTED, "num_heads * seq_len/64 exceeds 2^20");
     return BSATTN_OK;
 }
@@ -562,9 +563,9 @@ bsattn_status bsattn_make_layout(int32_t num_heads, int32_t seq_len, int32_t blo
                                  bsattn_layout** out) {
     if (!out) return fail(BSATTN_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
-    bsattn_status st = check_layout_dims(num_heads, seq_len, block);
+    bsattn_status st = check_layout_dims(num_heads, seq_len, block, true);
     if (st != BSATTN_OK) return st;
-    const int32_t nb = seq_len / block;
+    const int32_t nb = seq_len / block;   // blocks of the rule (64 or 128 tokens)
     if (window_blocks < 1 || window_blocks % 2 == 0)
         return fail(BSATTN_ERR_INVALID_ARG, "window_blocks must be odd and >= 1 (got %d)", window_blocks);
     if (window_blocks > kMaxWindowBlocks)
@@ -593,23 +594,35 @@ bsattn_status bsattn_make_layout(int32_t num_heads, int32_t seq_len, int32_t blo
     bsattn_layout* lay = new (std::nothrow) bsattn_layout();
     if (!lay) return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
     try {
+        // The rule runs on blocks of `block` tokens; the kernels walk 64-token
+        // tiles, so a 128-token block (I, J) becomes the 2 x 2 tiles
+        // (2I + a, 2J + b), rows and columns still ascending.
+        const int32_t f = block / kBlock;
+        const int32_t nt = seq_len / kBlock;
         lay->H = num_heads;
         lay->L = seq_len;
-        lay->nb = nb;
+        lay->nb = nt;
         lay->block = block;
         lay->kind = 0;
         lay->rule = rule;
-        const int32_t rows = num_heads * nb;
+        std::vector<int32_t> cnt((size_t)num_heads * nb), buf;
+        for (int32_t h = 0; h < num_heads; ++h)
+            for (int32_t i = 0; i < nb; ++i) cnt[(size_t)h * nb + i] = rule_row_count(rule, h, i);
+        const int32_t rows = num_heads * nt;
         lay->row_ptr.assign((size_t)rows + 1, 0);
         for (int32_t h = 0; h < num_heads; ++h)
-            for (int32_t i = 0; i < nb; ++i)
-                lay->row_ptr[(size_t)h * nb + i + 1] = rule_row_count(rule, h, i);
+            for (int32_t i = 0; i < nt; ++i) lay->row_ptr[(size_t)h * nt + i + 1] = f * cnt[(size_t)h * nb + i / f];
         for (int32_t r = 0; r < rows; ++r) lay->row_ptr[r + 1] += lay->row_ptr[r];
         lay->col_idx.assign((size_t)lay->row_ptr[rows], 0);
         for (int32_t h = 0; h < num_heads; ++h)
             for (int32_t i = 0; i < nb; ++i) {
-                const int32_t r = h * nb + i;
-                rule_row_fill(rule, h, i, lay->col_idx.data() + lay->row_ptr[r]);
+                buf.assign((size_t)cnt[(size_t)h * nb + i], 0);
+                rule_row_fill(rule, h, i, buf.data());
+                for (int32_t a = 0; a < f; ++a) {
+                    int32_t* dst = lay->col_idx.data() + lay->row_ptr[(size_t)h * nt + f * i + a];
+                    for (size_t c = 0; c < buf.size(); ++c)
+                        for (int32_t b = 0; b < f; ++b) *dst++ = f * buf[c] + b;
+                }
             }
     } catch (const std::bad_alloc&) {
         delete lay;
@@ -711,6 +724,7 @@ bsattn_status bsattn_layout_build_device(const bsattn_layout* lay, int32_t* row_
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
     if (!row_ptr_dev || (!col_idx_dev && !lay->col_idx.empty()))
         return fail(BSATTN_ERR_INVALID_ARG, "NULL device array");
+    if (lay->block != kBlock) return fail(BSATTN_ERR_UNSUPPORTED, "the device rule runs 64-token blocks only");
     hipError_t e = launch_layout_build(lay->rule, lay->kind, lay->H, lay->nb, lay->band_tokens,
                                        row_ptr_dev, col_idx_dev, stream);
     if (e != hipSuccess) return hip_fail(e, "layout build launch");

@@ -67,7 +67,11 @@ typedef struct bsattn_layout bsattn_layout;
  * SQA page, section 3.1 (block-sparse storage).
  *   num_heads      H >= 1; the layout is per head and shared by the batch.
  *   seq_len        L, a positive multiple of block.
- *   block          must be 64 (the tile of the kernels).
+ *   block          64 or 128 tokens (the SQA page recommends 64x64 blocks,
+ *                  section 5; 128 halves the layout's granularity).  The
+ *                  rule below runs on blocks of this size; the stored CSR is
+ *                  always over 64-token tiles (a 128-token block (I, J) is
+ *                  the tiles 2I..2I+1 x 2J..2J+1).
  *   window_blocks  odd >= 1: query block i sees key blocks j with
  *                  |i-j| <= (window_blocks-1)/2, clipped to [0, L/block).
  *   global_blocks  host array of num_global distinct block indices in range
@@ -84,7 +88,7 @@ typedef struct bsattn_layout bsattn_layout;
  *   seed           hash seed.
  *   out            receives the new layout (caller frees with bsattn_layout_destroy).
  * Rows are ascending and duplicate-free.  Limits: window_blocks <= 63,
- * num_global <= 64, random_blocks <= 64, H * (L/block) <= 2^20. */
+ * num_global <= 64, random_blocks <= 64, H * (L/64) <= 2^20. */
 bsattn_status bsattn_make_layout(int32_t num_heads, int32_t seq_len, int32_t block,
                                  int32_t window_blocks, const int32_t* global_blocks,
                                  int32_t num_global, int32_t random_blocks, uint64_t seed,
@@ -99,8 +103,9 @@ bsattn_status bsattn_make_band_layout(int32_t num_heads, int32_t seq_len, int32_
                                       int32_t band_tokens, bsattn_layout** out);
 
 /* Borrowed host view of the block-CSR arrays (valid until destroy).
- *   row_ptr [num_rows + 1], col_idx [nnz], num_rows = H * L / block, rows
- *   ordered head-major (row h*nb + i).  Any output pointer may be NULL. */
+ *   row_ptr [num_rows + 1], col_idx [nnz], num_rows = H * L / 64 (rows of
+ *   64-token tiles whatever the layout's block), rows ordered head-major
+ *   (row h*nb + i).  Any output pointer may be NULL. */
 bsattn_status bsattn_layout_csr(const bsattn_layout* layout, const int32_t** row_ptr,
                                 const int32_t** col_idx, int32_t* num_rows, int64_t* nnz);
 
@@ -113,7 +118,8 @@ bsattn_status bsattn_layout_upload(bsattn_layout* layout, hipStream_t stream);
 /* Rebuild the same layout on the device from its parameters (one thread per
  * row runs the identical integer rule) into caller-owned device arrays
  * row_ptr_dev [num_rows + 1] and col_idx_dev [nnz].  Exists to prove that
- * the host and device evaluations of the rule agree bit for bit. */
+ * the host and device evaluations of the rule agree bit for bit.  Layouts
+ * of 64-token blocks only (UNSUPPORTED for 128). */
 bsattn_status bsattn_layout_build_device(const bsattn_layout* layout, int32_t* row_ptr_dev,
                                          int32_t* col_idx_dev, hipStream_t stream);
 

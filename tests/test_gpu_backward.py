@@ -43,10 +43,10 @@ def _device():
 
 
 def _layouts(wl):
-    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                 wl.random_blocks, wl.layout_seed)
     bs.bsattn_layout_upload(lay)
-    olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+    olay = OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                           wl.random_blocks, wl.layout_seed)
     return lay, olay
 
@@ -173,3 +173,8 @@ def test_backward_rows_with_no_key():
     assert (got[0][0, :, 3 * 64:] == 0).all()          # rows of blocks >= 3 see no valid key
     assert (got[1][0, :, 100:] == 0).all() and (got[2][0, :, 100:] == 0).all()
     _compare(got, ref, "bwd empty rows")
+
+
+def test_backward_block128():
+    _case(WORKLOADS["bigbird128-L8192"].with_(batch=1, heads=2, seq_len=2048, global_blocks=(0, 15)),
+          "bwd block128 L2048")

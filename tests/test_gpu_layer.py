@@ -40,7 +40,7 @@ def _case(wl, tag):
     _say(tag, wl)
     p = make_layer_params(wl)
     vl = make_inputs(wl).get("valid_len") if wl.padded else None
-    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                 wl.random_blocks, wl.layout_seed)
     bs.bsattn_layout_upload(lay)
     d = {k: v.cuda() for k, v in p.items()}
@@ -48,7 +48,7 @@ def _case(wl, tag):
                            key_valid_len=None if vl is None else vl.cuda(), scale=wl.scale)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
-    olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+    olay = OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                           wl.random_blocks, wl.layout_seed)
     ref = OLY.layer_forward(p["x"], p["w_qkv"], p["b_qkv"], p["w_proj"], p["b_proj"], olay, wl.heads, wl.scale,
                             valid_len=None if vl is None else vl.tolist())

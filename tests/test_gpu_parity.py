@@ -38,10 +38,10 @@ def _device():
 
 
 def _layouts(wl):
-    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                 wl.random_blocks, wl.layout_seed)
     bs.bsattn_layout_upload(lay)
-    olay = OL.make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+    olay = OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                           wl.random_blocks, wl.layout_seed)
     return lay, olay
 
@@ -86,7 +86,7 @@ def _sample_rows(wl, valid_len=None, n_random=48, seed=0):
         for h in sorted({0, wl.heads - 1, int(g.integers(0, wl.heads))}):
             ts = {0, 63, 64, L - 1, L - 64, 65}
             for gb in wl.global_blocks:
-                ts |= {gb * 64, gb * 64 + 37, gb * 64 + 63}
+                ts |= {gb * wl.block, gb * wl.block + 37, gb * wl.block + wl.block - 1}
             if valid_len is not None:
                 v = int(valid_len[b])
                 ts |= {max(0, v - 1), min(L - 1, v), max(0, v - 65)}
@@ -202,14 +202,14 @@ def test_routed_head_dim_64():
 
 # ---------------- layout on the device, determinism ----------------
 
-@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.block == 64])
 def test_device_layout_equals_host(name):
     wl = WORKLOADS[name]
     _say("device layout", name)
     if wl.routed or wl.band:
         lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
     else:
-        lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, 64, wl.window_blocks, list(wl.global_blocks),
+        lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                     wl.random_blocks, wl.layout_seed)
     rp, ci = bs.bsattn_layout_csr(lay)
     drp = torch.full((rp.size,), -7, dtype=torch.int32, device="cuda")
@@ -383,3 +383,14 @@ def test_band_rejects_padding_and_fp32():
                    device="cuda"))
     with pytest.raises(bs.BsattnError):
         bs.forward(inp["q"].float(), inp["k"].float(), inp["v"].float(), lay)
+
+
+# ---------------- 128-token blocks ----------------
+
+def test_block128_full():
+    _full_check(WORKLOADS["bigbird128-L8192"].with_(batch=2, heads=2, seq_len=2048, global_blocks=(0, 15)),
+                "block128 L2048 full")
+
+
+def test_block128_benchmark_shape_sampled():
+    _sampled_check(WORKLOADS["bigbird128-L8192"], "bigbird128-L8192 full size, sampled rows")

@@ -68,3 +68,31 @@ def test_global_order_does_not_matter():
 def test_large_seed_and_head_values():
     (rp, ci), (orp, oci) = _both(3, 64 * 64, 5, [0, 63], 7, (1 << 64) - 1)
     assert np.array_equal(ci, oci)
+
+
+def _expand(rows_ptr, cols, f):
+    """A block-f*64 CSR expanded to 64-token tiles (each block -> f x f tiles)."""
+    out_ptr, out_col = [0], []
+    for r in range(len(rows_ptr) - 1):
+        row = cols[rows_ptr[r]:rows_ptr[r + 1]]
+        for _ in range(f):
+            out_col.extend(f * int(j) + b for j in row for b in range(f))
+            out_ptr.append(len(out_col))
+    return np.asarray(out_ptr, dtype=np.int32), np.asarray(out_col, dtype=np.int32)
+
+
+def test_block128_layouts_are_the_rule_on_128_blocks_expanded_to_tiles():
+    g = np.random.default_rng(99)
+    for _ in range(60):
+        nb = int(g.integers(1, 24))
+        H = int(g.integers(1, 3))
+        w = int(g.integers(0, 5)) * 2 + 1
+        ng = int(g.integers(0, min(nb, 3) + 1))
+        G = sorted(g.choice(nb, size=ng, replace=False).tolist())
+        r = int(g.integers(0, 6))
+        seed = int(g.integers(0, 2**63))
+        lay = bs.bsattn_make_layout(H, nb * 128, 128, w, G, r, seed)
+        rp, ci = bs.bsattn_layout_csr(lay)
+        orp, oci = OL.make_layout(H, nb * 128, 128, w, G, r, seed).csr()
+        erp, eci = _expand(orp, oci, 2)
+        assert np.array_equal(rp, erp) and np.array_equal(ci, eci), (nb, H, w, G, r, seed)

@@ -19,7 +19,7 @@ from workloads import WORKLOADS
 
 def _wl_layout(name):
     wl = WORKLOADS[name]
-    if wl.routed:
+    if wl.routed or wl.band:
         return OL.make_band_layout(wl.heads, wl.seq_len, wl.block, wl.band_tokens)
     return OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, wl.global_blocks,
                           wl.random_blocks, wl.layout_seed)

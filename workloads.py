@@ -95,6 +95,10 @@ WORKLOADS = {
         data_seed=3, window_blocks=5, global_blocks=(0,), random_blocks=0, layout_seed=3,
         sigma=0.5, padded=True),
     # Routed queries: per head the top-64 rows by q.w attend to every key, the rest to +-32 tokens.
+    # The BigBird layout on 128-token blocks at the throughput shape (64 blocks a side).
+    "bigbird128-L8192": Workload(
+        name="bigbird128-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
+        data_seed=6, block=128, window_blocks=3, global_blocks=(0, 63), random_blocks=3, layout_seed=6),
     # Token-granular sliding window |t - s| <= 256 (the BigBird page's 64-256 token windows)
     # at the throughput shape: a band layout through the plain forward.
     "band256-L8192": Workload(
