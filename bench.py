@@ -199,6 +199,12 @@ def main():
     row_ptr, col = bs.bsattn_layout_csr(lay)
     vl_host = inp.get("valid_len")
     tiles = tile_stats(wl, row_ptr, col, None if vl_host is None else vl_host.tolist())
+    stored_tiles = tiles
+    masks = bs.bsattn_layout_tile_masks(lay)
+    if masks is not None:
+        # 32-token blocks: the work is the layout's 32 x 32 blocks (a quarter of a
+        # stored tile each), not the whole tiles the kernels compute
+        tiles = wl.batch * int(np.unpackbits(masks).sum()) / 4.0
     flops_per_step = tiles * 4.0 * 64 * 64 * wl.head_dim
     elem = 2 if wl.dtype == "bf16" else 4
     alg_bytes = wl.batch * wl.heads * wl.seq_len * (4 * wl.head_dim * elem + 4)
@@ -338,10 +344,10 @@ def main():
         "data": ("synthetic (seeded Gaussian x and layer weights of the workload's shape)" if args.which == "layer"
                  else "synthetic (seeded Gaussian Q/K/V" + (" and dO" if backward else "") + " of the workload's shape)"),
         "config": {
-            "workload": wl.name, "pass": args.which, "batch": B, "heads": H, "seq_len": L, "head_dim": D, "block": 64,
+            "workload": wl.name, "pass": args.which, "batch": B, "heads": H, "seq_len": L, "head_dim": D, "block": wl.block,
             "window_blocks": wl.window_blocks, "global_blocks": list(wl.global_blocks),
             "random_blocks": wl.random_blocks, "layout_seed": wl.layout_seed, "band_tokens": wl.band_tokens,
-            "nonzero_tiles": tiles, "layout_density": round(tiles / (B * H * (L // 64) ** 2), 5),
+            "nonzero_tiles": stored_tiles, "layout_density": round(tiles / (B * H * (L // 64) ** 2), 5),
         },
         "eff_tflops": round(eff_tflops, 2),
         "pct_bf16_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),

@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     bsattn_layout_build_device,
     bsattn_layout_csr,
     bsattn_layout_destroy,
+    bsattn_layout_tile_masks,
     bsattn_layout_upload,
     bsattn_make_band_layout,
     bsattn_make_layout,

@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
     L.bsattn_make_band_layout.argtypes = [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_vp)]
     L.bsattn_layout_csr.argtypes = [_c_vp, ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_i32p),
                                     ctypes.POINTER(_c_int), ctypes.POINTER(ctypes.c_int64)]
+    L.bsattn_layout_tile_masks.argtypes = [_c_vp, ctypes.POINTER(ctypes.POINTER(ctypes.c_uint8)),
+                                           ctypes.POINTER(ctypes.c_int64)]
     L.bsattn_layout_upload.argtypes = [_c_vp, _c_vp]
     L.bsattn_layout_build_device.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp]
     L.bsattn_layout_destroy.argtypes = [_c_vp]
@@ -67,7 +69,8 @@ def lib() -> ctypes.CDLL:
     L.bsattn_status_string.restype = ctypes.c_char_p
     L.bsattn_last_error.argtypes = []
     L.bsattn_last_error.restype = ctypes.c_char_p
-    for name in ("bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr", "bsattn_layout_upload",
+    for name in ("bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr",
+                 "bsattn_layout_tile_masks", "bsattn_layout_upload",
                  "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
                  "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events"):
         getattr(L, name).restype = ctypes.c_int
@@ -152,6 +155,18 @@ def bsattn_layout_csr(layout: Layout) -> Tuple[np.ndarray, np.ndarray]:
     row_ptr = np.ctypeslib.as_array(rp, shape=(nrows.value + 1,)).copy()
     col = np.ctypeslib.as_array(ci, shape=(max(1, nnz.value),))[: nnz.value].copy()
     return row_ptr, col
+
+
+def bsattn_layout_tile_masks(layout: Layout) -> Optional[np.ndarray]:
+    """Copy of the quarter masks (uint8 [nnz], bit 2a + b: query half a sees key
+    half b) of a layout of 32-token blocks; None for other layouts."""
+    p = ctypes.POINTER(ctypes.c_uint8)()
+    n = ctypes.c_int64()
+    _check("bsattn_layout_tile_masks", lib().bsattn_layout_tile_masks(layout.handle, ctypes.byref(p),
+                                                                      ctypes.byref(n)))
+    if not p or n.value == 0:
+        return None
+    return np.ctypeslib.as_array(p, shape=(n.value,)).copy()
 
 
 def bsattn_layout_upload(layout: Layout, stream=None) -> None:

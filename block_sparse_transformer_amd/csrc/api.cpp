@@ -106,12 +106,17 @@ void build_bwd(bsattn_layout* lay) {
         }
     for (size_t c = 0; c + 1 < cptr.size(); ++c) cptr[c + 1] += cptr[c];
     bw.k_idx.assign((size_t)cptr.back(), 0);
+    const bool subs = !lay->tile_sub.empty();
+    if (subs) bw.k_sub.assign((size_t)cptr.back(), 0);
     std::vector<int32_t> fill(cptr.begin(), cptr.end() - 1);
     for (int32_t h = 0; h < H; ++h)
         for (int32_t i = 0; i < nb; ++i) {
             const int32_t r = h * nb + i;
-            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a)
-                bw.k_idx[(size_t)fill[(size_t)h * nb + lay->col_idx[a]]++] = i;
+            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a) {
+                const int32_t pos = fill[(size_t)h * nb + lay->col_idx[a]]++;
+                bw.k_idx[(size_t)pos] = i;
+                if (subs) bw.k_sub[(size_t)pos] = lay->tile_sub[(size_t)a];   // same bits: query half, key half
+            }
         }
     // per head, longest first, padded with empty items (head_blk -1) to a common length
     auto make = [&](const std::vector<int32_t>& ptr, std::vector<BwdItem>& items, std::vector<BwdSum>& sums,
@@ -157,9 +162,11 @@ void free_bwd_device(bsattn_layout* lay) {
     (void)hipFree(bw.d_q_sums);
     (void)hipFree(bw.d_k_sums);
     (void)hipFree(bw.d_k_idx);
+    (void)hipFree(bw.d_k_sub);
     bw.d_q_items = bw.d_k_items = nullptr;
     bw.d_q_sums = bw.d_k_sums = nullptr;
     bw.d_k_idx = nullptr;
+    bw.d_k_sub = nullptr;
     bw.uploaded = false;
 }
 
@@ -170,6 +177,7 @@ void free_device(bsattn_layout* lay) {
         if (cur != lay->device) (void)hipSetDevice(lay->device);
         (void)hipFree(lay->d_row_ptr);
         (void)hipFree(lay->d_col_idx);
+        (void)hipFree(lay->d_col_sub);
         (void)hipFree(lay->d_items);
         (void)hipFree(lay->d_merges);
         for (auto& sc : lay->scheds) {
@@ -183,19 +191,20 @@ void free_device(bsattn_layout* lay) {
     }
     lay->scheds.clear();
     lay->d_row_ptr = lay->d_col_idx = nullptr;
+    lay->d_col_sub = nullptr;
     lay->d_items = nullptr;
     lay->d_merges = nullptr;
     lay->device = -1;
 }
 
-bsattn_status check_layout_dims(int32_t H, int32_t L, int32_t block, bool allow_128 = false) {
+bsattn_status check_layout_dims(int32_t H, int32_t L, int32_t block, bool any_block = false) {
     if (H < 1) return fail(BSATTN_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", H);
-    if (block != kBlock && !(allow_128 && block == 2 * kBlock))
-        return fail(BSATTN_ERR_UNSUPPORTED, "block must be 64%s (got %d)", allow_128 ? " or 128" : "", block);
-    if (L < block || L % block != 0)
-        return fail(BSATTN_ERR_INVALID_ARG, "seq_len must be a positive multiple of %d (got %d)", block, L);
-    if ((int64_t)H * (L / kBlock) > (1 << 20))
-        return fail(BSATTN_ERR_UNSUPPORTED, "num_heads * seq_len/64 exceeds 2^20");
+    if (block != kBlock && !(any_block && (block == kBlock / 2 || block == 2 * kBlock)))
+        return fail(BSATTN_ERR_UNSUPPORTED, "block must be 64%s (got %d)", any_block ? ", 32 or 128" : "", block);
+    if (L < kBlock || L % kBlock != 0 || L % block != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "seq_len must be a positive multiple of 64 and of block (got %d)", L);
+    if ((int64_t)H * (L / kBlock) > (1 << 20) || L / kBlock > kTileJ + 1)
+        return fail(BSATTN_ERR_UNSUPPORTED, "num_heads * seq_len/64 exceeds 2^20 or seq_len/64 exceeds 2^18");
     return BSATTN_OK;
 }
 
@@ -213,20 +222,21 @@ bsattn_status finish_layout(bsattn_layout* lay) {
 bsattn_status upload_bwd(const bsattn_layout* lay, hipStream_t stream) {
     auto& bw = lay->bwd;
     if (bw.uploaded) return BSATTN_OK;
-    void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
-    const void* src[5] = {bw.q_items.data(), bw.k_items.data(), bw.q_sums.data(), bw.k_sums.data(),
-                          bw.k_idx.data()};
-    const size_t sz[5] = {bw.q_items.size() * sizeof(BwdItem), bw.k_items.size() * sizeof(BwdItem),
+    void* p[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    const void* src[6] = {bw.q_items.data(), bw.k_items.data(), bw.q_sums.data(), bw.k_sums.data(),
+                          bw.k_idx.data(), bw.k_sub.data()};
+    const size_t sz[6] = {bw.q_items.size() * sizeof(BwdItem), bw.k_items.size() * sizeof(BwdItem),
                           bw.q_sums.size() * sizeof(BwdSum), bw.k_sums.size() * sizeof(BwdSum),
-                          bw.k_idx.size() * sizeof(int32_t)};
+                          bw.k_idx.size() * sizeof(int32_t), bw.k_sub.size()};
     hipError_t e = hipSuccess;
-    for (int a = 0; a < 5 && e == hipSuccess; ++a) {
+    for (int a = 0; a < 6 && e == hipSuccess; ++a) {
+        if (a == 5 && sz[a] == 0) break;   // no sub-block masks
         e = hipMalloc(&p[a], std::max<size_t>(sz[a], 16));
         if (e == hipSuccess && sz[a] > 0) e = hipMemcpyAsync(p[a], src[a], sz[a], hipMemcpyHostToDevice, stream);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) {
-        for (int a = 0; a < 5; ++a) (void)hipFree(p[a]);
+        for (int a = 0; a < 6; ++a) (void)hipFree(p[a]);
         return fail(BSATTN_ERR_NO_MEMORY, "backward list upload: %s", hipGetErrorString(e));
     }
     bw.d_q_items = (BwdItem*)p[0];
@@ -234,6 +244,7 @@ bsattn_status upload_bwd(const bsattn_layout* lay, hipStream_t stream) {
     bw.d_q_sums = (BwdSum*)p[2];
     bw.d_k_sums = (BwdSum*)p[3];
     bw.d_k_idx = (int32_t*)p[4];
+    bw.d_k_sub = (uint8_t*)p[5];
     bw.uploaded = true;
     return BSATTN_OK;
 }
@@ -451,7 +462,8 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
                     }
                     for (int32_t t = 0; t < un.tiles; ++t) {
                         const int32_t j = routed ? first + t : lay->col_idx[(size_t)first + t];
-                        tiles.push_back(j | (k << kTileUnitShift) | (t == 0 ? kTileFirst : 0) |
+                        const int32_t sub = (routed || lay->tile_sub.empty()) ? 15 : lay->tile_sub[(size_t)first + t];
+                        tiles.push_back(j | (sub << kTileSubShift) | (k << kTileUnitShift) | (t == 0 ? kTileFirst : 0) |
                                         (t == un.tiles - 1 ? kTileLast : 0));
                     }
                     ++k;
@@ -565,7 +577,7 @@ bsattn_status bsattn_make_layout(int32_t num_heads, int32_t seq_len, int32_t blo
     *out = nullptr;
     bsattn_status st = check_layout_dims(num_heads, seq_len, block, true);
     if (st != BSATTN_OK) return st;
-    const int32_t nb = seq_len / block;   // blocks of the rule (64 or 128 tokens)
+    const int32_t nb = seq_len / block;   // blocks of the rule (32, 64 or 128 tokens)
     if (window_blocks < 1 || window_blocks % 2 == 0)
         return fail(BSATTN_ERR_INVALID_ARG, "window_blocks must be odd and >= 1 (got %d)", window_blocks);
     if (window_blocks > kMaxWindowBlocks)
@@ -596,9 +608,41 @@ bsattn_status bsattn_make_layout(int32_t num_heads, int32_t seq_len, int32_t blo
     try {
         // The rule runs on blocks of `block` tokens; the kernels walk 64-token
         // tiles, so a 128-token block (I, J) becomes the 2 x 2 tiles
-        // (2I + a, 2J + b), rows and columns still ascending.
-        const int32_t f = block / kBlock;
+        // (2I + a, 2J + b), rows and columns still ascending; a 32-token block
+        // (I, J) is sub-block (I % 2, J % 2) of tile (I / 2, J / 2).
         const int32_t nt = seq_len / kBlock;
+        if (block < kBlock) {
+            lay->H = num_heads;
+            lay->L = seq_len;
+            lay->nb = nt;
+            lay->block = block;
+            lay->kind = 0;
+            lay->rule = rule;
+            lay->row_ptr.assign((size_t)num_heads * nt + 1, 0);
+            std::vector<int32_t> r0, r1;
+            std::vector<uint8_t> sub((size_t)nt);
+            for (int32_t h = 0; h < num_heads; ++h)
+                for (int32_t i = 0; i < nt; ++i) {
+                    r0.assign((size_t)rule_row_count(rule, h, 2 * i), 0);
+                    rule_row_fill(rule, h, 2 * i, r0.data());
+                    r1.assign((size_t)rule_row_count(rule, h, 2 * i + 1), 0);
+                    rule_row_fill(rule, h, 2 * i + 1, r1.data());
+                    std::fill(sub.begin(), sub.end(), 0);
+                    for (int32_t J : r0) sub[(size_t)(J / 2)] |= (uint8_t)(1u << (J % 2));
+                    for (int32_t J : r1) sub[(size_t)(J / 2)] |= (uint8_t)(1u << (2 + J % 2));
+                    int32_t n = 0;
+                    for (int32_t j = 0; j < nt; ++j)
+                        if (sub[(size_t)j]) {
+                            lay->col_idx.push_back(j);
+                            lay->tile_sub.push_back(sub[(size_t)j]);
+                            ++n;
+                        }
+                    lay->row_ptr[(size_t)h * nt + i + 1] = lay->row_ptr[(size_t)h * nt + i] + n;
+                }
+            *out = lay;
+            return finish_layout(lay);
+        }
+        const int32_t f = block / kBlock;
         lay->H = num_heads;
         lay->L = seq_len;
         lay->nb = nt;
@@ -676,6 +720,13 @@ bsattn_status bsattn_layout_csr(const bsattn_layout* lay, const int32_t** row_pt
     return ok();
 }
 
+bsattn_status bsattn_layout_tile_masks(const bsattn_layout* lay, const uint8_t** masks, int64_t* n) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (masks) *masks = lay->tile_sub.empty() ? nullptr : lay->tile_sub.data();
+    if (n) *n = (int64_t)lay->tile_sub.size();
+    return ok();
+}
+
 bsattn_status bsattn_layout_upload(bsattn_layout* lay, hipStream_t stream) {
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
     free_device(lay);
@@ -709,6 +760,16 @@ bsattn_status bsattn_layout_upload(bsattn_layout* lay, hipStream_t stream) {
         if (e != hipSuccess) {
             free_device(lay);
             return hip_fail(e, "hipMemcpyAsync (layout upload)");
+        }
+    }
+    if (!lay->tile_sub.empty()) {
+        e = hipMalloc(&lay->d_col_sub, lay->tile_sub.size());
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(lay->d_col_sub, lay->tile_sub.data(), lay->tile_sub.size(), hipMemcpyHostToDevice,
+                               stream);
+        if (e != hipSuccess) {
+            free_device(lay);
+            return fail(BSATTN_ERR_NO_MEMORY, "sub-block mask upload: %s", hipGetErrorString(e));
         }
     }
     e = hipStreamSynchronize(stream);
@@ -773,6 +834,9 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     const bool band = lay->kind == 1;   // token band |t - s| <= band_tokens (a token-granular window)
     if (band && dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "band layouts are bf16 only");
     if (band && key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "band layouts take no key padding");
+    const bool sub = !lay->tile_sub.empty();   // 32-token blocks
+    if (sub && dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "32-token layouts are bf16 only");
+    if (sub && key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "32-token layouts take no key padding");
     size_t need = 0;
     st = bsattn_workspace_size(lay, B, D, 0, &need);
     if (st != BSATTN_OK) return st;
@@ -801,7 +865,7 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     a.band = band ? lay->band_tokens : -1;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const int mask = band ? MASK_BAND : (key_valid_len ? MASK_PAD : MASK_NONE);
+    const int mask = band ? MASK_BAND : (sub ? MASK_SUB : (key_valid_len ? MASK_PAD : MASK_NONE));
 
     hipError_t e;
     if (dtype == BSATTN_F32) {
@@ -921,6 +985,8 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
             if (o == in) return fail(BSATTN_ERR_INVALID_ARG, "a gradient output aliases an input");
     }
     if (dq == dk || dq == dv || dk == dv) return fail(BSATTN_ERR_INVALID_ARG, "gradient outputs alias");
+    const bool sub = !lay->tile_sub.empty();
+    if (sub && key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "32-token layouts take no key padding");
     // the forward's checks: shapes against the layout, q, k, v, out, lse, scale, the device
     bsattn_status st = check_forward_common(lay, B, H, L, D, q, k, v, const_cast<void*>(out),
                                             const_cast<float*>(lse), scale);
@@ -952,21 +1018,21 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
     a.B = B; a.H = H; a.L = L; a.nb = lay->nb;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const int mask = key_valid_len ? MASK_PAD : MASK_NONE;
+    const int mask = sub ? MASK_SUB : (key_valid_len ? MASK_PAD : MASK_NONE);
 
     hipError_t e = launch_bwd_delta(a, D, stream);
     if (e != hipSuccess) return hip_fail(e, "backward delta launch");
 
     a.items = bw.d_q_items; a.n_items = (int32_t)bw.q_items.size(); a.items_per_head = bw.q_per_head;
     a.sums = bw.d_q_sums; a.n_sums = (int32_t)bw.q_sums.size();
-    a.idx = lay->d_col_idx; a.n_slots = bw.n_qslots;
+    a.idx = lay->d_col_idx; a.idx_sub = lay->d_col_sub; a.n_slots = bw.n_qslots;
     e = launch_bwd_dq(a, D, mask, stream);
     if (e != hipSuccess) return hip_fail(e, "backward dQ launch");
     if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 0, stream)) != hipSuccess) return hip_fail(e, "backward dQ sum launch");
 
     a.items = bw.d_k_items; a.n_items = (int32_t)bw.k_items.size(); a.items_per_head = bw.k_per_head;
     a.sums = bw.d_k_sums; a.n_sums = (int32_t)bw.k_sums.size();
-    a.idx = bw.d_k_idx; a.n_slots = bw.n_kslots;
+    a.idx = bw.d_k_idx; a.idx_sub = bw.d_k_sub; a.n_slots = bw.n_kslots;
     if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     e = launch_bwd_dkdv(a, D, mask, stream);
     if (e != hipSuccess) return hip_fail(e, "backward dK/dV launch");

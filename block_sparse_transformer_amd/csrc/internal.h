@@ -17,7 +17,9 @@ constexpr int kBlock = 64;        // tokens per block and rows per query tile
 constexpr int kChunkTiles = 16;   // a row longer than this is split across workgroups
 constexpr int kMaxChunks = 32;    // upper bound on the split of one row
 
-enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2 };
+// MASK_SUB: layouts of 32-token blocks; each 64-token tile carries which of
+// its 2 x 2 sub-blocks are allowed (bit 2a + b: query half a, key half b).
+enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2, MASK_SUB = 3 };
 
 // One workgroup's share: query block `row` (= h*nb + i) over key blocks
 // col_idx[col_begin, col_end).  slot < 0: the whole row, written straight to
@@ -36,16 +38,18 @@ struct MergeItem {
     int32_t row, first_slot, n_chunks, pad;
 };
 
-constexpr int kXcds = 8;
+constexpr int kXcds = 8;             // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 constexpr int kMaxBinUnits = 64;     // units of one workgroup (one per lane)
 constexpr int kMaxBinTiles = 512;    // tiles of one workgroup (its list lives in LDS)
 // D = 64 kernel: one workgroup of kQWaves waves per CU, one unit/tile list per wave
 constexpr int kQWaves = 8;
-// Flat tile entry of a workgroup's list: key block | unit << 20 | first | last.
-constexpr int kTileJ = (1 << 20) - 1;
-constexpr int kTileUnitShift = 20;
+// Flat tile entry of a workgroup's list: key block (18 bits) | sub-block
+// mask << 18 (4 bits) | unit << 22 | first | last.
+constexpr int kTileJ = (1 << 18) - 1;
+constexpr int kTileSubShift = 18;
+constexpr int kTileUnitShift = 22;
 constexpr int kTileFirst = 1 << 29;
-constexpr int kTileLast = 1 << 30;   // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+constexpr int kTileLast = 1 << 30;
 
 // Chunking of a row of `len` tiles: number of chunks and tiles per chunk
 // (at most 64 tiles per chunk: a chunk's key-block list fits one wave's lanes).
@@ -80,8 +84,10 @@ struct FwdArgs {
     // slot within a batch entry, -1 for a whole row), kind < 0 routed tile
     // -1-kind (slot: chunk); group = b * H + h; first tile: offset of the
     // unit's tiles in the bin's list -- over the flat tile list
-    // tiles[tile_ptr[x*n_bins+bin] ..), entries key block | unit << 20 |
-    // kTileFirst | kTileLast (unit: index within the bin).
+    // tiles[tile_ptr[x*n_bins+bin] ..), entries key block | sub-block mask
+    // << 18 | unit << 22 | kTileFirst | kTileLast (unit: index within the
+    // bin; mask bit 2a + b: query half a may see key half b, 0xF unless the
+    // layout has 32-token blocks).
     int32_t n_bins;
     const int4* units;
     const int32_t* unit_ptr;
@@ -130,6 +136,7 @@ struct BwdArgs {
     float* ws_dv;             // [B*n_kslots][64][D]
     const BwdItem* items;     // this launch's items (dQ or dK/dV), [H][items_per_head]
     const int32_t* idx;       // this launch's block lists
+    const uint8_t* idx_sub;   // sub-block masks parallel to idx (32-token layouts), or null
     const BwdSum* sums;
     int32_t n_items, n_sums;
     int32_t items_per_head;   // per-head item lists padded to this length (head_blk < 0: none)
@@ -169,6 +176,9 @@ struct bsattn_layout {
     int32_t band_tokens = -1;
     bsattn::RowRule rule{};
     std::vector<int32_t> row_ptr, col_idx;
+    // 32-token layouts: for each tile of col_idx, its allowed 2 x 2 sub-blocks
+    // (bit 2a + b: query half a, key half b); empty for 64/128-token layouts
+    std::vector<uint8_t> tile_sub;
     std::vector<bsattn::WorkItem> items;
     std::vector<bsattn::MergeItem> merges;
     int32_t n_slots = 0;        // partial slots per batch entry
@@ -177,6 +187,7 @@ struct bsattn_layout {
     int32_t items_per_head = 0;
     int32_t* d_row_ptr = nullptr;
     int32_t* d_col_idx = nullptr;
+    uint8_t* d_col_sub = nullptr;   // device tile_sub (32-token layouts)
     bsattn::WorkItem* d_items = nullptr;
     bsattn::MergeItem* d_merges = nullptr;
     // persistent schedules built on first use, keyed by (batch, head width,
@@ -197,11 +208,13 @@ struct bsattn_layout {
         std::vector<bsattn::BwdItem> q_items, k_items;   // [H][per_head], longest first
         std::vector<bsattn::BwdSum> q_sums, k_sums;
         std::vector<int32_t> k_idx;                      // query blocks per key block (CSC)
+        std::vector<uint8_t> k_sub;                      // their sub-block masks (32-token layouts)
         bsattn::BwdItem* d_q_items = nullptr;
         bsattn::BwdItem* d_k_items = nullptr;
         bsattn::BwdSum* d_q_sums = nullptr;
         bsattn::BwdSum* d_k_sums = nullptr;
         int32_t* d_k_idx = nullptr;
+        uint8_t* d_k_sub = nullptr;
         bool built = false, uploaded = false;
     };
     mutable Bwd bwd;

@@ -238,6 +238,8 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
     }
     for (int e = item.begin; e < item.end; ++e) {
         const int j = a.idx[e];
+        // 32-token blocks: key halves this wave's query half may see
+        const int sub = MASK == MASK_SUB ? (int)a.idx_sub[e] >> (2 * wave) : 3;
         __syncthreads();   // the previous tile's reads are done
         commit_tile<D>(kt, kr, tid);
         commit_tile<D>(vt, vr, tid);
@@ -266,6 +268,7 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
             for (int i = 0; i < 16; ++i) {
                 float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, nl2));
                 if (MASK == MASK_PAD && j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) p = 0.f;
+                if (MASK == MASK_SUB && !((sub >> kb) & 1)) p = 0.f;
                 s[kb][i] = p * (dp[kb][i] - dl);
             }
         // dQ^T += K^T dS^T
@@ -332,6 +335,8 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
     };
     if (item.begin < item.end) fetch(a.idx[item.begin]);
     for (int e = item.begin; e < item.end; ++e) {
+        // 32-token blocks: query halves that may see this wave's key half
+        const int sub = MASK == MASK_SUB ? (int)a.idx_sub[e] >> wave : 15;
         __syncthreads();
         commit_tile<D>(qt, qr, tid);
         commit_tile<D>(ot, orr, tid);
@@ -366,6 +371,7 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
             for (int i = 0; i < 16; ++i) {
                 float p = __builtin_amdgcn_exp2f(s[qb][i] * c2);
                 if (!key_ok) p = 0.f;
+                if (MASK == MASK_SUB && !((sub >> (2 * qb)) & 1)) p = 0.f;
                 s[qb][i] = p;
                 dp[qb][i] *= p;
             }
@@ -461,13 +467,23 @@ hipError_t launch_bwd_delta(const BwdArgs& a, int head_dim, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s) {
-    if (head_dim == 64) return mask == MASK_PAD ? launch_dq_t<64, MASK_PAD>(a, s) : launch_dq_t<64, MASK_NONE>(a, s);
-    return mask == MASK_PAD ? launch_dq_t<128, MASK_PAD>(a, s) : launch_dq_t<128, MASK_NONE>(a, s);
+    if (head_dim == 64)
+        return mask == MASK_PAD   ? launch_dq_t<64, MASK_PAD>(a, s)
+             : mask == MASK_SUB   ? launch_dq_t<64, MASK_SUB>(a, s)
+                                  : launch_dq_t<64, MASK_NONE>(a, s);
+    return mask == MASK_PAD   ? launch_dq_t<128, MASK_PAD>(a, s)
+         : mask == MASK_SUB   ? launch_dq_t<128, MASK_SUB>(a, s)
+                              : launch_dq_t<128, MASK_NONE>(a, s);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s) {
-    if (head_dim == 64) return mask == MASK_PAD ? launch_dkdv_t<64, MASK_PAD>(a, s) : launch_dkdv_t<64, MASK_NONE>(a, s);
-    return mask == MASK_PAD ? launch_dkdv_t<128, MASK_PAD>(a, s) : launch_dkdv_t<128, MASK_NONE>(a, s);
+    if (head_dim == 64)
+        return mask == MASK_PAD   ? launch_dkdv_t<64, MASK_PAD>(a, s)
+             : mask == MASK_SUB   ? launch_dkdv_t<64, MASK_SUB>(a, s)
+                                  : launch_dkdv_t<64, MASK_NONE>(a, s);
+    return mask == MASK_PAD   ? launch_dkdv_t<128, MASK_PAD>(a, s)
+         : mask == MASK_SUB   ? launch_dkdv_t<128, MASK_SUB>(a, s)
+                              : launch_dkdv_t<128, MASK_NONE>(a, s);
 }
 
 hipError_t launch_bwd_sum(const BwdArgs& a, int head_dim, int which, hipStream_t s) {

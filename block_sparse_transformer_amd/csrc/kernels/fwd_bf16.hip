@@ -178,6 +178,8 @@ __device__ __forceinline__ void issue_half(const uint16_t* base, int j, const ui
 
 __device__ __forceinline__ int tile_j(int e) { return e & kTileJ; }
 __device__ __forceinline__ int tile_unit(int e) { return (e >> kTileUnitShift) & (kMaxBinUnits - 1); }
+// allowed 32 x 32 sub-blocks of a tile: bit 2a + b, query half a, key half b
+__device__ __forceinline__ int tile_sub(int e) { return (e >> kTileSubShift) & 15; }
 
 template <int D, int MASK>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
@@ -412,7 +414,17 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     // tiles keep the running max m as it is: the max is raised only when a
     // tile's probabilities grow too large (see softmax_pv), which on typical
     // rows happens rarely -- so no per-tile max is computed.
-    auto softmax_prep = [&](int j, int kind, int tq, int valid, f32x16_t (&s)[2], bool first) {
+    auto softmax_prep = [&](int e, int kind, int tq, int valid, f32x16_t (&s)[2], bool first) {
+        const int j = tile_j(e);
+        if (MASK == MASK_SUB) {
+            // 32-token blocks: this wave holds query half `wave` of the tile
+            const int sub = tile_sub(e);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (!((sub >> (2 * wave + kb)) & 1))
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s[kb][i] = -INFINITY;
+        }
         if (MASK == MASK_PAD) {
             if (j * 64 + 64 > valid) {
 #pragma unroll
@@ -536,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     // and it covers the latency of the previous step's output stores.
     auto step = [&](auto parity, int f, f32x16_t (&s_now)[2], f32x16_t (&s_next)[2]) {
         constexpr int P = decltype(parity)::value;
-        softmax_prep(tile_j(e0), kind_cur, tq_cur, valid_cur, s_now, (e0 & kTileFirst) != 0);
+        softmax_prep(e0, kind_cur, tq_cur, valid_cur, s_now, (e0 & kTileFirst) != 0);
         wait_vmcnt<0>();
         stage_barrier();
         // Q of the next unit: loaded during the first step of the current unit
@@ -904,9 +916,19 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         return pair_max(__builtin_fmaxf(v, s[1][qb][15])) * c2;
     };
     // masks; on a unit's first tile, the running max is the tile's max
-    auto softmax_prep = [&](int j, int kind, const int (&tq)[2], int valid, f32x16_t (&s)[2][2], bool first) {
+    auto softmax_prep = [&](int e, int kind, const int (&tq)[2], int valid, f32x16_t (&s)[2][2], bool first) {
+        const int j = tile_j(e);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+            if (MASK == MASK_SUB) {
+                // 32-token blocks: drop the key halves query half qb may not see
+                const int sub = tile_sub(e);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    if (!((sub >> (2 * qb + kb)) & 1))
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) s[kb][qb][i] = -INFINITY;
+            }
             if (MASK == MASK_PAD) {
                 if (j * 64 + 64 > valid) {
 #pragma unroll
@@ -1051,7 +1073,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             finish();
             pend = false;
         }
-        softmax_prep(tile_j(e0), kind_cur, tq_cur, valid_cur, sc, (e0 & kTileFirst) != 0);
+        softmax_prep(e0, kind_cur, tq_cur, valid_cur, sc, (e0 & kTileFirst) != 0);
         u32x4_t p0[2], p1[2], p2[2], p3[2];
         softmax_exp(sc, 0, C0(), p0);
         if (more) lds_load16x4_1k(kdo, kn + 32 * 64, kl + 4096 + 2048);
@@ -1214,10 +1236,12 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
     if (head_dim == 64) {
         e = mask == MASK_PAD ? launch_d64<MASK_PAD>(a, s)
           : mask == MASK_BAND ? launch_d64<MASK_BAND>(a, s)
+          : mask == MASK_SUB  ? launch_d64<MASK_SUB>(a, s)
                               : launch_d64<MASK_NONE>(a, s);
     } else {
         e = mask == MASK_PAD ? launch_fwd_t<128, MASK_PAD>(a, s)
           : mask == MASK_BAND ? launch_fwd_t<128, MASK_BAND>(a, s)
+          : mask == MASK_SUB  ? launch_fwd_t<128, MASK_SUB>(a, s)
                               : launch_fwd_t<128, MASK_NONE>(a, s);
     }
     if (e != hipSuccess) return e;

@@ -66,12 +66,16 @@ typedef struct bsattn_layout bsattn_layout;
  * BigBird page, section 核心实现 (global / sliding window / random patterns);
  * SQA page, section 3.1 (block-sparse storage).
  *   num_heads      H >= 1; the layout is per head and shared by the batch.
- *   seq_len        L, a positive multiple of block.
- *   block          64 or 128 tokens (the SQA page recommends 64x64 blocks,
- *                  section 5; 128 halves the layout's granularity).  The
+ *   seq_len        L, a positive multiple of 64 and of block.
+ *   block          32, 64 or 128 tokens (the SQA page recommends 64x64
+ *                  blocks, section 5, and treats the size as a tuning knob;
+ *                  128 halves the layout's granularity, 32 doubles it).  The
  *                  rule below runs on blocks of this size; the stored CSR is
- *                  always over 64-token tiles (a 128-token block (I, J) is
- *                  the tiles 2I..2I+1 x 2J..2J+1).
+ *                  always over 64-token tiles.  A 128-token block (I, J) is
+ *                  the tiles 2I..2I+1 x 2J..2J+1.  A 32-token block (I, J)
+ *                  is the quarter (I mod 2, J mod 2) of tile (I/2, J/2): a
+ *                  tile is stored when any of its quarters is in the layout,
+ *                  and bsattn_layout_tile_masks says which quarters are.
  *   window_blocks  odd >= 1: query block i sees key blocks j with
  *                  |i-j| <= (window_blocks-1)/2, clipped to [0, L/block).
  *   global_blocks  host array of num_global distinct block indices in range
@@ -88,7 +92,9 @@ typedef struct bsattn_layout bsattn_layout;
  *   seed           hash seed.
  *   out            receives the new layout (caller frees with bsattn_layout_destroy).
  * Rows are ascending and duplicate-free.  Limits: window_blocks <= 63,
- * num_global <= 64, random_blocks <= 64, H * (L/64) <= 2^20. */
+ * num_global <= 64, random_blocks <= 64, H * (L/64) <= 2^20, L/64 <= 2^18.
+ * Layouts of 32-token blocks run in bf16 without key padding (the forward
+ * and backward calls return UNSUPPORTED otherwise). */
 bsattn_status bsattn_make_layout(int32_t num_heads, int32_t seq_len, int32_t block,
                                  int32_t window_blocks, const int32_t* global_blocks,
                                  int32_t num_global, int32_t random_blocks, uint64_t seed,
@@ -109,6 +115,14 @@ bsattn_status bsattn_make_band_layout(int32_t num_heads, int32_t seq_len, int32_
 bsattn_status bsattn_layout_csr(const bsattn_layout* layout, const int32_t** row_ptr,
                                 const int32_t** col_idx, int32_t* num_rows, int64_t* nnz);
 
+/* Borrowed host view of the quarter masks of a layout of 32-token blocks
+ * (valid until destroy): masks[nnz], parallel to col_idx; bit 2a + b set
+ * when query half a of the tile's row block (tokens 32a .. 32a + 31 of it)
+ * attends key half b of its column block.  For 64- and 128-token layouts
+ * *masks is NULL and *n is 0 (every quarter of a stored tile is in).  Either
+ * output pointer may be NULL. */
+bsattn_status bsattn_layout_tile_masks(const bsattn_layout* layout, const uint8_t** masks, int64_t* n);
+
 /* Copy the CSR and the work schedule to the current HIP device (hipMalloc +
  * copies enqueued on `stream`, then synchronised).  Must precede the forward
  * calls that use the layout; calling it again re-uploads to the then-current
@@ -119,7 +133,7 @@ bsattn_status bsattn_layout_upload(bsattn_layout* layout, hipStream_t stream);
  * row runs the identical integer rule) into caller-owned device arrays
  * row_ptr_dev [num_rows + 1] and col_idx_dev [nnz].  Exists to prove that
  * the host and device evaluations of the rule agree bit for bit.  Layouts
- * of 64-token blocks only (UNSUPPORTED for 128). */
+ * of 64-token blocks only (UNSUPPORTED for 32 and 128). */
 bsattn_status bsattn_layout_build_device(const bsattn_layout* layout, int32_t* row_ptr_dev,
                                          int32_t* col_idx_dev, hipStream_t stream);
 

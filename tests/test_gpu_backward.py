@@ -178,3 +178,9 @@ def test_backward_rows_with_no_key():
 def test_backward_block128():
     _case(WORKLOADS["bigbird128-L8192"].with_(batch=1, heads=2, seq_len=2048, global_blocks=(0, 15)),
           "bwd block128 L2048")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_block32(D):
+    _case(WORKLOADS["bigbird32-L8192"].with_(batch=1, heads=2, seq_len=2048, head_dim=D, global_blocks=(0, 63)),
+          f"bwd block32 L2048 D={D}")

@@ -86,7 +86,7 @@ def _sample_rows(wl, valid_len=None, n_random=48, seed=0):
         for h in sorted({0, wl.heads - 1, int(g.integers(0, wl.heads))}):
             ts = {0, 63, 64, L - 1, L - 64, 65}
             for gb in wl.global_blocks:
-                ts |= {gb * wl.block, gb * wl.block + 37, gb * wl.block + wl.block - 1}
+                ts |= {gb * wl.block, gb * wl.block + 37 % wl.block, gb * wl.block + wl.block - 1}
             if valid_len is not None:
                 v = int(valid_len[b])
                 ts |= {max(0, v - 1), min(L - 1, v), max(0, v - 65)}
@@ -394,3 +394,36 @@ def test_block128_full():
 
 def test_block128_benchmark_shape_sampled():
     _sampled_check(WORKLOADS["bigbird128-L8192"], "bigbird128-L8192 full size, sampled rows")
+
+
+# ---------------- 32-token blocks (tiles with quarter masks) ----------------
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_block32_full(D):
+    _full_check(WORKLOADS["bigbird32-L8192"].with_(batch=2, heads=2, seq_len=2048, head_dim=D,
+                                                   global_blocks=(0, 63)), f"block32 L2048 D={D} full")
+
+
+def test_block32_ragged_rule():
+    # one 64-token tile a side, window wider than the sequence, and rows whose
+    # random blocks leave one query half of a tile with no key half in it
+    _full_check(WORKLOADS["bigbird32-L8192"].with_(batch=1, heads=3, seq_len=64, global_blocks=()),
+                "block32 L64")
+    _full_check(WORKLOADS["bigbird32-L8192"].with_(batch=1, heads=3, seq_len=40 * 64, window_blocks=1,
+                                                   global_blocks=(5,), random_blocks=1, layout_seed=11),
+                "block32 window 1")
+
+
+def test_block32_benchmark_shape_sampled():
+    _sampled_check(WORKLOADS["bigbird32-L8192"], "bigbird32-L8192 full size, sampled rows")
+
+
+def test_block32_rejects_padding_and_fp32():
+    wl = WORKLOADS["bigbird32-L8192"].with_(batch=1, heads=1, seq_len=512, global_blocks=(0,))
+    lay, _ = _layouts(wl)
+    inp = {k: v.cuda() for k, v in make_inputs(wl).items()}
+    vl = torch.tensor([100], dtype=torch.int32, device="cuda")
+    with pytest.raises(bs.BsattnError):
+        bs.forward(inp["q"], inp["k"], inp["v"], lay, key_valid_len=vl, scale=wl.scale)
+    with pytest.raises(bs.BsattnError):
+        bs.forward(inp["q"].float(), inp["k"].float(), inp["v"].float(), lay, scale=wl.scale)

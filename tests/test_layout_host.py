@@ -16,7 +16,7 @@ def _both(H, L, w, G, r, seed):
     return got, want
 
 
-@pytest.mark.parametrize("name", [n for n, wl in WORKLOADS.items() if not (wl.routed or wl.band)])
+@pytest.mark.parametrize("name", [n for n, wl in WORKLOADS.items() if not (wl.routed or wl.band) and wl.block == 64])
 def test_workload_layouts_bit_exact(name):
     wl = WORKLOADS[name]
     (rp, ci), (orp, oci) = _both(wl.heads, wl.seq_len, wl.window_blocks, wl.global_blocks,
@@ -96,3 +96,50 @@ def test_block128_layouts_are_the_rule_on_128_blocks_expanded_to_tiles():
         orp, oci = OL.make_layout(H, nb * 128, 128, w, G, r, seed).csr()
         erp, eci = _expand(orp, oci, 2)
         assert np.array_equal(rp, erp) and np.array_equal(ci, eci), (nb, H, w, G, r, seed)
+
+
+def _quarters(rp, ci, masks, H, nt):
+    """[H, 2nt, 2nt] bool: the 32-token block mask the tiles and quarter masks describe."""
+    m = np.zeros((H, 2 * nt, 2 * nt), dtype=bool)
+    for r in range(H * nt):
+        h, i = divmod(r, nt)
+        for e in range(rp[r], rp[r + 1]):
+            j, q = int(ci[e]), int(masks[e])
+            assert 0 < q < 16
+            for a in range(2):
+                for b in range(2):
+                    m[h, 2 * i + a, 2 * j + b] = bool((q >> (2 * a + b)) & 1)
+    return m
+
+
+def test_block32_layouts_are_the_rule_on_32_blocks_as_tile_quarters():
+    g = np.random.default_rng(32)
+    for _ in range(60):
+        nt = int(g.integers(1, 12))
+        nb = 2 * nt
+        H = int(g.integers(1, 3))
+        w = int(g.integers(0, 5)) * 2 + 1
+        ng = int(g.integers(0, min(nb, 3) + 1))
+        G = sorted(g.choice(nb, size=ng, replace=False).tolist())
+        r = int(g.integers(0, 6))
+        seed = int(g.integers(0, 2**63))
+        lay = bs.bsattn_make_layout(H, nt * 64, 32, w, G, r, seed)
+        rp, ci = bs.bsattn_layout_csr(lay)
+        masks = bs.bsattn_layout_tile_masks(lay)
+        assert masks is not None and masks.dtype == np.uint8 and masks.shape == ci.shape
+        assert rp.shape == (H * nt + 1,)
+        for row in range(H * nt):   # tiles ascending and unique within a row
+            assert np.all(np.diff(ci[rp[row]:rp[row + 1]]) > 0)
+        olay = OL.make_layout(H, nt * 64, 32, w, G, r, seed)
+        want = np.stack([olay.block_mask(h) for h in range(H)])
+        assert np.array_equal(_quarters(rp, ci, masks, H, nt), want), (nt, H, w, G, r, seed)
+
+
+def test_tile_masks_absent_for_64_and_128_blocks():
+    assert bs.bsattn_layout_tile_masks(bs.bsattn_make_layout(2, 512, 64, 3, [0], 1, 7)) is None
+    assert bs.bsattn_layout_tile_masks(bs.bsattn_make_layout(2, 512, 128, 3, [0], 1, 7)) is None
+
+
+def test_block32_rejects_lengths_that_are_not_whole_tiles():
+    with pytest.raises(RuntimeError):
+        bs.bsattn_make_layout(1, 32 * 5, 32, 3, [], 0, 1)

@@ -99,6 +99,11 @@ WORKLOADS = {
     "bigbird128-L8192": Workload(
         name="bigbird128-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
         data_seed=6, block=128, window_blocks=3, global_blocks=(0, 63), random_blocks=3, layout_seed=6),
+    # The BigBird layout on 32-token blocks at the throughput shape (256 blocks a side):
+    # stored as 64-token tiles with per-quarter masks.
+    "bigbird32-L8192": Workload(
+        name="bigbird32-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
+        data_seed=7, block=32, window_blocks=3, global_blocks=(0, 255), random_blocks=3, layout_seed=7),
     # Token-granular sliding window |t - s| <= 256 (the BigBird page's 64-256 token windows)
     # at the throughput shape: a band layout through the plain forward.
     "band256-L8192": Workload(
