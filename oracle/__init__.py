@@ -11,7 +11,9 @@ Modules
 -------
 ``layout``    the block layout rule (sliding window + global + hash-random
               blocks) written out with plain Python lists, expanded to a
-              0/1 token mask.
+              0/1 token mask; the token-granular pattern (linspace global
+              tokens, a token window, random tokens) as that rule on
+              1-token blocks.
 ``attention`` dense masked softmax attention in fp64 from that mask.
 ``router``    the routed-query selection: exact fp64 score q.w and top-k.
 ``attention_grad``  the gradients (dQ, dK, dV) of the masked attention for

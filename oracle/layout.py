@@ -186,3 +186,85 @@ def make_band_layout(num_heads: int, seq_len: int, block: int, band_tokens: int)
         rows_one.append(list(range(lo_tok // block, hi_tok // block + 1)))
     rows = [[list(r) for r in rows_one] for _ in range(num_heads)]
     return Layout(num_heads, seq_len, block, rows, band_tokens=band_tokens)
+
+
+# ---------------------------------------------------------------------------
+# Token-granular BigBird pattern
+# ---------------------------------------------------------------------------
+# BigBird page, section 核心实现: the code example picks its global tokens
+# uniformly with linspace(0, L-1, num_global) truncated to integers, every
+# token attends w neighbours on each side (typical w = 64) and r random
+# remote tokens (typical r = 8); the pitfalls section puts global tokens at
+# 5-10% of L.  Readings:
+# * global tokens G = {floor(i (L-1) / (n-1)) : 0 <= i < n} in exact integer
+#   arithmetic (n = 1: {0}; n = 0: none).  The page's float32 linspace gives
+#   the same integers except where rounding moves a value across an integer.
+# * the pattern is the block rule above on 1-token blocks: window of 2w+1
+#   tokens (|t - s| <= w), global blocks G, r random tokens per non-global row
+#   drawn by the same splitmix64 partial Fisher-Yates from the tokens outside
+#   the window and G, with the row stream seeded by the token index.
+
+
+def linspace_tokens(seq_len: int, n: int) -> List[int]:
+    """Global token positions: floor(i (L-1) / (n-1)), exact integers, ascending."""
+    if n <= 0:
+        return []
+    if n == 1:
+        return [0]
+    return [(i * (seq_len - 1)) // (n - 1) for i in range(n)]
+
+
+class TokenLayout:
+    """Token-granular pattern, rows evaluated on demand (the block rule with block = 1).
+
+    Row t of head h is ``row_blocks(h, t, L, 2w+1, G, r, seed)``: every token for a
+    global t, else the window, the global tokens and the random tokens, ascending.
+    """
+
+    def __init__(self, num_heads: int, seq_len: int, band_tokens: int, global_tokens: Sequence[int],
+                 random_tokens: int, seed: int):
+        self.num_heads = num_heads
+        self.seq_len = seq_len
+        self.block = 1
+        self.band_tokens = band_tokens
+        self.global_tokens = sorted(set(int(g) for g in global_tokens))
+        self.random_tokens = random_tokens
+        self.seed = seed
+        self._cache = {}
+
+    def row(self, head: int, t: int) -> List[int]:
+        key = (head, int(t))
+        if key not in self._cache:
+            self._cache[key] = row_blocks(head, int(t), self.seq_len, 2 * self.band_tokens + 1,
+                                          self.global_tokens, self.random_tokens, self.seed)
+        return self._cache[key]
+
+    def random_links(self, head: int, t: int) -> List[int]:
+        """The random tokens of row t (ascending; empty for a global row)."""
+        if int(t) in self.global_tokens:
+            return []
+        g = set(self.global_tokens)
+        w = self.band_tokens
+        return [s for s in self.row(head, t) if abs(s - int(t)) > w and s not in g]
+
+    def token_mask_rows(self, head: int, t_rows: np.ndarray, valid_len: Optional[int] = None) -> np.ndarray:
+        """[len(t_rows), L] bool: entry (t, s) is 1 iff s is in row t (and s < valid_len)."""
+        t_rows = np.asarray(t_rows, dtype=np.int64)
+        m = np.zeros((len(t_rows), self.seq_len), dtype=bool)
+        for n, t in enumerate(t_rows):
+            m[n, self.row(head, int(t))] = True
+        if valid_len is not None:
+            m &= (np.arange(self.seq_len) < valid_len)[None, :]
+        return m
+
+
+def make_token_layout(num_heads: int, seq_len: int, band_tokens: int, num_global: int,
+                      random_tokens: int, seed: int) -> TokenLayout:
+    if band_tokens < 0 or band_tokens >= seq_len:
+        raise ValueError("band_tokens must be in [0, seq_len)")
+    if num_global < 0 or num_global > seq_len:
+        raise ValueError("num_global must be in [0, seq_len]")
+    if random_tokens < 0:
+        raise ValueError("random_tokens must be >= 0")
+    return TokenLayout(num_heads, seq_len, band_tokens, linspace_tokens(seq_len, num_global),
+                       random_tokens, seed)
