@@ -185,12 +185,15 @@ def main():
         sys.exit(2)
     inp = make_inputs(wl)
 
-    if wl.band and args.which != "forward":
-        print("band workloads are timed in the forward only", file=sys.stderr)
+    if (wl.band or wl.token) and args.which != "forward":
+        print("band and token-pattern workloads are timed in the forward only", file=sys.stderr)
         sys.exit(2)
     t0 = time.perf_counter()
     if wl.band:
         lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+    elif wl.token:
+        lay = bs.bsattn_make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
+                                          wl.layout_seed)
     else:
         lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                     wl.random_blocks, wl.layout_seed)
@@ -199,6 +202,9 @@ def main():
     row_ptr, col = bs.bsattn_layout_csr(lay)
     vl_host = inp.get("valid_len")
     tiles = tile_stats(wl, row_ptr, col, None if vl_host is None else vl_host.tolist())
+    if wl.token:
+        # the global rows' tiles: ceil(n_global / 64) gathered-row tiles over every key block
+        tiles += wl.batch * wl.heads * (-(-wl.num_global // 64)) * (wl.seq_len // 64)
     stored_tiles = tiles
     masks = bs.bsattn_layout_tile_masks(lay)
     if masks is not None:
@@ -348,6 +354,7 @@ def main():
             "window_blocks": wl.window_blocks, "global_blocks": list(wl.global_blocks),
             "random_blocks": wl.random_blocks, "layout_seed": wl.layout_seed, "band_tokens": wl.band_tokens,
             "nonzero_tiles": stored_tiles, "layout_density": round(tiles / (B * H * (L // 64) ** 2), 5),
+            **({"num_global": wl.num_global, "random_tokens": wl.random_tokens} if wl.token else {}),
         },
         "eff_tflops": round(eff_tflops, 2),
         "pct_bf16_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),
@@ -370,6 +377,9 @@ def main():
         from oracle import layout as OL
         if wl.band:
             olay = OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+        elif wl.token:
+            olay = OL.make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
+                                        wl.layout_seed)
         else:
             olay = OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                   wl.random_blocks, wl.layout_seed)

@@ -25,9 +25,11 @@ from ._binding import (  # noqa: F401
     bsattn_layout_csr,
     bsattn_layout_destroy,
     bsattn_layout_tile_masks,
+    bsattn_layout_token_links,
     bsattn_layout_upload,
     bsattn_make_band_layout,
     bsattn_make_layout,
+    bsattn_make_token_layout,
     bsattn_route_topk,
     bsattn_set_profile_events,
     bsattn_status_string,

@@ -42,6 +42,10 @@ def lib() -> ctypes.CDLL:
     L.bsattn_make_layout.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_i32p, _c_int, _c_int,
                                      ctypes.c_uint64, ctypes.POINTER(_c_vp)]
     L.bsattn_make_band_layout.argtypes = [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_vp)]
+    L.bsattn_make_token_layout.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_uint64,
+                                           ctypes.POINTER(_c_vp)]
+    L.bsattn_layout_token_links.argtypes = [_c_vp, ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_int),
+                                            ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_int)]
     L.bsattn_layout_csr.argtypes = [_c_vp, ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_i32p),
                                     ctypes.POINTER(_c_int), ctypes.POINTER(ctypes.c_int64)]
     L.bsattn_layout_tile_masks.argtypes = [_c_vp, ctypes.POINTER(ctypes.POINTER(ctypes.c_uint8)),
@@ -69,7 +73,8 @@ def lib() -> ctypes.CDLL:
     L.bsattn_status_string.restype = ctypes.c_char_p
     L.bsattn_last_error.argtypes = []
     L.bsattn_last_error.restype = ctypes.c_char_p
-    for name in ("bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr",
+    for name in ("bsattn_make_layout", "bsattn_make_band_layout", "bsattn_make_token_layout",
+                 "bsattn_layout_token_links", "bsattn_layout_csr",
                  "bsattn_layout_tile_masks", "bsattn_layout_upload",
                  "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
                  "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events"):
@@ -144,6 +149,28 @@ def bsattn_make_band_layout(num_heads: int, seq_len: int, block: int, band_token
     _check("bsattn_make_band_layout", lib().bsattn_make_band_layout(num_heads, seq_len, block, band_tokens,
                                                                     ctypes.byref(out)))
     return Layout(out.value, num_heads, seq_len, band_tokens=band_tokens)
+
+
+def bsattn_make_token_layout(num_heads: int, seq_len: int, band_tokens: int, num_global: int,
+                             random_tokens: int, seed: int) -> Layout:
+    out = _c_vp()
+    _check("bsattn_make_token_layout", lib().bsattn_make_token_layout(
+        num_heads, seq_len, band_tokens, num_global, random_tokens, ctypes.c_uint64(seed & ((1 << 64) - 1)),
+        ctypes.byref(out)))
+    return Layout(out.value, num_heads, seq_len, band_tokens=band_tokens)
+
+
+def bsattn_layout_token_links(layout: Layout) -> Tuple[np.ndarray, np.ndarray]:
+    """Copies of a token layout's global tokens [n] and random tokens [H, L, r] (-1 padded)."""
+    g, lk = _c_i32p(), _c_i32p()
+    ng, r = _c_int(), _c_int()
+    _check("bsattn_layout_token_links", lib().bsattn_layout_token_links(layout.handle, ctypes.byref(g),
+                                                                        ctypes.byref(ng), ctypes.byref(lk),
+                                                                        ctypes.byref(r)))
+    gt = np.ctypeslib.as_array(g, shape=(ng.value,)).copy() if ng.value else np.zeros(0, np.int32)
+    shape = (layout.num_heads, layout.seq_len, r.value)
+    links = (np.ctypeslib.as_array(lk, shape=shape).copy() if r.value else np.zeros(shape, np.int32))
+    return gt, links
 
 
 def bsattn_layout_csr(layout: Layout) -> Tuple[np.ndarray, np.ndarray]:

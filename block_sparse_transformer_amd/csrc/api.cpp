@@ -59,7 +59,8 @@ void build_schedule(bsattn_layout* lay) {
             const int32_t r = h * lay->nb + i;
             const int32_t b0 = lay->row_ptr[r], b1 = lay->row_ptr[r + 1];
             const int32_t len = b1 - b0;
-            if (len <= kChunkTiles) {
+            // token layouts merge every row: the merge adds the row's random tokens
+            if (len <= kChunkTiles && lay->kind != 2) {
                 hi.push_back({r, b0, b1, -1, -1, 0, 0, 0});
                 continue;
             }
@@ -178,6 +179,9 @@ void free_device(bsattn_layout* lay) {
         (void)hipFree(lay->d_row_ptr);
         (void)hipFree(lay->d_col_idx);
         (void)hipFree(lay->d_col_sub);
+        (void)hipFree(lay->d_gtok);
+        (void)hipFree(lay->d_links);
+        (void)hipFree(lay->d_tok_flag);
         (void)hipFree(lay->d_items);
         (void)hipFree(lay->d_merges);
         for (auto& sc : lay->scheds) {
@@ -192,6 +196,8 @@ void free_device(bsattn_layout* lay) {
     lay->scheds.clear();
     lay->d_row_ptr = lay->d_col_idx = nullptr;
     lay->d_col_sub = nullptr;
+    lay->d_gtok = lay->d_links = nullptr;
+    lay->d_tok_flag = nullptr;
     lay->d_items = nullptr;
     lay->d_merges = nullptr;
     lay->device = -1;
@@ -209,11 +215,11 @@ bsattn_status check_layout_dims(int32_t H, int32_t L, int32_t block, bool any_bl
 }
 
 bsattn_status finish_layout(bsattn_layout* lay) {
-    build_schedule(lay);
     try {
-        build_bwd(lay);
+        build_schedule(lay);
+        if (lay->kind != 2) build_bwd(lay);   // token layouts have no backward
     } catch (const std::bad_alloc&) {
-        return fail(BSATTN_ERR_NO_MEMORY, "backward work list allocation failed");
+        return fail(BSATTN_ERR_NO_MEMORY, "work list allocation failed");
     }
     return ok();
 }
@@ -295,6 +301,28 @@ void routed_split(int32_t nb, int32_t k, int32_t* n_rt, int32_t* r_chunks, int32
     *n_rt = (k + kBlock - 1) / kBlock;
     split_row(nb, r_chunks, per);
     *r_chunks = (nb + *per - 1) / *per;
+}
+
+// Workspace of a forward over a token layout: the partial slots of every row
+// and of the global rows' routed chunks (fp32 O, then LSE), then the
+// gathered K and V tiles of the global tokens.
+struct TokenWs {
+    size_t slots, kg, vg, total;
+    int32_t n_rt, r_chunks, per;
+};
+TokenWs token_workspace(const bsattn_layout* lay, int32_t B, int32_t D) {
+    TokenWs w{};
+    const int32_t ng = (int32_t)lay->tok_g.size();
+    w.n_rt = 0;
+    w.r_chunks = 1;
+    w.per = 1;
+    if (ng > 0) routed_split(lay->nb, ng, &w.n_rt, &w.r_chunks, &w.per);
+    w.slots = (size_t)B * lay->n_slots + (size_t)B * lay->H * w.n_rt * w.r_chunks;
+    const size_t gbytes = (size_t)B * lay->H * lay->n_gt * kBlock * D * 2;
+    w.kg = align256(w.slots * slot_bytes(D));
+    w.vg = w.kg + align256(gbytes);
+    w.total = w.vg + align256(gbytes);
+    return w;
 }
 
 // Workgroups of the bf16 kernel that one device holds at once (CUs x
@@ -551,6 +579,62 @@ LayerWs layer_workspace(const bsattn_layout* lay, int32_t B, int32_t D, size_t a
     return w;
 }
 
+// Forward over a token layout (bf16): the gathered global K/V tiles, then the
+// attention kernel (band tiles and gathered tiles for every query block, the
+// global rows as routed tiles over all keys), then the merge that adds each
+// row's random tokens.  Every row goes through an fp32 partial and the merge.
+bsattn_status token_forward(const bsattn_layout* lay, int32_t B, int32_t D, const void* q, const void* k,
+                            const void* v, void* out, float* lse, float scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    const TokenWs w = token_workspace(lay, B, D);
+    if (!workspace || workspace_bytes < w.total)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", w.total, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const int32_t ng = (int32_t)lay->tok_g.size();
+    if ((int64_t)w.n_rt * w.r_chunks > (1 << 24)) return fail(BSATTN_ERR_UNSUPPORTED, "too many global tiles");
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.ws_o = (float*)workspace;
+    a.ws_lse = a.ws_o + w.slots * kBlock * D;
+    a.items = lay->d_items;
+    a.merges = lay->d_merges;
+    a.col_idx = lay->d_col_idx;
+    a.valid_len = nullptr;
+    a.routed_rows = lay->d_gtok;
+    a.routed_stride = 0;   // one list of global rows for every (batch, head)
+    a.n_items = (int32_t)lay->items.size();
+    a.n_merges = (int32_t)lay->merges.size();
+    a.items_per_head = lay->items_per_head;
+    a.B = B; a.H = lay->H; a.L = lay->L; a.nb = lay->nb; a.n_slots = lay->n_slots;
+    a.n_routed = ng; a.n_rt = w.n_rt; a.r_chunks = w.r_chunks; a.r_chunk_tiles = w.per;
+    a.r_slot_base = B * lay->n_slots;
+    a.band = lay->band_tokens;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.kg = (const uint16_t*)((char*)workspace + w.kg);
+    a.vg = (const uint16_t*)((char*)workspace + w.vg);
+    a.gtok = lay->d_gtok;
+    a.n_gt = lay->n_gt;
+    a.n_links = lay->n_links;
+    a.links = lay->d_links;
+    a.tok_global = lay->d_tok_flag;
+
+    bsattn_layout::Sched sc{};
+    bsattn_status st = get_schedule(lay, B, D, w.n_rt * w.r_chunks, w.per, w.r_chunks, stream, &sc);
+    if (st != BSATTN_OK) return st;
+    a.n_bins = sc.n_bins;
+    a.units = sc.d_units;
+    a.unit_ptr = sc.d_unit_ptr;
+    a.tiles = sc.d_tiles;
+    a.tile_ptr = sc.d_tile_ptr;
+    hipError_t e = launch_gather_global(a, D, stream);
+    if (e != hipSuccess) return hip_fail(e, "global gather launch");
+    e = launch_fwd_bf16(a, D, MASK_TOKEN, stream, g_ev_before, g_ev_after);
+    if (e != hipSuccess) return hip_fail(e, "token forward launch");
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -710,6 +794,83 @@ bsattn_status bsattn_make_band_layout(int32_t num_heads, int32_t seq_len, int32_
     return finish_layout(lay);
 }
 
+bsattn_status bsattn_make_token_layout(int32_t num_heads, int32_t seq_len, int32_t band_tokens,
+                                       int32_t num_global, int32_t random_tokens, uint64_t seed,
+                                       bsattn_layout** out) {
+    if (!out) return fail(BSATTN_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    bsattn_status st = check_layout_dims(num_heads, seq_len, kBlock);
+    if (st != BSATTN_OK) return st;
+    if (band_tokens < 0 || band_tokens >= seq_len)
+        return fail(BSATTN_ERR_INVALID_ARG, "band_tokens must be in [0, seq_len) (got %d)", band_tokens);
+    if (num_global < 0 || num_global > seq_len)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_global must be in [0, seq_len] (got %d)", num_global);
+    if (num_global > kMaxTokGlobal)
+        return fail(BSATTN_ERR_UNSUPPORTED, "num_global exceeds %d", kMaxTokGlobal);
+    if (random_tokens < 0 || random_tokens > kMaxLinks)
+        return fail(BSATTN_ERR_INVALID_ARG, "random_tokens must be in [0, %d] (got %d)", kMaxLinks, random_tokens);
+    if ((int64_t)num_heads * seq_len * random_tokens > ((int64_t)1 << 28))
+        return fail(BSATTN_ERR_UNSUPPORTED, "num_heads * seq_len * random_tokens exceeds 2^28");
+    const int32_t nb = seq_len / kBlock;
+    if (nb + (num_global + kBlock - 1) / kBlock > kTileJ + 1)
+        return fail(BSATTN_ERR_UNSUPPORTED, "seq_len too large for a token layout");
+    bsattn_layout* lay = new (std::nothrow) bsattn_layout();
+    if (!lay) return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    try {
+        lay->H = num_heads;
+        lay->L = seq_len;
+        lay->nb = nb;
+        lay->block = 1;
+        lay->kind = 2;
+        lay->band_tokens = band_tokens;
+        lay->rule.nb = nb;
+        lay->rule.seed = seed;
+        lay->rule.r = random_tokens;
+        // global tokens: floor(i (L - 1) / (n - 1)), distinct and ascending for n <= L
+        for (int32_t i = 0; i < num_global; ++i)
+            lay->tok_g.push_back(num_global == 1 ? 0
+                                                 : (int32_t)(((int64_t)i * (seq_len - 1)) / (num_global - 1)));
+        lay->tok_flag.assign((size_t)seq_len, 0);
+        for (int32_t g : lay->tok_g) lay->tok_flag[(size_t)g] = 1;
+        lay->n_gt = (num_global + kBlock - 1) / kBlock;
+        // random tokens of every row
+        lay->n_links = random_tokens;
+        lay->links.assign((size_t)num_heads * seq_len * random_tokens, -1);
+        TokenRule tr{seq_len, band_tokens, random_tokens, seed, lay->tok_g.data(), num_global};
+        for (int32_t h = 0; h < num_heads; ++h)
+            for (int32_t t = 0; t < seq_len; ++t)
+                token_links_fill(tr, h, t, lay->links.data() + ((size_t)h * seq_len + t) * random_tokens);
+        // tiles: the band's blocks, then the gathered global tiles
+        const int32_t rows = num_heads * nb;
+        lay->row_ptr.assign((size_t)rows + 1, 0);
+        for (int32_t r = 0; r < rows; ++r)
+            lay->row_ptr[r + 1] =
+                lay->row_ptr[r] + band_row_fill(nb, kBlock, band_tokens, r % nb, nullptr) + lay->n_gt;
+        lay->col_idx.assign((size_t)lay->row_ptr[rows], 0);
+        for (int32_t r = 0; r < rows; ++r) {
+            int32_t* dst = lay->col_idx.data() + lay->row_ptr[r];
+            const int32_t n = band_row_fill(nb, kBlock, band_tokens, r % nb, dst);
+            for (int32_t c = 0; c < lay->n_gt; ++c) dst[n + c] = nb + c;
+        }
+    } catch (const std::bad_alloc&) {
+        delete lay;
+        return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    }
+    *out = lay;
+    return finish_layout(lay);
+}
+
+bsattn_status bsattn_layout_token_links(const bsattn_layout* lay, const int32_t** global_tokens,
+                                        int32_t* num_global, const int32_t** links, int32_t* links_per_row) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (lay->kind != 2) return fail(BSATTN_ERR_INVALID_ARG, "not a token layout");
+    if (global_tokens) *global_tokens = lay->tok_g.empty() ? nullptr : lay->tok_g.data();
+    if (num_global) *num_global = (int32_t)lay->tok_g.size();
+    if (links) *links = lay->links.empty() ? nullptr : lay->links.data();
+    if (links_per_row) *links_per_row = lay->n_links;
+    return ok();
+}
+
 bsattn_status bsattn_layout_csr(const bsattn_layout* lay, const int32_t** row_ptr,
                                 const int32_t** col_idx, int32_t* num_rows, int64_t* nnz) {
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
@@ -762,6 +923,27 @@ bsattn_status bsattn_layout_upload(bsattn_layout* lay, hipStream_t stream) {
             return hip_fail(e, "hipMemcpyAsync (layout upload)");
         }
     }
+    if (lay->kind == 2) {
+        std::vector<int32_t> gpad((size_t)std::max(1, lay->n_gt * kBlock), -1);
+        std::copy(lay->tok_g.begin(), lay->tok_g.end(), gpad.begin());
+        const size_t nl = std::max<size_t>(1, lay->links.size());
+        e = hipMalloc(&lay->d_gtok, gpad.size() * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMalloc(&lay->d_links, nl * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMalloc(&lay->d_tok_flag, lay->tok_flag.size());
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(lay->d_gtok, gpad.data(), gpad.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess && !lay->links.empty())
+            e = hipMemcpyAsync(lay->d_links, lay->links.data(), lay->links.size() * sizeof(int32_t),
+                               hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(lay->d_tok_flag, lay->tok_flag.data(), lay->tok_flag.size(), hipMemcpyHostToDevice,
+                               stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);   // gpad is a local
+        if (e != hipSuccess) {
+            free_device(lay);
+            return fail(BSATTN_ERR_NO_MEMORY, "token layout upload: %s", hipGetErrorString(e));
+        }
+    }
     if (!lay->tile_sub.empty()) {
         e = hipMalloc(&lay->d_col_sub, lay->tile_sub.size());
         if (e == hipSuccess)
@@ -805,6 +987,10 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* lay, int32_t batch, int
     if (head_dim != 64 && head_dim != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (num_routed < 0 || num_routed > lay->L)
         return fail(BSATTN_ERR_INVALID_ARG, "num_routed must be in [0, seq_len]");
+    if (lay->kind == 2) {
+        *bytes = token_workspace(lay, batch, head_dim).total;
+        return ok();
+    }
     size_t slots = (size_t)batch * lay->n_slots;
     int32_t n_rt = 0;
     if (num_routed > 0) {
@@ -837,6 +1023,11 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     const bool sub = !lay->tile_sub.empty();   // 32-token blocks
     if (sub && dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "32-token layouts are bf16 only");
     if (sub && key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "32-token layouts take no key padding");
+    if (lay->kind == 2) {
+        if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "token layouts are bf16 only");
+        if (key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "token layouts take no key padding");
+        return token_forward(lay, B, D, q, k, v, out, lse, scale, workspace, workspace_bytes, stream);
+    }
     size_t need = 0;
     st = bsattn_workspace_size(lay, B, D, 0, &need);
     if (st != BSATTN_OK) return st;
@@ -862,6 +1053,7 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     a.items_per_head = lay->items_per_head;
     a.B = B; a.H = H; a.L = L; a.nb = lay->nb; a.n_slots = lay->n_slots;
     a.n_routed = 0; a.n_rt = 0; a.r_chunks = 1; a.r_chunk_tiles = 1; a.r_slot_base = 0;
+    a.routed_stride = 0;
     a.band = band ? lay->band_tokens : -1;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
@@ -939,6 +1131,7 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* lay, bsattn_dtype dtype
     a.items_per_head = lay->items_per_head;
     a.B = B; a.H = H; a.L = L; a.nb = lay->nb; a.n_slots = lay->n_slots;
     a.n_routed = num_routed; a.n_rt = n_rt; a.r_chunks = rch; a.r_chunk_tiles = per;
+    a.routed_stride = num_routed;
     a.r_slot_base = B * lay->n_slots;
     a.band = lay->band_tokens;
     a.scale = scale;

@@ -19,7 +19,11 @@ constexpr int kMaxChunks = 32;    // upper bound on the split of one row
 
 // MASK_SUB: layouts of 32-token blocks; each 64-token tile carries which of
 // its 2 x 2 sub-blocks are allowed (bit 2a + b: query half a, key half b).
-enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2, MASK_SUB = 3 };
+// MASK_TOKEN: token-granular layouts -- the token band on a row's own tiles,
+// and gathered tiles of the global tokens' keys (key blocks nb, nb + 1, ...).
+enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2, MASK_SUB = 3, MASK_TOKEN = 4 };
+constexpr int kMaxTokGlobal = 2048;   // global tokens of a token layout (their list lives in LDS)
+constexpr int kMaxLinks = 64;         // random tokens per row of a token layout
 
 // One workgroup's share: query block `row` (= h*nb + i) over key blocks
 // col_idx[col_begin, col_end).  slot < 0: the whole row, written straight to
@@ -100,7 +104,19 @@ struct FwdArgs {
     int32_t r_chunks;         // chunks per routed tile
     int32_t r_chunk_tiles;    // key blocks per chunk
     int32_t r_slot_base;      // first workspace slot of routed partials
-    int32_t band;             // token band of non-routed rows (MASK_BAND)
+    int32_t band;             // token band of non-routed rows (MASK_BAND, MASK_TOKEN)
+    int32_t routed_stride;    // routed_rows entries between (b, h) groups (0: one list shared by all)
+    // token layouts (MASK_TOKEN): key block j >= nb is gathered tile j - nb of
+    // the global tokens' keys, kg/vg [B*H][n_gt*64][D]; gtok the global tokens
+    // padded with -1 to n_gt*64; the merge adds each row's random tokens
+    // links[h][t][0..n_links) (-1: none) and skips global rows (tok_global).
+    const uint16_t* kg;
+    const uint16_t* vg;
+    const int32_t* gtok;
+    int32_t n_gt;
+    int32_t n_links;
+    const int32_t* links;
+    const uint8_t* tok_global;
     float scale;              // score scale
     float scale_log2;         // scale * log2(e)
 };
@@ -150,6 +166,8 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s,
                            hipEvent_t before, hipEvent_t after);
 int fwd_bf16_ctas_per_cu(int head_dim);   // workgroups of the bf16 kernel resident per CU
+// token layouts: K/V rows of the global tokens -> kg/vg (zero past the last global token)
+hipError_t launch_gather_global(const FwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, const int32_t* row_ptr, int head_dim, int mask,
                           hipStream_t s, hipEvent_t before, hipEvent_t after);
 hipError_t launch_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,
@@ -172,13 +190,22 @@ hipError_t launch_layout_build(const RowRule& rule, int kind, int32_t H, int32_t
 // The opaque layout handle of the C ABI.
 struct bsattn_layout {
     int32_t H = 0, L = 0, nb = 0, block = 0;
-    int32_t kind = 0;           // 0: window/global/random rule, 1: token band
+    int32_t kind = 0;           // 0: window/global/random rule, 1: token band, 2: token pattern
     int32_t band_tokens = -1;
     bsattn::RowRule rule{};
     std::vector<int32_t> row_ptr, col_idx;
     // 32-token layouts: for each tile of col_idx, its allowed 2 x 2 sub-blocks
     // (bit 2a + b: query half a, key half b); empty for 64/128-token layouts
     std::vector<uint8_t> tile_sub;
+    // token pattern (kind 2): global tokens, their flags [L], random tokens
+    // [H][L][n_links] (-1 past a row's count); the CSR rows list the band's
+    // tiles and then the gathered tiles nb .. nb + n_gt - 1 of the global keys
+    std::vector<int32_t> tok_g, links;
+    std::vector<uint8_t> tok_flag;
+    int32_t n_links = 0, n_gt = 0;
+    int32_t* d_gtok = nullptr;      // tok_g padded with -1 to n_gt * 64
+    int32_t* d_links = nullptr;
+    uint8_t* d_tok_flag = nullptr;
     std::vector<bsattn::WorkItem> items;
     std::vector<bsattn::MergeItem> merges;
     int32_t n_slots = 0;        // partial slots per batch entry

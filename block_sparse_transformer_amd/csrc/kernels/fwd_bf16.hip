@@ -83,6 +83,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     bf16x2_t r = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, r);
 }
+// The two bf16 of a packed pair as fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Combine a value across the two half-waves (lanes l and l^32).
 // v_permlane32_swap exchanges one half of its first operand with the other
@@ -190,6 +193,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     __shared__ __attribute__((aligned(1024))) uint16_t vbuf[2 * TILE];
     __shared__ int flat[kMaxBinTiles];
     __shared__ int s_count;
+    __shared__ __attribute__((aligned(16))) int gtok_s[MASK == MASK_TOKEN ? kMaxTokGlobal : 4];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -228,12 +232,22 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     auto gbase = [&](const void* t, int g) -> const uint16_t* {
         return (const uint16_t*)t + (size_t)g * a.L * D;
     };
+    // K (V) tile j of group g: a block of the sequence, or (token layouts,
+    // j >= nb) a gathered tile of the global tokens' keys
+    auto ktile = [&](int g, int j) -> const uint16_t* {
+        if (MASK == MASK_TOKEN && j >= a.nb) return a.kg + ((size_t)g * a.n_gt + (j - a.nb)) * TILE;
+        return gbase(a.k, g) + (size_t)j * TILE;
+    };
+    auto vtile = [&](int g, int j) -> const uint16_t* {
+        if (MASK == MASK_TOKEN && j >= a.nb) return a.vg + ((size_t)g * a.n_gt + (j - a.nb)) * TILE;
+        return gbase(a.v, g) + (size_t)j * TILE;
+    };
 
     // token of this lane's query row in a unit of kind `kind`, group g (-1: unused routed row)
     auto query_token = [&](int kind, int g) -> int {
         if (kind >= 0) return kind * 64 + rloc;
         const int kk = (-1 - kind) * 64 + rloc;
-        const int t = kk < a.n_routed ? a.routed_rows[(size_t)g * a.n_routed + kk] : -1;
+        const int t = kk < a.n_routed ? a.routed_rows[(size_t)g * a.routed_stride + kk] : -1;
         return (t >= a.L) ? -1 : t;          // out-of-range rows are skipped, never dereferenced
     };
     // Q^T fragments of a row (B operand of S^T): lane (ql, hh) holds Q[t][16c + 8hh .. +7].
@@ -282,6 +296,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     // (O = 0, LSE = -inf) right here.
     int F = nt;
     uint64_t empty_units = 0;
+    if (MASK == MASK_TOKEN)
+        for (int i = tid; i < a.n_gt * 64; i += kThreads) gtok_s[i] = a.gtok[i];
     if (MASK != MASK_PAD) {
         for (int i = tid; i < nt; i += kThreads) flat[i] = a.tiles[tp0 + i];
     } else {
@@ -434,9 +450,9 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                         if (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) s[kb][i] = -INFINITY;
             }
         }
-        if (MASK == MASK_BAND) {
+        if (MASK == MASK_BAND || MASK == MASK_TOKEN) {
             // a tile whose farthest (query, key) pair is inside the band needs no mask
-            if (kind >= 0 && 64 * abs(kind - j) + 63 > a.band) {
+            if (kind >= 0 && j < a.nb && 64 * abs(kind - j) + 63 > a.band) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -444,6 +460,20 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                         if (abs(tq - (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4))) > a.band)
                             s[kb][i] = -INFINITY;
             }
+        }
+        if (MASK == MASK_TOKEN && kind >= 0 && j >= a.nb) {
+            // gathered global keys: padding (-1) and keys the band already covers drop out
+            const int* gt = gtok_s + (j - a.nb) * 64;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int4 gv = *(const int4*)(gt + 32 * kb + 8 * g4 + 4 * hh);
+                    const int gs[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (gs[e] < 0 || abs(tq - gs[e]) <= a.band) s[kb][4 * g4 + e] = -INFINITY;
+                }
         }
         if (first) m = tile_max(s);   // o = 0 and l = 0 here
     };
@@ -523,10 +553,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     for (int c = 0; c < NC; ++c) qf_n[c] = qf[c];
 
     wait_vmcnt<0>();
-    issue_half<D>(gbase(a.k, g_cur), tile_j(e0), koffs, kl0);
-    issue_half<D>(gbase(a.v, g_cur), tile_j(e0), voffs, vl0);
+    issue_half<D>(ktile(g_cur, tile_j(e0)), 0, koffs, kl0);
+    issue_half<D>(vtile(g_cur, tile_j(e0)), 0, voffs, vl0);
     if (F > 1) {
-        issue_half<D>(gbase(a.k, tile_g(e1)), tile_j(e1), koffs, kl0 + TILE * 2);
+        issue_half<D>(ktile(tile_g(e1), tile_j(e1)), 0, koffs, kl0 + TILE * 2);
         wait_vmcnt<2 * Gm::LPT>();   // K(0) landed; V(0) and K(1) may still fly
     } else {
         wait_vmcnt<Gm::LPT>();
@@ -581,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         bf16x8_t kf[2][NC], va[4][NDB];
         kread(kbuf + (1 - P) * TILE, kf);
         vread(vbuf + P * TILE, va);
-        if (f + 2 < F) issue_half<D>(gbase(a.k, tile_g(e2)), tile_j(e2), koffs, kl0 + P * TILE * 2);
+        if (f + 2 < F) issue_half<D>(ktile(tile_g(e2), tile_j(e2)), 0, koffs, kl0 + P * TILE * 2);
         // Scores of tile f + 1 (past the end they read a stale buffer and are
         // discarded), interleaved by the scheduler with the softmax of tile f.
         using C0 = std::integral_constant<int, 0>;
@@ -595,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
         }
-        if (f + 1 < F) issue_half<D>(gbase(a.v, tile_g(e1)), tile_j(e1), voffs, vl0 + (1 - P) * TILE * 2);
+        if (f + 1 < F) issue_half<D>(vtile(tile_g(e1), tile_j(e1)), 0, voffs, vl0 + (1 - P) * TILE * 2);
         pv(va, C0(), pA);
         softmax_exp(s_now, C2(), pB);
 #pragma unroll
@@ -677,6 +707,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     __shared__ int flats[kQWaves][kMaxBinTiles];   // each wave's tile list
     __shared__ int simd_of[kQWaves];
     __shared__ int left[kQWaves];                  // tiles each wave has not finished
+    __shared__ __attribute__((aligned(16))) int gtok_s[MASK == MASK_TOKEN ? kMaxTokGlobal : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -692,6 +723,8 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         simd_of[wv] = my_simd;
         left[wv] = 0;
     }
+    if (MASK == MASK_TOKEN)
+        for (int i = tid; i < a.n_gt * 64; i += kQThreads) gtok_s[i] = a.gtok[i];
     __syncthreads();
     int rank = 0, partner = -1;
     bool paired = true;
@@ -730,11 +763,21 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     auto gbase = [&](const void* t, int g) -> const uint16_t* {
         return (const uint16_t*)t + (size_t)g * a.L * D;
     };
+    // K (V) tile j of group g: a block of the sequence, or (token layouts,
+    // j >= nb) a gathered tile of the global tokens' keys
+    auto ktile = [&](int g, int j) -> const uint16_t* {
+        if (MASK == MASK_TOKEN && j >= a.nb) return a.kg + ((size_t)g * a.n_gt + (j - a.nb)) * TILE;
+        return gbase(a.k, g) + (size_t)j * TILE;
+    };
+    auto vtile = [&](int g, int j) -> const uint16_t* {
+        if (MASK == MASK_TOKEN && j >= a.nb) return a.vg + ((size_t)g * a.n_gt + (j - a.nb)) * TILE;
+        return gbase(a.v, g) + (size_t)j * TILE;
+    };
     // token of query row r (0..63) of a unit (-1: unused routed row)
     auto query_token = [&](int kind, int g, int r) -> int {
         if (kind >= 0) return kind * 64 + r;
         const int kk = (-1 - kind) * 64 + r;
-        const int t = kk < a.n_routed ? a.routed_rows[(size_t)g * a.n_routed + kk] : -1;
+        const int t = kk < a.n_routed ? a.routed_rows[(size_t)g * a.routed_stride + kk] : -1;
         return (t >= a.L) ? -1 : t;
     };
     // Q^T fragments of both halves: qf[qb][c] holds Q[row 32qb + ql][16c + 8hh .. +7].
@@ -938,9 +981,9 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                             if (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) s[kb][qb][i] = -INFINITY;
                 }
             }
-            if (MASK == MASK_BAND) {
+            if (MASK == MASK_BAND || MASK == MASK_TOKEN) {
                 // a tile whose farthest (query, key) pair is inside the band needs no mask
-                if (kind >= 0 && 64 * abs(kind - j) + 63 > a.band) {
+                if (kind >= 0 && j < a.nb && 64 * abs(kind - j) + 63 > a.band) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -948,6 +991,20 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                             if (abs(tq[qb] - (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4))) > a.band)
                                 s[kb][qb][i] = -INFINITY;
                 }
+            }
+            if (MASK == MASK_TOKEN && kind >= 0 && j >= a.nb) {
+                // gathered global keys: padding (-1) and keys the band already covers drop out
+                const int* gt = gtok_s + (j - a.nb) * 64;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int4 gv = *(const int4*)(gt + 32 * kb + 8 * g4 + 4 * hh);
+                        const int gs[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (gs[e] < 0 || abs(tq[qb] - gs[e]) <= a.band) s[kb][qb][4 * g4 + e] = -INFINITY;
+                    }
             }
             if (first) m[qb] = tile_max(s, qb);
         }
@@ -1008,8 +1065,8 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     int tq_cur[2], tq_next[2] = {-1, -1};
     bf16x8_t qf[2][NC];
     load_q(kind_cur, g_cur, qf, tq_cur);
-    issue_tile1(gbase(a.k, g_cur), tile_j(e0), kdo, kl);
-    issue_tile1(gbase(a.v, g_cur), tile_j(e0), vdo, vl);
+    issue_tile1(ktile(g_cur, tile_j(e0)), 0, kdo, kl);
+    issue_tile1(vtile(g_cur, tile_j(e0)), 0, vdo, vl);
     reset();
 
     // A unit's epilogue (normalise, store O and LSE, reset) runs in the next
@@ -1066,8 +1123,8 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         // The buffers are free: the loads of tile f + 1 go out in four groups
         // spread over the softmax, so that no long burst stalls the wave.
         const bool more = f + 1 < F;
-        const uint16_t* kn = gbase(a.k, tile_g(e1)) + (size_t)tile_j(e1) * 64 * 64;
-        const uint16_t* vn = gbase(a.v, tile_g(e1)) + (size_t)tile_j(e1) * 64 * 64;
+        const uint16_t* kn = ktile(tile_g(e1), tile_j(e1));
+        const uint16_t* vn = vtile(tile_g(e1), tile_j(e1));
         if (more) lds_load16x4_1k(kdo, kn, kl + 2048);
         if (pend) {                         // the previous unit's epilogue
             finish();
@@ -1110,6 +1167,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // query rows each; 16 threads per row, each owning D/16 columns.  The chunk
 // LSEs and the first 8 chunks' partials are loaded in one batch, before any
 // of them is used.
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
     constexpr int DP = D / 16;   // columns per thread: 4 or 8
@@ -1132,7 +1190,7 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
         first = a.r_slot_base + (g * a.n_rt + rt) * a.r_chunks;
         nch = a.r_chunks;
         const int kk = rt * 64 + row;
-        t = kk < a.n_routed ? a.routed_rows[bh * a.n_routed + kk] : -1;
+        t = kk < a.n_routed ? a.routed_rows[bh * a.routed_stride + kk] : -1;
         if (t >= a.L) t = -1;   // out-of-range rows are skipped, never dereferenced
     }
     if (t < 0) return;
@@ -1198,6 +1256,210 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
     if (part == 0) a.lse[bh * a.L + t] = mxl + logf(wsum);
 }
 
+// Token layouts: the merge of every non-global row, with the row's random
+// tokens added.  A row's band-and-global partials (one per chunk, fp32 O
+// normalised over the chunk's keys, and its LSE) are combined by log-sum-exp
+// as in merge_bf16_kernel; each random token s then joins the same running
+// max and sum with score scale * q.k_s and value v_s.  Eight lanes per row,
+// D/8 columns each (16- or 32-byte loads); 32 rows per workgroup.  The loads
+// that depend on nothing -- chunk LSEs and partials, the q slice, the first
+// eight link ids -- go out together, so a row costs two memory round trips:
+// those, then the links' K and V slices.  The random tokens fall anywhere in
+// their head, so workgroups are mapped to XCDs by (batch, head) group: XCD x
+// (workgroup i runs on XCD i % 8) walks the rows of groups x, x + 8, ... one
+// group after the other, and the group's K and V (2 x L x D bf16) stay in that
+// XCD's L2.  Every row of a token layout is one merge item, in head-major
+// order, so row t of group g = b H + h is merge item h nb + t / 64 of batch
+// entry b.  Global rows are computed from the band units' partials like the
+// others but not written: their routed merge writes them.
+template <int D>
+__global__ __launch_bounds__(256) void links_merge_kernel(const FwdArgs a) {
+    constexpr int DP = D / 8;    // columns per lane: 8 or 16
+    constexpr int NC = 2;        // chunks whose partials are loaded up front
+    constexpr int LG = 4;        // links whose K and V slices are loaded together
+    const int tid = threadIdx.x;
+    const int part = tid & 7;
+    const int wg_per_group = a.L / 32;
+    const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+    const int g = x + kXcds * (j / wg_per_group);
+    if (g >= a.B * a.H) return;
+    const int t = (j % wg_per_group) * 32 + (tid >> 3);
+    const int b = g / a.H, h = g % a.H;
+    const MergeItem mi = a.merges[h * a.nb + t / 64];
+    const int r = t % 64;
+    const size_t bh = (size_t)g;
+    // read with the other first loads, tested only at the store: branching on
+    // it here would put a memory round trip in front of everything else
+    const bool global_row = a.tok_global[t] != 0;
+    const int first = b * a.n_slots + mi.first_slot, nch = mi.n_chunks;
+    const float* lse_p = a.ws_lse + (size_t)first * 64 + r;
+    const float* src = a.ws_o + ((size_t)first * 64 + r) * D + part * DP;
+    const int32_t* lk = a.links + ((size_t)(bh % a.H) * a.L + t) * a.n_links;
+    const uint16_t* kb = (const uint16_t*)a.k + bh * a.L * D + part * DP;
+    const uint16_t* vb = (const uint16_t*)a.v + bh * a.L * D + part * DP;
+
+    // ---- independent loads ----
+    float lsev[NC];
+    float4 pv4[NC][DP / 4];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        lsev[c] = c < nch ? lse_p[(size_t)c * 64] : -INFINITY;
+#pragma unroll
+        for (int d = 0; d < DP / 4; ++d)
+            pv4[c][d] = c < nch ? *(const float4*)(src + (size_t)c * 64 * D + 4 * d) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    u32x4_t qw[DP / 8];
+#pragma unroll
+    for (int d = 0; d < DP / 8; ++d) qw[d] = *(const u32x4_t*)((const uint16_t*)a.q + (bh * a.L + t) * D + part * DP + 8 * d);
+    // the row's link ids, eight at a time: lane `part` loads id j0 + part and
+    // the row's eight lanes share them by shuffle (one load instruction, not eight)
+    const int lane_base = (threadIdx.x & 63) & ~7;
+    int my_id = part < a.n_links ? lk[part] : -1;
+
+    // ---- the band-and-global partials ----
+    float mxl = -INFINITY;
+    for (int c = 0; c < nch; ++c) mxl = __builtin_fmaxf(mxl, c < NC ? lsev[c] : lse_p[(size_t)c * 64]);
+    float acc[DP], wsum = 0.f;
+#pragma unroll
+    for (int d = 0; d < DP; ++d) acc[d] = 0.f;
+    if (mxl != -INFINITY) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float w = expf(lsev[c] - mxl);   // 0 past nch
+            wsum += w;
+#pragma unroll
+            for (int d = 0; d < DP / 4; ++d) {
+                acc[4 * d] += w * pv4[c][d].x;
+                acc[4 * d + 1] += w * pv4[c][d].y;
+                acc[4 * d + 2] += w * pv4[c][d].z;
+                acc[4 * d + 3] += w * pv4[c][d].w;
+            }
+        }
+        for (int c = NC; c < nch; ++c) {
+            const float w = expf(lse_p[(size_t)c * 64] - mxl);
+            wsum += w;
+#pragma unroll
+            for (int d = 0; d < DP / 4; ++d) {
+                const float4 x = *(const float4*)(src + (size_t)c * 64 * D + 4 * d);
+                acc[4 * d] += w * x.x;
+                acc[4 * d + 1] += w * x.y;
+                acc[4 * d + 2] += w * x.z;
+                acc[4 * d + 3] += w * x.w;
+            }
+        }
+    }
+    float qv[DP];
+#pragma unroll
+    for (int d = 0; d < DP / 8; ++d) {
+        const uint32_t w4[4] = {qw[d].x, qw[d].y, qw[d].z, qw[d].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qv[8 * d + 2 * e] = bf16_lo(w4[e]);
+            qv[8 * d + 2 * e + 1] = bf16_hi(w4[e]);
+        }
+    }
+
+    // ---- random tokens: ids eight at a time, K and V slices LG at a time ----
+    for (int j0 = 0; j0 < a.n_links; j0 += 8) {
+        if (j0 > 0) my_id = j0 + part < a.n_links ? lk[j0 + part] : -1;
+        for (int q4 = 0; q4 < 8; q4 += LG) {
+            int sid[LG];
+#pragma unroll
+            for (int jj = 0; jj < LG; ++jj) sid[jj] = __shfl(my_id, lane_base + q4 + jj, 64);
+            u32x4_t kw[LG][DP / 8], vw[LG][DP / 8];
+#pragma unroll
+            for (int jj = 0; jj < LG; ++jj) {
+                const size_t off = (size_t)(sid[jj] < 0 ? t : sid[jj]) * D;   // a valid row either way
+#pragma unroll
+                for (int d = 0; d < DP / 8; ++d) {
+                    kw[jj][d] = *(const u32x4_t*)(kb + off + 8 * d);
+                    vw[jj][d] = *(const u32x4_t*)(vb + off + 8 * d);
+                }
+            }
+            float x[LG];
+            float mnew = mxl;
+#pragma unroll
+            for (int jj = 0; jj < LG; ++jj) {
+                float dot = 0.f;
+#pragma unroll
+                for (int d = 0; d < DP / 8; ++d) {
+                    const uint32_t w4[4] = {kw[jj][d].x, kw[jj][d].y, kw[jj][d].z, kw[jj][d].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dot = fmaf(qv[8 * d + 2 * e], bf16_lo(w4[e]), dot);
+                        dot = fmaf(qv[8 * d + 2 * e + 1], bf16_hi(w4[e]), dot);
+                    }
+                }
+                dot += __shfl_xor(dot, 4, 8);
+                dot += __shfl_xor(dot, 2, 8);
+                dot += __shfl_xor(dot, 1, 8);
+                x[jj] = sid[jj] < 0 ? -INFINITY : dot * a.scale;
+                mnew = __builtin_fmaxf(mnew, x[jj]);
+            }
+            if (mnew > mxl) {
+                const float c = mxl == -INFINITY ? 0.f : expf(mxl - mnew);
+#pragma unroll
+                for (int d = 0; d < DP; ++d) acc[d] *= c;
+                wsum *= c;
+                mxl = mnew;
+            }
+#pragma unroll
+            for (int jj = 0; jj < LG; ++jj) {
+                const float w = x[jj] == -INFINITY ? 0.f : expf(x[jj] - mxl);
+                wsum += w;
+#pragma unroll
+                for (int d = 0; d < DP / 8; ++d) {
+                    const uint32_t w4[4] = {vw[jj][d].x, vw[jj][d].y, vw[jj][d].z, vw[jj][d].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[8 * d + 2 * e] = fmaf(w, bf16_lo(w4[e]), acc[8 * d + 2 * e]);
+                        acc[8 * d + 2 * e + 1] = fmaf(w, bf16_hi(w4[e]), acc[8 * d + 2 * e + 1]);
+                    }
+                }
+            }
+        }
+    }
+
+    if (global_row) return;
+    uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * DP;
+    const bool empty = mxl == -INFINITY;
+    const float inv = empty ? 0.f : 1.f / wsum;
+#pragma unroll
+    for (int d = 0; d < DP / 8; ++d) {
+        u32x4_t w4;
+        w4.x = pack_bf16x2(acc[8 * d + 0] * inv, acc[8 * d + 1] * inv);
+        w4.y = pack_bf16x2(acc[8 * d + 2] * inv, acc[8 * d + 3] * inv);
+        w4.z = pack_bf16x2(acc[8 * d + 4] * inv, acc[8 * d + 5] * inv);
+        w4.w = pack_bf16x2(acc[8 * d + 6] * inv, acc[8 * d + 7] * inv);
+        *(u32x4_t*)(orow + 8 * d) = w4;
+    }
+    if (part == 0) a.lse[bh * a.L + t] = empty ? -INFINITY : mxl + logf(wsum);
+}
+
+// Token layouts: copy the K and V rows of the global tokens into contiguous
+// 64-row tiles, kg/vg [B*H][n_gt*64][D], zero past the last global token (a
+// masked key still meets V in the PV product, so it must hold a finite value).
+// One thread per 16 bytes.
+template <int D>
+__global__ __launch_bounds__(256) void gather_global_kernel(const FwdArgs a, uint16_t* kg, uint16_t* vg) {
+    const int rows_per_g = a.n_gt * 64;
+    const size_t n8 = (size_t)a.B * a.H * rows_per_g * (D / 8);
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const size_t row = i / (D / 8);
+    const int col = (int)(i % (D / 8)) * 8;
+    const size_t g = row / rows_per_g;
+    const int tok = a.gtok[row % rows_per_g];
+    u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (tok >= 0) {
+        const size_t src = (g * a.L + tok) * D + col;
+        kv = *(const u32x4_t*)((const uint16_t*)a.k + src);
+        vv = *(const u32x4_t*)((const uint16_t*)a.v + src);
+    }
+    *(u32x4_t*)(kg + row * D + col) = kv;
+    *(u32x4_t*)(vg + row * D + col) = vv;
+}
+
 template <int D, int MASK>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
     const int64_t grid = (int64_t)kXcds * a.n_bins;
@@ -1234,24 +1496,56 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
     hipError_t e;
     if (before && (e = hipEventRecord(before, s)) != hipSuccess) return e;
     if (head_dim == 64) {
-        e = mask == MASK_PAD ? launch_d64<MASK_PAD>(a, s)
-          : mask == MASK_BAND ? launch_d64<MASK_BAND>(a, s)
-          : mask == MASK_SUB  ? launch_d64<MASK_SUB>(a, s)
-                              : launch_d64<MASK_NONE>(a, s);
+        e = mask == MASK_PAD   ? launch_d64<MASK_PAD>(a, s)
+          : mask == MASK_BAND  ? launch_d64<MASK_BAND>(a, s)
+          : mask == MASK_SUB   ? launch_d64<MASK_SUB>(a, s)
+          : mask == MASK_TOKEN ? launch_d64<MASK_TOKEN>(a, s)
+                               : launch_d64<MASK_NONE>(a, s);
     } else {
-        e = mask == MASK_PAD ? launch_fwd_t<128, MASK_PAD>(a, s)
-          : mask == MASK_BAND ? launch_fwd_t<128, MASK_BAND>(a, s)
-          : mask == MASK_SUB  ? launch_fwd_t<128, MASK_SUB>(a, s)
-                              : launch_fwd_t<128, MASK_NONE>(a, s);
+        e = mask == MASK_PAD   ? launch_fwd_t<128, MASK_PAD>(a, s)
+          : mask == MASK_BAND  ? launch_fwd_t<128, MASK_BAND>(a, s)
+          : mask == MASK_SUB   ? launch_fwd_t<128, MASK_SUB>(a, s)
+          : mask == MASK_TOKEN ? launch_fwd_t<128, MASK_TOKEN>(a, s)
+                               : launch_fwd_t<128, MASK_NONE>(a, s);
     }
     if (e != hipSuccess) return e;
     if (after && (e = hipEventRecord(after, s)) != hipSuccess) return e;
     const int64_t units = (int64_t)a.B * a.n_merges + (a.n_routed > 0 ? (int64_t)a.B * a.H * a.n_rt : 0);
     if (units == 0) return hipSuccess;
+    if (mask == MASK_TOKEN) {
+        // the global rows (routed units) by the plain merge, every other row with its random tokens
+        FwdArgs g = a;
+        g.n_merges = 0;
+        const int64_t gu = a.n_routed > 0 ? (int64_t)a.B * a.H * a.n_rt : 0;
+        if (gu > 0) {
+            if (head_dim == 64) hipLaunchKernelGGL(merge_bf16_kernel<64>, dim3((unsigned)(4 * gu)), dim3(256), 0, s, g);
+            else hipLaunchKernelGGL(merge_bf16_kernel<128>, dim3((unsigned)(4 * gu)), dim3(256), 0, s, g);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        // every row is a merge item: n_merges == H * nb, one XCD slot per (batch, head) group
+        if (a.n_merges != a.H * a.nb) return hipErrorInvalidValue;
+        const int64_t groups = (int64_t)a.B * a.H;
+        if (groups == 0) return hipSuccess;
+        const dim3 grid((unsigned)(kXcds * ((groups + kXcds - 1) / kXcds) * (a.L / 32)));
+        if (head_dim == 64) hipLaunchKernelGGL(links_merge_kernel<64>, grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(links_merge_kernel<128>, grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if (head_dim == 64)
         hipLaunchKernelGGL(merge_bf16_kernel<64>, dim3((unsigned)(4 * units)), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(merge_bf16_kernel<128>, dim3((unsigned)(4 * units)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_global(const FwdArgs& a, int head_dim, hipStream_t s) {
+    const size_t n8 = (size_t)a.B * a.H * a.n_gt * 64 * (head_dim / 8);
+    if (n8 == 0) return hipSuccess;
+    const dim3 grid((unsigned)((n8 + 255) / 256));
+    uint16_t* kg = const_cast<uint16_t*>(a.kg);
+    uint16_t* vg = const_cast<uint16_t*>(a.vg);
+    if (head_dim == 64) hipLaunchKernelGGL(gather_global_kernel<64>, grid, dim3(256), 0, s, a, kg, vg);
+    else hipLaunchKernelGGL(gather_global_kernel<128>, grid, dim3(256), 0, s, a, kg, vg);
     return hipGetLastError();
 }
 

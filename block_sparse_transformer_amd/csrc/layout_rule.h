@@ -155,6 +155,93 @@ BSR_HD inline int32_t rule_row_fill(const RowRule& R, int32_t h, int32_t i, int3
     return o;
 }
 
+// Token-granular pattern: the rule above on 1-token blocks (window [t-w, t+w]
+// clipped, global tokens G of any number, r random tokens per non-global row
+// from the same per-row stream with the token index in place of the block
+// index).  The excluded set is one interval plus G, so the p-th candidate is
+// found by binary search over G instead of from a materialised list.
+struct TokenRule {
+    int32_t L;           // tokens
+    int32_t w;           // window half-width in tokens
+    int32_t r;           // random tokens per row (<= kMaxRandom)
+    uint64_t seed;
+    const int32_t* g;    // global tokens, ascending, distinct
+    int32_t ng;
+};
+
+// Number of global tokens < x.
+BSR_HD inline int32_t token_g_below(const TokenRule& R, int32_t x) {
+    int32_t lo = 0, hi = R.ng;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) / 2;
+        if (R.g[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+BSR_HD inline bool token_is_global(const TokenRule& R, int32_t t) {
+    const int32_t k = token_g_below(R, t);
+    return k < R.ng && R.g[k] == t;
+}
+
+// The q-th (0-based) token outside G: q + k, k = #{i : g[i] - i <= q} (g[i] - i
+// is non-decreasing for ascending distinct g).
+BSR_HD inline int32_t token_nonglobal_select(const TokenRule& R, int32_t q) {
+    int32_t lo = 0, hi = R.ng;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) / 2;
+        if (R.g[mid] - mid <= q) lo = mid + 1;
+        else hi = mid;
+    }
+    return q + lo;
+}
+
+// Random tokens of row t of head h, ascending, into out[] (capacity r);
+// returns how many (0 for a global row).
+BSR_HD inline int32_t token_links_fill(const TokenRule& R, int32_t h, int32_t t, int32_t* out) {
+    if (token_is_global(R, t)) return 0;
+    const int32_t lo = t - R.w < 0 ? 0 : t - R.w;
+    const int32_t hi = t + R.w > R.L - 1 ? R.L - 1 : t + R.w;
+    const int32_t before = lo - token_g_below(R, lo);            // candidates left of the window
+    const int32_t upto = (hi + 1) - token_g_below(R, hi + 1);    // non-global tokens in [0, hi]
+    const int32_t n = (R.L - R.ng) - (upto - before);
+    const int32_t take = R.r < n ? R.r : n;
+    auto cand = [&](int32_t p) {
+        return token_nonglobal_select(R, p < before ? p : p - before + upto);
+    };
+    int32_t pos[2 * kMaxRandom], val[2 * kMaxRandom];
+    int32_t nmap = 0;
+    uint64_t state = splitmix_first(splitmix_first(splitmix_first(R.seed) ^ (uint64_t)(uint32_t)h) ^
+                                    (uint64_t)(uint32_t)t);
+    for (int32_t j = 0; j < take; ++j) {
+        state += kGoldenGamma;
+        const uint64_t u = mix64(state);
+        const int32_t x = j + (int32_t)(u % (uint64_t)(n - j));
+        int32_t sj = -1, sx = -1;
+        for (int32_t a = 0; a < nmap; ++a) {
+            if (pos[a] == j) sj = a;
+            if (pos[a] == x) sx = a;
+        }
+        const int32_t vj = sj >= 0 ? val[sj] : cand(j);
+        const int32_t vx = sx >= 0 ? val[sx] : cand(x);
+        if (sj < 0) { sj = nmap; pos[nmap] = j; ++nmap; }
+        val[sj] = vx;
+        if (x != j) {
+            if (sx < 0) { sx = nmap; pos[nmap] = x; ++nmap; }
+            val[sx] = vj;
+        }
+        out[j] = vx;
+    }
+    for (int32_t a = 1; a < take; ++a) {   // insertion sort (take <= 64)
+        const int32_t y = out[a];
+        int32_t b = a - 1;
+        while (b >= 0 && out[b] > y) { out[b + 1] = out[b]; --b; }
+        out[b + 1] = y;
+    }
+    return take;
+}
+
 // Band layout: key blocks touched by |t - s| <= band for query block i.
 BSR_HD inline int32_t band_row_fill(int32_t nb, int32_t block, int32_t band, int32_t i, int32_t* out) {
     const int32_t L = nb * block;

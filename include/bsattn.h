@@ -108,6 +108,41 @@ bsattn_status bsattn_make_layout(int32_t num_heads, int32_t seq_len, int32_t blo
 bsattn_status bsattn_make_band_layout(int32_t num_heads, int32_t seq_len, int32_t block,
                                       int32_t band_tokens, bsattn_layout** out);
 
+/* Build the token-granular BigBird pattern on the host (no HIP call).
+ * BigBird page, section 核心实现: global tokens chosen uniformly by the code
+ * example's linspace, a sliding window of w neighbours on each side (typical
+ * w = 64), r random remote tokens per token (typical r = 8); section 避坑指南:
+ * global tokens at 5-10% of L.  Query t attends key s iff t is global, s is
+ * global, |t - s| <= band_tokens, or s is one of t's random tokens.
+ *   num_heads      H >= 1; the pattern is per head and shared by the batch.
+ *   seq_len        L, a positive multiple of 64.
+ *   band_tokens    w in [0, L).
+ *   num_global     n in [0, min(L, 2048)]: global tokens floor(i (L-1)/(n-1)),
+ *                  i = 0..n-1 (exact integers; n = 1 gives token 0).
+ *   random_tokens  r in [0, 64]: per non-global row, r distinct tokens drawn
+ *                  from those outside the window and the global tokens, by the
+ *                  same splitmix64 partial Fisher-Yates as bsattn_make_layout
+ *                  with the token index in place of the block index (the rule
+ *                  of bsattn_make_layout on 1-token blocks); all of them if
+ *                  fewer than r.  Global rows draw none.
+ *   seed           hash seed.
+ *   out            receives the new layout (caller frees with bsattn_layout_destroy).
+ * The stored CSR lists, per row of 64-token tiles, the tiles the band touches
+ * and then the gathered tiles L/64 .. L/64 + ceil(n/64) - 1 that hold the
+ * global tokens' keys.  Forward only (bf16, no key padding); the backward,
+ * the layer and the routed call return UNSUPPORTED or INVALID_ARG for it.
+ * Limits: H * L * r <= 2^28. */
+bsattn_status bsattn_make_token_layout(int32_t num_heads, int32_t seq_len, int32_t band_tokens,
+                                       int32_t num_global, int32_t random_tokens, uint64_t seed,
+                                       bsattn_layout** out);
+
+/* Borrowed host view of a token layout (valid until destroy): the global
+ * tokens [num_global], ascending, and the random tokens [H][L][links_per_row],
+ * each row ascending and padded with -1.  INVALID_ARG for other layouts.  Any
+ * output pointer may be NULL. */
+bsattn_status bsattn_layout_token_links(const bsattn_layout* layout, const int32_t** global_tokens,
+                                        int32_t* num_global, const int32_t** links, int32_t* links_per_row);
+
 /* Borrowed host view of the block-CSR arrays (valid until destroy).
  *   row_ptr [num_rows + 1], col_idx [nnz], num_rows = H * L / 64 (rows of
  *   64-token tiles whatever the layout's block), rows ordered head-major
@@ -145,7 +180,9 @@ void bsattn_layout_destroy(bsattn_layout* layout);
  * width: the fp32 partial outputs and partial LSEs of rows that are split
  * across workgroups (global rows, routed tiles), which a second kernel of the
  * same call merges by log-sum-exp.  Written to *bytes (0 when nothing is
- * split).  The workspace needs no initialisation and holds nothing between
+ * split).  For a token layout (num_routed ignored): the partials of every
+ * row and of the global rows, and the gathered K/V tiles of the global
+ * tokens.  The workspace needs no initialisation and holds nothing between
  * calls; calls that share one must not overlap in time. */
 bsattn_status bsattn_workspace_size(const bsattn_layout* layout, int32_t batch,
                                     int32_t head_dim, int32_t num_routed, size_t* bytes);
@@ -156,7 +193,12 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* layout, int32_t batch,
  *                  token-granular sliding window |t - s| <= band_tokens (the
  *                  primer page's window_size loop, the BigBird page's 64-256
  *                  token windows); it is bf16 only and takes no key padding
- *                  (BSATTN_ERR_UNSUPPORTED otherwise).
+ *                  (BSATTN_ERR_UNSUPPORTED otherwise).  A token layout
+ *                  (bsattn_make_token_layout) gives the token-granular
+ *                  BigBird pattern, also bf16 only without key padding: the
+ *                  call then runs a gather of the global tokens' K/V rows,
+ *                  the attention kernel and a merge that adds every row's
+ *                  random tokens.
  *   dtype          element type of q, k, v and out.
  *   batch..head_dim  B >= 1, H, L as in the layout, D in {64, 128}.
  *   q, k, v        device [B, H, L, D], contiguous, 16-byte aligned.

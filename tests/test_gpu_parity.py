@@ -202,7 +202,7 @@ def test_routed_head_dim_64():
 
 # ---------------- layout on the device, determinism ----------------
 
-@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.block == 64])
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.block == 64 and not w.token])
 def test_device_layout_equals_host(name):
     wl = WORKLOADS[name]
     _say("device layout", name)
@@ -427,3 +427,75 @@ def test_block32_rejects_padding_and_fp32():
         bs.forward(inp["q"], inp["k"], inp["v"], lay, key_valid_len=vl, scale=wl.scale)
     with pytest.raises(bs.BsattnError):
         bs.forward(inp["q"].float(), inp["k"].float(), inp["v"].float(), lay, scale=wl.scale)
+
+
+# ---------------- token-granular BigBird pattern ----------------
+
+def _token_layouts(wl):
+    lay = bs.bsattn_make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
+                                      wl.layout_seed)
+    bs.bsattn_layout_upload(lay)
+    olay = OL.make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
+                                wl.layout_seed)
+    return lay, olay
+
+
+def _token_full(wl, tag):
+    _say(tag, wl)
+    inp = make_inputs(wl)
+    lay, olay = _token_layouts(wl)
+    o, l = _run(wl, inp, lay)
+    ro, rl = OA.attention_forward(inp["q"], inp["k"], inp["v"], olay, wl.scale)
+    _compare(o, l, ro, rl, wl.dtype, tag)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_token_pattern_full(D):
+    _token_full(WORKLOADS["bigbird-tok-L8192"].with_(batch=2, heads=2, seq_len=1536, head_dim=D),
+                f"token pattern L1536 D={D}")
+
+
+@pytest.mark.parametrize("D,w,ng,r", [(64, 5, 77, 8), (128, 200, 77, 3), (64, 130, 150, 16)])
+def test_token_pattern_many_globals(D, w, ng, r):
+    # 5-10% global tokens: several gathered tiles, globals inside and outside the window
+    _token_full(WORKLOADS["bigbird-tok-L8192"].with_(batch=1, heads=2, seq_len=1536, head_dim=D, band_tokens=w,
+                                                     num_global=ng, random_tokens=r, layout_seed=D + w),
+                f"token pattern w={w} ng={ng} r={r} D={D}")
+
+
+def test_token_pattern_edges():
+    base = WORKLOADS["bigbird-tok-L8192"].with_(batch=2, heads=2, seq_len=256, head_dim=64)
+    _token_full(base.with_(num_global=0), "token: no global tokens")
+    _token_full(base.with_(random_tokens=0), "token: no random tokens")
+    _token_full(base.with_(num_global=1, band_tokens=0), "token: one global token, window 0")
+    _token_full(base.with_(seq_len=128, num_global=128), "token: every token global")
+    _token_full(base.with_(seq_len=64, num_global=2, band_tokens=63, random_tokens=64), "token: one tile")
+
+
+def test_token_pattern_benchmark_shape_sampled():
+    wl = WORKLOADS["bigbird-tok-L8192"]
+    _say("token pattern bench shape", wl)
+    inp = make_inputs(wl)
+    lay, olay = _token_layouts(wl)
+    o, l = _run(wl, inp, lay)
+    g = np.random.default_rng(6)
+    ts = list(g.integers(0, wl.seq_len, 40)) + [0, 1, 63, 64, 1169, 1170, 1171, 8190, 8191]
+    rows = [(int(g.integers(wl.batch)), int(g.integers(wl.heads)), int(t)) for t in ts]
+    ro, rl = OA.attention_rows(inp["q"], inp["k"], inp["v"], olay, wl.scale, rows)
+    go = np.stack([o[b, h, t] for b, h, t in rows])
+    gl = np.array([l[b, h, t] for b, h, t in rows])
+    _compare(go, gl, ro, rl, wl.dtype, "token pattern bench shape")
+
+
+def test_token_pattern_rejects():
+    wl = WORKLOADS["bigbird-tok-L8192"].with_(batch=1, heads=1, seq_len=256)
+    lay, _ = _token_layouts(wl)
+    inp = {k: v.cuda() for k, v in make_inputs(wl).items()}
+    with pytest.raises(bs.BsattnError):
+        bs.forward(inp["q"], inp["k"], inp["v"], lay, scale=wl.scale,
+                   key_valid_len=torch.tensor([100], dtype=torch.int32, device="cuda"))
+    with pytest.raises(bs.BsattnError):
+        bs.forward(inp["q"].float(), inp["k"].float(), inp["v"].float(), lay, scale=wl.scale)
+    o, l = bs.forward(inp["q"], inp["k"], inp["v"], lay, scale=wl.scale)
+    with pytest.raises(bs.BsattnError):
+        bs.backward(inp["q"], inp["k"], inp["v"], o, l, o, lay, scale=wl.scale)

@@ -16,7 +16,8 @@ def _both(H, L, w, G, r, seed):
     return got, want
 
 
-@pytest.mark.parametrize("name", [n for n, wl in WORKLOADS.items() if not (wl.routed or wl.band) and wl.block == 64])
+@pytest.mark.parametrize("name", [n for n, wl in WORKLOADS.items()
+                                  if not (wl.routed or wl.band or wl.token) and wl.block == 64])
 def test_workload_layouts_bit_exact(name):
     wl = WORKLOADS[name]
     (rp, ci), (orp, oci) = _both(wl.heads, wl.seq_len, wl.window_blocks, wl.global_blocks,
@@ -143,3 +144,60 @@ def test_tile_masks_absent_for_64_and_128_blocks():
 def test_block32_rejects_lengths_that_are_not_whole_tiles():
     with pytest.raises(RuntimeError):
         bs.bsattn_make_layout(1, 32 * 5, 32, 3, [], 0, 1)
+
+
+def _token_rows_match(H, L, w, ng, r, seed, rows=None):
+    lay = bs.bsattn_make_token_layout(H, L, w, ng, r, seed)
+    g, links = bs.bsattn_layout_token_links(lay)
+    olay = OL.make_token_layout(H, L, w, ng, r, seed)
+    assert g.tolist() == olay.global_tokens
+    assert links.shape == (H, L, r)
+    for h, t in (rows if rows is not None else [(h, t) for h in range(H) for t in range(L)]):
+        want = olay.random_links(h, t)
+        got = [int(x) for x in links[h, t] if x >= 0]
+        assert got == want, (H, L, w, ng, r, seed, h, t)
+        assert np.all(links[h, t, len(got):] == -1)
+    return lay
+
+
+def test_token_layout_random_tokens_bit_exact():
+    g = np.random.default_rng(17)
+    for _ in range(12):
+        L = 64 * int(g.integers(1, 9))
+        w = int(g.integers(0, min(L, 150)))
+        ng = int(g.integers(0, min(L, 40) + 1))
+        r = int(g.integers(0, 12))
+        _token_rows_match(int(g.integers(1, 3)), L, w, ng, r, int(g.integers(0, 2**63)))
+
+
+def test_token_layout_edge_cases():
+    _token_rows_match(1, 64, 63, 64, 8, 1)        # every token global: no random tokens at all
+    _token_rows_match(1, 128, 60, 1, 64, 2)       # fewer candidates than r near the middle rows
+    _token_rows_match(2, 256, 0, 0, 5, 3)         # no window beyond the diagonal, no global tokens
+
+
+def test_token_layout_benchmark_shape_sampled_rows():
+    from workloads import WORKLOADS
+    wl = WORKLOADS["bigbird-tok-L8192"]
+    g = np.random.default_rng(4)
+    rows = [(int(g.integers(wl.heads)), int(t)) for t in g.integers(0, wl.seq_len, 40)]
+    rows += [(0, 0), (0, wl.seq_len - 1), (wl.heads - 1, 1170), (3, 1171)]
+    _token_rows_match(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens, wl.layout_seed,
+                      rows=rows)
+
+
+def test_token_layout_csr_is_band_tiles_then_gathered_tiles():
+    lay = bs.bsattn_make_token_layout(2, 640, 70, 70, 3, 9)
+    rp, ci = bs.bsattn_layout_csr(lay)
+    nb, n_gt = 10, 2
+    for r in range(2 * nb):
+        i = r % nb
+        lo, hi = max(0, 64 * i - 70) // 64, min(639, 64 * i + 63 + 70) // 64
+        assert ci[rp[r]:rp[r + 1]].tolist() == list(range(lo, hi + 1)) + [nb + c for c in range(n_gt)]
+
+
+def test_token_layout_rejects():
+    for args in [(1, 100, 3, 2, 2, 0), (1, 256, 256, 2, 2, 0), (1, 256, 3, 257, 2, 0), (1, 256, 3, 2, 65, 0),
+                 (0, 256, 3, 2, 2, 0), (1, 8192, 3, 2049, 2, 0)]:
+        with pytest.raises(RuntimeError):
+            bs.bsattn_make_token_layout(*args)

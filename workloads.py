@@ -53,6 +53,9 @@ class Workload:
     padded: bool = False            # per-batch key valid length drawn after Q/K/V
     routed_k: int = 0               # >0: routed-query variant (top-k rows attend to all keys)
     band_tokens: int = 0            # routed variant: other rows see keys with |t-s| <= band
+    token: bool = False             # token-granular BigBird pattern (window band_tokens, below)
+    num_global: int = 0             # token pattern: linspace global tokens
+    random_tokens: int = 0          # token pattern: random tokens per row
 
     @property
     def routed(self) -> bool:
@@ -61,7 +64,7 @@ class Workload:
     @property
     def band(self) -> bool:
         """A token-band layout without routed rows (the plain forward on a band layout)."""
-        return self.band_tokens > 0 and not self.routed
+        return self.band_tokens > 0 and not self.routed and not self.token
 
     @property
     def num_blocks(self) -> int:
@@ -104,6 +107,11 @@ WORKLOADS = {
     "bigbird32-L8192": Workload(
         name="bigbird32-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
         data_seed=7, block=32, window_blocks=3, global_blocks=(0, 255), random_blocks=3, layout_seed=7),
+    # The token-granular BigBird pattern with the BigBird page's code defaults: a window of
+    # 64 tokens each side, 8 linspace global tokens, 8 random tokens per row.
+    "bigbird-tok-L8192": Workload(
+        name="bigbird-tok-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
+        data_seed=8, token=True, band_tokens=64, num_global=8, random_tokens=8, layout_seed=8),
     # Token-granular sliding window |t - s| <= 256 (the BigBird page's 64-256 token windows)
     # at the throughput shape: a band layout through the plain forward.
     "band256-L8192": Workload(
