@@ -20,6 +20,8 @@ Modules
               an upstream dO: the softmax Jacobian written out in fp64.
 ``layer``     the attention layer around it: qkv projection, head split,
               attention, head concatenation, output projection.
+``adaptive``  the content-adaptive block layout (top blocks per query block
+              by pooled fp64 scores) and its attention.
 
 Parity pins (see ``tests/test_oracle_*.py``): every function is checked
 against something other than itself -- published splitmix64 outputs, closed
@@ -30,4 +32,4 @@ Parity unpinned: the concrete choice of random blocks beyond the
 hash stream itself (the composition of the per-row seed and the shuffle are
 this library's own specification; any uniform draw satisfies the pages).
 """
-from . import layout, attention, attention_grad, layer, router  # noqa: F401
+from . import layout, attention, attention_grad, layer, router, adaptive  # noqa: F401
