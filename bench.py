@@ -131,6 +131,33 @@ def cpu_baseline(wl, inp, layout_o, seconds: float):
             "seconds": round(dt, 3)}
 
 
+def cpu_baseline_adaptive(wl, inp, seconds: float):
+    """The oracle's adaptive forward (block sums, scores, selection, dense masked attention) on
+    whole (batch, head) pairs taken in order until ``seconds`` have passed, scaled to the job."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import adaptive as OD
+    all_pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)]
+    pairs = []
+    t0 = time.perf_counter()
+    for b, h in all_pairs:
+        rows = [[None] * wl.heads for _ in range(wl.batch)]
+        rows[b][h] = OD.adaptive_rows(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1], wl.keep_blocks)[0][0]
+        OD.adaptive_attention_forward(inp["q"], inp["k"], inp["v"], wl.keep_blocks, wl.scale, rows=rows,
+                                      pairs=[(b, h)])
+        pairs.append((b, h))
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    full_s = dt * (wl.batch * wl.heads) / len(pairs)
+    return {"value": wl.batch * wl.seq_len / full_s, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(pairs)} of {wl.batch * wl.heads} (batch, head) pairs, all {wl.seq_len} query rows, "
+                      f"block selection and dense fp64 masked attention; {dt:.2f} s measured, scaled to the whole job",
+            "seconds": round(dt, 3)}
+
+
 def cpu_baseline_bwd(wl, inp, do, layout_o, seconds: float):
     """The oracle backward as it stands, on whole (batch, head) pairs taken in order until
     ``seconds`` have passed, scaled to the whole job."""
@@ -185,8 +212,8 @@ def main():
         sys.exit(2)
     inp = make_inputs(wl)
 
-    if (wl.band or wl.token) and args.which != "forward":
-        print("band and token-pattern workloads are timed in the forward only", file=sys.stderr)
+    if (wl.band or wl.token or wl.adaptive) and args.which != "forward":
+        print("band, token-pattern and adaptive workloads are timed in the forward only", file=sys.stderr)
         sys.exit(2)
     t0 = time.perf_counter()
     if wl.band:
@@ -194,6 +221,8 @@ def main():
     elif wl.token:
         lay = bs.bsattn_make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
                                           wl.layout_seed)
+    elif wl.adaptive:
+        lay = bs.bsattn_make_adaptive_layout(wl.heads, wl.seq_len, wl.keep_blocks)
     else:
         lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                     wl.random_blocks, wl.layout_seed)
@@ -355,6 +384,7 @@ def main():
             "random_blocks": wl.random_blocks, "layout_seed": wl.layout_seed, "band_tokens": wl.band_tokens,
             "nonzero_tiles": stored_tiles, "layout_density": round(tiles / (B * H * (L // 64) ** 2), 5),
             **({"num_global": wl.num_global, "random_tokens": wl.random_tokens} if wl.token else {}),
+            **({"keep_blocks": wl.keep_blocks} if wl.adaptive else {}),
         },
         "eff_tflops": round(eff_tflops, 2),
         "pct_bf16_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),
@@ -380,10 +410,14 @@ def main():
         elif wl.token:
             olay = OL.make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
                                         wl.layout_seed)
+        elif wl.adaptive:
+            olay = None   # chosen from the data, per (batch, head)
         else:
             olay = OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                   wl.random_blocks, wl.layout_seed)
-        if backward:
+        if wl.adaptive:
+            result["cpu_baseline"] = cpu_baseline_adaptive(wl, inp, args.cpu_seconds)
+        elif backward:
             result["cpu_baseline"] = cpu_baseline_bwd(wl, inp, do_host, olay, args.cpu_seconds)
         else:
             result["cpu_baseline"] = cpu_baseline(wl, inp, olay, args.cpu_seconds)

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     BsattnError,
     Layout,
     backward,
+    bsattn_adaptive_select,
     bsattn_backward,
     bsattn_backward_workspace_size,
     bsattn_forward,
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     bsattn_layout_token_links,
     bsattn_layout_upload,
     bsattn_make_band_layout,
+    bsattn_make_adaptive_layout,
     bsattn_make_layout,
     bsattn_make_token_layout,
     bsattn_route_topk,

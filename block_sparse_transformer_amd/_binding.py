@@ -44,6 +44,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_make_band_layout.argtypes = [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_vp)]
     L.bsattn_make_token_layout.argtypes = [_c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_uint64,
                                            ctypes.POINTER(_c_vp)]
+    L.bsattn_make_adaptive_layout.argtypes = [_c_int, _c_int, _c_int, ctypes.POINTER(_c_vp)]
+    L.bsattn_adaptive_select.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                         ctypes.c_size_t, _c_vp]
     L.bsattn_layout_token_links.argtypes = [_c_vp, ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_int),
                                             ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_int)]
     L.bsattn_layout_csr.argtypes = [_c_vp, ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_i32p),
@@ -74,6 +77,7 @@ def lib() -> ctypes.CDLL:
     L.bsattn_last_error.argtypes = []
     L.bsattn_last_error.restype = ctypes.c_char_p
     for name in ("bsattn_make_layout", "bsattn_make_band_layout", "bsattn_make_token_layout",
+                 "bsattn_make_adaptive_layout", "bsattn_adaptive_select",
                  "bsattn_layout_token_links", "bsattn_layout_csr",
                  "bsattn_layout_tile_masks", "bsattn_layout_upload",
                  "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
@@ -158,6 +162,28 @@ def bsattn_make_token_layout(num_heads: int, seq_len: int, band_tokens: int, num
         num_heads, seq_len, band_tokens, num_global, random_tokens, ctypes.c_uint64(seed & ((1 << 64) - 1)),
         ctypes.byref(out)))
     return Layout(out.value, num_heads, seq_len, band_tokens=band_tokens)
+
+
+def bsattn_make_adaptive_layout(num_heads: int, seq_len: int, keep_blocks: int) -> Layout:
+    out = _c_vp()
+    _check("bsattn_make_adaptive_layout", lib().bsattn_make_adaptive_layout(num_heads, seq_len, keep_blocks,
+                                                                            ctypes.byref(out)))
+    lay = Layout(out.value, num_heads, seq_len)
+    lay.keep_blocks = keep_blocks
+    return lay
+
+
+def bsattn_adaptive_select(layout: Layout, q, k, workspace=None, stream=None):
+    """The kept key blocks [B, H, L/64, keep] (device int32) of an adaptive layout for q, k."""
+    import torch
+    B, H, L, D = q.shape
+    cols = torch.empty((B, H, L // 64, layout.keep_blocks), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(layout, q)
+    _check("bsattn_adaptive_select", lib().bsattn_adaptive_select(
+        layout.handle, B, H, L, D, q.data_ptr(), k.data_ptr(), cols.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+    return cols
 
 
 def bsattn_layout_token_links(layout: Layout) -> Tuple[np.ndarray, np.ndarray]:

@@ -28,6 +28,7 @@ SOURCES = [
     "kernels/fwd_f32.hip",
     "kernels/router.hip",
     "kernels/layout_build.hip",
+    "kernels/adaptive.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -60,12 +60,12 @@ void build_schedule(bsattn_layout* lay) {
             const int32_t b0 = lay->row_ptr[r], b1 = lay->row_ptr[r + 1];
             const int32_t len = b1 - b0;
             // token layouts merge every row: the merge adds the row's random tokens
-            if (len <= kChunkTiles && lay->kind != 2) {
+            if (len <= lay->chunk_tiles && lay->kind != 2) {
                 hi.push_back({r, b0, b1, -1, -1, 0, 0, 0});
                 continue;
             }
             int32_t nch, per;
-            split_row(len, &nch, &per);
+            split_row(len, &nch, &per, lay->chunk_tiles);
             const int32_t m = (int32_t)lay->merges.size();
             lay->merges.push_back({r, slot, nch, 0});
             const int32_t first = slot;
@@ -217,7 +217,7 @@ bsattn_status check_layout_dims(int32_t H, int32_t L, int32_t block, bool any_bl
 bsattn_status finish_layout(bsattn_layout* lay) {
     try {
         build_schedule(lay);
-        if (lay->kind != 2) build_bwd(lay);   // token layouts have no backward
+        if (lay->kind < 2) build_bwd(lay);   // token and adaptive layouts have no backward
     } catch (const std::bad_alloc&) {
         return fail(BSATTN_ERR_NO_MEMORY, "work list allocation failed");
     }
@@ -322,6 +322,24 @@ TokenWs token_workspace(const bsattn_layout* lay, int32_t B, int32_t D) {
     w.kg = align256(w.slots * slot_bytes(D));
     w.vg = w.kg + align256(gbytes);
     w.total = w.vg + align256(gbytes);
+    return w;
+}
+
+// Workspace of a forward over a content-adaptive layout: the partial slots of
+// split rows (fp32 O, then LSE), the block sums of q and k (fp64), the kept key
+// blocks [B*H][nb][keep], and the filled schedule tile entries (one per tile).
+struct AdaptiveWs {
+    size_t qs, ks, cols, live, total;
+};
+AdaptiveWs adaptive_workspace(const bsattn_layout* lay, int32_t B, int32_t D) {
+    AdaptiveWs w{};
+    const size_t G = (size_t)B * lay->H;
+    const int32_t keep = lay->rule.r;
+    w.qs = align256((size_t)B * lay->n_slots * slot_bytes(D));
+    w.ks = w.qs + align256(G * lay->nb * D * sizeof(double));
+    w.cols = w.ks + align256(G * lay->nb * D * sizeof(double));
+    w.live = w.cols + align256(G * lay->nb * keep * sizeof(int32_t));
+    w.total = w.live + align256(G * lay->nb * keep * sizeof(int32_t));
     return w;
 }
 
@@ -635,6 +653,66 @@ bsattn_status token_forward(const bsattn_layout* lay, int32_t B, int32_t D, cons
     return ok();
 }
 
+// Forward over a content-adaptive layout (bf16): block sums of q and k and
+// the kept key blocks of every query block (written to cols_out too when
+// given), the schedule's tile entries filled with them, then the attention
+// kernel and the merge of split rows.  With attend = false only the
+// selection runs (cols_out required).
+bsattn_status adaptive_run(const bsattn_layout* lay, int32_t B, int32_t D, const void* q, const void* k,
+                           const void* v, void* out, float* lse, float scale, int32_t* cols_out, bool attend,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const AdaptiveWs w = adaptive_workspace(lay, B, D);
+    if (!workspace || workspace_bytes < w.total)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", w.total, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    char* base = (char*)workspace;
+    const int32_t keep = lay->rule.r;
+    int32_t* cols = cols_out ? cols_out : (int32_t*)(base + w.cols);
+    hipError_t e = launch_adaptive_select(q, k, (double*)(base + w.qs), (double*)(base + w.ks), cols, B * lay->H,
+                                          lay->L, D, keep, stream);
+    if (e != hipSuccess) return hip_fail(e, "adaptive selection launch");
+    if (!attend) return ok();
+
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.ws_o = (float*)workspace;
+    a.ws_lse = a.ws_o + (size_t)B * lay->n_slots * kBlock * D;
+    a.items = lay->d_items;
+    a.merges = lay->d_merges;
+    a.col_idx = lay->d_col_idx;
+    a.n_items = (int32_t)lay->items.size();
+    a.n_merges = (int32_t)lay->merges.size();
+    a.items_per_head = lay->items_per_head;
+    a.B = B; a.H = lay->H; a.L = lay->L; a.nb = lay->nb; a.n_slots = lay->n_slots;
+    a.n_routed = 0; a.n_rt = 0; a.r_chunks = 1; a.r_chunk_tiles = 1; a.r_slot_base = 0;
+    a.band = -1;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    bsattn_layout::Sched sc{};
+    bsattn_status st = get_schedule(lay, B, D, 0, 1, 1, stream, &sc);
+    if (st != BSATTN_OK) return st;
+    int32_t* live = (int32_t*)(base + w.live);
+    const int32_t n_lists = kXcds * sc.n_bins;
+    e = launch_fill_tiles(sc.d_tiles, live, sc.d_units, sc.d_unit_ptr, sc.d_tile_ptr, n_lists, cols, lay->nb, keep,
+                          stream);
+    if (e != hipSuccess) return hip_fail(e, "tile fill launch");
+    a.n_bins = sc.n_bins;
+    a.units = sc.d_units;
+    a.unit_ptr = sc.d_unit_ptr;
+    a.tiles = live;
+    a.tile_ptr = sc.d_tile_ptr;
+    e = launch_fwd_bf16(a, D, MASK_NONE, stream, g_ev_before, g_ev_after);
+    if (e != hipSuccess) return hip_fail(e, "adaptive forward launch");
+    return ok();
+}
+
+bsattn_status adaptive_forward(const bsattn_layout* lay, int32_t B, int32_t D, const void* q, const void* k,
+                               const void* v, void* out, float* lse, float scale, int32_t* cols_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return adaptive_run(lay, B, D, q, k, v, out, lse, scale, cols_out, true, workspace, workspace_bytes, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -860,6 +938,62 @@ bsattn_status bsattn_make_token_layout(int32_t num_heads, int32_t seq_len, int32
     return finish_layout(lay);
 }
 
+bsattn_status bsattn_make_adaptive_layout(int32_t num_heads, int32_t seq_len, int32_t keep_blocks,
+                                          bsattn_layout** out) {
+    if (!out) return fail(BSATTN_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    bsattn_status st = check_layout_dims(num_heads, seq_len, kBlock);
+    if (st != BSATTN_OK) return st;
+    const int32_t nb = seq_len / kBlock;
+    if (nb > kMaxAdaptiveBlocks)
+        return fail(BSATTN_ERR_UNSUPPORTED, "seq_len/64 exceeds %d for an adaptive layout", kMaxAdaptiveBlocks);
+    if (keep_blocks < 1 || keep_blocks > nb)
+        return fail(BSATTN_ERR_INVALID_ARG, "keep_blocks must be in [1, seq_len/64] (got %d)", keep_blocks);
+    bsattn_layout* lay = new (std::nothrow) bsattn_layout();
+    if (!lay) return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    try {
+        lay->H = num_heads;
+        lay->L = seq_len;
+        lay->nb = nb;
+        lay->block = kBlock;
+        lay->kind = 3;
+        lay->rule.nb = nb;
+        lay->rule.r = keep_blocks;
+        // Every row has the same length, so the split decides the balance alone:
+        // chunks of up to 24 tiles keep the merge traffic down (each chunk is an
+        // fp32 partial) while leaving several units per wave list.
+        lay->chunk_tiles = 24;
+        // every row holds keep_blocks tiles; the stored columns are positions
+        // 0 .. keep_blocks - 1, replaced on the device by the chosen key blocks
+        const int32_t rows = num_heads * nb;
+        lay->row_ptr.assign((size_t)rows + 1, 0);
+        lay->col_idx.assign((size_t)rows * keep_blocks, 0);
+        for (int32_t r = 0; r < rows; ++r) {
+            lay->row_ptr[r + 1] = (r + 1) * keep_blocks;
+            for (int32_t p = 0; p < keep_blocks; ++p) lay->col_idx[(size_t)r * keep_blocks + p] = p;
+        }
+    } catch (const std::bad_alloc&) {
+        delete lay;
+        return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    }
+    *out = lay;
+    return finish_layout(lay);
+}
+
+bsattn_status bsattn_adaptive_select(const bsattn_layout* lay, int32_t B, int32_t H, int32_t L, int32_t D,
+                                     const void* q, const void* k, int32_t* selected_blocks, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (lay->kind != 3) return fail(BSATTN_ERR_INVALID_ARG, "not an adaptive layout");
+    if (!selected_blocks) return fail(BSATTN_ERR_INVALID_ARG, "selected_blocks is NULL");
+    if (B < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", B);
+    if (H != lay->H || L != lay->L) return fail(BSATTN_ERR_INVALID_ARG, "H, L do not match the layout");
+    if (D != 64 && D != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+    if (!q || !k) return fail(BSATTN_ERR_INVALID_ARG, "NULL tensor pointer");
+    return adaptive_run(lay, B, D, q, k, nullptr, nullptr, nullptr, 1.f, selected_blocks, false, workspace,
+                        workspace_bytes, stream);
+}
+
 bsattn_status bsattn_layout_token_links(const bsattn_layout* lay, const int32_t** global_tokens,
                                         int32_t* num_global, const int32_t** links, int32_t* links_per_row) {
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
@@ -991,6 +1125,10 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* lay, int32_t batch, int
         *bytes = token_workspace(lay, batch, head_dim).total;
         return ok();
     }
+    if (lay->kind == 3) {
+        *bytes = adaptive_workspace(lay, batch, head_dim).total;
+        return ok();
+    }
     size_t slots = (size_t)batch * lay->n_slots;
     int32_t n_rt = 0;
     if (num_routed > 0) {
@@ -1027,6 +1165,11 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
         if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "token layouts are bf16 only");
         if (key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "token layouts take no key padding");
         return token_forward(lay, B, D, q, k, v, out, lse, scale, workspace, workspace_bytes, stream);
+    }
+    if (lay->kind == 3) {
+        if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "adaptive layouts are bf16 only");
+        if (key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "adaptive layouts take no key padding");
+        return adaptive_forward(lay, B, D, q, k, v, out, lse, scale, nullptr, workspace, workspace_bytes, stream);
     }
     size_t need = 0;
     st = bsattn_workspace_size(lay, B, D, 0, &need);

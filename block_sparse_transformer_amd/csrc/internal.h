@@ -24,6 +24,7 @@ constexpr int kMaxChunks = 32;    // upper bound on the split of one row
 enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2, MASK_SUB = 3, MASK_TOKEN = 4 };
 constexpr int kMaxTokGlobal = 2048;   // global tokens of a token layout (their list lives in LDS)
 constexpr int kMaxLinks = 64;         // random tokens per row of a token layout
+constexpr int kMaxAdaptiveBlocks = 1024;   // key blocks per side of a content-adaptive layout
 
 // One workgroup's share: query block `row` (= h*nb + i) over key blocks
 // col_idx[col_begin, col_end).  slot < 0: the whole row, written straight to
@@ -57,8 +58,8 @@ constexpr int kTileLast = 1 << 30;
 
 // Chunking of a row of `len` tiles: number of chunks and tiles per chunk
 // (at most 64 tiles per chunk: a chunk's key-block list fits one wave's lanes).
-inline void split_row(int32_t len, int32_t* n_chunks, int32_t* per_chunk) {
-    int32_t per = kChunkTiles;
+inline void split_row(int32_t len, int32_t* n_chunks, int32_t* per_chunk, int32_t limit = kChunkTiles) {
+    int32_t per = limit;
     if ((len + per - 1) / per > kMaxChunks) per = (len + kMaxChunks - 1) / kMaxChunks;
     if (per > 64) per = 64;
     const int32_t n = (len + per - 1) / per;
@@ -166,6 +167,13 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s,
                            hipEvent_t before, hipEvent_t after);
 int fwd_bf16_ctas_per_cu(int head_dim);   // workgroups of the bf16 kernel resident per CU
+// content-adaptive layouts (kernels/adaptive.hip): block sums of q and k, then the
+// kept key blocks cols [G][nb][keep]; and the schedule's tile entries filled from cols
+hipError_t launch_adaptive_select(const void* q, const void* k, double* qs, double* ks, int32_t* cols, int G,
+                                  int L, int D, int keep, hipStream_t s);
+hipError_t launch_fill_tiles(const int32_t* skel, int32_t* live, const int4* units, const int32_t* unit_ptr,
+                             const int32_t* tile_ptr, int n_lists, const int32_t* cols, int nb, int keep,
+                             hipStream_t s);
 // token layouts: K/V rows of the global tokens -> kg/vg (zero past the last global token)
 hipError_t launch_gather_global(const FwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, const int32_t* row_ptr, int head_dim, int mask,
@@ -190,7 +198,8 @@ hipError_t launch_layout_build(const RowRule& rule, int kind, int32_t H, int32_t
 // The opaque layout handle of the C ABI.
 struct bsattn_layout {
     int32_t H = 0, L = 0, nb = 0, block = 0;
-    int32_t kind = 0;           // 0: window/global/random rule, 1: token band, 2: token pattern
+    int32_t kind = 0;           // 0: window/global/random rule, 1: token band, 2: token pattern,
+                                // 3: content-adaptive (key blocks chosen per call from q and k)
     int32_t band_tokens = -1;
     bsattn::RowRule rule{};
     std::vector<int32_t> row_ptr, col_idx;
@@ -209,6 +218,7 @@ struct bsattn_layout {
     std::vector<bsattn::WorkItem> items;
     std::vector<bsattn::MergeItem> merges;
     int32_t n_slots = 0;        // partial slots per batch entry
+    int32_t chunk_tiles = bsattn::kChunkTiles;   // rows longer than this are split (into even chunks)
     // device copy (after upload)
     int device = -1;
     int32_t items_per_head = 0;

@@ -136,6 +136,37 @@ bsattn_status bsattn_make_token_layout(int32_t num_heads, int32_t seq_len, int32
                                        int32_t num_global, int32_t random_tokens, uint64_t seed,
                                        bsattn_layout** out);
 
+/* A content-adaptive block layout: its key blocks are chosen on the device
+ * from q and k at every bsattn_forward call (Adaptive Sparse Transformer
+ * page, importance evaluation: score candidate positions and keep the highest
+ * r% per query; here the candidates are 64-token key blocks, SQA page
+ * sections 3.1 and 5).  For each (b, h):
+ *   qs[i, d] = sum over u = 0..63 of q[64 i + u, d], added in that order in fp64
+ *   (ks likewise from k); S[i, j] = sum over d = 0..D-1 of qs[i, d] * ks[j, d],
+ *   each product rounded and added in order of d in fp64, no fused
+ *   multiply-add; query block i attends the keep_blocks key blocks of highest
+ *   S[i, j], ties to the lower j.  NaN scores give an unspecified (but valid,
+ *   distinct) choice.
+ *   num_heads     H >= 1.
+ *   seq_len       L, a positive multiple of 64, L/64 <= 1024.
+ *   keep_blocks   in [1, L/64]; floor(r L/64) keeps the fraction r.
+ *   out           receives the new layout (caller frees with bsattn_layout_destroy).
+ * Host only.  The stored CSR holds, per row, the positions 0 .. keep_blocks-1
+ * (the blocks themselves are per call).  bsattn_forward on it is bf16 only
+ * and takes no key padding; its workspace (bsattn_workspace_size) also holds
+ * the block sums and the chosen blocks.  No backward. */
+bsattn_status bsattn_make_adaptive_layout(int32_t num_heads, int32_t seq_len, int32_t keep_blocks,
+                                          bsattn_layout** out);
+
+/* The selection step of a forward over an adaptive layout alone: writes the
+ * kept key blocks of every query block, ascending, to selected_blocks (device
+ * int32 [B, H, L/64, keep_blocks]).  q, k device bf16 [B, H, L, D], D in
+ * {64, 128}; workspace as for bsattn_forward.  Enqueued on `stream`. */
+bsattn_status bsattn_adaptive_select(const bsattn_layout* layout, int32_t batch, int32_t num_heads,
+                                     int32_t seq_len, int32_t head_dim, const void* q, const void* k,
+                                     int32_t* selected_blocks, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* Borrowed host view of a token layout (valid until destroy): the global
  * tokens [num_global], ascending, and the random tokens [H][L][links_per_row],
  * each row ascending and padded with -1.  INVALID_ARG for other layouts.  Any
@@ -198,7 +229,9 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* layout, int32_t batch,
  *                  BigBird pattern, also bf16 only without key padding: the
  *                  call then runs a gather of the global tokens' K/V rows,
  *                  the attention kernel and a merge that adds every row's
- *                  random tokens.
+ *                  random tokens.  An adaptive layout
+ *                  (bsattn_make_adaptive_layout) chooses its key blocks from
+ *                  q and k first, in the same call.
  *   dtype          element type of q, k, v and out.
  *   batch..head_dim  B >= 1, H, L as in the layout, D in {64, 128}.
  *   q, k, v        device [B, H, L, D], contiguous, 16-byte aligned.

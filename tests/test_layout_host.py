@@ -17,7 +17,7 @@ def _both(H, L, w, G, r, seed):
 
 
 @pytest.mark.parametrize("name", [n for n, wl in WORKLOADS.items()
-                                  if not (wl.routed or wl.band or wl.token) and wl.block == 64])
+                                  if not (wl.routed or wl.band or wl.token or wl.adaptive) and wl.block == 64])
 def test_workload_layouts_bit_exact(name):
     wl = WORKLOADS[name]
     (rp, ci), (orp, oci) = _both(wl.heads, wl.seq_len, wl.window_blocks, wl.global_blocks,
@@ -201,3 +201,17 @@ def test_token_layout_rejects():
                  (0, 256, 3, 2, 2, 0), (1, 8192, 3, 2049, 2, 0)]:
         with pytest.raises(RuntimeError):
             bs.bsattn_make_token_layout(*args)
+
+
+def test_adaptive_layout_skeleton():
+    lay = bs.bsattn_make_adaptive_layout(3, 640, 4)
+    rp, ci = bs.bsattn_layout_csr(lay)
+    assert rp.tolist() == [4 * r for r in range(31)]
+    assert ci.tolist() == [0, 1, 2, 3] * 30
+    assert bs.bsattn_workspace_size(lay, 2, 64) > 2 * 3 * 10 * 64 * 8 * 2
+
+
+def test_adaptive_layout_rejects():
+    for args in [(1, 640, 0), (1, 640, 11), (1, 100, 1), (0, 640, 1), (1, 64 * 1025, 1)]:
+        with pytest.raises(RuntimeError):
+            bs.bsattn_make_adaptive_layout(*args)

@@ -56,6 +56,7 @@ class Workload:
     token: bool = False             # token-granular BigBird pattern (window band_tokens, below)
     num_global: int = 0             # token pattern: linspace global tokens
     random_tokens: int = 0          # token pattern: random tokens per row
+    keep_blocks: int = 0            # > 0: content-adaptive layout keeping this many key blocks per row
 
     @property
     def routed(self) -> bool:
@@ -65,6 +66,10 @@ class Workload:
     def band(self) -> bool:
         """A token-band layout without routed rows (the plain forward on a band layout)."""
         return self.band_tokens > 0 and not self.routed and not self.token
+
+    @property
+    def adaptive(self) -> bool:
+        return self.keep_blocks > 0
 
     @property
     def num_blocks(self) -> int:
@@ -112,6 +117,11 @@ WORKLOADS = {
     "bigbird-tok-L8192": Workload(
         name="bigbird-tok-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
         data_seed=8, token=True, band_tokens=64, num_global=8, random_tokens=8, layout_seed=8),
+    # Content-adaptive layout: every query block keeps the 30% of key blocks (the Adaptive page's
+    # r = 0.3) with the highest pooled score, chosen on the device from Q and K.
+    "adaptive-L8192": Workload(
+        name="adaptive-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
+        data_seed=9, keep_blocks=38),
     # Token-granular sliding window |t - s| <= 256 (the BigBird page's 64-256 token windows)
     # at the throughput shape: a band layout through the plain forward.
     "band256-L8192": Workload(
