@@ -421,12 +421,22 @@ def forward_routed(q, k, v, band_layout: Layout, routed_rows, scale: Optional[fl
     return out, lse
 
 
+# hipEventDisableSystemFence: the event only takes a timestamp; recording it does
+# not write back and invalidate the caches (HIP documents the flag for events used
+# only to measure time).  Readers synchronise the device before reading the times.
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 class HipEvents:
-    """Raw hipEvent_t pairs from the HIP runtime, for timing one kernel on a given stream."""
+    """Raw hipEvent_t pairs from the HIP runtime, for timing one kernel on a given stream.
+
+    The events are timing-only (no system-scope fence when recorded), so that
+    recording them between kernels does not add cache writebacks to the timed
+    work; synchronise the device before calling elapsed_ms."""
 
     def __init__(self, n: int):
         self._hip = ctypes.CDLL("libamdhip64.so")
-        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(_c_vp)]
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(_c_vp), ctypes.c_uint]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _c_vp, _c_vp]
         self._hip.hipEventSynchronize.argtypes = [_c_vp]
         self._hip.hipEventDestroy.argtypes = [_c_vp]
@@ -434,8 +444,8 @@ class HipEvents:
         for _ in range(n):
             for lst in (self.before, self.after):
                 e = _c_vp()
-                if self._hip.hipEventCreate(ctypes.byref(e)) != 0:
-                    raise RuntimeError("hipEventCreate failed")
+                if self._hip.hipEventCreateWithFlags(ctypes.byref(e), _HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
                 lst.append(e.value)
 
     def elapsed_ms(self, i: int) -> float:

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <functional>
+#include <map>
 #include <queue>
 #include <cstdarg>
 #include <cstdio>
@@ -189,6 +190,7 @@ void free_device(bsattn_layout* lay) {
             (void)hipFree(sc.d_unit_ptr);
             (void)hipFree(sc.d_tiles);
             (void)hipFree(sc.d_tile_ptr);
+            (void)hipFree(sc.d_wg_merge);
         }
         free_bwd_device(lay);
         if (cur >= 0 && cur != lay->device) (void)hipSetDevice(cur);
@@ -381,6 +383,13 @@ int device_capacity(int dev, int32_t D, int* cus_out = nullptr) {
 // max_bin_units units and max_bin_tiles tiles per bin.
 bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32_t nru, int32_t rct,
                            int32_t r_chunks, hipStream_t stream, bsattn_layout::Sched* out) {
+    // a built schedule is looked up before anything else: this runs on every call
+    std::lock_guard<std::mutex> guard(*lay->sched_mu);
+    for (const auto& sc : lay->scheds)
+        if (sc.batch == B && sc.head_dim == D && sc.nru == nru && sc.rct == rct) {
+            *out = sc;
+            return BSATTN_OK;
+        }
     const int32_t ipH = lay->items_per_head;
     const int64_t G = (int64_t)B * lay->H;
     auto routed_len = [&](int32_t v) {
@@ -425,20 +434,21 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
     if (nb64 * kXcds >= ((int64_t)1 << 31)) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
     int32_t n_bins = (int32_t)std::max<int64_t>(nb64, 1);
 
-    std::lock_guard<std::mutex> guard(*lay->sched_mu);
-    for (const auto& sc : lay->scheds)
-        if (sc.batch == B && sc.head_dim == D && sc.nru == nru && sc.rct == rct) {
-            *out = sc;
-            return BSATTN_OK;
-        }
     std::vector<int4> units;
-    std::vector<int32_t> unit_ptr, tiles, tile_ptr;
+    std::vector<int32_t> unit_ptr, tiles, tile_ptr, wg_merge;
+    // Fused merges (D = 64): every split row has kQWaves chunks and no routed
+    // units; each such row then gets a workgroup of its own (one chunk per
+    // wave list), which merges the row at its end.
+    bool fuse = per_wave && nru == 0 && !lay->merges.empty() && lay->kind != 2;
+    for (const auto& mi : lay->merges) fuse = fuse && mi.n_chunks == kQWaves;
     // pack every XCD's units into nbins bins; false if some bin overflows its lists
     auto pack = [&](int32_t nbins) -> bool {
         units.clear();
         tiles.clear();
         unit_ptr.assign(1, 0);
         tile_ptr.assign(1, 0);
+        const bool fuse_here = fuse && nbins == kQWaves * cus_per_xcd;
+        wg_merge.assign(fuse_here ? (size_t)kXcds * cus_per_xcd : 0, -1);
         for (int32_t x = 0; x < kXcds; ++x) {
             const auto& v = xu[(size_t)x];
             std::vector<std::vector<int32_t>> bins((size_t)nbins);
@@ -466,8 +476,29 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
                 // CU (workgroups of one CU, measured dispatch order; or the waves of
                 // one workgroup), and they share its SIMDs: balance the work per CU
                 // first, then split each CU's share -- in pairs of equal load when
-                // the waves of a SIMD pair up (lists 2s and 2s + 1).
-                const auto per_cu = lpt(order, cus_per_xcd);
+                // the waves of a SIMD pair up (lists 2s and 2s + 1).  With fused
+                // merges the first CUs each take the kQWaves chunks of one split row.
+                std::vector<std::vector<int32_t>> per_cu;
+                if (fuse_here) {
+                    std::map<std::pair<int32_t, int32_t>, std::vector<int32_t>> rows;   // (g, merge) -> chunks
+                    std::vector<int32_t> rest;
+                    for (int32_t u : order) {
+                        const Unit& un = v[(size_t)u];
+                        const WorkItem& wi = lay->items[(size_t)(un.g % lay->H) * ipH + un.id];
+                        if (wi.merge >= 0) rows[{un.g, wi.merge}].push_back(u);
+                        else rest.push_back(u);
+                    }
+                    if ((int32_t)rows.size() >= cus_per_xcd) return false;   // no room: pack without fusion
+                    for (const auto& kv : rows) {
+                        wg_merge[(size_t)x * cus_per_xcd + per_cu.size()] =
+                            (kv.first.first / lay->H) * (int32_t)lay->merges.size() + kv.first.second;
+                        per_cu.push_back(kv.second);
+                    }
+                    const auto others = lpt(rest, cus_per_xcd - (int32_t)per_cu.size());
+                    per_cu.insert(per_cu.end(), others.begin(), others.end());
+                } else {
+                    per_cu = lpt(order, cus_per_xcd);
+                }
                 const int32_t per = nbins / cus_per_xcd;
                 const bool pairs = per_wave && per % 2 == 0;
                 for (int32_t c = 0; c < cus_per_xcd; ++c) {
@@ -520,32 +551,37 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
         }
         return true;
     };
+    if (fuse && !pack(n_bins)) fuse = false;   // fusion did not fit: the merge kernel merges
     while (!pack(n_bins)) {
         if ((size_t)n_bins >= max_units) return fail(BSATTN_ERR_UNSUPPORTED, "a unit exceeds the per-workgroup tile list");
         const int64_t nn = std::min<int64_t>((int64_t)max_units, (int64_t)n_bins * 2);
         n_bins = (int32_t)((nn + lists_per_wg - 1) / lists_per_wg * lists_per_wg);
     }
+    if (wg_merge.empty()) fuse = false;
     if (units.empty()) units.push_back(make_int4(0, -1, 0, 0));
     if (tiles.empty()) tiles.push_back(0);
-    bsattn_layout::Sched sc{B, D, n_bins, nru, rct, nullptr, nullptr, nullptr, nullptr};
-    void* p[4] = {nullptr, nullptr, nullptr, nullptr};
-    const void* src[4] = {units.data(), unit_ptr.data(), tiles.data(), tile_ptr.data()};
-    const size_t sz[4] = {units.size() * sizeof(int4), unit_ptr.size() * sizeof(int32_t),
-                          tiles.size() * sizeof(int32_t), tile_ptr.size() * sizeof(int32_t)};
+    bsattn_layout::Sched sc{B, D, n_bins, nru, rct, nullptr, nullptr, nullptr, nullptr, nullptr};
+    void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    const void* src[5] = {units.data(), unit_ptr.data(), tiles.data(), tile_ptr.data(), wg_merge.data()};
+    const size_t sz[5] = {units.size() * sizeof(int4), unit_ptr.size() * sizeof(int32_t),
+                          tiles.size() * sizeof(int32_t), tile_ptr.size() * sizeof(int32_t),
+                          fuse ? wg_merge.size() * sizeof(int32_t) : 0};
     hipError_t e = hipSuccess;
-    for (int a = 0; a < 4 && e == hipSuccess; ++a) {
+    for (int a = 0; a < 5 && e == hipSuccess; ++a) {
+        if (sz[a] == 0) continue;
         e = hipMalloc(&p[a], sz[a]);
         if (e == hipSuccess) e = hipMemcpyAsync(p[a], src[a], sz[a], hipMemcpyHostToDevice, stream);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) {
-        for (int a = 0; a < 4; ++a) (void)hipFree(p[a]);
+        for (int a = 0; a < 5; ++a) (void)hipFree(p[a]);
         return fail(BSATTN_ERR_NO_MEMORY, "schedule upload: %s", hipGetErrorString(e));
     }
     sc.d_units = (int4*)p[0];
     sc.d_unit_ptr = (int32_t*)p[1];
     sc.d_tiles = (int32_t*)p[2];
     sc.d_tile_ptr = (int32_t*)p[3];
+    sc.d_wg_merge = (int32_t*)p[4];
     lay->scheds.push_back(sc);
     *out = sc;
     return BSATTN_OK;
@@ -1216,6 +1252,8 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     a.unit_ptr = sc.d_unit_ptr;
     a.tiles = sc.d_tiles;
     a.tile_ptr = sc.d_tile_ptr;
+    // padding can empty a wave's list, and a workgroup that merges needs all its waves
+    a.wg_merge = mask == MASK_PAD ? nullptr : sc.d_wg_merge;
     e = launch_fwd_bf16(a, D, mask, stream, g_ev_before, g_ev_after);
     if (e != hipSuccess) return hip_fail(e, "bf16 forward launch");
     return ok();
@@ -1369,10 +1407,8 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
     a.items = bw.d_k_items; a.n_items = (int32_t)bw.k_items.size(); a.items_per_head = bw.k_per_head;
     a.sums = bw.d_k_sums; a.n_sums = (int32_t)bw.k_sums.size();
     a.idx = bw.d_k_idx; a.idx_sub = bw.d_k_sub; a.n_slots = bw.n_kslots;
-    if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    e = launch_bwd_dkdv(a, D, mask, stream);
+    e = launch_bwd_dkdv(a, D, mask, stream, g_ev_before, g_ev_after);
     if (e != hipSuccess) return hip_fail(e, "backward dK/dV launch");
-    if (g_ev_after && (e = hipEventRecord(g_ev_after, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 1, stream)) != hipSuccess)
         return hip_fail(e, "backward dK/dV sum launch");
     return ok();

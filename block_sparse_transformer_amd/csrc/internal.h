@@ -105,6 +105,9 @@ struct FwdArgs {
     int32_t r_chunks;         // chunks per routed tile
     int32_t r_chunk_tiles;    // key blocks per chunk
     int32_t r_slot_base;      // first workspace slot of routed partials
+    // D = 64 kernel: per workgroup, the split row it merges after its lists
+    // (b * n_merges + m, or -1); nullptr when the merge kernel merges every row
+    const int32_t* wg_merge;
     int32_t band;             // token band of non-routed rows (MASK_BAND, MASK_TOKEN)
     int32_t routed_stride;    // routed_rows entries between (b, h) groups (0: one list shared by all)
     // token layouts (MASK_TOKEN): key block j >= nb is gathered tile j - nb of
@@ -182,7 +185,8 @@ hipError_t launch_route_topk(const void* q, const float* w, int32_t B, int32_t H
                              int32_t D, int32_t k, int32_t* out, hipStream_t s);
 hipError_t launch_bwd_delta(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s);
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before = nullptr,
+                           hipEvent_t after = nullptr);
 // sum split partials into the bf16 output(s): which = 0 dQ, 1 dK and dV
 hipError_t launch_bwd_sum(const BwdArgs& a, int head_dim, int which, hipStream_t s);
 // attention layer (kernels/layer.hip)
@@ -235,6 +239,11 @@ struct bsattn_layout {
         int32_t* d_unit_ptr;
         int32_t* d_tiles;
         int32_t* d_tile_ptr;
+        // D = 64 with every split row in 8 chunks: the workgroup (XCD x, index c)
+        // that holds a row's 8 chunks merges it itself; d_wg_merge[x * (n_bins /
+        // kQWaves) + c] = b * n_merges + m for such a workgroup, -1 otherwise.
+        // nullptr: rows are merged by the merge kernel.
+        int32_t* d_wg_merge;
     };
     mutable std::vector<Sched> scheds;
     mutable std::unique_ptr<std::mutex> sched_mu{new std::mutex};

@@ -37,6 +37,7 @@
 //    queries, each with its own LSE and delta.  They enter as the initial
 //    accumulator of the score and dP products (-LSE/scale and -delta per
 //    row), so no per-register statistics have to be held.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -447,11 +448,12 @@ hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
 }
 
 template <int D, int MASK>
-hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s, hipEvent_t before, hipEvent_t after) {
     const int64_t groups = (int64_t)a.B * a.H;
     const int64_t grid = (groups + kXcds - 1) / kXcds * kXcds * a.items_per_head;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK>), dim3((unsigned)grid), dim3(kBT), 0, s, a);
+    // given events, the dispatch records the kernel's own start and stop
+    hipExtLaunchKernelGGL((bwd_dkdv_kernel<D, MASK>), dim3((unsigned)grid), dim3(kBT), 0, s, before, after, 0, a);
     return hipGetLastError();
 }
 
@@ -476,14 +478,15 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s
                               : launch_dq_t<128, MASK_NONE>(a, s);
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s) {
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
+                           hipEvent_t after) {
     if (head_dim == 64)
-        return mask == MASK_PAD   ? launch_dkdv_t<64, MASK_PAD>(a, s)
-             : mask == MASK_SUB   ? launch_dkdv_t<64, MASK_SUB>(a, s)
-                                  : launch_dkdv_t<64, MASK_NONE>(a, s);
-    return mask == MASK_PAD   ? launch_dkdv_t<128, MASK_PAD>(a, s)
-         : mask == MASK_SUB   ? launch_dkdv_t<128, MASK_SUB>(a, s)
-                              : launch_dkdv_t<128, MASK_NONE>(a, s);
+        return mask == MASK_PAD   ? launch_dkdv_t<64, MASK_PAD>(a, s, before, after)
+             : mask == MASK_SUB   ? launch_dkdv_t<64, MASK_SUB>(a, s, before, after)
+                                  : launch_dkdv_t<64, MASK_NONE>(a, s, before, after);
+    return mask == MASK_PAD   ? launch_dkdv_t<128, MASK_PAD>(a, s, before, after)
+         : mask == MASK_SUB   ? launch_dkdv_t<128, MASK_SUB>(a, s, before, after)
+                              : launch_dkdv_t<128, MASK_NONE>(a, s, before, after);
 }
 
 hipError_t launch_bwd_sum(const BwdArgs& a, int head_dim, int which, hipStream_t s) {

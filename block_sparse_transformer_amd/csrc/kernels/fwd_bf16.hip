@@ -50,6 +50,7 @@
 //    runs on XCD i%8, and the kernel maps it to the (i/8)-th unit of the
 //    (batch, head) groups assigned to that XCD, so every group's K/V is read
 //    by one XCD and stays in its L2.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -1155,6 +1156,63 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (pend) finish();
     if (lane == 0) left[wv] = 0;
     wait_vmcnt<0>();
+
+    // A workgroup whose eight lists were the eight chunks of one split row
+    // merges that row here, once every chunk's partial is stored: wave w takes
+    // rows 8w .. 8w + 7, eight lanes per row and eight columns per lane, and
+    // combines the chunks by log-sum-exp as merge_bf16_kernel does.
+    if (a.wg_merge) {
+        const int mu = a.wg_merge[x * (a.n_bins / kQWaves) + blockIdx.x / kXcds];
+        if (mu >= 0) {
+            __syncthreads();
+            // every lane-derived value of this tail is computed here, from a copy
+            // the compiler cannot see through: nothing is hoisted above the
+            // main loop to stay live (and spill) across it
+            int tl = (int)threadIdx.x;
+            asm volatile("" : "+v"(tl));
+            const int tw = tl >> 6, tlane = tl & 63;
+            const int b = mu / a.n_merges;
+            const MergeItem mi = a.merges[mu % a.n_merges];
+            const size_t bh = (size_t)b * a.H + mi.row / a.nb;
+            const int r = 8 * tw + (tlane >> 3), part = tlane & 7;
+            const int t = (mi.row % a.nb) * 64 + r;
+            const size_t first = (size_t)b * a.n_slots + mi.first_slot;
+            float lsev[kQWaves];
+            float4 p0[kQWaves], p1[kQWaves];
+#pragma unroll
+            for (int c = 0; c < kQWaves; ++c) {
+                lsev[c] = a.ws_lse[(first + c) * 64 + r];
+                const float* src = a.ws_o + ((first + c) * 64 + r) * D + part * 8;
+                p0[c] = *(const float4*)src;
+                p1[c] = *(const float4*)(src + 4);
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < kQWaves; ++c) mx = __builtin_fmaxf(mx, lsev[c]);
+            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * 8;
+            if (mx == -INFINITY) {
+                *(u32x4_t*)orow = u32x4_t{0u, 0u, 0u, 0u};
+                if (part == 0) a.lse[bh * a.L + t] = -INFINITY;
+            } else {
+                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
+#pragma unroll
+                for (int c = 0; c < kQWaves; ++c) {
+                    const float w = expf(lsev[c] - mx);
+                    wsum += w;
+                    acc[0] += w * p0[c].x; acc[1] += w * p0[c].y; acc[2] += w * p0[c].z; acc[3] += w * p0[c].w;
+                    acc[4] += w * p1[c].x; acc[5] += w * p1[c].y; acc[6] += w * p1[c].z; acc[7] += w * p1[c].w;
+                }
+                const float inv = 1.f / wsum;
+                u32x4_t o4;
+                o4.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+                o4.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+                o4.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+                o4.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+                *(u32x4_t*)orow = o4;
+                if (part == 0) a.lse[bh * a.L + t] = mx + logf(wsum);
+            }
+        }
+    }
 }
 
 // Merge of a split row (global rows, routed tiles): the chunks of the row
@@ -1460,21 +1518,25 @@ __global__ __launch_bounds__(256) void gather_global_kernel(const FwdArgs a, uin
     *(u32x4_t*)(vg + row * D + col) = vv;
 }
 
+// The attention kernels are launched with hipExtLaunchKernelGGL: given events,
+// the dispatch itself records the kernel's start and stop (no separate marker
+// packets between kernels, which would add to the time they measure).
 template <int D, int MASK>
-hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s, hipEvent_t before, hipEvent_t after) {
     const int64_t grid = (int64_t)kXcds * a.n_bins;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipExtLaunchKernelGGL((fwd_bf16_kernel<D, MASK>), dim3((unsigned)grid), dim3(kThreads), 0, s, before, after, 0, a);
     return hipGetLastError();
 }
 
 template <int MASK>
-hipError_t launch_d64(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_d64(const FwdArgs& a, hipStream_t s, hipEvent_t before, hipEvent_t after) {
     // kQWaves lists (bins) per workgroup
     if (a.n_bins % kQWaves != 0) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)kXcds * (a.n_bins / kQWaves);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_bf16_d64_kernel<MASK>), dim3((unsigned)grid), dim3(kQThreads), 0, s, a);
+    hipExtLaunchKernelGGL((fwd_bf16_d64_kernel<MASK>), dim3((unsigned)grid), dim3(kQThreads), 0, s, before, after, 0,
+                          a);
     return hipGetLastError();
 }
 
@@ -1494,24 +1556,23 @@ int fwd_bf16_ctas_per_cu(int head_dim) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
                            hipEvent_t after) {
     hipError_t e;
-    if (before && (e = hipEventRecord(before, s)) != hipSuccess) return e;
     if (head_dim == 64) {
-        e = mask == MASK_PAD   ? launch_d64<MASK_PAD>(a, s)
-          : mask == MASK_BAND  ? launch_d64<MASK_BAND>(a, s)
-          : mask == MASK_SUB   ? launch_d64<MASK_SUB>(a, s)
-          : mask == MASK_TOKEN ? launch_d64<MASK_TOKEN>(a, s)
-                               : launch_d64<MASK_NONE>(a, s);
+        e = mask == MASK_PAD   ? launch_d64<MASK_PAD>(a, s, before, after)
+          : mask == MASK_BAND  ? launch_d64<MASK_BAND>(a, s, before, after)
+          : mask == MASK_SUB   ? launch_d64<MASK_SUB>(a, s, before, after)
+          : mask == MASK_TOKEN ? launch_d64<MASK_TOKEN>(a, s, before, after)
+                               : launch_d64<MASK_NONE>(a, s, before, after);
     } else {
-        e = mask == MASK_PAD   ? launch_fwd_t<128, MASK_PAD>(a, s)
-          : mask == MASK_BAND  ? launch_fwd_t<128, MASK_BAND>(a, s)
-          : mask == MASK_SUB   ? launch_fwd_t<128, MASK_SUB>(a, s)
-          : mask == MASK_TOKEN ? launch_fwd_t<128, MASK_TOKEN>(a, s)
-                               : launch_fwd_t<128, MASK_NONE>(a, s);
+        e = mask == MASK_PAD   ? launch_fwd_t<128, MASK_PAD>(a, s, before, after)
+          : mask == MASK_BAND  ? launch_fwd_t<128, MASK_BAND>(a, s, before, after)
+          : mask == MASK_SUB   ? launch_fwd_t<128, MASK_SUB>(a, s, before, after)
+          : mask == MASK_TOKEN ? launch_fwd_t<128, MASK_TOKEN>(a, s, before, after)
+                               : launch_fwd_t<128, MASK_NONE>(a, s, before, after);
     }
     if (e != hipSuccess) return e;
-    if (after && (e = hipEventRecord(after, s)) != hipSuccess) return e;
     const int64_t units = (int64_t)a.B * a.n_merges + (a.n_routed > 0 ? (int64_t)a.B * a.H * a.n_rt : 0);
     if (units == 0) return hipSuccess;
+    if (head_dim == 64 && a.wg_merge && a.n_routed == 0) return hipSuccess;   // merged inside the kernel
     if (mask == MASK_TOKEN) {
         // the global rows (routed units) by the plain merge, every other row with its random tokens
         FwdArgs g = a;

@@ -499,3 +499,20 @@ def test_token_pattern_rejects():
     o, l = bs.forward(inp["q"], inp["k"], inp["v"], lay, scale=wl.scale)
     with pytest.raises(bs.BsattnError):
         bs.backward(inp["q"], inp["k"], inp["v"], o, l, o, lay, scale=wl.scale)
+
+
+def test_global_rows_merged_in_kernel():
+    """At 128 blocks a side a global row splits into 8 chunks of 16 tiles; the D = 64
+    schedule gives each such row a workgroup whose 8 waves hold its chunks and merge it
+    at their end.  Every row of both global blocks is compared, plus rows around them."""
+    wl = WORKLOADS["bigbird-L8192"].with_(batch=1, heads=2)
+    _say("in-kernel merge of global rows", wl)
+    inp = make_inputs(wl)
+    lay, olay = _layouts(wl)
+    o, l = _run(wl, inp, lay)
+    ts = list(range(0, 64)) + list(range(wl.seq_len - 64, wl.seq_len)) + [64, 65, 127, 4000, 8127]
+    rows = [(0, h, t) for h in range(wl.heads) for t in ts]
+    ro, rl = OA.attention_rows(inp["q"], inp["k"], inp["v"], olay, wl.scale, rows)
+    go = np.stack([o[b, h, t] for b, h, t in rows])
+    gl = np.array([l[b, h, t] for b, h, t in rows])
+    _compare(go, gl, ro, rl, wl.dtype, "global rows merged in kernel")
