@@ -1394,9 +1394,9 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
     a.scale_log2 = scale * 1.4426950408889634f;
     const int mask = sub ? MASK_SUB : (key_valid_len ? MASK_PAD : MASK_NONE);
 
-    hipError_t e = launch_bwd_delta(a, D, stream);
-    if (e != hipSuccess) return hip_fail(e, "backward delta launch");
-
+    // delta = rowsum(dO * O) is computed by the dQ pass (every query row has an
+    // item there) and read by the dK/dV pass after it
+    hipError_t e;
     a.items = bw.d_q_items; a.n_items = (int32_t)bw.q_items.size(); a.items_per_head = bw.q_per_head;
     a.sums = bw.d_q_sums; a.n_sums = (int32_t)bw.q_sums.size();
     a.idx = lay->d_col_idx; a.idx_sub = lay->d_col_sub; a.n_slots = bw.n_qslots;

@@ -24,6 +24,8 @@
 //    a key block (the layout transposed on the host).  Rows and columns
 //    longer than 16 blocks (global rows and columns) are split into chunks;
 //    each chunk writes an fp32 partial and a small launch adds them up.
+//  * delta = rowsum(dO * O) is formed in the dQ pass, from the dO half-rows
+//    its lanes already load, and stored for the dK/dV pass that follows.
 //  * All products are v_mfma_f32_32x32x16_bf16 with the output transposed so
 //    that a lane owns one row of the pass's own block (a query in the dQ pass,
 //    a key in the dK/dV pass) and holds 16 entries of the other side in its
@@ -172,30 +174,6 @@ __device__ __forceinline__ bool take_item(const BwdArgs& a, int& b, int& h, int&
     return true;
 }
 
-// delta[row] = sum_d dO[row, d] * O[row, d].  D/8 lanes per row, 16 bytes
-// each, so a wave reads whole rows contiguously; reduced with lane shuffles.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdArgs a) {
-    constexpr int LPR = D / 8;   // lanes per row
-    const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t row = gid / LPR;
-    const int c = (int)(gid % LPR);
-    const size_t rows = (size_t)a.B * a.H * a.L;
-    float acc = 0.f;
-    if (row < rows) {
-        const u32x4_t uo = *(const u32x4_t*)((const uint16_t*)a.out + row * D + 8 * c);
-        const u32x4_t ug = *(const u32x4_t*)((const uint16_t*)a.dout + row * D + 8 * c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc = fmaf(bf16_to_f32(uo[e] & 0xffffu), bf16_to_f32(ug[e] & 0xffffu), acc);
-            acc = fmaf(bf16_to_f32(uo[e] >> 16), bf16_to_f32(ug[e] >> 16), acc);
-        }
-    }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (row < rows && c == 0) a.delta[row] = acc;
-}
-
 // dQ pass: workgroup = (item, batch entry); wave w owns queries 32w .. 32w + 31
 // of query block `blk`, each lane one query.
 template <int D, int MASK>
@@ -214,14 +192,17 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
     const int t = blk * 64 + wave * 32 + ql;
 
     bf16x8_t qf[NC], dof[NC];
+    u32x4_t ug[NC], uo[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        qf[c] = as_bf16x8(*(const u32x4_t*)((const uint16_t*)a.q + gbase + (size_t)t * D + 16 * c + 8 * hh));
-        dof[c] = as_bf16x8(*(const u32x4_t*)((const uint16_t*)a.dout + gbase + (size_t)t * D + 16 * c + 8 * hh));
+        const size_t off = gbase + (size_t)t * D + 16 * c + 8 * hh;
+        qf[c] = as_bf16x8(*(const u32x4_t*)((const uint16_t*)a.q + off));
+        ug[c] = *(const u32x4_t*)((const uint16_t*)a.dout + off);
+        uo[c] = *(const u32x4_t*)((const uint16_t*)a.out + off);
+        dof[c] = as_bf16x8(ug[c]);
     }
     const float lse = a.lse[grp * a.L + t];
     const float nl2 = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
-    const float dl = a.delta[grp * a.L + t];
     const int valid = MASK == MASK_PAD ? min(max(a.valid_len[b], 0), a.L) : a.L;
     const float c2 = a.scale_log2;
 
@@ -237,6 +218,20 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
         fetch_tile<D>(kr, (const uint16_t*)a.k + gbase + (size_t)j0 * TILE, tid);
         fetch_tile<D>(vr, (const uint16_t*)a.v + gbase + (size_t)j0 * TILE, tid);
     }
+    // delta = rowsum(dO * O) for this lane's query (lanes l and l + 32 hold the
+    // two halves of the row), formed once the first tile's loads are out; the
+    // dK/dV pass, which runs after this one, reads it (every item of a row
+    // writes the same value)
+    float dl = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dl = fmaf(bf16_to_f32(uo[c][e] & 0xffffu), bf16_to_f32(ug[c][e] & 0xffffu), dl);
+            dl = fmaf(bf16_to_f32(uo[c][e] >> 16), bf16_to_f32(ug[c][e] >> 16), dl);
+        }
+    dl += __shfl_xor(dl, 32);
+    if (hh == 0) a.delta[grp * a.L + t] = dl;
     for (int e = item.begin; e < item.end; ++e) {
         const int j = a.idx[e];
         // 32-token blocks: key halves this wave's query half may see
@@ -458,15 +453,6 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s, hipEvent_t before, hip
 }
 
 }  // namespace
-
-hipError_t launch_bwd_delta(const BwdArgs& a, int head_dim, hipStream_t s) {
-    const int64_t threads = (int64_t)a.B * a.H * a.L * (head_dim / 8);
-    const int64_t grid = (threads + 255) / 256;
-    if (grid == 0) return hipSuccess;
-    if (head_dim == 64) hipLaunchKernelGGL((bwd_delta_kernel<64>), dim3((unsigned)grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((bwd_delta_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s) {
     if (head_dim == 64)
