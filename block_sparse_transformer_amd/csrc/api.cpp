@@ -436,11 +436,14 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
 
     std::vector<int4> units;
     std::vector<int32_t> unit_ptr, tiles, tile_ptr, wg_merge;
-    // Fused merges (D = 64): every split row has kQWaves chunks and no routed
-    // units; each such row then gets a workgroup of its own (one chunk per
-    // wave list), which merges the row at its end.
-    bool fuse = per_wave && nru == 0 && !lay->merges.empty() && lay->kind != 2;
-    for (const auto& mi : lay->merges) fuse = fuse && mi.n_chunks == kQWaves;
+    // Fused merges (D = 64): every split row has the same number n of chunks, n
+    // divides kQWaves, and there are no routed units; each workgroup then
+    // takes the chunks of kQWaves / n split rows (one chunk per wave list) and
+    // merges those rows at its end.
+    const int32_t fuse_n = lay->merges.empty() ? 0 : lay->merges.front().n_chunks;
+    bool fuse = per_wave && nru == 0 && fuse_n >= 2 && kQWaves % fuse_n == 0 && lay->kind != 2;
+    for (const auto& mi : lay->merges) fuse = fuse && mi.n_chunks == fuse_n;
+    const int32_t rows_per_wg = fuse ? kQWaves / fuse_n : 1;
     // pack every XCD's units into nbins bins; false if some bin overflows its lists
     auto pack = [&](int32_t nbins) -> bool {
         units.clear();
@@ -448,7 +451,7 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
         unit_ptr.assign(1, 0);
         tile_ptr.assign(1, 0);
         const bool fuse_here = fuse && nbins == kQWaves * cus_per_xcd;
-        wg_merge.assign(fuse_here ? (size_t)kXcds * cus_per_xcd : 0, -1);
+        wg_merge.assign(fuse_here ? (size_t)kXcds * cus_per_xcd * kQWaves : 0, -1);
         for (int32_t x = 0; x < kXcds; ++x) {
             const auto& v = xu[(size_t)x];
             std::vector<std::vector<int32_t>> bins((size_t)nbins);
@@ -488,11 +491,18 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
                         if (wi.merge >= 0) rows[{un.g, wi.merge}].push_back(u);
                         else rest.push_back(u);
                     }
-                    if ((int32_t)rows.size() >= cus_per_xcd) return false;   // no room: pack without fusion
-                    for (const auto& kv : rows) {
-                        wg_merge[(size_t)x * cus_per_xcd + per_cu.size()] =
-                            (kv.first.first / lay->H) * (int32_t)lay->merges.size() + kv.first.second;
-                        per_cu.push_back(kv.second);
+                    // every wave of a merging workgroup must hold a chunk: whole workgroups only
+                    const int32_t wgs = (int32_t)rows.size() / rows_per_wg;
+                    if ((int32_t)rows.size() % rows_per_wg != 0 || wgs >= cus_per_xcd) return false;
+                    auto it = rows.begin();
+                    for (int32_t w = 0; w < wgs; ++w) {
+                        std::vector<int32_t> chunks;
+                        for (int32_t r = 0; r < rows_per_wg; ++r, ++it) {
+                            wg_merge[((size_t)x * cus_per_xcd + per_cu.size()) * kQWaves + r] =
+                                (it->first.first / lay->H) * (int32_t)lay->merges.size() + it->first.second;
+                            chunks.insert(chunks.end(), it->second.begin(), it->second.end());
+                        }
+                        per_cu.push_back(chunks);
                     }
                     const auto others = lpt(rest, cus_per_xcd - (int32_t)per_cu.size());
                     per_cu.insert(per_cu.end(), others.begin(), others.end());

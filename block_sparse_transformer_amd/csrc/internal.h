@@ -105,8 +105,9 @@ struct FwdArgs {
     int32_t r_chunks;         // chunks per routed tile
     int32_t r_chunk_tiles;    // key blocks per chunk
     int32_t r_slot_base;      // first workspace slot of routed partials
-    // D = 64 kernel: per workgroup, the split row it merges after its lists
-    // (b * n_merges + m, or -1); nullptr when the merge kernel merges every row
+    // D = 64 kernel: per workgroup, kQWaves entries: the split rows it merges
+    // after its lists (b * n_merges + m, or -1); nullptr when the merge kernel
+    // merges every row
     const int32_t* wg_merge;
     int32_t band;             // token band of non-routed rows (MASK_BAND, MASK_TOKEN)
     int32_t routed_stride;    // routed_rows entries between (b, h) groups (0: one list shared by all)
@@ -238,10 +239,11 @@ struct bsattn_layout {
         int32_t* d_unit_ptr;
         int32_t* d_tiles;
         int32_t* d_tile_ptr;
-        // D = 64 with every split row in 8 chunks: the workgroup (XCD x, index c)
-        // that holds a row's 8 chunks merges it itself; d_wg_merge[x * (n_bins /
-        // kQWaves) + c] = b * n_merges + m for such a workgroup, -1 otherwise.
-        // nullptr: rows are merged by the merge kernel.
+        // D = 64 with every split row in n chunks, n dividing kQWaves: the
+        // workgroup (XCD x, index c) holding the chunks of kQWaves / n rows
+        // merges them itself; d_wg_merge[(x * (n_bins / kQWaves) + c) * kQWaves
+        // + r] = b * n_merges + m of its r-th row, -1 past its rows (and for
+        // workgroups that merge nothing).  nullptr: the merge kernel merges.
         int32_t* d_wg_merge;
     };
     mutable std::vector<Sched> scheds;

@@ -1157,13 +1157,14 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (lane == 0) left[wv] = 0;
     wait_vmcnt<0>();
 
-    // A workgroup whose eight lists were the eight chunks of one split row
-    // merges that row here, once every chunk's partial is stored: wave w takes
-    // rows 8w .. 8w + 7, eight lanes per row and eight columns per lane, and
-    // combines the chunks by log-sum-exp as merge_bf16_kernel does.
+    // A workgroup whose eight lists were the chunks of 8 / n split rows of n
+    // chunks each merges those rows here, once every chunk's partial is
+    // stored: for each row, wave w takes rows 8w .. 8w + 7 of its 64, eight
+    // lanes per row and eight columns per lane, and combines the chunks by
+    // log-sum-exp as merge_bf16_kernel does.
     if (a.wg_merge) {
-        const int mu = a.wg_merge[x * (a.n_bins / kQWaves) + blockIdx.x / kXcds];
-        if (mu >= 0) {
+        const int* wm = a.wg_merge + (x * (a.n_bins / kQWaves) + blockIdx.x / kXcds) * kQWaves;
+        if (wm[0] >= 0) {
             __syncthreads();
             // every lane-derived value of this tail is computed here, from a copy
             // the compiler cannot see through: nothing is hoisted above the
@@ -1171,45 +1172,54 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             int tl = (int)threadIdx.x;
             asm volatile("" : "+v"(tl));
             const int tw = tl >> 6, tlane = tl & 63;
-            const int b = mu / a.n_merges;
-            const MergeItem mi = a.merges[mu % a.n_merges];
-            const size_t bh = (size_t)b * a.H + mi.row / a.nb;
             const int r = 8 * tw + (tlane >> 3), part = tlane & 7;
-            const int t = (mi.row % a.nb) * 64 + r;
-            const size_t first = (size_t)b * a.n_slots + mi.first_slot;
-            float lsev[kQWaves];
-            float4 p0[kQWaves], p1[kQWaves];
-#pragma unroll
-            for (int c = 0; c < kQWaves; ++c) {
-                lsev[c] = a.ws_lse[(first + c) * 64 + r];
-                const float* src = a.ws_o + ((first + c) * 64 + r) * D + part * 8;
-                p0[c] = *(const float4*)src;
-                p1[c] = *(const float4*)(src + 4);
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int c = 0; c < kQWaves; ++c) mx = __builtin_fmaxf(mx, lsev[c]);
-            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * 8;
-            if (mx == -INFINITY) {
-                *(u32x4_t*)orow = u32x4_t{0u, 0u, 0u, 0u};
-                if (part == 0) a.lse[bh * a.L + t] = -INFINITY;
-            } else {
-                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
+            for (int k = 0; k < kQWaves; ++k) {
+                const int mu = wm[k];
+                if (mu < 0) break;
+                const int b = mu / a.n_merges;
+                const MergeItem mi = a.merges[mu % a.n_merges];
+                const int nch = mi.n_chunks;
+                const size_t bh = (size_t)b * a.H + mi.row / a.nb;
+                const int t = (mi.row % a.nb) * 64 + r;
+                const size_t first = (size_t)b * a.n_slots + mi.first_slot;
+                float lsev[kQWaves];
+                float4 p0[kQWaves], p1[kQWaves];
 #pragma unroll
                 for (int c = 0; c < kQWaves; ++c) {
-                    const float w = expf(lsev[c] - mx);
-                    wsum += w;
-                    acc[0] += w * p0[c].x; acc[1] += w * p0[c].y; acc[2] += w * p0[c].z; acc[3] += w * p0[c].w;
-                    acc[4] += w * p1[c].x; acc[5] += w * p1[c].y; acc[6] += w * p1[c].z; acc[7] += w * p1[c].w;
+                    lsev[c] = -INFINITY;
+                    p0[c] = p1[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (c < nch) {
+                        lsev[c] = a.ws_lse[(first + c) * 64 + r];
+                        const float* src = a.ws_o + ((first + c) * 64 + r) * D + part * 8;
+                        p0[c] = *(const float4*)src;
+                        p1[c] = *(const float4*)(src + 4);
+                    }
                 }
-                const float inv = 1.f / wsum;
-                u32x4_t o4;
-                o4.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-                o4.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-                o4.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-                o4.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-                *(u32x4_t*)orow = o4;
-                if (part == 0) a.lse[bh * a.L + t] = mx + logf(wsum);
+                float mx = -INFINITY;
+#pragma unroll
+                for (int c = 0; c < kQWaves; ++c) mx = __builtin_fmaxf(mx, lsev[c]);
+                uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * 8;
+                if (mx == -INFINITY) {
+                    *(u32x4_t*)orow = u32x4_t{0u, 0u, 0u, 0u};
+                    if (part == 0) a.lse[bh * a.L + t] = -INFINITY;
+                } else {
+                    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
+#pragma unroll
+                    for (int c = 0; c < kQWaves; ++c) {
+                        const float w = expf(lsev[c] - mx);   // 0 past nch
+                        wsum += w;
+                        acc[0] += w * p0[c].x; acc[1] += w * p0[c].y; acc[2] += w * p0[c].z; acc[3] += w * p0[c].w;
+                        acc[4] += w * p1[c].x; acc[5] += w * p1[c].y; acc[6] += w * p1[c].z; acc[7] += w * p1[c].w;
+                    }
+                    const float inv = 1.f / wsum;
+                    u32x4_t o4;
+                    o4.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+                    o4.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+                    o4.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+                    o4.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+                    *(u32x4_t*)orow = o4;
+                    if (part == 0) a.lse[bh * a.L + t] = mx + logf(wsum);
+                }
             }
         }
     }

@@ -516,3 +516,20 @@ def test_global_rows_merged_in_kernel():
     go = np.stack([o[b, h, t] for b, h, t in rows])
     gl = np.array([l[b, h, t] for b, h, t in rows])
     _compare(go, gl, ro, rl, wl.dtype, "global rows merged in kernel")
+
+
+def test_two_chunk_rows_merged_in_kernel():
+    """At 32 blocks a side a global row splits into 2 chunks; with 8 batch entries and 12
+    heads every XCD holds 24 such rows, and the D = 64 schedule gives four of them to each
+    merging workgroup.  Every row of both global blocks of several (b, h) pairs is compared."""
+    wl = WORKLOADS["bigbird-L2048"]
+    _say("in-kernel merge of 2-chunk rows", wl)
+    inp = make_inputs(wl)
+    lay, olay = _layouts(wl)
+    o, l = _run(wl, inp, lay)
+    ts = list(range(0, 64)) + list(range(wl.seq_len - 64, wl.seq_len)) + [64, 1000]
+    rows = [(b, h, t) for b, h in [(0, 0), (3, 5), (7, 11), (5, 8)] for t in ts]
+    ro, rl = OA.attention_rows(inp["q"], inp["k"], inp["v"], olay, wl.scale, rows)
+    go = np.stack([o[b, h, t] for b, h, t in rows])
+    gl = np.array([l[b, h, t] for b, h, t in rows])
+    _compare(go, gl, ro, rl, wl.dtype, "2-chunk rows merged in kernel")
