@@ -60,8 +60,7 @@ void build_schedule(bsattn_layout* lay) {
             const int32_t r = h * lay->nb + i;
             const int32_t b0 = lay->row_ptr[r], b1 = lay->row_ptr[r + 1];
             const int32_t len = b1 - b0;
-            // token layouts merge every row: the merge adds the row's random tokens
-            if (len <= lay->chunk_tiles && lay->kind != 2) {
+            if (len <= lay->chunk_tiles) {
                 hi.push_back({r, b0, b1, -1, -1, 0, 0, 0});
                 continue;
             }
@@ -79,6 +78,11 @@ void build_schedule(bsattn_layout* lay) {
         std::stable_sort(hi.begin(), hi.end(), [](const WorkItem& x, const WorkItem& y) {
             return (x.col_end - x.col_begin) > (y.col_end - y.col_begin);
         });
+    }
+    // token layouts: which rows are split (their merge item), for the merge that adds random tokens
+    if (lay->kind == 2) {
+        lay->row_merge.assign((size_t)lay->H * lay->nb, -1);
+        for (size_t m = 0; m < lay->merges.size(); ++m) lay->row_merge[(size_t)lay->merges[m].row] = (int32_t)m;
     }
     size_t per = 0;
     for (auto& hi : per_head) per = std::max(per, hi.size());
@@ -183,6 +187,7 @@ void free_device(bsattn_layout* lay) {
         (void)hipFree(lay->d_gtok);
         (void)hipFree(lay->d_links);
         (void)hipFree(lay->d_tok_flag);
+        (void)hipFree(lay->d_row_merge);
         (void)hipFree(lay->d_items);
         (void)hipFree(lay->d_merges);
         for (auto& sc : lay->scheds) {
@@ -200,6 +205,7 @@ void free_device(bsattn_layout* lay) {
     lay->d_col_sub = nullptr;
     lay->d_gtok = lay->d_links = nullptr;
     lay->d_tok_flag = nullptr;
+    lay->d_row_merge = nullptr;
     lay->d_items = nullptr;
     lay->d_merges = nullptr;
     lay->device = -1;
@@ -651,7 +657,7 @@ bsattn_status token_forward(const bsattn_layout* lay, int32_t B, int32_t D, cons
                             const void* v, void* out, float* lse, float scale, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
     const TokenWs w = token_workspace(lay, B, D);
-    if (!workspace || workspace_bytes < w.total)
+    if (w.total > 0 && (!workspace || workspace_bytes < w.total))
         return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", w.total, workspace_bytes);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -683,6 +689,7 @@ bsattn_status token_forward(const bsattn_layout* lay, int32_t B, int32_t D, cons
     a.n_links = lay->n_links;
     a.links = lay->d_links;
     a.tok_global = lay->d_tok_flag;
+    a.row_merge = lay->d_row_merge;
 
     bsattn_layout::Sched sc{};
     bsattn_status st = get_schedule(lay, B, D, w.n_rt * w.r_chunks, w.per, w.r_chunks, stream, &sc);
@@ -1110,6 +1117,10 @@ bsattn_status bsattn_layout_upload(bsattn_layout* lay, hipStream_t stream) {
         e = hipMalloc(&lay->d_gtok, gpad.size() * sizeof(int32_t));
         if (e == hipSuccess) e = hipMalloc(&lay->d_links, nl * sizeof(int32_t));
         if (e == hipSuccess) e = hipMalloc(&lay->d_tok_flag, lay->tok_flag.size());
+        if (e == hipSuccess) e = hipMalloc(&lay->d_row_merge, lay->row_merge.size() * sizeof(int32_t));
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(lay->d_row_merge, lay->row_merge.data(), lay->row_merge.size() * sizeof(int32_t),
+                               hipMemcpyHostToDevice, stream);
         if (e == hipSuccess)
             e = hipMemcpyAsync(lay->d_gtok, gpad.data(), gpad.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream);
         if (e == hipSuccess && !lay->links.empty())

@@ -122,6 +122,7 @@ struct FwdArgs {
     int32_t n_links;
     const int32_t* links;
     const uint8_t* tok_global;
+    const int32_t* row_merge;   // token layouts: [H * nb] merge item of a split row, -1 for a whole row
     float scale;              // score scale
     float scale_log2;         // scale * log2(e)
 };
@@ -215,10 +216,12 @@ struct bsattn_layout {
     // tiles and then the gathered tiles nb .. nb + n_gt - 1 of the global keys
     std::vector<int32_t> tok_g, links;
     std::vector<uint8_t> tok_flag;
+    std::vector<int32_t> row_merge;   // [H * nb]: merge item of a split row, -1 for a whole row
     int32_t n_links = 0, n_gt = 0;
     int32_t* d_gtok = nullptr;      // tok_g padded with -1 to n_gt * 64
     int32_t* d_links = nullptr;
     uint8_t* d_tok_flag = nullptr;
+    int32_t* d_row_merge = nullptr;
     std::vector<bsattn::WorkItem> items;
     std::vector<bsattn::MergeItem> merges;
     int32_t n_slots = 0;        // partial slots per batch entry

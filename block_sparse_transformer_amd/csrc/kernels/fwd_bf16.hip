@@ -1324,11 +1324,13 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
     if (part == 0) a.lse[bh * a.L + t] = mxl + logf(wsum);
 }
 
-// Token layouts: the merge of every non-global row, with the row's random
-// tokens added.  A row's band-and-global partials (one per chunk, fp32 O
-// normalised over the chunk's keys, and its LSE) are combined by log-sum-exp
-// as in merge_bf16_kernel; each random token s then joins the same running
-// max and sum with score scale * q.k_s and value v_s.  Eight lanes per row,
+// Token layouts: every non-global row gets its random tokens here.  A row
+// that fit one unit was written by the attention kernel like any other row
+// (bf16 O normalised over its band and global keys, fp32 LSE): it is read
+// back from the output and updated in place.  A split row's chunk partials
+// (fp32 O and LSE per chunk) are combined by log-sum-exp as in
+// merge_bf16_kernel.  Each random token s then joins the same running max and
+// sum with score scale * q.k_s and value v_s.  Eight lanes per row,
 // D/8 columns each (16- or 32-byte loads); 32 rows per workgroup.  The loads
 // that depend on nothing -- chunk LSEs and partials, the q slice, the first
 // eight link ids -- go out together, so a row costs two memory round trips:
@@ -1336,10 +1338,8 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
 // their head, so workgroups are mapped to XCDs by (batch, head) group: XCD x
 // (workgroup i runs on XCD i % 8) walks the rows of groups x, x + 8, ... one
 // group after the other, and the group's K and V (2 x L x D bf16) stay in that
-// XCD's L2.  Every row of a token layout is one merge item, in head-major
-// order, so row t of group g = b H + h is merge item h nb + t / 64 of batch
-// entry b.  Global rows are computed from the band units' partials like the
-// others but not written: their routed merge writes them.
+// XCD's L2.  Global rows are computed like the others but not written: their
+// routed merge writes them.
 template <int D>
 __global__ __launch_bounds__(256) void links_merge_kernel(const FwdArgs a) {
     constexpr int DP = D / 8;    // columns per lane: 8 or 16
@@ -1353,15 +1353,21 @@ __global__ __launch_bounds__(256) void links_merge_kernel(const FwdArgs a) {
     if (g >= a.B * a.H) return;
     const int t = (j % wg_per_group) * 32 + (tid >> 3);
     const int b = g / a.H, h = g % a.H;
-    const MergeItem mi = a.merges[h * a.nb + t / 64];
+    const int m = a.row_merge[h * a.nb + t / 64];   // the same for the wave's 8 rows
     const int r = t % 64;
     const size_t bh = (size_t)g;
     // read with the other first loads, tested only at the store: branching on
     // it here would put a memory round trip in front of everything else
     const bool global_row = a.tok_global[t] != 0;
-    const int first = b * a.n_slots + mi.first_slot, nch = mi.n_chunks;
+    int first = 0, nch = 1;
+    if (m >= 0) {
+        const MergeItem mi = a.merges[m];
+        first = b * a.n_slots + mi.first_slot;
+        nch = mi.n_chunks;
+    }
     const float* lse_p = a.ws_lse + (size_t)first * 64 + r;
     const float* src = a.ws_o + ((size_t)first * 64 + r) * D + part * DP;
+    uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * DP;
     const int32_t* lk = a.links + ((size_t)(bh % a.H) * a.L + t) * a.n_links;
     const uint16_t* kb = (const uint16_t*)a.k + bh * a.L * D + part * DP;
     const uint16_t* vb = (const uint16_t*)a.v + bh * a.L * D + part * DP;
@@ -1369,12 +1375,29 @@ __global__ __launch_bounds__(256) void links_merge_kernel(const FwdArgs a) {
     // ---- independent loads ----
     float lsev[NC];
     float4 pv4[NC][DP / 4];
+    if (m >= 0) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        lsev[c] = c < nch ? lse_p[(size_t)c * 64] : -INFINITY;
+        for (int c = 0; c < NC; ++c) {
+            lsev[c] = c < nch ? lse_p[(size_t)c * 64] : -INFINITY;
 #pragma unroll
-        for (int d = 0; d < DP / 4; ++d)
-            pv4[c][d] = c < nch ? *(const float4*)(src + (size_t)c * 64 * D + 4 * d) : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int d = 0; d < DP / 4; ++d)
+                pv4[c][d] = c < nch ? *(const float4*)(src + (size_t)c * 64 * D + 4 * d) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else {
+        // a whole row: its output as the one "chunk"
+        lsev[0] = a.lse[bh * a.L + t];
+#pragma unroll
+        for (int d = 0; d < DP / 8; ++d) {
+            const u32x4_t w = *(const u32x4_t*)(orow + 8 * d);
+            pv4[0][2 * d] = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+            pv4[0][2 * d + 1] = make_float4(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w));
+        }
+#pragma unroll
+        for (int c = 1; c < NC; ++c) {
+            lsev[c] = -INFINITY;
+#pragma unroll
+            for (int d = 0; d < DP / 4; ++d) pv4[c][d] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
     u32x4_t qw[DP / 8];
 #pragma unroll
@@ -1489,7 +1512,6 @@ __global__ __launch_bounds__(256) void links_merge_kernel(const FwdArgs a) {
     }
 
     if (global_row) return;
-    uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * DP;
     const bool empty = mxl == -INFINITY;
     const float inv = empty ? 0.f : 1.f / wsum;
 #pragma unroll
@@ -1581,7 +1603,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
     }
     if (e != hipSuccess) return e;
     const int64_t units = (int64_t)a.B * a.n_merges + (a.n_routed > 0 ? (int64_t)a.B * a.H * a.n_rt : 0);
-    if (units == 0) return hipSuccess;
+    if (units == 0 && mask != MASK_TOKEN) return hipSuccess;
     if (head_dim == 64 && a.wg_merge && a.n_routed == 0) return hipSuccess;   // merged inside the kernel
     if (mask == MASK_TOKEN) {
         // the global rows (routed units) by the plain merge, every other row with its random tokens
@@ -1593,8 +1615,6 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
             else hipLaunchKernelGGL(merge_bf16_kernel<128>, dim3((unsigned)(4 * gu)), dim3(256), 0, s, g);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        // every row is a merge item: n_merges == H * nb, one XCD slot per (batch, head) group
-        if (a.n_merges != a.H * a.nb) return hipErrorInvalidValue;
         const int64_t groups = (int64_t)a.B * a.H;
         if (groups == 0) return hipSuccess;
         const dim3 grid((unsigned)(kXcds * ((groups + kXcds - 1) / kXcds) * (a.L / 32)));
