@@ -191,7 +191,7 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "each (batch, head) pair is independent, so more GPUs would shard heads with no collective.",
               file=sys.stderr)
         sys.exit(2)

@@ -1,5 +1,6 @@
 /*
- * bsattn.h -- block-sparse self-attention forward for AMD Instinct MI355X (gfx950).
+ * bsattn.h -- block-sparse self-attention (forward, backward, attention layer)
+ * for AMD Instinct MI355X (gfx950).
  *
  * C ABI of libbsattn.so.  Plain pointers and sizes only; no C++ or framework
  * types cross this boundary, and no C++ exception escapes it.
@@ -9,14 +10,22 @@
  *   O = softmax(scale * Q K^T under a 0/1 mask M) V,
  * with masked scores treated as -inf (the primer page's and the multi-head
  * page's code fill masked scores with a large negative value) and one softmax
- * over the union of all patterns.  M is given at 64x64 block granularity by a
- * BigBird-style layout (BigBird page, "BigBird 稀疏注意力机制解析：如何突破
- * Transformer 的序列长度限制", section 核心实现: global, sliding-window and random
- * patterns) stored in block-CSR form (SQA page, "Transformer计算效率优化：SQA稀疏
- * 注意力机制详解", section 3.1: block-sparse mask, attention only on non-zero
- * blocks; section 5: 64x64 blocks), optionally refined per token by a key
- * padding length or, in the routed-query variant (SQA page, section 2.1), by
- * a token band.
+ * over the union of all patterns.  M comes from a layout object:
+ *   - a BigBird-style block layout (BigBird page, "BigBird 稀疏注意力机制解析：如何突破
+ *     Transformer 的序列长度限制", section 核心实现: global, sliding-window and random
+ *     patterns) on 32-, 64- or 128-token blocks, stored in block-CSR form over
+ *     64x64 tiles (SQA page, "Transformer计算效率优化：SQA稀疏注意力机制详解",
+ *     section 3.1: block-sparse mask, attention only on non-zero blocks;
+ *     section 5: 64x64 blocks), optionally refined per token by a key padding
+ *     length (bsattn_make_layout);
+ *   - a token band |t - s| <= w, alone or in the routed-query variant (SQA page,
+ *     section 2.1) (bsattn_make_band_layout, bsattn_forward_routed);
+ *   - the token-granular BigBird pattern: linspace global tokens, a token
+ *     window and random tokens per row (bsattn_make_token_layout);
+ *   - a content-adaptive block layout whose key blocks are chosen from Q and K
+ *     at every call (bsattn_make_adaptive_layout).
+ * The gradients (bsattn_backward) and the attention layer around the kernel
+ * (bsattn_layer_forward) take the BigBird-style block layouts.
  *
  * Tensor layout everywhere: [B, H, L, D] row-major, D innermost, contiguous.
  * LSE is [B, H, L] fp32: the natural-log log-sum-exp of the scaled, masked
@@ -47,7 +56,7 @@ extern "C" {
 typedef enum {
     BSATTN_OK = 0,
     BSATTN_ERR_INVALID_ARG = 1,   /* bad pointer, size, shape or layout mismatch */
-    BSATTN_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (e.g. D=96) */
+    BSATTN_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement (e.g. D=96) */
     BSATTN_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed */
     BSATTN_ERR_NO_MEMORY = 4,     /* host or device allocation failed */
     BSATTN_ERR_STATE = 5          /* layout not uploaded to the current device */
