@@ -1368,8 +1368,11 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
                               void* dv, const int32_t* key_valid_len, float scale, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
-    if (lay->kind != 0) return fail(BSATTN_ERR_UNSUPPORTED, "the backward takes window/global/random layouts");
+    if (lay->kind != 0 && lay->kind != 1)
+        return fail(BSATTN_ERR_UNSUPPORTED, "the backward takes window/global/random and band layouts");
     if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "the backward is bf16 only");
+    const bool band = lay->kind == 1;
+    if (band && key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "band layouts take no key padding");
     if (!dout || !dq || !dk || !dv) return fail(BSATTN_ERR_INVALID_ARG, "NULL gradient pointer");
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return fail(BSATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
@@ -1411,9 +1414,10 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
     a.ws_dv = (float*)(ws + off_dv);
     a.valid_len = key_valid_len;
     a.B = B; a.H = H; a.L = L; a.nb = lay->nb;
+    a.band = band ? lay->band_tokens : 0;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const int mask = sub ? MASK_SUB : (key_valid_len ? MASK_PAD : MASK_NONE);
+    const int mask = band ? MASK_BAND : sub ? MASK_SUB : (key_valid_len ? MASK_PAD : MASK_NONE);
 
     // delta = rowsum(dO * O) is computed by the dQ pass (every query row has an
     // item there) and read by the dK/dV pass after it

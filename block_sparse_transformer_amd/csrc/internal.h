@@ -164,6 +164,7 @@ struct BwdArgs {
     int32_t items_per_head;   // per-head item lists padded to this length (head_blk < 0: none)
     const int32_t* valid_len; // [B] or null
     int32_t B, H, L, nb, n_slots;
+    int32_t band;             // band layouts: |t - s| <= band (MASK_BAND)
     float scale;              // score scale
     float scale_log2;         // scale * log2(e)
 };

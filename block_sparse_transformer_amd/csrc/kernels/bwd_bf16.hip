@@ -236,6 +236,8 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
         const int j = a.idx[e];
         // 32-token blocks: key halves this wave's query half may see
         const int sub = MASK == MASK_SUB ? (int)a.idx_sub[e] >> (2 * wave) : 3;
+        // band layouts: a tile whose farthest (query, key) pair is inside the band needs no mask
+        const bool band_cut = MASK == MASK_BAND && 64 * abs(blk - j) + 63 > a.band;
         __syncthreads();   // the previous tile's reads are done
         commit_tile<D>(kt, kr, tid);
         commit_tile<D>(vt, vr, tid);
@@ -265,6 +267,8 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
                 float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, nl2));
                 if (MASK == MASK_PAD && j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) p = 0.f;
                 if (MASK == MASK_SUB && !((sub >> kb) & 1)) p = 0.f;
+                if (MASK == MASK_BAND && band_cut && abs(t - (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4))) > a.band)
+                    p = 0.f;
                 s[kb][i] = p * (dp[kb][i] - dl);
             }
         // dQ^T += K^T dS^T
@@ -333,6 +337,9 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
     for (int e = item.begin; e < item.end; ++e) {
         // 32-token blocks: query halves that may see this wave's key half
         const int sub = MASK == MASK_SUB ? (int)a.idx_sub[e] >> wave : 15;
+        // band layouts: query block ib, masked per pair unless the whole tile is inside the band
+        const int ib = a.idx[e];
+        const bool band_cut = MASK == MASK_BAND && 64 * abs(blk - ib) + 63 > a.band;
         __syncthreads();
         commit_tile<D>(qt, qr, tid);
         commit_tile<D>(ot, orr, tid);
@@ -368,6 +375,8 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
                 float p = __builtin_amdgcn_exp2f(s[qb][i] * c2);
                 if (!key_ok) p = 0.f;
                 if (MASK == MASK_SUB && !((sub >> (2 * qb)) & 1)) p = 0.f;
+                if (MASK == MASK_BAND && band_cut && abs(ib * 64 + 32 * qb + 8 * (i / 4) + 4 * hh + (i % 4) - key) > a.band)
+                    p = 0.f;
                 s[qb][i] = p;
                 dp[qb][i] *= p;
             }
@@ -458,9 +467,11 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s
     if (head_dim == 64)
         return mask == MASK_PAD   ? launch_dq_t<64, MASK_PAD>(a, s)
              : mask == MASK_SUB   ? launch_dq_t<64, MASK_SUB>(a, s)
+             : mask == MASK_BAND  ? launch_dq_t<64, MASK_BAND>(a, s)
                                   : launch_dq_t<64, MASK_NONE>(a, s);
     return mask == MASK_PAD   ? launch_dq_t<128, MASK_PAD>(a, s)
          : mask == MASK_SUB   ? launch_dq_t<128, MASK_SUB>(a, s)
+         : mask == MASK_BAND  ? launch_dq_t<128, MASK_BAND>(a, s)
                               : launch_dq_t<128, MASK_NONE>(a, s);
 }
 
@@ -469,9 +480,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t
     if (head_dim == 64)
         return mask == MASK_PAD   ? launch_dkdv_t<64, MASK_PAD>(a, s, before, after)
              : mask == MASK_SUB   ? launch_dkdv_t<64, MASK_SUB>(a, s, before, after)
+             : mask == MASK_BAND  ? launch_dkdv_t<64, MASK_BAND>(a, s, before, after)
                                   : launch_dkdv_t<64, MASK_NONE>(a, s, before, after);
     return mask == MASK_PAD   ? launch_dkdv_t<128, MASK_PAD>(a, s, before, after)
          : mask == MASK_SUB   ? launch_dkdv_t<128, MASK_SUB>(a, s, before, after)
+         : mask == MASK_BAND  ? launch_dkdv_t<128, MASK_BAND>(a, s, before, after)
                               : launch_dkdv_t<128, MASK_NONE>(a, s, before, after);
 }
 

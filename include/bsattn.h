@@ -24,8 +24,9 @@
  *     window and random tokens per row (bsattn_make_token_layout);
  *   - a content-adaptive block layout whose key blocks are chosen from Q and K
  *     at every call (bsattn_make_adaptive_layout).
- * The gradients (bsattn_backward) and the attention layer around the kernel
- * (bsattn_layer_forward) take the BigBird-style block layouts.
+ * The gradients (bsattn_backward) take the BigBird-style block layouts and
+ * the token band; the attention layer around the kernel (bsattn_layer_forward)
+ * takes the BigBird-style block layouts.
  *
  * Tensor layout everywhere: [B, H, L, D] row-major, D innermost, contiguous.
  * LSE is [B, H, L] fp32: the natural-log log-sum-exp of the scaled, masked
@@ -306,7 +307,9 @@ bsattn_status bsattn_backward_workspace_size(const bsattn_layout* layout, int32_
  *   P = exp(scale * q.k - lse) on allowed keys, delta = rowsum(dout * out),
  *   dv = P^T dout,  ds = P * (dout v^T - delta),
  *   dq = scale * ds k,  dk = scale * ds^T q.
- *   layout          uploaded window/global/random layout (band layouts: UNSUPPORTED).
+ *   layout          uploaded window/global/random or band layout (token,
+ *                   adaptive layouts and the routed variant: UNSUPPORTED; band
+ *                   layouts take no key padding).
  *   dtype           BSATTN_BF16 (others: UNSUPPORTED).
  *   batch..head_dim as bsattn_forward.
  *   q, k, v         the forward's inputs, device bf16 [B, H, L, D].

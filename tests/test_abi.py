@@ -137,15 +137,17 @@ def test_backward_rejects_before_any_hip_call():
     L = bs.lib()
     lay = bs.bsattn_make_layout(2, 1024, 64, 3, [0], 1, 0)
     band = bs.bsattn_make_band_layout(2, 1024, 64, 32)
+    tok = bs.bsattn_make_token_layout(2, 1024, 32, 8, 2, 1)
     f = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(10)]
     ws = ctypes.c_size_t(0)
 
-    def call(layout, dtype=1, D=64, q=f[0], dq=f[6], dk=f[7], dv=f[8], dout=f[5], scale=0.125):
+    def call(layout, dtype=1, D=64, q=f[0], dq=f[6], dk=f[7], dv=f[8], dout=f[5], scale=0.125, kv=None):
         return L.bsattn_backward(layout, dtype, 1, 2, 1024, D, q, f[1], f[2], f[3], f[4], dout, dq, dk, dv,
-                                 None, scale, None, ws, None)
+                                 kv, scale, None, ws, None)
 
     assert call(None) == 1
-    assert call(band.handle) == 2 and "layout" in bs.bsattn_last_error()
+    assert call(tok.handle) == 2 and "layout" in bs.bsattn_last_error()
+    assert call(band.handle, kv=f[9]) == 2 and "padding" in bs.bsattn_last_error()
     assert call(lay.handle, dtype=0) == 2 and "bf16" in bs.bsattn_last_error()
     assert call(lay.handle, dout=None) == 1
     assert call(lay.handle, dq=f[0]) == 1 and "alias" in bs.bsattn_last_error()

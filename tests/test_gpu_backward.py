@@ -78,11 +78,17 @@ def _hip_backward(wl, inp, do, lay, o=None, lse=None):
     return _f64(dq), _f64(dk), _f64(dv)
 
 
-def _case(wl, tag, heads=None, batches=None):
+def _band_layouts(wl):
+    lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+    bs.bsattn_layout_upload(lay)
+    return lay, OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+
+
+def _case(wl, tag, heads=None, batches=None, layouts=_layouts):
     _say(tag, wl)
     inp = make_inputs(wl)
     do = make_grad_output(wl)
-    lay, olay = _layouts(wl)
+    lay, olay = layouts(wl)
     got = _hip_backward(wl, inp, do, lay)
     vl = inp.get("valid_len")
     ref = OG.attention_backward(inp["q"], inp["k"], inp["v"], do, olay, wl.scale,
@@ -184,3 +190,27 @@ def test_backward_block128():
 def test_backward_block32(D):
     _case(WORKLOADS["bigbird32-L8192"].with_(batch=1, heads=2, seq_len=2048, head_dim=D, global_blocks=(0, 63)),
           f"bwd block32 L2048 D={D}")
+
+
+# Token band |t - s| <= band (SQA page, section 2.1): narrow bands, bands that
+# cut through tiles, and a band wide enough that rows and columns are split.
+@pytest.mark.parametrize("band,D,L", [(37, 64, 1536), (128, 64, 1536), (256, 64, 1536), (600, 64, 2048),
+                                      (64, 128, 1536), (200, 128, 1536)])
+def test_backward_band(band, D, L):
+    wl = WORKLOADS["band256-L8192"].with_(batch=2, heads=2, seq_len=L, head_dim=D, band_tokens=band)
+    _case(wl, f"bwd band {band} D={D} L={L}", layouts=_band_layouts)
+
+
+def test_backward_band_benchmark_shape_one_head():
+    wl = WORKLOADS["band256-L8192"]
+    _case(wl, "bwd band256-L8192 (b=0, h=3)", heads=[3], batches=[0], layouts=_band_layouts)
+
+
+def test_backward_band_rejects_padding():
+    wl = WORKLOADS["band256-L8192"].with_(batch=1, heads=1, seq_len=512, band_tokens=64)
+    lay, _ = _band_layouts(wl)
+    dev = {k: v.cuda() for k, v in make_inputs(wl).items()}
+    o, lse = bs.forward(dev["q"], dev["k"], dev["v"], lay, scale=wl.scale)
+    vl = torch.tensor([300], dtype=torch.int32, device="cuda")
+    with pytest.raises(bs.BsattnError, match="padding"):
+        bs.backward(dev["q"], dev["k"], dev["v"], o, lse, torch.ones_like(o), lay, key_valid_len=vl, scale=wl.scale)
