@@ -40,16 +40,20 @@ def _case(wl, tag):
     _say(tag, wl)
     p = make_layer_params(wl)
     vl = make_inputs(wl).get("valid_len") if wl.padded else None
-    lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
-                                wl.random_blocks, wl.layout_seed)
+    if wl.band:
+        lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+        olay = OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+    else:
+        lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
+                                    wl.random_blocks, wl.layout_seed)
+        olay = OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
+                              wl.random_blocks, wl.layout_seed)
     bs.bsattn_layout_upload(lay)
     d = {k: v.cuda() for k, v in p.items()}
     out = bs.layer_forward(d["x"], d["w_qkv"], d["b_qkv"], d["w_proj"], d["b_proj"], lay, wl.heads,
                            key_valid_len=None if vl is None else vl.cuda(), scale=wl.scale)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
-    olay = OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
-                          wl.random_blocks, wl.layout_seed)
     ref = OLY.layer_forward(p["x"], p["w_qkv"], p["b_qkv"], p["w_proj"], p["b_proj"], olay, wl.heads, wl.scale,
                             valid_len=None if vl is None else vl.tolist())
     assert np.isfinite(got).all()
@@ -69,3 +73,10 @@ def test_layer_d128_padded():
 
 def test_layer_benchmark_shape():
     _case(WORKLOADS["bigbird-L8192"], "layer bigbird-L8192")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_layer_band(D):
+    # token band |t - s| <= 100 (SQA page, section 2.1) inside the layer
+    _case(WORKLOADS["band256-L8192"].with_(batch=2, heads=2, seq_len=1024, head_dim=D, band_tokens=100),
+          f"layer band D={D}")
