@@ -80,3 +80,9 @@ def test_layer_band(D):
     # token band |t - s| <= 100 (SQA page, section 2.1) inside the layer
     _case(WORKLOADS["band256-L8192"].with_(batch=2, heads=2, seq_len=1024, head_dim=D, band_tokens=100),
           f"layer band D={D}")
+
+
+def test_layer_block32():
+    # 32-token blocks (SQA page, section 5: block sizes) inside the layer
+    _case(WORKLOADS["bigbird32-L8192"].with_(batch=1, heads=2, seq_len=2048, global_blocks=(0, 63)),
+          "layer block32 L2048")
