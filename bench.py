@@ -215,8 +215,9 @@ def main():
         sys.exit(2)
     inp = make_inputs(wl)
 
-    if (wl.token or wl.adaptive) and args.which != "forward":
-        print("token-pattern and adaptive workloads are timed in the forward only", file=sys.stderr)
+    if (wl.adaptive and args.which != "forward") or (wl.token and args.which == "backward"):
+        print("adaptive workloads are timed in the forward only, token-pattern workloads in the forward and "
+              "the layer", file=sys.stderr)
         sys.exit(2)
     t0 = time.perf_counter()
     if wl.band:

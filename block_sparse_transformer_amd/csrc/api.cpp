@@ -1454,8 +1454,8 @@ bsattn_status bsattn_layer_forward(const bsattn_layout* lay, int32_t B, int32_t 
                                    const void* b_proj, void* out, const int32_t* key_valid_len, float scale,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
-    if (lay->kind != 0 && lay->kind != 1)
-        return fail(BSATTN_ERR_UNSUPPORTED, "the layer takes window/global/random and band layouts");
+    if (lay->kind == 3)
+        return fail(BSATTN_ERR_UNSUPPORTED, "the layer takes block, band and token layouts (not adaptive ones)");
     if (!x || !w_qkv || !b_qkv || !w_proj || !b_proj || !out) return fail(BSATTN_ERR_INVALID_ARG, "NULL pointer");
     const void* ps[6] = {x, w_qkv, b_qkv, w_proj, b_proj, out};
     for (const void* p : ps)

@@ -24,9 +24,9 @@
  *     window and random tokens per row (bsattn_make_token_layout);
  *   - a content-adaptive block layout whose key blocks are chosen from Q and K
  *     at every call (bsattn_make_adaptive_layout).
- * The gradients (bsattn_backward) and the attention layer around the kernel
- * (bsattn_layer_forward) take the BigBird-style block layouts and the token
- * band.
+ * The gradients (bsattn_backward) take the BigBird-style block layouts and the
+ * token band; the attention layer around the kernel (bsattn_layer_forward)
+ * takes these and the token-granular pattern.
  *
  * Tensor layout everywhere: [B, H, L, D] row-major, D innermost, contiguous.
  * LSE is [B, H, L] fp32: the natural-log log-sum-exp of the scaled, masked

@@ -160,7 +160,7 @@ def test_backward_rejects_before_any_hip_call():
 def test_layer_rejects_before_any_hip_call():
     L = bs.lib()
     lay = bs.bsattn_make_layout(2, 1024, 64, 3, [0], 1, 0)
-    tok = bs.bsattn_make_token_layout(2, 1024, 32, 8, 2, 1)
+    adp = bs.bsattn_make_adaptive_layout(2, 1024, 4)
     f = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(8)]
     ws = ctypes.c_size_t(0)
 
@@ -169,7 +169,7 @@ def test_layer_rejects_before_any_hip_call():
                                       None, ws, None)
 
     assert call(None) == 1
-    assert call(tok.handle) == 2 and "layout" in bs.bsattn_last_error()
+    assert call(adp.handle) == 2 and "layout" in bs.bsattn_last_error()
     assert call(lay.handle, out=f[0]) == 1 and "alias" in bs.bsattn_last_error()
     assert call(lay.handle, b_qkv=ctypes.c_void_p(0x3008)) == 1 and "aligned" in bs.bsattn_last_error()
     assert call(lay.handle, H=3) == 1

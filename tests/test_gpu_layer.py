@@ -40,7 +40,12 @@ def _case(wl, tag):
     _say(tag, wl)
     p = make_layer_params(wl)
     vl = make_inputs(wl).get("valid_len") if wl.padded else None
-    if wl.band:
+    if wl.token:
+        lay = bs.bsattn_make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
+                                          wl.layout_seed)
+        olay = OL.make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
+                                    wl.layout_seed)
+    elif wl.band:
         lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
         olay = OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
     else:
@@ -86,3 +91,9 @@ def test_layer_block32():
     # 32-token blocks (SQA page, section 5: block sizes) inside the layer
     _case(WORKLOADS["bigbird32-L8192"].with_(batch=1, heads=2, seq_len=2048, global_blocks=(0, 63)),
           "layer block32 L2048")
+
+
+def test_layer_token_pattern():
+    # token-granular BigBird pattern (BigBird page, 核心实现) inside the layer
+    _case(WORKLOADS["bigbird-tok-L8192"].with_(batch=2, heads=2, seq_len=1024, num_global=40, random_tokens=4),
+          "layer token pattern")
