@@ -186,6 +186,11 @@ def test_backward_block128():
           "bwd block128 L2048")
 
 
+def test_backward_block128_padded():
+    _case(WORKLOADS["bigbird128-L8192"].with_(batch=2, heads=2, seq_len=2048, global_blocks=(0, 15), padded=True),
+          "bwd block128 L2048 padded")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_backward_block32(D):
     _case(WORKLOADS["bigbird32-L8192"].with_(batch=1, heads=2, seq_len=2048, head_dim=D, global_blocks=(0, 63)),

@@ -392,6 +392,11 @@ def test_block128_full():
                 "block128 L2048 full")
 
 
+def test_block128_padded():
+    _full_check(WORKLOADS["bigbird128-L8192"].with_(batch=2, heads=2, seq_len=2048, global_blocks=(0, 15),
+                                                    padded=True), "block128 L2048 padded")
+
+
 def test_block128_benchmark_shape_sampled():
     _sampled_check(WORKLOADS["bigbird128-L8192"], "bigbird128-L8192 full size, sampled rows")
 
