@@ -309,7 +309,10 @@ bsattn_status bsattn_backward_workspace_size(const bsattn_layout* layout, int32_
  *   dq = scale * ds k,  dk = scale * ds^T q.
  *   layout          uploaded window/global/random or band layout (token,
  *                   adaptive layouts and the routed variant: UNSUPPORTED; band
- *                   layouts take no key padding).
+ *                   layouts take no key padding).  out and lse must come from
+ *                   bsattn_forward on this layout: outputs of
+ *                   bsattn_forward_routed are not detected and would give the
+ *                   band's gradients for the routed rows.
  *   dtype           BSATTN_BF16 (others: UNSUPPORTED).
  *   batch..head_dim as bsattn_forward.
  *   q, k, v         the forward's inputs, device bf16 [B, H, L, D].
