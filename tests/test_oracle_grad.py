@@ -130,3 +130,24 @@ def test_one_key_per_row_has_constant_softmax():
     for t in range(n):
         ref[cols[t]] += do[t]
     assert np.abs(dv - ref).max() < 1e-14
+
+
+def test_band_backward_matches_autograd_and_closed_form():
+    """Token band |t - s| <= w (SQA page, section 2.1): the oracle backward over a
+    band layout equals torch autograd of the dense formula with the band written
+    out directly, and for w = 0 (each query sees only its own key: P = 1) it has
+    the closed form dQ = dK = 0, dV = dO."""
+    L, D = 3 * 64, 8
+    q, k, v, do = (_rand((1, 1, L, D), s) for s in (41, 42, 43, 44))
+    t = np.arange(L)
+    for w in (0, 5, 70):
+        lay = OL.make_band_layout(1, L, 64, w)
+        dq, dk, dv = OG.attention_backward(q, k, v, do, lay, 0.3, chunk=50)
+        mask = np.abs(t[:, None] - t[None, :]) <= w
+        rq, rk, rv = _torch_dense_grad(q[0, 0], k[0, 0], v[0, 0], do[0, 0], mask, 0.3)
+        assert np.abs(dq[0, 0] - rq).max() < 1e-12, w
+        assert np.abs(dk[0, 0] - rk).max() < 1e-12, w
+        assert np.abs(dv[0, 0] - rv).max() < 1e-12, w
+        if w == 0:
+            assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+            assert np.array_equal(dv, do)
