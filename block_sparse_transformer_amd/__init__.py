@@ -32,6 +32,7 @@ from ._binding import (  # noqa: F401
     bsattn_make_adaptive_layout,
     bsattn_make_layout,
     bsattn_make_token_layout,
+    bsattn_prepare,
     bsattn_route_topk,
     bsattn_set_profile_events,
     bsattn_status_string,

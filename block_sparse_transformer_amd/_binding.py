@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
     L.bsattn_layer_forward.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                        _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_size_t, _c_vp]
     L.bsattn_set_profile_events.argtypes = [_c_vp, _c_vp]
+    L.bsattn_prepare.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp]
     L.bsattn_status_string.argtypes = [ctypes.c_int]
     L.bsattn_status_string.restype = ctypes.c_char_p
     L.bsattn_last_error.argtypes = []
@@ -81,7 +82,8 @@ def lib() -> ctypes.CDLL:
                  "bsattn_layout_token_links", "bsattn_layout_csr",
                  "bsattn_layout_tile_masks", "bsattn_layout_upload",
                  "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
-                 "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events"):
+                 "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events",
+                 "bsattn_prepare"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -224,6 +226,13 @@ def bsattn_layout_tile_masks(layout: Layout) -> Optional[np.ndarray]:
 
 def bsattn_layout_upload(layout: Layout, stream=None) -> None:
     _check("bsattn_layout_upload", lib().bsattn_layout_upload(layout.handle, _stream_handle(stream)))
+
+
+def bsattn_prepare(layout: Layout, batch: int, head_dim: int, num_routed: int = 0, backward: bool = False,
+                   stream=None) -> None:
+    """Build and upload the schedule of one call shape ahead of time (see bsattn.h)."""
+    _check("bsattn_prepare", lib().bsattn_prepare(layout.handle, batch, head_dim, num_routed, int(bool(backward)),
+                                                  _stream_handle(stream)))
 
 
 def bsattn_layout_build_device(layout: Layout, row_ptr_dev, col_idx_dev, stream=None) -> None:

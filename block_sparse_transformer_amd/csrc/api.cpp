@@ -1158,6 +1158,8 @@ bsattn_status bsattn_layout_build_device(const bsattn_layout* lay, int32_t* row_
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
     if (!row_ptr_dev || (!col_idx_dev && !lay->col_idx.empty()))
         return fail(BSATTN_ERR_INVALID_ARG, "NULL device array");
+    if (lay->kind != 0 && lay->kind != 1)
+        return fail(BSATTN_ERR_UNSUPPORTED, "the device rule builds window/global/random and band layouts only");
     if (lay->block != kBlock) return fail(BSATTN_ERR_UNSUPPORTED, "the device rule runs 64-token blocks only");
     hipError_t e = launch_layout_build(lay->rule, lay->kind, lay->H, lay->nb, lay->band_tokens,
                                        row_ptr_dev, col_idx_dev, stream);
@@ -1194,6 +1196,47 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* lay, int32_t batch, int
         slots += (size_t)batch * lay->H * n_rt * rch;
     }
     *bytes = slots * slot_bytes(head_dim);
+    return ok();
+}
+
+bsattn_status bsattn_prepare(const bsattn_layout* lay, int32_t batch, int32_t head_dim, int32_t num_routed,
+                             int32_t backward, hipStream_t stream) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (batch < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+    if (num_routed < 0 || num_routed > lay->L)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_routed must be in [0, seq_len] (got %d)", num_routed);
+    if (num_routed > 0 && lay->kind != 1)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_routed > 0 needs a band layout");
+    if (backward && lay->kind != 0 && lay->kind != 1)
+        return fail(BSATTN_ERR_UNSUPPORTED, "the backward takes window/global/random and band layouts");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (lay->device < 0 || lay->device != dev)
+        return fail(BSATTN_ERR_STATE, "layout is not uploaded to the current device (%d)", dev);
+    // the same schedule parameters the calls derive
+    int32_t nru = 0, rct = 1, rch = 1;
+    if (lay->kind == 2) {
+        const TokenWs w = token_workspace(lay, batch, head_dim);
+        nru = w.n_rt * w.r_chunks;
+        rct = w.per;
+        rch = w.r_chunks;
+    } else if (num_routed > 0) {
+        int32_t n_rt = 0, per = 1;
+        routed_split(lay->nb, num_routed, &n_rt, &rch, &per);
+        nru = n_rt * rch;
+        rct = per;
+    }
+    bsattn_layout::Sched sc{};
+    bsattn_status st = get_schedule(lay, batch, head_dim, nru, rct, rch, stream, &sc);
+    if (st != BSATTN_OK) return st;
+    if (backward) {
+        std::lock_guard<std::mutex> guard(*lay->sched_mu);
+        st = upload_bwd(lay, stream);
+        if (st != BSATTN_OK) return st;
+    }
     return ok();
 }
 

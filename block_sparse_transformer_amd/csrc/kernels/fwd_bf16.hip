@@ -1622,10 +1622,26 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
         else hipLaunchKernelGGL(links_merge_kernel<128>, grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    if (head_dim == 64)
-        hipLaunchKernelGGL(merge_bf16_kernel<64>, dim3((unsigned)(4 * units)), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(merge_bf16_kernel<128>, dim3((unsigned)(4 * units)), dim3(256), 0, s, a);
+    // Split band rows first, routed tiles after them: a routed token can lie
+    // in a split band row's block, and both merges write its O and LSE, so the
+    // routed result must come second (stream order) to be the one that stays.
+    auto merge = [&](const FwdArgs& m, int64_t n) {
+        if (n == 0) return;
+        if (head_dim == 64) hipLaunchKernelGGL(merge_bf16_kernel<64>, dim3((unsigned)(4 * n)), dim3(256), 0, s, m);
+        else hipLaunchKernelGGL(merge_bf16_kernel<128>, dim3((unsigned)(4 * n)), dim3(256), 0, s, m);
+    };
+    const int64_t band_units = (int64_t)a.B * a.n_merges;
+    if (a.n_routed > 0 && band_units > 0) {
+        FwdArgs band = a;
+        band.n_routed = 0;
+        merge(band, band_units);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        FwdArgs routed = a;
+        routed.n_merges = 0;
+        merge(routed, units - band_units);
+    } else {
+        merge(a, units);
+    }
     return hipGetLastError();
 }
 

@@ -39,9 +39,12 @@
  * are reported as BSATTN_ERR_HIP.  NaN inputs propagate to the outputs.  A
  * query row with no allowed key gets O = 0 and LSE = -inf.
  *
- * Asynchrony: functions taking a hipStream_t enqueue work on that stream and
- * return without synchronising; they are reentrant.  Calls that share a
- * workspace must be ordered (same stream, or synchronised).
+ * Asynchrony: the compute calls (forward, backward, layer, router) enqueue
+ * work on their hipStream_t and return without synchronising; they are
+ * reentrant.  Set-up calls (bsattn_layout_upload, bsattn_prepare) allocate and
+ * synchronise their stream; a compute call of a shape that was never prepared
+ * does the same once, on first use.  Calls that share a workspace must be
+ * ordered (same stream, or synchronised).
  */
 #ifndef BSATTN_H
 #define BSATTN_H
@@ -199,19 +202,40 @@ bsattn_status bsattn_layout_csr(const bsattn_layout* layout, const int32_t** row
  * output pointer may be NULL. */
 bsattn_status bsattn_layout_tile_masks(const bsattn_layout* layout, const uint8_t** masks, int64_t* n);
 
-/* Copy the CSR and the work schedule to the current HIP device (hipMalloc +
- * copies enqueued on `stream`, then synchronised).  Must precede the forward
- * calls that use the layout; calling it again re-uploads to the then-current
- * device.  The device copy is freed by bsattn_layout_destroy. */
+/* Copy the CSR and the layout's work items to the current HIP device
+ * (hipMalloc + copies enqueued on `stream`, then synchronised).  Must precede
+ * the forward calls that use the layout; calling it again re-uploads to the
+ * then-current device and drops the schedules built so far.  The device copy
+ * is freed by bsattn_layout_destroy.  The per-shape schedules are built by
+ * bsattn_prepare, or on a shape's first call. */
 bsattn_status bsattn_layout_upload(bsattn_layout* layout, hipStream_t stream);
 
 /* Rebuild the same layout on the device from its parameters (one thread per
  * row runs the identical integer rule) into caller-owned device arrays
  * row_ptr_dev [num_rows + 1] and col_idx_dev [nnz].  Exists to prove that
- * the host and device evaluations of the rule agree bit for bit.  Layouts
- * of 64-token blocks only (UNSUPPORTED for 32 and 128). */
+ * the host and device evaluations of the rule agree bit for bit.
+ * Window/global/random and band layouts of 64-token blocks only
+ * (UNSUPPORTED for 32- and 128-token blocks, token and adaptive layouts). */
 bsattn_status bsattn_layout_build_device(const bsattn_layout* layout, int32_t* row_ptr_dev,
                                          int32_t* col_idx_dev, hipStream_t stream);
+
+/* Build and upload, ahead of time, the work schedule of one call shape of an
+ * uploaded layout, so that every later bsattn_forward (and, with
+ * num_routed = k on a band layout, bsattn_forward_routed) of that shape
+ * allocates nothing and never synchronises -- it can then be captured in a
+ * HIP graph.  A call of a shape that was not prepared builds its schedule on
+ * first use (hipMalloc and a synchronous copy on its stream).
+ *   batch, head_dim  the calls' B and D (D in {64, 128}); one schedule per pair.
+ *   num_routed       0, or the calls' k for bsattn_forward_routed (band layouts).
+ *   backward         non-zero: also upload the backward work lists
+ *                    (window/global/random and band layouts), which
+ *                    bsattn_backward otherwise uploads on its first call.
+ * hipMalloc and copies enqueued on `stream`, then synchronised.  The device
+ * arrays belong to the layout (freed by bsattn_layout_destroy or a re-upload).
+ * Calling it again for a prepared shape does nothing.  fp32 forwards use no
+ * schedule. */
+bsattn_status bsattn_prepare(const bsattn_layout* layout, int32_t batch, int32_t head_dim,
+                             int32_t num_routed, int32_t backward, hipStream_t stream);
 
 /* Free a layout and its device copy.  NULL is a no-op. */
 void bsattn_layout_destroy(bsattn_layout* layout);
@@ -254,7 +278,9 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* layout, int32_t batch,
  *   workspace      device buffer of at least bsattn_workspace_size() bytes,
  *                  256-byte aligned, any contents (may be NULL if that size
  *                  is 0).
- * Enqueued on `stream`; no synchronisation. */
+ * Enqueued on `stream`.  When bsattn_prepare has built this (batch, head_dim)
+ * shape, the call allocates nothing and does not synchronise; otherwise its
+ * first call builds the schedule (hipMalloc and a synchronous copy). */
 bsattn_status bsattn_forward(const bsattn_layout* layout, bsattn_dtype dtype,
                              int32_t batch, int32_t num_heads, int32_t seq_len, int32_t head_dim,
                              const void* q, const void* k, const void* v,
@@ -282,7 +308,8 @@ bsattn_status bsattn_route_topk(const void* q, const float* w, int32_t batch, in
  * every key; all other rows attend to keys with |t - s| <= band, where
  * `band_layout` comes from bsattn_make_band_layout (and is uploaded).
  * dtype must be BSATTN_BF16.  Other arguments as bsattn_forward; the
- * workspace is sized with num_routed. */
+ * workspace is sized with num_routed, and bsattn_prepare with num_routed = k
+ * builds the schedule ahead of time. */
 bsattn_status bsattn_forward_routed(const bsattn_layout* band_layout, bsattn_dtype dtype,
                                     int32_t batch, int32_t num_heads, int32_t seq_len,
                                     int32_t head_dim, const void* q, const void* k,
@@ -325,9 +352,10 @@ bsattn_status bsattn_backward_workspace_size(const bsattn_layout* layout, int32_
  *   key_valid_len   as bsattn_forward.
  *   workspace       device buffer of at least bsattn_backward_workspace_size()
  *                   bytes, 256-byte aligned, any contents.
- * All pointers 16-byte aligned.  Enqueued on `stream`; no synchronisation.
- * The first call on a device uploads the layout's backward work lists
- * (hipMalloc and a synchronous copy); later calls allocate nothing. */
+ * All pointers 16-byte aligned.  Enqueued on `stream`.  Unless
+ * bsattn_prepare (backward != 0) uploaded them, the first call on a device
+ * uploads the layout's backward work lists (hipMalloc and a synchronous
+ * copy); later calls allocate nothing and do not synchronise. */
 bsattn_status bsattn_backward(const bsattn_layout* layout, bsattn_dtype dtype,
                               int32_t batch, int32_t num_heads, int32_t seq_len, int32_t head_dim,
                               const void* q, const void* k, const void* v,

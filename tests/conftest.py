@@ -24,3 +24,32 @@ def read_golden(name):
             if line and not line.startswith("#"):
                 rows.append(line.split())
     return rows
+
+
+# ---- measured parity errors, printed at the end of the run ----
+# Each GPU parity helper records (case, quantity, error, tolerance); the
+# terminal summary lists them, the cases at the benchmark shapes last.
+_PARITY = []
+
+
+def record_parity(case, quantity, err, tol):
+    _PARITY.append((str(case), str(quantity), float(err), float(tol)))
+
+
+def pytest_terminal_summary(terminalreporter):
+    if not _PARITY:
+        return
+    tw = terminalreporter
+    tw.write_line("")
+    tw.write_line(f"measured parity errors ({len(_PARITY)} comparisons; error / tolerance):")
+    whole = [p for p in _PARITY if "whole" in p[0]]
+    rest = [p for p in _PARITY if "whole" not in p[0]]
+    for case, q, e, t in sorted(rest, key=lambda p: -p[2] / p[3])[:12]:
+        tw.write_line(f"  {case}: {q} {e:.2e} / {t:.0e}")
+    if len(rest) > 12:
+        tw.write_line(f"  ... {len(rest) - 12} more, all at most {max(p[2] / p[3] for p in rest[12:]):.3f} of "
+                      f"their tolerance")
+    for case, q, e, t in whole:
+        tw.write_line(f"  {case}: {q} {e:.2e} / {t:.0e}")
+    worst = max(_PARITY, key=lambda p: p[2] / p[3])
+    tw.write_line(f"worst ratio {worst[2] / worst[3]:.3f} ({worst[0]}, {worst[1]})")

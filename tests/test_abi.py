@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
         "bsattn_forward", "bsattn_backward_workspace_size", "bsattn_backward",
         "bsattn_layer_workspace_size", "bsattn_layer_forward",
         "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
-        "bsattn_last_error"])
+        "bsattn_last_error", "bsattn_prepare"])
     lib = bs.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -177,3 +177,26 @@ def test_layer_rejects_before_any_hip_call():
     assert call(lay.handle) == 1 and "workspace" in bs.bsattn_last_error()
     n = bs.bsattn_layer_workspace_size(lay, 1, 64)
     assert n >= 1024 * 128 * (3 * 4 + 4 * 2)
+
+
+def test_prepare_rejects_before_any_hip_call():
+    L = bs.lib()
+    lay = bs.bsattn_make_layout(2, 1024, 64, 3, [0], 1, 0)
+    tok = bs.bsattn_make_token_layout(2, 1024, 16, 8, 2, 0)
+    assert L.bsattn_prepare(None, 1, 64, 0, 0, None) == 1           # NULL layout
+    assert L.bsattn_prepare(lay.handle, 0, 64, 0, 0, None) == 1     # batch < 1
+    assert L.bsattn_prepare(lay.handle, 1, 96, 0, 0, None) == 2     # head_dim
+    assert L.bsattn_prepare(lay.handle, 1, 64, 5, 0, None) == 1     # routed rows need a band layout
+    assert L.bsattn_prepare(lay.handle, 1, 64, 2000, 0, None) == 1  # num_routed > seq_len
+    assert L.bsattn_prepare(tok.handle, 1, 64, 0, 1, None) == 2     # no backward for token layouts
+    assert "backward" in bs.bsattn_last_error()
+
+
+def test_device_build_rejects_token_and_adaptive_layouts():
+    L = bs.lib()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    tok = bs.bsattn_make_token_layout(2, 1024, 16, 8, 2, 0)
+    ada = bs.bsattn_make_adaptive_layout(2, 1024, 4)
+    for lay in (tok, ada):
+        assert L.bsattn_layout_build_device(lay.handle, fake, fake, None) == 2
+        assert "device rule" in bs.bsattn_last_error()

@@ -13,6 +13,7 @@ import torch
 import block_sparse_transformer_amd as bs
 from oracle import adaptive as OD
 from oracle import attention as OA
+from conftest import record_parity
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -53,6 +54,8 @@ def _compare(o, l, ro, rl, tag):
     eo = float(np.abs(o - ro).max())
     el = float(np.abs(l - rl).max())
     _say(tag, f"max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    record_parity(tag, "O", eo, TOL_O)
+    record_parity(tag, "LSE", el, TOL_LSE)
     assert eo <= TOL_O and el <= TOL_LSE, (tag, eo, el)
 
 

@@ -22,6 +22,7 @@ import block_sparse_transformer_amd as bs
 from oracle import attention as OA
 from oracle import attention_grad as OG
 from oracle import layout as OL
+from conftest import record_parity
 from workloads import WORKLOADS, make_grad_output, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -63,6 +64,7 @@ def _compare(got, ref, what):
         e = np.abs(g - r).max() / scale
         errs.append(e)
         _say(what, name, "max|ref| %.4g  max|err|/max|ref| %.3e" % (scale, e))
+        record_parity(what, name + " (rel)", e, TOL_REL)
         assert e <= TOL_REL, f"{what}: {name} relative error {e}"
     return errs
 

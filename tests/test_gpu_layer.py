@@ -16,6 +16,7 @@ import torch
 import block_sparse_transformer_amd as bs
 from oracle import layer as OLY
 from oracle import layout as OL
+from conftest import record_parity
 from workloads import WORKLOADS, make_inputs, make_layer_params
 
 pytestmark = pytest.mark.gpu
@@ -65,6 +66,7 @@ def _case(wl, tag):
     scale = np.abs(ref).max()
     e = np.abs(got - ref).max() / scale
     _say(tag, "max|ref| %.4g  max|err|/max|ref| %.3e" % (scale, e))
+    record_parity(tag, "out (rel)", e, TOL_REL)
     assert e <= TOL_REL, f"{tag}: relative error {e}"
 
 

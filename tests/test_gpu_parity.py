@@ -17,6 +17,7 @@ import block_sparse_transformer_amd as bs
 from oracle import attention as OA
 from oracle import layout as OL
 from oracle import router as OR
+from conftest import record_parity
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -61,6 +62,9 @@ def _compare(o, l, ro, rl, dtype, what=""):
     fin = ~ninf_r
     eo = np.abs(o - ro).max() if o.size else 0.0
     el = np.abs(l[fin] - rl[fin]).max() if fin.any() else 0.0
+    _say(what, f"max|dO|={eo:.3e} (tol {to}) max|dLSE|={el:.3e} (tol {tl})")
+    record_parity(what, "O", eo, to)
+    record_parity(what, "LSE", el, tl)
     assert np.isfinite(o).all(), f"{what}: non-finite O"
     assert eo <= to, f"{what}: max |dO| = {eo}"
     assert el <= tl, f"{what}: max |dLSE| = {el}"
@@ -131,6 +135,38 @@ def test_bigbird_L8192_full_size_sampled():
     _sampled_check(WORKLOADS["bigbird-L8192"], "bigbird-L8192 full size, sampled rows")
 
 
+def _pairs_check(wl, pairs, tag):
+    """Every element of the given (b, h) pairs, from one call on the whole workload."""
+    _say(tag, wl, pairs)
+    inp = make_inputs(wl)
+    lay, olay = _layouts(wl)
+    o, l = _run(wl, inp, lay)
+    vl = inp.get("valid_len")
+    for b, h in pairs:
+        ro, rl = OA.attention_forward(inp["q"], inp["k"], inp["v"], olay, wl.scale,
+                                      valid_len=None if vl is None else vl.tolist(), heads=[h], batches=[b])
+        _compare(o[b, h], l[b, h], ro[b, h], rl[b, h], wl.dtype, f"{tag} (b={b}, h={h})")
+
+
+def test_bigbird_L8192_whole():
+    # the benchmark's own call: B=2, H=12, L=8192, every element of every (b, h)
+    _full_check(WORKLOADS["bigbird-L8192"], "bigbird-L8192 whole, B2 H12 (the benchmark call)")
+
+
+def test_bigbird_L2048_whole():
+    _full_check(WORKLOADS["bigbird-L2048"], "bigbird-L2048 whole, B8 H12")
+
+
+def test_window_pad_L16384_whole_pairs():
+    # three whole (b, h) pairs of the full-size call: the shortest and the
+    # longest valid length, and one between
+    wl = WORKLOADS["window-pad-L16384"]
+    vl = make_inputs(wl)["valid_len"].tolist()
+    order = sorted(range(wl.batch), key=lambda b: vl[b])
+    pairs = [(order[0], 0), (order[-1], wl.heads - 1), (order[len(order) // 2], wl.heads // 2)]
+    _pairs_check(wl, pairs, "window-pad-L16384 whole pairs")
+
+
 def test_bigbird_L8192_one_head_full():
     _full_check(WORKLOADS["bigbird-L8192"].with_(batch=1, heads=1), "bigbird-L8192 B1 H1 full")
 
@@ -193,6 +229,18 @@ def test_routed_ragged_k():
     for k in (1, 70, 130):
         _routed_case(WORKLOADS["routed-L4096"].with_(heads=2, seq_len=1024, routed_k=k, batch=2),
                      f"routed ragged k={k}")
+
+
+def test_routed_L4096_whole():
+    _routed_case(WORKLOADS["routed-L4096"], "routed-L4096 whole, B1 H32", full=True)
+
+
+def test_routed_wide_band_split_rows():
+    # a 512-token band splits the band rows into chunks: the band rows' merge and
+    # the routed rows' merge both write routed tokens inside those blocks
+    for d in (128, 64):
+        wl = WORKLOADS["routed-L4096"].with_(heads=2, seq_len=2048, band_tokens=512, head_dim=d, batch=1)
+        _routed_case(wl, f"routed band 512 D={d}")
 
 
 def test_routed_head_dim_64():

@@ -14,6 +14,7 @@ from oracle import adaptive as OD
 from oracle import attention as OA
 from oracle import attention_grad as OG
 from oracle import layout as OL
+from conftest import record_parity
 from workloads import WORKLOADS, make_grad_output, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -38,6 +39,8 @@ def _cmp(o, l, ro, rl, tag):
     eo = float(np.abs(o - ro).max())
     el = float(np.abs(l[~ninf] - rl[~ninf]).max()) if (~ninf).any() else 0.0
     _say(tag, f"dO={eo:.2e} dLSE={el:.2e}")
+    record_parity(tag, "O", eo, 2e-2)
+    record_parity(tag, "LSE", el, 1e-3)
     assert eo <= 2e-2 and el <= 1e-3, (tag, eo, el)
 
 
@@ -91,6 +94,7 @@ def _backward_check(wl, lay, olay, inp, tag):
     for name, gr, rf in zip(("dQ", "dK", "dV"), grads, refs):
         e = float(np.abs(gr.float().cpu().numpy() - rf).max() / max(np.abs(rf).max(), 1e-3))
         _say(tag, name, f"{e:.2e}")
+        record_parity(tag, name + " (rel)", e, 2e-2)
         assert e <= 2e-2, (tag, name, e)
 
 
