@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     bsattn_backward,
     bsattn_backward_workspace_size,
     bsattn_forward,
+    bsattn_forward_noalloc,
     bsattn_forward_routed,
     bsattn_last_error,
     bsattn_layer_forward,

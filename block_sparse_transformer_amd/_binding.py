@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                        _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_size_t, _c_vp]
     L.bsattn_set_profile_events.argtypes = [_c_vp, _c_vp]
     L.bsattn_prepare.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp]
+    L.bsattn_forward_noalloc.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp,
+                                         _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp]
     L.bsattn_status_string.argtypes = [ctypes.c_int]
     L.bsattn_status_string.restype = ctypes.c_char_p
     L.bsattn_last_error.argtypes = []
@@ -83,7 +85,7 @@ def lib() -> ctypes.CDLL:
                  "bsattn_layout_tile_masks", "bsattn_layout_upload",
                  "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
                  "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events",
-                 "bsattn_prepare"):
+                 "bsattn_prepare", "bsattn_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -285,6 +287,23 @@ def bsattn_forward(layout: Layout, q, k, v, out, lse, key_valid_len=None, scale:
     _check("bsattn_forward", lib().bsattn_forward(
         layout.handle, _dtype_code(q), B, H, L, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
         _ptr(key_valid_len), scale, _ptr(workspace), wbytes, _stream_handle(stream)))
+
+
+def bsattn_forward_noalloc(layout: Layout, q, k, v, out, lse, key_valid_len=None, scale: Optional[float] = None,
+                           stream=None) -> None:
+    """Enqueue the forward with the library's own device scratch as workspace (no allocation;
+    the shape must have been prepared with :func:`bsattn_prepare`)."""
+    import torch
+    _check_qkv(q, k, v, out)
+    B, H, L, D = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, L] tensor")
+    if key_valid_len is not None and (key_valid_len.dtype != torch.int32 or key_valid_len.numel() != B):
+        raise ValueError("key_valid_len must be int32 [B]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    _check("bsattn_forward_noalloc", lib().bsattn_forward_noalloc(
+        layout.handle, _dtype_code(q), B, H, L, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+        _ptr(key_valid_len), scale, _stream_handle(stream)))
 
 
 def bsattn_route_topk(q, w, k: int, routed_rows, stream=None) -> None:

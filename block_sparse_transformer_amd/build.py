@@ -29,6 +29,7 @@ SOURCES = [
     "kernels/router.hip",
     "kernels/layout_build.hip",
     "kernels/adaptive.hip",
+    "kernels/noalloc.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

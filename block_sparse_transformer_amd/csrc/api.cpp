@@ -22,6 +22,9 @@ namespace {
 thread_local std::string g_error;
 thread_local hipEvent_t g_ev_before = nullptr;
 thread_local hipEvent_t g_ev_after = nullptr;
+// Set while a call must not allocate (bsattn_forward_noalloc): a schedule that
+// was not built by bsattn_prepare is then an error instead of being built.
+thread_local bool g_no_build = false;
 
 bsattn_status fail(bsattn_status st, const char* fmt, ...) {
     char buf[512];
@@ -396,6 +399,8 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
             *out = sc;
             return BSATTN_OK;
         }
+    if (g_no_build)
+        return fail(BSATTN_ERR_STATE, "call shape (batch %d, head_dim %d) was not prepared with bsattn_prepare", B, D);
     const int32_t ipH = lay->items_per_head;
     const int64_t G = (int64_t)B * lay->H;
     auto routed_len = [&](int32_t v) {
@@ -767,6 +772,24 @@ bsattn_status adaptive_forward(const bsattn_layout* lay, int32_t B, int32_t D, c
 }
 
 }  // namespace
+
+namespace bsattn {
+
+bsattn_status set_failure(bsattn_status st, const char* msg) { return fail(st, "%s", msg); }
+
+bsattn_status forward_prepared_only(const bsattn_layout* lay, bsattn_dtype dtype, int32_t B, int32_t H,
+                                    int32_t L, int32_t D, const void* q, const void* k, const void* v,
+                                    void* out, float* lse, const int32_t* key_valid_len, float scale,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    struct Guard {
+        Guard() { g_no_build = true; }
+        ~Guard() { g_no_build = false; }
+    } guard;
+    return bsattn_forward(lay, dtype, B, H, L, D, q, k, v, out, lse, key_valid_len, scale, workspace,
+                          workspace_bytes, stream);
+}
+
+}  // namespace bsattn
 
 extern "C" {
 

@@ -169,6 +169,18 @@ struct BwdArgs {
     float scale_log2;         // scale * log2(e)
 };
 
+// ---- the allocation-free forward (kernels/noalloc.hip) ----
+// Size of the file-scope device array that serves as its workspace.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+// That array's device address on the current device (resolved once per device).
+hipError_t noalloc_scratch(void** ptr);
+// bsattn_forward that fails instead of building a schedule (api.cpp).
+bsattn_status forward_prepared_only(const bsattn_layout* lay, bsattn_dtype dtype, int32_t B, int32_t H,
+                                    int32_t L, int32_t D, const void* q, const void* k, const void* v,
+                                    void* out, float* lse, const int32_t* key_valid_len, float scale,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+bsattn_status set_failure(bsattn_status st, const char* msg);
+
 // ---- launchers (defined in kernels/*.hip) ----
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s,
                            hipEvent_t before, hipEvent_t after);

@@ -287,6 +287,23 @@ bsattn_status bsattn_forward(const bsattn_layout* layout, bsattn_dtype dtype,
                              void* out, float* lse, const int32_t* key_valid_len, float scale,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* bsattn_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same computation and kernels as bsattn_forward, without the workspace
+ * arguments: the workspace is a device array of 64 MiB that the library
+ * holds on each device it runs on until the process ends (resolved on the
+ * first call on a device).  The call allocates nothing, so the shape must
+ * have been built by bsattn_prepare(layout, batch, head_dim, 0, ...) first
+ * (BSATTN_ERR_STATE otherwise); a call whose bsattn_workspace_size exceeds
+ * 64 MiB returns BSATTN_ERR_UNSUPPORTED.  All calls on one device share the
+ * array: calls that overlap in time on one device race (order them on one
+ * stream).  Other arguments, layouts and errors as bsattn_forward. */
+bsattn_status bsattn_forward_noalloc(const bsattn_layout* layout, bsattn_dtype dtype,
+                                     int32_t batch, int32_t num_heads, int32_t seq_len, int32_t head_dim,
+                                     const void* q, const void* k, const void* v,
+                                     void* out, float* lse, const int32_t* key_valid_len, float scale,
+                                     hipStream_t stream);
+
 /* Routed-query selection (SQA page, section 2.1: a learned linear router
  * scores each query and keeps the top-k; section 3.2: the router runs in
  * higher precision than the model).  For each (b, h):

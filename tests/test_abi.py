@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
         "bsattn_forward", "bsattn_backward_workspace_size", "bsattn_backward",
         "bsattn_layer_workspace_size", "bsattn_layer_forward",
         "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
-        "bsattn_last_error", "bsattn_prepare"])
+        "bsattn_last_error", "bsattn_prepare", "bsattn_forward_noalloc"])
     lib = bs.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -190,6 +190,16 @@ def test_prepare_rejects_before_any_hip_call():
     assert L.bsattn_prepare(lay.handle, 1, 64, 2000, 0, None) == 1  # num_routed > seq_len
     assert L.bsattn_prepare(tok.handle, 1, 64, 0, 1, None) == 2     # no backward for token layouts
     assert "backward" in bs.bsattn_last_error()
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    L = bs.lib()
+    lay = bs.bsattn_make_layout(2, 1024, 64, 3, [0], 1, 0)
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    assert L.bsattn_forward_noalloc(None, 1, 1, 2, 1024, 64, fake, fake, fake, fake, fake, None,
+                                    ctypes.c_float(0.125), None) == 1
+    assert L.bsattn_forward_noalloc(lay.handle, 1, 1, 2, 1024, 96, fake, fake, fake, fake, fake, None,
+                                    ctypes.c_float(0.125), None) == 2
 
 
 def test_device_build_rejects_token_and_adaptive_layouts():
