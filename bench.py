@@ -11,15 +11,18 @@ the dQ pass, the dK/dV pass and the sums of split rows and columns) on the
 forward's outputs and a seeded upstream gradient; with ``--pass layer`` a
 step is one ``bsattn_layer_forward`` (qkv projection, head split, attention,
 head concatenation, output projection; no CPU baseline).  W untimed
-steps, then exactly K timed steps bracketed by device synchronisation; three
-copies of the inputs are rotated so that consecutive steps do not hit the
-256 MB last-level cache with the previous step's tensors.
+steps, then exactly K timed steps bracketed by device synchronisation; four
+sets of inputs and outputs (about 406 MB at bigbird-L8192) are rotated so that
+a step does not find the previous step's tensors in the 256 MB last-level
+cache.
 
 Prints ONE JSON line with the metric, ``roofline`` (the main attention
-kernel timed by HIP events that its own dispatch records, on one step in
-``--event-every`` of the timed region, priced against the bf16 dense MFMA
-peak) and ``cpu_baseline`` (the fp64 oracle on a bounded sample of the same
-workload, on the host cores).
+kernel timed by HIP events that its own dispatch records -- on every timed
+step when K <= 25, else on one in K // 25 -- mean and median over the timed
+region, priced against the bf16 dense MFMA peak; then the median of 25 warm
+launches on one input set) and ``cpu_baseline`` (the fp64 oracle on a
+bounded sample of the same workload, on the host cores, with the CPU model
+and the cores the process may use).
 """
 from __future__ import annotations
 
@@ -54,9 +57,14 @@ def parse_args():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default=None, help="default: the L=8192 BigBird workload")
-    p.add_argument("--rotate", type=int, default=3, help="input copies rotated across steps")
-    p.add_argument("--event-every", type=int, default=8,
-                   help="time the main kernel with HIP events on one timed step in this many")
+    p.add_argument("--rotate", type=int, default=4,
+                   help="input sets rotated across steps (4 bigbird-L8192 sets, inputs and outputs, hold "
+                        "about 406 MB: more than the 256 MB last-level cache)")
+    p.add_argument("--event-every", type=int, default=None,
+                   help="time the main kernel with HIP events on one timed step in this many "
+                        "(default: every step when K <= 25, else one in K // 25)")
+    p.add_argument("--warm-launches", type=int, default=25,
+                   help="after the timed region, launches on one input set (caches warm) timed by events")
     p.add_argument("--pass", dest="which", choices=("forward", "backward", "layer"), default="forward",
                    help="time the forward (default), the backward, or the whole attention layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -131,7 +139,20 @@ def cpu_baseline(wl, inp, layout_o, seconds: float):
             "kind": "oracle",
             "sample": f"{len(pairs)} of {wl.batch * wl.heads} (batch, head) pairs, all {wl.seq_len} query rows, "
                       f"dense fp64 masked attention; {dt:.2f} s measured, scaled to the whole job",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), **host_info()}
+
+
+def host_info():
+    """The host the CPU baseline ran on: CPU model and the cores this process may use."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline_adaptive(wl, inp, seconds: float):
@@ -158,7 +179,7 @@ def cpu_baseline_adaptive(wl, inp, seconds: float):
             "kind": "oracle",
             "sample": f"{len(pairs)} of {wl.batch * wl.heads} (batch, head) pairs, all {wl.seq_len} query rows, "
                       f"block selection and dense fp64 masked attention; {dt:.2f} s measured, scaled to the whole job",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), **host_info()}
 
 
 def cpu_baseline_bwd(wl, inp, do, layout_o, seconds: float):
@@ -184,7 +205,7 @@ def cpu_baseline_bwd(wl, inp, do, layout_o, seconds: float):
             "kind": "oracle",
             "sample": f"{len(pairs)} of {wl.batch * wl.heads} (batch, head) pairs, all {wl.seq_len} query rows, "
                       f"dense fp64 masked attention gradients; {dt:.2f} s measured, scaled to the whole job",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), **host_info()}
 
 
 def main():
@@ -256,6 +277,8 @@ def main():
     B, H, L, D = wl.batch, wl.heads, wl.seq_len, wl.head_dim
     outs = [torch.empty((B, H, L, D), dtype=base["q"].dtype, device=dev) for _ in sets]
     lses = [torch.empty((B, H, L), dtype=torch.float32, device=dev) for _ in sets]
+    rotation_bytes = sum(t.numel() * t.element_size() for st in sets for t in st.values()) + \
+        sum(o.numel() * o.element_size() + l_.numel() * l_.element_size() for o, l_ in zip(outs, lses))
     ws_bytes = bs.bsattn_workspace_size(lay, B, D)
     ws = torch.empty(max(1, (ws_bytes + 255) // 4), dtype=torch.float32, device=dev)
 
@@ -343,14 +366,15 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = bs.HipEvents(len(range(0, K, max(1, args.event_every))))
+    every = args.event_every if args.event_every is not None else (1 if K <= 25 else K // 25)
+    every = max(1, every)
+    ev = bs.HipEvents(len(range(0, K, every)))
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     set_ev = L_.bsattn_set_profile_events
     # The main kernel is timed by events its own dispatch records, on one step in
-    # `event_every` of the timed region: an instrumented step runs a few
-    # microseconds slower, and timing every step would charge that to the step.
-    every = max(1, args.event_every)
+    # `every` of the timed region (timing-only events, recorded by the dispatch
+    # itself, add no packets between kernels).
     timed = list(range(0, K, every))
     torch.cuda.synchronize()
     t_start.record(stream)
@@ -370,6 +394,18 @@ def main():
     kern_ms = [ev.elapsed_ms(n) for n in range(len(timed))]
     ev.destroy()
     kern_avg_ms = float(np.mean(kern_ms))
+    kern_med_ms = float(np.median(kern_ms))
+    # warm: the same launch on one input set, back to back, after the timed region
+    warm_ms = []
+    if args.warm_launches > 0:
+        wev = bs.HipEvents(args.warm_launches)
+        for n in range(args.warm_launches):
+            set_ev(wev.before[n], wev.after[n])
+            step(0)
+        set_ev(None, None)
+        torch.cuda.synchronize()
+        warm_ms = [wev.elapsed_ms(n) for n in range(args.warm_launches)]
+        wev.destroy()
 
     tokens = B * L
     value = tokens / (ms_step / 1e3)
@@ -413,7 +449,11 @@ def main():
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
+            "kernel_median_us": round(kern_med_ms * 1e3, 3),
             "kernel_timed_steps": len(kern_ms),
+            "kernel_warm_median_us": round(float(np.median(warm_ms)) * 1e3, 3) if warm_ms else None,
+            "input_sets": len(sets),
+            "rotation_bytes": int(rotation_bytes),
             "flop_per_launch": kernel_flops,
         },
         "cpu_baseline": None,
