@@ -8,11 +8,14 @@
 // section 3.1: FlashAttention-style computation restricted to non-zero
 // blocks; section 5: 64x64 blocks staged in on-chip memory).
 //
-// Design for gfx950 (CDNA4: wave64, 4 SIMDs and 160 KB LDS per CU, 8 XCDs):
+// Two attention kernels share the pieces below.  fwd_bf16_d64_kernel (D = 64)
+// runs one workgroup of eight waves per CU, each wave owning a whole 64-row
+// query tile and its own list of units; it is described where it is defined.
+// fwd_bf16_kernel<D> (D = 128, and the template at any D) runs two-wave
+// workgroups:
 //  * One workgroup = 2 waves = one 64-row query tile walking its list of key
 //    blocks; wave w owns query rows 32w..32w+31 against all 64 keys of every
-//    key tile.  The list (at most 64 blocks) is read once into a VGPR and
-//    each step takes its block index with v_readlane.
+//    key tile.
 //  * K and V tiles travel global -> LDS by direct LDS loads
 //    (global_load_lds_dwordx4, issued from inline asm so that only the
 //    pipeline's explicit waits govern them): no staging registers, no LDS
@@ -23,33 +26,33 @@
 //    consecutive keys of one d column -- exactly the A operand of
 //    O^T = V^T P^T, with no transpose pass over V.
 //  * Two LDS stages: the loads of the next tile are in flight while the
-//    current one is computed (a third stage cost more in occupancy than it
-//    gained in latency hiding).  Every step waits
-//    with an explicit vmcnt for its own tile only and passes a plain
-//    s_barrier (a fenced __syncthreads would wait for all loads in flight).
+//    current one is computed.  Every step waits with an explicit vmcnt for
+//    its own tile only and passes a plain s_barrier (a fenced __syncthreads
+//    would wait for all loads in flight).
 //  * Scores are computed transposed with v_mfma_f32_32x32x16_bf16: each lane
 //    holds 16 keys of ONE query per 32x32 block, so row reductions are in-lane
 //    plus one v_permlane32_swap between half-waves.  The same registers,
 //    rounded to bf16, are the B operand of the PV product (the order of a
 //    contraction index is free as long as both operands agree).
 //  * Online softmax in the log2 domain, p = exp2(s*scale*log2e - m): one FMA
-//    into v_exp_f32 (half rate on gfx950).  The running max m is taken from
-//    the first tile of a unit and afterwards raised only when half a tile's
-//    probabilities sum past kSumCap in some lane (then O and l are rescaled
-//    and that half is redone), so the per-tile row max and the O rescale are
-//    skipped on almost every tile and no probability overflows.  Row sums add
-//    the fp32 probabilities (a chained v_dot2c_f32_bf16 over the bf16 P gave
-//    wrong sums on gfx950 in testing, so it is not used).
-//  * Rows longer than 16 blocks (global rows, routed tiles) are split into
-//    chunks run by different workgroups; each writes a normalised fp32
+//    into v_exp_f32.  The running max m is taken from the first tile of a
+//    unit and afterwards raised only when half a tile's probabilities sum
+//    past kSumCap in some lane (then O and l are rescaled and that half is
+//    redone), so the per-tile row max and the O rescale are skipped on almost
+//    every tile and no probability overflows.  Row sums add the fp32
+//    probabilities: v_dot2c_f32_bf16 would add two products per instruction,
+//    but of the bf16-rounded probabilities, which moves LSE by up to 2^-9
+//    relative on a row with one dominant key -- more than the LSE tolerance.
+//  * Rows longer than the chunk size (global rows, routed tiles) are split
+//    into chunks run by different workgroups; each writes a normalised fp32
 //    partial and its LSE, and a small second launch merges them by
 //    log-sum-exp.  (Merging inside the attention kernel by the last chunk to
 //    arrive needs device-scope release/acquire fences, which on gfx950 write
 //    back and invalidate the XCD's L2 and slowed every resident workgroup.)
 //  * Scheduling: workgroups are dealt round-robin to the 8 XCDs; workgroup i
-//    runs on XCD i%8, and the kernel maps it to the (i/8)-th unit of the
-//    (batch, head) groups assigned to that XCD, so every group's K/V is read
-//    by one XCD and stays in its L2.
+//    runs on XCD i%8, and its list holds units of the (batch, head) groups
+//    assigned to that XCD, so every group's K/V is read by one XCD and stays
+//    in its L2.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
