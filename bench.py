@@ -5,7 +5,10 @@
 
 One step = one full forward (``bsattn_forward``: every non-zero 64x64 tile of
 the layout, the split of the dense global rows and their log-sum-exp merge)
-over one batch of the workload, inputs already resident in HBM.  With
+over one batch of the workload, inputs already resident in HBM.  For the
+routed workload a step is the router (``bsattn_route_topk``: fp64 scores and
+the per-head top-k) followed by ``bsattn_forward_routed`` (the band forward,
+the routed rows' tiles over every key and their merge).  With
 ``--pass backward`` a step is one full backward (``bsattn_backward``: delta,
 the dQ pass, the dK/dV pass and the sums of split rows and columns) on the
 forward's outputs and a seeded upstream gradient; with ``--pass layer`` a
@@ -19,8 +22,9 @@ cache.
 Prints ONE JSON line with the metric, ``roofline`` (the main attention
 kernel timed by HIP events that its own dispatch records -- on every timed
 step when K <= 25, else on one in K // 25 -- mean and median over the timed
-region, priced against the bf16 dense MFMA peak; then the median of 25 warm
-launches on one input set) and ``cpu_baseline`` (the fp64 oracle on a
+region, priced against the bf16 dense MFMA peak or the HBM bandwidth, whichever
+floor is larger for the kernel's algorithmic flops and bytes; then the median of
+25 warm launches on one input set) and ``cpu_baseline`` (the fp64 oracle on a
 bounded sample of the same workload, on the host cores, with the CPU model
 and the cores the process may use).
 """
@@ -44,6 +48,7 @@ METRIC_BWD = "block-sparse attn bwd tokens/s and effective TFLOP/s (% bf16 MFMA 
 METRIC_LAYER = "block-sparse attn layer fwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), L=8192"
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_HBM_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "fwd_bf16.hip")
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "bwd_bf16.hip")
 # the attention kernel that dominates a bf16 forward: one for D = 64, one for D = 128
@@ -182,6 +187,34 @@ def cpu_baseline_adaptive(wl, inp, seconds: float):
             "seconds": round(dt, 3), **host_info()}
 
 
+def cpu_baseline_routed(wl, inp, seconds: float):
+    """The oracle's routed path (fp64 scores, top-k, banded plus routed dense attention) on
+    whole (batch, head) pairs taken in order until ``seconds`` have passed, scaled to the job."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as OA
+    from oracle import router as OR
+    all_pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)]
+    pairs = []
+    t0 = time.perf_counter()
+    for b, h in all_pairs:
+        q, k, v = (inp[n][b:b + 1, h:h + 1] for n in ("q", "k", "v"))
+        rr = OR.topk_rows(OR.router_scores(q, inp["w"]), wl.routed_k)
+        OA.routed_attention_forward(q, k, v, rr, wl.band_tokens, wl.scale)
+        pairs.append((b, h))
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    full_s = dt * (wl.batch * wl.heads) / len(pairs)
+    return {"value": wl.batch * wl.seq_len / full_s, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(pairs)} of {wl.batch * wl.heads} (batch, head) pairs, all {wl.seq_len} query rows, "
+                      f"router top-{wl.routed_k} and dense fp64 masked attention; {dt:.2f} s measured, scaled to "
+                      "the whole job",
+            "seconds": round(dt, 3), **host_info()}
+
+
 def cpu_baseline_bwd(wl, inp, do, layout_o, seconds: float):
     """The oracle backward as it stands, on whole (batch, head) pairs taken in order until
     ``seconds`` have passed, scaled to the whole job."""
@@ -231,17 +264,14 @@ def main():
         return
 
     wl = WORKLOADS[args.workload or THROUGHPUT_WORKLOAD]
-    if wl.routed:
-        print("bench.py times the block-layout forward; routed workloads are parity cases", file=sys.stderr)
-        sys.exit(2)
     inp = make_inputs(wl)
 
-    if (wl.adaptive and args.which != "forward") or (wl.token and args.which == "backward"):
-        print("adaptive workloads are timed in the forward only, token-pattern workloads in the forward and "
-              "the layer", file=sys.stderr)
+    if ((wl.adaptive or wl.routed) and args.which != "forward") or (wl.token and args.which == "backward"):
+        print("adaptive and routed workloads are timed in the forward only, token-pattern workloads in the "
+              "forward and the layer", file=sys.stderr)
         sys.exit(2)
     t0 = time.perf_counter()
-    if wl.band:
+    if wl.band or wl.routed:
         lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
     elif wl.token:
         lay = bs.bsattn_make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
@@ -259,6 +289,9 @@ def main():
     if wl.token:
         # the global rows' tiles: ceil(n_global / 64) gathered-row tiles over every key block
         tiles += wl.batch * wl.heads * (-(-wl.num_global // 64)) * (wl.seq_len // 64)
+    if wl.routed:
+        # the routed rows, gathered into ceil(k / 64) tiles per head, over every key block
+        tiles += wl.batch * wl.heads * (-(-wl.routed_k // 64)) * (wl.seq_len // 64)
     stored_tiles = tiles
     masks = bs.bsattn_layout_tile_masks(lay)
     if masks is not None:
@@ -279,7 +312,7 @@ def main():
     lses = [torch.empty((B, H, L), dtype=torch.float32, device=dev) for _ in sets]
     rotation_bytes = sum(t.numel() * t.element_size() for st in sets for t in st.values()) + \
         sum(o.numel() * o.element_size() + l_.numel() * l_.element_size() for o, l_ in zip(outs, lses))
-    ws_bytes = bs.bsattn_workspace_size(lay, B, D)
+    ws_bytes = bs.bsattn_workspace_size(lay, B, D, wl.routed_k)
     ws = torch.empty(max(1, (ws_bytes + 255) // 4), dtype=torch.float32, device=dev)
 
     # Pre-marshalled C calls: the timed loop pays only the ctypes call itself.
@@ -353,6 +386,31 @@ def main():
             st = lfwd(*lcalls[i % len(lcalls)])
             if st != 0:
                 raise bs.BsattnError("bsattn_layer_forward", st)
+    elif wl.routed:
+        # one step: the router's top-k, then the band forward with the routed
+        # rows' tiles over every key and the merge of their split partials
+        kernel_flops = flops_per_step
+        k_r = wl.routed_k
+        wsr_bytes = bs.bsattn_route_workspace_size(B, H, L, k_r)
+        wsr = torch.empty(max(1, (wsr_bytes + 255) // 4), dtype=torch.float32, device=dev)
+        rrs = [torch.empty((B, H, k_r), dtype=torch.int32, device=dev) for _ in sets]
+        rcalls = []
+        for s, o, l, rr in zip(sets, outs, lses, rrs):
+            rcalls.append(((s["q"].data_ptr(), s["w"].data_ptr(), B, H, L, D, k_r, rr.data_ptr(), wsr.data_ptr(),
+                            ctypes.c_size_t(wsr_bytes), sh),
+                           (lay.handle, dtype_code, B, H, L, D, s["q"].data_ptr(), s["k"].data_ptr(),
+                            s["v"].data_ptr(), rr.data_ptr(), k_r, o.data_ptr(), l.data_ptr(), ctypes.c_float(wl.scale),
+                            ws.data_ptr(), ctypes.c_size_t(ws_bytes), sh)))
+        route, fwd_r = L_.bsattn_route_topk, L_.bsattn_forward_routed
+
+        def step(i):
+            rc, fc = rcalls[i % len(rcalls)]
+            st = route(*rc)
+            if st != 0:
+                raise bs.BsattnError("bsattn_route_topk", st)
+            st = fwd_r(*fc)
+            if st != 0:
+                raise bs.BsattnError("bsattn_forward_routed", st)
     else:
         kernel_flops = flops_per_step
 
@@ -412,6 +470,18 @@ def main():
     eff_tflops = flops_per_step / (ms_step / 1e3) / 1e12
     kern_tflops = kernel_flops / (kern_avg_ms / 1e3) / 1e12
     kname = "bwd_dkdv_kernel" if backward else main_kernel(D)
+    # the kernel's own algorithmic bytes: Q, K, V read and O, LSE written once (the
+    # backward's dK/dV pass: Q, K, V, dO read, dK, dV written, LSE and delta read)
+    kernel_bytes = wl.batch * wl.heads * wl.seq_len * ((6 if backward else 4) * wl.head_dim * elem + (8 if backward else 4))
+    kern_gbps = kernel_bytes / (kern_avg_ms / 1e3) / 1e9
+    # the roofline that bounds the kernel: the larger of its two floors at the
+    # published peaks; where they are within 10% the contraction's peak is kept
+    t_mfma = kernel_flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = kernel_bytes / (PEAK_HBM_GBPS * 1e9)
+    if t_hbm > 1.1 * t_mfma:
+        bound, achieved, peak, unit = "hbm", kern_gbps, PEAK_HBM_GBPS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", kern_tflops, round(PEAK_BF16_TFLOPS, 1), "TFLOP/s"
     traffic = traffic_from_profile(wl.name, kname, BWD_KERNEL_SOURCE if backward else KERNEL_SOURCE)
 
     result = {
@@ -435,19 +505,22 @@ def main():
             "nonzero_tiles": stored_tiles, "layout_density": round(tiles / (B * H * (L // 64) ** 2), 5),
             **({"num_global": wl.num_global, "random_tokens": wl.random_tokens} if wl.token else {}),
             **({"keep_blocks": wl.keep_blocks} if wl.adaptive else {}),
+            **({"routed_k": wl.routed_k} if wl.routed else {}),
         },
         "eff_tflops": round(eff_tflops, 2),
         "pct_bf16_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_alg_gbps": round(alg_bytes / (ms_step / 1e3) / 1e9, 1),
         "layout_build_host_us": round(layout_host_us, 1),
         "roofline": {
-            "bound": "mfma",
+            "bound": bound,
             "kernel": kname,
-            "achieved": round(kern_tflops, 2),
-            "peak": round(PEAK_BF16_TFLOPS, 1),
-            "unit": "TFLOP/s",
-            "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
+            "mfma_frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+            "hbm_frac": round(kern_gbps / PEAK_HBM_GBPS, 4),
             "kernel_avg_us": round(kern_avg_ms * 1e3, 3),
             "kernel_median_us": round(kern_med_ms * 1e3, 3),
             "kernel_timed_steps": len(kern_ms),
@@ -455,12 +528,13 @@ def main():
             "input_sets": len(sets),
             "rotation_bytes": int(rotation_bytes),
             "flop_per_launch": kernel_flops,
+            "alg_bytes_per_launch": kernel_bytes,
         },
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and args.which != "layer":
         from oracle import layout as OL
-        if wl.band:
+        if wl.band or wl.routed:
             olay = OL.make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
         elif wl.token:
             olay = OL.make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
@@ -472,6 +546,8 @@ def main():
                                   wl.random_blocks, wl.layout_seed)
         if wl.adaptive:
             result["cpu_baseline"] = cpu_baseline_adaptive(wl, inp, args.cpu_seconds)
+        elif wl.routed:
+            result["cpu_baseline"] = cpu_baseline_routed(wl, inp, args.cpu_seconds)
         elif backward:
             result["cpu_baseline"] = cpu_baseline_bwd(wl, inp, do_host, olay, args.cpu_seconds)
         else:

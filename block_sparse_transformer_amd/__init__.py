@@ -35,6 +35,7 @@ from ._binding import (  # noqa: F401
     bsattn_make_token_layout,
     bsattn_prepare,
     bsattn_route_topk,
+    bsattn_route_workspace_size,
     bsattn_set_profile_events,
     bsattn_status_string,
     bsattn_workspace_size,

@@ -60,7 +60,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_workspace_size.argtypes = [_c_vp, _c_int, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]
     L.bsattn_forward.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
                                  _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_size_t, _c_vp]
-    L.bsattn_route_topk.argtypes = [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp]
+    L.bsattn_route_workspace_size.argtypes = [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]
+    L.bsattn_route_topk.argtypes = [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp,
+                                    ctypes.c_size_t, _c_vp]
     L.bsattn_forward_routed.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp,
                                         _c_vp, _c_vp, _c_int, _c_vp, _c_vp, ctypes.c_float, _c_vp,
                                         ctypes.c_size_t, _c_vp]
@@ -84,7 +86,8 @@ def lib() -> ctypes.CDLL:
                  "bsattn_layout_token_links", "bsattn_layout_csr",
                  "bsattn_layout_tile_masks", "bsattn_layout_upload",
                  "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
-                 "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events",
+                 "bsattn_route_topk", "bsattn_route_workspace_size", "bsattn_forward_routed",
+                 "bsattn_set_profile_events",
                  "bsattn_prepare", "bsattn_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -306,7 +309,16 @@ def bsattn_forward_noalloc(layout: Layout, q, k, v, out, lse, key_valid_len=None
         _ptr(key_valid_len), scale, _stream_handle(stream)))
 
 
-def bsattn_route_topk(q, w, k: int, routed_rows, stream=None) -> None:
+def bsattn_route_workspace_size(batch: int, num_heads: int, seq_len: int, k: int) -> int:
+    n = ctypes.c_size_t()
+    _check("bsattn_route_workspace_size", lib().bsattn_route_workspace_size(batch, num_heads, seq_len, k,
+                                                                            ctypes.byref(n)))
+    return n.value
+
+
+def bsattn_route_topk(q, w, k: int, routed_rows, workspace=None, stream=None) -> None:
+    """Router top-k into routed_rows; a workspace of bsattn_route_workspace_size bytes
+    (uint8, on q's device) is allocated here when none is given."""
     import torch
     if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 4:
         raise ValueError("q must be a contiguous bf16 [B, H, L, D] tensor")
@@ -315,8 +327,12 @@ def bsattn_route_topk(q, w, k: int, routed_rows, stream=None) -> None:
         raise ValueError("w must be fp32 [D]")
     if routed_rows.dtype != torch.int32 or tuple(routed_rows.shape) != (B, H, k):
         raise ValueError("routed_rows must be int32 [B, H, k]")
+    need = bsattn_route_workspace_size(B, H, L, k)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
     _check("bsattn_route_topk", lib().bsattn_route_topk(_ptr(q), _ptr(w), B, H, L, D, k, _ptr(routed_rows),
-                                                        _stream_handle(stream)))
+                                                        _ptr(workspace), nbytes, _stream_handle(stream)))
 
 
 def bsattn_forward_routed(band_layout: Layout, q, k, v, routed_rows, out, lse, scale: Optional[float] = None,

@@ -1346,16 +1346,37 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     return ok();
 }
 
-bsattn_status bsattn_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,
-                                int32_t D, int32_t k, int32_t* routed_rows, hipStream_t stream) {
-    if (!q || !w || !routed_rows) return fail(BSATTN_ERR_INVALID_ARG, "NULL pointer");
+static bsattn_status check_route_shape(int32_t B, int32_t H, int32_t L, int32_t k) {
     if (B < 1 || H < 1 || L < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch, heads and seq_len must be >= 1");
-    if (D != 64 && D != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
     if (L > 8192) return fail(BSATTN_ERR_UNSUPPORTED, "seq_len > 8192 in the router");
     if (k < 1 || k > L) return fail(BSATTN_ERR_INVALID_ARG, "k must be in [1, seq_len] (got %d)", k);
+    if ((int64_t)B * H * ((L + 63) / 64) > 0x7fffffff)
+        return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+    return BSATTN_OK;
+}
+
+bsattn_status bsattn_route_workspace_size(int32_t B, int32_t H, int32_t L, int32_t k, size_t* bytes) {
+    if (!bytes) return fail(BSATTN_ERR_INVALID_ARG, "NULL argument");
+    bsattn_status st = check_route_shape(B, H, L, k);
+    if (st != BSATTN_OK) return st;
+    *bytes = route_workspace_bytes(B, H, L, k);
+    return ok();
+}
+
+bsattn_status bsattn_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,
+                                int32_t D, int32_t k, int32_t* routed_rows, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !w || !routed_rows) return fail(BSATTN_ERR_INVALID_ARG, "NULL pointer");
+    bsattn_status st = check_route_shape(B, H, L, k);
+    if (st != BSATTN_OK) return st;
+    if (D != 64 && D != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
     if (!aligned16(q)) return fail(BSATTN_ERR_INVALID_ARG, "q must be 16-byte aligned");
-    if ((int64_t)B * H > 0x7fffffff) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
-    hipError_t e = launch_route_topk(q, w, B, H, L, D, k, routed_rows, stream);
+    const size_t need = route_workspace_bytes(B, H, L, k);
+    if (!workspace || workspace_bytes < need)
+        return fail(BSATTN_ERR_INVALID_ARG, "router workspace too small (need %zu bytes, got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    hipError_t e = launch_route_topk(q, w, B, H, L, D, k, routed_rows, workspace, stream);
     if (e != hipSuccess) return hip_fail(e, "router launch");
     return ok();
 }

@@ -196,8 +196,10 @@ hipError_t launch_fill_tiles(const int32_t* skel, int32_t* live, const int4* uni
 hipError_t launch_gather_global(const FwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, const int32_t* row_ptr, int head_dim, int mask,
                           hipStream_t s, hipEvent_t before, hipEvent_t after);
+// router workspace: the fp64 scores [B, H, L]
+size_t route_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t k);
 hipError_t launch_route_topk(const void* q, const float* w, int32_t B, int32_t H, int32_t L,
-                             int32_t D, int32_t k, int32_t* out, hipStream_t s);
+                             int32_t D, int32_t k, int32_t* out, void* workspace, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before = nullptr,
                            hipEvent_t after = nullptr);

@@ -311,14 +311,23 @@ bsattn_status bsattn_forward_noalloc(const bsattn_layout* layout, bsattn_dtype d
  *   to right in fp64 (every product is exact, so the score is reproducible
  *   bit for bit), then the k rows with the largest score, ties to the lower
  *   row index, written ascending to routed_rows.
- *   q             device bf16 [B, H, L, D], D in {64, 128}.
- *   w             device fp32 [D].
- *   k             1 <= k <= L; L <= 8192.
- *   routed_rows   device int32 [B, H, k].
+ *   q                device bf16 [B, H, L, D], D in {64, 128}, 16-byte aligned.
+ *   w                device fp32 [D].
+ *   k                1 <= k <= L; L <= 8192.
+ *   routed_rows      device int32 [B, H, k].
+ *   workspace        device buffer of at least bsattn_route_workspace_size()
+ *                    bytes (B * H * L * 8: the fp64 scores), 16-byte
+ *                    aligned; it needs no initialisation and holds nothing
+ *                    between calls, and calls sharing it must not overlap.
+ * Errors: INVALID_ARG for NULL pointers, bad k or a short workspace;
+ * UNSUPPORTED for L > 8192 or another head_dim.  Nothing is allocated.
  * NaN scores give an unspecified (but valid, distinct) selection. */
+bsattn_status bsattn_route_workspace_size(int32_t batch, int32_t num_heads, int32_t seq_len, int32_t k,
+                                          size_t* bytes);
 bsattn_status bsattn_route_topk(const void* q, const float* w, int32_t batch, int32_t num_heads,
                                 int32_t seq_len, int32_t head_dim, int32_t k,
-                                int32_t* routed_rows, hipStream_t stream);
+                                int32_t* routed_rows, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /* Routed-query attention forward (SQA page, section 2.1): rows listed in
  * routed_rows [B, H, num_routed] (device int32, distinct, in [0, L)) attend to

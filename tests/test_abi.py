@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
         "bsattn_layout_token_links", "bsattn_make_adaptive_layout", "bsattn_adaptive_select", "bsattn_layout_destroy", "bsattn_workspace_size",
         "bsattn_forward", "bsattn_backward_workspace_size", "bsattn_backward",
         "bsattn_layer_workspace_size", "bsattn_layer_forward",
-        "bsattn_route_topk", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
+        "bsattn_route_topk", "bsattn_route_workspace_size", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
         "bsattn_last_error", "bsattn_prepare", "bsattn_forward_noalloc"])
     lib = bs.lib()
     for n in names:
@@ -111,10 +111,17 @@ def test_forward_rejects_before_any_hip_call():
                           -1.0, None, ws, None)
     assert st == 1
     # router argument checks
-    st = L.bsattn_route_topk(fake, fake, 1, 2, 1024, 64, 0, fake, None)
+    st = L.bsattn_route_topk(fake, fake, 1, 2, 1024, 64, 0, fake, fake, 1 << 20, None)
     assert st == 1
-    st = L.bsattn_route_topk(fake, fake, 1, 2, 16384, 64, 4, fake, None)
+    st = L.bsattn_route_topk(fake, fake, 1, 2, 16384, 64, 4, fake, fake, 1 << 20, None)
     assert st == 2
+    # router workspace: the fp64 scores of every row
+    assert bs.bsattn_route_workspace_size(1, 32, 4096, 64) == 32 * 4096 * 8
+    assert bs.bsattn_route_workspace_size(2, 3, 1000, 5) == 6 * 1000 * 8
+    st = L.bsattn_route_topk(fake, fake, 1, 32, 4096, 128, 64, fake, fake, 32 * 4096 * 8 - 1, None)
+    assert st == 1 and "workspace" in bs.bsattn_last_error()
+    st = L.bsattn_route_topk(fake, fake, 1, 32, 4096, 128, 64, fake, None, 0, None)
+    assert st == 1
     # profile events must be set in pairs
     assert L.bsattn_set_profile_events(fake, None) == 1
     assert L.bsattn_set_profile_events(None, None) == 0
