@@ -390,17 +390,11 @@ int device_capacity(int dev, int32_t D, int* cus_out = nullptr) {
 // group (which fits in its L2).  For every bin the device gets the unit
 // records and the flat list of the units' key blocks in order, at most
 // max_bin_units units and max_bin_tiles tiles per bin.
-bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32_t nru, int32_t rct,
-                           int32_t r_chunks, hipStream_t stream, bsattn_layout::Sched* out) {
-    // a built schedule is looked up before anything else: this runs on every call
-    std::lock_guard<std::mutex> guard(*lay->sched_mu);
-    for (const auto& sc : lay->scheds)
-        if (sc.batch == B && sc.head_dim == D && sc.nru == nru && sc.rct == rct) {
-            *out = sc;
-            return BSATTN_OK;
-        }
-    if (g_no_build)
-        return fail(BSATTN_ERR_STATE, "call shape (batch %d, head_dim %d) was not prepared with bsattn_prepare", B, D);
+}  // namespace
+
+// The host half of a schedule: pure computation on the layout, no HIP call.
+bsattn_status bsattn::pack_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32_t nru, int32_t rct,
+                            int32_t r_chunks, int capacity, int cus, PackedSchedule* ps) {
     const int32_t ipH = lay->items_per_head;
     const int64_t G = (int64_t)B * lay->H;
     auto routed_len = [&](int32_t v) {
@@ -435,8 +429,6 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
     }
     size_t max_units = 1;
     for (const auto& v : xu) max_units = std::max(max_units, v.size());
-    int cus = 1;
-    const int capacity = device_capacity(lay->device, D, &cus);
     const int32_t cus_per_xcd = std::max(1, cus / kXcds);
     const int32_t lists_per_wg = per_wave ? kQWaves : 1;
     int64_t nb64 = std::max<int64_t>((int64_t)capacity * lists_per_wg / kXcds, need);
@@ -581,12 +573,41 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
     if (wg_merge.empty()) fuse = false;
     if (units.empty()) units.push_back(make_int4(0, -1, 0, 0));
     if (tiles.empty()) tiles.push_back(0);
-    bsattn_layout::Sched sc{B, D, n_bins, nru, rct, nullptr, nullptr, nullptr, nullptr, nullptr};
+    if (!fuse) wg_merge.clear();
+    ps->n_bins = n_bins;
+    ps->units = std::move(units);
+    ps->unit_ptr = std::move(unit_ptr);
+    ps->tiles = std::move(tiles);
+    ps->tile_ptr = std::move(tile_ptr);
+    ps->wg_merge = std::move(wg_merge);
+    return BSATTN_OK;
+}
+
+namespace {
+
+bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32_t nru, int32_t rct,
+                           int32_t r_chunks, hipStream_t stream, bsattn_layout::Sched* out) {
+    // a built schedule is looked up before anything else: this runs on every call
+    std::lock_guard<std::mutex> guard(*lay->sched_mu);
+    for (const auto& sc : lay->scheds)
+        if (sc.batch == B && sc.head_dim == D && sc.nru == nru && sc.rct == rct) {
+            *out = sc;
+            return BSATTN_OK;
+        }
+    if (g_no_build)
+        return fail(BSATTN_ERR_STATE, "call shape (batch %d, head_dim %d) was not prepared with bsattn_prepare", B, D);
+    int cus = 1;
+    const int capacity = device_capacity(lay->device, D, &cus);
+    PackedSchedule ps;
+    bsattn_status st = pack_schedule(lay, B, D, nru, rct, r_chunks, capacity, cus, &ps);
+    if (st != BSATTN_OK) return st;
+    bsattn_layout::Sched sc{B, D, ps.n_bins, nru, rct, nullptr, nullptr, nullptr, nullptr, nullptr};
     void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
-    const void* src[5] = {units.data(), unit_ptr.data(), tiles.data(), tile_ptr.data(), wg_merge.data()};
-    const size_t sz[5] = {units.size() * sizeof(int4), unit_ptr.size() * sizeof(int32_t),
-                          tiles.size() * sizeof(int32_t), tile_ptr.size() * sizeof(int32_t),
-                          fuse ? wg_merge.size() * sizeof(int32_t) : 0};
+    const void* src[5] = {ps.units.data(), ps.unit_ptr.data(), ps.tiles.data(), ps.tile_ptr.data(),
+                          ps.wg_merge.data()};
+    const size_t sz[5] = {ps.units.size() * sizeof(int4), ps.unit_ptr.size() * sizeof(int32_t),
+                          ps.tiles.size() * sizeof(int32_t), ps.tile_ptr.size() * sizeof(int32_t),
+                          ps.wg_merge.size() * sizeof(int32_t)};
     hipError_t e = hipSuccess;
     for (int a = 0; a < 5 && e == hipSuccess; ++a) {
         if (sz[a] == 0) continue;

@@ -284,3 +284,20 @@ struct bsattn_layout {
     };
     mutable Bwd bwd;
 };
+
+namespace bsattn {
+
+// Host half of a forward schedule (no HIP call).  List i = x * n_bins + b
+// (XCD x, bin b) holds units [unit_ptr[i], unit_ptr[i + 1]) and flat tile
+// entries [tile_ptr[i], tile_ptr[i + 1]); wg_merge is empty unless the D = 64
+// kernel merges split rows itself.  capacity: workgroups resident at once;
+// cus: compute units.
+struct PackedSchedule {
+    int32_t n_bins = 0;
+    std::vector<int4> units;
+    std::vector<int32_t> unit_ptr, tiles, tile_ptr, wg_merge;
+};
+bsattn_status pack_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32_t nru, int32_t rct,
+                            int32_t r_chunks, int capacity, int cus, PackedSchedule* out);
+
+}  // namespace bsattn
