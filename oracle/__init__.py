@@ -22,6 +22,8 @@ Modules
               attention, head concatenation, output projection.
 ``adaptive``  the content-adaptive block layout (top blocks per query block
               by pooled fp64 scores) and its attention.
+``topr``      per-query top-keep attention: each query keeps its ``keep``
+              best keys by an in-order fp32 score, ties to the lower index.
 
 Parity pins (see ``tests/test_oracle_*.py``): every function is checked
 against something other than itself -- published splitmix64 outputs, closed
@@ -32,4 +34,4 @@ Parity unpinned: the concrete choice of random blocks beyond the
 hash stream itself (the composition of the per-row seed and the shuffle are
 this library's own specification; any uniform draw satisfies the pages).
 """
-from . import layout, attention, attention_grad, layer, router, adaptive  # noqa: F401
+from . import layout, attention, attention_grad, layer, router, adaptive, topr  # noqa: F401
