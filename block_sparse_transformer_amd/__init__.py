@@ -33,11 +33,13 @@ from ._binding import (  # noqa: F401
     bsattn_make_adaptive_layout,
     bsattn_make_layout,
     bsattn_make_token_layout,
+    bsattn_make_topr_layout,
     bsattn_prepare,
     bsattn_route_topk,
     bsattn_route_workspace_size,
     bsattn_set_profile_events,
     bsattn_status_string,
+    bsattn_topr_select,
     bsattn_workspace_size,
     forward,
     forward_routed,

@@ -47,6 +47,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_make_adaptive_layout.argtypes = [_c_int, _c_int, _c_int, ctypes.POINTER(_c_vp)]
     L.bsattn_adaptive_select.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
                                          ctypes.c_size_t, _c_vp]
+    L.bsattn_make_topr_layout.argtypes = [_c_int, _c_int, _c_int, ctypes.POINTER(_c_vp)]
+    L.bsattn_topr_select.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                     ctypes.c_size_t, _c_vp]
     L.bsattn_layout_token_links.argtypes = [_c_vp, ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_int),
                                             ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_int)]
     L.bsattn_layout_csr.argtypes = [_c_vp, ctypes.POINTER(_c_i32p), ctypes.POINTER(_c_i32p),
@@ -83,6 +86,7 @@ def lib() -> ctypes.CDLL:
     L.bsattn_last_error.restype = ctypes.c_char_p
     for name in ("bsattn_make_layout", "bsattn_make_band_layout", "bsattn_make_token_layout",
                  "bsattn_make_adaptive_layout", "bsattn_adaptive_select",
+                 "bsattn_make_topr_layout", "bsattn_topr_select",
                  "bsattn_layout_token_links", "bsattn_layout_csr",
                  "bsattn_layout_tile_masks", "bsattn_layout_upload",
                  "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
@@ -191,6 +195,29 @@ def bsattn_adaptive_select(layout: Layout, q, k, workspace=None, stream=None):
         layout.handle, B, H, L, D, q.data_ptr(), k.data_ptr(), cols.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return cols
+
+
+def bsattn_make_topr_layout(num_heads: int, seq_len: int, keep_tokens: int) -> Layout:
+    out = _c_vp()
+    _check("bsattn_make_topr_layout", lib().bsattn_make_topr_layout(num_heads, seq_len, keep_tokens,
+                                                                    ctypes.byref(out)))
+    lay = Layout(out.value, num_heads, seq_len)
+    lay.keep_tokens = keep_tokens
+    return lay
+
+
+def bsattn_topr_select(layout: Layout, q, k, workspace=None, stream=None):
+    """The kept-key words [B, H, L, L/64] (device int64; bit b of word j: key 64 j + b) of a
+    top-keep layout for q, k."""
+    import torch
+    B, H, L, D = q.shape
+    bits = torch.empty((B, H, L, L // 64), dtype=torch.int64, device=q.device)
+    if workspace is None:
+        workspace = _workspace(layout, q)
+    _check("bsattn_topr_select", lib().bsattn_topr_select(
+        layout.handle, B, H, L, D, q.data_ptr(), k.data_ptr(), bits.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+    return bits
 
 
 def bsattn_layout_token_links(layout: Layout) -> Tuple[np.ndarray, np.ndarray]:

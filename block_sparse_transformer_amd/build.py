@@ -30,6 +30,7 @@ SOURCES = [
     "kernels/layout_build.hip",
     "kernels/adaptive.hip",
     "kernels/noalloc.hip",
+    "kernels/topr.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

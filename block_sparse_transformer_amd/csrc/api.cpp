@@ -356,11 +356,11 @@ AdaptiveWs adaptive_workspace(const bsattn_layout* lay, int32_t B, int32_t D) {
 
 // Workgroups of the bf16 kernel that one device holds at once (CUs x
 // resident workgroups per CU), cached per device and head width.
-int device_capacity(int dev, int32_t D, int* cus_out = nullptr) {
+int device_capacity(int dev, int32_t D, int* cus_out = nullptr, bool two_wave = false) {
     static std::mutex mu;
-    static std::vector<int> cache, cus_cache;   // index 2 * dev + (D == 128)
+    static std::vector<int> cache, cus_cache;   // index 3 * dev + (D == 128 ? 1 : two_wave ? 2 : 0)
     std::lock_guard<std::mutex> g(mu);
-    const size_t idx = 2 * (size_t)dev + (D == 128 ? 1 : 0);
+    const size_t idx = 3 * (size_t)dev + (D == 128 ? 1 : two_wave ? 2 : 0);
     if (cache.size() <= idx) {
         cache.resize(idx + 1, 0);
         cus_cache.resize(idx + 1, 0);
@@ -370,7 +370,7 @@ int device_capacity(int dev, int32_t D, int* cus_out = nullptr) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             cus = 1;
         cus_cache[idx] = cus;
-        cache[idx] = cus * fwd_bf16_ctas_per_cu(D);
+        cache[idx] = cus * fwd_bf16_ctas_per_cu(D, two_wave);
     }
     if (cus_out) *cus_out = cus_cache[idx];
     return cache[idx];
@@ -417,7 +417,7 @@ bsattn_status bsattn::pack_schedule(const bsattn_layout* lay, int32_t B, int32_t
     }
     // D = 64 runs one workgroup of kQWaves waves per CU, one list (bin) per
     // wave; D = 128 one list per workgroup.
-    const bool per_wave = D == 64;
+    const bool per_wave = D == 64 && lay->kind != 4;   // top-keep layouts run the two-wave kernel
     const int32_t max_bin_units = kMaxBinUnits;
     const int32_t max_bin_tiles = kMaxBinTiles;
     int64_t need = 1;
@@ -597,7 +597,7 @@ bsattn_status get_schedule(const bsattn_layout* lay, int32_t B, int32_t D, int32
     if (g_no_build)
         return fail(BSATTN_ERR_STATE, "call shape (batch %d, head_dim %d) was not prepared with bsattn_prepare", B, D);
     int cus = 1;
-    const int capacity = device_capacity(lay->device, D, &cus);
+    const int capacity = device_capacity(lay->device, D, &cus, lay->kind == 4);
     PackedSchedule ps;
     bsattn_status st = pack_schedule(lay, B, D, nru, rct, r_chunks, capacity, cus, &ps);
     if (st != BSATTN_OK) return st;
@@ -790,6 +790,65 @@ bsattn_status adaptive_forward(const bsattn_layout* lay, int32_t B, int32_t D, c
                                const void* v, void* out, float* lse, float scale, int32_t* cols_out,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return adaptive_run(lay, B, D, q, k, v, out, lse, scale, cols_out, true, workspace, workspace_bytes, stream);
+}
+
+// Workspace of a forward over a per-query top-keep layout: the partial slots
+// of split rows (fp32 O, then LSE) and the kept-key words [B*H][L][nb].
+struct ToprWs {
+    size_t bits, total;
+};
+ToprWs topr_workspace(const bsattn_layout* lay, int32_t B, int32_t D) {
+    ToprWs w{};
+    w.bits = align256((size_t)B * lay->n_slots * slot_bytes(D));
+    w.total = w.bits + align256((size_t)B * lay->H * lay->L * lay->nb * sizeof(uint64_t));
+    return w;
+}
+
+// Forward over a per-query top-keep layout: the selection writes the kept-key
+// words (to bits_out too when given), then the two-wave attention kernel runs
+// every tile of the dense grid under that bit mask, then the merge of split
+// rows.  With attend = false only the selection runs (bits_out required).
+bsattn_status topr_run(const bsattn_layout* lay, int32_t B, int32_t D, const void* q, const void* k, const void* v,
+                       void* out, float* lse, float scale, uint64_t* bits_out, bool attend, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    const ToprWs w = topr_workspace(lay, B, D);
+    if (!workspace || workspace_bytes < w.total)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", w.total, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    char* base = (char*)workspace;
+    uint64_t* bits = bits_out ? bits_out : (uint64_t*)(base + w.bits);
+    hipError_t e = launch_topr_select(q, k, bits, B * lay->H, lay->L, D, lay->rule.r, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-keep selection launch");
+    if (!attend) return ok();
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.ws_o = (float*)workspace;
+    a.ws_lse = a.ws_o + (size_t)B * lay->n_slots * kBlock * D;
+    a.items = lay->d_items;
+    a.merges = lay->d_merges;
+    a.col_idx = lay->d_col_idx;
+    a.n_items = (int32_t)lay->items.size();
+    a.n_merges = (int32_t)lay->merges.size();
+    a.items_per_head = lay->items_per_head;
+    a.B = B; a.H = lay->H; a.L = lay->L; a.nb = lay->nb; a.n_slots = lay->n_slots;
+    a.n_routed = 0; a.n_rt = 0; a.r_chunks = 1; a.r_chunk_tiles = 1; a.r_slot_base = 0;
+    a.band = -1;
+    a.keep_bits = bits;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    bsattn_layout::Sched sc{};
+    bsattn_status st = get_schedule(lay, B, D, 0, 1, 1, stream, &sc);
+    if (st != BSATTN_OK) return st;
+    a.n_bins = sc.n_bins;
+    a.units = sc.d_units;
+    a.unit_ptr = sc.d_unit_ptr;
+    a.tiles = sc.d_tiles;
+    a.tile_ptr = sc.d_tile_ptr;
+    a.wg_merge = nullptr;
+    e = launch_fwd_bf16(a, D, MASK_BITS, stream, g_ev_before, g_ev_after);
+    if (e != hipSuccess) return hip_fail(e, "top-keep forward launch");
+    return ok();
 }
 
 }  // namespace
@@ -1091,6 +1150,58 @@ bsattn_status bsattn_adaptive_select(const bsattn_layout* lay, int32_t B, int32_
                         workspace_bytes, stream);
 }
 
+bsattn_status bsattn_make_topr_layout(int32_t num_heads, int32_t seq_len, int32_t keep_tokens, bsattn_layout** out) {
+    if (!out) return fail(BSATTN_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    bsattn_status st = check_layout_dims(num_heads, seq_len, kBlock);
+    if (st != BSATTN_OK) return st;
+    if (seq_len > kMaxTopLen)
+        return fail(BSATTN_ERR_UNSUPPORTED, "seq_len exceeds %d for a top-keep layout", kMaxTopLen);
+    if (keep_tokens < 1 || keep_tokens > seq_len)
+        return fail(BSATTN_ERR_INVALID_ARG, "keep_tokens must be in [1, seq_len] (got %d)", keep_tokens);
+    bsattn_layout* lay = new (std::nothrow) bsattn_layout();
+    if (!lay) return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    try {
+        const int32_t nb = seq_len / kBlock;
+        lay->H = num_heads;
+        lay->L = seq_len;
+        lay->nb = nb;
+        lay->block = kBlock;
+        lay->kind = 4;
+        lay->rule.nb = nb;
+        lay->rule.r = keep_tokens;
+        // every query block meets every key block; the kept keys are a bit mask per call
+        const int32_t rows = num_heads * nb;
+        lay->row_ptr.assign((size_t)rows + 1, 0);
+        lay->col_idx.assign((size_t)rows * nb, 0);
+        for (int32_t r = 0; r < rows; ++r) {
+            lay->row_ptr[r + 1] = (r + 1) * nb;
+            for (int32_t j = 0; j < nb; ++j) lay->col_idx[(size_t)r * nb + j] = j;
+        }
+    } catch (const std::bad_alloc&) {
+        delete lay;
+        return fail(BSATTN_ERR_NO_MEMORY, "layout allocation failed");
+    }
+    *out = lay;
+    return finish_layout(lay);
+}
+
+bsattn_status bsattn_topr_select(const bsattn_layout* lay, int32_t B, int32_t H, int32_t L, int32_t D, const void* q,
+                                 const void* k, uint64_t* keep_bits, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (lay->kind != 4) return fail(BSATTN_ERR_INVALID_ARG, "not a top-keep layout");
+    if (!keep_bits) return fail(BSATTN_ERR_INVALID_ARG, "keep_bits is NULL");
+    if (B < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", B);
+    if (H != lay->H || L != lay->L) return fail(BSATTN_ERR_INVALID_ARG, "H, L do not match the layout");
+    if (D != 64 && D != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+    if (!q || !k) return fail(BSATTN_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(keep_bits))
+        return fail(BSATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    return topr_run(lay, B, D, q, k, nullptr, nullptr, nullptr, 1.f, keep_bits, false, workspace, workspace_bytes,
+                    stream);
+}
+
 bsattn_status bsattn_layout_token_links(const bsattn_layout* lay, const int32_t** global_tokens,
                                         int32_t* num_global, const int32_t** links, int32_t* links_per_row) {
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
@@ -1232,6 +1343,10 @@ bsattn_status bsattn_workspace_size(const bsattn_layout* lay, int32_t batch, int
         *bytes = adaptive_workspace(lay, batch, head_dim).total;
         return ok();
     }
+    if (lay->kind == 4) {
+        *bytes = topr_workspace(lay, batch, head_dim).total;
+        return ok();
+    }
     size_t slots = (size_t)batch * lay->n_slots;
     int32_t n_rt = 0;
     if (num_routed > 0) {
@@ -1314,6 +1429,11 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
         if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "adaptive layouts are bf16 only");
         if (key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "adaptive layouts take no key padding");
         return adaptive_forward(lay, B, D, q, k, v, out, lse, scale, nullptr, workspace, workspace_bytes, stream);
+    }
+    if (lay->kind == 4) {
+        if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "top-keep layouts are bf16 only");
+        if (key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "top-keep layouts take no key padding");
+        return topr_run(lay, B, D, q, k, v, out, lse, scale, nullptr, true, workspace, workspace_bytes, stream);
     }
     size_t need = 0;
     st = bsattn_workspace_size(lay, B, D, 0, &need);
@@ -1562,8 +1682,9 @@ bsattn_status bsattn_layer_forward(const bsattn_layout* lay, int32_t B, int32_t 
                                    const void* b_proj, void* out, const int32_t* key_valid_len, float scale,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
-    if (lay->kind == 3)
-        return fail(BSATTN_ERR_UNSUPPORTED, "the layer takes block, band and token layouts (not adaptive ones)");
+    if (lay->kind == 3 || lay->kind == 4)
+        return fail(BSATTN_ERR_UNSUPPORTED,
+                    "the layer takes block, band and token layouts (not adaptive or top-keep ones)");
     if (!x || !w_qkv || !b_qkv || !w_proj || !b_proj || !out) return fail(BSATTN_ERR_INVALID_ARG, "NULL pointer");
     const void* ps[6] = {x, w_qkv, b_qkv, w_proj, b_proj, out};
     for (const void* p : ps)

@@ -21,10 +21,13 @@ constexpr int kMaxChunks = 32;    // upper bound on the split of one row
 // its 2 x 2 sub-blocks are allowed (bit 2a + b: query half a, key half b).
 // MASK_TOKEN: token-granular layouts -- the token band on a row's own tiles,
 // and gathered tiles of the global tokens' keys (key blocks nb, nb + 1, ...).
-enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2, MASK_SUB = 3, MASK_TOKEN = 4 };
+// MASK_BITS: per-query kept keys given as one 64-bit word per (query, key
+// block) (per-query top-keep layouts).
+enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2, MASK_SUB = 3, MASK_TOKEN = 4, MASK_BITS = 5 };
 constexpr int kMaxTokGlobal = 2048;   // global tokens of a token layout (their list lives in LDS)
 constexpr int kMaxLinks = 64;         // random tokens per row of a token layout
 constexpr int kMaxAdaptiveBlocks = 1024;   // key blocks per side of a content-adaptive layout
+constexpr int kMaxTopLen = 8192;           // sequence length of a per-query top-keep layout
 
 // One workgroup's share: query block `row` (= h*nb + i) over key blocks
 // col_idx[col_begin, col_end).  slot < 0: the whole row, written straight to
@@ -123,6 +126,9 @@ struct FwdArgs {
     const int32_t* links;
     const uint8_t* tok_global;
     const int32_t* row_merge;   // token layouts: [H * nb] merge item of a split row, -1 for a whole row
+    // per-query top-keep layouts (MASK_BITS): [B*H][L][nb] words, bit b of
+    // word (g, t, j) set iff query t of group g keeps key 64 j + b
+    const uint64_t* keep_bits;
     float scale;              // score scale
     float scale_log2;         // scale * log2(e)
 };
@@ -184,7 +190,12 @@ bsattn_status set_failure(bsattn_status st, const char* msg);
 // ---- launchers (defined in kernels/*.hip) ----
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s,
                            hipEvent_t before, hipEvent_t after);
-int fwd_bf16_ctas_per_cu(int head_dim);   // workgroups of the bf16 kernel resident per CU
+// workgroups of the bf16 kernel resident per CU; two_wave: the two-wave
+// kernel also at D = 64 (per-query top-keep layouts)
+int fwd_bf16_ctas_per_cu(int head_dim, bool two_wave = false);
+// per-query top-keep selection: bits [G][L][L/64] (see FwdArgs::keep_bits)
+hipError_t launch_topr_select(const void* q, const void* k, uint64_t* bits, int G, int L, int D, int keep,
+                              hipStream_t s);
 // content-adaptive layouts (kernels/adaptive.hip): block sums of q and k, then the
 // kept key blocks cols [G][nb][keep]; and the schedule's tile entries filled from cols
 hipError_t launch_adaptive_select(const void* q, const void* k, double* qs, double* ks, int32_t* cols, int G,
@@ -219,7 +230,8 @@ hipError_t launch_layout_build(const RowRule& rule, int kind, int32_t H, int32_t
 struct bsattn_layout {
     int32_t H = 0, L = 0, nb = 0, block = 0;
     int32_t kind = 0;           // 0: window/global/random rule, 1: token band, 2: token pattern,
-                                // 3: content-adaptive (key blocks chosen per call from q and k)
+                                // 3: content-adaptive (key blocks chosen per call from q and k),
+                                // 4: per-query top-keep (every key block; keys chosen per call)
     int32_t band_tokens = -1;
     bsattn::RowRule rule{};
     std::vector<int32_t> row_ptr, col_idx;

@@ -434,6 +434,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     // tiles keep the running max m as it is: the max is raised only when a
     // tile's probabilities grow too large (see softmax_pv), which on typical
     // rows happens rarely -- so no per-tile max is computed.
+    // MASK_BITS: kept-key words of this lane's query for tiles f, f + 1, f + 2
+    // (loaded two steps ahead, so the step's own memory wait covers them)
+    uint64_t wbits_cur = 0, wbits_n1 = 0, wbits_n2 = 0;
+    auto load_bits = [&](int e) -> uint64_t {
+        const int u = tile_unit(e);
+        const int g = rd(u_g, u);
+        const int t = rd(u_kind, u) * 64 + rloc;
+        return a.keep_bits[((size_t)g * a.L + t) * a.nb + tile_j(e)];
+    };
     auto softmax_prep = [&](int e, int kind, int tq, int valid, f32x16_t (&s)[2], bool first) {
         const int j = tile_j(e);
         if (MASK == MASK_SUB) {
@@ -478,6 +487,16 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                     for (int e = 0; e < 4; ++e)
                         if (gs[e] < 0 || abs(tq - gs[e]) <= a.band) s[kb][4 * g4 + e] = -INFINITY;
                 }
+        }
+        if (MASK == MASK_BITS) {
+            // this lane's query keeps key 32 kb + 8 (i / 4) + 4 hh + i % 4 iff its bit is set
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const uint32_t w = kb == 0 ? (uint32_t)wbits_cur : (uint32_t)(wbits_cur >> 32);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (!((w >> (8 * (i / 4) + 4 * hh + (i % 4))) & 1u)) s[kb][i] = -INFINITY;
+            }
         }
         if (first) m = tile_max(s);   // o = 0 and l = 0 here
     };
@@ -555,6 +574,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     load_q(tq_cur, g_cur, qf);
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf_n[c] = qf[c];
+    if (MASK == MASK_BITS) {
+        wbits_cur = load_bits(e0);
+        if (F > 1) wbits_n1 = load_bits(e1);
+    }
 
     wait_vmcnt<0>();
     issue_half<D>(ktile(g_cur, tile_j(e0)), 0, koffs, kl0);
@@ -585,6 +608,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         softmax_prep(e0, kind_cur, tq_cur, valid_cur, s_now, (e0 & kTileFirst) != 0);
         wait_vmcnt<0>();
         stage_barrier();
+        if (MASK == MASK_BITS && f + 2 < F) wbits_n2 = load_bits(e2);
         // Q of the next unit: loaded during the first step of the current unit
         // and, when the current unit ends here, moved in place for the scores
         // of tile f + 1 -- before this step's direct loads are issued, so that
@@ -655,6 +679,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         e0 = e1;
         e1 = e2;
         e2 = e3;
+        if (MASK == MASK_BITS) {
+            wbits_cur = wbits_n1;
+            wbits_n1 = wbits_n2;
+        }
     };
     for (int f = 0; f < F; f += 2) {
         step(std::integral_constant<int, 0>(), f, s_cur, s_nxt);
@@ -1577,21 +1605,28 @@ hipError_t launch_d64(const FwdArgs& a, hipStream_t s, hipEvent_t before, hipEve
 
 }  // namespace
 
-int fwd_bf16_ctas_per_cu(int head_dim) {
+int fwd_bf16_ctas_per_cu(int head_dim, bool two_wave) {
     // D = 64: one workgroup holds the whole CU.
-    if (head_dim == 64) return 1;
+    if (head_dim == 64 && !two_wave) return 1;
     int n = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<128, MASK_NONE>, kThreads, 0);
+    hipError_t e = head_dim == 64
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<64, MASK_BITS>, kThreads, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<128, MASK_NONE>, kThreads, 0);
     if (e != hipSuccess || n < 1) n = 1;
     // Measured on MI355X: with 32 KiB of LDS per workgroup only 4 workgroups
     // are resident per CU (the occupancy query reports 5); 64 KiB gives 2.
-    return n < 2 ? n : 2;
+    const int cap = head_dim == 64 ? 4 : 2;
+    return n < cap ? n : cap;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
                            hipEvent_t after) {
     hipError_t e;
-    if (head_dim == 64) {
+    if (mask == MASK_BITS) {
+        // the two-wave kernel at either width (the D = 64 kernel has no bit mask)
+        e = head_dim == 64 ? launch_fwd_t<64, MASK_BITS>(a, s, before, after)
+                           : launch_fwd_t<128, MASK_BITS>(a, s, before, after);
+    } else if (head_dim == 64) {
         e = mask == MASK_PAD   ? launch_d64<MASK_PAD>(a, s, before, after)
           : mask == MASK_BAND  ? launch_d64<MASK_BAND>(a, s, before, after)
           : mask == MASK_SUB   ? launch_d64<MASK_SUB>(a, s, before, after)

@@ -1,0 +1,216 @@
+// topr.hip -- per-query top-keep key selection.
+//
+// Adaptive Sparse Transformer page ("Adapt or Perish: 新手入门指南 – Adaptive
+// Sparse Transformer 核心原理与实战"), the importance-evaluation step: every
+// query keeps the keys with the highest scores (⌊L·r⌋ of them) and attends to
+// those alone.  The kept set is an integer decision, so it is taken on a
+// score with a fixed evaluation: q·k in fp32, products added in order of d
+// from +0 (each bf16 x bf16 product is exact in fp32, so fused and unfused
+// give the same bits), keys ranked by (score descending, index ascending).
+//
+// topr_select_kernel<TPQ, D>: one workgroup of 256 threads holds QW = 256/TPQ
+// queries of one (batch, head); TPQ threads share a query.  For every key
+// tile of 64 keys (staged in LDS as fp32, d-major, keys permuted so that a
+// thread's KPT = 64/TPQ keys are adjacent) each thread runs the exact chains
+// of its keys and keeps the scores in registers (L/TPQ <= 128 per thread).
+// Each score becomes a 32-bit key whose unsigned order is the score order
+// (-0 = +0, NaN lowest).  A radix select, four passes of 8 bits with a
+// 256-bin LDS histogram per query, finds the exact keep-th largest key T and
+// how many keys equal to T are kept; those are the lowest-index ones, counted
+// in index order with ballots.  The result is one 64-bit word per (query, key
+// tile): bit b set iff key 64j + b is kept.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../internal.h"
+
+namespace bsattn {
+namespace {
+
+constexpr int kSelThreads = 256;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+// unsigned key in score order: -0 and +0 alike, NaN below everything
+__device__ __forceinline__ uint32_t order_key(float s) {
+    if (s != s) return 0u;
+    if (s == 0.f) s = 0.f;
+    const uint32_t b = __float_as_uint(s);
+    return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+
+template <int TPQ, int D>
+__global__ __launch_bounds__(kSelThreads) void topr_select_kernel(const uint16_t* q, const uint16_t* k, uint64_t* bits,
+                                                                  int L, int keep, int qtiles) {
+    constexpr int QW = kSelThreads / TPQ;        // queries per workgroup
+    constexpr int KPT = 64 / TPQ;                // keys per thread per key tile
+    constexpr int NTMAX = 128 / KPT;             // key tiles a thread's registers hold
+    constexpr int BPL = 256 / TPQ;               // histogram bins per lane
+    constexpr int PIECES = 64 * D / 8 / kSelThreads;   // 16-byte pieces of a K tile per thread
+    static_assert(PIECES >= 1, "tile pieces");
+    __shared__ __attribute__((aligned(16))) float qs[QW][D];
+    __shared__ __attribute__((aligned(16))) float kt[D][64];
+    __shared__ uint32_t hist[QW][256];
+    __shared__ uint32_t s_digit[QW], s_above[QW];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int qi = tid / TPQ, tq = tid % TPQ;
+    const int gbase = (lane / TPQ) * TPQ;        // first lane of this query's group in the wave
+    const uint64_t gmask = TPQ == 64 ? ~0ull : ((1ull << TPQ) - 1ull);
+    const size_t g = blockIdx.x / qtiles;
+    const int t0 = (blockIdx.x % qtiles) * QW;
+    const int nt = L / 64;
+
+    for (int i = tid; i < QW * D; i += kSelThreads) {
+        const int r = i / D, d = i % D;
+        qs[r][d] = bf16_bits_to_float(q[(g * L + t0 + r) * D + d]);
+    }
+    const uint4* kg = (const uint4*)(k + g * (size_t)L * D);
+    uint4 pre[PIECES];
+    auto fetch = [&](int m) {
+#pragma unroll
+        for (int p = 0; p < PIECES; ++p) pre[p] = kg[(size_t)m * (64 * D / 8) + p * kSelThreads + tid];
+    };
+    // piece p of the tile: key r = p / (D / 8), columns d0 .. d0 + 7; key r sits
+    // at position KPT * (r % TPQ) + r / TPQ
+    auto stage = [&]() {
+#pragma unroll
+        for (int p = 0; p < PIECES; ++p) {
+            const int piece = p * kSelThreads + tid;
+            const int r = piece / (D / 8), d0 = (piece % (D / 8)) * 8;
+            const int pos = KPT * (r % TPQ) + r / TPQ;
+            const uint32_t w[4] = {pre[p].x, pre[p].y, pre[p].z, pre[p].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kt[d0 + 2 * e][pos] = bf16_bits_to_float(w[e] & 0xffffu);
+                kt[d0 + 2 * e + 1][pos] = bf16_bits_to_float(w[e] >> 16);
+            }
+        }
+    };
+
+    // ---- exact scores, kept as order keys ----
+    uint32_t key[NTMAX * KPT];
+    fetch(0);
+#pragma unroll
+    for (int m = 0; m < NTMAX; ++m) {
+        if (m < nt) {
+            __syncthreads();                 // previous tile's readers are done
+            stage();
+            __syncthreads();
+            if (m + 1 < nt) fetch(m + 1);    // in flight while this tile is scored
+            float acc[KPT];
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) acc[e] = 0.f;
+#pragma unroll 4
+            for (int d = 0; d < D; d += 4) {
+                const float4 qv = *(const float4*)&qs[qi][d];
+                const float qd[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+                for (int dd = 0; dd < 4; ++dd) {
+                    const float* kr = &kt[d + dd][KPT * tq];
+#pragma unroll
+                    for (int e = 0; e < KPT; ++e) acc[e] = fmaf(qd[dd], kr[e], acc[e]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) key[m * KPT + e] = order_key(acc[e]);
+        }
+    }
+
+    // ---- radix select of the keep-th largest key ----
+    uint32_t prefix = 0;
+    int need = keep;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int b = tq; b < 256; b += TPQ) hist[qi][b] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NTMAX * KPT; ++i) {
+            if (i / KPT < nt) {
+                const uint32_t kk = key[i];
+                const bool match = pass == 0 || (kk >> (shift + 8)) == (prefix >> (shift + 8));
+                if (match) atomicAdd(&hist[qi][(kk >> shift) & 255u], 1u);
+            }
+        }
+        __syncthreads();
+        uint32_t h[BPL], own = 0;
+#pragma unroll
+        for (int j = 0; j < BPL; ++j) {
+            h[j] = hist[qi][tq * BPL + j];
+            own += h[j];
+        }
+        uint32_t suffix = own;               // this lane's bins and those of higher lanes of the group
+#pragma unroll
+        for (int off = 1; off < TPQ; off <<= 1) {
+            const uint32_t o = __shfl_down(suffix, off, TPQ);
+            if (tq + off < TPQ) suffix += o;
+        }
+        uint32_t above = suffix - own;
+#pragma unroll
+        for (int j = BPL - 1; j >= 0; --j) {
+            if (above < (uint32_t)need && (uint32_t)need <= above + h[j]) {
+                s_digit[qi] = (uint32_t)(tq * BPL + j);
+                s_above[qi] = above;
+            }
+            above += h[j];
+        }
+        __syncthreads();
+        prefix |= s_digit[qi] << shift;
+        need -= (int)s_above[qi];
+        __syncthreads();                     // s_digit / hist are rewritten next pass
+    }
+
+    // ---- kept iff key > T, or key == T among the first `need` in index order ----
+    const uint32_t T = prefix;
+    uint32_t running = 0;
+    uint64_t words[NTMAX / TPQ > 0 ? NTMAX / TPQ : 1];
+#pragma unroll
+    for (int j = 0; j < (NTMAX / TPQ > 0 ? NTMAX / TPQ : 1); ++j) words[j] = 0;
+#pragma unroll
+    for (int m = 0; m < NTMAX; ++m) {
+        if (m < nt) {
+            uint64_t word = 0;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const uint32_t kk = key[m * KPT + e];
+                const bool eq = kk == T;
+                const uint64_t es = (__ballot(eq) >> gbase) & gmask;
+                const uint32_t rank = running + (uint32_t)__popcll(es & ((1ull << tq) - 1ull));
+                running += (uint32_t)__popcll(es);
+                const bool sel = kk > T || (eq && rank < (uint32_t)need);
+                const uint64_t ss = (__ballot(sel) >> gbase) & gmask;
+                word |= ss << (TPQ * e);     // key 64m + tq' + TPQ e  ->  bit tq' + TPQ e
+            }
+            if (tq == m % TPQ) words[m / TPQ] = word;
+        }
+    }
+    uint64_t* out = bits + (g * L + t0 + qi) * (size_t)nt;
+#pragma unroll
+    for (int j = 0; j < (NTMAX / TPQ > 0 ? NTMAX / TPQ : 1); ++j) {
+        const int m = tq + TPQ * j;
+        if (m < nt) out[m] = words[j];
+    }
+}
+
+template <int TPQ, int D>
+hipError_t launch_t(const void* q, const void* k, uint64_t* bits, int G, int L, int keep, hipStream_t s) {
+    constexpr int QW = kSelThreads / TPQ;
+    const int qtiles = L / QW;
+    hipLaunchKernelGGL((topr_select_kernel<TPQ, D>), dim3((unsigned)((int64_t)G * qtiles)), dim3(kSelThreads), 0, s,
+                       (const uint16_t*)q, (const uint16_t*)k, bits, L, keep, qtiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topr_select(const void* q, const void* k, uint64_t* bits, int G, int L, int D, int keep,
+                              hipStream_t s) {
+    if (L % 64 != 0 || L > kMaxTopLen || keep < 1 || keep > L || (D != 64 && D != 128)) return hipErrorInvalidValue;
+    if (L <= 2048) return D == 64 ? launch_t<16, 64>(q, k, bits, G, L, keep, s) : launch_t<16, 128>(q, k, bits, G, L, keep, s);
+    if (L <= 4096) return D == 64 ? launch_t<32, 64>(q, k, bits, G, L, keep, s) : launch_t<32, 128>(q, k, bits, G, L, keep, s);
+    return D == 64 ? launch_t<64, 64>(q, k, bits, G, L, keep, s) : launch_t<64, 128>(q, k, bits, G, L, keep, s);
+}
+
+}  // namespace bsattn

@@ -180,6 +180,37 @@ bsattn_status bsattn_adaptive_select(const bsattn_layout* layout, int32_t batch,
                                      int32_t* selected_blocks, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+/* A per-query top-keep layout (Adaptive Sparse Transformer page, the
+ * importance-evaluation step: each query keeps its floor(L r) best-scoring
+ * keys and attends to those alone).  For each (b, h) and query t:
+ *   rank[t, s] = sum over d = 0..D-1 of q[t, d] * k[s, d] in fp32, products
+ *   added in order of d from +0 (each bf16 product is exact in fp32, so the
+ *   value is reproducible bit for bit); query t keeps the keep_tokens keys of
+ *   highest rank, ties to the lower s, and attends to them with the usual
+ *   softmax of scale * q.k.  NaN ranks give an unspecified (but valid) choice
+ *   of exactly keep_tokens keys.
+ *   num_heads     H >= 1.
+ *   seq_len       L, a positive multiple of 64, L <= 8192.
+ *   keep_tokens   in [1, L]; floor(r L) keeps the fraction r.
+ *   out           receives the new layout (caller frees with bsattn_layout_destroy).
+ * Host only.  The stored CSR is the dense block grid (every key block in
+ * every row); the kept keys are chosen per call.  bsattn_forward on it is
+ * bf16 only and takes no key padding; its workspace (bsattn_workspace_size)
+ * also holds the kept-key words.  No backward. */
+bsattn_status bsattn_make_topr_layout(int32_t num_heads, int32_t seq_len, int32_t keep_tokens,
+                                      bsattn_layout** out);
+
+/* The selection step of a forward over a top-keep layout alone: writes the
+ * kept keys of every query to keep_bits (device uint64 [B, H, L, L/64],
+ * 16-byte aligned): bit b of word (b, h, t, j) is set iff query t keeps key
+ * 64 j + b, and every query has exactly keep_tokens bits set.  q, k device
+ * bf16 [B, H, L, D], D in {64, 128}; workspace as for bsattn_forward.
+ * Enqueued on `stream`. */
+bsattn_status bsattn_topr_select(const bsattn_layout* layout, int32_t batch, int32_t num_heads,
+                                 int32_t seq_len, int32_t head_dim, const void* q, const void* k,
+                                 uint64_t* keep_bits, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* Borrowed host view of a token layout (valid until destroy): the global
  * tokens [num_global], ascending, and the random tokens [H][L][links_per_row],
  * each row ascending and padded with -1.  INVALID_ARG for other layouts.  Any

@@ -9,7 +9,10 @@ namespace bsattn {
 hipError_t launch_fwd_bf16(const FwdArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t) {
     return hipErrorNotSupported;
 }
-int fwd_bf16_ctas_per_cu(int head_dim) { return head_dim == 64 ? 1 : 2; }
+int fwd_bf16_ctas_per_cu(int head_dim, bool two_wave) { return head_dim == 64 ? (two_wave ? 4 : 1) : 2; }
+hipError_t launch_topr_select(const void*, const void*, uint64_t*, int, int, int, int, hipStream_t) {
+    return hipErrorNotSupported;
+}
 hipError_t launch_adaptive_select(const void*, const void*, double*, double*, int32_t*, int, int, int, int,
                                   hipStream_t) {
     return hipErrorNotSupported;

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted([
         "bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr", "bsattn_layout_upload",
         "bsattn_layout_tile_masks", "bsattn_layout_build_device", "bsattn_make_token_layout",
-        "bsattn_layout_token_links", "bsattn_make_adaptive_layout", "bsattn_adaptive_select", "bsattn_layout_destroy", "bsattn_workspace_size",
+        "bsattn_layout_token_links", "bsattn_make_adaptive_layout", "bsattn_adaptive_select", "bsattn_make_topr_layout", "bsattn_topr_select", "bsattn_layout_destroy", "bsattn_workspace_size",
         "bsattn_forward", "bsattn_backward_workspace_size", "bsattn_backward",
         "bsattn_layer_workspace_size", "bsattn_layer_forward",
         "bsattn_route_topk", "bsattn_route_workspace_size", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",

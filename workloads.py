@@ -57,6 +57,7 @@ class Workload:
     num_global: int = 0             # token pattern: linspace global tokens
     random_tokens: int = 0          # token pattern: random tokens per row
     keep_blocks: int = 0            # > 0: content-adaptive layout keeping this many key blocks per row
+    keep_tokens: int = 0            # > 0: per-query top-keep layout keeping this many keys per query
 
     @property
     def routed(self) -> bool:
@@ -70,6 +71,10 @@ class Workload:
     @property
     def adaptive(self) -> bool:
         return self.keep_blocks > 0
+
+    @property
+    def topr(self) -> bool:
+        return self.keep_tokens > 0
 
     @property
     def num_blocks(self) -> int:
@@ -130,6 +135,11 @@ WORKLOADS = {
     "routed-L4096": Workload(
         name="routed-L4096", batch=1, heads=32, seq_len=4096, head_dim=128, dtype="bf16",
         data_seed=4, routed_k=64, band_tokens=32),
+    # Per-query top-keep attention (the Adaptive page's importance evaluation, r = 0.3): every
+    # query keeps its floor(0.3 L) = 614 best keys, chosen on the device, at a BERT-base head shape.
+    "topr-L2048": Workload(
+        name="topr-L2048", batch=1, heads=12, seq_len=2048, head_dim=64, dtype="bf16",
+        data_seed=10, keep_tokens=614),
 }
 
 THROUGHPUT_WORKLOAD = "bigbird-L8192"
