@@ -49,8 +49,12 @@ METRIC_LAYER = "block-sparse attn layer fwd tokens/s and effective TFLOP/s (% bf
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 PEAK_HBM_GBPS = 8000.0   # MI355X published HBM3E bandwidth
+# MI355X published fp32 vector peak (256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2 for packed
+# FMA x 2.4 GHz); code built without packed fp32 instructions can reach half of it
+PEAK_F32_VECTOR_TFLOPS = 157.3
 KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "fwd_bf16.hip")
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "bwd_bf16.hip")
+TOPR_KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "topr.hip")
 # the attention kernel that dominates a bf16 forward: one for D = 64, one for D = 128
 def main_kernel(head_dim: int) -> str:
     return "fwd_bf16_d64_kernel" if head_dim == 64 else "fwd_bf16_kernel"
@@ -215,6 +219,33 @@ def cpu_baseline_routed(wl, inp, seconds: float):
             "seconds": round(dt, 3), **host_info()}
 
 
+def cpu_baseline_topr(wl, inp, seconds: float):
+    """The oracle's top-keep forward (fp32 ranking scores, per-query selection, dense fp64
+    masked attention) on whole (batch, head) pairs taken in order until ``seconds`` have
+    passed, scaled to the job."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import topr as OT
+    all_pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)]
+    pairs = []
+    t0 = time.perf_counter()
+    for b, h in all_pairs:
+        OT.topr_attention_forward(inp["q"][b:b + 1], inp["k"][b:b + 1], inp["v"][b:b + 1], wl.keep_tokens,
+                                  wl.scale, heads=[h])
+        pairs.append((b, h))
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    full_s = dt * (wl.batch * wl.heads) / len(pairs)
+    return {"value": wl.batch * wl.seq_len / full_s, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(pairs)} of {wl.batch * wl.heads} (batch, head) pairs, all {wl.seq_len} query rows, "
+                      f"fp32 ranking scores, top-{wl.keep_tokens} per query and dense fp64 masked attention; "
+                      f"{dt:.2f} s measured, scaled to the whole job",
+            "seconds": round(dt, 3), **host_info()}
+
+
 def cpu_baseline_bwd(wl, inp, do, layout_o, seconds: float):
     """The oracle backward as it stands, on whole (batch, head) pairs taken in order until
     ``seconds`` have passed, scaled to the whole job."""
@@ -266,9 +297,9 @@ def main():
     wl = WORKLOADS[args.workload or THROUGHPUT_WORKLOAD]
     inp = make_inputs(wl)
 
-    if ((wl.adaptive or wl.routed) and args.which != "forward") or (wl.token and args.which == "backward"):
-        print("adaptive and routed workloads are timed in the forward only, token-pattern workloads in the "
-              "forward and the layer", file=sys.stderr)
+    if ((wl.adaptive or wl.routed or wl.topr) and args.which != "forward") or (wl.token and args.which == "backward"):
+        print("adaptive, routed and top-keep workloads are timed in the forward only, token-pattern workloads "
+              "in the forward and the layer", file=sys.stderr)
         sys.exit(2)
     t0 = time.perf_counter()
     if wl.band or wl.routed:
@@ -278,6 +309,8 @@ def main():
                                           wl.layout_seed)
     elif wl.adaptive:
         lay = bs.bsattn_make_adaptive_layout(wl.heads, wl.seq_len, wl.keep_blocks)
+    elif wl.topr:
+        lay = bs.bsattn_make_topr_layout(wl.heads, wl.seq_len, wl.keep_tokens)
     else:
         lay = bs.bsattn_make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                     wl.random_blocks, wl.layout_seed)
@@ -469,7 +502,7 @@ def main():
     value = tokens / (ms_step / 1e3)
     eff_tflops = flops_per_step / (ms_step / 1e3) / 1e12
     kern_tflops = kernel_flops / (kern_avg_ms / 1e3) / 1e12
-    kname = "bwd_dkdv_kernel" if backward else main_kernel(D)
+    kname = "bwd_dkdv_kernel" if backward else ("topr_select_kernel" if wl.topr else main_kernel(D))
     # the kernel's own algorithmic bytes: Q, K, V read and O, LSE written once (the
     # backward's dK/dV pass: Q, K, V, dO read, dK, dV written, LSE and delta read)
     kernel_bytes = wl.batch * wl.heads * wl.seq_len * ((6 if backward else 4) * wl.head_dim * elem + (8 if backward else 4))
@@ -478,11 +511,21 @@ def main():
     # published peaks; where they are within 10% the contraction's peak is kept
     t_mfma = kernel_flops / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = kernel_bytes / (PEAK_HBM_GBPS * 1e9)
-    if t_hbm > 1.1 * t_mfma:
+    if wl.topr:
+        # the timed kernel is the selection: 2 L^2 D flop of in-order fp32 FMA
+        # chains per (batch, head), bound by the vector ALU
+        sel_flops = 2.0 * B * H * L * L * D
+        kern_tflops = sel_flops / (kern_avg_ms / 1e3) / 1e12
+        bound, achieved, peak, unit = "alu", kern_tflops, PEAK_F32_VECTOR_TFLOPS, "TFLOP/s"
+        kernel_flops = sel_flops
+        kernel_bytes = B * H * L * 2 * D * elem + B * H * L * (L // 64) * 8
+        kern_gbps = kernel_bytes / (kern_avg_ms / 1e3) / 1e9
+    elif t_hbm > 1.1 * t_mfma:
         bound, achieved, peak, unit = "hbm", kern_gbps, PEAK_HBM_GBPS, "GB/s"
     else:
         bound, achieved, peak, unit = "mfma", kern_tflops, round(PEAK_BF16_TFLOPS, 1), "TFLOP/s"
-    traffic = traffic_from_profile(wl.name, kname, BWD_KERNEL_SOURCE if backward else KERNEL_SOURCE)
+    traffic = traffic_from_profile(wl.name, kname, BWD_KERNEL_SOURCE if backward else
+                                   TOPR_KERNEL_SOURCE if wl.topr else KERNEL_SOURCE)
 
     result = {
         "metric": METRIC_BWD if backward else (METRIC_LAYER if args.which == "layer" else METRIC),
@@ -506,6 +549,7 @@ def main():
             **({"num_global": wl.num_global, "random_tokens": wl.random_tokens} if wl.token else {}),
             **({"keep_blocks": wl.keep_blocks} if wl.adaptive else {}),
             **({"routed_k": wl.routed_k} if wl.routed else {}),
+            **({"keep_tokens": wl.keep_tokens} if wl.topr else {}),
         },
         "eff_tflops": round(eff_tflops, 2),
         "pct_bf16_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),
@@ -539,13 +583,15 @@ def main():
         elif wl.token:
             olay = OL.make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
                                         wl.layout_seed)
-        elif wl.adaptive:
+        elif wl.adaptive or wl.topr:
             olay = None   # chosen from the data, per (batch, head)
         else:
             olay = OL.make_layout(wl.heads, wl.seq_len, wl.block, wl.window_blocks, list(wl.global_blocks),
                                   wl.random_blocks, wl.layout_seed)
         if wl.adaptive:
             result["cpu_baseline"] = cpu_baseline_adaptive(wl, inp, args.cpu_seconds)
+        elif wl.topr:
+            result["cpu_baseline"] = cpu_baseline_topr(wl, inp, args.cpu_seconds)
         elif wl.routed:
             result["cpu_baseline"] = cpu_baseline_routed(wl, inp, args.cpu_seconds)
         elif backward:
