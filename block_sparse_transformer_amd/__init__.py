@@ -14,8 +14,11 @@ from ._binding import (  # noqa: F401
     BsattnError,
     Layout,
     backward,
+    backward_routed,
     bsattn_adaptive_select,
     bsattn_backward,
+    bsattn_backward_routed,
+    bsattn_backward_routed_workspace_size,
     bsattn_backward_workspace_size,
     bsattn_forward,
     bsattn_forward_noalloc,

@@ -73,6 +73,11 @@ def lib() -> ctypes.CDLL:
     L.bsattn_backward.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
                                   _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp,
                                   ctypes.c_size_t, _c_vp]
+    L.bsattn_backward_routed_workspace_size.argtypes = [_c_vp, _c_int, _c_int, _c_int,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+    L.bsattn_backward_routed.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
+                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_vp, ctypes.c_float,
+                                         _c_vp, ctypes.c_size_t, _c_vp]
     L.bsattn_layer_workspace_size.argtypes = [_c_vp, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]
     L.bsattn_layer_forward.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                        _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_size_t, _c_vp]
@@ -92,7 +97,8 @@ def lib() -> ctypes.CDLL:
                  "bsattn_layout_build_device", "bsattn_workspace_size", "bsattn_forward",
                  "bsattn_route_topk", "bsattn_route_workspace_size", "bsattn_forward_routed",
                  "bsattn_set_profile_events",
-                 "bsattn_prepare", "bsattn_forward_noalloc"):
+                 "bsattn_prepare", "bsattn_forward_noalloc", "bsattn_backward_routed_workspace_size",
+                 "bsattn_backward_routed"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -406,6 +412,34 @@ def bsattn_backward(layout: Layout, q, k, v, out, lse, dout, dq, dk, dv, key_val
         _stream_handle(stream)))
 
 
+def bsattn_backward_routed_workspace_size(layout: Layout, batch: int, head_dim: int, num_routed: int) -> int:
+    n = ctypes.c_size_t()
+    _check("bsattn_backward_routed_workspace_size", lib().bsattn_backward_routed_workspace_size(
+        layout.handle, batch, head_dim, num_routed, ctypes.byref(n)))
+    return n.value
+
+
+def bsattn_backward_routed(band_layout: Layout, q, k, v, out, lse, dout, routed_rows, dq, dk, dv,
+                           scale: Optional[float] = None, workspace=None, stream=None) -> None:
+    """Enqueue the routed-query backward; all tensors are caller-allocated device tensors."""
+    import torch
+    _check_qkv(q, k, v, out)
+    _check_qkv(q, dout, dq, dk)
+    _check_qkv(q, dv, dv, dv)
+    B, H, L, D = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, L] tensor")
+    if routed_rows.dtype != torch.int32 or routed_rows.dim() != 3 or tuple(routed_rows.shape[:2]) != (B, H) \
+            or not routed_rows.is_contiguous():
+        raise ValueError("routed_rows must be a contiguous int32 [B, H, k] tensor")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bsattn_backward_routed", lib().bsattn_backward_routed(
+        band_layout.handle, _dtype_code(q), B, H, L, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+        _ptr(dout), _ptr(routed_rows), int(routed_rows.shape[2]), _ptr(dq), _ptr(dk), _ptr(dv), scale,
+        _ptr(workspace), wbytes, _stream_handle(stream)))
+
+
 def bsattn_layer_workspace_size(layout: Layout, batch: int, head_dim: int) -> int:
     n = ctypes.c_size_t()
     _check("bsattn_layer_workspace_size",
@@ -478,6 +512,18 @@ def backward(q, k, v, out, lse, dout, layout: Layout, key_valid_len=None, scale:
         n = bsattn_backward_workspace_size(layout, q.shape[0], q.shape[3])
         workspace = torch.empty((n + 255) // 4, dtype=torch.float32, device=q.device)
     bsattn_backward(layout, q, k, v, out, lse, dout, dq, dk, dv, key_valid_len, scale, workspace)
+    return dq, dk, dv
+
+
+def backward_routed(q, k, v, out, lse, dout, band_layout: Layout, routed_rows, scale: Optional[float] = None,
+                    workspace=None):
+    """Allocate (dq, dk, dv) and workspace with torch and run :func:`bsattn_backward_routed`."""
+    import torch
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if workspace is None:
+        n = bsattn_backward_routed_workspace_size(band_layout, q.shape[0], q.shape[3], int(routed_rows.shape[2]))
+        workspace = torch.empty((n + 255) // 4, dtype=torch.float32, device=q.device)
+    bsattn_backward_routed(band_layout, q, k, v, out, lse, dout, routed_rows, dq, dk, dv, scale, workspace)
     return dq, dk, dv
 
 

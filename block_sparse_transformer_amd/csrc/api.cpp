@@ -177,6 +177,14 @@ void free_bwd_device(bsattn_layout* lay) {
     bw.d_k_idx = nullptr;
     bw.d_k_sub = nullptr;
     bw.uploaded = false;
+    for (auto& rb : lay->rbwd) {
+        (void)hipFree(rb.d_rq_items);
+        (void)hipFree(rb.d_k_items);
+        (void)hipFree(rb.d_rq_sums);
+        (void)hipFree(rb.d_k_sums);
+        (void)hipFree(rb.d_k_idx);
+    }
+    lay->rbwd.clear();
 }
 
 void free_device(bsattn_layout* lay) {
@@ -266,7 +274,133 @@ bsattn_status upload_bwd(const bsattn_layout* lay, hipStream_t stream) {
     return BSATTN_OK;
 }
 
+// Backward lists of a routed call with n_rt routed tiles per (b, h) on a band
+// layout.  dQ: the band rows' items are the layout's own (lay->bwd); each
+// routed tile r of head h adds r_chunks items over key blocks [c per, (c + 1)
+// per), all written as partials after the band rows' slots, and one gathered
+// sum.  dK/dV: every column lists the band's query blocks, then the routed
+// tiles as entries nb + r; columns longer than kChunkTiles are split.  Per
+// head, longest first, padded with empty items to a common length.
+bsattn_layout::RoutedBwd build_routed_bwd(const bsattn_layout* lay, int32_t n_rt) {
+    bsattn_layout::RoutedBwd rb;
+    const int32_t H = lay->H, nb = lay->nb;
+    rb.n_rt = n_rt;
+    split_row(nb, &rb.r_chunks, &rb.per);
+    rb.r_chunks = (nb + rb.per - 1) / rb.per;
+    const int32_t base = lay->bwd.n_qslots;
+    rb.n_qslots = base + H * n_rt * rb.r_chunks;
+    rb.rq_per_head = n_rt * rb.r_chunks;
+    for (int32_t h = 0; h < H; ++h)
+        for (int32_t r = 0; r < n_rt; ++r) {
+            const int32_t first = base + (h * n_rt + r) * rb.r_chunks;
+            rb.rq_sums.push_back({h * nb + r, first, rb.r_chunks, 0});
+            for (int32_t c = 0; c < rb.r_chunks; ++c)
+                rb.rq_items.push_back({h * nb + r, c * rb.per, std::min(nb, (c + 1) * rb.per), first + c});
+        }
+    // columns: the band's CSC plus the routed tiles
+    std::vector<int32_t> cptr((size_t)H * nb + 1, 0);
+    for (int32_t h = 0; h < H; ++h)
+        for (int32_t i = 0; i < nb; ++i) {
+            const int32_t r = h * nb + i;
+            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a) ++cptr[(size_t)h * nb + lay->col_idx[a] + 1];
+        }
+    for (size_t c = 1; c < cptr.size(); ++c) cptr[c] += n_rt;
+    for (size_t c = 0; c + 1 < cptr.size(); ++c) cptr[c + 1] += cptr[c];
+    rb.k_idx.assign((size_t)cptr.back(), 0);
+    std::vector<int32_t> fill(cptr.begin(), cptr.end() - 1);
+    for (int32_t h = 0; h < H; ++h)
+        for (int32_t i = 0; i < nb; ++i) {
+            const int32_t r = h * nb + i;
+            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a)
+                rb.k_idx[(size_t)fill[(size_t)h * nb + lay->col_idx[a]]++] = i;
+        }
+    for (size_t c = 0; c + 1 < cptr.size(); ++c)
+        for (int32_t r = 0; r < n_rt; ++r) rb.k_idx[(size_t)fill[c]++] = nb + r;
+    std::vector<std::vector<BwdItem>> heads((size_t)H);
+    rb.n_kslots = 0;
+    for (int32_t hb = 0; hb < H * nb; ++hb) {
+        auto& hi = heads[(size_t)(hb / nb)];
+        const int32_t b0 = cptr[(size_t)hb], b1 = cptr[(size_t)hb + 1], len = b1 - b0;
+        if (len <= kChunkTiles) {
+            hi.push_back({hb, b0, b1, -1});
+            continue;
+        }
+        int32_t nch, per;
+        split_row(len, &nch, &per);
+        rb.k_sums.push_back({hb, rb.n_kslots, nch, 0});
+        for (int32_t c = 0; c < nch; ++c) {
+            const int32_t s0 = b0 + c * per;
+            hi.push_back({hb, s0, std::min(b1, s0 + per), rb.n_kslots++});
+        }
+    }
+    rb.k_per_head = 0;
+    for (auto& hi : heads) {
+        std::stable_sort(hi.begin(), hi.end(),
+                         [](const BwdItem& x, const BwdItem& y) { return (x.end - x.begin) > (y.end - y.begin); });
+        rb.k_per_head = std::max<int32_t>(rb.k_per_head, (int32_t)hi.size());
+    }
+    for (auto& hi : heads) {
+        rb.k_items.insert(rb.k_items.end(), hi.begin(), hi.end());
+        for (size_t a = hi.size(); a < (size_t)rb.k_per_head; ++a) rb.k_items.push_back({-1, 0, 0, -1});
+    }
+    return rb;
+}
+
+// The routed lists for n_rt tiles, built and uploaded on first use (caller holds sched_mu).
+bsattn_status get_routed_bwd(const bsattn_layout* lay, int32_t n_rt, hipStream_t stream,
+                             const bsattn_layout::RoutedBwd** out) {
+    for (const auto& rb : lay->rbwd)
+        if (rb.n_rt == n_rt) {
+            *out = &rb;
+            return BSATTN_OK;
+        }
+    if (g_no_build) return fail(BSATTN_ERR_STATE, "routed backward lists were not prepared with bsattn_prepare");
+    bsattn_layout::RoutedBwd rb;
+    try {
+        rb = build_routed_bwd(lay, n_rt);
+    } catch (const std::bad_alloc&) {
+        return fail(BSATTN_ERR_NO_MEMORY, "routed backward list allocation failed");
+    }
+    void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    const void* src[5] = {rb.rq_items.data(), rb.k_items.data(), rb.rq_sums.data(), rb.k_sums.data(),
+                          rb.k_idx.data()};
+    const size_t sz[5] = {rb.rq_items.size() * sizeof(BwdItem), rb.k_items.size() * sizeof(BwdItem),
+                          rb.rq_sums.size() * sizeof(BwdSum), rb.k_sums.size() * sizeof(BwdSum),
+                          rb.k_idx.size() * sizeof(int32_t)};
+    hipError_t e = hipSuccess;
+    for (int a = 0; a < 5 && e == hipSuccess; ++a) {
+        e = hipMalloc(&p[a], std::max<size_t>(sz[a], 16));
+        if (e == hipSuccess && sz[a] > 0) e = hipMemcpyAsync(p[a], src[a], sz[a], hipMemcpyHostToDevice, stream);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        for (int a = 0; a < 5; ++a) (void)hipFree(p[a]);
+        return fail(BSATTN_ERR_NO_MEMORY, "routed backward list upload: %s", hipGetErrorString(e));
+    }
+    rb.d_rq_items = (BwdItem*)p[0];
+    rb.d_k_items = (BwdItem*)p[1];
+    rb.d_rq_sums = (BwdSum*)p[2];
+    rb.d_k_sums = (BwdSum*)p[3];
+    rb.d_k_idx = (int32_t*)p[4];
+    lay->rbwd.push_back(std::move(rb));
+    *out = &lay->rbwd.back();
+    return BSATTN_OK;
+}
+
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace of bsattn_backward_routed: delta, then the dQ (band and routed),
+// dK and dV partial slots.
+void routed_bwd_workspace_parts(const bsattn_layout* lay, int32_t B, int32_t D, int32_t n_qslots, int32_t n_kslots,
+                                size_t* off_dq, size_t* off_dk, size_t* off_dv, size_t* total) {
+    const size_t delta = align256((size_t)B * lay->H * lay->L * sizeof(float));
+    const size_t qs = align256((size_t)B * n_qslots * kBlock * D * sizeof(float));
+    const size_t ks = align256((size_t)B * n_kslots * kBlock * D * sizeof(float));
+    *off_dq = delta;
+    *off_dk = delta + qs;
+    *off_dv = delta + qs + ks;
+    *total = delta + qs + 2 * ks;
+}
 
 // Workspace of bsattn_backward: delta, then the dQ, dK and dV partial slots.
 void bwd_workspace_parts(const bsattn_layout* lay, int32_t B, int32_t D, size_t* off_dq, size_t* off_dk,
@@ -818,7 +952,9 @@ bsattn_status topr_run(const bsattn_layout* lay, int32_t B, int32_t D, const voi
         return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     char* base = (char*)workspace;
     uint64_t* bits = bits_out ? bits_out : (uint64_t*)(base + w.bits);
-    hipError_t e = launch_topr_select(q, k, bits, B * lay->H, lay->L, D, lay->rule.r, stream);
+    // profile events time the selection, the kernel that dominates a top-keep forward
+    hipError_t e = launch_topr_select(q, k, bits, B * lay->H, lay->L, D, lay->rule.r, stream, g_ev_before,
+                                      g_ev_after);
     if (e != hipSuccess) return hip_fail(e, "top-keep selection launch");
     if (!attend) return ok();
     FwdArgs a{};
@@ -846,7 +982,7 @@ bsattn_status topr_run(const bsattn_layout* lay, int32_t B, int32_t D, const voi
     a.tiles = sc.d_tiles;
     a.tile_ptr = sc.d_tile_ptr;
     a.wg_merge = nullptr;
-    e = launch_fwd_bf16(a, D, MASK_BITS, stream, g_ev_before, g_ev_after);
+    e = launch_fwd_bf16(a, D, MASK_BITS, stream, nullptr, nullptr);
     if (e != hipSuccess) return hip_fail(e, "top-keep forward launch");
     return ok();
 }
@@ -1395,6 +1531,11 @@ bsattn_status bsattn_prepare(const bsattn_layout* lay, int32_t batch, int32_t he
         std::lock_guard<std::mutex> guard(*lay->sched_mu);
         st = upload_bwd(lay, stream);
         if (st != BSATTN_OK) return st;
+        if (num_routed > 0) {   // the routed backward's lists
+            const bsattn_layout::RoutedBwd* rb = nullptr;
+            st = get_routed_bwd(lay, (num_routed + kBlock - 1) / kBlock, stream, &rb);
+            if (st != BSATTN_OK) return st;
+        }
     }
     return ok();
 }
@@ -1664,6 +1805,132 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
     if (e != hipSuccess) return hip_fail(e, "backward dK/dV launch");
     if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 1, stream)) != hipSuccess)
         return hip_fail(e, "backward dK/dV sum launch");
+    return ok();
+}
+
+bsattn_status bsattn_backward_routed_workspace_size(const bsattn_layout* lay, int32_t batch, int32_t head_dim,
+                                                    int32_t num_routed, size_t* bytes) {
+    if (!lay || !bytes) return fail(BSATTN_ERR_INVALID_ARG, "NULL argument");
+    if (lay->kind != 1) return fail(BSATTN_ERR_INVALID_ARG, "the routed backward needs a band layout");
+    if (batch < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch must be >= 1");
+    if (head_dim != 64 && head_dim != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (num_routed < 1 || num_routed > lay->L)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_routed must be in [1, seq_len] (got %d)", num_routed);
+    const int32_t n_rt = (num_routed + kBlock - 1) / kBlock;
+    int32_t rch, per;
+    split_row(lay->nb, &rch, &per);
+    rch = (lay->nb + per - 1) / per;
+    // column slots: count the split columns' chunks as the list builder does
+    int32_t n_kslots = 0;
+    std::vector<int32_t> len((size_t)lay->H * lay->nb, n_rt);
+    for (int32_t r = 0; r < lay->H * lay->nb; ++r)
+        for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a)
+            ++len[(size_t)(r / lay->nb) * lay->nb + lay->col_idx[a]];
+    for (int32_t c : len)
+        if (c > kChunkTiles) {
+            int32_t nch, pc;
+            split_row(c, &nch, &pc);
+            n_kslots += nch;
+        }
+    const int32_t n_qslots = lay->bwd.n_qslots + lay->H * n_rt * rch;
+    size_t a, b, c;
+    routed_bwd_workspace_parts(lay, batch, head_dim, n_qslots, n_kslots, &a, &b, &c, bytes);
+    return ok();
+}
+
+bsattn_status bsattn_backward_routed(const bsattn_layout* lay, bsattn_dtype dtype, int32_t B, int32_t H, int32_t L,
+                                     int32_t D, const void* q, const void* k, const void* v, const void* out,
+                                     const float* lse, const void* dout, const int32_t* routed_rows,
+                                     int32_t num_routed, void* dq, void* dk, void* dv, float scale, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+    if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
+    if (lay->kind != 1) return fail(BSATTN_ERR_INVALID_ARG, "bsattn_backward_routed needs a band layout");
+    if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "the backward is bf16 only");
+    if (!routed_rows) return fail(BSATTN_ERR_INVALID_ARG, "routed_rows is NULL");
+    if (num_routed < 1 || num_routed > L)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_routed must be in [1, seq_len] (got %d)", num_routed);
+    if (!dout || !dq || !dk || !dv) return fail(BSATTN_ERR_INVALID_ARG, "NULL gradient pointer");
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return fail(BSATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const void* ins[7] = {q, k, v, out, lse, dout, routed_rows};
+    const void* outs[3] = {dq, dk, dv};
+    for (const void* o : outs)
+        for (const void* in : ins)
+            if (o == in) return fail(BSATTN_ERR_INVALID_ARG, "a gradient output aliases an input");
+    if (dq == dk || dq == dv || dk == dv) return fail(BSATTN_ERR_INVALID_ARG, "gradient outputs alias");
+    bsattn_status st = check_forward_common(lay, B, H, L, D, q, k, v, const_cast<void*>(out),
+                                            const_cast<float*>(lse), scale);
+    if (st != BSATTN_OK) return st;
+    size_t need = 0;
+    st = bsattn_backward_routed_workspace_size(lay, B, D, num_routed, &need);
+    if (st != BSATTN_OK) return st;
+    if (!workspace || workspace_bytes < need)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const int32_t n_rt = (num_routed + kBlock - 1) / kBlock;
+    const auto& bw = lay->bwd;
+    // device lists copied out under the lock (later builds may move the cache)
+    BwdItem *rq_items, *k_items;
+    BwdSum *rq_sums, *k_sums;
+    int32_t* k_idx;
+    int32_t n_rq_items, n_rq_sums, rq_per_head, n_k_items, n_k_sums, k_per_head, n_qslots, n_kslots;
+    {
+        std::lock_guard<std::mutex> guard(*lay->sched_mu);
+        st = upload_bwd(lay, stream);
+        if (st != BSATTN_OK) return st;
+        const bsattn_layout::RoutedBwd* rb = nullptr;
+        st = get_routed_bwd(lay, n_rt, stream, &rb);
+        if (st != BSATTN_OK) return st;
+        rq_items = rb->d_rq_items; k_items = rb->d_k_items; rq_sums = rb->d_rq_sums; k_sums = rb->d_k_sums;
+        k_idx = rb->d_k_idx;
+        n_rq_items = (int32_t)rb->rq_items.size(); n_rq_sums = (int32_t)rb->rq_sums.size();
+        rq_per_head = rb->rq_per_head;
+        n_k_items = (int32_t)rb->k_items.size(); n_k_sums = (int32_t)rb->k_sums.size(); k_per_head = rb->k_per_head;
+        n_qslots = rb->n_qslots; n_kslots = rb->n_kslots;
+    }
+    if (((int64_t)B * H + kXcds) * std::max(std::max(bw.q_per_head, rq_per_head), k_per_head) >= ((int64_t)1 << 31))
+        return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+    size_t off_dq, off_dk, off_dv, total;
+    routed_bwd_workspace_parts(lay, B, D, n_qslots, n_kslots, &off_dq, &off_dk, &off_dv, &total);
+
+    BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    char* ws = (char*)workspace;
+    a.delta = (float*)ws;
+    a.ws_dq = (float*)(ws + off_dq);
+    a.ws_dk = (float*)(ws + off_dk);
+    a.ws_dv = (float*)(ws + off_dv);
+    a.valid_len = nullptr;
+    a.B = B; a.H = H; a.L = L; a.nb = lay->nb;
+    a.band = lay->band_tokens;
+    a.routed_rows = routed_rows;
+    a.n_routed = num_routed;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    hipError_t e;
+    // 1. dQ of every row over its band (routed rows are redone below), and delta
+    a.items = bw.d_q_items; a.n_items = (int32_t)bw.q_items.size(); a.items_per_head = bw.q_per_head;
+    a.sums = bw.d_q_sums; a.n_sums = (int32_t)bw.q_sums.size();
+    a.idx = lay->d_col_idx; a.idx_sub = nullptr; a.n_slots = n_qslots;
+    if ((e = launch_bwd_dq(a, D, MASK_BAND, stream)) != hipSuccess) return hip_fail(e, "backward dQ launch");
+    if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 0, stream)) != hipSuccess)
+        return hip_fail(e, "backward dQ sum launch");
+    // 2. dQ of the routed rows over every key block, as partials, summed into their rows
+    a.items = rq_items; a.n_items = n_rq_items; a.items_per_head = rq_per_head;
+    a.sums = rq_sums; a.n_sums = n_rq_sums;
+    a.idx = nullptr;
+    if ((e = launch_bwd_dq(a, D, MASK_ROUTED_Q, stream)) != hipSuccess) return hip_fail(e, "routed dQ launch");
+    if ((e = launch_bwd_routed_sum(a, D, stream)) != hipSuccess) return hip_fail(e, "routed dQ sum launch");
+    // 3. dK and dV over the band's query blocks and the routed tiles
+    a.items = k_items; a.n_items = n_k_items; a.items_per_head = k_per_head;
+    a.sums = k_sums; a.n_sums = n_k_sums;
+    a.idx = k_idx; a.n_slots = n_kslots;
+    if ((e = launch_bwd_dkdv(a, D, MASK_BAND_ROUTED, stream, g_ev_before, g_ev_after)) != hipSuccess)
+        return hip_fail(e, "routed dK/dV launch");
+    if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 1, stream)) != hipSuccess)
+        return hip_fail(e, "routed dK/dV sum launch");
     return ok();
 }
 

@@ -23,7 +23,14 @@ constexpr int kMaxChunks = 32;    // upper bound on the split of one row
 // and gathered tiles of the global tokens' keys (key blocks nb, nb + 1, ...).
 // MASK_BITS: per-query kept keys given as one 64-bit word per (query, key
 // block) (per-query top-keep layouts).
-enum MaskMode : int { MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2, MASK_SUB = 3, MASK_TOKEN = 4, MASK_BITS = 5 };
+// Backward only: MASK_ROUTED_Q -- dQ of gathered routed query tiles over every
+// key block; MASK_BAND_ROUTED -- dK/dV of band columns whose lists also hold
+// the routed tiles (entries nb + r), whose pairs inside the band are skipped
+// (the band entries hold them).
+enum MaskMode : int {
+    MASK_NONE = 0, MASK_PAD = 1, MASK_BAND = 2, MASK_SUB = 3, MASK_TOKEN = 4, MASK_BITS = 5,
+    MASK_ROUTED_Q = 6, MASK_BAND_ROUTED = 7
+};
 constexpr int kMaxTokGlobal = 2048;   // global tokens of a token layout (their list lives in LDS)
 constexpr int kMaxLinks = 64;         // random tokens per row of a token layout
 constexpr int kMaxAdaptiveBlocks = 1024;   // key blocks per side of a content-adaptive layout
@@ -171,6 +178,9 @@ struct BwdArgs {
     const int32_t* valid_len; // [B] or null
     int32_t B, H, L, nb, n_slots;
     int32_t band;             // band layouts: |t - s| <= band (MASK_BAND)
+    // routed variant: routed_rows [B*H][n_routed]; routed tile r holds rows r*64 .. r*64 + 63
+    const int32_t* routed_rows;
+    int32_t n_routed;
     float scale;              // score scale
     float scale_log2;         // scale * log2(e)
 };
@@ -193,9 +203,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
 // workgroups of the bf16 kernel resident per CU; two_wave: the two-wave
 // kernel also at D = 64 (per-query top-keep layouts)
 int fwd_bf16_ctas_per_cu(int head_dim, bool two_wave = false);
-// per-query top-keep selection: bits [G][L][L/64] (see FwdArgs::keep_bits)
+// per-query top-keep selection: bits [G][L][L/64] (see FwdArgs::keep_bits);
+// given events, its dispatch records its start and stop
 hipError_t launch_topr_select(const void* q, const void* k, uint64_t* bits, int G, int L, int D, int keep,
-                              hipStream_t s);
+                              hipStream_t s, hipEvent_t before = nullptr, hipEvent_t after = nullptr);
 // content-adaptive layouts (kernels/adaptive.hip): block sums of q and k, then the
 // kept key blocks cols [G][nb][keep]; and the schedule's tile entries filled from cols
 hipError_t launch_adaptive_select(const void* q, const void* k, double* qs, double* ks, int32_t* cols, int G,
@@ -216,6 +227,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t
                            hipEvent_t after = nullptr);
 // sum split partials into the bf16 output(s): which = 0 dQ, 1 dK and dV
 hipError_t launch_bwd_sum(const BwdArgs& a, int head_dim, int which, hipStream_t s);
+// sum the routed tiles' dQ partials into the dQ rows of their routed tokens
+hipError_t launch_bwd_routed_sum(const BwdArgs& a, int head_dim, hipStream_t s);
 // attention layer (kernels/layer.hip)
 hipError_t launch_split_heads(const float* qkv32, const void* b_qkv, void* q, void* k, void* v, int B, int L,
                               int H, int D, hipStream_t s);
@@ -295,6 +308,22 @@ struct bsattn_layout {
         bool built = false, uploaded = false;
     };
     mutable Bwd bwd;
+    // backward work lists of routed calls on a band layout, one per routed
+    // tile count, built and uploaded on first use
+    struct RoutedBwd {
+        int32_t n_rt = 0, r_chunks = 1, per = 1;
+        int32_t n_qslots = 0;                         // band dQ slots, then the routed tiles' chunks
+        int32_t rq_per_head = 0, k_per_head = 0, n_kslots = 0;
+        std::vector<bsattn::BwdItem> rq_items, k_items;
+        std::vector<bsattn::BwdSum> rq_sums, k_sums;
+        std::vector<int32_t> k_idx;                   // per column: band query blocks, then nb + r
+        bsattn::BwdItem* d_rq_items = nullptr;
+        bsattn::BwdItem* d_k_items = nullptr;
+        bsattn::BwdSum* d_rq_sums = nullptr;
+        bsattn::BwdSum* d_k_sums = nullptr;
+        int32_t* d_k_idx = nullptr;
+    };
+    mutable std::vector<RoutedBwd> rbwd;
 };
 
 namespace bsattn {

@@ -189,19 +189,27 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
     if (!take_item(a, b, h, blk, item)) return;
     const size_t grp = (size_t)b * a.H + h;
     const size_t gbase = grp * a.L * D;
-    const int t = blk * 64 + wave * 32 + ql;
+    // this lane's query: row 32 wave + ql of query block blk, or (MASK_ROUTED_Q)
+    // of routed tile blk, whose rows are gathered from routed_rows (-1: none)
+    int t = blk * 64 + wave * 32 + ql;
+    if (MASK == MASK_ROUTED_Q) {
+        const int kk = t;
+        t = kk < a.n_routed ? a.routed_rows[grp * a.n_routed + kk] : -1;
+        if (t >= a.L) t = -1;
+    }
 
     bf16x8_t qf[NC], dof[NC];
     u32x4_t ug[NC], uo[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const size_t off = gbase + (size_t)t * D + 16 * c + 8 * hh;
-        qf[c] = as_bf16x8(*(const u32x4_t*)((const uint16_t*)a.q + off));
-        ug[c] = *(const u32x4_t*)((const uint16_t*)a.dout + off);
-        uo[c] = *(const u32x4_t*)((const uint16_t*)a.out + off);
+        const size_t off = gbase + (size_t)max(t, 0) * D + 16 * c + 8 * hh;
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        qf[c] = as_bf16x8(t >= 0 ? *(const u32x4_t*)((const uint16_t*)a.q + off) : zero);
+        ug[c] = t >= 0 ? *(const u32x4_t*)((const uint16_t*)a.dout + off) : zero;
+        uo[c] = t >= 0 ? *(const u32x4_t*)((const uint16_t*)a.out + off) : zero;
         dof[c] = as_bf16x8(ug[c]);
     }
-    const float lse = a.lse[grp * a.L + t];
+    const float lse = t >= 0 ? a.lse[grp * a.L + t] : -INFINITY;
     const float nl2 = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
     const int valid = MASK == MASK_PAD ? min(max(a.valid_len[b], 0), a.L) : a.L;
     const float c2 = a.scale_log2;
@@ -212,9 +220,11 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) dqa[db][i] = 0.f;
 
+    // key block of list entry e: the layout's row list, or (routed tiles) every block in order
+    auto key_block = [&](int e) -> int { return MASK == MASK_ROUTED_Q ? e : a.idx[e]; };
     TileRegs<D> kr, vr;
     if (item.begin < item.end) {
-        const int j0 = a.idx[item.begin];
+        const int j0 = key_block(item.begin);
         fetch_tile<D>(kr, (const uint16_t*)a.k + gbase + (size_t)j0 * TILE, tid);
         fetch_tile<D>(vr, (const uint16_t*)a.v + gbase + (size_t)j0 * TILE, tid);
     }
@@ -231,9 +241,9 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
             dl = fmaf(bf16_to_f32(uo[c][e] >> 16), bf16_to_f32(ug[c][e] >> 16), dl);
         }
     dl += __shfl_xor(dl, 32);
-    if (hh == 0) a.delta[grp * a.L + t] = dl;
+    if (hh == 0 && t >= 0) a.delta[grp * a.L + t] = dl;
     for (int e = item.begin; e < item.end; ++e) {
-        const int j = a.idx[e];
+        const int j = key_block(e);
         // 32-token blocks: key halves this wave's query half may see
         const int sub = MASK == MASK_SUB ? (int)a.idx_sub[e] >> (2 * wave) : 3;
         // band layouts: a tile whose farthest (query, key) pair is inside the band needs no mask
@@ -243,7 +253,7 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
         commit_tile<D>(vt, vr, tid);
         __syncthreads();
         if (e + 1 < item.end) {   // the next tile's loads run behind this tile's products
-            const int jn = a.idx[e + 1];
+            const int jn = key_block(e + 1);
             fetch_tile<D>(kr, (const uint16_t*)a.k + gbase + (size_t)jn * TILE, tid);
             fetch_tile<D>(vr, (const uint16_t*)a.v + gbase + (size_t)jn * TILE, tid);
         }
@@ -281,7 +291,7 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
         }
     }
     if (item.slot < 0) {
-        store_row<D>(dqa, a.scale, (uint16_t*)a.dq + gbase + (size_t)t * D, nullptr, hh);
+        if (t >= 0) store_row<D>(dqa, a.scale, (uint16_t*)a.dq + gbase + (size_t)t * D, nullptr, hh);
     } else {
         float* row = a.ws_dq + (((size_t)b * a.n_slots + item.slot) * 64 + wave * 32 + ql) * D;
         store_row<D>(dqa, a.scale, nullptr, row, hh);
@@ -297,6 +307,7 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) uint16_t ot[TILE];   // dO tile
     __shared__ __attribute__((aligned(16))) float nlse[64];       // -LSE / scale (-inf: row sees no key)
     __shared__ __attribute__((aligned(16))) float ndel[64];       // -delta
+    __shared__ __attribute__((aligned(16))) int qtok[64];         // query token of each row (-1: none)
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int kl = lane & 31, hh = lane >> 5, gi = lane & 15, gsel = (lane >> 4) & 1;
@@ -324,13 +335,37 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
 
     TileRegs<D> qr, orr;
     float lse_r = 0.f, del_r = 0.f;
+    int tok_r = 0;
+    // token of row `row` of query entry ib: query block ib, or (ib >= nb, MASK_BAND_ROUTED)
+    // row `row` of routed tile ib - nb (-1 past the routed rows)
+    auto row_token = [&](int ib, int row) -> int {
+        if (MASK != MASK_BAND_ROUTED || ib < a.nb) return ib * 64 + row;
+        const int kk = (ib - a.nb) * 64 + row;
+        const int t = kk < a.n_routed ? a.routed_rows[grp * a.n_routed + kk] : -1;
+        return t < a.L ? t : -1;
+    };
     auto fetch = [&](int ib) {
-        fetch_tile<D>(qr, (const uint16_t*)a.q + gbase + (size_t)ib * TILE, tid);
-        fetch_tile<D>(orr, (const uint16_t*)a.dout + gbase + (size_t)ib * TILE, tid);
+        if (MASK == MASK_BAND_ROUTED && ib >= a.nb) {
+            // a routed tile: its rows gathered, missing rows zero
+            constexpr int P = D / 8;
+#pragma unroll
+            for (int r = 0; r < TileRegs<D>::R; ++r) {
+                const int p = tid + r * kBT;
+                const int t = row_token(ib, p / P);
+                const size_t off = gbase + (size_t)max(t, 0) * D + (p % P) * 8;
+                const u32x4_t zero = {0u, 0u, 0u, 0u};
+                qr.v[r] = t >= 0 ? *(const u32x4_t*)((const uint16_t*)a.q + off) : zero;
+                orr.v[r] = t >= 0 ? *(const u32x4_t*)((const uint16_t*)a.dout + off) : zero;
+            }
+        } else {
+            fetch_tile<D>(qr, (const uint16_t*)a.q + gbase + (size_t)ib * TILE, tid);
+            fetch_tile<D>(orr, (const uint16_t*)a.dout + gbase + (size_t)ib * TILE, tid);
+        }
         if (tid < 64) {
-            const size_t r = grp * a.L + (size_t)ib * 64 + tid;
-            lse_r = a.lse[r];
-            del_r = a.delta[r];
+            tok_r = row_token(ib, tid);
+            const size_t r = grp * a.L + (size_t)max(tok_r, 0);
+            lse_r = tok_r >= 0 ? a.lse[r] : -INFINITY;
+            del_r = tok_r >= 0 ? a.delta[r] : 0.f;
         }
     };
     if (item.begin < item.end) fetch(a.idx[item.begin]);
@@ -339,13 +374,16 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
         const int sub = MASK == MASK_SUB ? (int)a.idx_sub[e] >> wave : 15;
         // band layouts: query block ib, masked per pair unless the whole tile is inside the band
         const int ib = a.idx[e];
-        const bool band_cut = MASK == MASK_BAND && 64 * abs(blk - ib) + 63 > a.band;
+        const bool routed_entry = MASK == MASK_BAND_ROUTED && ib >= a.nb;
+        const bool band_cut = (MASK == MASK_BAND || MASK == MASK_BAND_ROUTED) && !routed_entry &&
+                              64 * abs(blk - ib) + 63 > a.band;
         __syncthreads();
         commit_tile<D>(qt, qr, tid);
         commit_tile<D>(ot, orr, tid);
         if (tid < 64) {
             nlse[tid] = lse_r == -INFINITY ? -INFINITY : -lse_r / a.scale;
             ndel[tid] = -del_r;
+            qtok[tid] = tok_r;
         }
         __syncthreads();
         if (e + 1 < item.end) fetch(a.idx[e + 1]);   // behind this tile's products
@@ -369,17 +407,29 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
         }
         // P = exp2(S * scale * log2e), dS = P * (dP - delta)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb) {
+            // routed tiles: a pair counts here only outside the band (the band entries hold the rest)
+            int tk[16];
+            if (MASK == MASK_BAND_ROUTED && routed_entry) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int4 t4 = *(const int4*)(qtok + 32 * qb + 8 * g4 + 4 * hh);
+                    tk[4 * g4 + 0] = t4.x; tk[4 * g4 + 1] = t4.y; tk[4 * g4 + 2] = t4.z; tk[4 * g4 + 3] = t4.w;
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float p = __builtin_amdgcn_exp2f(s[qb][i] * c2);
                 if (!key_ok) p = 0.f;
                 if (MASK == MASK_SUB && !((sub >> (2 * qb)) & 1)) p = 0.f;
-                if (MASK == MASK_BAND && band_cut && abs(ib * 64 + 32 * qb + 8 * (i / 4) + 4 * hh + (i % 4) - key) > a.band)
+                if ((MASK == MASK_BAND || MASK == MASK_BAND_ROUTED) && band_cut &&
+                    abs(ib * 64 + 32 * qb + 8 * (i / 4) + 4 * hh + (i % 4) - key) > a.band)
                     p = 0.f;
+                if (MASK == MASK_BAND_ROUTED && routed_entry && (tk[i] < 0 || abs(tk[i] - key) <= a.band)) p = 0.f;
                 s[qb][i] = p;
                 dp[qb][i] *= p;
             }
+        }
         // dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -442,6 +492,34 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(const BwdArgs a, int which
     }
 }
 
+// Sum of a routed tile's dQ partials into the dQ rows of its routed tokens.
+// One workgroup per (tile, batch entry, 1024-element slice of the 64 x D block).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_routed_sum_kernel(const BwdArgs a) {
+    constexpr int SLICES = 64 * D / 1024;
+    const int slice = blockIdx.x % SLICES;
+    const int rest = blockIdx.x / SLICES;
+    const int si = rest / a.B, b = rest % a.B;
+    const BwdSum sm = a.sums[si];
+    const int h = sm.head_blk / a.nb, r = sm.head_blk % a.nb;
+    const size_t grp = (size_t)b * a.H + h;
+    const int x = slice * 1024 + threadIdx.x * 4;
+    const int kk = r * 64 + x / D;
+    if (kk >= a.n_routed) return;
+    const int t = a.routed_rows[grp * a.n_routed + kk];
+    if (t < 0 || t >= a.L) return;
+    const float* src = a.ws_dq + ((size_t)b * a.n_slots + sm.first_slot) * 64 * D + x;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int ch = 0; ch < sm.n_chunks; ++ch) {
+        const float4 v = *(const float4*)(src + (size_t)ch * 64 * D);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    u32x2_t w;
+    w.x = pack_bf16x2(acc.x, acc.y);
+    w.y = pack_bf16x2(acc.z, acc.w);
+    *(u32x2_t*)((uint16_t*)a.dq + (grp * a.L + t) * D + x % D) = w;
+}
+
 template <int D, int MASK>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
     const int64_t groups = (int64_t)a.B * a.H;
@@ -464,6 +542,8 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s, hipEvent_t before, hip
 }  // namespace
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s) {
+    if (mask == MASK_ROUTED_Q)
+        return head_dim == 64 ? launch_dq_t<64, MASK_ROUTED_Q>(a, s) : launch_dq_t<128, MASK_ROUTED_Q>(a, s);
     if (head_dim == 64)
         return mask == MASK_PAD   ? launch_dq_t<64, MASK_PAD>(a, s)
              : mask == MASK_SUB   ? launch_dq_t<64, MASK_SUB>(a, s)
@@ -477,6 +557,9 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
                            hipEvent_t after) {
+    if (mask == MASK_BAND_ROUTED)
+        return head_dim == 64 ? launch_dkdv_t<64, MASK_BAND_ROUTED>(a, s, before, after)
+                              : launch_dkdv_t<128, MASK_BAND_ROUTED>(a, s, before, after);
     if (head_dim == 64)
         return mask == MASK_PAD   ? launch_dkdv_t<64, MASK_PAD>(a, s, before, after)
              : mask == MASK_SUB   ? launch_dkdv_t<64, MASK_SUB>(a, s, before, after)
@@ -486,6 +569,14 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t
          : mask == MASK_SUB   ? launch_dkdv_t<128, MASK_SUB>(a, s, before, after)
          : mask == MASK_BAND  ? launch_dkdv_t<128, MASK_BAND>(a, s, before, after)
                               : launch_dkdv_t<128, MASK_NONE>(a, s, before, after);
+}
+
+hipError_t launch_bwd_routed_sum(const BwdArgs& a, int head_dim, hipStream_t s) {
+    const int64_t grid = (int64_t)a.n_sums * a.B * (64 * head_dim / 1024);
+    if (grid == 0) return hipSuccess;
+    if (head_dim == 64) hipLaunchKernelGGL((bwd_routed_sum_kernel<64>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bwd_routed_sum_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_sum(const BwdArgs& a, int head_dim, int which, hipStream_t s) {

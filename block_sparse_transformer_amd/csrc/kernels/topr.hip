@@ -19,6 +19,7 @@
 // how many keys equal to T are kept; those are the lowest-index ones, counted
 // in index order with ballots.  The result is one 64-bit word per (query, key
 // tile): bit b set iff key 64j + b is kept.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -194,23 +195,31 @@ __global__ __launch_bounds__(kSelThreads) void topr_select_kernel(const uint16_t
     }
 }
 
+// Launched with hipExtLaunchKernelGGL: given events, the dispatch itself
+// records the kernel's start and stop.
 template <int TPQ, int D>
-hipError_t launch_t(const void* q, const void* k, uint64_t* bits, int G, int L, int keep, hipStream_t s) {
+hipError_t launch_t(const void* q, const void* k, uint64_t* bits, int G, int L, int keep, hipStream_t s,
+                    hipEvent_t before, hipEvent_t after) {
     constexpr int QW = kSelThreads / TPQ;
     const int qtiles = L / QW;
-    hipLaunchKernelGGL((topr_select_kernel<TPQ, D>), dim3((unsigned)((int64_t)G * qtiles)), dim3(kSelThreads), 0, s,
-                       (const uint16_t*)q, (const uint16_t*)k, bits, L, keep, qtiles);
+    hipExtLaunchKernelGGL((topr_select_kernel<TPQ, D>), dim3((unsigned)((int64_t)G * qtiles)), dim3(kSelThreads), 0,
+                          s, before, after, 0, (const uint16_t*)q, (const uint16_t*)k, bits, L, keep, qtiles);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_topr_select(const void* q, const void* k, uint64_t* bits, int G, int L, int D, int keep,
-                              hipStream_t s) {
+                              hipStream_t s, hipEvent_t before, hipEvent_t after) {
     if (L % 64 != 0 || L > kMaxTopLen || keep < 1 || keep > L || (D != 64 && D != 128)) return hipErrorInvalidValue;
-    if (L <= 2048) return D == 64 ? launch_t<16, 64>(q, k, bits, G, L, keep, s) : launch_t<16, 128>(q, k, bits, G, L, keep, s);
-    if (L <= 4096) return D == 64 ? launch_t<32, 64>(q, k, bits, G, L, keep, s) : launch_t<32, 128>(q, k, bits, G, L, keep, s);
-    return D == 64 ? launch_t<64, 64>(q, k, bits, G, L, keep, s) : launch_t<64, 128>(q, k, bits, G, L, keep, s);
+    if (L <= 2048)
+        return D == 64 ? launch_t<16, 64>(q, k, bits, G, L, keep, s, before, after)
+                       : launch_t<16, 128>(q, k, bits, G, L, keep, s, before, after);
+    if (L <= 4096)
+        return D == 64 ? launch_t<32, 64>(q, k, bits, G, L, keep, s, before, after)
+                       : launch_t<32, 128>(q, k, bits, G, L, keep, s, before, after);
+    return D == 64 ? launch_t<64, 64>(q, k, bits, G, L, keep, s, before, after)
+                   : launch_t<64, 128>(q, k, bits, G, L, keep, s, before, after);
 }
 
 }  // namespace bsattn

@@ -421,6 +421,29 @@ bsattn_status bsattn_backward(const bsattn_layout* layout, bsattn_dtype dtype,
                               float scale, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* Backward of the routed-query forward (bsattn_forward_routed; SQA page,
+ * sections 2.1 and 2.2: the routed model is trained end to end): dQ, dK and dV
+ * of that forward for an upstream dout, with the mask "row t sees every key
+ * if t is routed, else the keys with |t - s| <= band_tokens".
+ *   band_layout   the band layout the forward used (uploaded).
+ *   routed_rows   device int32 [B, H, num_routed], distinct rows in [0, L), as
+ *                 given to the forward; out and lse are the forward's outputs.
+ *   workspace     device buffer of at least
+ *                 bsattn_backward_routed_workspace_size() bytes, 256-byte
+ *                 aligned; needs no initialisation, holds nothing between calls.
+ * dtype must be BSATTN_BF16.  Other arguments, layouts and errors as
+ * bsattn_backward.  The first call for a routed tile count (ceil(num_routed /
+ * 64)) builds and uploads its work lists with hipMalloc and a stream
+ * synchronisation, unless bsattn_prepare(backward = 1, num_routed) did. */
+bsattn_status bsattn_backward_routed_workspace_size(const bsattn_layout* band_layout, int32_t batch,
+                                                    int32_t head_dim, int32_t num_routed, size_t* bytes);
+bsattn_status bsattn_backward_routed(const bsattn_layout* band_layout, bsattn_dtype dtype, int32_t batch,
+                                     int32_t num_heads, int32_t seq_len, int32_t head_dim, const void* q,
+                                     const void* k, const void* v, const void* out, const float* lse,
+                                     const void* dout, const int32_t* routed_rows, int32_t num_routed,
+                                     void* dq, void* dk, void* dv, float scale, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
 /* Device workspace bytes needed by bsattn_layer_forward: the fp32 qkv
  * projection, the per-head Q, K, V, O (bf16), LSE and the attention's own
  * workspace.  Written to *bytes. */
@@ -452,7 +475,8 @@ bsattn_status bsattn_layer_forward(const bsattn_layout* layout, int32_t batch, i
 
 /* Measurement hook: while set (non-NULL), every forward call made from this
  * thread records `before` on its stream immediately before the main attention
- * kernel and `after` immediately after it, and every backward call does the
+ * kernel and `after` immediately after it (over a top-keep layout: around the
+ * key selection, its dominant kernel), and every backward call does the
  * same around its dK/dV kernel, so a caller can time that kernel alone with
  * hipEventElapsedTime.  Pass NULLs to clear.  Events are caller owned. */
 bsattn_status bsattn_set_profile_events(hipEvent_t before, hipEvent_t after);

@@ -96,3 +96,35 @@ def attention_backward(q, k, v, do, layout: Layout, scale: float,
                 dk[b, h] += gk
                 dv[b, h] += gv
     return dq, dk, dv
+
+
+def routed_attention_backward(q, k, v, do, routed_rows: np.ndarray, band_tokens: int, scale: float,
+                              heads: Optional[Iterable[int]] = None,
+                              batches: Optional[Iterable[int]] = None,
+                              chunk: int = 1024) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of the routed-query attention (SQA page, section 2.1; the
+    forward is ``attention.routed_attention_forward``) by dense masking: row t
+    sees every key if it is one of routed_rows[b, h], else the keys with
+    |t - s| <= band_tokens.  Chunked over rows like ``attention_backward``.
+    Returns (dQ, dK, dV) [B, H, L, D] in fp64 for the selected batches and
+    heads (others NaN)."""
+    from .attention import routed_token_mask_rows
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    routed_rows = np.asarray(routed_rows)
+    B, H, L, D = q.shape
+    dq = np.full((B, H, L, D), np.nan)
+    dk = np.full((B, H, L, D), np.nan)
+    dv = np.full((B, H, L, D), np.nan)
+    for b in (range(B) if batches is None else batches):
+        for h in (range(H) if heads is None else heads):
+            dk[b, h] = 0.0
+            dv[b, h] = 0.0
+            for t0 in range(0, L, chunk):
+                t = np.arange(t0, min(L, t0 + chunk))
+                mask = routed_token_mask_rows(t, L, routed_rows[b, h], band_tokens)
+                gq, gk, gv = masked_attention_grad(q[b, h, t], k[b, h], v[b, h], mask, scale, do[b, h, t])
+                dq[b, h, t] = gq
+                dk[b, h] += gk
+                dv[b, h] += gv
+    return dq, dk, dv
+

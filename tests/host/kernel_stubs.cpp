@@ -10,7 +10,8 @@ hipError_t launch_fwd_bf16(const FwdArgs&, int, int, hipStream_t, hipEvent_t, hi
     return hipErrorNotSupported;
 }
 int fwd_bf16_ctas_per_cu(int head_dim, bool two_wave) { return head_dim == 64 ? (two_wave ? 4 : 1) : 2; }
-hipError_t launch_topr_select(const void*, const void*, uint64_t*, int, int, int, int, hipStream_t) {
+hipError_t launch_topr_select(const void*, const void*, uint64_t*, int, int, int, int, hipStream_t, hipEvent_t,
+                              hipEvent_t) {
     return hipErrorNotSupported;
 }
 hipError_t launch_adaptive_select(const void*, const void*, double*, double*, int32_t*, int, int, int, int,
@@ -35,6 +36,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs&, int, int, hipStream_t, hipEvent_t, hi
     return hipErrorNotSupported;
 }
 hipError_t launch_bwd_sum(const BwdArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_bwd_routed_sum(const BwdArgs&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_split_heads(const float*, const void*, void*, void*, void*, int, int, int, int, hipStream_t) {
     return hipErrorNotSupported;
 }

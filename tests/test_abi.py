@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
         "bsattn_layout_token_links", "bsattn_make_adaptive_layout", "bsattn_adaptive_select", "bsattn_make_topr_layout", "bsattn_topr_select", "bsattn_layout_destroy", "bsattn_workspace_size",
         "bsattn_forward", "bsattn_backward_workspace_size", "bsattn_backward",
         "bsattn_layer_workspace_size", "bsattn_layer_forward",
-        "bsattn_route_topk", "bsattn_route_workspace_size", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
+        "bsattn_route_topk", "bsattn_route_workspace_size", "bsattn_backward_routed", "bsattn_backward_routed_workspace_size", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
         "bsattn_last_error", "bsattn_prepare", "bsattn_forward_noalloc"])
     lib = bs.lib()
     for n in names:

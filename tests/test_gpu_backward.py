@@ -221,3 +221,57 @@ def test_backward_band_rejects_padding():
     vl = torch.tensor([300], dtype=torch.int32, device="cuda")
     with pytest.raises(bs.BsattnError, match="padding"):
         bs.backward(dev["q"], dev["k"], dev["v"], o, lse, torch.ones_like(o), lay, key_valid_len=vl, scale=wl.scale)
+
+
+# ---------------- routed-query variant ----------------
+
+def _routed_bwd_case(wl, tag, heads=None):
+    """bsattn_backward_routed against the oracle's routed gradients: the routed rows
+    come from the device router (bit-exact with the oracle's), the forward's O and
+    LSE from bsattn_forward_routed."""
+    from oracle import router as OR
+    _say(tag, wl)
+    inp = make_inputs(wl)
+    do = make_grad_output(wl)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    k = wl.routed_k
+    rr = torch.empty((wl.batch, wl.heads, k), dtype=torch.int32, device="cuda")
+    bs.bsattn_route_topk(dev["q"], dev["w"], k, rr)
+    band = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)
+    bs.bsattn_layout_upload(band)
+    o, lse = bs.forward_routed(dev["q"], dev["k"], dev["v"], band, rr, scale=wl.scale)
+    dq, dk, dv = bs.backward_routed(dev["q"], dev["k"], dev["v"], o, lse, do.cuda(), band, rr, scale=wl.scale)
+    torch.cuda.synchronize()
+    want_rows = OR.topk_rows(OR.router_scores(inp["q"], inp["w"]), k)
+    assert np.array_equal(rr.cpu().numpy(), want_rows), f"{tag}: routed rows differ"
+    got = (_f64(dq), _f64(dk), _f64(dv))
+    ref = OG.routed_attention_backward(inp["q"], inp["k"], inp["v"], do, want_rows, wl.band_tokens, wl.scale,
+                                       heads=heads)
+    if heads is not None:
+        got = tuple(x[:, list(heads)] for x in got)
+        ref = tuple(x[:, list(heads)] for x in ref)
+    return _compare(got, ref, tag)
+
+
+def test_backward_routed_small_d128():
+    wl = WORKLOADS["routed-L4096"].with_(heads=2, seq_len=512)
+    _routed_bwd_case(wl, "bwd routed L512 D128 k64 band32")
+
+
+def test_backward_routed_d64_ragged_k():
+    # 70 routed rows: two routed tiles, the second with 6 rows
+    wl = WORKLOADS["routed-L4096"].with_(batch=2, heads=2, seq_len=1024, head_dim=64, routed_k=70, band_tokens=100)
+    _routed_bwd_case(wl, "bwd routed L1024 D64 k70 band100")
+
+
+def test_backward_routed_wide_band_split_rows():
+    # band 512 at L = 2048: band rows of up to 17 blocks are split (dQ partials
+    # summed before the routed rows are rewritten) and so are the columns
+    wl = WORKLOADS["routed-L4096"].with_(heads=2, seq_len=2048, head_dim=64, band_tokens=512)
+    _routed_bwd_case(wl, "bwd routed L2048 D64 k64 band512")
+
+
+def test_backward_routed_full_size_heads():
+    """The routed workload's own shape (B1 H32 L4096 D128, band 32, top 64): whole heads."""
+    wl = WORKLOADS["routed-L4096"]
+    _routed_bwd_case(wl, "bwd routed-L4096 heads 0, 13, 31", heads=[0, 13, 31])

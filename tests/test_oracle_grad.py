@@ -151,3 +151,23 @@ def test_band_backward_matches_autograd_and_closed_form():
         if w == 0:
             assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
             assert np.array_equal(dv, do)
+
+
+def test_routed_backward_matches_torch_autograd():
+    """The routed gradients against torch autograd of the dense formula, with the
+    mask written out here by loops: row t sees key s iff t is routed or |t - s| <= band."""
+    B, H, L, D = 1, 2, 3 * 64, 8
+    band = 20
+    q, k, v, do = (_rand((B, H, L, D), s) for s in (31, 32, 33, 34))
+    routed = np.array([[[3, 64, 100, 191]], [[0, 5, 6, 150]]]).reshape(B, H, 4)
+    dq, dk, dv = OG.routed_attention_backward(q, k, v, do, routed, band, 0.3, chunk=70)
+    for h in range(H):
+        mask = np.zeros((L, L), dtype=bool)
+        for t in range(L):
+            for s_ in range(L):
+                mask[t, s_] = t in set(routed[0, h].tolist()) or abs(t - s_) <= band
+        rq, rk, rv = _torch_dense_grad(q[0, h], k[0, h], v[0, h], do[0, h], mask, 0.3)
+        assert np.abs(dq[0, h] - rq).max() < 1e-12
+        assert np.abs(dk[0, h] - rk).max() < 1e-12
+        assert np.abs(dv[0, h] - rv).max() < 1e-12
+
