@@ -57,7 +57,7 @@ def lib() -> ctypes.CDLL:
     L.bsattn_layout_tile_masks.argtypes = [_c_vp, ctypes.POINTER(ctypes.POINTER(ctypes.c_uint8)),
                                            ctypes.POINTER(ctypes.c_int64)]
     L.bsattn_layout_upload.argtypes = [_c_vp, _c_vp]
-    L.bsattn_layout_build_device.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp]
+    L.bsattn_layout_build_device.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp]
     L.bsattn_layout_destroy.argtypes = [_c_vp]
     L.bsattn_layout_destroy.restype = None
     L.bsattn_workspace_size.argtypes = [_c_vp, _c_int, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -273,9 +273,12 @@ def bsattn_prepare(layout: Layout, batch: int, head_dim: int, num_routed: int = 
                                                   _stream_handle(stream)))
 
 
-def bsattn_layout_build_device(layout: Layout, row_ptr_dev, col_idx_dev, stream=None) -> None:
+def bsattn_layout_build_device(layout: Layout, row_ptr_dev, col_idx_dev, tile_masks_dev=None,
+                               stream=None) -> None:
+    """The layout rebuilt on the device into caller tensors (tile_masks_dev: uint8 [nnz],
+    needed for layouts of 32-token blocks)."""
     _check("bsattn_layout_build_device", lib().bsattn_layout_build_device(
-        layout.handle, _ptr(row_ptr_dev), _ptr(col_idx_dev), _stream_handle(stream)))
+        layout.handle, _ptr(row_ptr_dev), _ptr(col_idx_dev), _ptr(tile_masks_dev), _stream_handle(stream)))
 
 
 def bsattn_layout_destroy(layout: Layout) -> None:

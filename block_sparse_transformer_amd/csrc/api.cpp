@@ -1445,15 +1445,24 @@ bsattn_status bsattn_layout_upload(bsattn_layout* lay, hipStream_t stream) {
 }
 
 bsattn_status bsattn_layout_build_device(const bsattn_layout* lay, int32_t* row_ptr_dev,
-                                         int32_t* col_idx_dev, hipStream_t stream) {
+                                         int32_t* col_idx_dev, uint8_t* tile_masks_dev, hipStream_t stream) {
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
     if (!row_ptr_dev || (!col_idx_dev && !lay->col_idx.empty()))
         return fail(BSATTN_ERR_INVALID_ARG, "NULL device array");
     if (lay->kind != 0 && lay->kind != 1)
         return fail(BSATTN_ERR_UNSUPPORTED, "the device rule builds window/global/random and band layouts only");
-    if (lay->block != kBlock) return fail(BSATTN_ERR_UNSUPPORTED, "the device rule runs 64-token blocks only");
-    hipError_t e = launch_layout_build(lay->rule, lay->kind, lay->H, lay->nb, lay->band_tokens,
-                                       row_ptr_dev, col_idx_dev, stream);
+    int kind = lay->kind;
+    if (lay->kind == 0 && lay->block == 32) {
+        if (!tile_masks_dev && !lay->col_idx.empty())
+            return fail(BSATTN_ERR_INVALID_ARG, "a layout of 32-token blocks needs tile_masks_dev");
+        kind = 2;
+    } else if (lay->kind == 0 && lay->block == 128) {
+        kind = 3;
+    } else if (lay->block != kBlock) {
+        return fail(BSATTN_ERR_UNSUPPORTED, "the device rule runs 32-, 64- and 128-token blocks");
+    }
+    hipError_t e = launch_layout_build(lay->rule, kind, lay->H, lay->nb, lay->band_tokens,
+                                       row_ptr_dev, col_idx_dev, tile_masks_dev, stream);
     if (e != hipSuccess) return hip_fail(e, "layout build launch");
     return ok();
 }

@@ -234,8 +234,10 @@ hipError_t launch_split_heads(const float* qkv32, const void* b_qkv, void* q, vo
                               int H, int D, hipStream_t s);
 hipError_t launch_merge_heads(const void* o, void* o2, int B, int L, int H, int D, hipStream_t s);
 hipError_t launch_bias_out(const float* out32, const void* b_proj, void* out, size_t rows, int C, hipStream_t s);
+// kind 0: rule (64-token blocks), 1: token band, 2: rule on 32-token blocks
+// (subs receives the quarter bits), 3: rule on 128-token blocks
 hipError_t launch_layout_build(const RowRule& rule, int kind, int32_t H, int32_t nb,
-                               int32_t band, int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+                               int32_t band, int32_t* row_ptr, int32_t* col_idx, uint8_t* subs, hipStream_t s);
 
 }  // namespace bsattn
 

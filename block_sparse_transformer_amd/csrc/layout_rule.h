@@ -155,6 +155,47 @@ BSR_HD inline int32_t rule_row_fill(const RowRule& R, int32_t h, int32_t i, int3
     return o;
 }
 
+// Tile row i (64 tokens) of a rule on 32-token blocks: the tiles j that hold a
+// block of rule row 2 i or 2 i + 1, ascending, each with its quarter bits (bit
+// 2 a + b: query half a, key half b).  cols / subs may be null (count only).
+// Returns the row length.
+BSR_HD inline int32_t sub_tile_row(const RowRule& R, int32_t h, int32_t i, int32_t* cols, uint8_t* subs) {
+    constexpr int32_t kCap = kMaxExcluded + kMaxRandom;   // bound on a non-global rule row
+    int32_t l0[kCap], l1[kCap];
+    const bool g0 = rule_is_global(R, 2 * i), g1 = rule_is_global(R, 2 * i + 1);
+    const int32_t n0 = g0 ? R.nb : rule_row_fill(R, h, 2 * i, l0);
+    const int32_t n1 = g1 ? R.nb : rule_row_fill(R, h, 2 * i + 1, l1);
+    int32_t a0 = 0, a1 = 0, n = 0;
+    while (a0 < n0 || a1 < n1) {
+        const int32_t b0 = a0 < n0 ? (g0 ? a0 : l0[a0]) : 0x7fffffff;
+        const int32_t b1 = a1 < n1 ? (g1 ? a1 : l1[a1]) : 0x7fffffff;
+        const int32_t j = (b0 < b1 ? b0 : b1) / 2;
+        int32_t sub = 0;
+        while (a0 < n0 && (g0 ? a0 : l0[a0]) / 2 == j) { sub |= 1 << ((g0 ? a0 : l0[a0]) % 2); ++a0; }
+        while (a1 < n1 && (g1 ? a1 : l1[a1]) / 2 == j) { sub |= 1 << (2 + (g1 ? a1 : l1[a1]) % 2); ++a1; }
+        if (cols) {
+            cols[n] = j;
+            subs[n] = (uint8_t)sub;
+        }
+        ++n;
+    }
+    return n;
+}
+
+// Tile row i of a rule on 128-token blocks: rule row i / 2 with every block c
+// spanning tiles 2 c and 2 c + 1 (expanded in place, from the back).  out may
+// be null (count only).  Returns the row length.
+BSR_HD inline int32_t wide_tile_row_fill(const RowRule& R, int32_t h, int32_t i, int32_t* out) {
+    if (!out) return 2 * rule_row_count(R, h, i / 2);
+    const int32_t n = rule_row_fill(R, h, i / 2, out);
+    for (int32_t c = n - 1; c >= 0; --c) {
+        const int32_t v = out[c];
+        out[2 * c + 1] = 2 * v + 1;
+        out[2 * c] = 2 * v;
+    }
+    return 2 * n;
+}
+
 // Token-granular pattern: the rule above on 1-token blocks (window [t-w, t+w]
 // clipped, global tokens G of any number, r random tokens per non-global row
 // from the same per-row stream with the token index in place of the block

@@ -243,12 +243,14 @@ bsattn_status bsattn_layout_upload(bsattn_layout* layout, hipStream_t stream);
 
 /* Rebuild the same layout on the device from its parameters (one thread per
  * row runs the identical integer rule) into caller-owned device arrays
- * row_ptr_dev [num_rows + 1] and col_idx_dev [nnz].  Exists to prove that
- * the host and device evaluations of the rule agree bit for bit.
- * Window/global/random and band layouts of 64-token blocks only
- * (UNSUPPORTED for 32- and 128-token blocks, token and adaptive layouts). */
+ * row_ptr_dev [num_rows + 1] and col_idx_dev [nnz] (the 64-token tile CSR, as
+ * bsattn_layout_csr), and for layouts of 32-token blocks tile_masks_dev [nnz]
+ * (the quarter masks, as bsattn_layout_tile_masks; may be NULL otherwise).
+ * Exists to prove that the host and device evaluations of the rule agree bit
+ * for bit.  Window/global/random layouts of 32-, 64- and 128-token blocks
+ * and band layouts; UNSUPPORTED for token, adaptive and top-keep layouts. */
 bsattn_status bsattn_layout_build_device(const bsattn_layout* layout, int32_t* row_ptr_dev,
-                                         int32_t* col_idx_dev, hipStream_t stream);
+                                         int32_t* col_idx_dev, uint8_t* tile_masks_dev, hipStream_t stream);
 
 /* Build and upload, ahead of time, the work schedule of one call shape of an
  * uploaded layout, so that every later bsattn_forward (and, with

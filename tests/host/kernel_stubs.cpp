@@ -44,7 +44,7 @@ hipError_t launch_merge_heads(const void*, void*, int, int, int, int, hipStream_
 hipError_t launch_bias_out(const float*, const void*, void*, size_t, int, hipStream_t) {
     return hipErrorNotSupported;
 }
-hipError_t launch_layout_build(const RowRule&, int, int32_t, int32_t, int32_t, int32_t*, int32_t*, hipStream_t) {
+hipError_t launch_layout_build(const RowRule&, int, int32_t, int32_t, int32_t, int32_t*, int32_t*, uint8_t*, hipStream_t) {
     return hipErrorNotSupported;
 }
 

@@ -177,6 +177,28 @@ int main(int argc, char** argv) {
             }
             continue;
         }
+        // the device rule's tile-row expansions (32- and 128-token blocks), run here on
+        // the host, must give the host builder's CSR and quarter masks
+        if (kind == 0 && (lay->block == 32 || lay->block == 128)) {
+            std::vector<int32_t> cols((size_t)lay->nb * 2 + 8);
+            std::vector<uint8_t> subs(cols.size());
+            for (int32_t r = 0; r < lay->H * lay->nb && !g_fail; ++r) {
+                const int32_t h = r / lay->nb, i = r % lay->nb;
+                const int32_t n = lay->block == 32 ? sub_tile_row(lay->rule, h, i, cols.data(), subs.data())
+                                                   : wide_tile_row_fill(lay->rule, h, i, cols.data());
+                const int32_t cnt = lay->block == 32 ? sub_tile_row(lay->rule, h, i, nullptr, nullptr)
+                                                     : wide_tile_row_fill(lay->rule, h, i, nullptr);
+                bool same = n == cnt && n == lay->row_ptr[r + 1] - lay->row_ptr[r];
+                for (int32_t a = 0; same && a < n; ++a) {
+                    same = cols[(size_t)a] == lay->col_idx[(size_t)lay->row_ptr[r] + a];
+                    if (lay->block == 32) same = same && subs[(size_t)a] == lay->tile_sub[(size_t)lay->row_ptr[r] + a];
+                }
+                if (!same) {
+                    std::fprintf(stderr, "FAIL %s: device-rule tile row %d differs from the host layout\n", tag, r);
+                    ++g_fail;
+                }
+            }
+        }
         // host-only queries must hold together with the layout
         const int32_t* rp = nullptr;
         const int32_t* ci = nullptr;

@@ -214,6 +214,11 @@ def test_device_build_rejects_token_and_adaptive_layouts():
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
     tok = bs.bsattn_make_token_layout(2, 1024, 16, 8, 2, 0)
     ada = bs.bsattn_make_adaptive_layout(2, 1024, 4)
-    for lay in (tok, ada):
-        assert L.bsattn_layout_build_device(lay.handle, fake, fake, None) == 2
+    top = bs.bsattn_make_topr_layout(2, 1024, 100)
+    for lay in (tok, ada, top):
+        assert L.bsattn_layout_build_device(lay.handle, fake, fake, fake, None) == 2
         assert "device rule" in bs.bsattn_last_error()
+    # a layout of 32-token blocks needs the mask array
+    sub = bs.bsattn_make_layout(2, 1024, 32, 3, [0], 1, 0)
+    assert L.bsattn_layout_build_device(sub.handle, fake, fake, None, None) == 1
+    assert "tile_masks_dev" in bs.bsattn_last_error()

@@ -288,6 +288,43 @@ def test_device_layout_random_tuples():
         assert np.array_equal(dci.cpu().numpy()[: ci.size], ci), (nb, H, w, G, r, seed)
 
 
+@pytest.mark.parametrize("block", [32, 128])
+def test_device_layout_other_block_sizes(block):
+    """32- and 128-token blocks: the device rule's tile CSR (and, for 32-token
+    blocks, the quarter masks) equal the host's, on the workloads' own layouts
+    and random tuples."""
+    g = np.random.default_rng(block)
+    cases = [WORKLOADS[f"bigbird{block}-L8192"]]
+    for _ in range(30):
+        nbr = int(g.integers(2, 80 if block == 32 else 40)) // 2 * 2   # rule blocks, an even count
+        nbr = max(nbr, 2)
+        H = int(g.integers(1, 4))
+        w = int(g.integers(0, 8)) * 2 + 1
+        ng = int(g.integers(0, min(nbr, 5) + 1))
+        G = sorted(g.choice(nbr, size=ng, replace=False).tolist())
+        r = int(g.integers(0, 12))
+        cases.append((H, nbr * block, w, G, r, int(g.integers(0, 2 ** 62))))
+    for c in cases:
+        if isinstance(c, tuple):
+            H, L, w, G, r, seed = c
+        else:
+            H, L, w, G, r, seed = c.heads, c.seq_len, c.window_blocks, list(c.global_blocks), c.random_blocks, \
+                c.layout_seed
+        _say("device layout", block, H, L, w, G, r)
+        lay = bs.bsattn_make_layout(H, L, block, w, G, r, seed)
+        rp, ci = bs.bsattn_layout_csr(lay)
+        masks = bs.bsattn_layout_tile_masks(lay)
+        drp = torch.full((rp.size,), -7, dtype=torch.int32, device="cuda")
+        dci = torch.full((max(1, ci.size),), -7, dtype=torch.int32, device="cuda")
+        dsub = torch.full((max(1, ci.size),), 0xEE, dtype=torch.uint8, device="cuda") if block == 32 else None
+        bs.bsattn_layout_build_device(lay, drp, dci, dsub)
+        torch.cuda.synchronize()
+        assert np.array_equal(drp.cpu().numpy(), rp), c
+        assert np.array_equal(dci.cpu().numpy()[: ci.size], ci), c
+        if block == 32:
+            assert np.array_equal(dsub.cpu().numpy()[: ci.size], masks), c
+
+
 def test_bitwise_deterministic():
     wl = WORKLOADS["bigbird-L8192"]
     _say("determinism", wl.name)
