@@ -10,7 +10,9 @@
 #include <cstdio>
 #include <new>
 #include <string>
+#include <tuple>
 
+#include <hipblaslt/hipblaslt.h>
 #include <rocblas/rocblas.h>
 
 #include "internal.h"
@@ -25,6 +27,12 @@ thread_local hipEvent_t g_ev_after = nullptr;
 // Set while a call must not allocate (bsattn_forward_noalloc): a schedule that
 // was not built by bsattn_prepare is then an error instead of being built.
 thread_local bool g_no_build = false;
+// Strides of Q/K/V and O for the forward that the attention layer runs on its
+// own buffers (null: contiguous [B, H, L, D]).
+struct LayerStrides {
+    int64_t qkv_bs, qkv_hs, qkv_ts, o_bs, o_hs, o_ts;
+};
+thread_local const LayerStrides* g_strides = nullptr;
 
 bsattn_status fail(bsattn_status st, const char* fmt, ...) {
     char buf[512];
@@ -786,8 +794,9 @@ rocblas_status gemm_xwt(rocblas_handle h, const void* A, const void* W, float* C
 
 // Workspace of bsattn_layer_forward: [qkv32 | out32] [q | o2] [k] [v] [o] [lse] [attention workspace].
 struct LayerWs {
-    size_t qkv32, q, k, v, o, lse, attn, total;
+    size_t qkv32, q, k, v, o, lse, attn, lt, total;
 };
+constexpr size_t kLtWorkspace = (size_t)32 << 20;   // hipBLASLt's workspace within the layer's
 LayerWs layer_workspace(const bsattn_layout* lay, int32_t B, int32_t D, size_t attn_bytes) {
     const size_t rows = (size_t)B * lay->L;
     const size_t C = (size_t)lay->H * D;
@@ -805,8 +814,85 @@ LayerWs layer_workspace(const bsattn_layout* lay, int32_t B, int32_t D, size_t a
     w.o = take(rows * C * 2);
     w.lse = take(rows * lay->H * sizeof(float));
     w.attn = take(attn_bytes);
+    w.lt = take(kLtWorkspace);
     w.total = off;
     return w;
+}
+
+// hipBLASLt handles, one per (thread, device); created on first use.
+hipblasLtHandle_t lt_handle(int dev) {
+    thread_local std::vector<hipblasLtHandle_t> handles;
+    if (handles.size() <= (size_t)dev) handles.resize((size_t)dev + 1, nullptr);
+    if (!handles[(size_t)dev] && hipblasLtCreate(&handles[(size_t)dev]) != HIPBLAS_STATUS_SUCCESS)
+        handles[(size_t)dev] = nullptr;
+    return handles[(size_t)dev];
+}
+
+// One GEMM shape with a bias epilogue: row-major Y[M, N] (bf16) = X[M, K] (bf16)
+// * W[N, K]^T (bf16) + bias[N] (bf16), fp32 accumulation, the bias added in
+// fp32 and the sum rounded once.  In hipBLASLt's column-major terms
+// Y^T = op(W) X^T with op = transpose, and the bias runs along Y^T's rows.
+struct LtPlan {
+    bool ok = false;
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ly = nullptr;
+    hipblasLtMatmulAlgo_t algo{};
+};
+
+// The plan of (device, M, N, K), built on first use per thread; !ok when the
+// library has no algorithm for it (the layer then takes its unfused path).
+const LtPlan& lt_plan(int dev, int M, int N, int K) {
+    thread_local std::map<std::tuple<int, int, int, int>, LtPlan> plans;
+    auto key = std::make_tuple(dev, M, N, K);
+    auto it = plans.find(key);
+    if (it != plans.end()) return it->second;
+    LtPlan p;
+    hipblasLtHandle_t h = lt_handle(dev);
+    bool good = h != nullptr;
+    good = good && hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
+    const hipblasOperation_t tA = HIPBLAS_OP_T, tB = HIPBLAS_OP_N;
+    const hipblasLtEpilogue_t epi = HIPBLASLT_EPILOGUE_BIAS;
+    const hipDataType bias_type = HIP_R_16BF;
+    good = good && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &tA, sizeof(tA)) ==
+                       HIPBLAS_STATUS_SUCCESS;
+    good = good && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tB, sizeof(tB)) ==
+                       HIPBLAS_STATUS_SUCCESS;
+    good = good && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof(epi)) ==
+                       HIPBLAS_STATUS_SUCCESS;
+    good = good && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_type,
+                                                   sizeof(bias_type)) == HIPBLAS_STATUS_SUCCESS;
+    // W as stored: column-major K x N (ld K); X^T: K x M (ld K); Y^T: N x M (ld N)
+    good = good && hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS;
+    good = good && hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, M, K) == HIPBLAS_STATUS_SUCCESS;
+    good = good && hipblasLtMatrixLayoutCreate(&p.ly, HIP_R_16BF, N, M, N) == HIPBLAS_STATUS_SUCCESS;
+    if (good) {
+        hipblasLtMatmulPreference_t pref = nullptr;
+        const uint64_t ws = kLtWorkspace;
+        good = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+               hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws,
+                                                     sizeof(ws)) == HIPBLAS_STATUS_SUCCESS;
+        hipblasLtMatmulHeuristicResult_t res{};
+        int found = 0;
+        good = good && hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.la, p.lb, p.ly, p.ly, pref, 1, &res, &found) ==
+                           HIPBLAS_STATUS_SUCCESS && found > 0;
+        if (good) p.algo = res.algo;
+        if (pref) (void)hipblasLtMatmulPreferenceDestroy(pref);
+    }
+    p.ok = good;
+    return plans.emplace(key, p).first->second;
+}
+
+// Y = X W^T + bias through the plan; false when the plan is unusable.
+bool lt_gemm_bias(int dev, const void* X, const void* W, const void* bias, void* Y, int M, int N, int K, void* ws,
+                  hipStream_t stream) {
+    const LtPlan& p = lt_plan(dev, M, N, K);
+    if (!p.ok) return false;
+    if (hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) !=
+        HIPBLAS_STATUS_SUCCESS)
+        return false;
+    const float one = 1.f, zero = 0.f;
+    return hipblasLtMatmul(lt_handle(dev), p.desc, &one, W, p.la, X, p.lb, &zero, Y, p.ly, Y, p.ly, &p.algo, ws,
+                           kLtWorkspace, stream) == HIPBLAS_STATUS_SUCCESS;
 }
 
 // Forward over a token layout (bf16): the gathered global K/V tiles, then the
@@ -1615,6 +1701,11 @@ bsattn_status bsattn_forward(const bsattn_layout* lay, bsattn_dtype dtype, int32
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
     const int mask = band ? MASK_BAND : (sub ? MASK_SUB : (key_valid_len ? MASK_PAD : MASK_NONE));
+    a.strided = g_strides != nullptr && dtype == BSATTN_BF16;
+    if (a.strided) {
+        a.qkv_bs = g_strides->qkv_bs; a.qkv_hs = g_strides->qkv_hs; a.qkv_ts = g_strides->qkv_ts;
+        a.o_bs = g_strides->o_bs; a.o_hs = g_strides->o_hs; a.o_ts = g_strides->o_ts;
+    }
 
     hipError_t e;
     if (dtype == BSATTN_F32) {
@@ -1992,6 +2083,25 @@ bsattn_status bsattn_layer_forward(const bsattn_layout* lay, int32_t B, int32_t 
     float* qkv32 = (float*)(ws + w.qkv32);
     void *q = ws + w.q, *k = ws + w.k, *v = ws + w.v, *o = ws + w.o;
     float* lse = (float*)(ws + w.lse);
+    if (lay->kind == 0 || lay->kind == 1) {
+        // Fused path: the qkv GEMM adds b_qkv in its epilogue and writes bf16
+        // token-major [B L, 3C] (into qkv32's space), the attention reads its
+        // heads in place and writes O as the concatenated heads [B L, C] (into
+        // q's space), and the output GEMM adds b_proj in its epilogue.
+        uint16_t* qkv = (uint16_t*)qkv32;
+        void* lt_ws = ws + w.lt;
+        if (lt_gemm_bias(dev, x, w_qkv, b_qkv, qkv, (int)rows, (int)(3 * C), (int)C, lt_ws, stream)) {
+            const LayerStrides ls{(int64_t)L * 3 * C, D, 3 * C, (int64_t)L * C, D, C};
+            g_strides = &ls;
+            st = bsattn_forward(lay, BSATTN_BF16, B, H, L, D, qkv, qkv + C, qkv + 2 * C, q, lse, key_valid_len,
+                                scale, attn_bytes ? ws + w.attn : nullptr, attn_bytes, stream);
+            g_strides = nullptr;
+            if (st != BSATTN_OK) return st;
+            if (!lt_gemm_bias(dev, q, w_proj, b_proj, out, (int)rows, (int)C, (int)C, lt_ws, stream))
+                return fail(BSATTN_ERR_HIP, "output GEMM failed");
+            return ok();
+        }
+    }
     // 1. qkv = x W_qkv^T (fp32), then + bias, rounded, split into heads
     if (gemm_xwt(hb, x, w_qkv, qkv32, (int)rows, (int)(3 * C), (int)C) != rocblas_status_success)
         return fail(BSATTN_ERR_HIP, "qkv GEMM failed");

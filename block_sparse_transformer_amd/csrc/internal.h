@@ -136,6 +136,12 @@ struct FwdArgs {
     // per-query top-keep layouts (MASK_BITS): [B*H][L][nb] words, bit b of
     // word (g, t, j) set iff query t of group g keeps key 64 j + b
     const uint64_t* keep_bits;
+    // strided tensors (the attention layer; the kernels' STRIDED instances):
+    // row t of head h of batch entry b of Q, K, V sits at b*qkv_bs + h*qkv_hs
+    // + t*qkv_ts elements from its base, of O at b*o_bs + h*o_hs + t*o_ts.
+    // Otherwise Q, K, V and O are contiguous [B, H, L, D].
+    bool strided;
+    int64_t qkv_bs, qkv_hs, qkv_ts, o_bs, o_hs, o_ts;
     float scale;              // score scale
     float scale_log2;         // scale * log2(e)
 };

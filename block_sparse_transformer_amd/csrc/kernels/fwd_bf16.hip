@@ -49,6 +49,9 @@
 //    log-sum-exp.  (Merging inside the attention kernel by the last chunk to
 //    arrive needs device-scope release/acquire fences, which on gfx950 write
 //    back and invalidate the XCD's L2 and slowed every resident workgroup.)
+//  * Both kernels have STRIDED instances for the attention layer: Q, K and V
+//    are read in place from the qkv projection's token-major output and O is
+//    written as the concatenated heads, at the strides FwdArgs gives.
 //  * Scheduling: workgroups are dealt round-robin to the 8 XCDs; workgroup i
 //    runs on XCD i%8, and its list holds units of the (batch, head) groups
 //    assigned to that XCD, so every group's K/V is read by one XCD and stays
@@ -183,12 +186,21 @@ __device__ __forceinline__ void issue_half(const uint16_t* base, int j, const ui
     }
 }
 
+// Row t of (b, h) group bh of the bf16 output O: contiguous [B, H, L, D], or
+// at the strides of the attention layer's concatenated heads.
+__device__ __forceinline__ uint16_t* o_row(const FwdArgs& a, size_t bh, int t, int D) {
+    if (a.strided)
+        return (uint16_t*)a.out + (int64_t)(bh / a.H) * a.o_bs + (int64_t)(bh % a.H) * a.o_hs + (int64_t)t * a.o_ts;
+    return (uint16_t*)a.out + (bh * a.L + t) * D;
+}
+
 __device__ __forceinline__ int tile_j(int e) { return e & kTileJ; }
 __device__ __forceinline__ int tile_unit(int e) { return (e >> kTileUnitShift) & (kMaxBinUnits - 1); }
 // allowed 32 x 32 sub-blocks of a tile: bit 2a + b, query half a, key half b
 __device__ __forceinline__ int tile_sub(int e) { return (e >> kTileSubShift) & 15; }
 
-template <int D, int MASK>
+// STRIDED: Q, K, V and O at the FwdArgs strides (the attention layer's layout)
+template <int D, int MASK, bool STRIDED = false>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
     using Gm = Geo<D>;
     constexpr int NC = Gm::NC, NDB = Gm::NDB, TILE = Gm::TILE;
@@ -233,18 +245,21 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         if (MASK == MASK_PAD) u_valid = min(max(a.valid_len[ub], 0), a.L);
     }
     auto rd = [](int v, int k) -> int { return __builtin_amdgcn_readlane(v, k); };
+    // row stride of Q, K and V (elements), and a group's first row
+    const int64_t RS = STRIDED ? a.qkv_ts : D;
     auto gbase = [&](const void* t, int g) -> const uint16_t* {
+        if (STRIDED) return (const uint16_t*)t + (int64_t)(g / a.H) * a.qkv_bs + (int64_t)(g % a.H) * a.qkv_hs;
         return (const uint16_t*)t + (size_t)g * a.L * D;
     };
     // K (V) tile j of group g: a block of the sequence, or (token layouts,
     // j >= nb) a gathered tile of the global tokens' keys
     auto ktile = [&](int g, int j) -> const uint16_t* {
         if (MASK == MASK_TOKEN && j >= a.nb) return a.kg + ((size_t)g * a.n_gt + (j - a.nb)) * TILE;
-        return gbase(a.k, g) + (size_t)j * TILE;
+        return gbase(a.k, g) + (size_t)j * 64 * RS;
     };
     auto vtile = [&](int g, int j) -> const uint16_t* {
         if (MASK == MASK_TOKEN && j >= a.nb) return a.vg + ((size_t)g * a.n_gt + (j - a.nb)) * TILE;
-        return gbase(a.v, g) + (size_t)j * TILE;
+        return gbase(a.v, g) + (size_t)j * 64 * RS;
     };
 
     // token of this lane's query row in a unit of kind `kind`, group g (-1: unused routed row)
@@ -260,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             u32x4_t u = {0u, 0u, 0u, 0u};
-            if (t >= 0) u = *(const u32x4_t*)(qp + (size_t)t * D + 16 * c + 8 * hh);
+            if (t >= 0) u = *(const u32x4_t*)(qp + (size_t)t * RS + 16 * c + 8 * hh);
             qf[c] = as_bf16x8(u);
         }
     };
@@ -270,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         const size_t bh = (size_t)g;
         // O^T register i of block db <-> d = 32db + 8(i/4) + 4hh + i%4
         if (slot < 0) {
-            uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D;
+            uint16_t* orow = STRIDED ? o_row(a, bh, t, D) : (uint16_t*)a.out + (bh * a.L + t) * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -367,8 +382,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
         const int sl = r * kThreads + tid;
         const int row = sl / Gm::PIECES, q = sl % Gm::PIECES;
         // minus the instruction offset 2048 (r % 4) - 4096 that the load adds
-        koffs[r] = (uint32_t)(row * D + swz_k(row, q) * 8) * 2u + 4096u - 2048u * (r % 4);
-        voffs[r] = (uint32_t)(row * D + swz_v(row, q) * 8) * 2u + 4096u - 2048u * (r % 4);
+        koffs[r] = (uint32_t)(row * RS + swz_k(row, q) * 8) * 2u + 4096u - 2048u * (r % 4);
+        voffs[r] = (uint32_t)(row * RS + swz_v(row, q) * 8) * 2u + 4096u - 2048u * (r % 4);
     }
     const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(wave * 64 * 16);
     const uint32_t kl0 = lds_addr(kbuf) + wave_lds, vl0 = lds_addr(vbuf) + wave_lds;
@@ -732,7 +747,38 @@ __device__ __forceinline__ void issue_tile1(const uint16_t* base, int j, uint32_
     lds_load16x4_1k(voff, t + 32 * 64, lds + 4096 + 2048);
 }
 
-template <int MASK>
+// As lds_load16x4_1k, for rows `rs` bytes apart: load r reads rows 8 r .. 8 r + 7
+// from its own scalar base (sbase + r (8 rs - 1 KB), so that the instruction
+// offset, which also places the LDS destination, cancels out).
+__device__ __forceinline__ void lds_load16x4_rows(uint32_t voff, const char* sbase, uint32_t rs, uint32_t m0v) {
+    const uint32_t step = 8u * rs - 1024u;
+    const char* s1 = sbase + step;
+    const char* s2 = s1 + step;
+    const char* s3 = s2 + step;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3 offset:-2048\n\t"
+        "global_load_lds_dwordx4 %1, %4 offset:-1024\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
+        "global_load_lds_dwordx4 %1, %6 offset:1024\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(m0v), "s"(sbase), "s"(s1), "s"(s2), "s"(s3)
+        : "memory");
+}
+
+// The 64x64 tile starting at `t`, rows rs bytes apart (the layer's strided
+// layout): voff is the lane's offset within rows 0..7 plus 2 KB.
+__device__ __forceinline__ void issue_tile_rows(const uint16_t* t, uint32_t rs, uint32_t voff, uint32_t lds) {
+    lds_load16x4_rows(voff, (const char*)t, rs, lds + 2048);
+    lds_load16x4_rows(voff, (const char*)t + 32u * rs, rs, lds + 4096 + 2048);
+}
+
+// STRIDED: Q, K, V and O at the FwdArgs strides (the attention layer's layout)
+template <int MASK, bool STRIDED = false>
 __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_d64_kernel(const FwdArgs a) {
     constexpr int D = 64, NC = 4, NDB = 2, TILE = 64 * 64;
     __shared__ __attribute__((aligned(1024))) uint16_t kvbuf[kQWaves][2][TILE];
@@ -792,18 +838,21 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         if (MASK == MASK_PAD) u_valid = min(max(a.valid_len[ub], 0), a.L);
     }
     auto rd = [](int v, int k) -> int { return __builtin_amdgcn_readlane(v, k); };
+    // row stride of Q, K and V (elements), and a group's first row
+    const int64_t RS = STRIDED ? a.qkv_ts : D;
     auto gbase = [&](const void* t, int g) -> const uint16_t* {
+        if (STRIDED) return (const uint16_t*)t + (int64_t)(g / a.H) * a.qkv_bs + (int64_t)(g % a.H) * a.qkv_hs;
         return (const uint16_t*)t + (size_t)g * a.L * D;
     };
     // K (V) tile j of group g: a block of the sequence, or (token layouts,
     // j >= nb) a gathered tile of the global tokens' keys
     auto ktile = [&](int g, int j) -> const uint16_t* {
         if (MASK == MASK_TOKEN && j >= a.nb) return a.kg + ((size_t)g * a.n_gt + (j - a.nb)) * TILE;
-        return gbase(a.k, g) + (size_t)j * TILE;
+        return gbase(a.k, g) + (size_t)j * 64 * RS;
     };
     auto vtile = [&](int g, int j) -> const uint16_t* {
         if (MASK == MASK_TOKEN && j >= a.nb) return a.vg + ((size_t)g * a.n_gt + (j - a.nb)) * TILE;
-        return gbase(a.v, g) + (size_t)j * TILE;
+        return gbase(a.v, g) + (size_t)j * 64 * RS;
     };
     // token of query row r (0..63) of a unit (-1: unused routed row)
     auto query_token = [&](int kind, int g, int r) -> int {
@@ -821,7 +870,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 u32x4_t u = {0u, 0u, 0u, 0u};
-                if (tq[qb] >= 0) u = *(const u32x4_t*)(qp + (uint32_t)(tq[qb] * D + 16 * c + 8 * hh));
+                if (tq[qb] >= 0) u = *(const u32x4_t*)(qp + (uint32_t)(tq[qb] * RS + 16 * c + 8 * hh));
                 qf[qb][c] = as_bf16x8(u);
             }
         }
@@ -832,7 +881,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         // O^T register i of block db <-> d = 32db + 8(i/4) + 4hh + i%4
         // group / slot bases are uniform (scalar), the lane offsets 32-bit
         if (slot < 0) {
-            uint16_t* orow = (uint16_t*)a.out + bh * a.L * D + (uint32_t)(t * D);
+            uint16_t* orow = STRIDED ? o_row(a, bh, t, D) : (uint16_t*)a.out + bh * a.L * D + (uint32_t)(t * D);
             // Lanes l and l + 32 hold d = 8gq + 0..3 and 8gq + 4..7 of the same
             // row: swapping halves (v_permlane32_swap moves the upper half-wave's
             // first operand to the lower half-wave's second, and back) leaves
@@ -920,8 +969,8 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     uint32_t kdo, vdo;
     {
         const int row0 = lane >> 3, q = lane & 7;
-        kdo = (uint32_t)(row0 * D + swz_k(row0, q) * 8) * 2u + 2048u;
-        vdo = (uint32_t)(row0 * D + swz_v(row0, q) * 8) * 2u + 2048u;
+        kdo = (uint32_t)(row0 * RS + swz_k(row0, q) * 8) * 2u + 2048u;
+        vdo = (uint32_t)(row0 * RS + swz_v(row0, q) * 8) * 2u + 2048u;
     }
     const uint16_t* kbuf = kvbuf[wv][0];
     const uint16_t* vbuf = kvbuf[wv][1];
@@ -1097,8 +1146,13 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     int tq_cur[2], tq_next[2] = {-1, -1};
     bf16x8_t qf[2][NC];
     load_q(kind_cur, g_cur, qf, tq_cur);
-    issue_tile1(ktile(g_cur, tile_j(e0)), 0, kdo, kl);
-    issue_tile1(vtile(g_cur, tile_j(e0)), 0, vdo, vl);
+    if (STRIDED) {
+        issue_tile_rows(ktile(g_cur, tile_j(e0)), (uint32_t)(RS * 2), kdo, kl);
+        issue_tile_rows(vtile(g_cur, tile_j(e0)), (uint32_t)(RS * 2), vdo, vl);
+    } else {
+        issue_tile1(ktile(g_cur, tile_j(e0)), 0, kdo, kl);
+        issue_tile1(vtile(g_cur, tile_j(e0)), 0, vdo, vl);
+    }
     reset();
 
     // A unit's epilogue (normalise, store O and LSE, reset) runs in the next
@@ -1157,7 +1211,10 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const bool more = f + 1 < F;
         const uint16_t* kn = ktile(tile_g(e1), tile_j(e1));
         const uint16_t* vn = vtile(tile_g(e1), tile_j(e1));
-        if (more) lds_load16x4_1k(kdo, kn, kl + 2048);
+        if (more) {
+            if (STRIDED) lds_load16x4_rows(kdo, (const char*)kn, (uint32_t)(RS * 2), kl + 2048);
+            else lds_load16x4_1k(kdo, kn, kl + 2048);
+        }
         if (pend) {                         // the previous unit's epilogue
             finish();
             pend = false;
@@ -1165,13 +1222,22 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         softmax_prep(e0, kind_cur, tq_cur, valid_cur, sc, (e0 & kTileFirst) != 0);
         u32x4_t p0[2], p1[2], p2[2], p3[2];
         softmax_exp(sc, 0, C0(), p0);
-        if (more) lds_load16x4_1k(kdo, kn + 32 * 64, kl + 4096 + 2048);
+        if (more) {
+            if (STRIDED) lds_load16x4_rows(kdo, (const char*)(kn + 32 * RS), (uint32_t)(RS * 2), kl + 4096 + 2048);
+            else lds_load16x4_1k(kdo, kn + 32 * 64, kl + 4096 + 2048);
+        }
         softmax_exp(sc, 1, C0(), p1);
         pv(va, 0, C0(), p0);
-        if (more) lds_load16x4_1k(vdo, vn, vl + 2048);
+        if (more) {
+            if (STRIDED) lds_load16x4_rows(vdo, (const char*)vn, (uint32_t)(RS * 2), vl + 2048);
+            else lds_load16x4_1k(vdo, vn, vl + 2048);
+        }
         softmax_exp(sc, 0, C2(), p2);
         pv(va, 1, C0(), p1);
-        if (more) lds_load16x4_1k(vdo, vn + 32 * 64, vl + 4096 + 2048);
+        if (more) {
+            if (STRIDED) lds_load16x4_rows(vdo, (const char*)(vn + 32 * RS), (uint32_t)(RS * 2), vl + 4096 + 2048);
+            else lds_load16x4_1k(vdo, vn + 32 * 64, vl + 4096 + 2048);
+        }
         softmax_exp(sc, 1, C2(), p3);
         pv(va, 0, C2(), p2);
         pv(va, 1, C2(), p3);
@@ -1229,7 +1295,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 float mx = -INFINITY;
 #pragma unroll
                 for (int c = 0; c < kQWaves; ++c) mx = __builtin_fmaxf(mx, lsev[c]);
-                uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * 8;
+                uint16_t* orow = (STRIDED ? o_row(a, bh, t, D) : (uint16_t*)a.out + (bh * a.L + t) * D) + part * 8;
                 if (mx == -INFINITY) {
                     *(u32x4_t*)orow = u32x4_t{0u, 0u, 0u, 0u};
                     if (part == 0) a.lse[bh * a.L + t] = -INFINITY;
@@ -1309,7 +1375,7 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(const FwdArgs a) {
     float mxl = -INFINITY;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) mxl = __builtin_fmaxf(mxl, lsev[c]);
-    uint16_t* orow = (uint16_t*)a.out + (bh * a.L + t) * D + part * DP;
+    uint16_t* orow = o_row(a, bh, t, D) + part * DP;
     if (mxl == -INFINITY) {
 #pragma unroll
         for (int d = 0; d < DP; d += 2) *(uint32_t*)(orow + d) = 0u;
@@ -1584,22 +1650,23 @@ __global__ __launch_bounds__(256) void gather_global_kernel(const FwdArgs a, uin
 // The attention kernels are launched with hipExtLaunchKernelGGL: given events,
 // the dispatch itself records the kernel's start and stop (no separate marker
 // packets between kernels, which would add to the time they measure).
-template <int D, int MASK>
+template <int D, int MASK, bool STRIDED = false>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s, hipEvent_t before, hipEvent_t after) {
     const int64_t grid = (int64_t)kXcds * a.n_bins;
     if (grid == 0) return hipSuccess;
-    hipExtLaunchKernelGGL((fwd_bf16_kernel<D, MASK>), dim3((unsigned)grid), dim3(kThreads), 0, s, before, after, 0, a);
+    hipExtLaunchKernelGGL((fwd_bf16_kernel<D, MASK, STRIDED>), dim3((unsigned)grid), dim3(kThreads), 0, s, before,
+                          after, 0, a);
     return hipGetLastError();
 }
 
-template <int MASK>
+template <int MASK, bool STRIDED = false>
 hipError_t launch_d64(const FwdArgs& a, hipStream_t s, hipEvent_t before, hipEvent_t after) {
     // kQWaves lists (bins) per workgroup
     if (a.n_bins % kQWaves != 0) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)kXcds * (a.n_bins / kQWaves);
     if (grid == 0) return hipSuccess;
-    hipExtLaunchKernelGGL((fwd_bf16_d64_kernel<MASK>), dim3((unsigned)grid), dim3(kQThreads), 0, s, before, after, 0,
-                          a);
+    hipExtLaunchKernelGGL((fwd_bf16_d64_kernel<MASK, STRIDED>), dim3((unsigned)grid), dim3(kQThreads), 0, s, before,
+                          after, 0, a);
     return hipGetLastError();
 }
 
@@ -1622,7 +1689,20 @@ int fwd_bf16_ctas_per_cu(int head_dim, bool two_wave) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
                            hipEvent_t after) {
     hipError_t e;
-    if (mask == MASK_BITS) {
+    if (a.strided) {
+        // the attention layer's layout: block (any block size) and band layouts
+        if (mask == MASK_TOKEN || mask == MASK_BITS) return hipErrorInvalidValue;
+        if (head_dim == 64)
+            e = mask == MASK_PAD    ? launch_d64<MASK_PAD, true>(a, s, before, after)
+              : mask == MASK_BAND   ? launch_d64<MASK_BAND, true>(a, s, before, after)
+              : mask == MASK_SUB    ? launch_d64<MASK_SUB, true>(a, s, before, after)
+                                    : launch_d64<MASK_NONE, true>(a, s, before, after);
+        else
+            e = mask == MASK_PAD    ? launch_fwd_t<128, MASK_PAD, true>(a, s, before, after)
+              : mask == MASK_BAND   ? launch_fwd_t<128, MASK_BAND, true>(a, s, before, after)
+              : mask == MASK_SUB    ? launch_fwd_t<128, MASK_SUB, true>(a, s, before, after)
+                                    : launch_fwd_t<128, MASK_NONE, true>(a, s, before, after);
+    } else if (mask == MASK_BITS) {
         // the two-wave kernel at either width (the D = 64 kernel has no bit mask)
         e = head_dim == 64 ? launch_fwd_t<64, MASK_BITS>(a, s, before, after)
                            : launch_fwd_t<128, MASK_BITS>(a, s, before, after);

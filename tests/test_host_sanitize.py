@@ -35,7 +35,7 @@ def _build():
         assert r.returncode == 0, f"g++ failed for {src}:\n{r.stderr[-4000:]}"
         objs.append(obj)
     exe = os.path.join(OUT, "schedule_check")
-    r = subprocess.run(["g++", *FLAGS, *objs, "-o", exe, f"-L{ROCM}/lib", "-lamdhip64", "-lrocblas",
+    r = subprocess.run(["g++", *FLAGS, *objs, "-o", exe, f"-L{ROCM}/lib", "-lamdhip64", "-lrocblas", "-lhipblaslt",
                         f"-Wl,-rpath,{ROCM}/lib"], capture_output=True, text=True)
     assert r.returncode == 0, f"link failed:\n{r.stderr[-4000:]}"
     return exe
