@@ -502,7 +502,9 @@ def main():
     value = tokens / (ms_step / 1e3)
     eff_tflops = flops_per_step / (ms_step / 1e3) / 1e12
     kern_tflops = kernel_flops / (kern_avg_ms / 1e3) / 1e12
-    kname = "bwd_dkdv_kernel" if backward else ("topr_select_kernel" if wl.topr else main_kernel(D))
+    # the top-keep selection: key-stationary at D = 64, L <= 2048, else the LDS-tiled kernel
+    topr_kernel = "topr_select_ks_kernel" if (D == 64 and L <= 2048) else "topr_select_kernel"
+    kname = "bwd_dkdv_kernel" if backward else (topr_kernel if wl.topr else main_kernel(D))
     # the kernel's own algorithmic bytes: Q, K, V read and O, LSE written once (the
     # backward's dK/dV pass: Q, K, V, dO read, dK, dV written, LSE and delta read)
     kernel_bytes = wl.batch * wl.heads * wl.seq_len * ((6 if backward else 4) * wl.head_dim * elem + (8 if backward else 4))

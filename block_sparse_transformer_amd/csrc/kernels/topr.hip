@@ -19,6 +19,10 @@
 // how many keys equal to T are kept; those are the lowest-index ones, counted
 // in index order with ballots.  The result is one 64-bit word per (query, key
 // tile): bit b set iff key 64j + b is kept.
+//
+// topr_select_ks_kernel<KPL> (D = 64, L <= 2048) turns this around: the keys
+// stay in registers and the queries arrive as scalar operands, so the FMA
+// loop reads no LDS (the LDS-tiled kernel above is bound by its key reads).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -197,6 +201,220 @@ __global__ __launch_bounds__(kSelThreads) void topr_select_kernel(const uint16_t
 
 // Launched with hipExtLaunchKernelGGL: given events, the dispatch itself
 // records the kernel's start and stop.
+// Key-stationary selection, D = 64, L <= 1024 KPL: one workgroup of 1024
+// threads per (batch, head, chunk of queries).  Lane `lane` of wave w holds the
+// KPL keys s = (w KPL + j) 64 + lane in registers as packed bf16; the queries
+// come in batches of QB, their values as scalar operands, so the in-order
+// FMA chains read nothing from LDS.  Each batch's QB queries then share one
+// radix select (LDS histograms, a wave per query scans), ties are ranked in
+// index order from per-tile counts, and the kept-key word of tile w KPL + j is
+// the wave's ballot.
+constexpr int kKsThreads = 1024;
+constexpr int kKsWaves = kKsThreads / 64;
+constexpr int kKsBatch = 8;
+
+template <int KPL>
+__global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16_t* __restrict__ q,
+                                                                    const uint16_t* __restrict__ k,
+                                                                    uint64_t* __restrict__ bits, int L, int keep,
+                                                                    int chunk, int nchunks) {
+    constexpr int D = 64;
+    constexpr int QB = kKsBatch;
+    constexpr int NTILE = kKsWaves * KPL;          // key tiles a workgroup covers
+    __shared__ uint32_t hist[QB][256];
+    __shared__ uint32_t s_digit[QB], s_above[QB];
+    __shared__ uint32_t eqc[QB][NTILE];             // keys equal to T per (query, tile), then their prefix
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const size_t g = blockIdx.x / nchunks;
+    const int c0 = (blockIdx.x % nchunks) * chunk;
+    const int c1 = min(L, c0 + chunk);
+    const int nt = L / 64;
+
+    // this lane's keys, packed bf16 pairs
+    uint32_t kp[KPL][D / 2];
+    bool kvalid[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const int m = wave * KPL + j;
+        kvalid[j] = m < nt;
+        const uint4* src = (const uint4*)(k + (g * L + (size_t)(kvalid[j] ? m : 0) * 64 + lane) * D);
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const uint4 u = kvalid[j] ? src[c] : make_uint4(0, 0, 0, 0);
+            kp[j][4 * c + 0] = u.x; kp[j][4 * c + 1] = u.y; kp[j][4 * c + 2] = u.z; kp[j][4 * c + 3] = u.w;
+        }
+    }
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+
+    for (int t0 = c0; t0 < c1; t0 += QB) {
+        constexpr int nq = QB;   // chunks and L are multiples of QB: every batch is full
+        // keep the keys packed: without this the compiler converts all of them
+        // to fp32 once, ahead of the loop, and runs out of registers
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+#pragma unroll
+            for (int x = 0; x < D / 2; ++x) asm volatile("" : "+v"(kp[j][x]));
+        // ---- exact in-order scores of the batch's queries against this lane's keys ----
+        float acc[QB][KPL];
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) acc[i][j] = 0.f;
+        // the batch's q values are uniform: scalar loads from one base (rows D
+        // elements apart), 4 d (2 packed pairs) per chunk, the next chunk's
+        // issued before this chunk's FMAs; a scheduling fence per chunk bounds
+        // how many are live
+        const uint32_t* qbase = (const uint32_t*)(q + (g * L + (size_t)t0) * D);
+        uint32_t qa[QB][2], qn[QB][2];
+        auto loadq = [&](int c, uint32_t (&dst)[QB][2]) {
+#pragma unroll
+            for (int i = 0; i < QB; ++i) {
+                const uint2 u = *(const uint2*)(qbase + i * (D / 2) + 2 * c);
+                dst[i][0] = u.x; dst[i][1] = u.y;
+            }
+        };
+        loadq(0, qa);
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) {
+            if (c + 1 < D / 4) loadq(c + 1, qn);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int hi = 0; hi < 2; ++hi) {
+                    float kf[KPL];
+#pragma unroll
+                    for (int j = 0; j < KPL; ++j) {
+                        const uint32_t w = kp[j][2 * c + e];
+                        kf[j] = __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
+                    }
+#pragma unroll
+                    for (int i = 0; i < QB; ++i) {
+                        const uint32_t w = qa[i][e];
+                        const float qv = __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
+#pragma unroll
+                        for (int j = 0; j < KPL; ++j) acc[i][j] = fmaf(qv, kf[j], acc[i][j]);
+                    }
+                }
+            // this chunk's FMAs all come before this point and the next chunk's
+            // after it (the accumulators pass through it), so only two chunks'
+            // q values are live and QB x KPL independent chains interleave
+#pragma unroll
+            for (int i = 0; i < QB; ++i)
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) asm volatile("" : "+v"(acc[i][j]));
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (c + 1 < D / 4) {
+#pragma unroll
+                for (int i = 0; i < QB; ++i) { qa[i][0] = qn[i][0]; qa[i][1] = qn[i][1]; }
+            }
+        }
+        uint32_t key[QB][KPL];
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) key[i][j] = order_key(acc[i][j]);
+
+        // ---- radix select of each query's keep-th largest key ----
+        uint32_t prefix[QB];
+        int need[QB];
+#pragma unroll
+        for (int i = 0; i < QB; ++i) { prefix[i] = 0; need[i] = keep; }
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            for (int x = tid; x < QB * 256; x += kKsThreads) hist[x / 256][x % 256] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < QB; ++i)
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) {
+                    const uint32_t kk = key[i][j];
+                    const bool match = pass == 0 || (kk >> (shift + 8)) == (prefix[i] >> (shift + 8));
+                    if (i < nq && kvalid[j] && match) atomicAdd(&hist[i][(kk >> shift) & 255u], 1u);
+                }
+            __syncthreads();
+            if (wave < nq) {
+                // one wave per query: lane l owns bins 4l .. 4l + 3
+                const int qi = wave;
+                uint32_t h[4], own = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) { h[b] = hist[qi][4 * lane + b]; own += h[b]; }
+                uint32_t suffix = own;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t o = __shfl_down(suffix, off);
+                    if (lane + off < 64) suffix += o;
+                }
+                uint32_t above = suffix - own;
+                int nd = need[0];
+#pragma unroll
+                for (int x = 1; x < QB; ++x)
+                    if (qi == x) nd = need[x];
+#pragma unroll
+                for (int b = 3; b >= 0; --b) {
+                    if (above < (uint32_t)nd && (uint32_t)nd <= above + h[b]) {
+                        s_digit[qi] = (uint32_t)(4 * lane + b);
+                        s_above[qi] = above;
+                    }
+                    above += h[b];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < QB; ++i)
+                if (i < nq) {
+                    prefix[i] |= s_digit[i] << shift;
+                    need[i] -= (int)s_above[i];
+                }
+            __syncthreads();
+        }
+
+        // ---- ties: rank keys equal to T in index order (tile, lane) ----
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                const uint64_t eb = __ballot(i < nq && kvalid[j] && key[i][j] == prefix[i]);
+                if (lane == 0) eqc[i][wave * KPL + j] = (uint32_t)__popcll(eb);
+            }
+        __syncthreads();
+        if (wave < QB) {
+            // exclusive prefix of query `wave`'s per-tile counts, one tile per lane
+            const uint32_t c = lane < NTILE ? eqc[wave][lane] : 0u;
+            uint32_t incl = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t o = __shfl_up(incl, off);
+                if (lane >= off) incl += o;
+            }
+            if (lane < NTILE) eqc[wave][lane] = incl - c;
+        }
+        __syncthreads();
+        uint64_t myword = 0;
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                const uint32_t kk = key[i][j];
+                const bool eq = i < nq && kvalid[j] && kk == prefix[i];
+                const uint64_t eb = __ballot(eq);
+                const uint32_t rank = eqc[i][wave * KPL + j] + (uint32_t)__popcll(eb & lt_mask);
+                const bool sel = i < nq && kvalid[j] && (kk > prefix[i] || (eq && rank < (uint32_t)need[i]));
+                const uint64_t word = __ballot(sel);
+                if (lane == i * KPL + j) myword = word;
+            }
+        // lane i KPL + j writes the word of query i, tile wave KPL + j
+        {
+            const int i = lane / KPL, j = lane % KPL;
+            const int m = wave * KPL + j;
+            if (lane < QB * KPL && i < nq && m < nt) bits[(g * L + t0 + i) * (size_t)nt + m] = myword;
+        }
+        __syncthreads();   // hist / eqc are rewritten by the next batch
+    }
+}
+
 template <int TPQ, int D>
 hipError_t launch_t(const void* q, const void* k, uint64_t* bits, int G, int L, int keep, hipStream_t s,
                     hipEvent_t before, hipEvent_t after) {
@@ -212,6 +430,22 @@ hipError_t launch_t(const void* q, const void* k, uint64_t* bits, int G, int L, 
 hipError_t launch_topr_select(const void* q, const void* k, uint64_t* bits, int G, int L, int D, int keep,
                               hipStream_t s, hipEvent_t before, hipEvent_t after) {
     if (L % 64 != 0 || L > kMaxTopLen || keep < 1 || keep > L || (D != 64 && D != 128)) return hipErrorInvalidValue;
+    if (D == 64 && L <= 2 * kKsThreads) {
+        // key-stationary: at most one workgroup per CU (a second round of
+        // workgroups would double the time), each over a chunk of queries
+        int nchunks = G >= 256 ? 1 : 256 / G;
+        int chunk = (L + nchunks - 1) / nchunks;
+        chunk = (chunk + kKsBatch - 1) / kKsBatch * kKsBatch;
+        nchunks = (L + chunk - 1) / chunk;
+        const dim3 grid((unsigned)((int64_t)G * nchunks));
+        if (L <= kKsThreads)
+            hipExtLaunchKernelGGL((topr_select_ks_kernel<1>), grid, dim3(kKsThreads), 0, s, before, after, 0,
+                                  (const uint16_t*)q, (const uint16_t*)k, bits, L, keep, chunk, nchunks);
+        else
+            hipExtLaunchKernelGGL((topr_select_ks_kernel<2>), grid, dim3(kKsThreads), 0, s, before, after, 0,
+                                  (const uint16_t*)q, (const uint16_t*)k, bits, L, keep, chunk, nchunks);
+        return hipGetLastError();
+    }
     if (L <= 2048)
         return D == 64 ? launch_t<16, 64>(q, k, bits, G, L, keep, s, before, after)
                        : launch_t<16, 128>(q, k, bits, G, L, keep, s, before, after);
