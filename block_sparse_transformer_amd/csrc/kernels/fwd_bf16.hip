@@ -713,6 +713,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
 // wave reads the tile's fragments first; the loads of its next tile then go
 // into the same buffers while it runs the softmax and the PV products.
 //
+// A step works on the four 32 x 32 score blocks (key half, query half) in
+// turn: the scores of the first block are issued alone, and each later
+// scheduling region pairs the softmax of one block (VALU) with matrix
+// products that do not depend on it -- the scores of later blocks, the PV
+// product of earlier ones -- interleaved by group barriers.  The running max
+// of a unit starts at its first block's max; the lazy raise (as in the
+// two-wave kernel) works per block.
+//
 // The two waves that share a SIMD get lists of equal length, and they keep
 // pace with each other: the SIMD's issue arbiter favours the older wave, so
 // left alone the younger one would fall behind and finish long after it,
@@ -982,22 +990,6 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
             for (int c = 0; c < NC; ++c) kf[kb][c] = as_bf16x8(*(const u32x4_t*)(Ks + koff[c] + 32 * kb * D));
     };
-    // S^T = K Q^T for both halves: s[kb][qb] register i <-> key 32kb + 8(i/4) + 4hh + i%4.
-    auto smma = [&](const bf16x8_t (&kf)[2][NC], const bf16x8_t (&q)[2][NC], f32x16_t (&s)[2][2]) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][c], q[qb][c], s[kb][qb], 0, 0, 0);
-    };
     // V^T fragments (A operand of O^T = V^T P^T), transposed on read.
     auto vread = [&](const uint16_t* Vs, bf16x8_t (&va)[4][NDB]) {
 #pragma unroll
@@ -1030,72 +1022,70 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             l[qb] = 0.f;
         }
     };
-    // row max (log2 units) of one half
-    auto tile_max = [&](const f32x16_t (&s)[2][2], int qb) -> float {
-        float v = __builtin_fmaxf(__builtin_fmaxf(s[0][qb][0], s[0][qb][1]), s[1][qb][0]);
+    // max (log2 units) of one 32 x 32 score block over the lane's 16 keys and
+    // its partner lane's (the same query)
+    auto blk_max = [&](const f32x16_t& s) -> float {
+        float v = __builtin_fmaxf(s[0], s[1]);
 #pragma unroll
-        for (int i = 2; i < 16; i += 2) v = __builtin_fmaxf(__builtin_fmaxf(v, s[0][qb][i]), s[0][qb][i + 1]);
-#pragma unroll
-        for (int i = 1; i < 15; i += 2) v = __builtin_fmaxf(__builtin_fmaxf(v, s[1][qb][i]), s[1][qb][i + 1]);
-        return pair_max(__builtin_fmaxf(v, s[1][qb][15])) * c2;
+        for (int i = 2; i < 16; i += 2) v = __builtin_fmaxf(__builtin_fmaxf(v, s[i]), s[i + 1]);
+        return pair_max(v) * c2;
     };
-    // masks; on a unit's first tile, the running max is the tile's max
-    auto softmax_prep = [&](int e, int kind, const int (&tq)[2], int valid, f32x16_t (&s)[2][2], bool first) {
+    // masks of score block (kb, qb): keys 32kb .. 32kb + 31 of the tile for
+    // query half qb, whose row this lane holds is tqq
+    auto mask_blk = [&](int e, int kind, int tqq, int valid, f32x16_t& s, int kb, int qb) {
         const int j = tile_j(e);
+        if (MASK == MASK_SUB) {
+            // 32-token blocks: drop the key halves query half qb may not see
+            if (!((tile_sub(e) >> (2 * qb + kb)) & 1))
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            if (MASK == MASK_SUB) {
-                // 32-token blocks: drop the key halves query half qb may not see
-                const int sub = tile_sub(e);
+                for (int i = 0; i < 16; ++i) s[i] = -INFINITY;
+        }
+        if (MASK == MASK_PAD) {
+            if (j * 64 + 64 > valid) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-                    if (!((sub >> (2 * qb + kb)) & 1))
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) s[kb][qb][i] = -INFINITY;
+                for (int i = 0; i < 16; ++i)
+                    if (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) s[i] = -INFINITY;
             }
-            if (MASK == MASK_PAD) {
-                if (j * 64 + 64 > valid) {
+        }
+        if (MASK == MASK_BAND || MASK == MASK_TOKEN) {
+            // a tile whose farthest (query, key) pair is inside the band needs no mask
+            if (kind >= 0 && j < a.nb && 64 * abs(kind - j) + 63 > a.band) {
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            if (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= valid) s[kb][qb][i] = -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (abs(tqq - (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4))) > a.band) s[i] = -INFINITY;
             }
-            if (MASK == MASK_BAND || MASK == MASK_TOKEN) {
-                // a tile whose farthest (query, key) pair is inside the band needs no mask
-                if (kind >= 0 && j < a.nb && 64 * abs(kind - j) + 63 > a.band) {
+        }
+        if (MASK == MASK_TOKEN && kind >= 0 && j >= a.nb) {
+            // gathered global keys: padding (-1) and keys the band already covers drop out
+            const int* gt = gtok_s + (j - a.nb) * 64;
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int4 gv = *(const int4*)(gt + 32 * kb + 8 * g4 + 4 * hh);
+                const int gs[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            if (abs(tq[qb] - (j * 64 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4))) > a.band)
-                                s[kb][qb][i] = -INFINITY;
-                }
+                for (int e2 = 0; e2 < 4; ++e2)
+                    if (gs[e2] < 0 || abs(tqq - gs[e2]) <= a.band) s[4 * g4 + e2] = -INFINITY;
             }
-            if (MASK == MASK_TOKEN && kind >= 0 && j >= a.nb) {
-                // gathered global keys: padding (-1) and keys the band already covers drop out
-                const int* gt = gtok_s + (j - a.nb) * 64;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int4 gv = *(const int4*)(gt + 32 * kb + 8 * g4 + 4 * hh);
-                        const int gs[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (gs[e] < 0 || abs(tq[qb] - gs[e]) <= a.band) s[kb][qb][4 * g4 + e] = -INFINITY;
-                    }
-            }
-            if (first) m[qb] = tile_max(s, qb);
         }
     };
-    // Probabilities of half qb, key chunks c0 and c0 + 1.  The running max is
-    // raised only when a lane's probabilities would sum past kSumCap (or a
-    // -inf max meets a finite score): then O and l are rescaled to the tile's
-    // max and the chunk pair is redone.
-    auto softmax_exp = [&](const f32x16_t (&s)[2][2], int qb, auto c0, u32x4_t (&u)[2]) {
-        constexpr int C0 = decltype(c0)::value;
+    // S^T block (kb, qb) = K[32kb ..] Q[32qb ..]^T: register i <-> key 32kb + 8(i/4) + 4hh + i%4.
+    auto sblk = [&](const bf16x8_t (&kfb)[NC], const bf16x8_t (&qfb)[NC], f32x16_t& s) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfb[c], qfb[c], s, 0, 0, 0);
+    };
+    // Probabilities of one score block of half qb (key chunks 2kb, 2kb + 1).
+    // On a unit's first tile the running max starts at the block's max.  It is
+    // raised only when a lane's 16 probabilities would sum past kSumCap (or a
+    // -inf max meets a finite score): then O and l are rescaled to the block's
+    // max and the block is redone.  `issue` places NM matrix products (scores
+    // of later blocks, PV products of earlier ones) in the same scheduling
+    // region, and the group barriers alternate them with the exp/pack work, so
+    // the wave keeps its matrix core busy during its own softmax.
+    auto softmax_blk = [&](const f32x16_t& s, int qb, bool first, u32x4_t (&u)[2], auto&& issue, auto nm) {
+        constexpr int NM = decltype(nm)::value;
+        if (first) m[qb] = blk_max(s);
         float lsum;
         auto chunks = [&]() {
             const float muse = m[qb] == -INFINITY ? 0.f : m[qb];
@@ -1104,18 +1094,23 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             for (int k = 0; k < 2; ++k)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int c = C0 + k;
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][qb][8 * (c % 2) + 2 * e], c2, -muse));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[c / 2][qb][8 * (c % 2) + 2 * e + 1], c2, -muse));
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * k + 2 * e], c2, -muse));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * k + 2 * e + 1], c2, -muse));
                     u[k][e] = pack_bf16x2(p0, p1);
                     acc[4 * k + e] = p0 + p1;
                 }
             lsum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
         };
+        issue();
         chunks();
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 56 / NM, 0);   // then a share of the VALU work
+        }
         const bool bad = lsum > kSumCap || (m[qb] == -INFINITY && lsum > 0.f);
         if (__ballot(bad) != 0) {          // wave-uniform, rare
-            const float mx = tile_max(s, qb);
+            const float mx = blk_max(s);
             const bool raise = mx > m[qb];
             const float alpha = raise ? __builtin_amdgcn_exp2f(m[qb] - mx) : 1.f;
             l[qb] *= alpha;
@@ -1174,10 +1169,13 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
     using C0 = std::integral_constant<int, 0>;
     using C2 = std::integral_constant<int, 2>;
+    // The next list entry and the partner's count are read from LDS one step
+    // ahead (pf_e, pf_left), so the step never waits on them.
+    int e1 = F > 1 ? __builtin_amdgcn_readfirstlane(flat[1]) : 0;
+    int pf_e = 0, pf_left = F;
     for (int f = 0; f < F; ++f) {
-        const int e1 = f + 1 < F ? __builtin_amdgcn_readfirstlane(flat[f + 1]) : 0;
         if (lane == 0) left[wv] = F - f;
-        const int partner_left = partner >= 0 ? __builtin_amdgcn_readfirstlane(left[partner]) : 0;
+        const int partner_left = __builtin_amdgcn_readfirstlane(pf_left);
         if ((e0 & kTileFirst) && f > 0) {   // a new unit (its Q was loaded during the last step)
             u_cur = tile_unit(e0);
             kind_cur = rd(u_kind, u_cur);
@@ -1191,18 +1189,17 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         asm volatile("" ::: "memory");
         bf16x8_t kf[2][NC];
         kread(kbuf, kf);
-        f32x16_t sc[2][2];
-        smma(kf, qf, sc);
-        // On a unit's last tile Q is free once the products are issued: load
-        // the next unit's, so that its latency hides behind this step.
-        if ((e0 & kTileLast) && f + 1 < F) {
-            const int un = tile_unit(e1);
-            load_q(rd(u_kind, un), rd(u_g, un), qf, tq_next);
-        }
         bf16x8_t va[4][NDB];
         vread(vbuf, va);
+        // Step order: the scores of block (0, 0) first; each later region pairs
+        // the softmax of one block with the products that do not depend on it:
+        //   S01 S10 | P00;  S11 PV(P00) | P01;  PV(P01) | P10;  PV(P10) | P11;  PV(P11).
+        f32x16_t s00, s01, s10, s11;
+        sblk(kf[0], qf[0], s00);
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): every fragment read returned
         asm volatile("" ::: "memory");
+        pf_e = f + 2 < F ? flat[f + 2] : 0;
+        pf_left = partner >= 0 ? left[partner] : F - f;
         // behind the partner wave: issue first until caught up
         if (F - f > partner_left) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
@@ -1219,27 +1216,36 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             finish();
             pend = false;
         }
-        softmax_prep(e0, kind_cur, tq_cur, valid_cur, sc, (e0 & kTileFirst) != 0);
+        const bool first = (e0 & kTileFirst) != 0;
+        using I4 = std::integral_constant<int, 4>;
+        using I8 = std::integral_constant<int, 8>;
         u32x4_t p0[2], p1[2], p2[2], p3[2];
-        softmax_exp(sc, 0, C0(), p0);
+        mask_blk(e0, kind_cur, tq_cur[0], valid_cur, s00, 0, 0);
+        softmax_blk(s00, 0, first, p0, [&]() { sblk(kf[0], qf[1], s01); sblk(kf[1], qf[0], s10); }, I8());
         if (more) {
             if (STRIDED) lds_load16x4_rows(kdo, (const char*)(kn + 32 * RS), (uint32_t)(RS * 2), kl + 4096 + 2048);
             else lds_load16x4_1k(kdo, kn + 32 * 64, kl + 4096 + 2048);
         }
-        softmax_exp(sc, 1, C0(), p1);
-        pv(va, 0, C0(), p0);
+        mask_blk(e0, kind_cur, tq_cur[1], valid_cur, s01, 0, 1);
+        softmax_blk(s01, 1, first, p1, [&]() { sblk(kf[1], qf[1], s11); pv(va, 0, C0(), p0); }, I8());
+        // On a unit's last tile Q is free once every score product is issued:
+        // load the next unit's, so that its latency hides behind this step.
+        if ((e0 & kTileLast) && f + 1 < F) {
+            const int un = tile_unit(e1);
+            load_q(rd(u_kind, un), rd(u_g, un), qf, tq_next);
+        }
         if (more) {
             if (STRIDED) lds_load16x4_rows(vdo, (const char*)vn, (uint32_t)(RS * 2), vl + 2048);
             else lds_load16x4_1k(vdo, vn, vl + 2048);
         }
-        softmax_exp(sc, 0, C2(), p2);
-        pv(va, 1, C0(), p1);
+        mask_blk(e0, kind_cur, tq_cur[0], valid_cur, s10, 1, 0);
+        softmax_blk(s10, 0, false, p2, [&]() { pv(va, 1, C0(), p1); }, I4());
         if (more) {
             if (STRIDED) lds_load16x4_rows(vdo, (const char*)(vn + 32 * RS), (uint32_t)(RS * 2), vl + 4096 + 2048);
             else lds_load16x4_1k(vdo, vn + 32 * 64, vl + 4096 + 2048);
         }
-        softmax_exp(sc, 1, C2(), p3);
-        pv(va, 0, C2(), p2);
+        mask_blk(e0, kind_cur, tq_cur[1], valid_cur, s11, 1, 1);
+        softmax_blk(s11, 1, false, p3, [&]() { pv(va, 0, C2(), p2); }, I4());
         pv(va, 1, C2(), p3);
         if (e0 & kTileLast) {               // finished once the next tile's loads are out
             pend = true;
@@ -1249,6 +1255,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             p_tq[1] = tq_cur[1];
         }
         e0 = e1;
+        e1 = __builtin_amdgcn_readfirstlane(pf_e);
     }
     if (pend) finish();
     if (lane == 0) left[wv] = 0;
