@@ -97,6 +97,22 @@ def tile_stats(wl, row_ptr, col, valid_len=None):
     return total
 
 
+def token_extra_pairs(bs, lay, wl):
+    """(query, key) pairs of one batch entry that the token kernels add: every non-global
+    row's global keys outside its band, and its random tokens."""
+    import numpy as np
+    g, links = bs.bsattn_layout_token_links(lay)
+    g = np.asarray(g, dtype=np.int64)
+    t = np.arange(wl.seq_len)
+    nonglobal = ~np.isin(t, g)
+    inside = np.searchsorted(g, t + wl.band_tokens, side="right") - np.searchsorted(g, t - wl.band_tokens, side="left")
+    per_row = (len(g) - inside) * nonglobal
+    total = int(per_row.sum()) * wl.heads
+    if links is not None and links.size:
+        total += int(((links >= 0) & nonglobal[None, :, None]).sum())
+    return total
+
+
 def traffic_from_profile(workload: str, kernel: str, source: str = KERNEL_SOURCE):
     """HBM bytes per launch of the main kernel from the committed counter summary, or None
     when the summary is missing or the kernel source changed since the counters were taken."""
@@ -297,9 +313,8 @@ def main():
     wl = WORKLOADS[args.workload or THROUGHPUT_WORKLOAD]
     inp = make_inputs(wl)
 
-    if ((wl.adaptive or wl.routed or wl.topr) and args.which != "forward") or (wl.token and args.which == "backward"):
-        print("adaptive, routed and top-keep workloads are timed in the forward only, token-pattern workloads "
-              "in the forward and the layer", file=sys.stderr)
+    if (wl.adaptive or wl.routed or wl.topr) and args.which != "forward":
+        print("adaptive, routed and top-keep workloads are timed in the forward only", file=sys.stderr)
         sys.exit(2)
     t0 = time.perf_counter()
     if wl.band or wl.routed:
@@ -384,8 +399,15 @@ def main():
         # algorithmic work: the five products of a backward that recomputes P
         # (S, dP, dV, dK, dQ), 2 * 64 * 64 * D flop each per tile; the dK/dV
         # kernel does the first four of them
-        flops_per_step = tiles * 10.0 * 64 * 64 * wl.head_dim
-        kernel_flops = tiles * 8.0 * 64 * 64 * wl.head_dim
+        bwd_tiles, extra_pairs = tiles, 0
+        if wl.token:
+            # the block passes walk the band tiles and the global rows' tiles; each
+            # non-global row's global keys outside its band and its random tokens
+            # are pairs of the token kernels (the same five products, 10 D flop a pair)
+            bwd_tiles = tiles - wl.batch * (len(row_ptr) - 1) * (-(-wl.num_global // 64))   # less the gathered tiles
+            extra_pairs = wl.batch * token_extra_pairs(bs, lay, wl)
+        flops_per_step = bwd_tiles * 10.0 * 64 * 64 * wl.head_dim + extra_pairs * 10.0 * wl.head_dim
+        kernel_flops = bwd_tiles * 8.0 * 64 * 64 * wl.head_dim
         alg_bytes = wl.batch * wl.heads * wl.seq_len * (8 * wl.head_dim * elem + 4)
 
         def step(i):

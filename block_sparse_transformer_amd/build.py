@@ -31,6 +31,7 @@ SOURCES = [
     "kernels/adaptive.hip",
     "kernels/noalloc.hip",
     "kernels/topr.hip",
+    "kernels/bwd_token.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

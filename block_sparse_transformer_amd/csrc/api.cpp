@@ -105,6 +105,13 @@ void build_schedule(bsattn_layout* lay) {
     lay->n_slots = slot;
 }
 
+// End of the tiles of CSR row r that the backward's block passes walk: a
+// token layout's rows end with its n_gt gathered tiles of global keys, whose
+// pairs the token kernels take instead; the band tiles come first.
+int32_t bwd_row_end(const bsattn_layout* lay, int32_t r) {
+    return lay->row_ptr[(size_t)r + 1] - (lay->kind == 2 ? lay->n_gt : 0);
+}
+
 // Backward work lists.  dQ: every query block against the key blocks of its
 // row; dK/dV: every key block against the query blocks whose rows hold it
 // (the layout transposed, per head).  Lists longer than kChunkTiles are
@@ -119,7 +126,7 @@ void build_bwd(bsattn_layout* lay) {
     for (int32_t h = 0; h < H; ++h)
         for (int32_t i = 0; i < nb; ++i) {
             const int32_t r = h * nb + i;
-            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a) ++cptr[(size_t)h * nb + lay->col_idx[a] + 1];
+            for (int32_t a = lay->row_ptr[r]; a < bwd_row_end(lay, r); ++a) ++cptr[(size_t)h * nb + lay->col_idx[a] + 1];
         }
     for (size_t c = 0; c + 1 < cptr.size(); ++c) cptr[c + 1] += cptr[c];
     bw.k_idx.assign((size_t)cptr.back(), 0);
@@ -129,20 +136,21 @@ void build_bwd(bsattn_layout* lay) {
     for (int32_t h = 0; h < H; ++h)
         for (int32_t i = 0; i < nb; ++i) {
             const int32_t r = h * nb + i;
-            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a) {
+            for (int32_t a = lay->row_ptr[r]; a < bwd_row_end(lay, r); ++a) {
                 const int32_t pos = fill[(size_t)h * nb + lay->col_idx[a]]++;
                 bw.k_idx[(size_t)pos] = i;
                 if (subs) bw.k_sub[(size_t)pos] = lay->tile_sub[(size_t)a];   // same bits: query half, key half
             }
         }
     // per head, longest first, padded with empty items (head_blk -1) to a common length
-    auto make = [&](const std::vector<int32_t>& ptr, std::vector<BwdItem>& items, std::vector<BwdSum>& sums,
+    // list hb is [begin(hb), end(hb)) of its index array
+    auto make = [&](auto begin, auto end, std::vector<BwdItem>& items, std::vector<BwdSum>& sums,
                     int32_t& n_slots, int32_t& per_head) {
         n_slots = 0;
         std::vector<std::vector<BwdItem>> heads((size_t)H);
         for (int32_t hb = 0; hb < H * nb; ++hb) {
             auto& hi = heads[(size_t)(hb / nb)];
-            const int32_t b0 = ptr[(size_t)hb], b1 = ptr[(size_t)hb + 1];
+            const int32_t b0 = begin(hb), b1 = end(hb);
             const int32_t len = b1 - b0;
             if (len <= kChunkTiles) {
                 hi.push_back({hb, b0, b1, -1});
@@ -167,8 +175,10 @@ void build_bwd(bsattn_layout* lay) {
             for (size_t a = hi.size(); a < (size_t)per_head; ++a) items.push_back({-1, 0, 0, -1});
         }
     };
-    make(lay->row_ptr, bw.q_items, bw.q_sums, bw.n_qslots, bw.q_per_head);
-    make(cptr, bw.k_items, bw.k_sums, bw.n_kslots, bw.k_per_head);
+    make([&](int32_t hb) { return lay->row_ptr[(size_t)hb]; }, [&](int32_t hb) { return bwd_row_end(lay, hb); },
+         bw.q_items, bw.q_sums, bw.n_qslots, bw.q_per_head);
+    make([&](int32_t hb) { return cptr[(size_t)hb]; }, [&](int32_t hb) { return cptr[(size_t)hb + 1]; }, bw.k_items,
+         bw.k_sums, bw.n_kslots, bw.k_per_head);
     bw.built = true;
 }
 
@@ -185,14 +195,20 @@ void free_bwd_device(bsattn_layout* lay) {
     bw.d_k_idx = nullptr;
     bw.d_k_sub = nullptr;
     bw.uploaded = false;
+    // the routed lists' host copies stay (a token layout's are built with it)
     for (auto& rb : lay->rbwd) {
         (void)hipFree(rb.d_rq_items);
         (void)hipFree(rb.d_k_items);
         (void)hipFree(rb.d_rq_sums);
         (void)hipFree(rb.d_k_sums);
         (void)hipFree(rb.d_k_idx);
+        rb.d_rq_items = rb.d_k_items = nullptr;
+        rb.d_rq_sums = rb.d_k_sums = nullptr;
+        rb.d_k_idx = nullptr;
     }
-    lay->rbwd.clear();
+    (void)hipFree(lay->d_tlink_ptr);
+    (void)hipFree(lay->d_tlink_rows);
+    lay->d_tlink_ptr = lay->d_tlink_rows = nullptr;
 }
 
 void free_device(bsattn_layout* lay) {
@@ -241,10 +257,13 @@ bsattn_status check_layout_dims(int32_t H, int32_t L, int32_t block, bool any_bl
     return BSATTN_OK;
 }
 
+void build_token_bwd(bsattn_layout* lay);
+
 bsattn_status finish_layout(bsattn_layout* lay) {
     try {
         build_schedule(lay);
-        if (lay->kind < 2) build_bwd(lay);   // token and adaptive layouts have no backward
+        if (lay->kind <= 2) build_bwd(lay);   // adaptive and top-keep layouts have no backward
+        if (lay->kind == 2) build_token_bwd(lay);
     } catch (const std::bad_alloc&) {
         return fail(BSATTN_ERR_NO_MEMORY, "work list allocation failed");
     }
@@ -272,6 +291,24 @@ bsattn_status upload_bwd(const bsattn_layout* lay, hipStream_t stream) {
         for (int a = 0; a < 6; ++a) (void)hipFree(p[a]);
         return fail(BSATTN_ERR_NO_MEMORY, "backward list upload: %s", hipGetErrorString(e));
     }
+    if (lay->kind == 2) {   // token layouts: the transposed random-token lists
+        void* tp = nullptr;
+        void* tr = nullptr;
+        const size_t np = lay->tlink_ptr.size() * sizeof(int32_t), nr = lay->tlink_rows.size() * sizeof(int32_t);
+        e = hipMalloc(&tp, np);
+        if (e == hipSuccess) e = hipMalloc(&tr, nr);
+        if (e == hipSuccess) e = hipMemcpyAsync(tp, lay->tlink_ptr.data(), np, hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipMemcpyAsync(tr, lay->tlink_rows.data(), nr, hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) {
+            (void)hipFree(tp);
+            (void)hipFree(tr);
+            for (int a = 0; a < 6; ++a) (void)hipFree(p[a]);
+            return fail(BSATTN_ERR_NO_MEMORY, "token backward list upload: %s", hipGetErrorString(e));
+        }
+        lay->d_tlink_ptr = (int32_t*)tp;
+        lay->d_tlink_rows = (int32_t*)tr;
+    }
     bw.d_q_items = (BwdItem*)p[0];
     bw.d_k_items = (BwdItem*)p[1];
     bw.d_q_sums = (BwdSum*)p[2];
@@ -283,8 +320,9 @@ bsattn_status upload_bwd(const bsattn_layout* lay, hipStream_t stream) {
 }
 
 // Backward lists of a routed call with n_rt routed tiles per (b, h) on a band
-// layout.  dQ: the band rows' items are the layout's own (lay->bwd); each
-// routed tile r of head h adds r_chunks items over key blocks [c per, (c + 1)
+// layout (or on a token layout's band, its global rows as the routed tiles).
+// dQ: the band rows' items are the layout's own (lay->bwd); each routed tile
+// r of head h adds r_chunks items over key blocks [c per, (c + 1)
 // per), all written as partials after the band rows' slots, and one gathered
 // sum.  dK/dV: every column lists the band's query blocks, then the routed
 // tiles as entries nb + r; columns longer than kChunkTiles are split.  Per
@@ -310,7 +348,7 @@ bsattn_layout::RoutedBwd build_routed_bwd(const bsattn_layout* lay, int32_t n_rt
     for (int32_t h = 0; h < H; ++h)
         for (int32_t i = 0; i < nb; ++i) {
             const int32_t r = h * nb + i;
-            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a) ++cptr[(size_t)h * nb + lay->col_idx[a] + 1];
+            for (int32_t a = lay->row_ptr[r]; a < bwd_row_end(lay, r); ++a) ++cptr[(size_t)h * nb + lay->col_idx[a] + 1];
         }
     for (size_t c = 1; c < cptr.size(); ++c) cptr[c] += n_rt;
     for (size_t c = 0; c + 1 < cptr.size(); ++c) cptr[c + 1] += cptr[c];
@@ -319,7 +357,7 @@ bsattn_layout::RoutedBwd build_routed_bwd(const bsattn_layout* lay, int32_t n_rt
     for (int32_t h = 0; h < H; ++h)
         for (int32_t i = 0; i < nb; ++i) {
             const int32_t r = h * nb + i;
-            for (int32_t a = lay->row_ptr[r]; a < lay->row_ptr[r + 1]; ++a)
+            for (int32_t a = lay->row_ptr[r]; a < bwd_row_end(lay, r); ++a)
                 rb.k_idx[(size_t)fill[(size_t)h * nb + lay->col_idx[a]]++] = i;
         }
     for (size_t c = 0; c + 1 < cptr.size(); ++c)
@@ -354,21 +392,63 @@ bsattn_layout::RoutedBwd build_routed_bwd(const bsattn_layout* lay, int32_t n_rt
     return rb;
 }
 
+// Token layouts, backward: the global rows' routed lists (built with the
+// layout, so that the workspace size is known before any device work), and
+// for each (head, key s) the non-global rows whose random tokens hold s.
+void build_token_bwd(bsattn_layout* lay) {
+    const int32_t H = lay->H, L = lay->L, nl = lay->n_links;
+    if (!lay->tok_g.empty()) lay->rbwd.push_back(build_routed_bwd(lay, lay->n_gt));
+    lay->tlink_ptr.assign((size_t)H * (L + 1), 0);
+    for (int32_t h = 0; h < H; ++h) {
+        int32_t* ptr = lay->tlink_ptr.data() + (size_t)h * (L + 1);
+        for (int32_t t = 0; t < L; ++t) {
+            if (lay->tok_flag[(size_t)t]) continue;
+            const int32_t* lk = lay->links.data() + ((size_t)h * L + t) * nl;
+            for (int32_t j = 0; j < nl; ++j)
+                if (lk[j] >= 0) ++ptr[lk[j] + 1];
+        }
+        for (int32_t s2 = 0; s2 < L; ++s2) ptr[s2 + 1] += ptr[s2];
+    }
+    // rows of head h are placed after those of heads < h
+    size_t total = 0;
+    for (int32_t h = 0; h < H; ++h) {
+        int32_t* ptr = lay->tlink_ptr.data() + (size_t)h * (L + 1);
+        const int32_t n = ptr[L];
+        for (int32_t s2 = 0; s2 <= L; ++s2) ptr[s2] += (int32_t)total;
+        total += (size_t)n;
+    }
+    lay->tlink_rows.assign(std::max<size_t>(total, 1), 0);
+    std::vector<int32_t> fill(lay->tlink_ptr.size());
+    std::copy(lay->tlink_ptr.begin(), lay->tlink_ptr.end(), fill.begin());
+    for (int32_t h = 0; h < H; ++h)
+        for (int32_t t = 0; t < L; ++t) {   // ascending t: each key's rows come out ascending
+            if (lay->tok_flag[(size_t)t]) continue;
+            const int32_t* lk = lay->links.data() + ((size_t)h * L + t) * nl;
+            for (int32_t j = 0; j < nl; ++j)
+                if (lk[j] >= 0) lay->tlink_rows[(size_t)fill[(size_t)h * (L + 1) + lk[j]]++] = t;
+        }
+}
+
 // The routed lists for n_rt tiles, built and uploaded on first use (caller holds sched_mu).
 bsattn_status get_routed_bwd(const bsattn_layout* lay, int32_t n_rt, hipStream_t stream,
                              const bsattn_layout::RoutedBwd** out) {
-    for (const auto& rb : lay->rbwd)
-        if (rb.n_rt == n_rt) {
-            *out = &rb;
-            return BSATTN_OK;
-        }
-    if (g_no_build) return fail(BSATTN_ERR_STATE, "routed backward lists were not prepared with bsattn_prepare");
-    bsattn_layout::RoutedBwd rb;
-    try {
-        rb = build_routed_bwd(lay, n_rt);
-    } catch (const std::bad_alloc&) {
-        return fail(BSATTN_ERR_NO_MEMORY, "routed backward list allocation failed");
+    bsattn_layout::RoutedBwd* found = nullptr;
+    for (auto& rb : lay->rbwd)
+        if (rb.n_rt == n_rt) found = &rb;
+    if (found && found->d_rq_items) {
+        *out = found;
+        return BSATTN_OK;
     }
+    if (g_no_build) return fail(BSATTN_ERR_STATE, "routed backward lists were not prepared with bsattn_prepare");
+    bsattn_layout::RoutedBwd built;
+    if (!found) {
+        try {
+            built = build_routed_bwd(lay, n_rt);
+        } catch (const std::bad_alloc&) {
+            return fail(BSATTN_ERR_NO_MEMORY, "routed backward list allocation failed");
+        }
+    }
+    bsattn_layout::RoutedBwd& rb = found ? *found : built;   // host lists (a token layout builds them up front)
     void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
     const void* src[5] = {rb.rq_items.data(), rb.k_items.data(), rb.rq_sums.data(), rb.k_sums.data(),
                           rb.k_idx.data()};
@@ -390,6 +470,10 @@ bsattn_status get_routed_bwd(const bsattn_layout* lay, int32_t n_rt, hipStream_t
     rb.d_rq_sums = (BwdSum*)p[2];
     rb.d_k_sums = (BwdSum*)p[3];
     rb.d_k_idx = (int32_t*)p[4];
+    if (found) {
+        *out = found;
+        return BSATTN_OK;
+    }
     lay->rbwd.push_back(std::move(rb));
     *out = &lay->rbwd.back();
     return BSATTN_OK;
@@ -420,6 +504,38 @@ void bwd_workspace_parts(const bsattn_layout* lay, int32_t B, int32_t D, size_t*
     *off_dk = delta + qs;
     *off_dv = delta + qs + ks;
     *total = delta + qs + 2 * ks;
+}
+
+// Workspace of the token-layout backward: the routed call's parts (delta, dQ,
+// dK and dV slots; the global rows are the routed tiles), then the global
+// keys' dK/dV chunk partials.  Row chunks per global key: enough workgroups
+// (each takes tok_global_keys_per_wg keys) to fill the chip, at least 256
+// rows each.
+struct TokenBwdWs {
+    size_t off_dq = 0, off_dk = 0, off_dv = 0, off_g = 0, total = 0;
+    int32_t g_chunks = 0;
+    int32_t n_qslots = 0, n_kslots = 0;
+};
+TokenBwdWs token_bwd_workspace(const bsattn_layout* lay, int32_t B, int32_t D) {
+    TokenBwdWs w;
+    const int32_t ng = (int32_t)lay->tok_g.size();
+    w.n_qslots = lay->bwd.n_qslots;
+    w.n_kslots = lay->bwd.n_kslots;
+    for (const auto& rb : lay->rbwd)
+        if (ng > 0 && rb.n_rt == lay->n_gt) {
+            w.n_qslots = rb.n_qslots;
+            w.n_kslots = rb.n_kslots;
+        }
+    routed_bwd_workspace_parts(lay, B, D, w.n_qslots, w.n_kslots, &w.off_dq, &w.off_dk, &w.off_dv, &w.total);
+    if (ng > 0) {
+        const int64_t keys = (int64_t)B * lay->H * ng;
+        const int gk = tok_global_keys_per_wg(D);
+        const int64_t wgs = (int64_t)B * lay->H * ((ng + gk - 1) / gk);
+        w.g_chunks = (int32_t)std::max<int64_t>(1, std::min<int64_t>(lay->L / 256, (2048 + wgs - 1) / wgs));
+        w.off_g = w.total;
+        w.total += align256((size_t)keys * w.g_chunks * 2 * D * sizeof(float));
+    }
+    return w;
 }
 
 // Shape/pointer checks shared by both forward entry points.
@@ -1073,6 +1189,106 @@ bsattn_status topr_run(const bsattn_layout* lay, int32_t B, int32_t D, const voi
     return ok();
 }
 
+// Backward over a token layout (bf16).  The band and the global rows run
+// through the block passes as a routed call whose routed tiles are the global
+// rows, one list shared by every (batch, head) group:
+//   1. dQ of every row over its band tiles, and delta;
+//   2. dQ of the global rows over every key block, summed into their rows;
+//   3. dK and dV over the band's query blocks and the global rows' tiles
+//      (outside the band);
+//   4. the token kernels: each non-global row's global keys outside its band
+//      and its random tokens, added to dQ, dK and dV.
+bsattn_status token_backward(const bsattn_layout* lay, int32_t B, int32_t H, int32_t L, int32_t D, const void* q,
+                             const void* k, const void* v, const void* out, const float* lse, const void* dout,
+                             void* dq, void* dk, void* dv, float scale, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    const TokenBwdWs w = token_bwd_workspace(lay, B, D);
+    if (!workspace || workspace_bytes < w.total)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", w.total, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(BSATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const int32_t ng = (int32_t)lay->tok_g.size();
+    const auto& bw = lay->bwd;
+    BwdItem *rq_items = nullptr, *k_items = bw.d_k_items;
+    BwdSum *rq_sums = nullptr, *k_sums = bw.d_k_sums;
+    int32_t* k_idx = bw.d_k_idx;
+    int32_t n_rq_items = 0, n_rq_sums = 0, rq_per_head = 0;
+    int32_t n_k_items = (int32_t)bw.k_items.size(), n_k_sums = (int32_t)bw.k_sums.size(), k_per_head = bw.k_per_head;
+    {
+        std::lock_guard<std::mutex> guard(*lay->sched_mu);
+        bsattn_status st = upload_bwd(lay, stream);
+        if (st != BSATTN_OK) return st;
+        k_items = bw.d_k_items; k_sums = bw.d_k_sums; k_idx = bw.d_k_idx;
+        if (ng > 0) {
+            const bsattn_layout::RoutedBwd* rb = nullptr;
+            st = get_routed_bwd(lay, lay->n_gt, stream, &rb);
+            if (st != BSATTN_OK) return st;
+            rq_items = rb->d_rq_items; rq_sums = rb->d_rq_sums;
+            n_rq_items = (int32_t)rb->rq_items.size(); n_rq_sums = (int32_t)rb->rq_sums.size();
+            rq_per_head = rb->rq_per_head;
+            k_items = rb->d_k_items; k_sums = rb->d_k_sums; k_idx = rb->d_k_idx;
+            n_k_items = (int32_t)rb->k_items.size(); n_k_sums = (int32_t)rb->k_sums.size();
+            k_per_head = rb->k_per_head;
+        }
+    }
+    if (((int64_t)B * H + kXcds) * std::max(std::max(bw.q_per_head, rq_per_head), std::max(k_per_head, L / 32)) >=
+        ((int64_t)1 << 31))
+        return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+    BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    char* ws = (char*)workspace;
+    a.delta = (float*)ws;
+    a.ws_dq = (float*)(ws + w.off_dq);
+    a.ws_dk = (float*)(ws + w.off_dk);
+    a.ws_dv = (float*)(ws + w.off_dv);
+    a.valid_len = nullptr;
+    a.B = B; a.H = H; a.L = L; a.nb = lay->nb;
+    a.band = lay->band_tokens;
+    a.routed_rows = lay->d_gtok;
+    a.n_routed = ng;
+    a.routed_stride = 0;   // one list of global rows for every (batch, head)
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.gtok = lay->d_gtok;
+    a.n_g = ng;
+    a.tok_global = lay->d_tok_flag;
+    a.links = lay->d_links;
+    a.n_links = lay->n_links;
+    a.tptr = lay->d_tlink_ptr;
+    a.trows = lay->d_tlink_rows;
+    a.ws_g = ng > 0 ? (float*)(ws + w.off_g) : nullptr;
+    a.g_chunks = w.g_chunks;
+    hipError_t e;
+    // 1. dQ of every row over its band (the global rows are redone below), and delta
+    a.items = bw.d_q_items; a.n_items = (int32_t)bw.q_items.size(); a.items_per_head = bw.q_per_head;
+    a.sums = bw.d_q_sums; a.n_sums = (int32_t)bw.q_sums.size();
+    a.idx = lay->d_col_idx; a.idx_sub = nullptr; a.n_slots = w.n_qslots;
+    if ((e = launch_bwd_dq(a, D, MASK_BAND, stream)) != hipSuccess) return hip_fail(e, "backward dQ launch");
+    if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 0, stream)) != hipSuccess)
+        return hip_fail(e, "backward dQ sum launch");
+    // 2. dQ of the global rows over every key block, as partials, summed into their rows
+    if (ng > 0) {
+        a.items = rq_items; a.n_items = n_rq_items; a.items_per_head = rq_per_head;
+        a.sums = rq_sums; a.n_sums = n_rq_sums;
+        a.idx = nullptr;
+        if ((e = launch_bwd_dq(a, D, MASK_ROUTED_Q, stream)) != hipSuccess) return hip_fail(e, "global-row dQ launch");
+        if ((e = launch_bwd_routed_sum(a, D, stream)) != hipSuccess) return hip_fail(e, "global-row dQ sum launch");
+    }
+    // 3. dK and dV over the band's query blocks (and the global rows' tiles)
+    a.items = k_items; a.n_items = n_k_items; a.items_per_head = k_per_head;
+    a.sums = k_sums; a.n_sums = n_k_sums;
+    a.idx = k_idx; a.n_slots = w.n_kslots;
+    if ((e = launch_bwd_dkdv(a, D, ng > 0 ? MASK_BAND_ROUTED : MASK_BAND, stream, g_ev_before, g_ev_after)) !=
+        hipSuccess)
+        return hip_fail(e, "token dK/dV launch");
+    if (a.n_sums > 0 && (e = launch_bwd_sum(a, D, 1, stream)) != hipSuccess)
+        return hip_fail(e, "token dK/dV sum launch");
+    // 4. the global keys outside each row's band and the random tokens
+    if ((e = launch_tok_bwd_extra(a, D, stream)) != hipSuccess) return hip_fail(e, "token backward launch");
+    return ok();
+}
+
 }  // namespace
 
 namespace bsattn {
@@ -1599,8 +1815,8 @@ bsattn_status bsattn_prepare(const bsattn_layout* lay, int32_t batch, int32_t he
         return fail(BSATTN_ERR_INVALID_ARG, "num_routed must be in [0, seq_len] (got %d)", num_routed);
     if (num_routed > 0 && lay->kind != 1)
         return fail(BSATTN_ERR_INVALID_ARG, "num_routed > 0 needs a band layout");
-    if (backward && lay->kind != 0 && lay->kind != 1)
-        return fail(BSATTN_ERR_UNSUPPORTED, "the backward takes window/global/random and band layouts");
+    if (backward && lay->kind != 0 && lay->kind != 1 && lay->kind != 2)
+        return fail(BSATTN_ERR_UNSUPPORTED, "the backward takes window/global/random, band and token layouts");
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -1626,9 +1842,10 @@ bsattn_status bsattn_prepare(const bsattn_layout* lay, int32_t batch, int32_t he
         std::lock_guard<std::mutex> guard(*lay->sched_mu);
         st = upload_bwd(lay, stream);
         if (st != BSATTN_OK) return st;
-        if (num_routed > 0) {   // the routed backward's lists
+        if (num_routed > 0 || (lay->kind == 2 && !lay->tok_g.empty())) {   // the routed (global-row) lists
             const bsattn_layout::RoutedBwd* rb = nullptr;
-            st = get_routed_bwd(lay, (num_routed + kBlock - 1) / kBlock, stream, &rb);
+            const int32_t n_rt = lay->kind == 2 ? lay->n_gt : (num_routed + kBlock - 1) / kBlock;
+            st = get_routed_bwd(lay, n_rt, stream, &rb);
             if (st != BSATTN_OK) return st;
         }
     }
@@ -1826,10 +2043,15 @@ bsattn_status bsattn_backward_workspace_size(const bsattn_layout* lay, int32_t b
     if (!lay || !bytes) return fail(BSATTN_ERR_INVALID_ARG, "NULL argument");
     if (batch < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch must be >= 1");
     if (head_dim != 64 && head_dim != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (lay->kind == 2) {
+        *bytes = token_bwd_workspace(lay, batch, head_dim).total;
+        return ok();
+    }
     size_t a, b, c;
     bwd_workspace_parts(lay, batch, head_dim, &a, &b, &c, bytes);
     return ok();
 }
+
 
 bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int32_t B, int32_t H,
                               int32_t L, int32_t D, const void* q, const void* k, const void* v,
@@ -1837,11 +2059,12 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
                               void* dv, const int32_t* key_valid_len, float scale, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
     if (!lay) return fail(BSATTN_ERR_INVALID_ARG, "layout is NULL");
-    if (lay->kind != 0 && lay->kind != 1)
-        return fail(BSATTN_ERR_UNSUPPORTED, "the backward takes window/global/random and band layouts");
+    if (lay->kind != 0 && lay->kind != 1 && lay->kind != 2)
+        return fail(BSATTN_ERR_UNSUPPORTED, "the backward takes window/global/random, band and token layouts");
     if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "the backward is bf16 only");
     const bool band = lay->kind == 1;
     if (band && key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "band layouts take no key padding");
+    if (lay->kind == 2 && key_valid_len) return fail(BSATTN_ERR_UNSUPPORTED, "token layouts take no key padding");
     if (!dout || !dq || !dk || !dv) return fail(BSATTN_ERR_INVALID_ARG, "NULL gradient pointer");
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return fail(BSATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
@@ -1858,6 +2081,9 @@ bsattn_status bsattn_backward(const bsattn_layout* lay, bsattn_dtype dtype, int3
     bsattn_status st = check_forward_common(lay, B, H, L, D, q, k, v, const_cast<void*>(out),
                                             const_cast<float*>(lse), scale);
     if (st != BSATTN_OK) return st;
+    if (lay->kind == 2)
+        return token_backward(lay, B, H, L, D, q, k, v, out, lse, dout, dq, dk, dv, scale, workspace, workspace_bytes,
+                              stream);
     size_t off_dq, off_dk, off_dv, need;
     bwd_workspace_parts(lay, B, D, &off_dq, &off_dk, &off_dv, &need);
     if (!workspace || workspace_bytes < need)
@@ -2007,6 +2233,7 @@ bsattn_status bsattn_backward_routed(const bsattn_layout* lay, bsattn_dtype dtyp
     a.band = lay->band_tokens;
     a.routed_rows = routed_rows;
     a.n_routed = num_routed;
+    a.routed_stride = num_routed;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
     hipError_t e;

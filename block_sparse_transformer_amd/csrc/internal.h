@@ -184,11 +184,27 @@ struct BwdArgs {
     const int32_t* valid_len; // [B] or null
     int32_t B, H, L, nb, n_slots;
     int32_t band;             // band layouts: |t - s| <= band (MASK_BAND)
-    // routed variant: routed_rows [B*H][n_routed]; routed tile r holds rows r*64 .. r*64 + 63
+    // routed variant: routed tile r holds rows routed_rows[grp * routed_stride
+    // + r*64 ..] (routed_stride = n_routed: one list per (b, h); 0: one list
+    // shared by all, the global rows of a token layout)
     const int32_t* routed_rows;
     int32_t n_routed;
+    int32_t routed_stride;
     float scale;              // score scale
     float scale_log2;         // scale * log2(e)
+    // token layouts: the global tokens gtok[0 .. n_g) and their flags [L]; the
+    // random tokens links[h][t][0 .. n_links) (-1: none); per key, the rows whose
+    // random tokens hold it: trows[tptr[h (L + 1) + s] .. tptr[h (L + 1) + s + 1]);
+    // ws_g: fp32 partials of the global keys' dK, dV [B*H][n_g][g_chunks][2][D]
+    const int32_t* gtok;
+    int32_t n_g;
+    const uint8_t* tok_global;
+    const int32_t* links;
+    int32_t n_links;
+    const int32_t* tptr;
+    const int32_t* trows;
+    float* ws_g;
+    int32_t g_chunks;
 };
 
 // ---- the allocation-free forward (kernels/noalloc.hip) ----
@@ -235,6 +251,12 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t
 hipError_t launch_bwd_sum(const BwdArgs& a, int head_dim, int which, hipStream_t s);
 // sum the routed tiles' dQ partials into the dQ rows of their routed tokens
 hipError_t launch_bwd_routed_sum(const BwdArgs& a, int head_dim, hipStream_t s);
+// token layouts (kernels/bwd_token.hip): the pairs the band and the global rows
+// do not cover, added to dQ, dK, dV in place -- every non-global row's global
+// keys outside its band and its random tokens
+hipError_t launch_tok_bwd_extra(const BwdArgs& a, int head_dim, hipStream_t s);
+// global keys whose dK/dV one workgroup of the token backward accumulates
+constexpr int tok_global_keys_per_wg(int head_dim) { return head_dim == 64 ? 4 : 2; }
 // attention layer (kernels/layer.hip)
 hipError_t launch_split_heads(const float* qkv32, const void* b_qkv, void* q, void* k, void* v, int B, int L,
                               int H, int D, hipStream_t s);
@@ -332,6 +354,11 @@ struct bsattn_layout {
         int32_t* d_k_idx = nullptr;
     };
     mutable std::vector<RoutedBwd> rbwd;
+    // token layouts, backward: for each (head, key s) the non-global rows whose
+    // random tokens hold s, ascending: tlink_rows[tlink_ptr[h (L + 1) + s] ..)
+    std::vector<int32_t> tlink_ptr, tlink_rows;
+    mutable int32_t* d_tlink_ptr = nullptr;
+    mutable int32_t* d_tlink_rows = nullptr;
 };
 
 namespace bsattn {

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
     int t = blk * 64 + wave * 32 + ql;
     if (MASK == MASK_ROUTED_Q) {
         const int kk = t;
-        t = kk < a.n_routed ? a.routed_rows[grp * a.n_routed + kk] : -1;
+        t = kk < a.n_routed ? a.routed_rows[grp * a.routed_stride + kk] : -1;
         if (t >= a.L) t = -1;
     }
 
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
     auto row_token = [&](int ib, int row) -> int {
         if (MASK != MASK_BAND_ROUTED || ib < a.nb) return ib * 64 + row;
         const int kk = (ib - a.nb) * 64 + row;
-        const int t = kk < a.n_routed ? a.routed_rows[grp * a.n_routed + kk] : -1;
+        const int t = kk < a.n_routed ? a.routed_rows[grp * a.routed_stride + kk] : -1;
         return t < a.L ? t : -1;
     };
     auto fetch = [&](int ib) {
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(256) void bwd_routed_sum_kernel(const BwdArgs a) {
     const int x = slice * 1024 + threadIdx.x * 4;
     const int kk = r * 64 + x / D;
     if (kk >= a.n_routed) return;
-    const int t = a.routed_rows[grp * a.n_routed + kk];
+    const int t = a.routed_rows[grp * a.routed_stride + kk];
     if (t < 0 || t >= a.L) return;
     const float* src = a.ws_dq + ((size_t)b * a.n_slots + sm.first_slot) * 64 * D + x;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

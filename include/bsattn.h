@@ -379,7 +379,8 @@ bsattn_status bsattn_forward_routed(const bsattn_layout* band_layout, bsattn_dty
 /* Device workspace bytes needed by bsattn_backward for this layout, batch and
  * head width: delta = rowsum(dO * O) per query row (fp32 [B, H, L]), then the
  * fp32 partial gradients of rows and columns of the layout that are split
- * across workgroups (global rows and the key blocks every row attends).
+ * across workgroups (global rows and the key blocks every row attends; for a
+ * token layout also its global rows' tiles and its global keys' partials).
  * Written to *bytes.  The workspace needs no initialisation and holds nothing
  * between calls; calls that share one must not overlap in time. */
 bsattn_status bsattn_backward_workspace_size(const bsattn_layout* layout, int32_t batch,
@@ -393,9 +394,15 @@ bsattn_status bsattn_backward_workspace_size(const bsattn_layout* layout, int32_
  *   P = exp(scale * q.k - lse) on allowed keys, delta = rowsum(dout * out),
  *   dv = P^T dout,  ds = P * (dout v^T - delta),
  *   dq = scale * ds k,  dk = scale * ds^T q.
- *   layout          uploaded window/global/random or band layout (token,
- *                   adaptive layouts and the routed variant: UNSUPPORTED; band
- *                   layouts take no key padding).  out and lse must come from
+ *   layout          uploaded window/global/random, band or token layout
+ *                   (adaptive and top-keep layouts, and the routed variant:
+ *                   UNSUPPORTED; band and token layouts take no key padding).
+ *                   A token layout (BigBird page, its token-granular code
+ *                   example) runs the band and its global rows through the
+ *                   block passes and adds each non-global row's global keys
+ *                   outside its band and its random tokens with gather
+ *                   kernels, in place on dq, dk and dv (one more bf16
+ *                   rounding there).  out and lse must come from
  *                   bsattn_forward on this layout: outputs of
  *                   bsattn_forward_routed are not detected and would give the
  *                   band's gradients for the routed rows.

@@ -140,11 +140,31 @@ def test_backward_workspace_size_and_lists():
         bs.bsattn_backward_workspace_size(lay, 2, 96)
 
 
+def test_token_backward_workspace_size():
+    """Token layouts: delta, the band and global-row partial slots, then the global
+    keys' chunk partials (one chunk per 256 rows at most, about 2048 workgroups)."""
+    B, H, L, ng = 2, 3, 4096, 40
+    tok = bs.bsattn_make_token_layout(H, L, 64, ng, 4, 7)
+    n = bs.bsattn_backward_workspace_size(tok, B, 64)
+    delta = B * H * L * 4
+    chunks = max(1, min(L // 256, -(-2048 // (B * H * -(-ng // 4)))))   # 4 global keys per workgroup at D = 64
+    glob = B * H * ng * chunks * 2 * 64 * 4
+    assert n >= delta + glob and n % 256 == 0
+    # the global rows' dQ partials grow with B, and so does everything else
+    assert bs.bsattn_backward_workspace_size(tok, 2 * B, 64) > n
+    assert bs.bsattn_backward_workspace_size(tok, B, 128) > n
+    # no global tokens: no global partials, no global-row slots
+    tok0 = bs.bsattn_make_token_layout(H, L, 64, 0, 4, 7)
+    band = bs.bsattn_make_band_layout(H, L, 64, 64)
+    assert bs.bsattn_backward_workspace_size(tok0, B, 64) == bs.bsattn_backward_workspace_size(band, B, 64)
+
+
 def test_backward_rejects_before_any_hip_call():
     L = bs.lib()
     lay = bs.bsattn_make_layout(2, 1024, 64, 3, [0], 1, 0)
     band = bs.bsattn_make_band_layout(2, 1024, 64, 32)
     tok = bs.bsattn_make_token_layout(2, 1024, 32, 8, 2, 1)
+    adp = bs.bsattn_make_adaptive_layout(2, 1024, 4)
     f = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(10)]
     ws = ctypes.c_size_t(0)
 
@@ -153,7 +173,8 @@ def test_backward_rejects_before_any_hip_call():
                                  kv, scale, None, ws, None)
 
     assert call(None) == 1
-    assert call(tok.handle) == 2 and "layout" in bs.bsattn_last_error()
+    assert call(adp.handle) == 2 and "layout" in bs.bsattn_last_error()
+    assert call(tok.handle, kv=f[9]) == 2 and "padding" in bs.bsattn_last_error()
     assert call(band.handle, kv=f[9]) == 2 and "padding" in bs.bsattn_last_error()
     assert call(lay.handle, dtype=0) == 2 and "bf16" in bs.bsattn_last_error()
     assert call(lay.handle, dout=None) == 1
@@ -189,13 +210,13 @@ def test_layer_rejects_before_any_hip_call():
 def test_prepare_rejects_before_any_hip_call():
     L = bs.lib()
     lay = bs.bsattn_make_layout(2, 1024, 64, 3, [0], 1, 0)
-    tok = bs.bsattn_make_token_layout(2, 1024, 16, 8, 2, 0)
+    adp = bs.bsattn_make_adaptive_layout(2, 1024, 4)
     assert L.bsattn_prepare(None, 1, 64, 0, 0, None) == 1           # NULL layout
     assert L.bsattn_prepare(lay.handle, 0, 64, 0, 0, None) == 1     # batch < 1
     assert L.bsattn_prepare(lay.handle, 1, 96, 0, 0, None) == 2     # head_dim
     assert L.bsattn_prepare(lay.handle, 1, 64, 5, 0, None) == 1     # routed rows need a band layout
     assert L.bsattn_prepare(lay.handle, 1, 64, 2000, 0, None) == 1  # num_routed > seq_len
-    assert L.bsattn_prepare(tok.handle, 1, 64, 0, 1, None) == 2     # no backward for token layouts
+    assert L.bsattn_prepare(adp.handle, 1, 64, 0, 1, None) == 2     # no backward for adaptive layouts
     assert "backward" in bs.bsattn_last_error()
 
 

@@ -275,3 +275,63 @@ def test_backward_routed_full_size_heads():
     """The routed workload's own shape (B1 H32 L4096 D128, band 32, top 64): whole heads."""
     wl = WORKLOADS["routed-L4096"]
     _routed_bwd_case(wl, "bwd routed-L4096 heads 0, 13, 31", heads=[0, 13, 31])
+
+
+# ---------------- token-granular BigBird pattern ----------------
+# Query t sees key s iff t or s is global, |t - s| <= w, or s is one of t's
+# random tokens (BigBird page, code example).  The band and the global rows go
+# through the block passes; each non-global row's global keys outside its
+# band and its random tokens through the token kernels.
+
+def _token_layouts(wl):
+    lay = bs.bsattn_make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
+                                      wl.layout_seed)
+    bs.bsattn_layout_upload(lay)
+    olay = OL.make_token_layout(wl.heads, wl.seq_len, wl.band_tokens, wl.num_global, wl.random_tokens,
+                                wl.layout_seed)
+    return lay, olay
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_token_pattern(D):
+    wl = WORKLOADS["bigbird-tok-L8192"].with_(batch=2, heads=2, seq_len=1536, head_dim=D)
+    _case(wl, f"bwd token L1536 D={D}", layouts=_token_layouts)
+
+
+@pytest.mark.parametrize("D,w,ng,r", [(64, 5, 77, 8), (128, 200, 77, 3), (64, 130, 150, 16)])
+def test_backward_token_many_globals(D, w, ng, r):
+    # 5-10% global tokens: two or three global-row tiles, global keys inside and outside the band
+    wl = WORKLOADS["bigbird-tok-L8192"].with_(batch=1, heads=2, seq_len=1536, head_dim=D, band_tokens=w,
+                                              num_global=ng, random_tokens=r, layout_seed=D + w)
+    _case(wl, f"bwd token w={w} ng={ng} r={r} D={D}", layouts=_token_layouts)
+
+
+def test_backward_token_wide_band_split():
+    # a 600-token band at L = 2048: band rows and columns of up to 21 blocks are split
+    wl = WORKLOADS["bigbird-tok-L8192"].with_(batch=1, heads=2, seq_len=2048, band_tokens=600, num_global=20)
+    _case(wl, "bwd token w=600 L2048", layouts=_token_layouts)
+
+
+def test_backward_token_edges():
+    base = WORKLOADS["bigbird-tok-L8192"].with_(batch=2, heads=2, seq_len=256, head_dim=64)
+    _case(base.with_(num_global=0), "bwd token: no global tokens", layouts=_token_layouts)
+    _case(base.with_(random_tokens=0), "bwd token: no random tokens", layouts=_token_layouts)
+    _case(base.with_(num_global=1, band_tokens=0), "bwd token: one global token, window 0", layouts=_token_layouts)
+    _case(base.with_(seq_len=128, num_global=128), "bwd token: every token global", layouts=_token_layouts)
+    _case(base.with_(seq_len=64, num_global=2, band_tokens=63, random_tokens=64), "bwd token: one tile",
+          layouts=_token_layouts)
+
+
+def test_backward_token_benchmark_shape_one_head():
+    wl = WORKLOADS["bigbird-tok-L8192"]
+    _case(wl, "bwd bigbird-tok-L8192 (b=1, h=5)", heads=[5], batches=[1], layouts=_token_layouts)
+
+
+def test_backward_token_rejects_padding():
+    wl = WORKLOADS["bigbird-tok-L8192"].with_(batch=1, heads=1, seq_len=256)
+    lay, _ = _token_layouts(wl)
+    dev = {k: v.cuda() for k, v in make_inputs(wl).items()}
+    o, lse = bs.forward(dev["q"], dev["k"], dev["v"], lay, scale=wl.scale)
+    vl = torch.tensor([100], dtype=torch.int32, device="cuda")
+    with pytest.raises(bs.BsattnError, match="padding"):
+        bs.backward(dev["q"], dev["k"], dev["v"], o, lse, torch.ones_like(o), lay, key_valid_len=vl, scale=wl.scale)

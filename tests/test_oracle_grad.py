@@ -171,3 +171,29 @@ def test_routed_backward_matches_torch_autograd():
         assert np.abs(dk[0, h] - rk).max() < 1e-12
         assert np.abs(dv[0, h] - rv).max() < 1e-12
 
+
+
+def test_token_pattern_backward_matches_torch_autograd():
+    """The token-granular pattern's gradients (attention_backward over a TokenLayout)
+    against torch autograd of the dense formula, with the mask composed here from its
+    four parts: t global, s global, |t - s| <= w, or s one of t's random tokens (the
+    random draws themselves are pinned in the token-layout tests)."""
+    from oracle import layout as OL
+    B, H, L, D = 1, 2, 160, 8
+    w, ng, r = 6, 5, 3
+    q, k, v, do = (_rand((B, H, L, D), s) for s in (41, 42, 43, 44))
+    lay = OL.make_token_layout(H, L, w, ng, r, 9)
+    gset = set(lay.global_tokens)
+    assert len(gset) == ng
+    dq, dk, dv = OG.attention_backward(q, k, v, do, lay, 0.3, chunk=50)
+    for h in range(H):
+        mask = np.zeros((L, L), dtype=bool)
+        for t in range(L):
+            links = set(lay.random_links(h, t))
+            assert len(links) == (0 if t in gset else r)
+            for s_ in range(L):
+                mask[t, s_] = t in gset or s_ in gset or abs(t - s_) <= w or s_ in links
+        rq, rk, rv = _torch_dense_grad(q[0, h], k[0, h], v[0, h], do[0, h], mask, 0.3)
+        assert np.abs(dq[0, h] - rq).max() < 1e-12
+        assert np.abs(dk[0, h] - rk).max() < 1e-12
+        assert np.abs(dv[0, h] - rv).max() < 1e-12
