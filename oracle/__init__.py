@@ -24,6 +24,9 @@ Modules
               by pooled fp64 scores) and its attention.
 ``topr``      per-query top-keep attention: each query keeps its ``keep``
               best keys by an in-order fp32 score, ties to the lower index.
+``candidates`` candidate-list attention: a convolution of the hidden states
+              predicts key positions per query (fp64, fixed order), the best
+              of them by the same fp32 score are kept and attended to.
 
 Parity pins (see ``tests/test_oracle_*.py``): every function is checked
 against something other than itself -- published splitmix64 outputs, closed
@@ -34,4 +37,4 @@ Parity unpinned: the concrete choice of random blocks beyond the
 hash stream itself (the composition of the per-row seed and the shuffle are
 this library's own specification; any uniform draw satisfies the pages).
 """
-from . import layout, attention, attention_grad, layer, router, adaptive, topr  # noqa: F401
+from . import layout, attention, attention_grad, layer, router, adaptive, topr, candidates  # noqa: F401
