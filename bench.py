@@ -55,6 +55,7 @@ PEAK_F32_VECTOR_TFLOPS = 157.3
 KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "fwd_bf16.hip")
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "bwd_bf16.hip")
 TOPR_KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "topr.hip")
+CAND_KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_transformer_amd", "csrc", "kernels", "candidates.hip")
 # the attention kernel that dominates a bf16 forward: one for D = 64, one for D = 128
 def main_kernel(head_dim: int) -> str:
     return "fwd_bf16_d64_kernel" if head_dim == 64 else "fwd_bf16_kernel"
@@ -111,6 +112,151 @@ def token_extra_pairs(bs, lay, wl):
     if links is not None and links.size:
         total += int(((links >= 0) & nonglobal[None, :, None]).sum())
     return total
+
+
+def cpu_baseline_candidates(wl, inp, seconds: float):
+    """The oracle as it stands on the candidate workload: the positions of batch entry 0,
+    then whole heads of it until ``seconds`` have passed, scaled to the whole job."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import candidates as OC
+    t0 = time.perf_counter()
+    pos = OC.candidate_positions(inp["x"][:1], inp["w_conv"].permute(2, 1, 0).contiguous().numpy(),
+                                 inp["b_conv"].numpy())
+    t_conv = time.perf_counter() - t0
+    pos_all = np.zeros((wl.batch,) + pos.shape[1:], dtype=np.int32)
+    pos_all[0] = pos[0]
+    heads = 0
+    t1 = time.perf_counter()
+    for h in range(wl.heads):
+        OC.candidate_attention_forward(inp["q"], inp["k"], inp["v"], pos_all, wl.cand_keep, wl.scale,
+                                       rows=[(0, h, t) for t in range(wl.seq_len)])
+        heads += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    t_head = (time.perf_counter() - t1) / heads
+    full_s = wl.batch * (t_conv + wl.heads * t_head)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": wl.batch * wl.seq_len / full_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the positions of 1 of {wl.batch} batch entries ({t_conv:.2f} s, fp64 fixed-order "
+                      f"convolution) and {heads} of its {wl.heads} heads ({t_head:.2f} s each: fp32 ranking of "
+                      f"the candidates and fp64 attention over the kept ones), scaled to the whole job",
+            "seconds": round(time.perf_counter() - t0, 3), **host_info()}
+
+
+def run_candidates(args, wl, inp, bs, torch, np):
+    """Candidate-list attention: one step is the candidate positions of the hidden
+    states followed by the attention over each query's kept candidates."""
+    dev = torch.device("cuda:0")
+    base = {k: v.to(dev) for k, v in inp.items()}
+    sets = [{k: (v if r == 0 else v.clone()) for k, v in base.items()} for r in range(max(1, args.rotate))]
+    B, H, L, D = wl.batch, wl.heads, wl.seq_len, wl.head_dim
+    C, kc, keep = H * D, wl.num_candidates, wl.cand_keep
+    poss = [torch.empty((B, L, kc), dtype=torch.int32, device=dev) for _ in sets]
+    outs = [torch.empty((B, H, L, D), dtype=torch.bfloat16, device=dev) for _ in sets]
+    lses = [torch.empty((B, H, L), dtype=torch.float32, device=dev) for _ in sets]
+    rotation_bytes = sum(t.numel() * t.element_size() for st in sets for t in st.values()) + \
+        sum(t.numel() * t.element_size() for lst in (poss, outs, lses) for t in lst)
+    L_ = bs.lib()
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    calls = []
+    for s_, p_, o_, l_ in zip(sets, poss, outs, lses):
+        calls.append(((s_["x"].data_ptr(), s_["w_conv"].data_ptr(), s_["b_conv"].data_ptr(), B, L, C, kc,
+                       p_.data_ptr(), sh),
+                      (1, B, H, L, D, s_["q"].data_ptr(), s_["k"].data_ptr(), s_["v"].data_ptr(), p_.data_ptr(), kc,
+                       keep, ctypes.c_float(wl.scale), o_.data_ptr(), l_.data_ptr(), None, sh)))
+    posf, fwd = L_.bsattn_candidate_positions, L_.bsattn_candidate_forward
+
+    def step(i):
+        pc, fc = calls[i % len(calls)]
+        st = posf(*pc)
+        if st != 0:
+            raise bs.BsattnError("bsattn_candidate_positions", st)
+        st = fwd(*fc)
+        if st != 0:
+            raise bs.BsattnError("bsattn_candidate_forward", st)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    every = max(1, args.event_every if args.event_every is not None else (1 if K <= 25 else K // 25))
+    timed = list(range(0, K, every))
+    ev = bs.HipEvents(len(timed))
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    set_ev = L_.bsattn_set_profile_events
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    j = 0
+    for i in range(K):
+        if i % every == 0:
+            set_ev(ev.before[j], ev.after[j])
+            step(i)
+            set_ev(None, None)
+            j += 1
+        else:
+            step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / K
+    kern_ms = [ev.elapsed_ms(n) for n in range(len(timed))]
+    ev.destroy()
+    warm_ms = []
+    if args.warm_launches > 0:
+        wev = bs.HipEvents(args.warm_launches)
+        for n in range(args.warm_launches):
+            set_ev(wev.before[n], wev.after[n])
+            step(0)
+        set_ev(None, None)
+        torch.cuda.synchronize()
+        warm_ms = [wev.elapsed_ms(n) for n in range(args.warm_launches)]
+        wev.destroy()
+    kern_avg_ms, kern_med_ms = float(np.mean(kern_ms)), float(np.median(kern_ms))
+    # work: the convolution (2 x 3C flop per output), the candidates' scores (2 D per
+    # candidate) and the attention over the kept keys (4 D per kept key)
+    conv_flops = 2.0 * B * L * kc * 3 * C
+    attn_flops = B * H * L * (2.0 * kc * D + 4.0 * keep * D)
+    flops_per_step = conv_flops + attn_flops
+    # the attention kernel's algorithmic bytes: Q, K, V read and O, LSE written once, the positions read
+    kernel_bytes = B * H * L * (4 * D * 2 + 4) + B * L * kc * 4
+    kern_gbps = kernel_bytes / (kern_avg_ms / 1e3) / 1e9
+    kern_tflops = attn_flops / (kern_avg_ms / 1e3) / 1e12
+    t_hbm = kernel_bytes / (PEAK_HBM_GBPS * 1e9)
+    t_alu = attn_flops / (PEAK_F32_VECTOR_TFLOPS * 1e12)
+    if t_hbm >= t_alu:
+        bound, achieved, peak, unit = "hbm", kern_gbps, PEAK_HBM_GBPS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "alu", kern_tflops, PEAK_F32_VECTOR_TFLOPS, "TFLOP/s"
+    kname = "cand_attention_kernel"
+    traffic = traffic_from_profile(wl.name, kname, CAND_KERNEL_SOURCE)
+    result = {
+        "metric": METRIC, "value": round(B * L / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded Gaussian Q/K/V, hidden states and candidate-generator weights of the workload's "
+                "shape)",
+        "config": {"workload": wl.name, "pass": "forward", "batch": B, "heads": H, "seq_len": L, "head_dim": D,
+                   "channels": C, "num_candidates": kc, "keep": keep},
+        "eff_tflops": round(flops_per_step / (ms_step / 1e3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * flops_per_step / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "hbm_alg_gbps": round(kernel_bytes / (ms_step / 1e3) / 1e9, 1),
+        "roofline": {
+            "bound": bound, "kernel": kname, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "mfma_frac": 0.0, "hbm_frac": round(kern_gbps / PEAK_HBM_GBPS, 4),
+            "kernel_avg_us": round(kern_avg_ms * 1e3, 3), "kernel_median_us": round(kern_med_ms * 1e3, 3),
+            "kernel_timed_steps": len(kern_ms),
+            "kernel_warm_median_us": round(float(np.median(warm_ms)) * 1e3, 3) if warm_ms else None,
+            "input_sets": len(sets), "rotation_bytes": int(rotation_bytes),
+            "flop_per_launch": attn_flops, "alg_bytes_per_launch": kernel_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_candidates(wl, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
 
 
 def traffic_from_profile(workload: str, kernel: str, source: str = KERNEL_SOURCE):
@@ -313,9 +459,12 @@ def main():
     wl = WORKLOADS[args.workload or THROUGHPUT_WORKLOAD]
     inp = make_inputs(wl)
 
-    if (wl.adaptive or wl.routed or wl.topr) and args.which != "forward":
-        print("adaptive, routed and top-keep workloads are timed in the forward only", file=sys.stderr)
+    if (wl.adaptive or wl.routed or wl.topr or wl.candidates) and args.which != "forward":
+        print("adaptive, routed, top-keep and candidate workloads are timed in the forward only", file=sys.stderr)
         sys.exit(2)
+    if wl.candidates:
+        run_candidates(args, wl, inp, bs, torch, np)
+        return
     t0 = time.perf_counter()
     if wl.band or wl.routed:
         lay = bs.bsattn_make_band_layout(wl.heads, wl.seq_len, 64, wl.band_tokens)

@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     bsattn_backward_routed,
     bsattn_backward_routed_workspace_size,
     bsattn_backward_workspace_size,
+    bsattn_candidate_forward,
+    bsattn_candidate_positions,
     bsattn_forward,
     bsattn_forward_noalloc,
     bsattn_forward_routed,

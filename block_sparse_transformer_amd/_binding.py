@@ -81,6 +81,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_layer_workspace_size.argtypes = [_c_vp, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)]
     L.bsattn_layer_forward.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                        _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_size_t, _c_vp]
+    L.bsattn_candidate_positions.argtypes = [_c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp]
+    L.bsattn_candidate_forward.argtypes = [ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
+                                           _c_vp, _c_int, _c_int, ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp]
     L.bsattn_set_profile_events.argtypes = [_c_vp, _c_vp]
     L.bsattn_prepare.argtypes = [_c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp]
     L.bsattn_forward_noalloc.argtypes = [_c_vp, ctypes.c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp,
@@ -98,7 +101,7 @@ def lib() -> ctypes.CDLL:
                  "bsattn_route_topk", "bsattn_route_workspace_size", "bsattn_forward_routed",
                  "bsattn_set_profile_events",
                  "bsattn_prepare", "bsattn_forward_noalloc", "bsattn_backward_routed_workspace_size",
-                 "bsattn_backward_routed"):
+                 "bsattn_backward_routed", "bsattn_candidate_positions", "bsattn_candidate_forward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -224,6 +227,44 @@ def bsattn_topr_select(layout: Layout, q, k, workspace=None, stream=None):
         layout.handle, B, H, L, D, q.data_ptr(), k.data_ptr(), bits.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return bits
+
+
+def bsattn_candidate_positions(x, w, bias, positions=None, stream=None):
+    """Candidate positions [B, L, k] (device int32) of the hidden states x (bf16 [B, L, C]);
+    w fp32 [3, C, k] (tap-major Conv1d weight), bias fp32 [k]."""
+    import torch
+    B, L, C = x.shape
+    k = w.shape[2]
+    if x.dtype != torch.bfloat16 or w.dtype != torch.float32 or bias.dtype != torch.float32:
+        raise ValueError("x must be bf16, w and bias fp32")
+    if tuple(w.shape) != (3, C, k) or tuple(bias.shape) != (k,) or not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("w must be a contiguous [3, C, k] tensor and bias [k]")
+    if positions is None:
+        positions = torch.empty((B, L, k), dtype=torch.int32, device=x.device)
+    _check("bsattn_candidate_positions", lib().bsattn_candidate_positions(
+        x.data_ptr(), w.data_ptr(), bias.data_ptr(), B, L, C, k, positions.data_ptr(), _stream_handle(stream)))
+    return positions
+
+
+def bsattn_candidate_forward(q, k, v, positions, keep: int, scale: Optional[float] = None, out=None, lse=None,
+                             kept=None, stream=None):
+    """Attention of every query over its `keep` best candidates; returns (out, lse)."""
+    import torch
+    _check_qkv(q, k, v, q if out is None else out)
+    B, H, L, D = q.shape
+    n_cand = positions.shape[-1]
+    if positions.dtype != torch.int32 or tuple(positions.shape) != (B, L, n_cand) or not positions.is_contiguous():
+        raise ValueError("positions must be a contiguous int32 [B, L, k] tensor")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    _check("bsattn_candidate_forward", lib().bsattn_candidate_forward(
+        _dtype_code(q), B, H, L, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), positions.data_ptr(), n_cand,
+        int(keep), scale, out.data_ptr(), lse.data_ptr(), None if kept is None else kept.data_ptr(),
+        _stream_handle(stream)))
+    return out, lse
 
 
 def bsattn_layout_token_links(layout: Layout) -> Tuple[np.ndarray, np.ndarray]:

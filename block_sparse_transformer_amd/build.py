@@ -32,6 +32,7 @@ SOURCES = [
     "kernels/noalloc.hip",
     "kernels/topr.hip",
     "kernels/bwd_token.hip",
+    "kernels/candidates.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

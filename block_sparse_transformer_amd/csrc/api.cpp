@@ -1852,6 +1852,56 @@ bsattn_status bsattn_prepare(const bsattn_layout* lay, int32_t batch, int32_t he
     return ok();
 }
 
+bsattn_status bsattn_candidate_positions(const void* x, const float* w, const float* bias, int32_t batch,
+                                         int32_t seq_len, int32_t channels, int32_t num_candidates,
+                                         int32_t* positions, hipStream_t stream) {
+    if (!x || !w || !bias || !positions) return fail(BSATTN_ERR_INVALID_ARG, "NULL pointer");
+    if (batch < 1 || seq_len < 1 || channels < 1)
+        return fail(BSATTN_ERR_INVALID_ARG, "batch, seq_len and channels must be >= 1");
+    if (num_candidates < 1 || num_candidates > kMaxCandidates)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_candidates must be in [1, %d] (got %d)", kMaxCandidates,
+                    num_candidates);
+    if ((reinterpret_cast<uintptr_t>(x) & 1u) || (reinterpret_cast<uintptr_t>(w) & 3u) ||
+        (reinterpret_cast<uintptr_t>(bias) & 3u) || (reinterpret_cast<uintptr_t>(positions) & 3u))
+        return fail(BSATTN_ERR_INVALID_ARG, "pointers must be aligned to their element size");
+    if ((int64_t)batch * seq_len * std::max(channels, num_candidates) >= ((int64_t)1 << 40) ||
+        (int64_t)batch * seq_len >= ((int64_t)1 << 31) / 4)
+        return fail(BSATTN_ERR_UNSUPPORTED, "input too large");
+    const hipError_t e = launch_cand_positions(x, w, bias, batch, seq_len, channels, num_candidates, positions,
+                                               stream);
+    if (e != hipSuccess) return hip_fail(e, "candidate positions launch");
+    return ok();
+}
+
+bsattn_status bsattn_candidate_forward(bsattn_dtype dtype, int32_t B, int32_t H, int32_t L, int32_t D, const void* q,
+                                       const void* k, const void* v, const int32_t* positions,
+                                       int32_t num_candidates, int32_t keep, float scale, void* out, float* lse,
+                                       int32_t* kept, hipStream_t stream) {
+    if (dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "candidate attention is bf16 only");
+    if (!q || !k || !v || !positions || !out || !lse) return fail(BSATTN_ERR_INVALID_ARG, "NULL pointer");
+    if (B < 1 || H < 1 || L < 1) return fail(BSATTN_ERR_INVALID_ARG, "batch, heads and seq_len must be >= 1");
+    if (D != 64 && D != 128) return fail(BSATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+    if (num_candidates < 1 || num_candidates > kMaxCandidates)
+        return fail(BSATTN_ERR_INVALID_ARG, "num_candidates must be in [1, %d] (got %d)", kMaxCandidates,
+                    num_candidates);
+    if (keep < 1 || keep > num_candidates)
+        return fail(BSATTN_ERR_INVALID_ARG, "keep must be in [1, num_candidates] (got %d)", keep);
+    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(BSATTN_ERR_INVALID_ARG, "scale must be > 0 and finite");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(positions) & 3u) ||
+        (reinterpret_cast<uintptr_t>(kept) & 3u))
+        return fail(BSATTN_ERR_INVALID_ARG, "q, k, v, out must be 16-byte aligned, the others 4-byte");
+    const void* ins[4] = {q, k, v, positions};
+    for (const void* in : ins)
+        if (in == out || in == (const void*)lse || (kept && in == (const void*)kept))
+            return fail(BSATTN_ERR_INVALID_ARG, "an output aliases an input");
+    if (((int64_t)B * H * L + 3) / 4 >= ((int64_t)1 << 31)) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+    const hipError_t e = launch_cand_attention(q, k, v, positions, B, H, L, D, num_candidates, keep, scale, out, lse,
+                                               kept, stream, g_ev_before, g_ev_after);
+    if (e != hipSuccess) return hip_fail(e, "candidate attention launch");
+    return ok();
+}
+
 bsattn_status bsattn_set_profile_events(hipEvent_t before, hipEvent_t after) {
     if ((before == nullptr) != (after == nullptr))
         return fail(BSATTN_ERR_INVALID_ARG, "set both events or neither");

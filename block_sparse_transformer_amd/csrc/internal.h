@@ -255,6 +255,17 @@ hipError_t launch_bwd_routed_sum(const BwdArgs& a, int head_dim, hipStream_t s);
 // do not cover, added to dQ, dK, dV in place -- every non-global row's global
 // keys outside its band and its random tokens
 hipError_t launch_tok_bwd_extra(const BwdArgs& a, int head_dim, hipStream_t s);
+// candidate-list attention (kernels/candidates.hip): positions [B, L, k] of the
+// candidate generator (x bf16 [B, L, C], w fp32 [3][C][k], bias fp32 [k]),
+// then attention over the best `keep` distinct candidates of every query
+// (kept: optional int32 [B, H, L, keep], ascending, -1 padded)
+constexpr int kMaxCandidates = 64;
+hipError_t launch_cand_positions(const void* x, const float* w, const float* bias, int B, int L, int C, int k,
+                                 int32_t* pos, hipStream_t s);
+hipError_t launch_cand_attention(const void* q, const void* k, const void* v, const int32_t* pos, int B, int H,
+                                 int L, int D, int n_cand, int keep, float scale, void* out, float* lse,
+                                 int32_t* kept, hipStream_t s, hipEvent_t before = nullptr,
+                                 hipEvent_t after = nullptr);
 // global keys whose dK/dV one workgroup of the token backward accumulates
 constexpr int tok_global_keys_per_wg(int head_dim) { return head_dim == 64 ? 4 : 2; }
 // attention layer (kernels/layer.hip)

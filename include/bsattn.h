@@ -211,6 +211,51 @@ bsattn_status bsattn_topr_select(const bsattn_layout* layout, int32_t batch, int
                                  uint64_t* keep_bits, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/* Candidate positions of every query from the hidden states (Adaptive
+ * Sparse Transformer page, "Adapt or Perish: 新手入门指南 – Adaptive Sparse
+ * Transformer 核心原理与实战", its candidate generator: a Conv1d from the
+ * model width to k channels, kernel 3, padding 1, predicts k relevant
+ * positions per query).  y[b, t, j] = bias[j] + sum over taps u = 0, 1, 2
+ * and channels c of w[u][c][j] * x[b, t + u - 1, c] (zeros outside the
+ * sequence; w is PyTorch's Conv1d weight W[j, c, u] stored tap-major).  The
+ * sum is taken in fp64 in one fixed order -- from bias[j], taps u = 0, 1, 2
+ * in turn, channels c = 0 .. C - 1 within a tap -- so the position is
+ * reproducible: positions[b, t, j] = y rounded to the nearest integer (ties
+ * to even), clamped to [0, L - 1] (NaN: 0).
+ *   x          device bf16 [batch, seq_len, channels], the hidden states.
+ *   w          device fp32 [3, channels, num_candidates].
+ *   bias       device fp32 [num_candidates].
+ *   positions  device int32 [batch, seq_len, num_candidates], written.
+ * 1 <= num_candidates <= 64; channels >= 1; seq_len >= 1.  Enqueued on
+ * `stream`; allocates nothing. */
+bsattn_status bsattn_candidate_positions(const void* x, const float* w, const float* bias, int32_t batch,
+                                         int32_t seq_len, int32_t channels, int32_t num_candidates,
+                                         int32_t* positions, hipStream_t stream);
+
+/* Attention over each query's best candidates (the same page: its importance
+ * evaluation scores the candidate positions and keeps the best r%; then the
+ * SparseAttention formula with M = 1 on the kept keys).  For every (batch,
+ * head, query): the distinct positions among positions[b, t, 0 .. k) (values
+ * outside [0, seq_len) are ignored) are ranked by the fp32 score q.k taken in
+ * order of d from +0 (each bf16 product is exact in fp32, so the rank is
+ * reproducible), ties to the lower position; the first `keep` are kept (all
+ * of them when fewer are distinct).  out = softmax(scale * q.k) over the kept
+ * keys times their V rows, lse = the log-sum-exp of those scaled scores.
+ *   dtype        BSATTN_BF16 (others: UNSUPPORTED).
+ *   q, k, v      device bf16 [B, H, L, D], D in {64, 128}, 16-byte aligned.
+ *   positions    device int32 [B, L, num_candidates] (shared by the heads),
+ *                e.g. from bsattn_candidate_positions.
+ *   keep         1 <= keep <= num_candidates <= 64 (the page: floor(k r)).
+ *   out, lse     device bf16 [B, H, L, D] and fp32 [B, H, L], written; a
+ *                query with no candidate in range gets O = 0, lse = -inf.
+ *   kept         optional device int32 [B, H, L, keep]: the kept positions,
+ *                ascending, -1 past their count; NULL to skip.
+ * Enqueued on `stream`; allocates nothing. */
+bsattn_status bsattn_candidate_forward(bsattn_dtype dtype, int32_t batch, int32_t num_heads, int32_t seq_len,
+                                       int32_t head_dim, const void* q, const void* k, const void* v,
+                                       const int32_t* positions, int32_t num_candidates, int32_t keep,
+                                       float scale, void* out, float* lse, int32_t* kept, hipStream_t stream);
+
 /* Borrowed host view of a token layout (valid until destroy): the global
  * tokens [num_global], ascending, and the random tokens [H][L][links_per_row],
  * each row ascending and padded with -1.  INVALID_ARG for other layouts.  Any
@@ -485,8 +530,9 @@ bsattn_status bsattn_layer_forward(const bsattn_layout* layout, int32_t batch, i
 /* Measurement hook: while set (non-NULL), every forward call made from this
  * thread records `before` on its stream immediately before the main attention
  * kernel and `after` immediately after it (over a top-keep layout: around the
- * key selection, its dominant kernel), and every backward call does the
- * same around its dK/dV kernel, so a caller can time that kernel alone with
+ * key selection, its dominant kernel; in bsattn_candidate_forward: around its
+ * attention kernel), and every backward call does the same around its dK/dV
+ * kernel, so a caller can time that kernel alone with
  * hipEventElapsedTime.  Pass NULLs to clear.  Events are caller owned. */
 bsattn_status bsattn_set_profile_events(hipEvent_t before, hipEvent_t after);
 

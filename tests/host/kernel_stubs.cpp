@@ -38,6 +38,13 @@ hipError_t launch_bwd_dkdv(const BwdArgs&, int, int, hipStream_t, hipEvent_t, hi
 hipError_t launch_bwd_sum(const BwdArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd_routed_sum(const BwdArgs&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_tok_bwd_extra(const BwdArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_cand_positions(const void*, const float*, const float*, int, int, int, int, int32_t*, hipStream_t) {
+    return hipErrorNotSupported;
+}
+hipError_t launch_cand_attention(const void*, const void*, const void*, const int32_t*, int, int, int, int, int, int,
+                                 float, void*, float*, int32_t*, hipStream_t, hipEvent_t, hipEvent_t) {
+    return hipErrorNotSupported;
+}
 hipError_t launch_split_heads(const float*, const void*, void*, void*, void*, int, int, int, int, hipStream_t) {
     return hipErrorNotSupported;
 }

@@ -23,7 +23,9 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted([
         "bsattn_make_layout", "bsattn_make_band_layout", "bsattn_layout_csr", "bsattn_layout_upload",
         "bsattn_layout_tile_masks", "bsattn_layout_build_device", "bsattn_make_token_layout",
-        "bsattn_layout_token_links", "bsattn_make_adaptive_layout", "bsattn_adaptive_select", "bsattn_make_topr_layout", "bsattn_topr_select", "bsattn_layout_destroy", "bsattn_workspace_size",
+        "bsattn_layout_token_links", "bsattn_make_adaptive_layout", "bsattn_adaptive_select",
+        "bsattn_make_topr_layout", "bsattn_topr_select", "bsattn_candidate_positions", "bsattn_candidate_forward",
+        "bsattn_layout_destroy", "bsattn_workspace_size",
         "bsattn_forward", "bsattn_backward_workspace_size", "bsattn_backward",
         "bsattn_layer_workspace_size", "bsattn_layer_forward",
         "bsattn_route_topk", "bsattn_route_workspace_size", "bsattn_backward_routed", "bsattn_backward_routed_workspace_size", "bsattn_forward_routed", "bsattn_set_profile_events", "bsattn_status_string",
@@ -243,3 +245,32 @@ def test_device_build_rejects_token_and_adaptive_layouts():
     sub = bs.bsattn_make_layout(2, 1024, 32, 3, [0], 1, 0)
     assert L.bsattn_layout_build_device(sub.handle, fake, fake, None, None) == 1
     assert "tile_masks_dev" in bs.bsattn_last_error()
+
+
+def test_candidate_entries_reject_before_any_hip_call():
+    L = bs.lib()
+    f = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(8)]
+
+    def pos(x=f[0], w=f[1], b=f[2], B=1, Ln=64, C=32, k=32, out=f[3]):
+        return L.bsattn_candidate_positions(x, w, b, B, Ln, C, k, out, None)
+
+    assert pos(x=None) == 1
+    assert pos(k=0) == 1 and "num_candidates" in bs.bsattn_last_error()
+    assert pos(k=65) == 1
+    assert pos(C=0) == 1
+    assert pos(w=ctypes.c_void_p(0x2002)) == 1 and "aligned" in bs.bsattn_last_error()
+
+    def fwd(dtype=1, D=64, k=32, keep=9, scale=0.125, q=f[0], out=f[4], kept=None):
+        return L.bsattn_candidate_forward(dtype, 1, 2, 64, D, q, f[1], f[2], f[3], k, keep, scale, out, f[5],
+                                          kept, None)
+
+    assert fwd(dtype=0) == 2 and "bf16" in bs.bsattn_last_error()
+    assert fwd(D=96) == 2
+    assert fwd(keep=0) == 1 and "keep" in bs.bsattn_last_error()
+    assert fwd(keep=33) == 1
+    assert fwd(k=65, keep=9) == 1
+    assert fwd(scale=0.0) == 1
+    assert fwd(q=None) == 1
+    assert fwd(out=f[0]) == 1 and "alias" in bs.bsattn_last_error()
+    assert fwd(kept=f[3]) == 1 and "alias" in bs.bsattn_last_error()
+    assert fwd(out=ctypes.c_void_p(0x5008)) == 1 and "aligned" in bs.bsattn_last_error()

@@ -250,7 +250,7 @@ def test_routed_head_dim_64():
 
 # ---------------- layout on the device, determinism ----------------
 
-@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.block == 64 and not (w.token or w.adaptive or w.topr)])
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.block == 64 and not (w.token or w.adaptive or w.topr or w.candidates)])
 def test_device_layout_equals_host(name):
     wl = WORKLOADS[name]
     _say("device layout", name)

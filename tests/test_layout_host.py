@@ -17,7 +17,8 @@ def _both(H, L, w, G, r, seed):
 
 
 @pytest.mark.parametrize("name", [n for n, wl in WORKLOADS.items()
-                                  if not (wl.routed or wl.band or wl.token or wl.adaptive or wl.topr) and wl.block == 64])
+                                  if not (wl.routed or wl.band or wl.token or wl.adaptive or wl.topr or wl.candidates)
+                                  and wl.block == 64])
 def test_workload_layouts_bit_exact(name):
     wl = WORKLOADS[name]
     (rp, ci), (orp, oci) = _both(wl.heads, wl.seq_len, wl.window_blocks, wl.global_blocks,

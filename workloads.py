@@ -58,6 +58,8 @@ class Workload:
     random_tokens: int = 0          # token pattern: random tokens per row
     keep_blocks: int = 0            # > 0: content-adaptive layout keeping this many key blocks per row
     keep_tokens: int = 0            # > 0: per-query top-keep layout keeping this many keys per query
+    num_candidates: int = 0         # > 0: candidate-list attention with this many predicted positions
+    cand_keep: int = 0              # candidate-list attention: candidates kept per query
 
     @property
     def routed(self) -> bool:
@@ -75,6 +77,10 @@ class Workload:
     @property
     def topr(self) -> bool:
         return self.keep_tokens > 0
+
+    @property
+    def candidates(self) -> bool:
+        return self.num_candidates > 0
 
     @property
     def num_blocks(self) -> int:
@@ -140,6 +146,12 @@ WORKLOADS = {
     "topr-L2048": Workload(
         name="topr-L2048", batch=1, heads=12, seq_len=2048, head_dim=64, dtype="bf16",
         data_seed=10, keep_tokens=614),
+    # Candidate-list attention (the Adaptive page's candidate generator, k = 32, and importance
+    # evaluation, r = 0.3): a Conv1d of the hidden states (width C = H D = 768) predicts 32 key
+    # positions per query; every head keeps the floor(32 * 0.3) = 9 best of them.
+    "candidates-L8192": Workload(
+        name="candidates-L8192", batch=2, heads=12, seq_len=8192, head_dim=64, dtype="bf16",
+        data_seed=11, num_candidates=32, cand_keep=9),
 }
 
 THROUGHPUT_WORKLOAD = "bigbird-L8192"
@@ -153,8 +165,9 @@ def make_inputs(wl: Workload, device: Optional[str] = None) -> dict:
     """Draw the inputs of ``wl`` on the CPU (optionally moved to ``device``).
 
     Returns a dict with ``q, k, v`` ([B, H, L, D], contiguous, the workload's
-    dtype), ``w`` ([D] fp32, routed workloads only) and ``valid_len``
-    ([B] int32, padded workloads only).
+    dtype), ``w`` ([D] fp32, routed workloads only), ``valid_len`` ([B]
+    int32, padded workloads only) and, for candidate-list workloads, ``x``
+    (bf16 [B, L, C]), ``w_conv`` (fp32 [3, C, k]) and ``b_conv`` (fp32 [k]).
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(wl.data_seed)
@@ -169,6 +182,15 @@ def make_inputs(wl: Workload, device: Optional[str] = None) -> dict:
     if wl.padded:
         out["valid_len"] = torch.randint(wl.seq_len // 2, wl.seq_len + 1, (wl.batch,),
                                          generator=g, dtype=torch.int64).to(torch.int32)
+    if wl.candidates:
+        # the candidate generator's input and weights (the page's are trained; these are seeded):
+        # x [B, L, C] standard normal; the weights w [3, C, k] (tap-major) normal with standard
+        # deviation (L / 2k) / sqrt(3C), so that each output spreads over about L / k tokens;
+        # bias j = (j + 1/2) L / k, so that the k channels spread their positions over the sequence
+        C, k, L = wl.heads * wl.head_dim, wl.num_candidates, wl.seq_len
+        out["x"] = torch.randn((wl.batch, L, C), generator=g, dtype=torch.float32).to(torch.bfloat16)
+        out["w_conv"] = torch.randn((3, C, k), generator=g, dtype=torch.float32) * ((L / (2 * k)) / (3 * C) ** 0.5)
+        out["b_conv"] = (torch.arange(k, dtype=torch.float32) + 0.5) * (L / k)
     if device is not None:
         out = {k: v.to(device) for k, v in out.items()}
     return out
