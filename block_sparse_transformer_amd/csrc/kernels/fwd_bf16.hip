@@ -186,6 +186,43 @@ __device__ __forceinline__ void issue_half(const uint16_t* base, int j, const ui
     }
 }
 
+// One wave's share of a 64 x 128 tile (rows rs bytes apart, t pointing at the
+// wave's first row): load r = 0..7 reads rows 8r .. 8r + 3 after t, the lane's
+// row and piece given by the byte offset lo, and lands at LDS
+// lds + 2048 r + 16 lane.  Two groups of four loads with one M0 setting each;
+// every load of a group has its own scalar base, less its instruction offset
+// (which also moves the LDS destination), so any row stride works.
+__device__ __forceinline__ void issue_rows128(const char* t, uint32_t rs, uint32_t lo, uint32_t lds) {
+    const int64_t step = 8 * (int64_t)rs - 2048;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const char* s0 = t + (int64_t)g * 32 * rs + 4096;
+        const char* s1 = s0 + step;
+        const char* s2 = s1 + step;
+        const char* s3 = s2 + step;
+        uint32_t saved;
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %3 offset:-4096\n\t"
+            "global_load_lds_dwordx4 %1, %4 offset:-2048\n\t"
+            "global_load_lds_dwordx4 %1, %5\n\t"
+            "global_load_lds_dwordx4 %1, %6 offset:2048\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "v"(lo), "s"(lds + 8192u * g + 4096u), "s"(s0), "s"(s1), "s"(s2), "s"(s3)
+            : "memory");
+    }
+}
+
+// s_waitcnt lgkmcnt(0) with the other counters left alone, after every LDS
+// access before it in program order.
+__device__ __forceinline__ void wait_lgkm0() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
 // Row t of (b, h) group bh of the bf16 output O: contiguous [B, H, L, D], or
 // at the strides of the attention layer's concatenated heads.
 __device__ __forceinline__ uint16_t* o_row(const FwdArgs& a, size_t bh, int t, int D) {
@@ -201,12 +238,14 @@ __device__ __forceinline__ int tile_sub(int e) { return (e >> kTileSubShift) & 1
 
 // STRIDED: Q, K, V and O at the FwdArgs strides (the attention layer's layout)
 template <int D, int MASK, bool STRIDED = false>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(const FwdArgs a) {
     using Gm = Geo<D>;
     constexpr int NC = Gm::NC, NDB = Gm::NDB, TILE = Gm::TILE;
-    // K ring and V ring, two tiles each, and the workgroup's tile list.
-    __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2 * TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t vbuf[2 * TILE];
+    // D = 128 walks its list with one K and one V buffer (see below); other
+    // widths with a ring of two tiles each.
+    constexpr int NBUF = D == 128 ? 1 : 2;
+    __shared__ __attribute__((aligned(1024))) uint16_t kbuf[NBUF * TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vbuf[NBUF * TILE];
     __shared__ int flat[kMaxBinTiles];
     __shared__ int s_count;
     __shared__ __attribute__((aligned(16))) int gtok_s[MASK == MASK_TOKEN ? kMaxTokGlobal : 4];
@@ -567,141 +606,272 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdArgs a) {
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[C0 + k][db], as_bf16x8(u[k]), o[db], 0, 0, 0);
     };
 
-    // ---- software pipeline over the flat tile list ----
-    // Tile f's K sits in K buffer f & 1 and its V in V buffer f & 1.  Step f
-    // computes the scores of tile f + 1 (MFMA) while it runs the softmax of
-    // tile f (VALU), then accumulates tile f's PV product.  During step f the
-    // direct loads of K(f + 2) and V(f + 1) are in flight, into the buffers
-    // whose last readers (step f - 1) are behind the step's barrier.  A unit's
-    // Q is loaded during the first step of the unit before it, so a unit
-    // boundary costs no load latency.
-    int e0 = flat[0];
-    int e1 = F > 1 ? flat[1] : 0;
-    int e2 = F > 2 ? flat[2] : 0;
-    // group of a flat tile entry's unit
-    auto tile_g = [&](int e) -> int { return rd(u_g, tile_unit(e)); };
-    int u_cur = tile_unit(e0);
-    int kind_cur = rd(u_kind, u_cur), slot_cur = rd(u_slot, u_cur), g_cur = rd(u_g, u_cur);
-    int valid_cur = rd(u_valid, u_cur);
-    int tq_cur = query_token(kind_cur, g_cur);
-    int kind_n = 0, slot_n = -1, tq_n = -1, u_n = 0, g_n = 0, valid_n = a.L;
-    bf16x8_t qf[NC], qf_n[NC];
-    load_q(tq_cur, g_cur, qf);
+    if constexpr (D == 128) {
+        // ---- one K and one V buffer, two waves per SIMD ----
+        // At D = 128 a tile is 32 KB (K and V); with one buffer of each the
+        // workgroup holds 34 KB of LDS and at most 256 registers per wave, so
+        // four workgroups fit a CU and every SIMD runs two waves, which cover
+        // each other's waits.  Step f: wait for this wave's loads of tile f,
+        // then a barrier (the other wave's half has landed); read all K
+        // fragments, issue the score MFMAs, read all V fragments (into the
+        // registers the K fragments leave); a second barrier (both waves hold
+        // their fragments), after which the loads of tile f + 1 go into the
+        // same buffers while the softmax and the PV product of tile f run.  On
+        // a unit's last tile Q is free once the score MFMAs are issued, and
+        // the next unit's Q is loaded into the same registers.
+        auto tile_g = [&](int e) -> int { return rd(u_g, tile_unit(e)); };
+        const int wrow = __builtin_amdgcn_readfirstlane(4 * wave);   // the wave's rows 8r + wrow .. +3
+        const int lr = lane >> 4;
+        const uint32_t lo_k = (uint32_t)((lr * RS + swz_k(wrow + lr, lane & 15) * 8) * 2);
+        const uint32_t lo_v = (uint32_t)((lr * RS + swz_v(wrow + lr, lane & 15) * 8) * 2);
+        const uint32_t rsb = (uint32_t)(RS * 2);
+        const uint32_t kl = lds_addr(kbuf) + 256u * wrow, vl = lds_addr(vbuf) + 256u * wrow;
+        auto issue_tile = [&](const uint16_t* t, uint32_t lo, uint32_t lds) {
+            issue_rows128((const char*)(t + (int64_t)wrow * RS), rsb, lo, lds);
+        };
+        // Fragment offsets as a few base registers plus constants (instruction
+        // offsets): K chunk c >= 4 sits 64 elements after chunk c - 4 of the
+        // same row (the swizzle permutes pieces within groups of eight), and
+        // V column block db >= 2 sits 64 elements after db - 2.
+        int kb0[4], vb0[2];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf_n[c] = qf[c];
-    if (MASK == MASK_BITS) {
-        wbits_cur = load_bits(e0);
-        if (F > 1) wbits_n1 = load_bits(e1);
-    }
-
-    wait_vmcnt<0>();
-    issue_half<D>(ktile(g_cur, tile_j(e0)), 0, koffs, kl0);
-    issue_half<D>(vtile(g_cur, tile_j(e0)), 0, voffs, vl0);
-    if (F > 1) {
-        issue_half<D>(ktile(tile_g(e1), tile_j(e1)), 0, koffs, kl0 + TILE * 2);
-        wait_vmcnt<2 * Gm::LPT>();   // K(0) landed; V(0) and K(1) may still fly
-    } else {
-        wait_vmcnt<Gm::LPT>();
-    }
-    stage_barrier();
-    f32x16_t s_cur[2], s_nxt[2];
-    {
-        bf16x8_t kf[2][NC];
-        kread(kbuf, kf);
-        smma(kf, qf, s_cur);
-    }
-    reset();
-
-
-    // One step, written for a compile-time parity P = f & 1 so that the ring
-    // buffers' addresses fold into instruction offsets; the loop runs steps in
-    // pairs, swapping the roles of the two score register sets.  The running
-    // max of tile f is taken before the step's wait: it needs only registers,
-    // and it covers the latency of the previous step's output stores.
-    auto step = [&](auto parity, int f, f32x16_t (&s_now)[2], f32x16_t (&s_next)[2]) {
-        constexpr int P = decltype(parity)::value;
-        softmax_prep(e0, kind_cur, tq_cur, valid_cur, s_now, (e0 & kTileFirst) != 0);
-        wait_vmcnt<0>();
-        stage_barrier();
-        if (MASK == MASK_BITS && f + 2 < F) wbits_n2 = load_bits(e2);
-        // Q of the next unit: loaded during the first step of the current unit
-        // and, when the current unit ends here, moved in place for the scores
-        // of tile f + 1 -- before this step's direct loads are issued, so that
-        // any wait the compiler places for the Q loads cannot also wait for
-        // the direct loads in flight.
-        if (e0 & kTileFirst) {
-            const uint64_t rest = u_cur >= 63 ? 0ull : (live_units & ~((2ull << u_cur) - 1ull));
-            if (rest != 0) {
-                u_n = __builtin_ctzll(rest);
-                kind_n = rd(u_kind, u_n);
-                slot_n = rd(u_slot, u_n);
-                g_n = rd(u_g, u_n);
-                valid_n = rd(u_valid, u_n);
-                tq_n = query_token(kind_n, g_n);
-                load_q(tq_n, g_n, qf_n);
-            }
+        for (int c = 0; c < 4; ++c) kb0[c] = ql * D + swz_k(ql, 2 * c + hh) * 8;
+#pragma unroll
+        for (int d1 = 0; d1 < 2; ++d1) {
+            const int row = 4 * hh + (gi >> 2);
+            const int d0 = 32 * d1 + 16 * gsel + 4 * (gi & 3);
+            vb0[d1] = row * D + swz_v(row, d0 >> 3) * 8 + (d0 & 7);
         }
-        if (e0 & kTileLast) {
+        auto kread1 = [&](bf16x8_t (&kf)[2][NC]) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) qf[c] = qf_n[c];
-        }
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) asm volatile("" ::"v"(qf[c]));   // materialise qf here
-        const int e3 = f + 3 < F ? flat[f + 3] : 0;
-        // Fragment reads first; the direct loads of K(f + 2) and V(f + 1) are
-        // spread over the step (a burst of them right after the barrier makes
-        // every wave queue at the texture unit with nothing else to issue).
-        bf16x8_t kf[2][NC], va[4][NDB];
-        kread(kbuf + (1 - P) * TILE, kf);
-        vread(vbuf + P * TILE, va);
-        if (f + 2 < F) issue_half<D>(ktile(tile_g(e2), tile_j(e2)), 0, koffs, kl0 + P * TILE * 2);
-        // Scores of tile f + 1 (past the end they read a stale buffer and are
-        // discarded), interleaved by the scheduler with the softmax of tile f.
+                for (int c = 0; c < NC; ++c)
+                    kf[kb][c] = as_bf16x8(*(const u32x4_t*)(kbuf + kb0[c & 3] + (c >> 2) * 64 + kb * 32 * D));
+        };
+        auto vread1 = [&](bf16x8_t (&va)[4][NDB]) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const uint16_t* p = vbuf + vb0[db & 1] + (db >> 1) * 64 + 16 * c * D;
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(p));
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(p + 8 * D));
+                    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+                    const u32x4_t lh = {l2.x, l2.y, h2.x, h2.y};
+                    va[c][db] = as_bf16x8(lh);
+                }
+        };
+
+        int e0 = flat[0];
+        int u_cur = tile_unit(e0);
+        int kind_cur = rd(u_kind, u_cur), slot_cur = rd(u_slot, u_cur), g_cur = rd(u_g, u_cur);
+        int valid_cur = rd(u_valid, u_cur);
+        int tq_cur = query_token(kind_cur, g_cur);
+        bf16x8_t qf[NC];
+        load_q(tq_cur, g_cur, qf);
+        if (MASK == MASK_BITS) wbits_cur = load_bits(e0);
+        issue_tile(ktile(g_cur, tile_j(e0)), lo_k, kl);
+        issue_tile(vtile(g_cur, tile_j(e0)), lo_v, vl);
+        reset();
         using C0 = std::integral_constant<int, 0>;
         using C2 = std::integral_constant<int, 2>;
-        u32x4_t pA[2], pB[2];
-        smma(kf, qf, s_next);
-        softmax_exp(s_now, C0(), pA);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8 + 8 * NDB, 0);   // LDS reads first
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
+        for (int f = 0; f < F; ++f) {
+            const int e1 = f + 1 < F ? flat[f + 1] : 0;
+            wait_vmcnt<0>();   // this wave's loads of tile f (and Q, mask bits)
+            stage_barrier();   // the other wave's
+            f32x16_t s[2];
+            {
+                bf16x8_t kf[2][NC];
+                kread1(kf);
+                smma(kf, qf, s);
+            }
+            bf16x8_t va[4][NDB];
+            vread1(va);
+            wait_lgkm0();      // this wave's fragment reads are done,
+            stage_barrier();   // and the other wave's: the buffers take tile f + 1
+            if (f + 1 < F) {
+                const int g1 = tile_g(e1), j1 = tile_j(e1);
+                issue_tile(ktile(g1, j1), lo_k, kl);
+                issue_tile(vtile(g1, j1), lo_v, vl);
+                if (MASK == MASK_BITS) wbits_n1 = load_bits(e1);
+            }
+            const bool last = (e0 & kTileLast) != 0;
+            int u_n = u_cur, kind_n = kind_cur, slot_n = slot_cur, g_n = g_cur, valid_n = valid_cur, tq_n = tq_cur;
+            if (last) {
+                const uint64_t rest = u_cur >= 63 ? 0ull : (live_units & ~((2ull << u_cur) - 1ull));
+                if (rest != 0) {
+                    u_n = __builtin_ctzll(rest);
+                    kind_n = rd(u_kind, u_n);
+                    slot_n = rd(u_slot, u_n);
+                    g_n = rd(u_g, u_n);
+                    valid_n = rd(u_valid, u_n);
+                    tq_n = query_token(kind_n, g_n);
+                    load_q(tq_n, g_n, qf);   // the score MFMAs above have taken Q
+                }
+            }
+            softmax_prep(e0, kind_cur, tq_cur, valid_cur, s, (e0 & kTileFirst) != 0);
+            u32x4_t pA[2], pB[2];
+            softmax_exp(s, C0(), pA);
+            pv(va, C0(), pA);
+            softmax_exp(s, C2(), pB);
+            pv(va, C2(), pB);
+            if (last) {
+                // ---- unit done: O = acc / l, LSE = (m + log2 l) ln 2 ----
+                const float lt = pair_sum(l);
+                const float inv = lt > 0.f ? 1.f / lt : 0.f;
+                const float lse_v = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+                store_unit(slot_cur, tq_cur, g_cur, rloc, o, inv, lse_v);
+                reset();
+                u_cur = u_n;
+                kind_cur = kind_n;
+                slot_cur = slot_n;
+                tq_cur = tq_n;
+                g_cur = g_n;
+                valid_cur = valid_n;
+            }
+            if (MASK == MASK_BITS) wbits_cur = wbits_n1;
+            e0 = e1;
         }
-        if (f + 1 < F) issue_half<D>(vtile(tile_g(e1), tile_j(e1)), 0, voffs, vl0 + (1 - P) * TILE * 2);
-        pv(va, C0(), pA);
-        softmax_exp(s_now, C2(), pB);
-#pragma unroll
-        for (int i = 0; i < 2 * NDB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // then eight VALU
-        }
-        pv(va, C2(), pB);
-        if (e0 & kTileLast) {
-            // ---- unit done: O = acc / l, LSE = (m + log2 l) ln 2 ----
-            const float lt = pair_sum(l);
-            const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            const float lse_v = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
-            store_unit(slot_cur, tq_cur, g_cur, rloc, o, inv, lse_v);
-            reset();
-            u_cur = u_n;
-            kind_cur = kind_n;
-            slot_cur = slot_n;
-            tq_cur = tq_n;
-            g_cur = g_n;
-            valid_cur = valid_n;
-        }
-        e0 = e1;
-        e1 = e2;
-        e2 = e3;
+    } else {
+        // ---- software pipeline over the flat tile list ----
+        // Tile f's K sits in K buffer f & 1 and its V in V buffer f & 1.  Step f
+        // computes the scores of tile f + 1 (MFMA) while it runs the softmax of
+        // tile f (VALU), then accumulates tile f's PV product.  During step f the
+        // direct loads of K(f + 2) and V(f + 1) are in flight, into the buffers
+        // whose last readers (step f - 1) are behind the step's barrier.  A unit's
+        // Q is loaded during the first step of the unit before it, so a unit
+        // boundary costs no load latency.
+        int e0 = flat[0];
+        int e1 = F > 1 ? flat[1] : 0;
+        int e2 = F > 2 ? flat[2] : 0;
+        // group of a flat tile entry's unit
+        auto tile_g = [&](int e) -> int { return rd(u_g, tile_unit(e)); };
+        int u_cur = tile_unit(e0);
+        int kind_cur = rd(u_kind, u_cur), slot_cur = rd(u_slot, u_cur), g_cur = rd(u_g, u_cur);
+        int valid_cur = rd(u_valid, u_cur);
+        int tq_cur = query_token(kind_cur, g_cur);
+        int kind_n = 0, slot_n = -1, tq_n = -1, u_n = 0, g_n = 0, valid_n = a.L;
+        bf16x8_t qf[NC], qf_n[NC];
+        load_q(tq_cur, g_cur, qf);
+    #pragma unroll
+        for (int c = 0; c < NC; ++c) qf_n[c] = qf[c];
         if (MASK == MASK_BITS) {
-            wbits_cur = wbits_n1;
-            wbits_n1 = wbits_n2;
+            wbits_cur = load_bits(e0);
+            if (F > 1) wbits_n1 = load_bits(e1);
         }
-    };
-    for (int f = 0; f < F; f += 2) {
-        step(std::integral_constant<int, 0>(), f, s_cur, s_nxt);
-        if (f + 1 < F) step(std::integral_constant<int, 1>(), f + 1, s_nxt, s_cur);
+
+        wait_vmcnt<0>();
+        issue_half<D>(ktile(g_cur, tile_j(e0)), 0, koffs, kl0);
+        issue_half<D>(vtile(g_cur, tile_j(e0)), 0, voffs, vl0);
+        if (F > 1) {
+            issue_half<D>(ktile(tile_g(e1), tile_j(e1)), 0, koffs, kl0 + TILE * 2);
+            wait_vmcnt<2 * Gm::LPT>();   // K(0) landed; V(0) and K(1) may still fly
+        } else {
+            wait_vmcnt<Gm::LPT>();
+        }
+        stage_barrier();
+        f32x16_t s_cur[2], s_nxt[2];
+        {
+            bf16x8_t kf[2][NC];
+            kread(kbuf, kf);
+            smma(kf, qf, s_cur);
+        }
+        reset();
+
+
+        // One step, written for a compile-time parity P = f & 1 so that the ring
+        // buffers' addresses fold into instruction offsets; the loop runs steps in
+        // pairs, swapping the roles of the two score register sets.  The running
+        // max of tile f is taken before the step's wait: it needs only registers,
+        // and it covers the latency of the previous step's output stores.
+        auto step = [&](auto parity, int f, f32x16_t (&s_now)[2], f32x16_t (&s_next)[2]) {
+            constexpr int P = decltype(parity)::value;
+            softmax_prep(e0, kind_cur, tq_cur, valid_cur, s_now, (e0 & kTileFirst) != 0);
+            wait_vmcnt<0>();
+            stage_barrier();
+            if (MASK == MASK_BITS && f + 2 < F) wbits_n2 = load_bits(e2);
+            // Q of the next unit: loaded during the first step of the current unit
+            // and, when the current unit ends here, moved in place for the scores
+            // of tile f + 1 -- before this step's direct loads are issued, so that
+            // any wait the compiler places for the Q loads cannot also wait for
+            // the direct loads in flight.
+            if (e0 & kTileFirst) {
+                const uint64_t rest = u_cur >= 63 ? 0ull : (live_units & ~((2ull << u_cur) - 1ull));
+                if (rest != 0) {
+                    u_n = __builtin_ctzll(rest);
+                    kind_n = rd(u_kind, u_n);
+                    slot_n = rd(u_slot, u_n);
+                    g_n = rd(u_g, u_n);
+                    valid_n = rd(u_valid, u_n);
+                    tq_n = query_token(kind_n, g_n);
+                    load_q(tq_n, g_n, qf_n);
+                }
+            }
+            if (e0 & kTileLast) {
+    #pragma unroll
+                for (int c = 0; c < NC; ++c) qf[c] = qf_n[c];
+            }
+    #pragma unroll
+            for (int c = 0; c < NC; ++c) asm volatile("" ::"v"(qf[c]));   // materialise qf here
+            const int e3 = f + 3 < F ? flat[f + 3] : 0;
+            // Fragment reads first; the direct loads of K(f + 2) and V(f + 1) are
+            // spread over the step (a burst of them right after the barrier makes
+            // every wave queue at the texture unit with nothing else to issue).
+            bf16x8_t kf[2][NC], va[4][NDB];
+            kread(kbuf + (1 - P) * TILE, kf);
+            vread(vbuf + P * TILE, va);
+            if (f + 2 < F) issue_half<D>(ktile(tile_g(e2), tile_j(e2)), 0, koffs, kl0 + P * TILE * 2);
+            // Scores of tile f + 1 (past the end they read a stale buffer and are
+            // discarded), interleaved by the scheduler with the softmax of tile f.
+            using C0 = std::integral_constant<int, 0>;
+            using C2 = std::integral_constant<int, 2>;
+            u32x4_t pA[2], pB[2];
+            smma(kf, qf, s_next);
+            softmax_exp(s_now, C0(), pA);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8 + 8 * NDB, 0);   // LDS reads first
+    #pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // then one MFMA
+            }
+            if (f + 1 < F) issue_half<D>(vtile(tile_g(e1), tile_j(e1)), 0, voffs, vl0 + (1 - P) * TILE * 2);
+            pv(va, C0(), pA);
+            softmax_exp(s_now, C2(), pB);
+    #pragma unroll
+            for (int i = 0; i < 2 * NDB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // then eight VALU
+            }
+            pv(va, C2(), pB);
+            if (e0 & kTileLast) {
+                // ---- unit done: O = acc / l, LSE = (m + log2 l) ln 2 ----
+                const float lt = pair_sum(l);
+                const float inv = lt > 0.f ? 1.f / lt : 0.f;
+                const float lse_v = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+                store_unit(slot_cur, tq_cur, g_cur, rloc, o, inv, lse_v);
+                reset();
+                u_cur = u_n;
+                kind_cur = kind_n;
+                slot_cur = slot_n;
+                tq_cur = tq_n;
+                g_cur = g_n;
+                valid_cur = valid_n;
+            }
+            e0 = e1;
+            e1 = e2;
+            e2 = e3;
+            if (MASK == MASK_BITS) {
+                wbits_cur = wbits_n1;
+                wbits_n1 = wbits_n2;
+            }
+        };
+        for (int f = 0; f < F; f += 2) {
+            step(std::integral_constant<int, 0>(), f, s_cur, s_nxt);
+            if (f + 1 < F) step(std::integral_constant<int, 1>(), f + 1, s_nxt, s_cur);
+        }
     }
 }
 
@@ -1688,9 +1858,9 @@ int fwd_bf16_ctas_per_cu(int head_dim, bool two_wave) {
         : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<128, MASK_NONE>, kThreads, 0);
     if (e != hipSuccess || n < 1) n = 1;
     // Measured on MI355X: with 32 KiB of LDS per workgroup only 4 workgroups
-    // are resident per CU (the occupancy query reports 5); 64 KiB gives 2.
-    const int cap = head_dim == 64 ? 4 : 2;
-    return n < cap ? n : cap;
+    // are resident per CU (the occupancy query reports 5).  Both widths hold
+    // about 34 KiB: four per CU, two waves per SIMD.
+    return n < 4 ? n : 4;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
