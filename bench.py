@@ -229,7 +229,7 @@ def run_candidates(args, wl, inp, bs, torch, np):
         bound, achieved, peak, unit = "hbm", kern_gbps, PEAK_HBM_GBPS, "GB/s"
     else:
         bound, achieved, peak, unit = "alu", kern_tflops, PEAK_F32_VECTOR_TFLOPS, "TFLOP/s"
-    kname = "cand_attention_kernel"
+    kname = "cand_attention2_kernel" if kc <= 32 else "cand_attention_kernel"   # two queries per wave up to k = 32
     traffic = traffic_from_profile(wl.name, kname, CAND_KERNEL_SOURCE)
     result = {
         "metric": METRIC, "value": round(B * L / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,

@@ -13,15 +13,18 @@
 // output); the fp64 chains are latency-bound (see the kernel and the design
 // notes for the variants measured).
 //
-// cand_attention_kernel: one wave per (batch, head, query).  Lane j < k holds
-// candidate position j; a position seen in a lower lane is dropped (the
-// candidate set).  Each remaining lane takes the in-order fp32 score q.k of
-// its key (products added in order of d from +0, as the top-keep selection
-// does), the lanes are ranked by (score descending, position ascending) and
-// the first `keep` are kept.  The softmax of scale * score over the kept keys
-// then weighs their V rows: every lane owns D/64 output columns and walks the
-// kept keys, eight V rows per round of loads, so each row is read once,
-// coalesced.
+// The importance evaluation keeps, per (batch, head, query), the `keep` best
+// distinct candidates by the in-order fp32 score q.k of their keys (products
+// added in order of d from +0, as the top-keep selection does), the lower
+// position first on equal scores; the softmax of scale * score over the kept
+// keys then weighs their V rows.  Two kernels compute it:
+// * cand_attention2_kernel (k <= 32): two queries per wave, one candidate per
+//   lane; the ranking is a bitonic sort within each half-wave (see there);
+// * cand_attention_kernel (k up to 64): one wave per query.  Lane j < k holds
+//   candidate position j; a position seen in a lower lane is dropped, and each
+//   lane counts the lanes ahead of it.  Every lane owns D/64 output columns
+//   and walks the kept keys, eight V rows per round of loads, so each row is
+//   read once, coalesced.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -36,6 +39,7 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 
 __device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
@@ -193,6 +197,206 @@ __global__ __launch_bounds__(256) void cand_attention_kernel(const uint16_t* __r
     }
 }
 
+// The value of lane (j ^ X) of the same half-wave (ds_swizzle, bit-mask mode:
+// and-mask 31, or-mask 0, xor-mask X).
+template <int X>
+__device__ __forceinline__ uint32_t swz_xor(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (X << 10));
+}
+
+// One compare-exchange stage of a bitonic sort, descending, over the 32 lanes
+// of each half-wave: lane j meets lane j ^ X, and of the pair the lane with
+// bit B (the highest bit of X) clear keeps the larger value.  The comparison
+// is one ballot; the lanes' side is a constant lane mask.
+template <int X>
+__device__ __forceinline__ uint64_t bitonic_cx(uint64_t v) {
+    constexpr int B = X >= 16 ? 16 : X >= 8 ? 8 : X >= 4 ? 4 : X >= 2 ? 2 : 1;
+    constexpr uint32_t low32 = B == 16 ? 0x0000ffffu : B == 8 ? 0x00ff00ffu : B == 4 ? 0x0f0f0f0fu
+                             : B == 2 ? 0x33333333u : 0x55555555u;   // lanes j with bit B clear
+    constexpr uint64_t low = ((uint64_t)low32 << 32) | low32;
+    const uint32_t lo = swz_xor<X>((uint32_t)v), hi = swz_xor<X>((uint32_t)(v >> 32));
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    const uint64_t gt = __builtin_amdgcn_ballot_w64(v > o);
+    return __builtin_amdgcn_inverse_ballot_w64(~(gt ^ low)) ? v : o;   // larger to the low side
+}
+
+// Sort of the 32 values of each half-wave, descending (lane 0 the largest):
+// for each block size, a mirrored stage (j meets the lane at the same distance
+// from the block's other end) and then the halving stages.
+__device__ __forceinline__ uint64_t bitonic_sort32(uint64_t v) {
+    v = bitonic_cx<1>(v);
+    v = bitonic_cx<3>(v);
+    v = bitonic_cx<1>(v);
+    v = bitonic_cx<7>(v);
+    v = bitonic_cx<2>(v);
+    v = bitonic_cx<1>(v);
+    v = bitonic_cx<15>(v);
+    v = bitonic_cx<4>(v);
+    v = bitonic_cx<2>(v);
+    v = bitonic_cx<1>(v);
+    v = bitonic_cx<31>(v);
+    v = bitonic_cx<8>(v);
+    v = bitonic_cx<4>(v);
+    v = bitonic_cx<2>(v);
+    return bitonic_cx<1>(v);
+}
+
+// Sum over the 32 lanes of each half-wave.
+__device__ __forceinline__ float half_sum(float x) {
+    x += __uint_as_float(swz_xor<16>(__float_as_uint(x)));
+    x += __uint_as_float(swz_xor<8>(__float_as_uint(x)));
+    x += __uint_as_float(swz_xor<4>(__float_as_uint(x)));
+    x += __uint_as_float(swz_xor<2>(__float_as_uint(x)));
+    x += __uint_as_float(swz_xor<1>(__float_as_uint(x)));
+    return x;
+}
+
+// Two queries per wave, for k <= 32: half-wave hq = lane / 32 holds query
+// 2 w + hq and its lane j = lane % 32 candidate j.  Each lane computes the
+// in-order fp32 score of its candidate (the same products and order as the
+// one-query kernel), then the half-wave sorts the pairs (order key of the
+// score, position) descending -- score first, the lower position first on
+// equal scores -- with a bitonic network of lane swaps.  Repeats of a
+// position carry equal pairs, so they become neighbours and all but the first
+// drop out; a lane's rank is the number of distinct candidates before it, and
+// the first `keep` are kept.  The largest kept score is then in lane 0 of the
+// half.  Each lane owns D / 32 output columns and walks the kept keys of its
+// half, V rows read whole by the 32 lanes.
+template <int D>
+__global__ __launch_bounds__(256) void cand_attention2_kernel(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ kk,
+                                                              const uint16_t* __restrict__ v,
+                                                              const int32_t* __restrict__ pos, int H, int L, int k,
+                                                              int keep, float scale, uint16_t* __restrict__ out,
+                                                              float* __restrict__ lse, int32_t* __restrict__ kept_out) {
+    constexpr int DH = D / 32;   // output columns per lane
+    const int lane = threadIdx.x & 63;
+    const int hq = lane >> 5, j = lane & 31;
+    // grid: x = queries of one (batch, head) group in eights, y = the group
+    const int g = blockIdx.y;        // b * H + h
+    const int t0 = blockIdx.x * 8 + (threadIdx.x >> 6) * 2;
+    if (t0 >= L) return;             // the whole wave
+    const int t = t0 + hq;
+    const bool live = t < L;         // the second half of the last wave may be past the end
+    const int b = g / H;
+    const int64_t qi = (int64_t)g * L + (live ? t : t0);   // row of Q, O and LSE
+    const int64_t prow = (int64_t)b * L + (live ? t : t0); // row of the positions
+    const uint16_t* kb = kk + (size_t)g * L * D;
+    const uint16_t* vb = v + (size_t)g * L * D;
+    int p = (live && j < k) ? pos[(size_t)prow * k + j] : -1;
+    if (p < 0 || p >= L) p = -1;
+    // in-order fp32 score of this lane's key
+    float s = 0.f;
+    if (p >= 0) {
+        const uint16_t* qr = q + (size_t)qi * D;
+        const uint16_t* kr = kb + (size_t)p * D;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const u32x4_t qw = *(const u32x4_t*)(qr + 8 * c);
+            const u32x4_t kw = *(const u32x4_t*)(kr + 8 * c);
+            const uint32_t qe[4] = {qw.x, qw.y, qw.z, qw.w}, ke[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s = fmaf(lo16(qe[e]), lo16(ke[e]), s);
+                s = fmaf(hi16(qe[e]), hi16(ke[e]), s);
+            }
+        }
+    }
+    // sort (order key, complement of the position) descending; no candidate:
+    // key 0 and the largest position, below every candidate
+    const uint32_t pk = p >= 0 ? (uint32_t)p : 0x7fffffffu;
+    uint64_t sv = ((uint64_t)(p >= 0 ? order_key(s) : 0u) << 32) | (uint32_t)~pk;
+    sv = bitonic_sort32(sv);
+    const uint32_t key = (uint32_t)(sv >> 32);
+    const int ps = (int)~(uint32_t)sv;           // position of this lane's pair after the sort
+    const bool valid = ps != 0x7fffffff;
+    const int prev = __shfl_up(ps, 1);           // the pair before (lane j - 1 of the half for j > 0)
+    const bool distinct = valid && !(j > 0 && prev == ps);
+    const uint32_t dm = (uint32_t)(__ballot(distinct) >> (32 * hq));
+    const int rank = __builtin_popcount(dm & ((1u << j) - 1u));
+    const bool kept = distinct && rank < keep;
+    // the score back from its order key (exact, -0 aside; a NaN stays a NaN)
+    const float ss = __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+    const float z = kept ? ss * scale * 1.4426950408889634f : -INFINITY;
+    const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), 0));
+    const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), 32));
+    const float m = hq ? m1 : m0;                // the largest kept score of the half (lane 0 of the half)
+    const float pw = kept ? __builtin_amdgcn_exp2f(z - m) : 0.f;   // z - m <= 0
+    const float lsum = half_sum(pw);
+    // the kept V rows of both halves, four at a time
+    const uint64_t km = __ballot(kept);
+    uint32_t mlo = (uint32_t)km, mhi = (uint32_t)(km >> 32);
+    float acc[DH];
+#pragma unroll
+    for (int e = 0; e < DH; ++e) acc[e] = 0.f;
+    constexpr int VB = 4;
+    while (mlo | mhi) {
+        int pi[VB];
+        float wi[VB];
+#pragma unroll
+        for (int n = 0; n < VB; ++n) {
+            const int il = mlo ? __builtin_ctz(mlo) : 0, ih = mhi ? 32 + __builtin_ctz(mhi) : 32;
+            const int pl = mlo ? __builtin_amdgcn_readlane(ps, il) : -1;
+            const int ph = mhi ? __builtin_amdgcn_readlane(ps, ih) : -1;
+            const float wl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), il));
+            const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), ih));
+            pi[n] = hq ? ph : pl;
+            wi[n] = hq ? wh : wl;
+            mlo &= mlo - 1u;
+            mhi &= mhi - 1u;
+        }
+        uint32_t vv[VB][DH / 2 > 0 ? DH / 2 : 1];
+#pragma unroll
+        for (int n = 0; n < VB; ++n) {
+            if (pi[n] >= 0) {
+                const uint16_t* vr = vb + (size_t)pi[n] * D + DH * j;
+                if constexpr (DH == 2) {
+                    vv[n][0] = *(const uint32_t*)vr;
+                } else {
+                    const u32x2_t w2 = *(const u32x2_t*)vr;
+                    vv[n][0] = w2.x;
+                    vv[n][1] = w2.y;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < DH / 2; ++e) vv[n][e] = 0u;
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < VB; ++n)
+            if (pi[n] >= 0)
+#pragma unroll
+                for (int e = 0; e < DH / 2; ++e) {
+                    acc[2 * e] = fmaf(wi[n], lo16(vv[n][e]), acc[2 * e]);
+                    acc[2 * e + 1] = fmaf(wi[n], hi16(vv[n][e]), acc[2 * e + 1]);
+                }
+    }
+    if (!live) return;
+    const bool any = ((km >> (32 * hq)) & 0xffffffffull) != 0;
+    // no kept key (every position outside the sequence): O = 0, LSE = -inf
+    const float inv = any ? 1.f / lsum : 0.f;
+    uint16_t* orow = out + (size_t)qi * D + DH * j;
+    if constexpr (DH == 2) {
+        *(uint32_t*)orow = pack2(acc[0] * inv, acc[1] * inv);
+    } else {
+        u32x2_t w2;
+        w2.x = pack2(acc[0] * inv, acc[1] * inv);
+        w2.y = pack2(acc[2] * inv, acc[3] * inv);
+        *(u32x2_t*)orow = w2;
+    }
+    if (j == 0) lse[qi] = any ? (m + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
+    if (kept_out) {
+        // ascending kept positions, -1 past their count
+        const uint32_t hm = (uint32_t)(km >> (32 * hq));
+        const int n_kept = __builtin_popcount(hm);
+        int slot = 0;
+        for (uint32_t mm = hm; mm; mm &= mm - 1u) slot += __shfl(ps, 32 * hq + __builtin_ctz(mm)) < ps ? 1 : 0;
+        int32_t* ko = kept_out + (size_t)qi * keep;
+        if (kept) ko[slot] = ps;
+        if (j >= n_kept && j < keep) ko[j] = -1;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_cand_positions(const void* x, const float* w, const float* bias, int B, int L, int C, int k,
@@ -217,6 +421,18 @@ hipError_t launch_cand_attention(const void* q, const void* k, const void* v, co
     const int64_t grid = (nq + 3) / 4;
     if (grid == 0) return hipSuccess;
     // given events, the dispatch records the kernel's own start and stop
+    if (n_cand <= 32) {
+        const dim3 grid2((unsigned)((L + 7) / 8), (unsigned)(B * H));   // two queries per wave
+        if (D == 64)
+            hipExtLaunchKernelGGL(cand_attention2_kernel<64>, grid2, dim3(256), 0, s, before, after, 0,
+                                  (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, pos, H, L, n_cand, keep,
+                                  scale, (uint16_t*)out, lse, kept);
+        else
+            hipExtLaunchKernelGGL(cand_attention2_kernel<128>, grid2, dim3(256), 0, s, before, after,
+                                  0, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, pos, H, L, n_cand,
+                                  keep, scale, (uint16_t*)out, lse, kept);
+        return hipGetLastError();
+    }
     if (D == 64)
         hipExtLaunchKernelGGL(cand_attention_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, before, after, 0,
                               (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, pos, H, L, n_cand, keep,
