@@ -5,7 +5,9 @@ for bit: the positions come from the fp64 fixed-order convolution on both
 sides, the kept keys from the in-order fp32 ranking.  The attention output
 is compared with the fp64 oracle at the bf16 tolerances (O 2e-2, LSE 1e-3).
 Cases: several (C, k) shapes including a k that is not a power of two and
-k = 1 and 64, a sequence length that does not fill the last workgroup,
+k = 1 and 64 (positions), forward at k = 20, 32, 48 and 64 (the two-queries-
+per-wave kernel up to k = 32, the one-query kernel above), a sequence length
+that does not fill the last workgroup,
 rounding at the ends of the sequence and a NaN input row, positions given
 directly with many repeats and values outside the sequence, keep = 1 and
 keep = k, integer-valued scores (ties), D = 64 and 128, and the benchmark
@@ -148,6 +150,20 @@ def test_forward_from_generated_positions(D, keep):
     x, w, bias = _generator(B, L, C, k, seed=D + keep)
     pos = _device_positions(x, w, bias)
     q, kk, v = _inputs(B, H, L, D, seed=3 * D + keep)
+    out, lse, kept = _run(q, kk, v, pos, keep)
+    _check_kept(q, kk, pos, keep, kept, tag)
+    _check_forward(q, kk, v, pos, keep, out, lse, tag)
+
+
+@pytest.mark.parametrize("D,k,keep", [(64, 20, 5), (64, 48, 12), (128, 64, 16)])
+def test_forward_other_candidate_counts(D, k, keep):
+    """k not a power of two (two queries per wave) and k above 32 (one query per wave)."""
+    B, H, L, C = 1, 2, 200, 24
+    tag = f"candidates D={D} k={k} keep={keep}"
+    _say(tag)
+    x, w, bias = _generator(B, L, C, k, seed=D + k + keep)
+    pos = _device_positions(x, w, bias)
+    q, kk, v = _inputs(B, H, L, D, seed=5 * k + keep)
     out, lse, kept = _run(q, kk, v, pos, keep)
     _check_kept(q, kk, pos, keep, kept, tag)
     _check_forward(q, kk, v, pos, keep, out, lse, tag)
