@@ -9,9 +9,10 @@
 // point, so the sum has one fixed evaluation: fp64, from bias[j], adding the
 // products of tap u = 0, 1, 2 in turn and, within a tap, of channel c = 0 ..
 // C - 1.  A bf16 x fp32 product is exact in fp64 (fused or not); taps
-// outside the sequence add nothing.  A thread runs the chain of one (token,
-// output); the fp64 chains are latency-bound (see the kernel and the design
-// notes for the variants measured).
+// outside the sequence add nothing.  cand_positions4_kernel (k % 4 == 0,
+// C % 8 == 0) runs the four chains of outputs 4g .. 4g + 3 of one token per
+// thread, so that each x value is loaded and converted once for four fused
+// multiply-adds; cand_positions_kernel runs one chain per thread otherwise.
 //
 // The importance evaluation keeps, per (batch, head, query), the `keep` best
 // distinct candidates by the in-order fp32 score q.k of their keys (products
@@ -80,6 +81,56 @@ __global__ __launch_bounds__(kPosThreads) void cand_positions_kernel(const uint1
     if (acc != acc) p = 0;
     else p = (int)fmin(fmax(rint(acc), 0.0), (double)(L - 1));
     pos[((size_t)b * L + t) * k + j] = p;
+}
+
+// Four outputs per thread (k % 4 == 0, C % 8 == 0, x 16-byte aligned): thread
+// (token t, group g) runs the chains of outputs 4g .. 4g + 3, each in the same
+// fixed order as above.  Per step of eight channels it loads the eight x
+// values of the row once (16 bytes, one conversion each, shared by the four
+// chains) and the four weights of each channel as one float4.
+__global__ __launch_bounds__(kPosThreads) void cand_positions4_kernel(const uint16_t* __restrict__ x,
+                                                                      const float* __restrict__ w,
+                                                                      const float* __restrict__ bias, int L, int C,
+                                                                      int k, int gp, int32_t* __restrict__ pos) {
+    const int T = kPosThreads / gp;   // tokens per workgroup, gp lanes (output groups) per token
+    const int tiles = (L + T - 1) / T;
+    const int b = blockIdx.x / tiles;
+    const int g = threadIdx.x % gp;
+    const int t = (blockIdx.x % tiles) * T + threadIdx.x / gp;
+    if (4 * g >= k || t >= L) return;
+    const uint16_t* xb = x + (size_t)b * L * C;
+    double acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = (double)bias[4 * g + i];
+#pragma unroll 1
+    for (int u = 0; u < 3; ++u) {
+        const int row = t + u - 1;
+        if (row < 0 || row >= L) continue;   // padding: the tap adds nothing
+        const uint16_t* xr = xb + (size_t)row * C;
+        const float* wu = w + (size_t)u * C * k + 4 * g;
+#pragma unroll 2
+        for (int c0 = 0; c0 < C; c0 += 8) {
+            const u32x4_t xv = *(const u32x4_t*)(xr + c0);
+            float4 wv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wv[i] = *(const float4*)(wu + (size_t)(c0 + i) * k);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double xd = (double)((i & 1) ? hi16(xw[i >> 1]) : lo16(xw[i >> 1]));
+                acc[0] = fma(xd, (double)wv[i].x, acc[0]);
+                acc[1] = fma(xd, (double)wv[i].y, acc[1]);
+                acc[2] = fma(xd, (double)wv[i].z, acc[2]);
+                acc[3] = fma(xd, (double)wv[i].w, acc[3]);
+            }
+        }
+    }
+    int32_t* pr = pos + ((size_t)b * L + t) * k + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double a = acc[i];
+        pr[i] = a != a ? 0 : (int)fmin(fmax(rint(a), 0.0), (double)(L - 1));
+    }
 }
 
 // unsigned key in score order: -0 and +0 alike, NaN below everything
@@ -402,6 +453,16 @@ __global__ __launch_bounds__(256) void cand_attention2_kernel(const uint16_t* __
 hipError_t launch_cand_positions(const void* x, const float* w, const float* bias, int B, int L, int C, int k,
                                  int32_t* pos, hipStream_t s) {
     if (k < 1 || k > kMaxCandidates || C < 1) return hipErrorInvalidValue;
+    if (k % 4 == 0 && C % 8 == 0 && ((uintptr_t)x & 15) == 0) {
+        int gp = 1;
+        while (gp < k / 4) gp <<= 1;
+        const int T = kPosThreads / gp;
+        const int64_t grid = (int64_t)B * ((L + T - 1) / T);
+        if (grid == 0) return hipSuccess;
+        hipLaunchKernelGGL(cand_positions4_kernel, dim3((unsigned)grid), dim3(kPosThreads), 0, s, (const uint16_t*)x,
+                           w, bias, L, C, k, gp, pos);
+        return hipGetLastError();
+    }
     int kp = 1;
     while (kp < k) kp <<= 1;
     const int T = kPosThreads / kp;
