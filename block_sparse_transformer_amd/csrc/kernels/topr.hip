@@ -221,8 +221,11 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
     constexpr int D = 64;
     constexpr int QB = kKsBatch;
     constexpr int NTILE = kKsWaves * KPL;          // key tiles a workgroup covers
-    __shared__ uint32_t hist[QB][256];
-    __shared__ uint32_t s_digit[QB], s_above[QB];
+    // two sets of histograms and scan results, used by alternate passes: a
+    // pass's scan clears its own set for the pass after next, so a pass needs
+    // no barrier before its atomics and none after its results are read
+    __shared__ uint32_t hist[2][QB][256];
+    __shared__ uint32_t s_digit[2][QB], s_above[2][QB];
     __shared__ uint32_t eqc[QB][NTILE];             // keys equal to T per (query, tile), then their prefix
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -246,6 +249,8 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
         }
     }
     const uint64_t lt_mask = (1ull << lane) - 1ull;
+    for (int x = tid; x < 2 * QB * 256; x += kKsThreads) (&hist[0][0][0])[x] = 0u;
+    __syncthreads();
 
     for (int t0 = c0; t0 < c1; t0 += QB) {
         constexpr int nq = QB;   // chunks and L are multiples of QB: every batch is full
@@ -324,23 +329,26 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
 #pragma unroll
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
-            for (int x = tid; x < QB * 256; x += kKsThreads) hist[x / 256][x % 256] = 0u;
-            __syncthreads();
+            const int hb = pass & 1;
 #pragma unroll
             for (int i = 0; i < QB; ++i)
 #pragma unroll
                 for (int j = 0; j < KPL; ++j) {
                     const uint32_t kk = key[i][j];
                     const bool match = pass == 0 || (kk >> (shift + 8)) == (prefix[i] >> (shift + 8));
-                    if (i < nq && kvalid[j] && match) atomicAdd(&hist[i][(kk >> shift) & 255u], 1u);
+                    if (i < nq && kvalid[j] && match) atomicAdd(&hist[hb][i][(kk >> shift) & 255u], 1u);
                 }
             __syncthreads();
             if (wave < nq) {
-                // one wave per query: lane l owns bins 4l .. 4l + 3
+                // one wave per query: lane l owns bins 4l .. 4l + 3, read and cleared
                 const int qi = wave;
                 uint32_t h[4], own = 0;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) { h[b] = hist[qi][4 * lane + b]; own += h[b]; }
+                for (int b = 0; b < 4; ++b) {
+                    h[b] = hist[hb][qi][4 * lane + b];
+                    own += h[b];
+                    hist[hb][qi][4 * lane + b] = 0u;
+                }
                 uint32_t suffix = own;
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {
@@ -355,8 +363,8 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
 #pragma unroll
                 for (int b = 3; b >= 0; --b) {
                     if (above < (uint32_t)nd && (uint32_t)nd <= above + h[b]) {
-                        s_digit[qi] = (uint32_t)(4 * lane + b);
-                        s_above[qi] = above;
+                        s_digit[hb][qi] = (uint32_t)(4 * lane + b);
+                        s_above[hb][qi] = above;
                     }
                     above += h[b];
                 }
@@ -365,10 +373,9 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
 #pragma unroll
             for (int i = 0; i < QB; ++i)
                 if (i < nq) {
-                    prefix[i] |= s_digit[i] << shift;
-                    need[i] -= (int)s_above[i];
+                    prefix[i] |= s_digit[hb][i] << shift;
+                    need[i] -= (int)s_above[hb][i];
                 }
-            __syncthreads();
         }
 
         // ---- ties: rank keys equal to T in index order (tile, lane) ----
