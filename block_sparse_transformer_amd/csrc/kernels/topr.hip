@@ -226,6 +226,7 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
     // no barrier before its atomics and none after its results are read
     __shared__ uint32_t hist[2][QB][256];
     __shared__ uint32_t s_digit[2][QB], s_above[2][QB];
+    __shared__ uint32_t s_tie[QB];                  // some keys equal to T are dropped
     __shared__ uint32_t eqc[QB][NTILE];             // keys equal to T per (query, tile), then their prefix
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -365,6 +366,8 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
                     if (above < (uint32_t)nd && (uint32_t)nd <= above + h[b]) {
                         s_digit[hb][qi] = (uint32_t)(4 * lane + b);
                         s_above[hb][qi] = above;
+                        // last pass: h[b] keys equal T, and nd - above of them are kept
+                        if (pass == 3) s_tie[qi] = (uint32_t)nd - above != h[b];
                     }
                     above += h[b];
                 }
@@ -379,26 +382,33 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
         }
 
         // ---- ties: rank keys equal to T in index order (tile, lane) ----
+        // Only needed when some keys equal to T are dropped; with continuous
+        // scores T is almost always unique, and every key equal to it is kept.
+        bool any_tie = false;
 #pragma unroll
-        for (int i = 0; i < QB; ++i)
+        for (int i = 0; i < QB; ++i) any_tie = any_tie || (i < nq && s_tie[i] != 0u);
+        if (any_tie) {
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) {
-                const uint64_t eb = __ballot(i < nq && kvalid[j] && key[i][j] == prefix[i]);
-                if (lane == 0) eqc[i][wave * KPL + j] = (uint32_t)__popcll(eb);
+            for (int i = 0; i < QB; ++i)
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) {
+                    const uint64_t eb = __ballot(i < nq && kvalid[j] && key[i][j] == prefix[i]);
+                    if (lane == 0) eqc[i][wave * KPL + j] = (uint32_t)__popcll(eb);
+                }
+            __syncthreads();
+            if (wave < QB) {
+                // exclusive prefix of query `wave`'s per-tile counts, one tile per lane
+                const uint32_t c = lane < NTILE ? eqc[wave][lane] : 0u;
+                uint32_t incl = c;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t o = __shfl_up(incl, off);
+                    if (lane >= off) incl += o;
+                }
+                if (lane < NTILE) eqc[wave][lane] = incl - c;
             }
-        __syncthreads();
-        if (wave < QB) {
-            // exclusive prefix of query `wave`'s per-tile counts, one tile per lane
-            const uint32_t c = lane < NTILE ? eqc[wave][lane] : 0u;
-            uint32_t incl = c;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t o = __shfl_up(incl, off);
-                if (lane >= off) incl += o;
-            }
-            if (lane < NTILE) eqc[wave][lane] = incl - c;
+            __syncthreads();
         }
-        __syncthreads();
         uint64_t myword = 0;
 #pragma unroll
         for (int i = 0; i < QB; ++i)
@@ -406,9 +416,13 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
             for (int j = 0; j < KPL; ++j) {
                 const uint32_t kk = key[i][j];
                 const bool eq = i < nq && kvalid[j] && kk == prefix[i];
-                const uint64_t eb = __ballot(eq);
-                const uint32_t rank = eqc[i][wave * KPL + j] + (uint32_t)__popcll(eb & lt_mask);
-                const bool sel = i < nq && kvalid[j] && (kk > prefix[i] || (eq && rank < (uint32_t)need[i]));
+                bool take_eq = eq;
+                if (any_tie) {
+                    const uint64_t eb = __ballot(eq);
+                    const uint32_t rank = eqc[i][wave * KPL + j] + (uint32_t)__popcll(eb & lt_mask);
+                    take_eq = eq && rank < (uint32_t)need[i];
+                }
+                const bool sel = i < nq && kvalid[j] && (kk > prefix[i] || take_eq);
                 const uint64_t word = __ballot(sel);
                 if (lane == i * KPL + j) myword = word;
             }
@@ -418,7 +432,9 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
             const int m = wave * KPL + j;
             if (lane < QB * KPL && i < nq && m < nt) bits[(g * L + t0 + i) * (size_t)nt + m] = myword;
         }
-        __syncthreads();   // hist / eqc are rewritten by the next batch
+        // No barrier here: the next batch writes LDS (its pass 0 histogram,
+        // cleared by this batch's pass 2, and eqc) only after barriers that
+        // every thread reaches once done with this batch's reads.
     }
 }
 
