@@ -482,7 +482,7 @@ hipError_t launch_cand_attention(const void* q, const void* k, const void* v, co
     const int64_t grid = (nq + 3) / 4;
     if (grid == 0) return hipSuccess;
     // given events, the dispatch records the kernel's own start and stop
-    if (n_cand <= 32) {
+    if (n_cand <= 32 && (int64_t)B * H <= 65535) {   // (the group is the grid's y index)
         const dim3 grid2((unsigned)((L + 7) / 8), (unsigned)(B * H));   // two queries per wave
         if (D == 64)
             hipExtLaunchKernelGGL(cand_attention2_kernel<64>, grid2, dim3(256), 0, s, before, after, 0,

@@ -155,13 +155,14 @@ def test_forward_from_generated_positions(D, keep):
     _check_forward(q, kk, v, pos, keep, out, lse, tag)
 
 
-@pytest.mark.parametrize("D,k,keep", [(64, 20, 5), (64, 48, 12), (128, 64, 16)])
-def test_forward_other_candidate_counts(D, k, keep):
-    """k not a power of two (two queries per wave) and k above 32 (one query per wave)."""
-    B, H, L, C = 1, 2, 200, 24
-    tag = f"candidates D={D} k={k} keep={keep}"
+@pytest.mark.parametrize("D,k,keep,L", [(64, 20, 5, 200), (64, 48, 12, 200), (128, 64, 16, 200), (64, 32, 9, 101)])
+def test_forward_other_candidate_counts(D, k, keep, L):
+    """k not a power of two (two queries per wave), k above 32 (one query per wave), and an odd
+    sequence length, whose last wave has no second query."""
+    B, H, C = 1, 2, 24
+    tag = f"candidates D={D} k={k} keep={keep} L={L}"
     _say(tag)
-    x, w, bias = _generator(B, L, C, k, seed=D + k + keep)
+    x, w, bias = _generator(B, L, C, k, seed=D + k + keep + L)
     pos = _device_positions(x, w, bias)
     q, kk, v = _inputs(B, H, L, D, seed=5 * k + keep)
     out, lse, kept = _run(q, kk, v, pos, keep)
