@@ -319,13 +319,18 @@ __global__ __launch_bounds__(256) void cand_attention2_kernel(const uint16_t* __
                                                               const uint16_t* __restrict__ v,
                                                               const int32_t* __restrict__ pos, int H, int L, int k,
                                                               int keep, float scale, uint16_t* __restrict__ out,
-                                                              float* __restrict__ lse, int32_t* __restrict__ kept_out) {
+                                                              float* __restrict__ lse, int32_t* __restrict__ kept_out,
+                                                              int n_groups) {
     constexpr int DH = D / 32;   // output columns per lane
     const int lane = threadIdx.x & 63;
     const int hq = lane >> 5, j = lane & 31;
-    // grid: x = queries of one (batch, head) group in eights, y = the group
-    const int g = blockIdx.y;        // b * H + h
-    const int t0 = blockIdx.x * 8 + (threadIdx.x >> 6) * 2;
+    // Workgroup i runs on XCD i % 8, and XCD x takes the groups x, x + 8, ...:
+    // a group's K and V, which its queries gather, stay in one XCD's L2.
+    const int tb_per_group = (L + 7) / 8;   // workgroups (eight queries each) per group
+    const int xcd = blockIdx.x % kXcds, jw = blockIdx.x / kXcds;
+    const int g = xcd + kXcds * (jw / tb_per_group);   // b * H + h
+    if (g >= n_groups) return;
+    const int t0 = (jw % tb_per_group) * 8 + (threadIdx.x >> 6) * 2;
     if (t0 >= L) return;             // the whole wave
     const int t = t0 + hq;
     const bool live = t < L;         // the second half of the last wave may be past the end
@@ -482,16 +487,17 @@ hipError_t launch_cand_attention(const void* q, const void* k, const void* v, co
     const int64_t grid = (nq + 3) / 4;
     if (grid == 0) return hipSuccess;
     // given events, the dispatch records the kernel's own start and stop
-    if (n_cand <= 32 && (int64_t)B * H <= 65535) {   // (the group is the grid's y index)
-        const dim3 grid2((unsigned)((L + 7) / 8), (unsigned)(B * H));   // two queries per wave
+    const int64_t groups = (int64_t)B * H;
+    const int64_t grid2 = (int64_t)kXcds * ((groups + kXcds - 1) / kXcds) * ((L + 7) / 8);   // two queries per wave
+    if (n_cand <= 32 && grid2 < ((int64_t)1 << 31)) {
         if (D == 64)
-            hipExtLaunchKernelGGL(cand_attention2_kernel<64>, grid2, dim3(256), 0, s, before, after, 0,
+            hipExtLaunchKernelGGL(cand_attention2_kernel<64>, dim3((unsigned)grid2), dim3(256), 0, s, before, after, 0,
                                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, pos, H, L, n_cand, keep,
-                                  scale, (uint16_t*)out, lse, kept);
+                                  scale, (uint16_t*)out, lse, kept, (int)groups);
         else
-            hipExtLaunchKernelGGL(cand_attention2_kernel<128>, grid2, dim3(256), 0, s, before, after,
+            hipExtLaunchKernelGGL(cand_attention2_kernel<128>, dim3((unsigned)grid2), dim3(256), 0, s, before, after,
                                   0, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, pos, H, L, n_cand,
-                                  keep, scale, (uint16_t*)out, lse, kept);
+                                  keep, scale, (uint16_t*)out, lse, kept, (int)groups);
         return hipGetLastError();
     }
     if (D == 64)
