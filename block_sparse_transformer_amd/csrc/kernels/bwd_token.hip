@@ -83,11 +83,22 @@ __device__ __forceinline__ void add_slice(void* base, size_t off, const float (&
     }
 }
 
-// sum over the eight lanes of a row (lanes 8k .. 8k + 7 of the wave)
+// The value of another lane of the same row of 16, by a DPP lane move (no
+// LDS round trip, unlike a shuffle through ds_bpermute).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the eight lanes of a row (lanes 8k .. 8k + 7 of the wave, all
+// active together): lane ^ 1 and lane ^ 2 within the quad, then the other
+// quad's sum through the half-row mirror (lane i meets lane 7 - i).  Every
+// lane ends with the same value (each step adds the same two numbers on both
+// sides).
 __device__ __forceinline__ float group_sum(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
+    x += dpp_move<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_move<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_move<0x141>(x);   // row_half_mirror
     return x;
 }
 
