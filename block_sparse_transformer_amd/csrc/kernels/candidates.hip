@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kPosThreads) void cand_positions_kernel(const uint1
     pos[((size_t)b * L + t) * k + j] = p;
 }
 
-// Four outputs per thread (k % 4 == 0, C % 8 == 0, x 16-byte aligned): thread
+// Four outputs per thread (k % 4 == 0, C % 8 == 0, x and w 16-byte aligned): thread
 // (token t, group g) runs the chains of outputs 4g .. 4g + 3, each in the same
 // fixed order as above.  Per step of eight channels it loads the eight x
 // values of the row once (16 bytes, one conversion each, shared by the four
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(256) void cand_attention2_kernel(const uint16_t* __
 hipError_t launch_cand_positions(const void* x, const float* w, const float* bias, int B, int L, int C, int k,
                                  int32_t* pos, hipStream_t s) {
     if (k < 1 || k > kMaxCandidates || C < 1) return hipErrorInvalidValue;
-    if (k % 4 == 0 && C % 8 == 0 && ((uintptr_t)x & 15) == 0) {
+    if (k % 4 == 0 && C % 8 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)w & 15) == 0) {
         int gp = 1;
         while (gp < k / 4) gp <<= 1;
         const int T = kPosThreads / gp;

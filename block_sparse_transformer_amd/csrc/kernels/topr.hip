@@ -209,6 +209,23 @@ __global__ __launch_bounds__(kSelThreads) void topr_select_kernel(const uint16_t
 // radix select (LDS histograms, a wave per query scans), ties are ranked in
 // index order from per-tile counts, and the kept-key word of tile w KPL + j is
 // the wave's ballot.
+// Inclusive prefix sum over the 64 lanes of a wave by DPP lane moves (no LDS
+// round trips): sums of four within each row of 16 from three shifted adds,
+// then the rows' halves (shift by 4 into banks 1-3, by 8 into banks 2-3), then
+// the rows (lane 15 of each row into the next odd row, lane 31 into rows 2 and
+// 3).  Lanes a move leaves without a source add 0.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+    const int xi = (int)x;
+    int s = xi + __builtin_amdgcn_update_dpp(0, xi, 0x111, 0xF, 0xF, true);   // row_shr:1
+    s += __builtin_amdgcn_update_dpp(0, xi, 0x112, 0xF, 0xF, true);           // row_shr:2
+    s += __builtin_amdgcn_update_dpp(0, xi, 0x113, 0xF, 0xF, true);           // row_shr:3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xF, 0xE, false);           // row_shr:4, banks 1-3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xF, 0xC, false);           // row_shr:8, banks 2-3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xA, 0xF, false);           // row_bcast:15, rows 1, 3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xC, 0xF, false);           // row_bcast:31, rows 2, 3
+    return (uint32_t)s;
+}
+
 constexpr int kKsThreads = 1024;
 constexpr int kKsWaves = kKsThreads / 64;
 constexpr int kKsBatch = 8;
@@ -341,30 +358,26 @@ __global__ __launch_bounds__(kKsThreads) void topr_select_ks_kernel(const uint16
                 }
             __syncthreads();
             if (wave < nq) {
-                // one wave per query: lane l owns bins 4l .. 4l + 3, read and cleared
+                // one wave per query: lane l owns bins 255 - 4l - b, b = 0 .. 3
+                // (lane 0 the highest), read and cleared; the keys above a
+                // lane's bins are the prefix sum over the lanes before it
                 const int qi = wave;
                 uint32_t h[4], own = 0;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    h[b] = hist[hb][qi][4 * lane + b];
+                    h[b] = hist[hb][qi][255 - 4 * lane - b];
                     own += h[b];
-                    hist[hb][qi][4 * lane + b] = 0u;
+                    hist[hb][qi][255 - 4 * lane - b] = 0u;
                 }
-                uint32_t suffix = own;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t o = __shfl_down(suffix, off);
-                    if (lane + off < 64) suffix += o;
-                }
-                uint32_t above = suffix - own;
+                uint32_t above = wave_prefix_sum(own) - own;
                 int nd = need[0];
 #pragma unroll
                 for (int x = 1; x < QB; ++x)
                     if (qi == x) nd = need[x];
 #pragma unroll
-                for (int b = 3; b >= 0; --b) {
+                for (int b = 0; b < 4; ++b) {
                     if (above < (uint32_t)nd && (uint32_t)nd <= above + h[b]) {
-                        s_digit[hb][qi] = (uint32_t)(4 * lane + b);
+                        s_digit[hb][qi] = (uint32_t)(255 - 4 * lane - b);
                         s_above[hb][qi] = above;
                         // last pass: h[b] keys equal T, and nd - above of them are kept
                         if (pass == 3) s_tie[qi] = (uint32_t)nd - above != h[b];
