@@ -81,6 +81,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 // running max is raised.  Besides preventing overflow it keeps a dominant
 // probability near 1, where its bf16 rounding is exact or small.
 constexpr float kSumCap = 256.0f;
+// Finite stand-in for the running max of a row that has met no key yet (the
+// D = 64 kernel): any finite score then has an infinite probability, which
+// trips the kSumCap test, and exp2(kNoMax - m) is 0 for every finite m.
+constexpr float kNoMax = -1e30f;
 constexpr int kThreads = 128;      // 2 waves per workgroup
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -1188,7 +1192,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 for (int i = 0; i < 16; ++i) o[db][qb][i] = 0.f;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            m[qb] = -INFINITY;
+            m[qb] = kNoMax;
             l[qb] = 0.f;
         }
     };
@@ -1198,6 +1202,15 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         float v = __builtin_fmaxf(s[0], s[1]);
 #pragma unroll
         for (int i = 2; i < 16; i += 2) v = __builtin_fmaxf(__builtin_fmaxf(v, s[i]), s[i + 1]);
+        return pair_max(v) * c2;
+    };
+    // the same maximum taken in the opposite order, for the rare rescale: the
+    // compiler then shares no partial maxima between the two and keeps none of
+    // them on the common path
+    auto blk_max_rev = [&](const f32x16_t& s) -> float {
+        float v = __builtin_fmaxf(s[15], s[14]);
+#pragma unroll
+        for (int i = 13; i > 0; i -= 2) v = __builtin_fmaxf(__builtin_fmaxf(v, s[i]), s[i - 1]);
         return pair_max(v) * c2;
     };
     // masks of score block (kb, qb): keys 32kb .. 32kb + 31 of the tile for
@@ -1246,19 +1259,23 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         for (int c = 0; c < NC; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfb[c], qfb[c], s, 0, 0, 0);
     };
     // Probabilities of one score block of half qb (key chunks 2kb, 2kb + 1).
-    // On a unit's first tile the running max starts at the block's max.  It is
-    // raised only when a lane's 16 probabilities would sum past kSumCap (or a
-    // -inf max meets a finite score): then O and l are rescaled to the block's
-    // max and the block is redone.  `issue` places NM matrix products (scores
-    // of later blocks, PV products of earlier ones) in the same scheduling
-    // region, and the group barriers alternate them with the exp/pack work, so
-    // the wave keeps its matrix core busy during its own softmax.
+    // On a unit's first tile the running max starts at the block's max, or at
+    // the finite stand-in kNoMax when the lane's query sees no key of the block.
+    // It is raised only when a lane's 16 probabilities would sum past kSumCap:
+    // then O and l are rescaled to the block's max and the block is redone.  A
+    // finite score met while the max is still kNoMax gives an infinite
+    // probability, so it takes the same path, and l and O, still zero, are
+    // scaled by exp2(kNoMax - max) = 0.  `issue` places NM matrix products
+    // (scores of later blocks, PV products of earlier ones) in the same
+    // scheduling region, and the group barriers alternate them with the
+    // exp/pack work, so the wave keeps its matrix core busy during its own
+    // softmax.
     auto softmax_blk = [&](const f32x16_t& s, int qb, bool first, u32x4_t (&u)[2], auto&& issue, auto nm) {
         constexpr int NM = decltype(nm)::value;
-        if (first) m[qb] = blk_max(s);
+        if (first) m[qb] = __builtin_fmaxf(blk_max(s), kNoMax);
         float lsum;
         auto chunks = [&]() {
-            const float muse = m[qb] == -INFINITY ? 0.f : m[qb];
+            const float muse = m[qb];
             float acc[8];
 #pragma unroll
             for (int k = 0; k < 2; ++k)
@@ -1278,9 +1295,9 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 56 / NM, 0);   // then a share of the VALU work
         }
-        const bool bad = lsum > kSumCap || (m[qb] == -INFINITY && lsum > 0.f);
+        const bool bad = lsum > kSumCap;
         if (__ballot(bad) != 0) {          // wave-uniform, rare
-            const float mx = blk_max(s);
+            const float mx = blk_max_rev(s);
             const bool raise = mx > m[qb];
             const float alpha = raise ? __builtin_amdgcn_exp2f(m[qb] - mx) : 1.f;
             l[qb] *= alpha;
