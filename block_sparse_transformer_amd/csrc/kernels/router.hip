@@ -52,13 +52,26 @@ __global__ __launch_bounds__(64) void route_score_kernel(const uint16_t* q, cons
     const int t0 = (blockIdx.x % n_tiles) * 64;
     const int n_rows = min(64, L - t0);
     const uint4* src = (const uint4*)(q + (bh * (size_t)L + t0) * D);
-    for (int p = lane; p < 64 * kPieces; p += 64) {
-        const int r = p / kPieces, c = p % kPieces;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (r < n_rows) u = src[p];
-        *(uint4*)(rows + r * kStride + c * 16) = u;
+    // every load of the 64 rows is issued before any is stored, so the wave
+    // waits for memory once instead of once per 16-byte piece
+    uint4 u[kPieces];
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+        const int p = lane + 64 * i;
+        u[i] = make_uint4(0, 0, 0, 0);
+        if (p / kPieces < n_rows) u[i] = src[p];
     }
-    for (int d = lane; d < D; d += 64) wd[d] = (double)w[d];
+    float wf[(D + 63) / 64];
+#pragma unroll
+    for (int i = 0; i < (D + 63) / 64; ++i) wf[i] = lane + 64 * i < D ? w[lane + 64 * i] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+        const int p = lane + 64 * i;
+        *(uint4*)(rows + (p / kPieces) * kStride + (p % kPieces) * 16) = u[i];
+    }
+#pragma unroll
+    for (int i = 0; i < (D + 63) / 64; ++i)
+        if (lane + 64 * i < D) wd[lane + 64 * i] = (double)wf[i];
     __syncthreads();
     if (lane >= n_rows) return;
     const unsigned char* row = rows + lane * kStride;
