@@ -158,6 +158,31 @@ __device__ __forceinline__ void store_row(const f32x16_t (&acc)[D / 32], float m
         }
 }
 
+// An item's list entries, one per lane, loaded once: entry e of the item is
+// then a lane read (v_readlane) instead of a memory round trip in front of the
+// next tile's loads.  Items longer than a wave read the list directly.
+struct ItemList {
+    int32_t first, n, idx;
+    uint32_t sub;
+    __device__ __forceinline__ bool in_regs() const { return n <= 64; }
+};
+__device__ __forceinline__ ItemList load_list(const BwdArgs& a, const BwdItem& item, bool with_sub) {
+    ItemList l;
+    l.first = item.begin;
+    l.n = item.end - item.begin;
+    const int lane = threadIdx.x & 63;
+    const bool mine = lane < l.n;
+    l.idx = mine ? a.idx[item.begin + lane] : 0;
+    l.sub = with_sub && mine ? (uint32_t)a.idx_sub[item.begin + lane] : 0u;
+    return l;
+}
+__device__ __forceinline__ int list_idx(const BwdArgs& a, const ItemList& l, int e) {
+    return l.in_regs() ? __builtin_amdgcn_readlane(l.idx, e - l.first) : a.idx[e];
+}
+__device__ __forceinline__ int list_sub(const BwdArgs& a, const ItemList& l, int e) {
+    return l.in_regs() ? (int)__builtin_amdgcn_readlane(l.sub, e - l.first) : (int)a.idx_sub[e];
+}
+
 // Workgroup -> (batch entry, head, item).  Workgroups are dealt round-robin
 // to the 8 XCDs; XCD x takes the (b, h) groups x, x + 8, ... one after the
 // other, so that the tiles a group's items read stay in that XCD's L2.
@@ -221,7 +246,8 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
         for (int i = 0; i < 16; ++i) dqa[db][i] = 0.f;
 
     // key block of list entry e: the layout's row list, or (routed tiles) every block in order
-    auto key_block = [&](int e) -> int { return MASK == MASK_ROUTED_Q ? e : a.idx[e]; };
+    const ItemList lst = MASK == MASK_ROUTED_Q ? ItemList{item.begin, 0, 0, 0u} : load_list(a, item, MASK == MASK_SUB);
+    auto key_block = [&](int e) -> int { return MASK == MASK_ROUTED_Q ? e : list_idx(a, lst, e); };
     TileRegs<D> kr, vr;
     if (item.begin < item.end) {
         const int j0 = key_block(item.begin);
@@ -245,7 +271,7 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
     for (int e = item.begin; e < item.end; ++e) {
         const int j = key_block(e);
         // 32-token blocks: key halves this wave's query half may see
-        const int sub = MASK == MASK_SUB ? (int)a.idx_sub[e] >> (2 * wave) : 3;
+        const int sub = MASK == MASK_SUB ? list_sub(a, lst, e) >> (2 * wave) : 3;
         // band layouts: a tile whose farthest (query, key) pair is inside the band needs no mask
         const bool band_cut = MASK == MASK_BAND && 64 * abs(blk - j) + 63 > a.band;
         __syncthreads();   // the previous tile's reads are done
@@ -368,12 +394,13 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
             del_r = tok_r >= 0 ? a.delta[r] : 0.f;
         }
     };
-    if (item.begin < item.end) fetch(a.idx[item.begin]);
+    const ItemList lst = load_list(a, item, MASK == MASK_SUB);
+    if (item.begin < item.end) fetch(list_idx(a, lst, item.begin));
     for (int e = item.begin; e < item.end; ++e) {
         // 32-token blocks: query halves that may see this wave's key half
-        const int sub = MASK == MASK_SUB ? (int)a.idx_sub[e] >> wave : 15;
+        const int sub = MASK == MASK_SUB ? list_sub(a, lst, e) >> wave : 15;
         // band layouts: query block ib, masked per pair unless the whole tile is inside the band
-        const int ib = a.idx[e];
+        const int ib = list_idx(a, lst, e);
         const bool routed_entry = MASK == MASK_BAND_ROUTED && ib >= a.nb;
         const bool band_cut = (MASK == MASK_BAND || MASK == MASK_BAND_ROUTED) && !routed_entry &&
                               64 * abs(blk - ib) + 63 > a.band;
@@ -386,7 +413,7 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
             qtok[tid] = tok_r;
         }
         __syncthreads();
-        if (e + 1 < item.end) fetch(a.idx[e + 1]);   // behind this tile's products
+        if (e + 1 < item.end) fetch(list_idx(a, lst, e + 1));   // behind this tile's products
         // S = Q K^T - LSE/scale and dP = dO V^T - delta: block qb holds queries 32qb .. 32qb + 31,
         // register i <-> query 32qb + 8(i/4) + 4hh + i%4
         f32x16_t s[2], dp[2];
