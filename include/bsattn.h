@@ -515,11 +515,17 @@ bsattn_status bsattn_layer_workspace_size(const bsattn_layout* layout, int32_t b
  *   out      device bf16 [B, L, C]; must not alias an input.
  *   layout, key_valid_len, scale as bsattn_forward (the page divides by sqrt(C);
  *   pass the scale wanted).
- * The two projections are rocBLAS GEMMs (bf16 inputs, fp32 accumulation and
- * output); the bias adds, the head split and concatenation and the attention
- * are this library's kernels.  q, k, v and the projections are rounded to
- * bf16 once each.  Pointers 16-byte aligned, workspace 256-byte aligned.
- * Enqueued on `stream`; the first call on a thread creates a rocBLAS handle. */
+ * The two projections are hipBLASLt GEMMs (bf16 inputs, fp32 accumulation)
+ * whose epilogue adds the bias and writes bf16: the qkv projection token-major
+ * [B L, 3C], from which the attention reads each head in place, and the output
+ * projection from the attention's concatenated heads [B L, C].  Where
+ * hipBLASLt has no algorithm for a shape, rocBLAS GEMMs with fp32 output and
+ * this library's bias, head split and concatenation kernels are used instead.
+ * q, k, v and the projections are rounded to bf16 once each.  Pointers 16-byte
+ * aligned, workspace 256-byte aligned.
+ * Enqueued on `stream`; the first call of a shape on a thread creates the
+ * library handles and hipBLASLt's plan for the two projections (the first
+ * algorithm of its heuristic). */
 bsattn_status bsattn_layer_forward(const bsattn_layout* layout, int32_t batch, int32_t num_heads,
                                    int32_t seq_len, int32_t head_dim, const void* x,
                                    const void* w_qkv, const void* b_qkv, const void* w_proj,
