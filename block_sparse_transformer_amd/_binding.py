@@ -8,7 +8,8 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libbsattn.so")
+# BSATTN_LIBRARY names another build of the library (e.g. libbsattn_debug.so)
+_LIB_PATH = os.environ.get("BSATTN_LIBRARY") or os.path.join(_HERE, "libbsattn.so")
 _lib = None
 
 BSATTN_F32 = 0

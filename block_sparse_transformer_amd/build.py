@@ -5,6 +5,12 @@
 Every HIP source is compiled to an object in parallel, then linked into
 ``block_sparse_transformer_amd/libbsattn.so``.  Packed-fp32 instructions are
 disabled for device code (the target feature ``-packed-fp32-ops``).
+
+``build(debug=True)`` (``--debug`` on the command line) builds
+``libbsattn_debug.so`` with ``-DBSATTN_DEBUG``: the forward kernels bounds-check
+every schedule entry they read, and each forward call synchronises its stream
+and fails (BSATTN_ERR_HIP, "device-side assert") if a check did not hold.
+Setting ``BSATTN_LIBRARY`` to its path makes the binding load it instead.
 """
 from __future__ import annotations
 
@@ -19,6 +25,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsattn.so")
+BUILD_DEBUG = os.path.join(ROOT, "_build_debug")
+LIB_DEBUG = os.path.join(PKG, "libbsattn_debug.so")
 
 SOURCES = [
     "api.cpp",
@@ -46,11 +54,11 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _compile(src: str, verbose: bool, debug: bool = False) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
+    obj = os.path.join(BUILD_DEBUG if debug else BUILD, src.replace("/", "_") + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", path, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *(["-DBSATTN_DEBUG"] if debug else []), *lang, "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,11 +67,12 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    out_dir, lib = (BUILD_DEBUG, LIB_DEBUG) if debug else (BUILD, LIB)
+    os.makedirs(out_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, debug), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
            "-L/opt/rocm/lib", "-lrocblas", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
@@ -71,9 +80,9 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

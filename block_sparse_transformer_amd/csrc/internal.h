@@ -144,6 +144,10 @@ struct FwdArgs {
     int64_t qkv_bs, qkv_hs, qkv_ts, o_bs, o_hs, o_ts;
     float scale;              // score scale
     float scale_log2;         // scale * log2(e)
+    // debug builds (BSATTN_DEBUG): a device word the forward kernels OR a bit
+    // into for every schedule entry out of bounds (1 unit record, 2 tile
+    // entry, 4 list length); null otherwise
+    uint32_t* dbg;
 };
 
 // ---- backward ----

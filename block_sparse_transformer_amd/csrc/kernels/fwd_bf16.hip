@@ -240,6 +240,42 @@ __device__ __forceinline__ int tile_unit(int e) { return (e >> kTileUnitShift) &
 // allowed 32 x 32 sub-blocks of a tile: bit 2a + b, query half a, key half b
 __device__ __forceinline__ int tile_sub(int e) { return (e >> kTileSubShift) & 15; }
 
+// Debug builds (BSATTN_DEBUG) check the schedule as the kernels walk it: list
+// lengths, unit records and tile entries.  A bad value sets a bit of *a.dbg
+// and is replaced by one that stays in bounds, so the walk goes on and the
+// host reports the error after the launch.  Release builds compile to nothing.
+__device__ __forceinline__ void dbg_lengths(const FwdArgs& a, int& nu, int& nt) {
+#ifdef BSATTN_DEBUG
+    if (nu > kMaxBinUnits || nt > kMaxBinTiles) {
+        atomicOr(a.dbg, 4u);
+        nu = min(nu, kMaxBinUnits);
+        nt = min(nt, kMaxBinTiles);
+    }
+#endif
+}
+__device__ __forceinline__ int4 dbg_unit(const FwdArgs& a, int4 r) {
+#ifdef BSATTN_DEBUG
+    const bool group_ok = r.z >= 0 && r.z < a.B * a.H;
+    const bool row_ok = r.x >= 0 ? r.x < a.nb && r.y >= -1 && r.y < a.n_slots
+                                 : (-1 - r.x) < a.n_rt && r.y >= 0 && r.y < a.r_chunks;
+    if (!group_ok || !row_ok) {
+        atomicOr(a.dbg, 1u);
+        r = make_int4(0, -1, 0, r.w);
+    }
+#endif
+    return r;
+}
+__device__ __forceinline__ int dbg_tile(const FwdArgs& a, int e, int nu, bool gathered) {
+#ifdef BSATTN_DEBUG
+    const int limit = a.nb + (gathered ? a.n_gt : 0);
+    if (tile_j(e) >= limit || ((e >> kTileUnitShift) & 127) >= nu) {
+        atomicOr(a.dbg, 2u);
+        e &= kTileFirst | kTileLast | (15 << kTileSubShift);
+    }
+#endif
+    return e;
+}
+
 // STRIDED: Q, K, V and O at the FwdArgs strides (the attention layer's layout)
 template <int D, int MASK, bool STRIDED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(const FwdArgs a) {
@@ -270,8 +306,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int x = blockIdx.x % kXcds;
     const int bin = blockIdx.x / kXcds;
     const int bi = x * a.n_bins + bin;
-    const int up0 = a.unit_ptr[bi], nu = a.unit_ptr[bi + 1] - up0;   // <= 64
-    const int tp0 = a.tile_ptr[bi], nt = a.tile_ptr[bi + 1] - tp0;   // <= kMaxBinTiles
+    const int up0 = a.unit_ptr[bi];
+    const int tp0 = a.tile_ptr[bi];
+    int nu = a.unit_ptr[bi + 1] - up0;   // <= 64
+    int nt = a.tile_ptr[bi + 1] - tp0;   // <= kMaxBinTiles
+    dbg_lengths(a, nu, nt);
     if (nu <= 0) return;
 
     // Unit table, lane k describing unit k: kind >= 0 query block of a layout
@@ -279,7 +318,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // g its (batch, head) group; valid its batch entry's key length.
     int u_kind = 0, u_slot = -1, u_g = 0, u_valid = a.L;
     if (lane < nu) {
-        const int4 r = a.units[up0 + lane];
+        const int4 r = dbg_unit(a, a.units[up0 + lane]);
         const int ub = r.z / a.H;
         u_kind = r.x;
         u_g = r.z;
@@ -361,14 +400,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (MASK == MASK_TOKEN)
         for (int i = tid; i < a.n_gt * 64; i += kThreads) gtok_s[i] = a.gtok[i];
     if (MASK != MASK_PAD) {
-        for (int i = tid; i < nt; i += kThreads) flat[i] = a.tiles[tp0 + i];
+        for (int i = tid; i < nt; i += kThreads) flat[i] = dbg_tile(a, a.tiles[tp0 + i], nu, MASK == MASK_TOKEN);
     } else {
         // both waves scan the list (wave 0 writes it) and write their half of empty units
         int kept_total = 0;
         for (int base = 0; base < nt; base += 64) {
             const int i = base + lane;
-            const int e = i < nt ? a.tiles[tp0 + i] : 0;
-            const int en = i + 1 < nt ? a.tiles[tp0 + i + 1] : 0;
+            const int e = i < nt ? dbg_tile(a, a.tiles[tp0 + i], nu, MASK == MASK_TOKEN) : 0;
+            const int en = i + 1 < nt ? dbg_tile(a, a.tiles[tp0 + i + 1], nu, MASK == MASK_TOKEN) : 0;
             const int valid = __shfl(u_valid, tile_unit(e));   // the tile's unit's key length
             const bool keep = i < nt && tile_j(e) * 64 < valid;
             const bool keep_next = i + 1 < nt && !(e & kTileLast) && tile_j(en) * 64 < valid;
@@ -1005,13 +1044,16 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int x = blockIdx.x % kXcds;
     const int bin = blockIdx.x / kXcds + list * (a.n_bins / kQWaves);
     const int bi = x * a.n_bins + bin;
-    const int up0 = a.unit_ptr[bi], nu = a.unit_ptr[bi + 1] - up0;   // <= kMaxBinUnits
-    const int tp0 = a.tile_ptr[bi], nt = a.tile_ptr[bi + 1] - tp0;   // <= kMaxBinTiles
+    const int up0 = a.unit_ptr[bi];
+    const int tp0 = a.tile_ptr[bi];
+    int nu = a.unit_ptr[bi + 1] - up0;   // <= kMaxBinUnits
+    int nt = a.tile_ptr[bi + 1] - tp0;   // <= kMaxBinTiles
+    dbg_lengths(a, nu, nt);
     if (nu <= 0) return;
 
     int u_kind = 0, u_slot = -1, u_g = 0, u_valid = a.L;
     if (lane < nu) {
-        const int4 r = a.units[up0 + lane];
+        const int4 r = dbg_unit(a, a.units[up0 + lane]);
         const int ub = r.z / a.H;
         u_kind = r.x;
         u_g = r.z;
@@ -1102,13 +1144,13 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     int F = nt;
     uint64_t empty_units = 0;
     if (MASK != MASK_PAD) {
-        for (int i = lane; i < nt; i += 64) flat[i] = a.tiles[tp0 + i];
+        for (int i = lane; i < nt; i += 64) flat[i] = dbg_tile(a, a.tiles[tp0 + i], nu, MASK == MASK_TOKEN);
     } else {
         int kept_total = 0;
         for (int base = 0; base < nt; base += 64) {
             const int i = base + lane;
-            const int e = i < nt ? a.tiles[tp0 + i] : 0;
-            const int en = i + 1 < nt ? a.tiles[tp0 + i + 1] : 0;
+            const int e = i < nt ? dbg_tile(a, a.tiles[tp0 + i], nu, MASK == MASK_TOKEN) : 0;
+            const int en = i + 1 < nt ? dbg_tile(a, a.tiles[tp0 + i + 1], nu, MASK == MASK_TOKEN) : 0;
             const int valid = __shfl(u_valid, tile_unit(e));
             const bool keep = i < nt && tile_j(e) * 64 < valid;
             const bool keep_next = i + 1 < nt && !(e & kTileLast) && tile_j(en) * 64 < valid;
@@ -1880,8 +1922,14 @@ int fwd_bf16_ctas_per_cu(int head_dim, bool two_wave) {
     return n < 4 ? n : 4;
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
-                           hipEvent_t after) {
+#ifdef BSATTN_DEBUG
+// Debug builds: the word the kernels report schedule errors into (one per
+// device, cleared before and read back after every forward launch).
+__device__ uint32_t g_dbg_word;
+#endif
+
+static hipError_t launch_fwd_bf16_impl(const FwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
+                                hipEvent_t after) {
     hipError_t e;
     if (a.strided) {
         // the attention layer's layout: block (any block size) and band layouts
@@ -1955,6 +2003,28 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t
         merge(a, units);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
+                           hipEvent_t after) {
+#ifdef BSATTN_DEBUG
+    // Debug builds synchronise the stream: the kernels' schedule checks are
+    // read back and a failed one is reported as a device-side assert.
+    uint32_t* dw = nullptr;
+    hipError_t e = hipGetSymbolAddress((void**)&dw, HIP_SYMBOL(g_dbg_word));
+    if (e != hipSuccess) return e;
+    static const uint32_t zero = 0;
+    if ((e = hipMemcpyAsync(dw, &zero, sizeof(zero), hipMemcpyHostToDevice, s)) != hipSuccess) return e;
+    FwdArgs ad = a;
+    ad.dbg = dw;
+    if ((e = launch_fwd_bf16_impl(ad, head_dim, mask, s, before, after)) != hipSuccess) return e;
+    uint32_t flag = 0;
+    if ((e = hipMemcpyAsync(&flag, dw, sizeof(flag), hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    return flag ? hipErrorAssert : hipSuccess;
+#else
+    return launch_fwd_bf16_impl(a, head_dim, mask, s, before, after);
+#endif
 }
 
 hipError_t launch_gather_global(const FwdArgs& a, int head_dim, hipStream_t s) {

@@ -35,6 +35,15 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_debug_build_exports_the_same_symbols():
+    """libbsattn_debug.so (-DBSATTN_DEBUG, built by __graft_entry__.build()) is the same C ABI."""
+    path = os.path.join(os.path.dirname(bs.library_path()), "libbsattn_debug.so")
+    assert os.path.exists(path), f"{path} is missing: run __graft_entry__.build()"
+    dbg = ctypes.CDLL(path)
+    for n in _declared():
+        assert hasattr(dbg, n), n
+
+
 def test_status_strings_and_last_error():
     for code in range(6):
         assert bs.bsattn_status_string(code)
