@@ -8,8 +8,9 @@ disabled for device code (the target feature ``-packed-fp32-ops``).
 
 ``build(debug=True)`` (``--debug`` on the command line) builds
 ``libbsattn_debug.so`` with ``-DBSATTN_DEBUG``: the forward kernels bounds-check
-every schedule entry they read, and each forward call synchronises its stream
-and fails (BSATTN_ERR_HIP, "device-side assert") if a check did not hold.
+every schedule entry they read and the backward passes every item and block-list
+entry; each of those launches synchronises its stream and fails (BSATTN_ERR_HIP,
+"device-side assert") if a check did not hold.
 Setting ``BSATTN_LIBRARY`` to its path makes the binding load it instead.
 """
 from __future__ import annotations

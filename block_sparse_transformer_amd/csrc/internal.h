@@ -209,6 +209,9 @@ struct BwdArgs {
     const int32_t* trows;
     float* ws_g;
     int32_t g_chunks;
+    // debug builds (BSATTN_DEBUG): a device word the dQ and dK/dV kernels OR a
+    // bit into for an item (8) or a list entry (16) out of bounds; null otherwise
+    uint32_t* dbg;
 };
 
 // ---- the allocation-free forward (kernels/noalloc.hip) ----

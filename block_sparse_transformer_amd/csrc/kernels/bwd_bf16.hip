@@ -166,18 +166,29 @@ struct ItemList {
     uint32_t sub;
     __device__ __forceinline__ bool in_regs() const { return n <= 64; }
 };
-__device__ __forceinline__ ItemList load_list(const BwdArgs& a, const BwdItem& item, bool with_sub) {
+// Debug builds (BSATTN_DEBUG): a list entry at or past `limit` sets bit 16 of
+// *a.dbg and reads as block 0; release builds compile this to nothing.
+__device__ __forceinline__ int dbg_entry(const BwdArgs& a, int v, int limit) {
+#ifdef BSATTN_DEBUG
+    if (v < 0 || v >= limit) {
+        atomicOr(a.dbg, 16u);
+        v = 0;
+    }
+#endif
+    return v;
+}
+__device__ __forceinline__ ItemList load_list(const BwdArgs& a, const BwdItem& item, bool with_sub, int limit) {
     ItemList l;
     l.first = item.begin;
     l.n = item.end - item.begin;
     const int lane = threadIdx.x & 63;
     const bool mine = lane < l.n;
-    l.idx = mine ? a.idx[item.begin + lane] : 0;
+    l.idx = mine ? dbg_entry(a, a.idx[item.begin + lane], limit) : 0;
     l.sub = with_sub && mine ? (uint32_t)a.idx_sub[item.begin + lane] : 0u;
     return l;
 }
-__device__ __forceinline__ int list_idx(const BwdArgs& a, const ItemList& l, int e) {
-    return l.in_regs() ? __builtin_amdgcn_readlane(l.idx, e - l.first) : a.idx[e];
+__device__ __forceinline__ int list_idx(const BwdArgs& a, const ItemList& l, int e, int limit) {
+    return l.in_regs() ? __builtin_amdgcn_readlane(l.idx, e - l.first) : dbg_entry(a, a.idx[e], limit);
 }
 __device__ __forceinline__ int list_sub(const BwdArgs& a, const ItemList& l, int e) {
     return l.in_regs() ? (int)__builtin_amdgcn_readlane(l.sub, e - l.first) : (int)a.idx_sub[e];
@@ -195,6 +206,14 @@ __device__ __forceinline__ bool take_item(const BwdArgs& a, int& b, int& h, int&
     h = g % a.H;
     item = a.items[(size_t)h * a.items_per_head + k % a.items_per_head];
     if (item.head_blk < 0) return false;
+#ifdef BSATTN_DEBUG
+    // debug builds: an item out of bounds sets bit 8 of *a.dbg and is skipped
+    if (item.head_blk / a.nb != h || item.begin > item.end || item.begin < 0 || item.slot < -1 ||
+        item.slot >= a.n_slots) {
+        atomicOr(a.dbg, 8u);
+        return false;
+    }
+#endif
     blk = item.head_blk % a.nb;
     return true;
 }
@@ -246,8 +265,14 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(const BwdArgs a) {
         for (int i = 0; i < 16; ++i) dqa[db][i] = 0.f;
 
     // key block of list entry e: the layout's row list, or (routed tiles) every block in order
-    const ItemList lst = MASK == MASK_ROUTED_Q ? ItemList{item.begin, 0, 0, 0u} : load_list(a, item, MASK == MASK_SUB);
-    auto key_block = [&](int e) -> int { return MASK == MASK_ROUTED_Q ? e : list_idx(a, lst, e); };
+    const ItemList lst = MASK == MASK_ROUTED_Q ? ItemList{item.begin, 0, 0, 0u} : load_list(a, item, MASK == MASK_SUB, a.nb);
+#ifdef BSATTN_DEBUG
+    if (MASK == MASK_ROUTED_Q && item.end > a.nb) {   // a routed tile's entries are the key blocks themselves
+        atomicOr(a.dbg, 16u);
+        item.end = item.begin;
+    }
+#endif
+    auto key_block = [&](int e) -> int { return MASK == MASK_ROUTED_Q ? e : list_idx(a, lst, e, a.nb); };
     TileRegs<D> kr, vr;
     if (item.begin < item.end) {
         const int j0 = key_block(item.begin);
@@ -394,13 +419,15 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
             del_r = tok_r >= 0 ? a.delta[r] : 0.f;
         }
     };
-    const ItemList lst = load_list(a, item, MASK == MASK_SUB);
-    if (item.begin < item.end) fetch(list_idx(a, lst, item.begin));
+    // query blocks, and (MASK_BAND_ROUTED) routed tiles nb + r
+    const int qlimit = a.nb + (MASK == MASK_BAND_ROUTED ? (a.n_routed + 63) / 64 : 0);
+    const ItemList lst = load_list(a, item, MASK == MASK_SUB, qlimit);
+    if (item.begin < item.end) fetch(list_idx(a, lst, item.begin, qlimit));
     for (int e = item.begin; e < item.end; ++e) {
         // 32-token blocks: query halves that may see this wave's key half
         const int sub = MASK == MASK_SUB ? list_sub(a, lst, e) >> wave : 15;
         // band layouts: query block ib, masked per pair unless the whole tile is inside the band
-        const int ib = list_idx(a, lst, e);
+        const int ib = list_idx(a, lst, e, qlimit);
         const bool routed_entry = MASK == MASK_BAND_ROUTED && ib >= a.nb;
         const bool band_cut = (MASK == MASK_BAND || MASK == MASK_BAND_ROUTED) && !routed_entry &&
                               64 * abs(blk - ib) + 63 > a.band;
@@ -413,7 +440,7 @@ __global__ __launch_bounds__(kBT) void bwd_dkdv_kernel(const BwdArgs a) {
             qtok[tid] = tok_r;
         }
         __syncthreads();
-        if (e + 1 < item.end) fetch(list_idx(a, lst, e + 1));   // behind this tile's products
+        if (e + 1 < item.end) fetch(list_idx(a, lst, e + 1, qlimit));   // behind this tile's products
         // S = Q K^T - LSE/scale and dP = dO V^T - delta: block qb holds queries 32qb .. 32qb + 31,
         // register i <-> query 32qb + 8(i/4) + 4hh + i%4
         f32x16_t s[2], dp[2];
@@ -568,7 +595,30 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s, hipEvent_t before, hip
 
 }  // namespace
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s) {
+#ifdef BSATTN_DEBUG
+// Debug builds: the word the backward kernels report list errors into.
+__device__ uint32_t g_bwd_dbg_word;
+
+// Clear the word, run `launch` with it, read it back (synchronising the
+// stream); a set bit is reported as a device-side assert.
+template <class F>
+hipError_t debug_launch(const BwdArgs& a, hipStream_t s, F&& launch) {
+    uint32_t* dw = nullptr;
+    hipError_t e = hipGetSymbolAddress((void**)&dw, HIP_SYMBOL(g_bwd_dbg_word));
+    if (e != hipSuccess) return e;
+    static const uint32_t zero = 0;
+    if ((e = hipMemcpyAsync(dw, &zero, sizeof(zero), hipMemcpyHostToDevice, s)) != hipSuccess) return e;
+    BwdArgs ad = a;
+    ad.dbg = dw;
+    if ((e = launch(ad)) != hipSuccess) return e;
+    uint32_t flag = 0;
+    if ((e = hipMemcpyAsync(&flag, dw, sizeof(flag), hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    return flag ? hipErrorAssert : hipSuccess;
+}
+#endif
+
+static hipError_t launch_bwd_dq_impl(const BwdArgs& a, int head_dim, int mask, hipStream_t s) {
     if (mask == MASK_ROUTED_Q)
         return head_dim == 64 ? launch_dq_t<64, MASK_ROUTED_Q>(a, s) : launch_dq_t<128, MASK_ROUTED_Q>(a, s);
     if (head_dim == 64)
@@ -582,8 +632,8 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s
                               : launch_dq_t<128, MASK_NONE>(a, s);
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
-                           hipEvent_t after) {
+static hipError_t launch_bwd_dkdv_impl(const BwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
+                                       hipEvent_t after) {
     if (mask == MASK_BAND_ROUTED)
         return head_dim == 64 ? launch_dkdv_t<64, MASK_BAND_ROUTED>(a, s, before, after)
                               : launch_dkdv_t<128, MASK_BAND_ROUTED>(a, s, before, after);
@@ -596,6 +646,25 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t
          : mask == MASK_SUB   ? launch_dkdv_t<128, MASK_SUB>(a, s, before, after)
          : mask == MASK_BAND  ? launch_dkdv_t<128, MASK_BAND>(a, s, before, after)
                               : launch_dkdv_t<128, MASK_NONE>(a, s, before, after);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int mask, hipStream_t s) {
+#ifdef BSATTN_DEBUG
+    return debug_launch(a, s, [&](const BwdArgs& ad) { return launch_bwd_dq_impl(ad, head_dim, mask, s); });
+#else
+    return launch_bwd_dq_impl(a, head_dim, mask, s);
+#endif
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int mask, hipStream_t s, hipEvent_t before,
+                           hipEvent_t after) {
+#ifdef BSATTN_DEBUG
+    return debug_launch(a, s, [&](const BwdArgs& ad) {
+        return launch_bwd_dkdv_impl(ad, head_dim, mask, s, before, after);
+    });
+#else
+    return launch_bwd_dkdv_impl(a, head_dim, mask, s, before, after);
+#endif
 }
 
 hipError_t launch_bwd_routed_sum(const BwdArgs& a, int head_dim, hipStream_t s) {

@@ -1,14 +1,15 @@
 """The bounds-checking debug build (libbsattn_debug.so, -DBSATTN_DEBUG) on the GPU.
 
 In that build the forward kernels check every schedule entry they read (list
-lengths, unit records, tile entries) and each forward call synchronises and
-fails if a check did not hold.  Run as a script, this file computes forwards of
-every schedule kind (D = 64 rows with split global rows merged in the kernel,
-D = 128 with key padding, the routed variant, the token pattern) with whichever
-library BSATTN_LIBRARY selects and saves them; the test runs it once with each
-build, in child processes one after the other, and requires the debug build's
-calls to succeed and to give the release build's outputs bit for bit (the
-checks change no arithmetic)."""
+lengths, unit records, tile entries), the backward kernels every item and block
+list entry, and each forward and backward pass synchronises and fails if a check
+did not hold.  Run as a script, this file computes forwards and backwards of
+every schedule kind (D = 64 rows with split global rows, D = 128 with key
+padding, the routed variant, the token pattern) with whichever library
+BSATTN_LIBRARY selects and saves them; the test runs it once with each build,
+in child processes one after the other, and requires the debug build's calls to
+succeed and to give the release build's outputs bit for bit (the checks change
+no arithmetic)."""
 import os
 import subprocess
 import sys
@@ -25,7 +26,7 @@ def _cases(out_path):
     import torch
 
     import block_sparse_transformer_amd as bs
-    from workloads import WORKLOADS, make_inputs
+    from workloads import WORKLOADS, make_grad_output, make_inputs
 
     res = {}
 
@@ -41,6 +42,9 @@ def _cases(out_path):
     bs.bsattn_layout_upload(lay)
     o, l = bs.forward(inp["q"], inp["k"], inp["v"], lay, scale=wl.scale)
     res["d64_o"], res["d64_l"] = o, l
+    do = make_grad_output(wl).cuda()
+    res["d64_dq"], res["d64_dk"], res["d64_dv"] = bs.backward(inp["q"], inp["k"], inp["v"], o, l, do, lay,
+                                                              scale=wl.scale)
     # D = 128 with key padding (the two-wave kernel)
     wl = WORKLOADS["window-pad-L16384"].with_(batch=2, heads=2, seq_len=2048)
     say("debug-build", wl.name, "D=128 padded")
@@ -50,6 +54,9 @@ def _cases(out_path):
     bs.bsattn_layout_upload(lay)
     o, l = bs.forward(inp["q"], inp["k"], inp["v"], lay, key_valid_len=inp["valid_len"], scale=wl.scale)
     res["pad_o"], res["pad_l"] = o, l
+    do = make_grad_output(wl).cuda()
+    res["pad_dq"], res["pad_dk"], res["pad_dv"] = bs.backward(inp["q"], inp["k"], inp["v"], o, l, do, lay,
+                                                              key_valid_len=inp["valid_len"], scale=wl.scale)
     # routed rows over a token band
     wl = WORKLOADS["routed-L4096"].with_(heads=2, seq_len=1024, routed_k=70)
     say("debug-build", wl.name, "routed k=70")
@@ -60,6 +67,9 @@ def _cases(out_path):
     bs.bsattn_layout_upload(band)
     o, l = bs.forward_routed(inp["q"], inp["k"], inp["v"], band, rr, scale=wl.scale)
     res["routed_o"], res["routed_l"] = o, l
+    do = make_grad_output(wl).cuda()
+    res["routed_dq"], res["routed_dk"], res["routed_dv"] = bs.backward_routed(
+        inp["q"], inp["k"], inp["v"], o, l, do, band, rr, scale=wl.scale)
     # the token pattern (gathered global-key tiles, per-token random links)
     wl = WORKLOADS["bigbird-tok-L8192"].with_(batch=1, heads=2, seq_len=1536)
     say("debug-build", wl.name, "token pattern")
@@ -69,6 +79,9 @@ def _cases(out_path):
     bs.bsattn_layout_upload(lay)
     o, l = bs.forward(inp["q"], inp["k"], inp["v"], lay, scale=wl.scale)
     res["tok_o"], res["tok_l"] = o, l
+    do = make_grad_output(wl).cuda()
+    res["tok_dq"], res["tok_dk"], res["tok_dv"] = bs.backward(inp["q"], inp["k"], inp["v"], o, l, do, lay,
+                                                              scale=wl.scale)
     torch.cuda.synchronize()
     np.savez(out_path, **{k: (v.view(torch.int16) if v.dtype == torch.bfloat16 else v).cpu().numpy()
                           for k, v in res.items()})
